@@ -1,0 +1,263 @@
+"""Python binding of the MI355X DP / Split-K / Stream-K GEMM library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libdgw_gemm.so`` (built in-tree by ``dense_gemm_work_amd.build``).
+The functions carry the names of the C entry points in ``include/gemm.h``:
+
+* ``gemm(A, B, C, M, N, K, layout, mode, splits)`` -- raw device pointers.
+* ``gemm_ex(args)``, ``gemm_plan(...)``, ``gemm_unit_range(...)``,
+  ``gemm_set_stream``, ``gemm_sync_status``, ``gemm_release``,
+  ``gemm_last_error``, ``gemm_num_cus``, ``gemm_version``.
+
+``gemm_tensors(a, b, c, ...)`` is the torch-facing convenience: it checks the
+tensors' device, dtype, shape and contiguity on the host, passes their data
+pointers and torch's current HIP stream, and raises ``GemmError`` on a
+negative status.  Importing this module fails loudly when the library has not
+been built; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+from typing import Optional
+
+__all__ = [
+    "GemmError", "GemmPlan", "GemmArgs", "gemm", "gemm_ex", "gemm_plan", "gemm_unit_range",
+    "gemm_set_stream", "gemm_sync_status", "gemm_release", "gemm_last_error", "gemm_num_cus",
+    "gemm_version", "gemm_tensors", "plan_dict", "library_path",
+]
+
+_PKG = Path(__file__).resolve().parent
+_LIB_PATH = _PKG / "libdgw_gemm.so"
+
+# ---- constants (include/gemm.h) ------------------------------------------------
+GEMM_OK = 0
+GEMM_ERR_INVALID = -1
+GEMM_ERR_UNSUPPORTED = -2
+GEMM_ERR_WORKSPACE = -3
+GEMM_ERR_HIP = -4
+GEMM_ERR_TIMEOUT = -5
+
+GEMM_B_KN = 0x00
+GEMM_B_NK = 0x01
+GEMM_BF16 = 0x00
+GEMM_FP16 = 0x10
+
+GEMM_HEURISTIC = 0x0
+GEMM_DP = 0x1
+GEMM_SPLITK = 0x2
+GEMM_STREAMK = 0x3
+GEMM_DETERMINISTIC = 0x000
+GEMM_ATOMIC = 0x100
+
+GEMM_DEBUG_NO_PUBLISH = 0x1
+
+GEMM_BM = 128
+GEMM_BN = 128
+GEMM_BK = 64
+
+MODES = {"heuristic": GEMM_HEURISTIC, "dp": GEMM_DP, "splitk": GEMM_SPLITK, "streamk": GEMM_STREAMK}
+DECISION_NAMES = {GEMM_DP: "DataParallel", GEMM_SPLITK: "SplitK", GEMM_STREAMK: "StreamK"}
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"gemm status {status}: {message}")
+        self.status = status
+
+
+class GemmPlan(ctypes.Structure):
+    _fields_ = [
+        ("decision", ctypes.c_int32), ("atomic", ctypes.c_int32),
+        ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
+        ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("tiles", ctypes.c_int64),
+        ("ipt", ctypes.c_int64), ("full_waves", ctypes.c_int64), ("total_waves", ctypes.c_int64),
+        ("tail", ctypes.c_int64), ("sk_tiles", ctypes.c_int64), ("sk_units", ctypes.c_int64),
+        ("dp_tiles", ctypes.c_int64), ("q", ctypes.c_int64), ("big", ctypes.c_int64),
+        ("splits", ctypes.c_int32), ("max_segments", ctypes.c_int32), ("max_fold", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("workers", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64), ("trace_ints", ctypes.c_int64),
+    ]
+
+
+class GemmArgs(ctypes.Structure):
+    _fields_ = [
+        ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("layout", ctypes.c_uint32), ("mode", ctypes.c_uint32), ("splits", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32), ("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("unit_perm", ctypes.c_void_p),
+        ("trace", ctypes.c_void_p), ("trace_ints", ctypes.c_int64),
+        ("spin_limit", ctypes.c_uint32), ("debug", ctypes.c_uint32),
+    ]
+
+
+def library_path() -> Path:
+    return _LIB_PATH
+
+
+def _load() -> ctypes.CDLL:
+    if not _LIB_PATH.exists():
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run __graft_entry__.build() (or python -m "
+            "dense_gemm_work_amd.build) first -- there is no fallback implementation")
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    i64, u32, i32, vp = ctypes.c_int64, ctypes.c_uint32, ctypes.c_int32, ctypes.c_void_p
+    lib.gemm.restype = ctypes.c_int
+    lib.gemm.argtypes = [vp, vp, vp, i64, i64, i64, u32, u32, i32]
+    lib.gemm_ex.restype = ctypes.c_int
+    lib.gemm_ex.argtypes = [ctypes.POINTER(GemmArgs)]
+    lib.gemm_plan.restype = ctypes.c_int
+    lib.gemm_plan.argtypes = [i64, i64, i64, u32, u32, i32, i32, ctypes.POINTER(GemmPlan)]
+    lib.gemm_unit_range.restype = ctypes.c_int
+    lib.gemm_unit_range.argtypes = [ctypes.POINTER(GemmPlan), i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.gemm_set_stream.restype = ctypes.c_int
+    lib.gemm_set_stream.argtypes = [vp]
+    lib.gemm_sync_status.restype = ctypes.c_int
+    lib.gemm_sync_status.argtypes = [vp]
+    lib.gemm_release.restype = None
+    lib.gemm_release.argtypes = []
+    lib.gemm_last_error.restype = ctypes.c_char_p
+    lib.gemm_last_error.argtypes = []
+    lib.gemm_num_cus.restype = ctypes.c_int32
+    lib.gemm_num_cus.argtypes = []
+    lib.gemm_version.restype = ctypes.c_int32
+    lib.gemm_version.argtypes = []
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int) -> int:
+    if status < 0:
+        raise GemmError(status, gemm_last_error())
+    return status
+
+
+# ---- C entry points, same names ----------------------------------------------------
+def gemm(A: int, B: int, C: int, M: int, N: int, K: int, layout: int, mode: int, splits: int) -> int:
+    """Raw call on device pointers; returns the status (no exception)."""
+    return _lib.gemm(A, B, C, M, N, K, layout, mode, splits)
+
+
+def gemm_ex(args: GemmArgs) -> int:
+    return _lib.gemm_ex(ctypes.byref(args))
+
+
+def gemm_plan(M: int, N: int, K: int, layout: int, mode: int, splits: int, num_cus: int) -> GemmPlan:
+    p = GemmPlan()
+    _check(_lib.gemm_plan(M, N, K, layout, mode, splits, num_cus, ctypes.byref(p)))
+    return p
+
+
+def gemm_unit_range(plan: GemmPlan, unit: int):
+    b, e = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.gemm_unit_range(ctypes.byref(plan), unit, ctypes.byref(b), ctypes.byref(e)))
+    return b.value, e.value
+
+
+def gemm_set_stream(stream: Optional[int]) -> int:
+    return _lib.gemm_set_stream(stream or None)
+
+
+def gemm_sync_status(stream: Optional[int] = None) -> int:
+    return _lib.gemm_sync_status(stream or None)
+
+
+def gemm_release() -> None:
+    _lib.gemm_release()
+
+
+def gemm_last_error() -> str:
+    return (_lib.gemm_last_error() or b"").decode()
+
+
+def gemm_num_cus() -> int:
+    return int(_lib.gemm_num_cus())
+
+
+def gemm_version() -> int:
+    return int(_lib.gemm_version())
+
+
+# ---- helpers ---------------------------------------------------------------------------
+def plan_dict(p: GemmPlan) -> dict:
+    d = {name: getattr(p, name) for name, _ in GemmPlan._fields_}
+    d["decision_name"] = DECISION_NAMES.get(p.decision, str(p.decision))
+    return d
+
+
+def layout_word(b_layout: str, dtype: str) -> int:
+    lw = {"kn": GEMM_B_KN, "nk": GEMM_B_NK}[b_layout]
+    return lw | {"bf16": GEMM_BF16, "fp16": GEMM_FP16}[dtype]
+
+
+def mode_word(mode: str, atomic: bool = False) -> int:
+    return MODES[mode] | (GEMM_ATOMIC if atomic else 0)
+
+
+def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits: int = 0,
+                 atomic: bool = False, num_cus: int = 0, unit_perm=None, trace=None,
+                 workspace=None, spin_limit: int = 0, debug: int = 0, stream=None) -> None:
+    """``c[M,N] = a[M,K] . b`` (b [K,N]) or ``a . b^T`` (b [N,K]) on torch tensors.
+
+    a, b: contiguous bf16/fp16 tensors on one HIP device; c: contiguous fp32 [M,N].
+    unit_perm / trace / workspace: optional int32 / int32 / any-dtype device tensors.
+    Enqueues on ``stream`` (a torch.cuda.Stream) or torch's current stream.
+    """
+    import torch
+
+    if a.dim() != 2 or b.dim() != 2 or c.dim() != 2:
+        raise ValueError("a, b and c must be 2-D")
+    if a.dtype not in (torch.bfloat16, torch.float16) or b.dtype != a.dtype:
+        raise TypeError("a and b must both be bf16 or both fp16")
+    if c.dtype != torch.float32:
+        raise TypeError("c must be fp32")
+    for name, t in (("a", a), ("b", b), ("c", c)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (a.device == b.device == c.device):
+        raise ValueError("a, b and c must be on one device")
+    M, K = a.shape
+    if b_layout == "kn":
+        if b.shape[0] != K:
+            raise ValueError("b must be [K, N]")
+        N = b.shape[1]
+    elif b_layout == "nk":
+        if b.shape[1] != K:
+            raise ValueError("b must be [N, K]")
+        N = b.shape[0]
+    else:
+        raise ValueError("b_layout must be 'kn' or 'nk'")
+    if tuple(c.shape) != (M, N):
+        raise ValueError("c must be [M, N]")
+    dtype = "bf16" if a.dtype == torch.bfloat16 else "fp16"
+    args = GemmArgs()
+    args.A, args.B, args.C = a.data_ptr(), b.data_ptr(), c.data_ptr()
+    args.M, args.N, args.K = M, N, K
+    args.layout = layout_word(b_layout, dtype)
+    args.mode = mode_word(mode, atomic)
+    args.splits = splits
+    args.num_cus = num_cus
+    with torch.cuda.device(a.device):
+        s = stream if stream is not None else torch.cuda.current_stream(a.device)
+        args.stream = s.cuda_stream
+        if unit_perm is not None:
+            if unit_perm.dtype != torch.int32 or not unit_perm.is_cuda or not unit_perm.is_contiguous():
+                raise TypeError("unit_perm must be a contiguous int32 device tensor")
+            args.unit_perm = unit_perm.data_ptr()
+        if trace is not None:
+            if trace.dtype != torch.int32 or not trace.is_cuda or not trace.is_contiguous():
+                raise TypeError("trace must be a contiguous int32 device tensor")
+            args.trace = trace.data_ptr()
+            args.trace_ints = trace.numel()
+        if workspace is not None:
+            args.workspace = workspace.data_ptr()
+            args.workspace_bytes = workspace.numel() * workspace.element_size()
+        args.spin_limit = spin_limit
+        args.debug = debug
+        _check(gemm_ex(args))

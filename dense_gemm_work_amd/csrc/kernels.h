@@ -1,0 +1,57 @@
+// kernels.h -- launch interface of the gfx950 GEMM kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace dgw {
+
+// Which epilogue/fixup a launch performs.
+enum KernelMode : int {
+    K_DP = 0,         // whole-K tiles, plain store
+    K_SPLITK = 1,     // split s of tile t; fp32 partial [S,M,N]; last arriver folds in split order
+    K_SK = 2,         // Stream-K, deterministic turnstile through per-unit partial slots
+    K_SK_ATOMIC = 3,  // Stream-K, split tiles merged by fp32 atomic adds into zeroed C
+};
+
+// Error bits of the device status word.
+enum : uint32_t { STATUS_TIMEOUT = 1u };
+
+struct KParams {
+    const uint16_t *A;     // [M,K] row-major 16-bit operands
+    const uint16_t *B;     // [K,N] or [N,K] row-major
+    float *C;              // [M,N] row-major fp32
+    int M, N, K;
+    int tiles_n;           // output tiles along N
+    int ipt;               // k-iterations per tile
+    int tile_base;         // first tile id of this launch (hybrid: Stream-K part starts at dp_tiles)
+    int ntiles;            // tiles of a DP / Split-K launch
+    int units, q, big;     // Stream-K unit ranges: unit u starts at u*q + min(u, big)
+    int splits;            // Split-K factor S
+    int worker_base;       // trace id of this launch's worker 0
+    float *part;           // Stream-K slots [units][BM*BN] or Split-K partials [S][M][N]
+    uint32_t *flags;       // Stream-K: flag per unit (epoch-valued)
+    uint32_t *counters;    // Split-K: arrival counter per tile (reset by the last arriver)
+    uint32_t *status;      // device error word
+    uint32_t epoch;        // value a publishing unit writes into its flag
+    uint32_t spin_limit;   // polls before a wait gives up
+    uint32_t debug;        // GEMM_DEBUG_* bits
+    const int *perm;       // optional workgroup -> worker map
+    int *trace;            // optional debug trace (see gemm.h)
+    int trace_maxseg, trace_maxfold, trace_workers, trace_tiles;
+};
+
+// Launch `grid` workgroups of the kernel for (dtype, B layout, mode) on `stream`.
+// dtype: 0 bf16, 1 fp16; blayout: 0 = B [K,N], 1 = B [N,K].
+hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParams &p,
+                       hipStream_t stream);
+
+// Fill n 32-bit words with zero (used instead of hipMemsetAsync so the call can
+// be captured in a HIP graph).
+hipError_t launch_zero(void *ptr, int64_t n_words, hipStream_t stream);
+
+// Resident workgroups per CU for the kernel of (dtype, blayout, kmode).
+hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int *out);
+
+}  // namespace dgw

@@ -1,0 +1,188 @@
+// plan.cpp -- host-side planning of a GEMM call: tile and wave arithmetic, the
+// decomposition rule, Stream-K unit ranges and workspace sizing.  Integer code
+// only; no GPU is touched.
+//
+// Sources (Split-K/Stream-K book chapter, "Split-K and Stream-K: The Last Wave
+// of a GEMM"):
+//  * Case 1: tiles = ceil(M/BM) ceil(N/BN), waves = ceil(tiles/SMs), tail wave.
+//  * Stream-K paragraph after the glossary: unit u owns a contiguous slice of
+//    the flattened (tile, k-iteration) space; Case 2 gives the first
+//    (total mod units) units one extra iteration.
+//  * Case 2 and Case 4 (decomposition rule): data-parallel when there is no
+//    partial wave or a tile has at most 8 k-iterations; data-parallel when the
+//    tail wave is at least half full; otherwise Stream-K over the last two
+//    waves with at least 8 iterations per unit, and Split-K when the units
+//    divide evenly over the split tiles.
+// docc StreamK page, "MMA fragment accumulators (aligned split)": Split-K with
+// S dividing the panel count.
+#include "plan.h"
+
+#include <algorithm>
+#include <cstring>
+
+namespace dgw {
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+int64_t unit_begin(int64_t unit, int64_t q, int64_t big) {
+    // units below `big` are one iteration longer
+    return unit * q + std::min(unit, big);
+}
+
+int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, int32_t splits,
+              int32_t num_cus, gemm_plan_t *out, const char **why) {
+    static const char *none = "";
+    *why = none;
+    if (!out) { *why = "plan output pointer is null"; return GEMM_ERR_INVALID; }
+    std::memset(out, 0, sizeof *out);
+    if (M < 0 || N < 0 || K < 0) { *why = "M, N and K must be >= 0"; return GEMM_ERR_INVALID; }
+    if (num_cus < 1) { *why = "num_cus must be >= 1"; return GEMM_ERR_INVALID; }
+    const uint32_t b_layout = layout & 0xFu, dtype = layout & 0xF0u;
+    if ((layout & ~0xFFu) || (b_layout != GEMM_B_KN && b_layout != GEMM_B_NK) ||
+        (dtype != GEMM_BF16 && dtype != GEMM_FP16)) {
+        *why = "layout word has unknown bits";
+        return GEMM_ERR_INVALID;
+    }
+    const uint32_t decomp = mode & 0xFu;
+    const bool atomic = (mode & GEMM_ATOMIC) != 0;
+    if ((mode & ~(0xFu | GEMM_ATOMIC)) || decomp > GEMM_STREAMK) {
+        *why = "mode word has unknown bits";
+        return GEMM_ERR_INVALID;
+    }
+    if (atomic && decomp != GEMM_STREAMK && decomp != GEMM_HEURISTIC) {
+        *why = "GEMM_ATOMIC applies to Stream-K only";
+        return GEMM_ERR_INVALID;
+    }
+    if ((decomp == GEMM_DP || decomp == GEMM_HEURISTIC) && splits != 0) {
+        *why = "splits must be 0 for GEMM_DP and GEMM_HEURISTIC";
+        return GEMM_ERR_INVALID;
+    }
+    if (splits < 0) { *why = "splits must be >= 0"; return GEMM_ERR_INVALID; }
+    if (K % 8 != 0) { *why = "K must be a multiple of 8 (128-bit row loads)"; return GEMM_ERR_UNSUPPORTED; }
+    if (b_layout == GEMM_B_KN && N % 8 != 0) {
+        *why = "N must be a multiple of 8 when B is stored [K,N] (128-bit row loads)";
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    // keep every flattened index and element offset in range of the kernels' arithmetic
+    if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) {
+        *why = "M, N and K must each be at most 2^31";
+        return GEMM_ERR_UNSUPPORTED;
+    }
+
+    gemm_plan_t &p = *out;
+    p.atomic = 0;
+    p.bm = GEMM_BM; p.bn = GEMM_BN; p.bk = GEMM_BK;
+    p.num_cus = num_cus;
+    p.tiles_m = ceil_div(M, GEMM_BM);
+    p.tiles_n = ceil_div(N, GEMM_BN);
+    p.tiles = p.tiles_m * p.tiles_n;
+    p.ipt = ceil_div(K, GEMM_BK);
+    p.full_waves = p.tiles / num_cus;
+    p.total_waves = ceil_div(p.tiles, num_cus);
+    p.tail = p.tiles - (p.total_waves > 0 ? (p.total_waves - 1) * num_cus : 0);
+    p.splits = 1;
+    if (p.tiles * std::max<int64_t>(p.ipt, 1) >= (int64_t(1) << 31)) {
+        *why = "tiles x k-iterations must stay below 2^31";
+        return GEMM_ERR_UNSUPPORTED;
+    }
+
+    uint32_t chosen = decomp;
+    int64_t units = 0, sk_tiles = 0;
+    int32_t S = 1;
+    if (decomp == GEMM_HEURISTIC) {
+        const int64_t min_iters = 8;
+        const bool whole_waves = p.full_waves == p.total_waves;
+        const int64_t tail = p.tiles - p.full_waves * num_cus;
+        if (whole_waves || p.ipt <= min_iters || 2 * tail >= num_cus) {
+            chosen = GEMM_DP;
+        } else {
+            const int64_t dp_waves = p.full_waves > 1 ? p.full_waves - 1 : 0;
+            sk_tiles = p.tiles - dp_waves * num_cus;
+            units = std::min<int64_t>(num_cus, (p.ipt * sk_tiles) / min_iters);
+            if (units > sk_tiles && units % sk_tiles == 0) {
+                chosen = GEMM_SPLITK;
+                S = int32_t(units / sk_tiles);
+            } else {
+                chosen = GEMM_STREAMK;
+            }
+        }
+        if (atomic && chosen != GEMM_STREAMK) {
+            // atomic merging only changes Stream-K; other choices ignore it
+        }
+    } else if (decomp == GEMM_SPLITK) {
+        if (splits < 1) { *why = "GEMM_SPLITK needs splits >= 1"; return GEMM_ERR_INVALID; }
+        if (p.ipt == 0 || p.ipt % splits != 0) {
+            *why = "GEMM_SPLITK needs splits to divide ceil(K/64)";
+            return GEMM_ERR_INVALID;
+        }
+        S = splits;
+    } else if (decomp == GEMM_STREAMK) {
+        units = splits > 0 ? splits : num_cus;
+        sk_tiles = p.tiles;
+    }
+
+    p.decision = int32_t(chosen);
+    switch (chosen) {
+    case GEMM_DP:
+        p.dp_tiles = p.tiles;
+        p.workers = p.tiles;
+        p.max_segments = 1;
+        p.max_fold = 1;
+        p.workspace_bytes = 0;
+        break;
+    case GEMM_SPLITK:
+        p.splits = S;
+        p.workers = p.tiles * S;
+        p.max_segments = 1;
+        p.max_fold = S;
+        // fp32 partials [S, M, N] plus one arrival counter per tile
+        p.workspace_bytes = S > 1 ? int64_t(S) * M * N * 4 : 0;
+        break;
+    case GEMM_STREAMK: {
+        p.atomic = atomic ? 1 : 0;
+        p.sk_units = units;
+        p.sk_tiles = sk_tiles;
+        p.dp_tiles = p.tiles - sk_tiles;
+        const int64_t total = sk_tiles * p.ipt;
+        p.q = units > 0 ? total / units : 0;
+        p.big = units > 0 ? total % units : 0;
+        p.workers = units + p.dp_tiles;
+        const int64_t longest = p.q + (p.big > 0 ? 1 : 0);
+        const int64_t ipt1 = std::max<int64_t>(p.ipt, 1);
+        p.max_segments = int32_t(std::min<int64_t>(std::max<int64_t>(sk_tiles, 1),
+                                                   ceil_div(longest, ipt1) + 1));
+        p.max_fold = int32_t(std::min<int64_t>(units, ceil_div(ipt1, std::max<int64_t>(p.q, 1)) + 1));
+        p.max_fold = std::max(p.max_fold, 1);
+        // fp32 partial slot per unit (a unit publishes at most its first segment)
+        p.workspace_bytes = atomic ? 0 : units * int64_t(GEMM_BM) * GEMM_BN * 4;
+        break;
+    }
+    default:
+        *why = "internal: no decision";
+        return GEMM_ERR_INVALID;
+    }
+    // control words: status (64 B), Stream-K flags, Split-K counters, each 256-B aligned
+    p.workspace_bytes += control_bytes(p);
+    p.trace_ints = 8 + p.workers * (1 + 4 * int64_t(p.max_segments)) +
+                   p.tiles * (1 + int64_t(p.max_fold)) + p.tiles * p.ipt;
+    return GEMM_OK;
+}
+
+int64_t control_bytes(const gemm_plan_t &p) {
+    auto round = [](int64_t b) { return (b + 255) / 256 * 256; };
+    return 256 + round(std::max<int64_t>(p.sk_units, 1) * 4) + round(std::max<int64_t>(p.tiles, 1) * 4);
+}
+
+}  // namespace dgw
+
+extern "C" int gemm_unit_range(const gemm_plan_t *plan, int64_t unit, int64_t *begin, int64_t *end) {
+    if (!plan || !begin || !end) return GEMM_ERR_INVALID;
+    if (plan->decision != GEMM_STREAMK || unit < 0 || unit >= plan->sk_units) return GEMM_ERR_INVALID;
+    *begin = dgw::unit_begin(unit, plan->q, plan->big);
+    *end = *begin + plan->q + (unit < plan->big ? 1 : 0);
+    return GEMM_OK;
+}

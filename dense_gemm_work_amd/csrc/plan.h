@@ -1,0 +1,20 @@
+// plan.h -- host planner interface (internal to the library).
+#pragma once
+
+#include <cstdint>
+
+#include "../../include/gemm.h"
+
+namespace dgw {
+
+// Fill *out for a call; returns a GEMM_* status and points *why at a message.
+int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, int32_t splits,
+              int32_t num_cus, gemm_plan_t *out, const char **why);
+
+// First flattened iteration of Stream-K unit `unit` ("big" units first).
+int64_t unit_begin(int64_t unit, int64_t q, int64_t big);
+
+// Bytes of control words (status, flags, counters) at the head of the workspace.
+int64_t control_bytes(const gemm_plan_t &p);
+
+}  // namespace dgw

@@ -1,0 +1,241 @@
+/*
+ * gemm.h -- C ABI of the MI355X (gfx950) data-parallel / Split-K / Stream-K GEMM.
+ *
+ * Operation (every entry point computes the same thing):
+ *
+ *     C[M,N] = A[M,K] . B          (B stored [K,N], row-major)        layout GEMM_B_KN
+ *     C[M,N] = A[M,K] . B^T        (B stored [N,K], row-major)        layout GEMM_B_NK
+ *
+ * A and B hold bf16 or fp16 values; products are accumulated in fp32 and C is
+ * written in fp32 (overwrite: no alpha/beta).  The work decomposition is the
+ * subject of the Split-K/Stream-K book chapter ("Split-K and Stream-K: The Last
+ * Wave of a GEMM", kanthi.in): output tiles of 128x128 elements, one
+ * "MAC-loop iteration" per 64-wide step of K (glossary table), and three ways
+ * to hand iterations to workgroups:
+ *
+ *   GEMM_DP       one workgroup per output tile, whole K loop (glossary, "Data-parallel").
+ *   GEMM_SPLITK   S workgroups per tile; tile t, split s covers k-iterations
+ *                 [s P/S, (s+1) P/S) of the tile's P iterations, stores an fp32
+ *                 partial into a [S,M,N] workspace and arrives at the tile's
+ *                 counter; the last arriver adds the S partials in split order
+ *                 (docc StreamK page, "MMA fragment accumulators (aligned split)").
+ *   GEMM_STREAMK  one persistent workgroup per unit; unit u owns a contiguous,
+ *                 equal slice of the flattened (tile x k-iteration) space, the
+ *                 first (total mod units) units taking one extra iteration
+ *                 (book chapter, Stream-K paragraph after the glossary, and Case 2).
+ *                 A unit that starts a tile mid-K publishes an fp32 partial and
+ *                 a flag; the unit holding the tile's k = 0 iteration waits for
+ *                 its peers in k order, adds their partials and writes C
+ *                 (deterministic "turnstile", Case 4's reduction modes).  With
+ *                 GEMM_ATOMIC, split tiles are instead merged by fp32 atomic
+ *                 adds into C, which the library zero-fills first
+ *                 (nondeterministic mode; docc StreamK page, "Rewrite it produces").
+ *   GEMM_HEURISTIC  the decomposition rule of Case 2 / Case 4 with SMs = CUs:
+ *                 DP if there is no partial wave or P <= 8; DP if the tail wave
+ *                 is at least half full; otherwise Stream-K over the last two
+ *                 waves with at least 8 iterations per unit (the earlier waves
+ *                 stay DP), or Split-K when those units divide evenly over the
+ *                 Stream-K tiles.
+ *
+ * Threading and streams: every call is asynchronous on a HIP stream (the one
+ * given to gemm_ex, else the calling thread's stream from gemm_set_stream,
+ * else the null stream).  The library-owned workspace is one per device;
+ * calls that use it must be ordered on the device (one stream, or streams
+ * synchronised by the caller).  Calls that overlap on one device race.
+ *
+ * Errors: a negative status is returned and nothing is launched (C untouched)
+ * for every condition the host can detect; gemm_last_error() then describes it.
+ */
+#ifndef DGW_GEMM_H
+#define DGW_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------- */
+#define GEMM_OK               0
+#define GEMM_ERR_INVALID     (-1)   /* bad argument (null pointer, bad size, bad mode bits, ...) */
+#define GEMM_ERR_UNSUPPORTED (-2)   /* legal but outside what the kernels handle (alignment, capacity) */
+#define GEMM_ERR_WORKSPACE   (-3)   /* workspace too small or could not be allocated */
+#define GEMM_ERR_HIP         (-4)   /* a HIP runtime call or a launch failed */
+#define GEMM_ERR_TIMEOUT     (-5)   /* a Stream-K/Split-K wait hit its spin limit (gemm_sync_status) */
+
+/* ---- layout word ------------------------------------------------------------- */
+/* bits 0-3: how B is stored (A is always [M,K] row-major, C always fp32 [M,N] row-major) */
+#define GEMM_B_KN   0x00u   /* B is [K,N] row-major: C = A.B                      */
+#define GEMM_B_NK   0x01u   /* B is [N,K] row-major: C = A.B^T (weights as [N,K]) */
+/* bits 4-7: operand type of A and B */
+#define GEMM_BF16   0x00u
+#define GEMM_FP16   0x10u
+
+/* ---- mode word ----------------------------------------------------------------- */
+/* bits 0-3: decomposition */
+#define GEMM_HEURISTIC 0x0u
+#define GEMM_DP        0x1u
+#define GEMM_SPLITK    0x2u
+#define GEMM_STREAMK   0x3u
+/* bit 8: how Stream-K merges split tiles */
+#define GEMM_DETERMINISTIC 0x000u  /* k-ordered turnstile through an fp32 partial workspace */
+#define GEMM_ATOMIC        0x100u  /* fp32 atomic adds into a zero-filled C */
+
+/* ---- debug bits for gemm_args_t.debug -------------------------------------------- */
+#define GEMM_DEBUG_NO_PUBLISH 0x1u /* contributors store partials but never raise their
+                                      flags: every wait ends at its spin limit and
+                                      gemm_sync_status() reports GEMM_ERR_TIMEOUT.
+                                      Exercises the failure path; C is not valid.   */
+
+/* Tile shape used by every decomposition. */
+#define GEMM_BM 128
+#define GEMM_BN 128
+#define GEMM_BK 64
+
+/*
+ * Result of planning one call (host arithmetic only; never touches a GPU).
+ * Tile counts follow the wave arithmetic of the book chapter, Case 1:
+ * tiles = ceil(M/BM) ceil(N/BN), waves = ceil(tiles/CUs).
+ */
+typedef struct gemm_plan_t {
+    int32_t decision;     /* GEMM_DP, GEMM_SPLITK or GEMM_STREAMK                          */
+    int32_t atomic;       /* 1 when Stream-K merges by atomics                              */
+    int32_t bm, bn, bk;   /* tile shape                                                     */
+    int32_t num_cus;      /* compute units the plan was made for                            */
+    int64_t tiles_m, tiles_n, tiles;
+    int64_t ipt;          /* k-iterations per tile, P = ceil(K / bk)                        */
+    int64_t full_waves;   /* floor(tiles / CUs)                                             */
+    int64_t total_waves;  /* ceil(tiles / CUs)                                              */
+    int64_t tail;         /* tiles in the last wave                                         */
+    int64_t sk_tiles;     /* Stream-K: tiles in the stream part (the LAST sk_tiles tiles)   */
+    int64_t sk_units;     /* Stream-K: units (persistent workgroups)                        */
+    int64_t dp_tiles;     /* tiles run as whole-K data-parallel tiles (tiles 0..dp_tiles-1) */
+    int64_t q;            /* Stream-K: floor(sk_tiles * ipt / units)                        */
+    int64_t big;          /* Stream-K: (sk_tiles * ipt) mod units = units with q+1 iters    */
+    int32_t splits;       /* Split-K factor S (1 for the other decompositions)              */
+    int32_t max_segments; /* most tile segments one worker can touch                        */
+    int32_t max_fold;     /* most workers contributing to one tile                          */
+    int32_t reserved;
+    int64_t workers;      /* traced workers: units + dp_tiles, tiles * S, or tiles          */
+    int64_t workspace_bytes; /* device workspace the call needs                             */
+    int64_t trace_ints;   /* int32 elements of a debug trace buffer for this call           */
+} gemm_plan_t;
+
+/*
+ * Extended arguments.  Zero-initialise, then fill what you need.
+ *   A, B, C, M, N, K, layout, mode, splits: as for gemm().
+ *   stream:   hipStream_t to enqueue on; NULL = the thread's gemm_set_stream value.
+ *   workspace, workspace_bytes: caller-owned device memory of at least
+ *             plan.workspace_bytes, zero-filled before its first use and used by
+ *             one stream at a time; NULL = the library's per-device workspace.
+ *   num_cus:  plan for this many CUs instead of the device's count (>= 1).  The
+ *             Stream-K grid must still fit on the device (all units co-resident).
+ *   unit_perm: optional device int32[grid]: workgroup b runs unit unit_perm[b]
+ *             (Stream-K) or worker unit_perm[b] (DP / Split-K).  Must be a
+ *             permutation of 0..grid-1.  The schedule does not change, only which
+ *             workgroup runs it (stresses arrival order).
+ *   trace, trace_ints: optional device int32 buffer of at least plan.trace_ints
+ *             elements; the kernels record what they did (layout in
+ *             gemm_trace_layout below).  The library zero-fills it first.
+ *   spin_limit: bound on every inter-workgroup wait, in polls (0 = default).
+ *   debug:    GEMM_DEBUG_* bits (0 in normal use).
+ */
+typedef struct gemm_args_t {
+    const void *A;
+    const void *B;
+    float *C;
+    int64_t M, N, K;
+    uint32_t layout;
+    uint32_t mode;
+    int32_t splits;
+    int32_t num_cus;
+    void *stream;
+    void *workspace;
+    size_t workspace_bytes;
+    const int32_t *unit_perm;
+    int32_t *trace;
+    int64_t trace_ints;
+    uint32_t spin_limit;
+    uint32_t debug;
+} gemm_args_t;
+
+/*
+ * Debug trace layout (int32 elements), written only when gemm_args_t.trace is set:
+ *   [0..7]   header: 0x4B525453 ("STRK"), decision, workers, tiles, ipt,
+ *            max_segments, max_fold, splits
+ *   then, per worker w (0..workers-1): 1 + 4*max_segments ints:
+ *            count, then count records (tile, k0, k1, role) in execution order,
+ *            role 0 = whole tile, 1 = k = 0 holder that waits and folds,
+ *            2 = starts mid-tile and publishes a partial
+ *   then, per tile t: 1 + max_fold ints: count, then the workers whose partials
+ *            were summed into the tile, in summation order (a whole tile lists
+ *            its one worker; under GEMM_ATOMIC a split tile's count stays 0)
+ *   then, per tile t: ipt ints: how many times each (tile, k-iteration) was run.
+ * Worker ids: Stream-K unit u -> u; hybrid DP tile t -> units + t;
+ * Split-K tile t split s -> t*S + s; DP tile t -> t.
+ */
+
+/*
+ * gemm -- the core call.
+ *   A: device pointer, [M,K] row-major bf16/fp16.
+ *   B: device pointer, [K,N] (GEMM_B_KN) or [N,K] (GEMM_B_NK) row-major, same type as A.
+ *   C: device pointer, [M,N] row-major fp32; overwritten.  Must not overlap A or B.
+ *   M, N, K >= 0.  M == 0 or N == 0: nothing to do.  K == 0: C is zero-filled.
+ *   layout: GEMM_B_KN|GEMM_B_NK combined with GEMM_BF16|GEMM_FP16.
+ *   mode: GEMM_HEURISTIC|GEMM_DP|GEMM_SPLITK|GEMM_STREAMK, optionally | GEMM_ATOMIC
+ *         (Stream-K only).
+ *   splits: GEMM_SPLITK: S >= 1 dividing ceil(K/64).  GEMM_STREAMK: unit count
+ *           (0 = one per CU).  GEMM_DP / GEMM_HEURISTIC: must be 0.
+ * Requirements (else GEMM_ERR_UNSUPPORTED): A, B, C 16-byte aligned; K a
+ * multiple of 8; N a multiple of 8 for GEMM_B_KN (128-bit row loads).
+ * Ownership: the caller owns A, B, C and the stream; nothing is retained.
+ * Returns GEMM_OK once the work is enqueued (asynchronous).
+ */
+int gemm(const void *A, const void *B, float *C, int64_t M, int64_t N, int64_t K,
+         uint32_t layout, uint32_t mode, int32_t splits);
+
+/* gemm_ex -- gemm() with the extended arguments above. */
+int gemm_ex(const gemm_args_t *args);
+
+/*
+ * gemm_plan -- decide the decomposition for a call without running it.
+ * num_cus >= 1 (no device is queried).  Fills *out; returns a status.
+ */
+int gemm_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode,
+              int32_t splits, int32_t num_cus, gemm_plan_t *out);
+
+/*
+ * gemm_unit_range -- [begin, end) of Stream-K unit u in the flattened space of
+ * the plan's Stream-K tiles (host arithmetic).  Returns a status.
+ */
+int gemm_unit_range(const gemm_plan_t *plan, int64_t unit, int64_t *begin, int64_t *end);
+
+/* gemm_set_stream -- the calling thread's default stream (hipStream_t, may be NULL). */
+int gemm_set_stream(void *stream);
+
+/*
+ * gemm_sync_status -- wait for the calling thread's stream (or `stream` if not
+ * NULL), then report and clear the device-side error word of the current
+ * device's library workspace: GEMM_OK, or GEMM_ERR_TIMEOUT if a bounded wait
+ * gave up since the last call.
+ */
+int gemm_sync_status(void *stream);
+
+/* gemm_release -- free the library-owned workspace of every device (synchronises them). */
+void gemm_release(void);
+
+/* gemm_last_error -- text for the calling thread's last failing call ("" if none). */
+const char *gemm_last_error(void);
+
+/* gemm_num_cus -- compute units of the current device (0 if there is none). */
+int32_t gemm_num_cus(void);
+
+/* gemm_version -- ABI version of this header (1). */
+int32_t gemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGW_GEMM_H */

@@ -1,0 +1,203 @@
+"""Host-side tests of the C-ABI library: it loads, exports every entry point that
+include/gemm.h declares, rejects bad arguments before touching a GPU, and its
+planner agrees with the CPU schedule simulator (oracle/schedule.py)."""
+import ctypes
+import itertools
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+from oracle import schedule as sch
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "gemm.h"
+
+
+@pytest.fixture(scope="module")
+def dg():
+    from dense_gemm_work_amd import build as b
+
+    if b.is_stale():
+        b.build()
+    import dense_gemm_work_amd as dg
+
+    return dg
+
+
+def _declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_core_entry_points():
+    names = _declared_functions()
+    for n in ("gemm", "gemm_ex", "gemm_plan", "gemm_unit_range", "gemm_set_stream",
+              "gemm_sync_status", "gemm_release", "gemm_last_error", "gemm_num_cus", "gemm_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(dg):
+    lib = ctypes.CDLL(str(dg.library_path()))
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} declared in gemm.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", str(dg.library_path())],
+                         capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in _declared_functions():
+        assert name in exported
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "gemm.h"\nint main(void){gemm_plan_t p; gemm_args_t a; (void)p; (void)a;'
+                   ' return gemm_version() == 1 ? 0 : 1;}\n')
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-c", f"-I{HEADER.parent}", str(src),
+                        "-o", str(tmp_path / "t.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_version(dg):
+    assert dg.gemm_version() == 1
+
+
+def test_struct_sizes_match_c(dg, tmp_path):
+    src = tmp_path / "s.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "gemm.h"\n'
+                   'int main(void){printf("%zu %zu %zu %zu\\n", sizeof(gemm_plan_t), sizeof(gemm_args_t),'
+                   ' offsetof(gemm_args_t, stream), offsetof(gemm_plan_t, trace_ints)); return 0;}\n')
+    exe = tmp_path / "s"
+    subprocess.run(["gcc", f"-I{HEADER.parent}", str(src), "-o", str(exe)], check=True)
+    got = subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()
+    assert int(got[0]) == ctypes.sizeof(dg.GemmPlan)
+    assert int(got[1]) == ctypes.sizeof(dg.GemmArgs)
+    assert int(got[2]) == dg.GemmArgs.stream.offset
+    assert int(got[3]) == dg.GemmPlan.trace_ints.offset
+
+
+# -- planner vs simulator -------------------------------------------------------------
+def _compare(dg, M, N, K, mode, splits, cus, atomic=False):
+    mw = dg.mode_word(mode, atomic)
+    p = dg.gemm_plan(M, N, K, dg.GEMM_B_KN | dg.GEMM_BF16, mw, splits, cus)
+    s = sch.plan_schedule(M, N, K, mode, splits, sms=cus)
+    assert dg.DECISION_NAMES[p.decision] == s.kind
+    assert (p.tiles_m, p.tiles_n, p.ipt) == (s.tiles_m, s.tiles_n, s.ipt)
+    w = sch.wave_stats(s.tiles, cus)
+    assert (p.total_waves, p.tail) == (w.waves, w.tail)
+    if s.kind == "StreamK":
+        assert (p.sk_units, p.sk_tiles, p.dp_tiles, p.q, p.big) == (s.units, s.sk_tiles, s.dp_tiles, s.q, s.big)
+        bounds = sch.unit_ranges(s.sk_tiles * s.ipt, s.units)
+        for u in {0, s.units // 2, s.units - 1}:
+            assert dg.gemm_unit_range(p, u) == bounds[u]
+        segs = [x for x in s.segments if x.unit < s.units]
+        per_unit = {}
+        for x in segs:
+            per_unit[x.unit] = per_unit.get(x.unit, 0) + 1
+        assert max(per_unit.values(), default=0) <= p.max_segments
+        assert sch.max_units_per_tile(segs) <= p.max_fold
+    elif s.kind == "SplitK":
+        assert p.splits == s.splits
+    return p, s
+
+
+@pytest.mark.parametrize("name,M,N,K,mode,splits,kind", [
+    ("c1", 256, 512, 2048, "streamk", 32, "StreamK"),
+    ("c2a", 96, 512, 2048, "splitk", 8, "SplitK"),
+    ("c2b", 256, 512, 2048, "splitk", 2, "SplitK"),
+    ("c3", 2048, 2176, 4096, "heuristic", 0, "StreamK"),
+    ("c4", 8192, 8192, 8192, "heuristic", 0, "DataParallel"),
+    ("c5", 1536, 1536, 16384, "streamk", 0, "StreamK"),
+])
+def test_workload_plans(dg, name, M, N, K, mode, splits, kind):
+    p, s = _compare(dg, M, N, K, mode, splits, 256)
+    assert s.kind == kind
+    if name == "c3":
+        assert (p.sk_units, p.sk_tiles, p.q) == (256, 272, 68)
+    if name == "c5":
+        assert (p.sk_units, p.q) == (256, 144)
+    if name == "c1":
+        assert p.q == 8
+
+
+def test_heuristic_sweep_matches_simulator(dg):
+    # brute-force sweep: M, N multiples of 32 up to 4096, K up to 4096, several CU counts
+    ms = [32, 96, 128, 160, 640, 1024, 1536, 2048, 2176, 3840, 4096]
+    ks = [64, 256, 512, 576, 2048, 4096]
+    for cus in (4, 108, 132, 148, 256):
+        for M, N, K in itertools.product(ms, ms, ks):
+            p = dg.gemm_plan(M, N, K, dg.GEMM_B_KN | dg.GEMM_BF16, dg.GEMM_HEURISTIC, 0, cus)
+            tm, tn = sch.tile_grid(M, N)
+            d = sch.decide(tm * tn, sch.cdiv(K, 64), cus)
+            assert dg.DECISION_NAMES[p.decision] == d.kind, (M, N, K, cus)
+            if d.kind == "StreamK":
+                assert (p.sk_tiles, p.sk_units) == (d.sk_tiles, d.sk_units)
+            if d.kind == "SplitK":
+                assert p.splits == d.splits
+
+
+def test_printed_table_decisions(dg):
+    # the decisions printed in the book chapter's Case 2 table
+    for (M, N, K, cus, kind, skt, units) in [(1536, 1536, 4096, 132, "StreamK", 144, 132),
+                                            (128, 4096, 4096, 132, "StreamK", 32, 132),
+                                            (3840, 3840, 4096, 148, "StreamK", 160, 148),
+                                            (4096, 4096, 4096, 132, "DataParallel", 0, 0)]:
+        p = dg.gemm_plan(M, N, K, 0, dg.GEMM_HEURISTIC, 0, cus)
+        assert dg.DECISION_NAMES[p.decision] == kind
+        if kind == "StreamK":
+            assert (p.sk_tiles, p.sk_units) == (skt, units)
+
+
+def test_streamk_unit_ranges_cover(dg):
+    for tiles_m, ipt, units in [(1, 3, 7), (2, 5, 3), (5, 9, 64), (3, 1, 2)]:
+        M, K = tiles_m * 128, ipt * 64
+        p = dg.gemm_plan(M, 128, K, 0, dg.GEMM_STREAMK, units, 256)
+        bounds = [dg.gemm_unit_range(p, u) for u in range(units)]
+        assert bounds == sch.unit_ranges(tiles_m * ipt, units)
+
+
+def test_ragged_shapes_plan(dg):
+    p, s = _compare(dg, 300, 200, 200, "streamk", 5, 256)
+    assert (p.tiles_m, p.tiles_n, p.ipt) == (3, 2, 4)
+    _compare(dg, 1000, 1000, 1000, "heuristic", 0, 256)
+    _compare(dg, 130, 136, 72, "splitk", 2, 256)
+
+
+# -- validation before any GPU work -----------------------------------------------------
+def test_plan_rejects_bad_arguments(dg):
+    bad = [
+        dict(M=-1), dict(layout=0x2), dict(layout=0x20), dict(mode=0x7), dict(mode=0x400),
+        dict(mode=dg.GEMM_DP, splits=2), dict(mode=dg.GEMM_SPLITK, splits=0),
+        dict(mode=dg.GEMM_SPLITK, splits=3), dict(mode=dg.GEMM_DP | dg.GEMM_ATOMIC),
+        dict(cus=0),
+    ]
+    for b in bad:
+        args = dict(M=256, N=256, K=2048, layout=0, mode=dg.GEMM_DP, splits=0, cus=256)
+        args.update(b)
+        with pytest.raises(dg.GemmError) as ei:
+            dg.gemm_plan(args["M"], args["N"], args["K"], args["layout"], args["mode"], args["splits"],
+                         args["cus"])
+        assert ei.value.status == dg.GEMM_ERR_INVALID, b
+    for b in [dict(K=100), dict(N=100)]:
+        args = dict(M=256, N=256, K=2048)
+        args.update(b)
+        with pytest.raises(dg.GemmError) as ei:
+            dg.gemm_plan(args["M"], args["N"], args["K"], 0, dg.GEMM_DP, 0, 256)
+        assert ei.value.status == dg.GEMM_ERR_UNSUPPORTED
+    # [N,K] weights only need K % 8 == 0
+    dg.gemm_plan(256, 100, 2048, dg.GEMM_B_NK, dg.GEMM_DP, 0, 256)
+
+
+def test_gemm_rejects_before_launch(dg):
+    # host-detectable errors return before any HIP call (no GPU needed)
+    assert dg.gemm(0, 0, 0, 256, 256, 256, 0, dg.GEMM_DP, 0) == dg.GEMM_ERR_INVALID
+    assert "non-null" in dg.gemm_last_error()
+    assert dg.gemm(16, 32, 48, 256, 256, 256, 0, dg.GEMM_SPLITK, 3) == dg.GEMM_ERR_INVALID
+    assert dg.gemm(8, 32, 1 << 40, 256, 256, 256, 0, dg.GEMM_DP, 0) == dg.GEMM_ERR_UNSUPPORTED
+    # C overlapping A
+    assert dg.gemm(1 << 20, 1 << 30, (1 << 20) + 4096, 256, 256, 256, 0, dg.GEMM_DP, 0) == dg.GEMM_ERR_INVALID
+    # empty problems are a no-op, even with null pointers
+    assert dg.gemm(0, 0, 0, 0, 256, 256, 0, dg.GEMM_DP, 0) == dg.GEMM_OK
+    assert dg.gemm(0, 0, 0, 256, 0, 256, 0, dg.GEMM_DP, 0) == dg.GEMM_OK

@@ -1,0 +1,312 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle and the
+schedule simulator.
+
+Bar (per element): |C_gpu - C_ref| <= 1e-4 * sum_k |a_ik||b_kj|, outputs that
+start poisoned at 7 are all overwritten, and 64 trailing guard elements keep
+their value 11.  Schedules (segments, fold order, coverage) must equal the
+simulator's exactly.  Deterministic modes must be bit-identical across runs
+and unit orders."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import schedule as sch
+from workloads import WORKLOADS, make_operands
+
+from gpu_util import (check_against_oracle, decode_trace, expected_trace, guarded_output,
+                      guards_intact, sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dg():
+    import dense_gemm_work_amd as dg
+
+    assert torch.cuda.is_available(), "GPU test run without a visible GPU"
+    return dg
+
+
+DEV = "cuda:0"
+
+
+def run(dg, w, mode=None, splits=None, atomic=None, A=None, B=None, **kw):
+    mode = w.mode if mode is None else mode
+    splits = w.splits if splits is None else splits
+    atomic = w.atomic if atomic is None else atomic
+    if A is None:
+        A, B = make_operands(w)
+    a, b = A.to(DEV), B.to(DEV)
+    full, c = guarded_output(w.M, w.N, DEV)
+    say(f"  gemm {w.name} {w.M}x{w.N}x{w.K} {w.dtype} {w.b_layout} mode={mode} splits={splits} atomic={atomic}")
+    dg.gemm_tensors(a, b, c, b_layout=w.b_layout, mode=mode, splits=splits, atomic=atomic, **kw)
+    st = dg.gemm_sync_status()
+    assert st == 0, dg.gemm_last_error()
+    assert guards_intact(full, w.M, w.N), "guard band overwritten"
+    return A, B, c
+
+
+def assert_parity(c, A, B, w, rows=None):
+    ok, worst, idx = check_against_oracle(c, A, B, w, rows=rows)
+    say(f"    worst err/bound = {worst:.3e} at {idx}")
+    assert ok, f"outside tolerance: worst ratio {worst} at {idx}"
+
+
+# ---------------------------------------------------------------------------
+# Layout probe: identity A makes C equal B exactly, so any mistake in the
+# MFMA operand/result layout shows up as a permutation.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("b_layout", ["kn", "nk"])
+def test_identity_layout(dg, b_layout):
+    M = N = K = 128
+    A = torch.eye(M, K, dtype=torch.bfloat16)
+    vals = (torch.arange(K * N) % 251 - 125).to(torch.float32).view(K, N)
+    B = vals.to(torch.bfloat16) if b_layout == "kn" else vals.t().contiguous().to(torch.bfloat16)
+    w = WORKLOADS["c1_sk32"].with_(name="identity", M=M, N=N, K=K, b_layout=b_layout)
+    _, _, c = run(dg, w, mode="dp", splits=0, A=A, B=B)
+    assert torch.equal(c.cpu(), vals), "MFMA layout mismatch"
+
+
+# ---------------------------------------------------------------------------
+# The five workloads
+# ---------------------------------------------------------------------------
+def test_c1_streamk_32_units(dg):
+    w = WORKLOADS["c1_sk32"]
+    A, B, c = run(dg, w)
+    assert_parity(c, A, B, w)
+
+
+@pytest.mark.parametrize("name", ["c2a_m96_s8", "c2b_m256_s2"])
+def test_c2_splitk(dg, name):
+    w = WORKLOADS[name]
+    A, B, c = run(dg, w)
+    assert_parity(c, A, B, w)
+    assert torch.all(c[0] == 0), "row 0 of A is zero, so row 0 of C must be exactly zero"
+
+
+def test_c3_heuristic_streamk(dg):
+    w = WORKLOADS["c3_wavequant"]
+    p = dg.gemm_plan(w.M, w.N, w.K, 0, dg.GEMM_HEURISTIC, 0, 256)
+    assert (dg.DECISION_NAMES[p.decision], p.sk_units, p.sk_tiles) == ("StreamK", 256, 272)
+    A, B, c = run(dg, w)
+    assert_parity(c, A, B, w, rows=sample_rows(w.M, 48))
+
+
+def test_c4_heuristic_dp(dg):
+    w = WORKLOADS["c4_large_dp"]
+    p = dg.gemm_plan(w.M, w.N, w.K, 0, dg.GEMM_HEURISTIC, 0, 256)
+    assert dg.DECISION_NAMES[p.decision] == "DataParallel"
+    A, B, c = run(dg, w)
+    assert_parity(c, A, B, w, rows=sample_rows(w.M, 10))
+
+
+@pytest.mark.parametrize("atomic", [False, True])
+def test_c5_streamk_fp16(dg, atomic):
+    w = WORKLOADS["c5_longk_fp16"]
+    A, B, c = run(dg, w, atomic=atomic)
+    assert_parity(c, A, B, w, rows=sample_rows(w.M, 24))
+
+
+# ---------------------------------------------------------------------------
+# Every decomposition and layout on small, ragged shapes (full comparison)
+# ---------------------------------------------------------------------------
+SMALL = [
+    # (M, N, K, layout, dtype)
+    (256, 256, 512, "kn", "bf16"),
+    (300, 200, 320, "kn", "bf16"),     # ragged M and N tails
+    (300, 200, 328, "nk", "bf16"),     # ragged K (not a multiple of 64)
+    (130, 136, 72, "kn", "fp16"),
+    (96, 100, 2048, "nk", "fp16"),     # N not a multiple of 8 ([N,K] layout allows it)
+    (1, 8, 8, "kn", "bf16"),           # a single element row
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s[:3])) + f"-{s[3]}-{s[4]}")
+@pytest.mark.parametrize("mode,splits,atomic", [
+    ("dp", 0, False), ("splitk", 1, False), ("splitk", -1, False), ("streamk", 7, False),
+    ("streamk", 3, True), ("streamk", 0, False), ("heuristic", 0, False),
+])
+def test_small_shapes_all_modes(dg, shape, mode, splits, atomic):
+    M, N, K, layout, dtype = shape
+    ipt = -(-K // 64)
+    if splits == -1:   # largest split factor dividing ipt (at most 8)
+        splits = max(s for s in range(1, 9) if ipt % s == 0)
+    dist = dict(dist="uniform", low=-1.0, high=1.0) if dtype == "bf16" else dict(dist="uniform", low=-0.5, high=0.5)
+    w = WORKLOADS["c1_sk32"].with_(name="small", M=M, N=N, K=K, b_layout=layout, dtype=dtype, **dist)
+    A, B, c = run(dg, w, mode=mode, splits=splits, atomic=atomic)
+    assert_parity(c, A, B, w)
+
+
+def test_k_zero_writes_zeros(dg):
+    full, c = guarded_output(64, 64, DEV)
+    a = torch.empty((64, 0), dtype=torch.bfloat16, device=DEV)
+    b = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    dg.gemm_tensors(a, b, c, mode="dp")
+    torch.cuda.synchronize()
+    assert torch.all(c == 0) and guards_intact(full, 64, 64)
+
+
+def test_units_more_than_iterations(dg):
+    # 2 tiles x 2 iterations over 6 units: two units have nothing to do
+    w = WORKLOADS["c1_sk32"].with_(name="tiny", M=256, N=128, K=128)
+    A, B, c = run(dg, w, mode="streamk", splits=6)
+    assert_parity(c, A, B, w)
+
+
+def test_hybrid_dp_plus_streamk(dg):
+    # with 20 CUs planned, 66 tiles = 3 full waves + 6: two DP waves, Stream-K on the last 26 tiles
+    w = WORKLOADS["c3_wavequant"].with_(name="hybrid", M=1408, N=768, K=1024)
+    p = dg.gemm_plan(w.M, w.N, w.K, 0, dg.GEMM_HEURISTIC, 0, 20)
+    assert dg.DECISION_NAMES[p.decision] == "StreamK" and p.dp_tiles == 40 and p.sk_tiles == 26
+    A, B, c = run(dg, w, mode="heuristic", splits=0, num_cus=20)
+    assert_parity(c, A, B, w)
+
+
+# ---------------------------------------------------------------------------
+# Schedule: the kernels' own trace equals the simulator, bit for bit
+# ---------------------------------------------------------------------------
+TRACE_CASES = [
+    ("c1", 256, 512, 2048, "streamk", 32, 256, False),
+    ("c3", 2048, 2176, 4096, "heuristic", 0, 256, False),
+    ("c5", 1536, 1536, 16384, "streamk", 0, 256, False),
+    ("c5-atomic", 1536, 1536, 16384, "streamk", 0, 256, True),
+    ("c2a", 96, 512, 2048, "splitk", 8, 256, False),
+    ("ragged-7u", 300, 200, 320, "streamk", 7, 256, False),
+    ("hybrid", 1408, 768, 1024, "heuristic", 0, 20, False),
+    ("dp", 640, 384, 256, "dp", 0, 256, False),
+]
+
+
+@pytest.mark.parametrize("case", TRACE_CASES, ids=lambda c: c[0])
+def test_trace_matches_simulator(dg, case):
+    name, M, N, K, mode, splits, cus, atomic = case
+    layout = "nk" if name == "c2a" else "kn"
+    lw = dg.layout_word(layout, "bf16")
+    p = dg.gemm_plan(M, N, K, lw, dg.mode_word(mode, atomic), splits, cus)
+    tr = torch.zeros(p.trace_ints, dtype=torch.int32, device=DEV)
+    w = WORKLOADS["c1_sk32"].with_(name=name, M=M, N=N, K=K, b_layout=layout)
+    A, B = make_operands(w)
+    full, c = guarded_output(M, N, DEV)
+    say(f"  trace {name}")
+    dg.gemm_tensors(A.to(DEV), B.to(DEV), c, b_layout=layout, mode=mode, splits=splits, atomic=atomic,
+                    num_cus=cus, trace=tr)
+    assert dg.gemm_sync_status() == 0
+    got = decode_trace(tr)
+    s, segs, folds = expected_trace(M, N, K, mode, splits, cus)
+    assert got["segments"] == segs
+    assert np.all(got["coverage"] == 1), "every (tile, k) pair must run exactly once"
+    if not atomic:
+        assert got["folds"] == folds
+    else:
+        for t, f in got["folds"].items():
+            assert f == (folds[t] if len(folds[t]) == 1 else [])
+
+
+# ---------------------------------------------------------------------------
+# Determinism
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["c1_sk32", "c5_longk_fp16", "c3_wavequant"])
+def test_deterministic_bit_identical_10_runs(dg, name):
+    w = WORKLOADS[name]
+    A, B = make_operands(w)
+    a, b = A.to(DEV), B.to(DEV)
+    c0 = torch.empty((w.M, w.N), dtype=torch.float32, device=DEV)
+    say(f"  10 runs {name}")
+    dg.gemm_tensors(a, b, c0, b_layout=w.b_layout, mode=w.mode, splits=w.splits)
+    for _ in range(9):
+        c = torch.full((w.M, w.N), 7.0, dtype=torch.float32, device=DEV)
+        dg.gemm_tensors(a, b, c, b_layout=w.b_layout, mode=w.mode, splits=w.splits)
+        assert torch.equal(c.view(torch.int32), c0.view(torch.int32))
+    assert dg.gemm_sync_status() == 0
+
+
+@pytest.mark.parametrize("order", ["reverse", "shuffle"])
+def test_unit_order_does_not_change_bits(dg, order):
+    w = WORKLOADS["c5_longk_fp16"]
+    A, B = make_operands(w)
+    a, b = A.to(DEV), B.to(DEV)
+    ref = torch.empty((w.M, w.N), dtype=torch.float32, device=DEV)
+    dg.gemm_tensors(a, b, ref, mode="streamk", splits=0)
+    units = dg.gemm_plan(w.M, w.N, w.K, dg.GEMM_FP16, dg.GEMM_STREAMK, 0, dg.gemm_num_cus()).sk_units
+    if order == "reverse":
+        perm = torch.arange(units - 1, -1, -1, dtype=torch.int32)
+    else:
+        perm = torch.from_numpy(np.random.default_rng(5).permutation(units).astype(np.int32))
+    c = torch.empty_like(ref)
+    say(f"  perm {order}")
+    dg.gemm_tensors(a, b, c, mode="streamk", splits=0, unit_perm=perm.to(DEV))
+    assert dg.gemm_sync_status() == 0
+    assert torch.equal(c.view(torch.int32), ref.view(torch.int32))
+
+
+def test_streamk_equals_splitk_bits_when_segments_coincide(dg):
+    # 8 tiles x 32 iterations over 32 units = 4 segments of 8 per tile, the same k
+    # ranges as Split-K with S = 4; both fold ((P0 + P1) + P2) + P3 in k order
+    w = WORKLOADS["c1_sk32"]
+    A, B = make_operands(w)
+    a, b = A.to(DEV), B.to(DEV)
+    c_sk = torch.empty((w.M, w.N), dtype=torch.float32, device=DEV)
+    c_s4 = torch.empty_like(c_sk)
+    c_dp = torch.empty_like(c_sk)
+    dg.gemm_tensors(a, b, c_sk, mode="streamk", splits=32)
+    dg.gemm_tensors(a, b, c_s4, mode="splitk", splits=4)
+    dg.gemm_tensors(a, b, c_dp, mode="dp")
+    torch.cuda.synchronize()
+    assert torch.equal(c_sk.view(torch.int32), c_s4.view(torch.int32))
+    # a different addition order is expected to change some bits against DP
+    assert not torch.equal(c_sk.view(torch.int32), c_dp.view(torch.int32))
+
+
+def test_atomic_mode_within_tolerance_over_runs(dg):
+    w = WORKLOADS["c5_longk_fp16"].with_(M=512, N=512)   # 16 tiles, 3 contributors on some
+    A, B = make_operands(w)
+    a, b = A.to(DEV), B.to(DEV)
+    for i in range(3):
+        c = torch.full((w.M, w.N), 7.0, dtype=torch.float32, device=DEV)
+        dg.gemm_tensors(a, b, c, mode="streamk", splits=0, atomic=True)
+        assert_parity(c, A, B, w)
+
+
+# ---------------------------------------------------------------------------
+# Failure path: a wait that can never be satisfied ends at its spin limit
+# ---------------------------------------------------------------------------
+def test_bounded_wait_reports_timeout(dg):
+    w = WORKLOADS["c1_sk32"].with_(name="timeout", M=256, N=256, K=512)
+    A, B = make_operands(w)
+    a, b = A.to(DEV), B.to(DEV)
+    c = torch.empty((w.M, w.N), dtype=torch.float32, device=DEV)
+    say("  forced timeout (contributors never raise flags, spin limit 2000 polls)")
+    dg.gemm_tensors(a, b, c, mode="streamk", splits=12, spin_limit=2000, debug=dg.GEMM_DEBUG_NO_PUBLISH)
+    assert dg.gemm_sync_status() == dg.GEMM_ERR_TIMEOUT
+    # the status is cleared and the next call is healthy
+    full, c2 = guarded_output(w.M, w.N, DEV)
+    dg.gemm_tensors(a, b, c2, mode="streamk", splits=12)
+    assert dg.gemm_sync_status() == 0
+    assert_parity(c2, A, B, w)
+
+
+def test_capacity_refusal(dg):
+    w = WORKLOADS["c1_sk32"]
+    a = torch.zeros((w.M, w.K), dtype=torch.bfloat16, device=DEV)
+    b = torch.zeros((w.K, w.N), dtype=torch.bfloat16, device=DEV)
+    c = torch.full((w.M, w.N), 7.0, dtype=torch.float32, device=DEV)
+    with pytest.raises(dg.GemmError) as ei:
+        dg.gemm_tensors(a, b, c, mode="streamk", splits=100000)
+    assert ei.value.status == dg.GEMM_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(c == 7.0), "a refused call must not touch C"
+
+
+def test_caller_workspace(dg):
+    w = WORKLOADS["c1_sk32"]
+    p = dg.gemm_plan(w.M, w.N, w.K, 0, dg.GEMM_STREAMK, 32, dg.gemm_num_cus())
+    ws = torch.zeros(p.workspace_bytes // 4 + 64, dtype=torch.int32, device=DEV)
+    A, B = make_operands(w)
+    full, c = guarded_output(w.M, w.N, DEV)
+    dg.gemm_tensors(A.to(DEV), B.to(DEV), c, mode="streamk", splits=32, workspace=ws)
+    assert dg.gemm_sync_status() == 0
+    assert_parity(c, A, B, w)
+    small = torch.zeros(16, dtype=torch.int32, device=DEV)
+    with pytest.raises(dg.GemmError) as ei:
+        dg.gemm_tensors(A.to(DEV), B.to(DEV), c, mode="streamk", splits=32, workspace=small)
+    assert ei.value.status == dg.GEMM_ERR_WORKSPACE
