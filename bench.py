@@ -46,6 +46,13 @@ def parse():
     ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape arms")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--shape-steps", type=int, default=50)
+    ap.add_argument("--mode", default=None, choices=["heuristic", "dp", "splitk", "streamk"],
+                    help="override the workload's decomposition (for profiling one arm)")
+    ap.add_argument("--splits", type=int, default=None, help="Split-K factor or Stream-K units")
+    ap.add_argument("--atomic", action="store_true", help="Stream-K atomic fixup")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a known-size "
+                         "reference dispatch for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -146,6 +153,13 @@ def shape_arms(dg, name, steps, warmup):
     return out
 
 
+def kernel_name(dg, plan, w):
+    kind = {dg.GEMM_DP: "gemm_dp", dg.GEMM_SPLITK: "gemm_splitk", dg.GEMM_STREAMK: "gemm_streamk"}[plan.decision]
+    lay = "B[K,N]" if w.b_layout == "kn" else "B[N,K]"
+    fix = (", atomic" if plan.atomic else ", deterministic") if plan.decision == dg.GEMM_STREAMK else ""
+    return f"{kind}<{w.dtype}, {lay}{fix}>"
+
+
 def cpu_baseline(w, A, B):
     from oracle import gemm as og
 
@@ -177,6 +191,9 @@ def main():
     from workloads import WORKLOADS, make_operands
 
     w = WORKLOADS[args.workload]
+    if args.mode is not None:
+        w = w.with_(mode=args.mode, splits=args.splits if args.splits is not None else 0,
+                    atomic=args.atomic)
     A, B = make_operands(w)
     a, b = A.cuda(), B.cuda()
     c = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
@@ -197,6 +214,16 @@ def main():
         f"({achieved:.1f} TFLOP/s, {100 * achieved / PEAK_BF16_TFLOPS:.1f}% of peak)")
 
     # ---- arms on the same shape and the other shapes -------------------------------
+    if args.copy_probe_mb > 0:
+        n = args.copy_probe_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copy probe {args.copy_probe_mb} MiB read + {args.copy_probe_mb} MiB written")
+        del src, dst
+
     shapes = {}
     if not args.no_shapes:
         for name in ("c3_wavequant", "c1_sk32", "c2a_m96_s8", "c2b_m256_s2", "c5_longk_fp16", "c4_large_dp"):
@@ -237,7 +264,7 @@ def main():
         "speedups": speedups,
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_streamk<bf16, B[K,N], deterministic>",
+            "kernel": kernel_name(dg, call.plan, w),
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

@@ -90,6 +90,7 @@ class GemmArgs(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t), ("unit_perm", ctypes.c_void_p),
         ("trace", ctypes.c_void_p), ("trace_ints", ctypes.c_int64),
         ("spin_limit", ctypes.c_uint32), ("debug", ctypes.c_uint32),
+        ("timing", ctypes.c_void_p),
     ]
 
 
@@ -200,11 +201,13 @@ def mode_word(mode: str, atomic: bool = False) -> int:
 
 def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits: int = 0,
                  atomic: bool = False, num_cus: int = 0, unit_perm=None, trace=None,
-                 workspace=None, spin_limit: int = 0, debug: int = 0, stream=None) -> None:
+                 workspace=None, spin_limit: int = 0, debug: int = 0, timing=None,
+                 stream=None) -> None:
     """``c[M,N] = a[M,K] . b`` (b [K,N]) or ``a . b^T`` (b [N,K]) on torch tensors.
 
     a, b: contiguous bf16/fp16 tensors on one HIP device; c: contiguous fp32 [M,N].
-    unit_perm / trace / workspace: optional int32 / int32 / any-dtype device tensors.
+    unit_perm / trace / workspace / timing: optional int32 / int32 / any-dtype / int64
+    device tensors (see gemm_args_t in include/gemm.h).
     Enqueues on ``stream`` (a torch.cuda.Stream) or torch's current stream.
     """
     import torch
@@ -258,6 +261,10 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
         if workspace is not None:
             args.workspace = workspace.data_ptr()
             args.workspace_bytes = workspace.numel() * workspace.element_size()
+        if timing is not None:
+            if timing.dtype != torch.int64 or not timing.is_cuda or not timing.is_contiguous():
+                raise TypeError("timing must be a contiguous int64 device tensor")
+            args.timing = timing.data_ptr()
         args.spin_limit = spin_limit
         args.debug = debug
         _check(gemm_ex(args))

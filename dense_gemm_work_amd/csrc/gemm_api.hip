@@ -16,6 +16,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -34,6 +35,21 @@ thread_local hipStream_t g_stream = nullptr;
 
 constexpr uint32_t kDefaultSpin = 1u << 22;
 constexpr int64_t kStatusWords = 64;
+constexpr int kGroupM = 8;   // tile rows per raster group (DGW_GROUP_M overrides)
+
+// Tuning overrides from the environment, read once.
+struct Tuning {
+    int group_m = kGroupM;
+    int xcd_spread = 1;
+    Tuning() {
+        if (const char *v = std::getenv("DGW_GROUP_M")) group_m = std::max(0, std::atoi(v));
+        if (const char *v = std::getenv("DGW_XCD_SPREAD")) xcd_spread = std::atoi(v) ? 1 : 0;
+    }
+};
+const Tuning &tuning() {
+    static const Tuning t;
+    return t;
+}
 
 int fail(int code, const std::string &msg) {
     g_err = msg;
@@ -233,7 +249,11 @@ int run(const gemm_args_t &a) {
     kp.M = (int)a.M;
     kp.N = (int)a.N;
     kp.K = (int)a.K;
+    kp.tiles_m = (int)p.tiles_m;
     kp.tiles_n = (int)p.tiles_n;
+    kp.group_m = tuning().group_m;
+    kp.xcd_spread = a.unit_perm ? 0 : tuning().xcd_spread;
+    kp.timing = reinterpret_cast<long long *>(a.timing);
     kp.ipt = (int)p.ipt;
     kp.splits = p.splits;
     kp.part = part;
@@ -287,6 +307,7 @@ int run(const gemm_args_t &a) {
             dp.tile_base = 0;
             dp.ntiles = (int)p.dp_tiles;
             dp.worker_base = (int)p.sk_units;
+            dp.timing_base = (int)p.sk_units;
             dp.perm = nullptr;
             if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_DP, (int)p.dp_tiles, dp, stream)) != hipSuccess)
                 return fail_hip(e, "launch DP kernel (hybrid part)");

@@ -49,11 +49,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = GEMM_BK;
 constexpr int NT = 256;                       // threads per workgroup
 constexpr int SLAB = BM * BK;                 // 16-bit values per operand slab (A and B alike)
-constexpr int STAGE = 2 * SLAB;               // A slab then B slab
+constexpr int STAGE_BYTES = 2 * SLAB * 2;     // A slab then B slab: 32 KiB
+// LDS stages per workgroup: the persistent Stream-K kernel (one workgroup per
+// CU) keeps 4 stages (128 KiB of the CU's 160 KiB) in flight; the DP and
+// Split-K kernels keep 2 (64 KiB) so that two workgroups share a CU.
+constexpr int NS_STREAMK = 4;
+constexpr int NS_GRID = 2;
 static_assert(BM == BN, "the LDS addressing below assumes square tiles");
 
 struct Acc {
@@ -61,12 +67,6 @@ struct Acc {
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-
-__device__ __forceinline__ u32x4 load16(const uint16_t *p, bool ok) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (ok) v = *reinterpret_cast<const u32x4 *>(p);
-    return v;
-}
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
@@ -79,141 +79,290 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 // ---------------------------------------------------------------------------
-// Global -> register staging of one k-iteration
+// Operand staging: buffer loads straight into LDS (no register round trip)
 // ---------------------------------------------------------------------------
-// k-contiguous operand (A [M,K], or B [N,K]): thread t moves the 16-byte chunk
-// (t & 7) of rows (t >> 3) + 32 i, i = 0..3.
-struct RowStage {
-    u32x4 r[4];
+// Each buffer_load ... lds instruction moves 16 bytes per lane into LDS at
+// (wave-uniform base) + 16 * lane, i.e. 1 KiB of contiguous LDS per wave; the
+// swizzle is therefore applied by choosing which global 16-byte chunk each lane
+// fetches.  Loads whose address falls outside the buffer's range return zero,
+// which masks ragged M/N edges; a ragged K tail is masked by pointing the lane
+// at an offset beyond the range.
+constexpr uint32_t OOB = 0x7ffffff0u;        // an offset outside every buffer range used here
+constexpr uint32_t RSRC_DW3 = 0x00020000u;    // raw buffer, 32-bit data format
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Buffer resource (wave-uniform, in SGPRs): base address, byte range, format word.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = (int)RSRC_DW3;
+    return r;
+}
+
+// 16-byte buffer load of every lane straight into LDS at lds + 16 * lane.  Issued
+// as inline assembly so that the compiler does not wait for it before unrelated
+// LDS reads; completion is awaited explicitly with wait_stage().
+__device__ __forceinline__ void dma16(i32x4 rsrc, const void *lds, uint32_t voff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)reinterpret_cast<uintptr_t>((const lds_void *)lds));
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+
+// B [K,N] rows in LDS are 256 bytes (128 n-values); 16-byte chunk c of k-row r
+// lives at chunk c ^ kn_swz(r).  The four k-rows read together by a 16-lane
+// transpose read then fall on distinct banks.
+__device__ __forceinline__ int kn_swz(int r) { return ((r & 1) << 2) ^ ((r & 2) * 5); }
+
+// Wait until at most `n` vector-memory operations of this wave are outstanding
+// and all of its LDS reads have returned, then synchronise the workgroup.
+__device__ __forceinline__ void wait_stage(int n) {
+    // s_waitcnt on gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+#define DGW_WAIT(x) (((x) & 15) | (((x) >> 4) << 14) | (7 << 4) | (0 << 8))
+    switch (n) {
+    case 8: __builtin_amdgcn_s_waitcnt(DGW_WAIT(8)); break;
+    case 16: __builtin_amdgcn_s_waitcnt(DGW_WAIT(16)); break;
+    case 24: __builtin_amdgcn_s_waitcnt(DGW_WAIT(24)); break;
+    default: __builtin_amdgcn_s_waitcnt(DGW_WAIT(0)); break;
+    }
+#undef DGW_WAIT
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// Per-thread load plan of one tile: 4 A instructions and 4 B instructions per
+// wave and k-iteration (16 KiB each per workgroup).
+template <int BL>
+struct LoadPlan {
+    const char *a_base;      // A + m0 * K (bytes)
+    const char *b_base;      // B + n0 * K ([N,K]) or B + n0 ([K,N]) (bytes)
+    uint32_t a_rows_bytes;   // valid A rows * K * 2
+    uint32_t b_rows_bytes;   // [N,K]: valid B rows * K * 2
+    uint32_t a_off[4];       // byte offsets at k-iteration 0
+    uint32_t b_off[4];
+    int a_kc[4];             // first k of the lane's chunk (ragged-K mask)
+    int b_kc[4];             // [N,K]: first k of the chunk; [K,N]: the k-row
+    bool b_nok[4];           // [K,N]: chunk beyond N
 };
 
-__device__ __forceinline__ void fetch_rows(RowStage &s, const uint16_t *X, int rows, int ld,
-                                           int r0, int kb) {
-    const int t = threadIdx.x;
-    const int ch = t & 7;
-    const int kc = kb + ch * 8;
+template <int BL>
+__device__ __forceinline__ void make_load_plan(LoadPlan<BL> &lp, const KParams &p, int m0, int n0) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int K = p.K, N = p.N;
+    lp.a_base = reinterpret_cast<const char *>(p.A) + (size_t)m0 * K * 2;
+    lp.a_rows_bytes = (uint32_t)(min(BM, p.M - m0) * K * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int row = r0 + (t >> 3) + 32 * i;
-        const bool ok = row < rows && kc < ld;
-        s.r[i] = load16(X + (size_t)row * ld + kc, ok);
+        const int r = (wave * 4 + i) * 8 + (lane >> 3);          // row of the 128 x 64 slab
+        const int c = (lane & 7) ^ swz(r);                       // logical 8-value chunk
+        lp.a_off[i] = (uint32_t)(r * K + c * 8) * 2;
+        lp.a_kc[i] = c * 8;
     }
-}
-
-__device__ __forceinline__ void put_rows(const RowStage &s, uint16_t *slab) {
-    const int t = threadIdx.x;
-    const int ch = t & 7;
+    if constexpr (BL == 1) {
+        lp.b_base = reinterpret_cast<const char *>(p.B) + (size_t)n0 * K * 2;
+        lp.b_rows_bytes = (uint32_t)(min(BN, N - n0) * K * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = (t >> 3) + 32 * i;
-        *reinterpret_cast<u32x4 *>(slab + row * BK + ((ch ^ swz(row)) << 3)) = s.r[i];
-    }
-}
-
-// n-contiguous B [K,N]: thread t loads k-rows 4g..4g+3 (g = 2 (t>>5) + (t&1)) of
-// the eight n-values of chunk c = (t>>1) & 15, and writes them transposed.
-struct ColStage {
-    u32x4 r[4];
-};
-
-__device__ __forceinline__ void fetch_cols(ColStage &s, const uint16_t *B, int K, int N, int n0,
-                                           int kb) {
-    const int t = threadIdx.x;
-    const int g = ((t >> 5) << 1) | (t & 1);
-    const int c = (t >> 1) & 15;
-    const int n = n0 + c * 8;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int k = kb + 4 * g + r;
-        s.r[r] = load16(B + (size_t)k * N + n, k < K && n < N);
-    }
-}
-
-__device__ __forceinline__ void put_cols(const ColStage &s, uint16_t *slab) {
-    const int t = threadIdx.x;
-    const int gh = t >> 5;          // 8-value k chunk within the row
-    const int h = t & 1;            // which 4-value half of that chunk
-    const int c = (t >> 1) & 15;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int d = j >> 1;
-        uint32_t lo, hi;
-        if (j & 1) {
-            lo = (s.r[0][d] >> 16) | (s.r[1][d] & 0xffff0000u);
-            hi = (s.r[2][d] >> 16) | (s.r[3][d] & 0xffff0000u);
-        } else {
-            lo = (s.r[0][d] & 0xffffu) | (s.r[1][d] << 16);
-            hi = (s.r[2][d] & 0xffffu) | (s.r[3][d] << 16);
+        for (int i = 0; i < 4; ++i) {
+            const int r = (wave * 4 + i) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ swz(r);
+            lp.b_off[i] = (uint32_t)(r * K + c * 8) * 2;
+            lp.b_kc[i] = c * 8;
+            lp.b_nok[i] = false;
         }
-        const int n = c * 8 + j;
-        u32x2 v = {lo, hi};
-        *reinterpret_cast<u32x2 *>(slab + n * BK + ((gh ^ swz(n)) << 3) + h * 4) = v;
+    } else {
+        lp.b_base = reinterpret_cast<const char *>(p.B) + (size_t)n0 * 2;
+        lp.b_rows_bytes = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = (wave * 4 + i) * 4 + (lane >> 4);          // k-row of the 64 x 128 slab
+            const int c = (lane & 15) ^ kn_swz(r);                   // logical 8-value n chunk
+            lp.b_off[i] = (uint32_t)(r * N + c * 8) * 2;
+            lp.b_kc[i] = r;
+            lp.b_nok[i] = n0 + c * 8 >= N;
+        }
+    }
+}
+
+// Issue the 8 loads of k-iteration `it` into `stage` (A slab then B slab).
+template <int BL>
+__device__ __forceinline__ void issue_loads(const LoadPlan<BL> &lp, const KParams &p, char *stage, int it) {
+    const int wave = threadIdx.x >> 6;
+    const int kb = it * BK;
+    // A: base advances along K; rows beyond M fall outside [0, a_rows_bytes - 2 kb)
+    const i32x4 ra = make_rsrc(lp.a_base + (size_t)kb * 2, lp.a_rows_bytes - kb * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (kb + lp.a_kc[i] < p.K) ? lp.a_off[i] : OOB;
+        dma16(ra, stage + (wave * 4 + i) * 1024, off);
+    }
+    if constexpr (BL == 1) {
+        const i32x4 rb = make_rsrc(lp.b_base + (size_t)kb * 2, lp.b_rows_bytes - kb * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t off = (kb + lp.b_kc[i] < p.K) ? lp.b_off[i] : OOB;
+            dma16(rb, stage + SLAB * 2 + (wave * 4 + i) * 1024, off);
+        }
+    } else {
+        const int krows = min(BK, p.K - kb);
+        const i32x4 rb =
+            make_rsrc(lp.b_base + (size_t)kb * p.N * 2, (uint32_t)(krows * p.N * 2));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t off = (lp.b_kc[i] < krows && !lp.b_nok[i]) ? lp.b_off[i] : OOB;
+            dma16(rb, stage + SLAB * 2 + (wave * 4 + i) * 1024, off);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core work on one staged slab pair
+// Matrix-core work on one staged slab pair: per 16-wide k-step (kk) every wave
+// reads its two A and two B operand fragments and issues four MFMAs.
 // ---------------------------------------------------------------------------
-template <int DT>
-__device__ __forceinline__ void mma_stage(const uint16_t *stage, Acc &acc) {
+struct Frag {
+    u32x4 a[2];   // rows wm*64 + {0, 32} + lane % 32, k = 16 kk + 8 (lane / 32) + 0..7
+    u32x4 b[2];   // cols wn*64 + {0, 32} + lane % 32, same k
+};
+
+template <int BL>
+__device__ __forceinline__ void load_frag(const char *stage, int kk, Frag &f) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const uint16_t *As = stage;
-    const uint16_t *Bs = stage + SLAB;
-    const int ra0 = wm * 64 + (lane & 31), ra1 = ra0 + 32;
-    const int rb0 = wn * 64 + (lane & 31), rb1 = rb0 + 32;
+    const char *As = stage;
+    const char *Bs = stage + SLAB * 2;
     const int hk = lane >> 5;
+    const int ch = kk * 2 + hk;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-        const int ch = kk * 2 + hk;
-        const u32x4 a0 = *reinterpret_cast<const u32x4 *>(As + ra0 * BK + ((ch ^ swz(ra0)) << 3));
-        const u32x4 a1 = *reinterpret_cast<const u32x4 *>(As + ra1 * BK + ((ch ^ swz(ra1)) << 3));
-        const u32x4 b0 = *reinterpret_cast<const u32x4 *>(Bs + rb0 * BK + ((ch ^ swz(rb0)) << 3));
-        const u32x4 b1 = *reinterpret_cast<const u32x4 *>(Bs + rb1 * BK + ((ch ^ swz(rb1)) << 3));
-        acc.v[0][0] = mfma<DT>(a0, b0, acc.v[0][0]);
-        acc.v[0][1] = mfma<DT>(a0, b1, acc.v[0][1]);
-        acc.v[1][0] = mfma<DT>(a1, b0, acc.v[1][0]);
-        acc.v[1][1] = mfma<DT>(a1, b1, acc.v[1][1]);
+    for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + (lane & 31);
+        f.a[i] = *reinterpret_cast<const u32x4 *>(As + r * 128 + ((ch ^ swz(r)) << 4));
+    }
+    if constexpr (BL == 1) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = wn * 64 + j * 32 + (lane & 31);
+            f.b[j] = *reinterpret_cast<const u32x4 *>(Bs + r * 128 + ((ch ^ swz(r)) << 4));
+        }
+    } else {
+        // transpose reads: lane l of a 16-lane group names 4 n-values of one k-row;
+        // it receives 4 k-values of column n = l % 32 (two reads give 8 k)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = wn * 64 + j * 32 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+            u32x2 h[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int r = kk * 16 + 8 * hk + 4 * half + ((lane & 15) >> 2);
+                const char *addr = Bs + r * 256 + ((((n >> 3) ^ kn_swz(r)) << 4) | ((n & 7) << 1));
+                const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)addr);
+                h[half] = __builtin_bit_cast(u32x2, t);
+            }
+            f.b[j] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+        }
     }
 }
 
-// acc += A[m0:m0+128, k0*64:k1*64] . B[k0*64:k1*64, n0:n0+128], k-iterations k0..k1-1.
-// Ends with a barrier, so the LDS is free again on return.
-template <int DT, int BL>
-__device__ __forceinline__ void mac_loop(const KParams &p, uint16_t *lds, int m0, int n0, int k0,
-                                         int k1, Acc &acc, int *cov) {
-    RowStage sa;
-    RowStage sb_rows;
-    ColStage sb_cols;
-    auto fetch = [&](int it) {
-        const int kb = it * BK;
-        fetch_rows(sa, p.A, p.M, p.K, m0, kb);
-        if constexpr (BL == 1)
-            fetch_rows(sb_rows, p.B, p.N, p.K, n0, kb);
-        else
-            fetch_cols(sb_cols, p.B, p.K, p.N, n0, kb);
-    };
-    auto put = [&](uint16_t *stage) {
-        put_rows(sa, stage);
-        if constexpr (BL == 1)
-            put_rows(sb_rows, stage + SLAB);
-        else
-            put_cols(sb_cols, stage + SLAB);
-    };
-    fetch(k0);
-    put(lds);
-    __syncthreads();
-    for (int it = k0; it < k1; ++it) {
-        uint16_t *cur = lds + ((it - k0) & 1) * STAGE;
-        uint16_t *nxt = lds + (((it - k0) & 1) ^ 1) * STAGE;
-        const bool more = it + 1 < k1;
-        if (more) fetch(it + 1);
-        mma_stage<DT>(cur, acc);
-        if (cov && threadIdx.x == 0) atomicAdd(cov + it, 1);
-        if (more) put(nxt);
-        __syncthreads();
+template <int DT>
+__device__ __forceinline__ void mma(const Frag &f, Acc &acc) {
+    acc.v[0][0] = mfma<DT>(f.a[0], f.b[0], acc.v[0][0]);
+    acc.v[0][1] = mfma<DT>(f.a[0], f.b[1], acc.v[0][1]);
+    acc.v[1][0] = mfma<DT>(f.a[1], f.b[0], acc.v[1][0]);
+    acc.v[1][1] = mfma<DT>(f.a[1], f.b[1], acc.v[1][1]);
+}
+
+// acc += A[m0:m0+128, K-slabs] . B[K-slabs, n0:n0+128] over the tile's logical
+// k-iterations k0..k1-1, logical iteration k reading physical 64-wide K-slab
+// (k + rot) mod ipt (rot = 0 walks K in order; a rotation lets the units that
+// share a tile's panels walk them in phase -- the set of slabs a segment covers
+// is what the schedule defines, the order inside a segment is free).
+// NS LDS stages: the loads of iteration i + NS are issued as soon as stage i has
+// been read.  Fragment reads run one k-step ahead of the MFMAs, also across the
+// stage barrier, so the matrix cores do not drain at every iteration.  Ends
+// with a barrier, so the LDS is free again on return.
+template <int DT, int BL, int NS>
+__device__ __forceinline__ void mac_loop(const KParams &p, char *lds, int m0, int n0, int k0, int k1,
+                                         int rot, Acc &acc, int *cov) {
+    const int n = k1 - k0;
+    if (n <= 0) return;
+    LoadPlan<BL> lp;
+    make_load_plan<BL>(lp, p, m0, n0);
+    int phys = k0 + rot;                 // physical slab of the next iteration to load
+    if (phys >= p.ipt) phys -= p.ipt;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        if (s < n) {
+            issue_loads<BL>(lp, p, lds + s * STAGE_BYTES, phys);
+            if (++phys == p.ipt) phys = 0;
+        }
+    wait_stage(8 * (min(NS, n) - 1));                       // stage 0 complete for every wave
+    Frag f0, f1;
+    load_frag<BL>(lds, 0, f0);
+    for (int i = 0; i < n; ++i) {
+        char *st = lds + (i % NS) * STAGE_BYTES;
+        load_frag<BL>(st, 1, f1);
+        mma<DT>(f0, acc);
+        load_frag<BL>(st, 2, f0);
+        mma<DT>(f1, acc);
+        load_frag<BL>(st, 3, f1);
+        mma<DT>(f0, acc);
+        if (i + 1 < n) {
+            wait_stage(8 * min(NS - 2, n - 2 - i));        // stage i+1 complete; stage i fully read
+            if (i + NS < n) {
+                issue_loads<BL>(lp, p, st, phys);
+                if (++phys == p.ipt) phys = 0;
+            }
+            load_frag<BL>(lds + ((i + 1) % NS) * STAGE_BYTES, 0, f0);
+        }
+        mma<DT>(f1, acc);
+        if (cov && threadIdx.x == 0) atomicAdd(cov + k0 + i, 1);
     }
+    wait_stage(0);
+}
+
+// ---------------------------------------------------------------------------
+// Work placement.  Workgroup b runs on XCD b % 8; `spread` gives every XCD a
+// contiguous range of workers so that neighbouring tiles share an L2.  Tiles
+// are numbered in groups of `group_m` tile rows, column by column inside a
+// group, so a contiguous range of tile ids is a compact 2-D block.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int spread(int b, int n) {
+    const int x = b & 7, j = b >> 3;
+    int base = 0;
+    for (int xx = 0; xx < x; ++xx) base += (n - xx + 7) >> 3;
+    return base + j;
+}
+
+// First flattened iteration of Stream-K unit u (the first `big` units own q + 1).
+__device__ __forceinline__ int unit_start(int u, int q, int big) { return u * q + min(u, big); }
+
+// The unit whose range contains flattened iteration g (q >= 1, or g < big).
+__device__ __forceinline__ int unit_of(int g, int q, int big) {
+    const int long_part = big * (q + 1);
+    return g < long_part ? g / (q + 1) : big + (g - long_part) / max(q, 1);
+}
+
+__device__ __forceinline__ int worker_of(const KParams &p, int n) {
+    const int b = (int)blockIdx.x;
+    if (p.perm) return p.perm[b];
+    return p.xcd_spread ? spread(b, n) : b;
+}
+
+__device__ __forceinline__ void tile_origin(const KParams &p, int tile, int &m0, int &n0) {
+    const int gm_full = p.group_m > 0 ? p.group_m : p.tiles_m;
+    const int per_group = gm_full * p.tiles_n;
+    const int g = tile / per_group;
+    const int first = g * gm_full;
+    const int gm = min(gm_full, p.tiles_m - first);
+    const int w = tile - g * per_group;
+    m0 = (first + w % gm) * BM;
+    n0 = (w / gm) * BN;
 }
 
 // ---------------------------------------------------------------------------
@@ -248,8 +397,86 @@ __device__ __forceinline__ void for_each_element(int m0, int n0, int M, int N, F
         }
 }
 
-__device__ __forceinline__ void store_c(float *C, int m0, int n0, int M, int N, const Acc &acc) {
-    for_each_element(m0, n0, M, N, [&](int i, int j, int e, size_t off) { C[off] = acc.v[i][j][e]; });
+// Row-major staging of the fp32 tile in LDS (64 KiB), then coalesced float4
+// traffic: thread t owns quads t + 256 q (q = 0..15), quad f covering columns
+// 4 (f % 32) .. +3 of tile row f / 32.  Column c of row r is stored at
+// c ^ epi_swz(r): the two rows written by one MFMA result register (4 apart)
+// then fall on different banks, and every aligned quad stays contiguous.
+constexpr int EPI_LD = BN;
+__device__ __forceinline__ int epi_swz(int r) { return ((r >> 2) & 1) << 5; }
+
+__device__ __forceinline__ void acc_to_lds(float *tile, const Acc &acc) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                tile[row * EPI_LD + (col ^ epi_swz(row))] = acc.v[i][j][e];
+            }
+        }
+}
+
+// Calls f(q, row, col, global offset, valid columns in the quad (0..4)) for the
+// thread's 16 quads; rows beyond M and quads wholly beyond N are skipped.
+template <class F>
+__device__ __forceinline__ void for_each_quad(int m0, int n0, int M, int N, F &&f) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int fq = threadIdx.x + NT * q;
+        const int r = fq >> 5, c = (fq & 31) * 4;
+        const int row = m0 + r, col = n0 + c;
+        if (row < M && col < N) f(q, r, c, (size_t)row * N + col, min(4, N - col));
+    }
+}
+
+__device__ __forceinline__ void put_quad(float *dst, f32x4 v, int nvalid, bool vec) {
+    if (vec && nvalid == 4) {
+        *reinterpret_cast<f32x4 *>(dst) = v;
+    } else {
+        for (int x = 0; x < nvalid; ++x) dst[x] = v[x];
+    }
+}
+
+__device__ __forceinline__ f32x4 get_quad(const float *src, int nvalid, bool vec) {
+    if (vec && nvalid == 4) return *reinterpret_cast<const f32x4 *>(src);
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < nvalid; ++x) v[x] = src[x];
+    return v;
+}
+
+// Calls f(q, row, col, global offset) for the thread's 64 elements of the staged
+// tile: column threadIdx % 128, rows threadIdx / 128 + 2 q (q = 0..63), so each
+// wave touches 64 consecutive floats of one row per call.
+template <class F>
+__device__ __forceinline__ void for_each_float(int m0, int n0, int M, int N, F &&f) {
+    const int c = threadIdx.x & 127, r0 = threadIdx.x >> 7;
+    const int col = n0 + c;
+    if (col >= N) return;
+#pragma unroll
+    for (int q = 0; q < 64; ++q) {
+        const int r = r0 + 2 * q, row = m0 + r;
+        if (row < M) f(q, r, c, (size_t)row * N + col);
+    }
+}
+
+// Write the accumulator tile to X[M,N] (C or a Split-K partial).  `lds` must be
+// free; it is free again on return.
+__device__ __forceinline__ void store_tile(float *X, int m0, int n0, int M, int N, const Acc &acc,
+                                           char *lds) {
+    float *tile = reinterpret_cast<float *>(lds);
+    acc_to_lds(tile, acc);
+    __syncthreads();
+    const bool vec = (N & 3) == 0;
+    for_each_quad(m0, n0, M, N, [&](int, int r, int c, size_t off, int nv) {
+        put_quad(X + off, *reinterpret_cast<const f32x4 *>(tile + r * EPI_LD + (c ^ epi_swz(r))), nv, vec);
+    });
+    __syncthreads();
 }
 
 __device__ __forceinline__ void atomic_add_c(float *C, int m0, int n0, int M, int N, const Acc &acc) {
@@ -257,37 +484,66 @@ __device__ __forceinline__ void atomic_add_c(float *C, int m0, int n0, int M, in
                      [&](int i, int j, int e, size_t off) { unsafeAtomicAdd(C + off, acc.v[i][j][e]); });
 }
 
-// Stream-K partial slot: register-native order, one float4 per lane per store,
-// so every store/load instruction moves 1 KiB of contiguous memory.
+// Partial exchange between workgroups.  Partials are written and read with
+// device-scope (sc1) 128-bit buffer accesses, which the gfx950 memory hierarchy
+// keeps coherent across the XCDs' separate L2 caches without writing back or
+// invalidating whole caches; the writer waits for its stores to complete before
+// the flag or counter is raised, and the reader only loads after observing it.
+constexpr int CPOL_DEVICE = 16;   // cache-policy bits: sc1 (device scope)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)RSRC_DW3);
+}
+__device__ __forceinline__ void put4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, CPOL_DEVICE);
+}
+__device__ __forceinline__ f32x4 get4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CPOL_DEVICE));
+}
+__device__ __forceinline__ void put_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_coherent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every vector-memory operation of this wave has completed.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
+
+// Stream-K partial slot (64 KiB) in register-native order: for accumulator block
+// b and element quad e4, the 64 lanes of a wave move 1 KiB of contiguous memory.
+__device__ __forceinline__ uint32_t slot_off(int wave, int b, int e4, int lane) {
+    return (uint32_t)((((wave * 4 + b) * 4 + e4) * 64 + lane) * 16);
+}
+
 __device__ __forceinline__ void put_slot(float *slot, const Acc &acc) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    f32x4 *s = reinterpret_cast<f32x4 *>(slot);
+    const __amdgpu_buffer_rsrc_t r = span(slot, BM * BN * 4);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
             const f32x16 &v = acc.v[b >> 1][b & 1];
-            f32x4 x = {v[4 * e4], v[4 * e4 + 1], v[4 * e4 + 2], v[4 * e4 + 3]};
-            s[((wave * 4 + b) * 4 + e4) * 64 + lane] = x;
+            put4_coherent(r, slot_off(wave, b, e4, lane),
+                          f32x4{v[4 * e4], v[4 * e4 + 1], v[4 * e4 + 2], v[4 * e4 + 3]});
         }
 }
 
 __device__ __forceinline__ void add_slot(const float *slot, Acc &acc) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const f32x4 *s = reinterpret_cast<const f32x4 *>(slot);
+    const __amdgpu_buffer_rsrc_t r = span(slot, BM * BN * 4);
+    f32x4 x[4][4];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            const f32x4 x = s[((wave * 4 + b) * 4 + e4) * 64 + lane];
-            f32x16 &v = acc.v[b >> 1][b & 1];
-            v[4 * e4] += x[0];
-            v[4 * e4 + 1] += x[1];
-            v[4 * e4 + 2] += x[2];
-            v[4 * e4 + 3] += x[3];
-        }
+        for (int e4 = 0; e4 < 4; ++e4) x[b][e4] = get4_coherent(r, slot_off(wave, b, e4, lane));
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) acc.v[b >> 1][b & 1][4 * e4 + y] += x[b][e4][y];
 }
 
 // Poll `flag` until it holds `epoch` (one thread).  Gives up after `limit`
@@ -302,7 +558,6 @@ __device__ __forceinline__ void wait_flag(const uint32_t *flag, uint32_t epoch, 
         }
         __builtin_amdgcn_s_sleep(1);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 // Trace helpers (thread 0 only; active only when p.trace is set).
@@ -334,21 +589,48 @@ __device__ __forceinline__ void trace_folded(const KParams &p, int tile, int pos
     rec[0] = pos + 1;
 }
 
+// Per-workgroup placement and busy time (only when p.timing is set): 8 int64 per
+// workgroup, {start, end, HW_ID, XCC_ID, mark0..mark3} in 100 MHz ticks.
+struct WgClock {
+    unsigned long long t0;
+    __device__ __forceinline__ explicit WgClock(const KParams &p) : t0(0) {
+        if (p.timing) t0 = __builtin_amdgcn_s_memrealtime();
+    }
+    __device__ __forceinline__ long long *entry(const KParams &p) const {
+        return p.timing + 8 * ((size_t)p.timing_base + blockIdx.x);
+    }
+    __device__ __forceinline__ void mark(const KParams &p, int k) const {
+        if (p.timing && threadIdx.x == 0 && k < 4) entry(p)[4 + k] = (long long)__builtin_amdgcn_s_memrealtime();
+    }
+    __device__ __forceinline__ void done(const KParams &p) const {
+        if (!p.timing || threadIdx.x != 0) return;
+        long long *e = entry(p);
+        e[0] = (long long)t0;
+        e[1] = (long long)__builtin_amdgcn_s_memrealtime();
+        e[2] = (long long)__builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));   // HW_REG_HW_ID
+        e[3] = (long long)__builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11));  // HW_REG_XCC_ID
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Data-parallel: one workgroup per tile of [tile_base, tile_base + ntiles).
 // ---------------------------------------------------------------------------
 template <int DT, int BL>
 __global__ __launch_bounds__(NT, 2) void gemm_dp(KParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-    const int w = p.perm ? p.perm[blockIdx.x] : (int)blockIdx.x;
+    __shared__ __attribute__((aligned(16))) char lds[NS_GRID * STAGE_BYTES];
+    const WgClock clk(p);
+    const int w = worker_of(p, p.ntiles);
     const int tile = p.tile_base + w;
-    const int m0 = (tile / p.tiles_n) * BM, n0 = (tile % p.tiles_n) * BN;
+    int m0, n0;
+    tile_origin(p, tile, m0, n0);
     Acc acc;
     zero_acc(acc);
-    mac_loop<DT, BL>(p, lds, m0, n0, 0, p.ipt, acc, p.trace ? trace_cov(p, tile) : nullptr);
-    store_c(p.C, m0, n0, p.M, p.N, acc);
+    mac_loop<DT, BL, NS_GRID>(p, lds, m0, n0, 0, p.ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
+    clk.mark(p, 0);
+    store_tile(p.C, m0, n0, p.M, p.N, acc, lds);
     trace_segment(p, p.worker_base + w, 0, tile, 0, p.ipt, 0);
     trace_folded(p, tile, 0, p.worker_base + w);
+    clk.done(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -356,49 +638,117 @@ __global__ __launch_bounds__(NT, 2) void gemm_dp(KParams p) {
 // ---------------------------------------------------------------------------
 template <int DT, int BL>
 __global__ __launch_bounds__(NT, 2) void gemm_splitk(KParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-    const int w = p.perm ? p.perm[blockIdx.x] : (int)blockIdx.x;
+    __shared__ __attribute__((aligned(16))) char lds[NS_GRID * STAGE_BYTES];
+    __shared__ int last_arriver;
+    const WgClock clk(p);
     const int S = p.splits;
+    const int w = worker_of(p, p.ntiles * S);
     const int tile = w / S, s = w % S;
     const int k0 = (int)((int64_t)s * p.ipt / S), k1 = (int)((int64_t)(s + 1) * p.ipt / S);
-    const int m0 = (tile / p.tiles_n) * BM, n0 = (tile % p.tiles_n) * BN;
+    int m0, n0;
+    tile_origin(p, tile, m0, n0);
     Acc acc;
     zero_acc(acc);
-    mac_loop<DT, BL>(p, lds, m0, n0, k0, k1, acc, p.trace ? trace_cov(p, tile) : nullptr);
+    mac_loop<DT, BL, NS_GRID>(p, lds, m0, n0, k0, k1, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
+    clk.mark(p, 0);
     trace_segment(p, w, 0, tile, k0, k1, S == 1 ? 0 : (s == 0 ? 1 : 2));
     if (S == 1) {
-        store_c(p.C, m0, n0, p.M, p.N, acc);
+        store_tile(p.C, m0, n0, p.M, p.N, acc, lds);
         trace_folded(p, tile, 0, w);
+        clk.done(p);
         return;
     }
+    // stage the accumulator in LDS; write this split's partial P[s] as row quads
+    // with device-scope stores (LDS keeps the copy this workgroup may fold itself)
     const size_t mn = (size_t)p.M * p.N;
-    store_c(p.part + (size_t)s * mn, m0, n0, p.M, p.N, acc);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    float *stg = reinterpret_cast<float *>(lds);
+    acc_to_lds(stg, acc);
     __syncthreads();
-    int *last = reinterpret_cast<int *>(lds);
+    const size_t org = (size_t)m0 * p.N + n0;                 // tile origin within [M,N]
+    const uint32_t span_bytes = (uint32_t)(((size_t)(min(BM, p.M - m0) - 1) * p.N + min(BN, p.N - n0)) * 4);
+    auto quad_off = [&](int r, int c) { return (uint32_t)(((size_t)r * p.N + c) * 4); };
+    auto staged = [&](int r, int c) { return *reinterpret_cast<const f32x4 *>(stg + r * EPI_LD + (c ^ epi_swz(r))); };
+    {
+        const __amdgpu_buffer_rsrc_t rp = span(p.part + (size_t)s * mn + org, span_bytes);
+        float *Ps = p.part + (size_t)s * mn;
+        for_each_quad(m0, n0, p.M, p.N, [&](int, int r, int c, size_t off, int nv) {
+            const f32x4 v = staged(r, c);
+            if (nv == 4) put4_coherent(rp, quad_off(r, c), v);
+            else for (int x = 0; x < nv; ++x) put_coherent(Ps + off + x, v[x]);
+        });
+    }
+    wait_vm_all();                 // this wave's partial stores are complete
+    __syncthreads();               // ... and every other wave's
+    clk.mark(p, 1);
+    int *last = &last_arriver;
     if (threadIdx.x == 0) {
         const uint32_t before =
-            __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool is_last = before == (uint32_t)(S - 1);
-        if (is_last)
+        if (is_last)   // every split has arrived: reset for the next call
             __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *last = is_last ? 1 : 0;
     }
     __syncthreads();
-    if (!*last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    // Fold the S partials in split order: ((P0 + P1) + P2) + ...
-    Acc sum;
-    zero_acc(sum);
-    for (int t = 0; t < S; ++t) {
-        const float *P = p.part + (size_t)t * mn;
-        for_each_element(m0, n0, p.M, p.N, [&](int i, int j, int e, size_t off) {
-            const float x = (t == s) ? acc.v[i][j][e] : P[off];
-            sum.v[i][j][e] = (t == 0) ? x : sum.v[i][j][e] + x;
-        });
-        trace_folded(p, tile, t, tile * S + t);
+    if (!*last) {
+        clk.done(p);
+        return;
     }
-    store_c(p.C, m0, n0, p.M, p.N, sum);
+    // Fold the S partials in split order, ((P0 + P1) + P2) + ..., taking this
+    // workgroup's own split from LDS.  Per round: 4 quads of the thread, and the
+    // loads of up to 4 partials for them in flight before they are added.
+    const bool vec = (p.N & 3) == 0;
+    for (int q0 = 0; q0 < 16; q0 += 4) {
+        int rr[4], cc[4];
+        bool ok[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int fq = threadIdx.x + NT * (q0 + g);
+            rr[g] = fq >> 5;
+            cc[g] = (fq & 31) * 4;
+            ok[g] = m0 + rr[g] < p.M && n0 + cc[g] < p.N;
+        }
+        f32x4 sum[4];
+        for (int t0 = 0; t0 < S; t0 += 4) {
+            f32x4 buf[4][4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int t = t0 + tt;
+                if (t >= S || t == s) continue;
+                const __amdgpu_buffer_rsrc_t rt = span(p.part + (size_t)t * mn + org, span_bytes);
+                const float *Pt = p.part + (size_t)t * mn;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    if (!ok[g]) continue;
+                    const int nv = min(4, p.N - (n0 + cc[g]));
+                    if (vec && nv == 4) {
+                        buf[tt][g] = get4_coherent(rt, quad_off(rr[g], cc[g]));
+                    } else {
+                        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                        for (int x = 0; x < nv; ++x)
+                            v[x] = get_coherent(Pt + (size_t)(m0 + rr[g]) * p.N + n0 + cc[g] + x);
+                        buf[tt][g] = v;
+                    }
+                }
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int t = t0 + tt;
+                if (t >= S) break;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 x = (t == s) ? staged(rr[g], cc[g]) : buf[tt][g];
+                    sum[g] = (t == 0) ? x : sum[g] + x;
+                }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            if (ok[g]) put_quad(p.C + (size_t)(m0 + rr[g]) * p.N + n0 + cc[g], sum[g], min(4, p.N - (n0 + cc[g])), vec);
+    }
+    for (int t = 0; t < S; ++t) trace_folded(p, tile, t, tile * S + t);
+    clk.mark(p, 2);
+    clk.done(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -406,10 +756,11 @@ __global__ __launch_bounds__(NT, 2) void gemm_splitk(KParams p) {
 // ---------------------------------------------------------------------------
 template <int DT, int BL, bool ATOMIC>
 __global__ __launch_bounds__(NT, 1) void gemm_streamk(KParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-    const int u = p.perm ? p.perm[blockIdx.x] : (int)blockIdx.x;
+    __shared__ __attribute__((aligned(16))) char lds[NS_STREAMK * STAGE_BYTES];
+    const WgClock clk(p);
+    const int u = worker_of(p, p.units);
     const int ipt = p.ipt;
-    const int begin = u * p.q + min(u, p.big);
+    const int begin = unit_start(u, p.q, p.big);
     const int end = begin + p.q + (u < p.big ? 1 : 0);
     int nseg = 0;
     for (int pos = begin; pos < end;) {
@@ -418,41 +769,48 @@ __global__ __launch_bounds__(NT, 1) void gemm_streamk(KParams p) {
         const int k0 = pos - tb;
         const int k1 = min(end - tb, ipt);
         const int tile = p.tile_base + t;
-        const int m0 = (tile / p.tiles_n) * BM, n0 = (tile % p.tiles_n) * BN;
+        int m0, n0;
+        tile_origin(p, tile, m0, n0);
         const int role = k0 > 0 ? 2 : (k1 == ipt ? 0 : 1);
         Acc acc;
         zero_acc(acc);
-        mac_loop<DT, BL>(p, lds, m0, n0, k0, k1, acc, p.trace ? trace_cov(p, tile) : nullptr);
+        // walk the tile's K-slabs in the phase of its k = 0 holder: the units that
+        // meet in this tile then stream the same slabs close together in time
+        const int owner = unit_of(tb, p.q, p.big);
+        const int rot = (tb - unit_start(owner, p.q, p.big)) % ipt;
+        mac_loop<DT, BL, NS_STREAMK>(p, lds, m0, n0, k0, k1, rot, acc, p.trace ? trace_cov(p, tile) : nullptr);
+        clk.mark(p, 2 * min(nseg, 1));
         trace_segment(p, u, nseg++, tile, k0, k1, role);
         if (role == 0) {
-            store_c(p.C, m0, n0, p.M, p.N, acc);
+            store_tile(p.C, m0, n0, p.M, p.N, acc, lds);
             trace_folded(p, tile, 0, u);
         } else if constexpr (ATOMIC) {
             atomic_add_c(p.C, m0, n0, p.M, p.N, acc);
         } else if (role == 2) {
             // starts mid-tile: publish the partial, then the flag
             put_slot(p.part + (size_t)u * (BM * BN), acc);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            __syncthreads();
+            wait_vm_all();                 // this wave's partial stores are complete
+            __syncthreads();               // ... and every other wave's
             if (threadIdx.x == 0 && !(p.debug & GEMM_DEBUG_NO_PUBLISH))
-                __hip_atomic_store(p.flags + u, p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(p.flags + u, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             // holds k = 0 of a split tile: fold the next units' partials in k order
             trace_folded(p, tile, 0, u);
             const int tile_end = tb + ipt;
             int pos_fold = 1;
             for (int v = u + 1; v < p.units; ++v) {
-                if (v * p.q + min(v, p.big) >= tile_end) break;
+                if (unit_start(v, p.q, p.big) >= tile_end) break;
                 if (threadIdx.x == 0) wait_flag(p.flags + v, p.epoch, p.spin_limit, p.status);
                 __syncthreads();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                 add_slot(p.part + (size_t)v * (BM * BN), acc);
                 trace_folded(p, tile, pos_fold++, v);
             }
-            store_c(p.C, m0, n0, p.M, p.N, acc);
+            store_tile(p.C, m0, n0, p.M, p.N, acc, lds);
         }
+        clk.mark(p, 2 * min(nseg - 1, 1) + 1);
         pos = tb + k1;
     }
+    clk.done(p);
 }
 
 // ---------------------------------------------------------------------------

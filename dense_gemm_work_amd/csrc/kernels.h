@@ -23,7 +23,9 @@ struct KParams {
     const uint16_t *B;     // [K,N] or [N,K] row-major
     float *C;              // [M,N] row-major fp32
     int M, N, K;
-    int tiles_n;           // output tiles along N
+    int tiles_m, tiles_n;  // output tiles along M and N
+    int group_m;           // tile ids run column by column in groups of group_m tile rows (0: row-major)
+    int xcd_spread;        // 1: give each XCD a contiguous range of workers
     int ipt;               // k-iterations per tile
     int tile_base;         // first tile id of this launch (hybrid: Stream-K part starts at dp_tiles)
     int ntiles;            // tiles of a DP / Split-K launch
@@ -39,6 +41,8 @@ struct KParams {
     uint32_t debug;        // GEMM_DEBUG_* bits
     const int *perm;       // optional workgroup -> worker map
     int *trace;            // optional debug trace (see gemm.h)
+    long long *timing;     // optional per-workgroup {start, end, HW_ID, XCC_ID}
+    int timing_base;       // entry of this launch's workgroup 0
     int trace_maxseg, trace_maxfold, trace_workers, trace_tiles;
 };
 

@@ -67,9 +67,10 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
         *why = "N must be a multiple of 8 when B is stored [K,N] (128-bit row loads)";
         return GEMM_ERR_UNSUPPORTED;
     }
-    // keep every flattened index and element offset in range of the kernels' arithmetic
-    if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31)) {
-        *why = "M, N and K must each be at most 2^31";
+    // keep every flattened index and every per-tile buffer range (32-bit byte
+    // offsets of a 128-row panel) within the kernels' arithmetic
+    if (M > (int64_t(1) << 31) || N > (int64_t(1) << 22) || K > (int64_t(1) << 22)) {
+        *why = "M must be at most 2^31, N and K at most 2^22";
         return GEMM_ERR_UNSUPPORTED;
     }
 

@@ -140,6 +140,19 @@ typedef struct gemm_plan_t {
  *             gemm_trace_layout below).  The library zero-fills it first.
  *   spin_limit: bound on every inter-workgroup wait, in polls (0 = default).
  *   debug:    GEMM_DEBUG_* bits (0 in normal use).
+ *   timing:   optional device int64 buffer of at least 8 * plan.workers elements:
+ *             workgroup g of the call (launch order: the main grid, then the DP
+ *             tiles of a hybrid) writes {start, end, HW_ID, XCC_ID, m0, m1, m2, m3}:
+ *             times in ticks of the 100 MHz s_memrealtime clock, HW_ID and XCC_ID
+ *             as read from the hardware registers (CU, SE and XCD placement).
+ *             Marks: DP m0 = mainloop done; Split-K m0 = mainloop done, m1 =
+ *             partial stored, m2 = fold done (last arriver); Stream-K m0/m1 =
+ *             first segment's mainloop / fixup-and-store done, m2/m3 = the same
+ *             for the unit's last segment.  Unset marks stay as the caller left them.
+ * Tuning overrides read once from the environment (defaults in brackets):
+ *   DGW_GROUP_M    tile rows per raster group [8]; tile ids run column by column
+ *                  within a group of rows (0 = plain row-major)
+ *   DGW_XCD_SPREAD 1: consecutive workers on the same XCD [1]; 0: workgroup order
  */
 typedef struct gemm_args_t {
     const void *A;
@@ -158,6 +171,7 @@ typedef struct gemm_args_t {
     int64_t trace_ints;
     uint32_t spin_limit;
     uint32_t debug;
+    int64_t *timing;
 } gemm_args_t;
 
 /*

@@ -180,7 +180,7 @@ def test_plan_rejects_bad_arguments(dg):
             dg.gemm_plan(args["M"], args["N"], args["K"], args["layout"], args["mode"], args["splits"],
                          args["cus"])
         assert ei.value.status == dg.GEMM_ERR_INVALID, b
-    for b in [dict(K=100), dict(N=100)]:
+    for b in [dict(K=100), dict(N=100), dict(K=(1 << 22) + 8), dict(N=(1 << 22) + 8)]:
         args = dict(M=256, N=256, K=2048)
         args.update(b)
         with pytest.raises(dg.GemmError) as ei:
