@@ -1,28 +1,33 @@
 // gemm_kernels.hip -- gfx950 (MI355X) kernels of the DP / Split-K / Stream-K GEMM.
 //
-// One mainloop serves every decomposition.  A workgroup of 256 threads (four
-// 64-wide waves in a 2x2 arrangement) computes one 128x128 fp32 output tile;
-// one "MAC-loop iteration" (Split-K/Stream-K book chapter, glossary) is a
-// 64-wide step of K: the A slab [128 x 64] and the B slab [64 x 128] are staged
-// in LDS and each wave issues 16 v_mfma_f32_32x32x16_{bf16,f16} on its 64x64
-// quarter.  Slabs are double-buffered in LDS: the 128-bit global loads of
-// iteration i+1 are in flight while iteration i runs on the matrix cores
-// (CUTLASS optimisation guide, "Software Pipelining").
+// One mainloop serves every decomposition.  A workgroup computes one 128x128
+// fp32 output tile at a time; one "MAC-loop iteration" (Split-K/Stream-K book
+// chapter, glossary) is a 64-wide step of K: the A slab [128 x 64] and the
+// B slab [64 x 128] are staged in LDS and the workgroup issues 64
+// v_mfma_f32_32x32x16_{bf16,f16} on them.  Four "quadrant" waves in a 2x2
+// arrangement own the four 64x64 quarters of the tile.  A workgroup has NW = 4
+// waves (one per SIMD) or NW = 8 waves (two per SIMD): with 8, the two waves of
+// a SIMD own the same quarter and split each iteration's four 16-wide k-steps
+// between them, and their accumulators are added once per segment.  Eight
+// waves keep a single workgroup per CU (the persistent Stream-K kernel) from
+// idling its matrix cores at every barrier and LDS round trip.
 //
-// LDS layout: both operands are stored "k-contiguous", one 128-byte row of 64
-// values per M row (A) or N column (B), with the 16-byte chunks of row r
-// XOR-swizzled by (r ^ r>>3) & 7 so that the MFMA operand reads (eight rows,
-// same logical chunk, per 128 bytes) hit distinct banks.  A [M,K] and B [N,K]
-// rows are copied as they are; B [K,N] is transposed in registers on its way
-// to LDS (four k-rows of eight n-values per thread become eight 4-value
-// k-runs), so the matrix cores always read 8 consecutive k per lane.
+// Operands move global -> LDS with buffer_load ... lds (16 bytes per lane, no
+// register round trip), in NS LDS stages: the loads of iteration i + NS are
+// issued as soon as stage i has been read (CUTLASS optimisation guide,
+// "Software Pipelining").  A [M,K] and B [N,K] are stored k-contiguous (one
+// 128-byte row of 64 values per row), the 16-byte chunks of row r XOR-swizzled
+// by (r ^ r>>3) & 7; B [K,N] is stored as k-rows of 128 n-values, chunk c of
+// k-row r at c ^ kn_swz(r), and read with ds_read_b64_tr_b16, which hands every
+// MFMA lane four consecutive k of one column.  Fragment reads run one k-step
+// ahead of the MFMAs, also across the stage barrier.
 //
 // Epilogues (book chapter, Stream-K paragraph after the glossary; Case 4's
 // reduction modes; docc StreamK page):
 //   K_DP         store the tile.
 //   K_SPLITK     store the fp32 partial into P[s] of [S,M,N], arrive at the
 //                tile's counter; the last arriver sums P[0..S-1] in split order
-//                (its own split from registers) and stores C.
+//                (its own split from LDS) and stores C.
 //   K_SK         a segment that covers the whole tile is stored; one that starts
 //                mid-tile (always the unit's first) publishes its accumulator to
 //                the unit's slot and raises the unit's flag; the unit holding the
@@ -50,23 +55,42 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = GEMM_BK;
-constexpr int NT = 256;                       // threads per workgroup
 constexpr int SLAB = BM * BK;                 // 16-bit values per operand slab (A and B alike)
 constexpr int STAGE_BYTES = 2 * SLAB * 2;     // A slab then B slab: 32 KiB
-// LDS stages per workgroup: the persistent Stream-K kernel (one workgroup per
-// CU) keeps 4 stages (128 KiB of the CU's 160 KiB) in flight; the DP and
-// Split-K kernels keep 2 (64 KiB) so that two workgroups share a CU.
-constexpr int NS_STREAMK = 4;
-constexpr int NS_GRID = 2;
-static_assert(BM == BN, "the LDS addressing below assumes square tiles");
+constexpr int SLAB_DMAS = SLAB * 2 / 1024;    // 1 KiB wave loads per slab: 16
 
 struct Acc {
     f32x16 v[2][2];   // [i: 32-row block][j: 32-column block] of the wave's 64x64 quarter
 };
 
+// Wave roles in a workgroup of NW waves.
+template <int NW>
+struct Role {
+    static constexpr int NT = 64 * NW;              // threads
+    static constexpr int KSTEPS = 4 * 4 / NW;       // 16-wide k-steps per wave and stage: 4 or 2
+    static constexpr int DPW = SLAB_DMAS / NW;      // loads per wave and operand slab: 4 or 2
+    int lane, wave, quad, wm, wn, kh;
+    __device__ __forceinline__ Role() {
+        lane = threadIdx.x & 63;
+        wave = threadIdx.x >> 6;
+        quad = wave & 3;
+        wm = quad >> 1;
+        wn = quad & 1;
+        kh = wave >> 2;                             // which half of the k-steps (8 waves only)
+    }
+};
+
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// B [K,N] rows in LDS are 256 bytes (128 n-values); 16-byte chunk c of k-row r
+// lives at chunk c ^ kn_swz(r).  The four k-rows read together by a 16-lane
+// transpose read then fall on distinct banks.
+__device__ __forceinline__ int kn_swz(int r) { return ((r & 1) << 2) ^ ((r & 2) * 5); }
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
@@ -79,22 +103,17 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 // ---------------------------------------------------------------------------
-// Operand staging: buffer loads straight into LDS (no register round trip)
+// Operand staging: buffer loads straight into LDS
 // ---------------------------------------------------------------------------
 // Each buffer_load ... lds instruction moves 16 bytes per lane into LDS at
 // (wave-uniform base) + 16 * lane, i.e. 1 KiB of contiguous LDS per wave; the
-// swizzle is therefore applied by choosing which global 16-byte chunk each lane
-// fetches.  Loads whose address falls outside the buffer's range return zero,
-// which masks ragged M/N edges; a ragged K tail is masked by pointing the lane
-// at an offset beyond the range.
+// swizzle is applied by choosing which global 16-byte chunk each lane fetches.
+// Loads whose address falls outside the buffer's range return zero, which
+// masks ragged M/N edges; a ragged K tail is masked by pointing the lane at an
+// offset beyond the range.
 constexpr uint32_t OOB = 0x7ffffff0u;        // an offset outside every buffer range used here
 constexpr uint32_t RSRC_DW3 = 0x00020000u;    // raw buffer, 32-bit data format
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// Buffer resource (wave-uniform, in SGPRs): base address, byte range, format word.
 __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     i32x4 r;
@@ -105,9 +124,8 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
     return r;
 }
 
-// 16-byte buffer load of every lane straight into LDS at lds + 16 * lane.  Issued
-// as inline assembly so that the compiler does not wait for it before unrelated
-// LDS reads; completion is awaited explicitly with wait_stage().
+// Issued as inline assembly so that the compiler does not wait for it before
+// unrelated LDS reads; completion is awaited explicitly with wait_stage().
 __device__ __forceinline__ void dma16(i32x4 rsrc, const void *lds, uint32_t voff) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)reinterpret_cast<uintptr_t>((const lds_void *)lds));
@@ -117,18 +135,15 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, const void *lds, uint32_t voff
                  : "memory");
 }
 
-// B [K,N] rows in LDS are 256 bytes (128 n-values); 16-byte chunk c of k-row r
-// lives at chunk c ^ kn_swz(r).  The four k-rows read together by a 16-lane
-// transpose read then fall on distinct banks.
-__device__ __forceinline__ int kn_swz(int r) { return ((r & 1) << 2) ^ ((r & 2) * 5); }
-
 // Wait until at most `n` vector-memory operations of this wave are outstanding
 // and all of its LDS reads have returned, then synchronise the workgroup.
 __device__ __forceinline__ void wait_stage(int n) {
     // s_waitcnt on gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
 #define DGW_WAIT(x) (((x) & 15) | (((x) >> 4) << 14) | (7 << 4) | (0 << 8))
     switch (n) {
+    case 4: __builtin_amdgcn_s_waitcnt(DGW_WAIT(4)); break;
     case 8: __builtin_amdgcn_s_waitcnt(DGW_WAIT(8)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(DGW_WAIT(12)); break;
     case 16: __builtin_amdgcn_s_waitcnt(DGW_WAIT(16)); break;
     case 24: __builtin_amdgcn_s_waitcnt(DGW_WAIT(24)); break;
     default: __builtin_amdgcn_s_waitcnt(DGW_WAIT(0)); break;
@@ -137,31 +152,34 @@ __device__ __forceinline__ void wait_stage(int n) {
     asm volatile("s_barrier" ::: "memory");
 }
 
-// Per-thread load plan of one tile: 4 A instructions and 4 B instructions per
-// wave and k-iteration (16 KiB each per workgroup).
-template <int BL>
+// Per-thread load plan of one tile: the wave's DPW instructions per slab.
+template <int BL, int NW>
 struct LoadPlan {
+    static constexpr int DPW = Role<NW>::DPW;
     const char *a_base;      // A + m0 * K (bytes)
     const char *b_base;      // B + n0 * K ([N,K]) or B + n0 ([K,N]) (bytes)
     uint32_t a_rows_bytes;   // valid A rows * K * 2
     uint32_t b_rows_bytes;   // [N,K]: valid B rows * K * 2
-    uint32_t a_off[4];       // byte offsets at k-iteration 0
-    uint32_t b_off[4];
-    int a_kc[4];             // first k of the lane's chunk (ragged-K mask)
-    int b_kc[4];             // [N,K]: first k of the chunk; [K,N]: the k-row
-    bool b_nok[4];           // [K,N]: chunk beyond N
+    uint32_t a_off[DPW];     // byte offsets at k-iteration 0
+    uint32_t b_off[DPW];
+    int a_kc[DPW];           // first k of the lane's chunk (ragged-K mask)
+    int b_kc[DPW];           // [N,K]: first k of the chunk; [K,N]: the k-row
+    bool b_nok[DPW];         // [K,N]: chunk beyond N
+    int first;               // the wave's first instruction of a slab
 };
 
-template <int BL>
-__device__ __forceinline__ void make_load_plan(LoadPlan<BL> &lp, const KParams &p, int m0, int n0) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <int BL, int NW>
+__device__ __forceinline__ void make_load_plan(LoadPlan<BL, NW> &lp, const KParams &p, int m0, int n0) {
+    constexpr int DPW = Role<NW>::DPW;
+    const Role<NW> w;
     const int K = p.K, N = p.N;
+    lp.first = w.wave * DPW;
     lp.a_base = reinterpret_cast<const char *>(p.A) + (size_t)m0 * K * 2;
     lp.a_rows_bytes = (uint32_t)(min(BM, p.M - m0) * K * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (wave * 4 + i) * 8 + (lane >> 3);          // row of the 128 x 64 slab
-        const int c = (lane & 7) ^ swz(r);                       // logical 8-value chunk
+    for (int i = 0; i < DPW; ++i) {
+        const int r = (lp.first + i) * 8 + (w.lane >> 3);      // row of the 128 x 64 slab
+        const int c = (w.lane & 7) ^ swz(r);                   // logical 8-value chunk
         lp.a_off[i] = (uint32_t)(r * K + c * 8) * 2;
         lp.a_kc[i] = c * 8;
     }
@@ -169,9 +187,9 @@ __device__ __forceinline__ void make_load_plan(LoadPlan<BL> &lp, const KParams &
         lp.b_base = reinterpret_cast<const char *>(p.B) + (size_t)n0 * K * 2;
         lp.b_rows_bytes = (uint32_t)(min(BN, N - n0) * K * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = (wave * 4 + i) * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ swz(r);
+        for (int i = 0; i < DPW; ++i) {
+            const int r = (lp.first + i) * 8 + (w.lane >> 3);
+            const int c = (w.lane & 7) ^ swz(r);
             lp.b_off[i] = (uint32_t)(r * K + c * 8) * 2;
             lp.b_kc[i] = c * 8;
             lp.b_nok[i] = false;
@@ -180,9 +198,9 @@ __device__ __forceinline__ void make_load_plan(LoadPlan<BL> &lp, const KParams &
         lp.b_base = reinterpret_cast<const char *>(p.B) + (size_t)n0 * 2;
         lp.b_rows_bytes = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = (wave * 4 + i) * 4 + (lane >> 4);          // k-row of the 64 x 128 slab
-            const int c = (lane & 15) ^ kn_swz(r);                   // logical 8-value n chunk
+        for (int i = 0; i < DPW; ++i) {
+            const int r = (lp.first + i) * 4 + (w.lane >> 4);       // k-row of the 64 x 128 slab
+            const int c = (w.lane & 15) ^ kn_swz(r);                // logical 8-value n chunk
             lp.b_off[i] = (uint32_t)(r * N + c * 8) * 2;
             lp.b_kc[i] = r;
             lp.b_nok[i] = n0 + c * 8 >= N;
@@ -190,64 +208,61 @@ __device__ __forceinline__ void make_load_plan(LoadPlan<BL> &lp, const KParams &
     }
 }
 
-// Issue the 8 loads of k-iteration `it` into `stage` (A slab then B slab).
-template <int BL>
-__device__ __forceinline__ void issue_loads(const LoadPlan<BL> &lp, const KParams &p, char *stage, int it) {
-    const int wave = threadIdx.x >> 6;
-    const int kb = it * BK;
+// Issue the wave's loads of physical K-slab `slab` into `stage` (A slab then B slab).
+template <int BL, int NW>
+__device__ __forceinline__ void issue_loads(const LoadPlan<BL, NW> &lp, const KParams &p, char *stage,
+                                            int slab) {
+    constexpr int DPW = Role<NW>::DPW;
+    const int kb = slab * BK;
     // A: base advances along K; rows beyond M fall outside [0, a_rows_bytes - 2 kb)
     const i32x4 ra = make_rsrc(lp.a_base + (size_t)kb * 2, lp.a_rows_bytes - kb * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < DPW; ++i) {
         const uint32_t off = (kb + lp.a_kc[i] < p.K) ? lp.a_off[i] : OOB;
-        dma16(ra, stage + (wave * 4 + i) * 1024, off);
+        dma16(ra, stage + (lp.first + i) * 1024, off);
     }
     if constexpr (BL == 1) {
         const i32x4 rb = make_rsrc(lp.b_base + (size_t)kb * 2, lp.b_rows_bytes - kb * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < DPW; ++i) {
             const uint32_t off = (kb + lp.b_kc[i] < p.K) ? lp.b_off[i] : OOB;
-            dma16(rb, stage + SLAB * 2 + (wave * 4 + i) * 1024, off);
+            dma16(rb, stage + SLAB * 2 + (lp.first + i) * 1024, off);
         }
     } else {
         const int krows = min(BK, p.K - kb);
-        const i32x4 rb =
-            make_rsrc(lp.b_base + (size_t)kb * p.N * 2, (uint32_t)(krows * p.N * 2));
+        const i32x4 rb = make_rsrc(lp.b_base + (size_t)kb * p.N * 2, (uint32_t)(krows * p.N * 2));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < DPW; ++i) {
             const uint32_t off = (lp.b_kc[i] < krows && !lp.b_nok[i]) ? lp.b_off[i] : OOB;
-            dma16(rb, stage + SLAB * 2 + (wave * 4 + i) * 1024, off);
+            dma16(rb, stage + SLAB * 2 + (lp.first + i) * 1024, off);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core work on one staged slab pair: per 16-wide k-step (kk) every wave
-// reads its two A and two B operand fragments and issues four MFMAs.
+// Matrix-core work: per 16-wide k-step (kk) a quadrant wave reads its two A and
+// two B operand fragments and issues four MFMAs.
 // ---------------------------------------------------------------------------
 struct Frag {
     u32x4 a[2];   // rows wm*64 + {0, 32} + lane % 32, k = 16 kk + 8 (lane / 32) + 0..7
     u32x4 b[2];   // cols wn*64 + {0, 32} + lane % 32, same k
 };
 
-template <int BL>
-__device__ __forceinline__ void load_frag(const char *stage, int kk, Frag &f) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+template <int BL, int NW>
+__device__ __forceinline__ void load_frag(const Role<NW> &w, const char *stage, int kk, Frag &f) {
     const char *As = stage;
     const char *Bs = stage + SLAB * 2;
-    const int hk = lane >> 5;
+    const int hk = w.lane >> 5;
     const int ch = kk * 2 + hk;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + (lane & 31);
+        const int r = w.wm * 64 + i * 32 + (w.lane & 31);
         f.a[i] = *reinterpret_cast<const u32x4 *>(As + r * 128 + ((ch ^ swz(r)) << 4));
     }
     if constexpr (BL == 1) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int r = wn * 64 + j * 32 + (lane & 31);
+            const int r = w.wn * 64 + j * 32 + (w.lane & 31);
             f.b[j] = *reinterpret_cast<const u32x4 *>(Bs + r * 128 + ((ch ^ swz(r)) << 4));
         }
     } else {
@@ -255,11 +270,11 @@ __device__ __forceinline__ void load_frag(const char *stage, int kk, Frag &f) {
         // it receives 4 k-values of column n = l % 32 (two reads give 8 k)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int n = wn * 64 + j * 32 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+            const int n = w.wn * 64 + j * 32 + ((w.lane >> 4) & 1) * 16 + 4 * (w.lane & 3);
             u32x2 h[2];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const int r = kk * 16 + 8 * hk + 4 * half + ((lane & 15) >> 2);
+                const int r = kk * 16 + 8 * hk + 4 * half + ((w.lane & 15) >> 2);
                 const char *addr = Bs + r * 256 + ((((n >> 3) ^ kn_swz(r)) << 4) | ((n & 7) << 1));
                 const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)addr);
                 h[half] = __builtin_bit_cast(u32x2, t);
@@ -281,49 +296,87 @@ __device__ __forceinline__ void mma(const Frag &f, Acc &acc) {
 // k-iterations k0..k1-1, logical iteration k reading physical 64-wide K-slab
 // (k + rot) mod ipt (rot = 0 walks K in order; a rotation lets the units that
 // share a tile's panels walk them in phase -- the set of slabs a segment covers
-// is what the schedule defines, the order inside a segment is free).
-// NS LDS stages: the loads of iteration i + NS are issued as soon as stage i has
-// been read.  Fragment reads run one k-step ahead of the MFMAs, also across the
-// stage barrier, so the matrix cores do not drain at every iteration.  Ends
-// with a barrier, so the LDS is free again on return.
-template <int DT, int BL, int NS>
+// is what the schedule defines, the order inside a segment is free).  With 8
+// waves each wave covers half of every slab's k-steps and holds a partial sum
+// of its quarter (see merge_k_halves).  Ends with a barrier, so the LDS is
+// free again on return.
+template <int DT, int BL, int NS, int NW>
 __device__ __forceinline__ void mac_loop(const KParams &p, char *lds, int m0, int n0, int k0, int k1,
                                          int rot, Acc &acc, int *cov) {
+    constexpr int KS = Role<NW>::KSTEPS;
+    constexpr int DPI = 2 * Role<NW>::DPW;                 // loads per wave and iteration
     const int n = k1 - k0;
     if (n <= 0) return;
-    LoadPlan<BL> lp;
-    make_load_plan<BL>(lp, p, m0, n0);
-    int phys = k0 + rot;                 // physical slab of the next iteration to load
+    const Role<NW> w;
+    LoadPlan<BL, NW> lp;
+    make_load_plan<BL, NW>(lp, p, m0, n0);
+    int phys = k0 + rot;                                   // physical slab of the next load
     if (phys >= p.ipt) phys -= p.ipt;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
         if (s < n) {
-            issue_loads<BL>(lp, p, lds + s * STAGE_BYTES, phys);
+            issue_loads<BL, NW>(lp, p, lds + s * STAGE_BYTES, phys);
             if (++phys == p.ipt) phys = 0;
         }
-    wait_stage(8 * (min(NS, n) - 1));                       // stage 0 complete for every wave
-    Frag f0, f1;
-    load_frag<BL>(lds, 0, f0);
+    wait_stage(DPI * (min(NS, n) - 1));                    // stage 0 complete for every wave
+    const int kk0 = w.kh * KS;                             // the wave's first k-step of a slab
+    Frag f[2];
+    load_frag<BL, NW>(w, lds, kk0, f[0]);
     for (int i = 0; i < n; ++i) {
         char *st = lds + (i % NS) * STAGE_BYTES;
-        load_frag<BL>(st, 1, f1);
-        mma<DT>(f0, acc);
-        load_frag<BL>(st, 2, f0);
-        mma<DT>(f1, acc);
-        load_frag<BL>(st, 3, f1);
-        mma<DT>(f0, acc);
-        if (i + 1 < n) {
-            wait_stage(8 * min(NS - 2, n - 2 - i));        // stage i+1 complete; stage i fully read
-            if (i + NS < n) {
-                issue_loads<BL>(lp, p, st, phys);
-                if (++phys == p.ipt) phys = 0;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            if (j + 1 < KS) {
+                load_frag<BL, NW>(w, st, kk0 + j + 1, f[(j + 1) & 1]);
+            } else if (i + 1 < n) {
+                wait_stage(DPI * min(NS - 2, n - 2 - i));  // stage i+1 complete; stage i fully read
+                if (i + NS < n) {
+                    issue_loads<BL, NW>(lp, p, st, phys);
+                    if (++phys == p.ipt) phys = 0;
+                }
+                load_frag<BL, NW>(w, lds + ((i + 1) % NS) * STAGE_BYTES, kk0, f[(j + 1) & 1]);
             }
-            load_frag<BL>(lds + ((i + 1) % NS) * STAGE_BYTES, 0, f0);
+            mma<DT>(f[j & 1], acc);
         }
-        mma<DT>(f1, acc);
         if (cov && threadIdx.x == 0) atomicAdd(cov + k0 + i, 1);
     }
     wait_stage(0);
+}
+
+// With 8 waves: add the k-half-1 wave's accumulator into its quadrant partner
+// (k-half 0) through LDS; afterwards only the k-half-0 waves hold the tile.
+// The sum is taken in a fixed order.  `lds` must be free; it is free on return.
+template <int NW>
+__device__ __forceinline__ void merge_k_halves(Acc &acc, char *lds) {
+    if constexpr (NW == 8) {
+        const Role<NW> w;
+        f32x4 *buf = reinterpret_cast<f32x4 *>(lds);
+        if (w.kh == 1) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const f32x16 &v = acc.v[b >> 1][b & 1];
+                    buf[((w.quad * 4 + b) * 4 + e4) * 64 + w.lane] =
+                        f32x4{v[4 * e4], v[4 * e4 + 1], v[4 * e4 + 2], v[4 * e4 + 3]};
+                }
+        }
+        __syncthreads();
+        if (w.kh == 0) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const f32x4 x = buf[((w.quad * 4 + b) * 4 + e4) * 64 + w.lane];
+                    f32x16 &v = acc.v[b >> 1][b & 1];
+                    v[4 * e4] += x[0];
+                    v[4 * e4 + 1] += x[1];
+                    v[4 * e4 + 2] += x[2];
+                    v[4 * e4 + 3] += x[3];
+                }
+        }
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -368,7 +421,8 @@ __device__ __forceinline__ void tile_origin(const KParams &p, int tile, int &m0,
 // ---------------------------------------------------------------------------
 // Epilogue helpers.  Accumulator element e of block (i, j) in lane l sits at
 // row 32 i + 8 (e / 4) + 4 (l / 32) + e % 4 and column 32 j + l % 32 of the
-// wave's quarter (output layout of the 32x32 MFMA).
+// wave's quarter (output layout of the 32x32 MFMA).  Only the quadrant waves
+// (k-half 0) take part in accumulator-layout steps.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void zero_acc(Acc &acc) {
 #pragma unroll
@@ -379,55 +433,59 @@ __device__ __forceinline__ void zero_acc(Acc &acc) {
             for (int e = 0; e < 16; ++e) acc.v[i][j][e] = 0.0f;
 }
 
-template <class F>
+template <int NW, class F>
 __device__ __forceinline__ void for_each_element(int m0, int n0, int M, int N, F &&f) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const Role<NW> w;
+    if (w.kh != 0) return;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+            const int col = n0 + w.wn * 64 + j * 32 + (w.lane & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int row = m0 + w.wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (w.lane >> 5) + (e & 3);
                 if (row < M && col < N) f(i, j, e, (size_t)row * N + col);
             }
         }
 }
 
 // Row-major staging of the fp32 tile in LDS (64 KiB), then coalesced float4
-// traffic: thread t owns quads t + 256 q (q = 0..15), quad f covering columns
-// 4 (f % 32) .. +3 of tile row f / 32.  Column c of row r is stored at
-// c ^ epi_swz(r): the two rows written by one MFMA result register (4 apart)
-// then fall on different banks, and every aligned quad stays contiguous.
+// traffic: thread t owns quads t + NT q, quad f covering columns 4 (f % 32) .. +3
+// of tile row f / 32.  Column c of row r is stored at c ^ epi_swz(r): the two
+// rows written by one MFMA result register (4 apart) then fall on different
+// banks, and every aligned quad stays contiguous.
 constexpr int EPI_LD = BN;
 __device__ __forceinline__ int epi_swz(int r) { return ((r >> 2) & 1) << 5; }
 
+template <int NW>
 __device__ __forceinline__ void acc_to_lds(float *tile, const Acc &acc) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const Role<NW> w;
+    if (w.kh != 0) return;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int col = wn * 64 + j * 32 + (lane & 31);
+            const int col = w.wn * 64 + j * 32 + (w.lane & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int row = w.wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (w.lane >> 5) + (e & 3);
                 tile[row * EPI_LD + (col ^ epi_swz(row))] = acc.v[i][j][e];
             }
         }
 }
 
-// Calls f(q, row, col, global offset, valid columns in the quad (0..4)) for the
-// thread's 16 quads; rows beyond M and quads wholly beyond N are skipped.
-template <class F>
+__device__ __forceinline__ f32x4 staged_quad(const float *tile, int r, int c) {
+    return *reinterpret_cast<const f32x4 *>(tile + r * EPI_LD + (c ^ epi_swz(r)));
+}
+
+// Calls f(q, row, col, global offset, valid columns in the quad (1..4)) for the
+// thread's quads; rows beyond M and quads wholly beyond N are skipped.
+template <int NW, class F>
 __device__ __forceinline__ void for_each_quad(int m0, int n0, int M, int N, F &&f) {
+    constexpr int NT = Role<NW>::NT, QPT = BM * BN / 4 / NT;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < QPT; ++q) {
         const int fq = threadIdx.x + NT * q;
         const int r = fq >> 5, c = (fq & 31) * 4;
         const int row = m0 + r, col = n0 + c;
@@ -443,52 +501,34 @@ __device__ __forceinline__ void put_quad(float *dst, f32x4 v, int nvalid, bool v
     }
 }
 
-__device__ __forceinline__ f32x4 get_quad(const float *src, int nvalid, bool vec) {
-    if (vec && nvalid == 4) return *reinterpret_cast<const f32x4 *>(src);
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    for (int x = 0; x < nvalid; ++x) v[x] = src[x];
-    return v;
-}
-
-// Calls f(q, row, col, global offset) for the thread's 64 elements of the staged
-// tile: column threadIdx % 128, rows threadIdx / 128 + 2 q (q = 0..63), so each
-// wave touches 64 consecutive floats of one row per call.
-template <class F>
-__device__ __forceinline__ void for_each_float(int m0, int n0, int M, int N, F &&f) {
-    const int c = threadIdx.x & 127, r0 = threadIdx.x >> 7;
-    const int col = n0 + c;
-    if (col >= N) return;
-#pragma unroll
-    for (int q = 0; q < 64; ++q) {
-        const int r = r0 + 2 * q, row = m0 + r;
-        if (row < M) f(q, r, c, (size_t)row * N + col);
-    }
-}
-
-// Write the accumulator tile to X[M,N] (C or a Split-K partial).  `lds` must be
-// free; it is free again on return.
+// Write the accumulator tile to C.  `lds` must be free; it is free again on return.
+template <int NW>
 __device__ __forceinline__ void store_tile(float *X, int m0, int n0, int M, int N, const Acc &acc,
                                            char *lds) {
     float *tile = reinterpret_cast<float *>(lds);
-    acc_to_lds(tile, acc);
+    acc_to_lds<NW>(tile, acc);
     __syncthreads();
     const bool vec = (N & 3) == 0;
-    for_each_quad(m0, n0, M, N, [&](int, int r, int c, size_t off, int nv) {
-        put_quad(X + off, *reinterpret_cast<const f32x4 *>(tile + r * EPI_LD + (c ^ epi_swz(r))), nv, vec);
+    for_each_quad<NW>(m0, n0, M, N, [&](int, int r, int c, size_t off, int nv) {
+        put_quad(X + off, staged_quad(tile, r, c), nv, vec);
     });
     __syncthreads();
 }
 
+template <int NW>
 __device__ __forceinline__ void atomic_add_c(float *C, int m0, int n0, int M, int N, const Acc &acc) {
-    for_each_element(m0, n0, M, N,
-                     [&](int i, int j, int e, size_t off) { unsafeAtomicAdd(C + off, acc.v[i][j][e]); });
+    for_each_element<NW>(m0, n0, M, N,
+                         [&](int i, int j, int e, size_t off) { unsafeAtomicAdd(C + off, acc.v[i][j][e]); });
 }
 
+// ---------------------------------------------------------------------------
 // Partial exchange between workgroups.  Partials are written and read with
-// device-scope (sc1) 128-bit buffer accesses, which the gfx950 memory hierarchy
-// keeps coherent across the XCDs' separate L2 caches without writing back or
-// invalidating whole caches; the writer waits for its stores to complete before
-// the flag or counter is raised, and the reader only loads after observing it.
+// device-scope (sc1) buffer accesses, which the gfx950 memory hierarchy keeps
+// coherent across the XCDs' separate L2 caches without writing back or
+// invalidating whole caches; the writer waits for its stores to complete
+// before the flag or counter is raised, and the reader only loads after
+// observing it.
+// ---------------------------------------------------------------------------
 constexpr int CPOL_DEVICE = 16;   // cache-policy bits: sc1 (device scope)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t span(const void *base, uint32_t bytes) {
@@ -510,40 +550,43 @@ __device__ __forceinline__ float get_coherent(const float *p) {
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
 
 // Stream-K partial slot (64 KiB) in register-native order: for accumulator block
-// b and element quad e4, the 64 lanes of a wave move 1 KiB of contiguous memory.
-__device__ __forceinline__ uint32_t slot_off(int wave, int b, int e4, int lane) {
-    return (uint32_t)((((wave * 4 + b) * 4 + e4) * 64 + lane) * 16);
+// b and element quad e4, the 64 lanes of a quadrant wave move 1 KiB of
+// contiguous memory.
+__device__ __forceinline__ uint32_t slot_off(int quad, int b, int e4, int lane) {
+    return (uint32_t)((((quad * 4 + b) * 4 + e4) * 64 + lane) * 16);
 }
 
+template <int NW>
 __device__ __forceinline__ void put_slot(float *slot, const Acc &acc) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const Role<NW> w;
+    if (w.kh != 0) return;
     const __amdgpu_buffer_rsrc_t r = span(slot, BM * BN * 4);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
             const f32x16 &v = acc.v[b >> 1][b & 1];
-            put4_coherent(r, slot_off(wave, b, e4, lane),
+            put4_coherent(r, slot_off(w.quad, b, e4, w.lane),
                           f32x4{v[4 * e4], v[4 * e4 + 1], v[4 * e4 + 2], v[4 * e4 + 3]});
         }
 }
 
+template <int NW>
 __device__ __forceinline__ void add_slot(const float *slot, Acc &acc) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const Role<NW> w;
+    if (w.kh != 0) return;
     const __amdgpu_buffer_rsrc_t r = span(slot, BM * BN * 4);
-    f32x4 x[4][4];
+    // one accumulator block (four 1 KiB loads) per round keeps register pressure bounded
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 4; ++b) {
+        f32x4 x[4];
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) x[b][e4] = get4_coherent(r, slot_off(wave, b, e4, lane));
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
+        for (int e4 = 0; e4 < 4; ++e4) x[e4] = get4_coherent(r, slot_off(w.quad, b, e4, w.lane));
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4)
 #pragma unroll
-            for (int y = 0; y < 4; ++y) acc.v[b >> 1][b & 1][4 * e4 + y] += x[b][e4][y];
+            for (int y = 0; y < 4; ++y) acc.v[b >> 1][b & 1][4 * e4 + y] += x[e4][y];
+    }
 }
 
 // Poll `flag` until it holds `epoch` (one thread).  Gives up after `limit`
@@ -560,7 +603,9 @@ __device__ __forceinline__ void wait_flag(const uint32_t *flag, uint32_t epoch, 
     }
 }
 
-// Trace helpers (thread 0 only; active only when p.trace is set).
+// ---------------------------------------------------------------------------
+// Debug trace (thread 0 only; active only when p.trace is set)
+// ---------------------------------------------------------------------------
 __device__ __forceinline__ int *trace_worker(const KParams &p, int w) {
     return p.trace + 8 + (size_t)w * (1 + 4 * p.trace_maxseg);
 }
@@ -615,9 +660,9 @@ struct WgClock {
 // ---------------------------------------------------------------------------
 // Data-parallel: one workgroup per tile of [tile_base, tile_base + ntiles).
 // ---------------------------------------------------------------------------
-template <int DT, int BL>
-__global__ __launch_bounds__(NT, 2) void gemm_dp(KParams p) {
-    __shared__ __attribute__((aligned(16))) char lds[NS_GRID * STAGE_BYTES];
+template <int DT, int BL, int NS, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_dp(KParams p) {
+    __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_BYTES];
     const WgClock clk(p);
     const int w = worker_of(p, p.ntiles);
     const int tile = p.tile_base + w;
@@ -625,9 +670,10 @@ __global__ __launch_bounds__(NT, 2) void gemm_dp(KParams p) {
     tile_origin(p, tile, m0, n0);
     Acc acc;
     zero_acc(acc);
-    mac_loop<DT, BL, NS_GRID>(p, lds, m0, n0, 0, p.ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
+    mac_loop<DT, BL, NS, NW>(p, lds, m0, n0, 0, p.ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
+    merge_k_halves<NW>(acc, lds);
     clk.mark(p, 0);
-    store_tile(p.C, m0, n0, p.M, p.N, acc, lds);
+    store_tile<NW>(p.C, m0, n0, p.M, p.N, acc, lds);
     trace_segment(p, p.worker_base + w, 0, tile, 0, p.ipt, 0);
     trace_folded(p, tile, 0, p.worker_base + w);
     clk.done(p);
@@ -636,9 +682,10 @@ __global__ __launch_bounds__(NT, 2) void gemm_dp(KParams p) {
 // ---------------------------------------------------------------------------
 // Split-K: worker w = tile * S + s covers k-iterations [s P / S, (s+1) P / S).
 // ---------------------------------------------------------------------------
-template <int DT, int BL>
-__global__ __launch_bounds__(NT, 2) void gemm_splitk(KParams p) {
-    __shared__ __attribute__((aligned(16))) char lds[NS_GRID * STAGE_BYTES];
+template <int DT, int BL, int NS, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
+    constexpr int NT = Role<NW>::NT, QPT = BM * BN / 4 / NT;
+    __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_BYTES];
     __shared__ int last_arriver;
     const WgClock clk(p);
     const int S = p.splits;
@@ -649,11 +696,12 @@ __global__ __launch_bounds__(NT, 2) void gemm_splitk(KParams p) {
     tile_origin(p, tile, m0, n0);
     Acc acc;
     zero_acc(acc);
-    mac_loop<DT, BL, NS_GRID>(p, lds, m0, n0, k0, k1, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
+    mac_loop<DT, BL, NS, NW>(p, lds, m0, n0, k0, k1, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
+    merge_k_halves<NW>(acc, lds);
     clk.mark(p, 0);
     trace_segment(p, w, 0, tile, k0, k1, S == 1 ? 0 : (s == 0 ? 1 : 2));
     if (S == 1) {
-        store_tile(p.C, m0, n0, p.M, p.N, acc, lds);
+        store_tile<NW>(p.C, m0, n0, p.M, p.N, acc, lds);
         trace_folded(p, tile, 0, w);
         clk.done(p);
         return;
@@ -662,35 +710,36 @@ __global__ __launch_bounds__(NT, 2) void gemm_splitk(KParams p) {
     // with device-scope stores (LDS keeps the copy this workgroup may fold itself)
     const size_t mn = (size_t)p.M * p.N;
     float *stg = reinterpret_cast<float *>(lds);
-    acc_to_lds(stg, acc);
+    acc_to_lds<NW>(stg, acc);
     __syncthreads();
     const size_t org = (size_t)m0 * p.N + n0;                 // tile origin within [M,N]
     const uint32_t span_bytes = (uint32_t)(((size_t)(min(BM, p.M - m0) - 1) * p.N + min(BN, p.N - n0)) * 4);
     auto quad_off = [&](int r, int c) { return (uint32_t)(((size_t)r * p.N + c) * 4); };
-    auto staged = [&](int r, int c) { return *reinterpret_cast<const f32x4 *>(stg + r * EPI_LD + (c ^ epi_swz(r))); };
     {
         const __amdgpu_buffer_rsrc_t rp = span(p.part + (size_t)s * mn + org, span_bytes);
         float *Ps = p.part + (size_t)s * mn;
-        for_each_quad(m0, n0, p.M, p.N, [&](int, int r, int c, size_t off, int nv) {
-            const f32x4 v = staged(r, c);
-            if (nv == 4) put4_coherent(rp, quad_off(r, c), v);
-            else for (int x = 0; x < nv; ++x) put_coherent(Ps + off + x, v[x]);
+        for_each_quad<NW>(m0, n0, p.M, p.N, [&](int, int r, int c, size_t off, int nv) {
+            const f32x4 v = staged_quad(stg, r, c);
+            if (nv == 4) {
+                put4_coherent(rp, quad_off(r, c), v);
+            } else {
+                for (int x = 0; x < nv; ++x) put_coherent(Ps + off + x, v[x]);
+            }
         });
     }
     wait_vm_all();                 // this wave's partial stores are complete
     __syncthreads();               // ... and every other wave's
     clk.mark(p, 1);
-    int *last = &last_arriver;
     if (threadIdx.x == 0) {
         const uint32_t before =
             __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool is_last = before == (uint32_t)(S - 1);
         if (is_last)   // every split has arrived: reset for the next call
             __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *last = is_last ? 1 : 0;
+        last_arriver = is_last ? 1 : 0;
     }
     __syncthreads();
-    if (!*last) {
+    if (!last_arriver) {
         clk.done(p);
         return;
     }
@@ -698,7 +747,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_splitk(KParams p) {
     // workgroup's own split from LDS.  Per round: 4 quads of the thread, and the
     // loads of up to 4 partials for them in flight before they are added.
     const bool vec = (p.N & 3) == 0;
-    for (int q0 = 0; q0 < 16; q0 += 4) {
+    for (int q0 = 0; q0 < QPT; q0 += 4) {
         int rr[4], cc[4];
         bool ok[4];
 #pragma unroll
@@ -737,7 +786,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_splitk(KParams p) {
                 if (t >= S) break;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const f32x4 x = (t == s) ? staged(rr[g], cc[g]) : buf[tt][g];
+                    const f32x4 x = (t == s) ? staged_quad(stg, rr[g], cc[g]) : buf[tt][g];
                     sum[g] = (t == 0) ? x : sum[g] + x;
                 }
             }
@@ -752,11 +801,11 @@ __global__ __launch_bounds__(NT, 2) void gemm_splitk(KParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Stream-K: persistent; workgroup b runs unit perm[b] (default b).
+// Stream-K: persistent; workgroup b runs unit worker_of(b).
 // ---------------------------------------------------------------------------
-template <int DT, int BL, bool ATOMIC>
-__global__ __launch_bounds__(NT, 1) void gemm_streamk(KParams p) {
-    __shared__ __attribute__((aligned(16))) char lds[NS_STREAMK * STAGE_BYTES];
+template <int DT, int BL, int NS, int NW, bool ATOMIC>
+__global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
+    __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_BYTES];
     const WgClock clk(p);
     const int u = worker_of(p, p.units);
     const int ipt = p.ipt;
@@ -778,17 +827,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_streamk(KParams p) {
         // meet in this tile then stream the same slabs close together in time
         const int owner = unit_of(tb, p.q, p.big);
         const int rot = (tb - unit_start(owner, p.q, p.big)) % ipt;
-        mac_loop<DT, BL, NS_STREAMK>(p, lds, m0, n0, k0, k1, rot, acc, p.trace ? trace_cov(p, tile) : nullptr);
+        mac_loop<DT, BL, NS, NW>(p, lds, m0, n0, k0, k1, rot, acc, p.trace ? trace_cov(p, tile) : nullptr);
+        merge_k_halves<NW>(acc, lds);
         clk.mark(p, 2 * min(nseg, 1));
         trace_segment(p, u, nseg++, tile, k0, k1, role);
         if (role == 0) {
-            store_tile(p.C, m0, n0, p.M, p.N, acc, lds);
+            store_tile<NW>(p.C, m0, n0, p.M, p.N, acc, lds);
             trace_folded(p, tile, 0, u);
         } else if constexpr (ATOMIC) {
-            atomic_add_c(p.C, m0, n0, p.M, p.N, acc);
+            atomic_add_c<NW>(p.C, m0, n0, p.M, p.N, acc);
         } else if (role == 2) {
             // starts mid-tile: publish the partial, then the flag
-            put_slot(p.part + (size_t)u * (BM * BN), acc);
+            put_slot<NW>(p.part + (size_t)u * (BM * BN), acc);
             wait_vm_all();                 // this wave's partial stores are complete
             __syncthreads();               // ... and every other wave's
             if (threadIdx.x == 0 && !(p.debug & GEMM_DEBUG_NO_PUBLISH))
@@ -802,10 +852,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_streamk(KParams p) {
                 if (unit_start(v, p.q, p.big) >= tile_end) break;
                 if (threadIdx.x == 0) wait_flag(p.flags + v, p.epoch, p.spin_limit, p.status);
                 __syncthreads();
-                add_slot(p.part + (size_t)v * (BM * BN), acc);
+                add_slot<NW>(p.part + (size_t)v * (BM * BN), acc);
                 trace_folded(p, tile, pos_fold++, v);
             }
-            store_tile(p.C, m0, n0, p.M, p.N, acc, lds);
+            store_tile<NW>(p.C, m0, n0, p.M, p.N, acc, lds);
         }
         clk.mark(p, 2 * min(nseg - 1, 1) + 1);
         pos = tb + k1;
@@ -832,26 +882,35 @@ __global__ void zero_words(uint32_t *p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// Host-side dispatch
+// Host-side dispatch.  Kernel shapes (stages x waves):
+//   DP            2 stages x 4 waves  (64 KiB LDS: two workgroups share a CU)
+//   Split-K       4 stages x 8 waves  (128 KiB LDS; the same per-segment
+//                 accumulation order as Stream-K, so the two agree bit for bit
+//                 whenever their segments coincide)
+//   Stream-K      4 stages x 8 waves  (128 KiB LDS: one persistent workgroup per CU)
 // ---------------------------------------------------------------------------
 namespace {
 
 typedef void (*KernelFn)(KParams);
 
+struct Shape {
+    int ns, nw;
+};
+
 template <int DT, int BL>
-KernelFn pick(int kmode) {
+KernelFn pick(int kmode, Shape &shape) {
     switch (kmode) {
-    case K_DP: return gemm_dp<DT, BL>;
-    case K_SPLITK: return gemm_splitk<DT, BL>;
-    case K_SK: return gemm_streamk<DT, BL, false>;
-    case K_SK_ATOMIC: return gemm_streamk<DT, BL, true>;
+    case K_DP: shape = {2, 4}; return gemm_dp<DT, BL, 2, 4>;
+    case K_SPLITK: shape = {4, 8}; return gemm_splitk<DT, BL, 4, 8>;
+    case K_SK: shape = {4, 8}; return gemm_streamk<DT, BL, 4, 8, false>;
+    case K_SK_ATOMIC: shape = {4, 8}; return gemm_streamk<DT, BL, 4, 8, true>;
     default: return nullptr;
     }
 }
 
-KernelFn kernel_for(int dtype, int blayout, int kmode) {
-    if (dtype == 0) return blayout == 0 ? pick<0, 0>(kmode) : pick<0, 1>(kmode);
-    if (dtype == 1) return blayout == 0 ? pick<1, 0>(kmode) : pick<1, 1>(kmode);
+KernelFn kernel_for(int dtype, int blayout, int kmode, Shape &shape) {
+    if (dtype == 0) return blayout == 0 ? pick<0, 0>(kmode, shape) : pick<0, 1>(kmode, shape);
+    if (dtype == 1) return blayout == 0 ? pick<1, 0>(kmode, shape) : pick<1, 1>(kmode, shape);
     return nullptr;
 }
 
@@ -859,9 +918,10 @@ KernelFn kernel_for(int dtype, int blayout, int kmode) {
 
 hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParams &p,
                        hipStream_t stream) {
-    KernelFn fn = kernel_for(dtype, blayout, kmode);
+    Shape shape{0, 0};
+    KernelFn fn = kernel_for(dtype, blayout, kmode, shape);
     if (!fn || grid <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * shape.nw), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -876,9 +936,11 @@ hipError_t launch_zero(void *ptr, int64_t n_words, hipStream_t stream) {
 }
 
 hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int *out) {
-    KernelFn fn = kernel_for(dtype, blayout, kmode);
+    Shape shape{0, 0};
+    KernelFn fn = kernel_for(dtype, blayout, kmode, shape);
     if (!fn) return hipErrorInvalidValue;
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, reinterpret_cast<const void *>(fn), NT, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, reinterpret_cast<const void *>(fn),
+                                                        64 * shape.nw, 0);
 }
 
 }  // namespace dgw
