@@ -160,6 +160,24 @@ def kernel_name(dg, plan, w):
     return f"{kind}<{w.dtype}, {lay}{fix}>"
 
 
+def measured_traffic(profile: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary `profile` (scaled by a plain copy of known size), or None
+    when there is none or the kernel source has changed since it was taken."""
+    import hashlib
+
+    path = ROOT / "profiles" / "traffic.json"
+    if not path.exists():
+        return None
+    entry = json.loads(path.read_text()).get(profile)
+    if not entry or kernel not in entry.get("kernel", ""):
+        return None
+    src = ROOT / "dense_gemm_work_amd" / "csrc" / "gemm_kernels.hip"
+    if hashlib.sha256(src.read_bytes()).hexdigest() != entry.get("source_sha256"):
+        return None
+    return int(entry["bytes"])
+
+
 def cpu_baseline(w, A, B):
     from oracle import gemm as og
 
@@ -269,7 +287,9 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(f"gemm_streamk_bf16_kn_{w.M}x{w.N}x{w.K}", "gemm_streamk<0, 0,")
+            if call.plan.decision == dg.GEMM_STREAMK and not call.plan.atomic and w.dtype == "bf16"
+            and w.b_layout == "kn" else None,
             "kernel_mean_us": round(kern_ms * 1e3, 3),
         },
         "cpu_baseline": cpu,
