@@ -4,24 +4,26 @@
 // fp32 output tile at a time; one "MAC-loop iteration" (Split-K/Stream-K book
 // chapter, glossary) is a 64-wide step of K: the A slab [128 x 64] and the
 // B slab [64 x 128] are staged in LDS and the workgroup issues 64
-// v_mfma_f32_32x32x16_{bf16,f16} on them.  Four "quadrant" waves in a 2x2
-// arrangement own the four 64x64 quarters of the tile.  A workgroup has NW = 4
-// waves (one per SIMD) or NW = 8 waves (two per SIMD): with 8, the two waves of
-// a SIMD own the same quarter and split each iteration's four 16-wide k-steps
-// between them, and their accumulators are added once per segment.  Eight
-// waves keep a single workgroup per CU (the persistent Stream-K kernel) from
-// idling its matrix cores at every barrier and LDS round trip.
+// v_mfma_f32_32x32x16_{bf16,f16} on them.  Every kernel runs eight waves (two
+// per SIMD): waves w and w + 4 own the same 64x64 quarter of the tile and
+// split each iteration's four 16-wide k-steps between them; after a segment
+// they swap halves through LDS so that each holds the complete sums of one
+// 32-row block of the quarter.
 //
 // Operands move global -> LDS with buffer_load ... lds (16 bytes per lane, no
-// register round trip), in NS LDS stages: the loads of iteration i + NS are
-// issued as soon as stage i has been read (CUTLASS optimisation guide,
-// "Software Pipelining").  A [M,K] and B [N,K] are stored k-contiguous (one
-// 128-byte row of 64 values per row), the 16-byte chunks of row r XOR-swizzled
-// by (r ^ r>>3) & 7; B [K,N] is stored as k-rows of 128 n-values, chunk c of
-// k-row r at c ^ kn_swz(r), and read with ds_read_b64_tr_b16, which hands every
-// MFMA lane four consecutive k of one column.  Fragment reads run one k-step
-// ahead of the MFMAs, also across the stage barrier.
-//
+// register round trip) into four LDS stages (A slabs of all stages first, then
+// the B slabs, so every fragment read is a base register plus an immediate
+// offset).  Iteration i waits for the loads of iteration i + 1, synchronises
+// the workgroup once, issues the loads of iteration i + 4 into the stage just
+// consumed, reads all fragments of iteration i + 1 into a second register set
+// and issues the MFMAs of iteration i, which therefore never wait for LDS
+// (CUTLASS optimisation guide, "Software Pipelining": multistage shared-memory
+// pipeline plus register double buffering).  A [M,K] and B [N,K] rows are
+// stored k-contiguous (128 bytes per row), 16-byte chunks XOR-swizzled by
+// (r & 7) ^ ((r >> 3) & 3); B [K,N] is stored as k-rows of 128 n-values, chunk
+// c of k-row r at c ^ nswz(r), and read with ds_read_b64_tr_b16, which hands
+// every MFMA lane four consecutive k of one column.
+
 // Epilogues (book chapter, Stream-K paragraph after the glossary; Case 4's
 // reduction modes; docc StreamK page):
 //   K_DP         store the tile.
@@ -58,11 +60,11 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = GEMM_BK;
 constexpr int SLAB = BM * BK;                 // 16-bit values per operand slab (A and B alike)
 constexpr int STAGE_BYTES = 2 * SLAB * 2;     // A slab then B slab: 32 KiB
-constexpr int SLAB_DMAS = SLAB * 2 / 1024;    // 1 KiB wave loads per slab: 16
 
 struct Acc {
     f32x16 v[2][2];   // [i: 32-row block][j: 32-column block] of the wave's 64x64 quarter
@@ -72,12 +74,10 @@ struct Acc {
 template <int NW>
 struct Role {
     static constexpr int NT = 64 * NW;              // threads
-    static constexpr int KSTEPS = 4 * 4 / NW;       // 16-wide k-steps per wave and stage: 4 or 2
-    static constexpr int DPW = SLAB_DMAS / NW;      // loads per wave and operand slab: 4 or 2
     int lane, wave, quad, wm, wn, kh;
     __device__ __forceinline__ Role() {
         lane = threadIdx.x & 63;
-        wave = threadIdx.x >> 6;
+        wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
         quad = wave & 3;
         wm = quad >> 1;
         wn = quad & 1;
@@ -85,12 +85,19 @@ struct Role {
     }
 };
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// A [M,K] and B [N,K] slabs in LDS: row r (64 values = 128 bytes = 8 chunks of
+// 16 bytes) at r * 128, logical chunk c at physical chunk c ^ kswz(r).  Any 8
+// consecutive rows read at one logical chunk then cover 8 distinct chunk
+// positions, and 16 consecutive rows all 64 banks, so the 32-row fragment reads
+// are conflict free; rows 32 apart share the swizzle, so a second 32-row block
+// is a constant 4 KiB further.
+__device__ __forceinline__ int kswz(int r) { return (r & 7) ^ ((r >> 3) & 3); }
 
-// B [K,N] rows in LDS are 256 bytes (128 n-values); 16-byte chunk c of k-row r
-// lives at chunk c ^ kn_swz(r).  The four k-rows read together by a 16-lane
-// transpose read then fall on distinct banks.
-__device__ __forceinline__ int kn_swz(int r) { return ((r & 1) << 2) ^ ((r & 2) * 5); }
+// B [K,N] slabs: k-row r (128 n-values = 256 bytes = 16 chunks) at r * 256,
+// chunk c at c ^ nswz(r).  The four k-rows read together by a 16-lane transpose
+// read then fall on distinct banks; the swizzle depends on r % 4 only, so other
+// k-steps and the second k-half of a fragment are constant offsets.
+__device__ __forceinline__ int nswz(int r) { return ((r & 1) << 2) ^ ((r & 2) * 5); }
 
 template <int DT>
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
@@ -125,258 +132,331 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
 }
 
 // Issued as inline assembly so that the compiler does not wait for it before
-// unrelated LDS reads; completion is awaited explicitly with wait_stage().
-__device__ __forceinline__ void dma16(i32x4 rsrc, const void *lds, uint32_t voff) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)reinterpret_cast<uintptr_t>((const lds_void *)lds));
+// unrelated LDS reads; completion is awaited explicitly (wait_vm_lgkm).
+// `lds_addr` is the wave-uniform LDS byte address of the 1 KiB destination.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
-                 : "s"(m0), "v"(voff), "s"(rsrc)
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc)
                  : "memory");
 }
 
-// Wait until at most `n` vector-memory operations of this wave are outstanding
-// and all of its LDS reads have returned, then synchronise the workgroup.
-__device__ __forceinline__ void wait_stage(int n) {
-    // s_waitcnt on gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
-#define DGW_WAIT(x) (((x) & 15) | (((x) >> 4) << 14) | (7 << 4) | (0 << 8))
-    switch (n) {
-    case 4: __builtin_amdgcn_s_waitcnt(DGW_WAIT(4)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(DGW_WAIT(8)); break;
-    case 12: __builtin_amdgcn_s_waitcnt(DGW_WAIT(12)); break;
-    case 16: __builtin_amdgcn_s_waitcnt(DGW_WAIT(16)); break;
-    case 24: __builtin_amdgcn_s_waitcnt(DGW_WAIT(24)); break;
-    default: __builtin_amdgcn_s_waitcnt(DGW_WAIT(0)); break;
-    }
-#undef DGW_WAIT
-    asm volatile("s_barrier" ::: "memory");
+// Wait until at most N vector-memory operations of this wave are outstanding
+// and all of its LDS reads have returned.
+// s_waitcnt on gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
-
-// Per-thread load plan of one tile: the wave's DPW instructions per slab.
-template <int BL, int NW>
-struct LoadPlan {
-    static constexpr int DPW = Role<NW>::DPW;
-    const char *a_base;      // A + m0 * K (bytes)
-    const char *b_base;      // B + n0 * K ([N,K]) or B + n0 ([K,N]) (bytes)
-    uint32_t a_rows_bytes;   // valid A rows * K * 2
-    uint32_t b_rows_bytes;   // [N,K]: valid B rows * K * 2
-    uint32_t a_off[DPW];     // byte offsets at k-iteration 0
-    uint32_t b_off[DPW];
-    int a_kc[DPW];           // first k of the lane's chunk (ragged-K mask)
-    int b_kc[DPW];           // [N,K]: first k of the chunk; [K,N]: the k-row
-    bool b_nok[DPW];         // [K,N]: chunk beyond N
-    int first;               // the wave's first instruction of a slab
-};
-
-template <int BL, int NW>
-__device__ __forceinline__ void make_load_plan(LoadPlan<BL, NW> &lp, const KParams &p, int m0, int n0) {
-    constexpr int DPW = Role<NW>::DPW;
-    const Role<NW> w;
-    const int K = p.K, N = p.N;
-    lp.first = w.wave * DPW;
-    lp.a_base = reinterpret_cast<const char *>(p.A) + (size_t)m0 * K * 2;
-    lp.a_rows_bytes = (uint32_t)(min(BM, p.M - m0) * K * 2);
-#pragma unroll
-    for (int i = 0; i < DPW; ++i) {
-        const int r = (lp.first + i) * 8 + (w.lane >> 3);      // row of the 128 x 64 slab
-        const int c = (w.lane & 7) ^ swz(r);                   // logical 8-value chunk
-        lp.a_off[i] = (uint32_t)(r * K + c * 8) * 2;
-        lp.a_kc[i] = c * 8;
-    }
-    if constexpr (BL == 1) {
-        lp.b_base = reinterpret_cast<const char *>(p.B) + (size_t)n0 * K * 2;
-        lp.b_rows_bytes = (uint32_t)(min(BN, N - n0) * K * 2);
-#pragma unroll
-        for (int i = 0; i < DPW; ++i) {
-            const int r = (lp.first + i) * 8 + (w.lane >> 3);
-            const int c = (w.lane & 7) ^ swz(r);
-            lp.b_off[i] = (uint32_t)(r * K + c * 8) * 2;
-            lp.b_kc[i] = c * 8;
-            lp.b_nok[i] = false;
-        }
-    } else {
-        lp.b_base = reinterpret_cast<const char *>(p.B) + (size_t)n0 * 2;
-        lp.b_rows_bytes = 0;
-#pragma unroll
-        for (int i = 0; i < DPW; ++i) {
-            const int r = (lp.first + i) * 4 + (w.lane >> 4);       // k-row of the 64 x 128 slab
-            const int c = (w.lane & 15) ^ kn_swz(r);                // logical 8-value n chunk
-            lp.b_off[i] = (uint32_t)(r * N + c * 8) * 2;
-            lp.b_kc[i] = r;
-            lp.b_nok[i] = n0 + c * 8 >= N;
-        }
+// The same with N known only at run time (0 <= n <= 3 stages' worth).
+template <int DPI>
+__device__ __forceinline__ void wait_vm_lgkm_stages(int stages) {
+    switch (stages) {
+    case 3: wait_vm_lgkm<3 * DPI>(); break;
+    case 2: wait_vm_lgkm<2 * DPI>(); break;
+    case 1: wait_vm_lgkm<1 * DPI>(); break;
+    default: wait_vm_lgkm<0>(); break;
     }
 }
+__device__ __forceinline__ void wait_stage0() {
+    wait_vm_lgkm<0>();
+    __builtin_amdgcn_s_barrier();
+}
 
-// Issue the wave's loads of physical K-slab `slab` into `stage` (A slab then B slab).
-template <int BL, int NW>
-__device__ __forceinline__ void issue_loads(const LoadPlan<BL, NW> &lp, const KParams &p, char *stage,
-                                            int slab) {
-    constexpr int DPW = Role<NW>::DPW;
-    const int kb = slab * BK;
-    // A: base advances along K; rows beyond M fall outside [0, a_rows_bytes - 2 kb)
-    const i32x4 ra = make_rsrc(lp.a_base + (size_t)kb * 2, lp.a_rows_bytes - kb * 2);
-#pragma unroll
-    for (int i = 0; i < DPW; ++i) {
-        const uint32_t off = (kb + lp.a_kc[i] < p.K) ? lp.a_off[i] : OOB;
-        dma16(ra, stage + (lp.first + i) * 1024, off);
-    }
-    if constexpr (BL == 1) {
-        const i32x4 rb = make_rsrc(lp.b_base + (size_t)kb * 2, lp.b_rows_bytes - kb * 2);
-#pragma unroll
-        for (int i = 0; i < DPW; ++i) {
-            const uint32_t off = (kb + lp.b_kc[i] < p.K) ? lp.b_off[i] : OOB;
-            dma16(rb, stage + SLAB * 2 + (lp.first + i) * 1024, off);
-        }
-    } else {
-        const int krows = min(BK, p.K - kb);
-        const i32x4 rb = make_rsrc(lp.b_base + (size_t)kb * p.N * 2, (uint32_t)(krows * p.N * 2));
-#pragma unroll
-        for (int i = 0; i < DPW; ++i) {
-            const uint32_t off = (lp.b_kc[i] < krows && !lp.b_nok[i]) ? lp.b_off[i] : OOB;
-            dma16(rb, stage + SLAB * 2 + (lp.first + i) * 1024, off);
-        }
-    }
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_b128(uint32_t addr) {
+    return *reinterpret_cast<const lds_u32x4 *>(static_cast<uintptr_t>(addr + OFF));
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_tr16(uint32_t addr) {
+    return __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_v4i16 *>(static_cast<uintptr_t>(addr + OFF))));
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core work: per 16-wide k-step (kk) a quadrant wave reads its two A and
-// two B operand fragments and issues four MFMAs.
+// The mainloop.  One "MAC-loop iteration" is a 64-wide step of K: the A slab
+// [128 x 64] and B slab [64 x 128] of the iteration are in LDS stage i % NS
+// (A slabs of all stages in [0, NS * 16 KiB), B slabs after them, so every
+// fragment read is a base register plus an immediate), and each wave issues
+// 4 * KSW MFMAs on them: its 64x64 quarter over KSW of the iteration's four
+// 16-wide k-steps.
+//
+// Iteration i, per wave: wait until its own loads of iteration i + 1 landed and
+// its fragment reads of iteration i returned; barrier (every wave's loads of
+// i + 1 landed, every wave finished reading stage i); issue the loads of
+// iteration i + NS into stage i; read all fragments of iteration i + 1 into the
+// other register buffer; issue the MFMAs of iteration i.  The MFMAs never wait
+// for LDS, and the fragment reads have a whole iteration to return.
 // ---------------------------------------------------------------------------
-struct Frag {
-    u32x4 a[2];   // rows wm*64 + {0, 32} + lane % 32, k = 16 kk + 8 (lane / 32) + 0..7
-    u32x4 b[2];   // cols wn*64 + {0, 32} + lane % 32, same k
-};
+constexpr int SLAB_BYTES = BM * BK * 2;   // 16 KiB
 
-template <int BL, int NW>
-__device__ __forceinline__ void load_frag(const Role<NW> &w, const char *stage, int kk, Frag &f) {
-    const char *As = stage;
-    const char *Bs = stage + SLAB * 2;
-    const int hk = w.lane >> 5;
-    const int ch = kk * 2 + hk;
+template <int DT, int BL, int NS, int NW>
+struct MainLoop {
+    static constexpr int KSW = 16 / NW;          // k-steps per wave and iteration
+    static constexpr int DPW = 16 / NW;          // loads per wave and operand slab
+    static constexpr int DPI = 2 * DPW;          // loads per wave and iteration
+    static constexpr int BREG = NS * SLAB_BYTES; // start of the B slabs
+    static_assert(NS == 4, "the unrolled loop body assumes four stages");
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
+
+    const KParams &p;
+    uint32_t lds0;
+    int lane, wave, kh;
+    // fragment read addresses (stage 0): A block 0 per k-step of the wave;
+    // B [N,K]: block 0 per k-step; B [K,N]: column block jb at the wave's first k-step
+    uint32_t aoff[KSW], boff[KSW > 2 ? KSW : 2];
+    // per-lane global byte offsets of the wave's loads at k-slab 0
+    uint32_t adma[DPW], bdma[DPW];
+    int a_kc[DPW], b_kc[DPW];     // first k of the lane's chunk / B [K,N]: k-row of the lane
+    const char *a_base, *b_base;
+    uint32_t a_rows_bytes, b_rows_bytes;
+
+    __device__ __forceinline__ MainLoop(const KParams &p_, char *lds, int m0, int n0) : p(p_) {
+        lds0 = (uint32_t)reinterpret_cast<uintptr_t>((const lds_void *)lds);
+        lane = threadIdx.x & 63;
+        wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+        const int quad = wave & 3, wm = quad >> 1, wn = quad & 1;
+        kh = wave >> 2;
+        const int K = p.K, N = p.N;
+        const int r32 = lane & 31, hk = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r = w.wm * 64 + i * 32 + (w.lane & 31);
-        f.a[i] = *reinterpret_cast<const u32x4 *>(As + r * 128 + ((ch ^ swz(r)) << 4));
-    }
-    if constexpr (BL == 1) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = w.wn * 64 + j * 32 + (w.lane & 31);
-            f.b[j] = *reinterpret_cast<const u32x4 *>(Bs + r * 128 + ((ch ^ swz(r)) << 4));
+        for (int j = 0; j < KSW; ++j) {
+            const int kk = kh * KSW + j;
+            const uint32_t rowpart = (uint32_t)(r32 * 128 + ((((2 * kk + hk) ^ kswz(r32)) & 7) << 4));
+            aoff[j] = lds0 + wm * 8192 + rowpart;
+            if constexpr (BL == 1) boff[j] = lds0 + BREG + wn * 8192 + rowpart;
         }
-    } else {
-        // transpose reads: lane l of a 16-lane group names 4 n-values of one k-row;
-        // it receives 4 k-values of column n = l % 32 (two reads give 8 k)
+        if constexpr (BL == 0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = w.wn * 64 + j * 32 + ((w.lane >> 4) & 1) * 16 + 4 * (w.lane & 3);
-            u32x2 h[2];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int r = kk * 16 + 8 * hk + 4 * half + ((w.lane & 15) >> 2);
-                const char *addr = Bs + r * 256 + ((((n >> 3) ^ kn_swz(r)) << 4) | ((n & 7) << 1));
-                const v4i16 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)addr);
-                h[half] = __builtin_bit_cast(u32x2, t);
+            for (int jb = 0; jb < 2; ++jb) {
+                const int n = wn * 64 + jb * 32 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+                const int r = kh * KSW * 16 + 8 * hk + ((lane & 15) >> 2);
+                boff[jb] = lds0 + BREG + r * 256 + ((((n >> 3) ^ nswz(r)) & 15) << 4) + ((n & 7) << 1);
             }
-            f.b[j] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+        }
+        const int first = wave * DPW;
+        a_base = reinterpret_cast<const char *>(p.A) + (size_t)m0 * K * 2;
+        a_rows_bytes = (uint32_t)(min(BM, p.M - m0) * K * 2);
+#pragma unroll
+        for (int x = 0; x < DPW; ++x) {
+            const int r = 8 * (first + x) + (lane >> 3);
+            const int c = (lane & 7) ^ kswz(r);
+            adma[x] = (uint32_t)(r * K + 8 * c) * 2;
+            a_kc[x] = 8 * c;
+            if constexpr (BL == 1) {
+                bdma[x] = adma[x];
+                b_kc[x] = 8 * c;
+            } else {
+                const int rb = 4 * (first + x) + (lane >> 4);
+                const int cb = (lane & 15) ^ nswz(rb);
+                // chunks beyond N (last tile column only) always read zeros
+                bdma[x] = n0 + 8 * cb >= N ? OOB : (uint32_t)(rb * N + 8 * cb) * 2;
+                b_kc[x] = rb;
+            }
+        }
+        if constexpr (BL == 1) {
+            b_base = reinterpret_cast<const char *>(p.B) + (size_t)n0 * K * 2;
+            b_rows_bytes = (uint32_t)(min(BN, N - n0) * K * 2);
+        } else {
+            b_base = reinterpret_cast<const char *>(p.B) + (size_t)n0 * 2;
+            b_rows_bytes = 0;
         }
     }
-}
 
-template <int DT>
-__device__ __forceinline__ void mma(const Frag &f, Acc &acc) {
-    acc.v[0][0] = mfma<DT>(f.a[0], f.b[0], acc.v[0][0]);
-    acc.v[0][1] = mfma<DT>(f.a[0], f.b[1], acc.v[0][1]);
-    acc.v[1][0] = mfma<DT>(f.a[1], f.b[0], acc.v[1][0]);
-    acc.v[1][1] = mfma<DT>(f.a[1], f.b[1], acc.v[1][1]);
-}
+    // Loads of physical K-slab `slab` into stage `st`.  RAGGED (K not a multiple
+    // of 64): lanes whose chunk starts at or beyond K read zeros.
+    template <bool RAGGED>
+    __device__ __forceinline__ void issue(int slab, int st) const {
+        const int kb = slab * BK;
+        const int first = wave * DPW;
+        const i32x4 ra = make_rsrc(a_base + (size_t)kb * 2, a_rows_bytes - kb * 2);
+        i32x4 rb;
+        int krows = BK;
+        if constexpr (BL == 1) {
+            rb = make_rsrc(b_base + (size_t)kb * 2, b_rows_bytes - kb * 2);
+        } else {
+            krows = min(BK, p.K - kb);   // k-rows beyond K fall outside the range
+            rb = make_rsrc(b_base + (size_t)kb * p.N * 2, (uint32_t)(krows * p.N * 2));
+        }
+        const uint32_t a_dst = lds0 + st * SLAB_BYTES + first * 1024;
+        const uint32_t b_dst = lds0 + BREG + st * SLAB_BYTES + first * 1024;
+#pragma unroll
+        for (int x = 0; x < DPW; ++x) dma16(ra, a_dst + x * 1024, !RAGGED || kb + a_kc[x] < p.K ? adma[x] : OOB);
+#pragma unroll
+        for (int x = 0; x < DPW; ++x) {
+            uint32_t off = bdma[x];
+            if constexpr (RAGGED && BL == 1) off = kb + b_kc[x] < p.K ? off : OOB;
+            dma16(rb, b_dst + x * 1024, off);
+        }
+    }
+
+    struct Frags {
+        u32x4 a[KSW][2];   // [k-step][32-row block]
+        u32x4 b[KSW][2];   // [k-step][32-column block]
+    };
+
+    template <int ST>
+    __device__ __forceinline__ void read(Frags &f) const {
+#pragma unroll
+        for (int j = 0; j < KSW; ++j) {
+            f.a[j][0] = lds_b128<ST * SLAB_BYTES>(aoff[j]);
+            f.a[j][1] = lds_b128<ST * SLAB_BYTES + 4096>(aoff[j]);
+            if constexpr (BL == 1) {
+                f.b[j][0] = lds_b128<ST * SLAB_BYTES>(boff[j]);
+                f.b[j][1] = lds_b128<ST * SLAB_BYTES + 4096>(boff[j]);
+            }
+        }
+        if constexpr (BL == 0) {
+#pragma unroll
+            for (int j = 0; j < KSW; ++j)
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) {
+                    const u32x2 h0 = lds_tr16<ST * SLAB_BYTES>(boff[jb] + j * 4096);
+                    const u32x2 h1 = lds_tr16<ST * SLAB_BYTES + 1024>(boff[jb] + j * 4096);
+                    f.b[j][jb] = u32x4{h0[0], h0[1], h1[0], h1[1]};
+                }
+        }
+    }
+
+    static __device__ __forceinline__ void mma(const Frags &f, Acc &acc) {
+#pragma unroll
+        for (int j = 0; j < KSW; ++j)
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) acc.v[a][b] = mfma<DT>(f.a[j][a], f.b[j][b], acc.v[a][b]);
+    }
+};
 
 // acc += A[m0:m0+128, K-slabs] . B[K-slabs, n0:n0+128] over the tile's logical
 // k-iterations k0..k1-1, logical iteration k reading physical 64-wide K-slab
-// (k + rot) mod ipt (rot = 0 walks K in order; a rotation lets the units that
-// share a tile's panels walk them in phase -- the set of slabs a segment covers
-// is what the schedule defines, the order inside a segment is free).  With 8
-// waves each wave covers half of every slab's k-steps and holds a partial sum
-// of its quarter (see merge_k_halves).  Ends with a barrier, so the LDS is
-// free again on return.
+// (k + rot) mod ipt (rot = 0 walks K in order; the set of slabs a segment
+// covers is what the schedule defines, the order inside a segment is free).
+// With 8 waves each wave covers half of every slab's k-steps and holds a
+// partial sum of its quarter (see merge_k_halves).  Ends with a barrier, so the
+// LDS is free again on return.
+template <int DT, int BL, int NS, int NW, bool RAGGED>
+__device__ __forceinline__ void mac_loop_impl(const KParams &p, char *lds, int m0, int n0, int k0, int k1,
+                                              int rot, Acc &acc, int *cov) {
+    using ML = MainLoop<DT, BL, NS, NW>;
+    constexpr int DPI = ML::DPI;
+    const int n = k1 - k0;
+    if (n <= 0) return;
+    const ML ml(p, lds, m0, n0);
+    const int ipt = p.ipt;
+    int phys = k0 + rot;                       // physical slab of the next load
+    phys = phys >= ipt ? phys - ipt : phys;
+    phys = phys >= ipt ? phys - ipt : phys;
+    auto issue_next = [&](int st) {
+        ml.template issue<RAGGED>(phys, st);
+        phys = phys + 1 == ipt ? 0 : phys + 1;
+    };
+    typename ML::Frags f[2];
+    issue_next(0);
+    if (n > 1) issue_next(1);
+    if (n > 2) issue_next(2);
+    if (n > 3) issue_next(3);
+    wait_vm_lgkm_stages<DPI>(min(NS, n) - 1);   // this wave's loads of iteration 0 landed
+    __builtin_amdgcn_s_barrier();
+    ml.template read<0>(f[0]);
+    int done = 0;                              // iterations issued to the matrix cores
+    // One iteration; U = i % NS (the stage and, with NS even, the fragment buffer parity).
+    auto body = [&](int i, auto U, auto STEADY) {
+        constexpr int u = decltype(U)::value;
+        constexpr bool steady = decltype(STEADY)::value;
+        if constexpr (steady) wait_vm_lgkm<(NS - 2) * DPI>();
+        else wait_vm_lgkm_stages<DPI>(max(0, min(NS - 2, n - i - 2)));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (steady || i + NS < n) issue_next(u);
+        if (steady || i + 1 < n) ml.template read<(u + 1) % NS>(f[(u + 1) & 1]);
+        ML::mma(f[u & 1], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        ++done;
+    };
+    int i0 = 0;
+    for (; i0 + 2 * NS <= n; i0 += NS) {
+        body(i0 + 0, std::integral_constant<int, 0>(), std::true_type());
+        body(i0 + 1, std::integral_constant<int, 1>(), std::true_type());
+        body(i0 + 2, std::integral_constant<int, 2>(), std::true_type());
+        body(i0 + 3, std::integral_constant<int, 3>(), std::true_type());
+    }
+    for (; i0 < n; i0 += NS) {
+        body(i0 + 0, std::integral_constant<int, 0>(), std::false_type());
+        if (i0 + 1 < n) body(i0 + 1, std::integral_constant<int, 1>(), std::false_type());
+        if (i0 + 2 < n) body(i0 + 2, std::integral_constant<int, 2>(), std::false_type());
+        if (i0 + 3 < n) body(i0 + 3, std::integral_constant<int, 3>(), std::false_type());
+    }
+    wait_stage0();
+    // debug coverage: one count per logical iteration the loop above executed
+    if (cov && threadIdx.x == 0)
+        for (int k = 0; k < done; ++k) atomicAdd(cov + k0 + k, 1);
+}
+
 template <int DT, int BL, int NS, int NW>
 __device__ __forceinline__ void mac_loop(const KParams &p, char *lds, int m0, int n0, int k0, int k1,
                                          int rot, Acc &acc, int *cov) {
-    constexpr int KS = Role<NW>::KSTEPS;
-    constexpr int DPI = 2 * Role<NW>::DPW;                 // loads per wave and iteration
-    const int n = k1 - k0;
-    if (n <= 0) return;
-    const Role<NW> w;
-    LoadPlan<BL, NW> lp;
-    make_load_plan<BL, NW>(lp, p, m0, n0);
-    int phys = k0 + rot;                                   // physical slab of the next load
-    if (phys >= p.ipt) phys -= p.ipt;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-        if (s < n) {
-            issue_loads<BL, NW>(lp, p, lds + s * STAGE_BYTES, phys);
-            if (++phys == p.ipt) phys = 0;
-        }
-    wait_stage(DPI * (min(NS, n) - 1));                    // stage 0 complete for every wave
-    const int kk0 = w.kh * KS;                             // the wave's first k-step of a slab
-    Frag f[2];
-    load_frag<BL, NW>(w, lds, kk0, f[0]);
-    for (int i = 0; i < n; ++i) {
-        char *st = lds + (i % NS) * STAGE_BYTES;
-#pragma unroll
-        for (int j = 0; j < KS; ++j) {
-            if (j + 1 < KS) {
-                load_frag<BL, NW>(w, st, kk0 + j + 1, f[(j + 1) & 1]);
-            } else if (i + 1 < n) {
-                wait_stage(DPI * min(NS - 2, n - 2 - i));  // stage i+1 complete; stage i fully read
-                if (i + NS < n) {
-                    issue_loads<BL, NW>(lp, p, st, phys);
-                    if (++phys == p.ipt) phys = 0;
-                }
-                load_frag<BL, NW>(w, lds + ((i + 1) % NS) * STAGE_BYTES, kk0, f[(j + 1) & 1]);
-            }
-            mma<DT>(f[j & 1], acc);
-        }
-        if (cov && threadIdx.x == 0) atomicAdd(cov + k0 + i, 1);
-    }
-    wait_stage(0);
+    if (p.K % BK == 0) mac_loop_impl<DT, BL, NS, NW, false>(p, lds, m0, n0, k0, k1, rot, acc, cov);
+    else mac_loop_impl<DT, BL, NS, NW, true>(p, lds, m0, n0, k0, k1, rot, acc, cov);
 }
 
-// With 8 waves: add the k-half-1 wave's accumulator into its quadrant partner
-// (k-half 0) through LDS; afterwards only the k-half-0 waves hold the tile.
-// The sum is taken in a fixed order.  `lds` must be free; it is free on return.
+// With 8 waves the two waves of a quadrant (k-halves 0 and 1) each hold a
+// partial sum of the whole 64x64 quarter.  They swap halves through LDS: wave
+// (quad, kh) sends its 32-row block 1 - kh to its partner and adds the
+// partner's block kh to its own, so afterwards it holds the complete sums of
+// block row kh (fp32 addition is commutative, so both block rows are exactly
+// acc(kh 0) + acc(kh 1)).  With 4 waves every wave already holds both block
+// rows.  The result names its block rows at run time but keeps the values in
+// fixed registers (the accumulator is only ever indexed by constants, so it
+// stays in registers).  `lds` must be free; it is free on return.
 template <int NW>
-__device__ __forceinline__ void merge_k_halves(Acc &acc, char *lds) {
+struct Tile {
+    static constexpr int R = NW == 8 ? 1 : 2;   // block rows a wave holds
+    f32x16 v[R][2];                             // [held row][32-column block]
+    int i[R];                                   // which 32-row block of the quarter
+};
+
+template <int NW>
+__device__ __forceinline__ Tile<NW> merge_k_halves(const Acc &acc, char *lds) {
+    Tile<NW> t;
     if constexpr (NW == 8) {
         const Role<NW> w;
+        const bool hi = w.kh != 0;
         f32x4 *buf = reinterpret_cast<f32x4 *>(lds);
-        if (w.kh == 1) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+        for (int j = 0; j < 2; ++j) {
+            const f32x16 give = hi ? acc.v[0][j] : acc.v[1][j];
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const f32x16 &v = acc.v[b >> 1][b & 1];
-                    buf[((w.quad * 4 + b) * 4 + e4) * 64 + w.lane] =
-                        f32x4{v[4 * e4], v[4 * e4 + 1], v[4 * e4 + 2], v[4 * e4 + 3]};
-                }
+            for (int e4 = 0; e4 < 4; ++e4)
+                buf[((w.quad * 2 + w.kh) * 8 + j * 4 + e4) * 64 + w.lane] =
+                    f32x4{give[4 * e4], give[4 * e4 + 1], give[4 * e4 + 2], give[4 * e4 + 3]};
         }
         __syncthreads();
-        if (w.kh == 0) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+        for (int j = 0; j < 2; ++j) {
+            f32x16 keep = hi ? acc.v[1][j] : acc.v[0][j];
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const f32x4 x = buf[((w.quad * 4 + b) * 4 + e4) * 64 + w.lane];
-                    f32x16 &v = acc.v[b >> 1][b & 1];
-                    v[4 * e4] += x[0];
-                    v[4 * e4 + 1] += x[1];
-                    v[4 * e4 + 2] += x[2];
-                    v[4 * e4 + 3] += x[3];
-                }
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const f32x4 x = buf[((w.quad * 2 + (1 - w.kh)) * 8 + j * 4 + e4) * 64 + w.lane];
+                keep[4 * e4] += x[0];
+                keep[4 * e4 + 1] += x[1];
+                keep[4 * e4 + 2] += x[2];
+                keep[4 * e4 + 3] += x[3];
+            }
+            t.v[0][j] = keep;
         }
+        t.i[0] = w.kh;
         __syncthreads();
+    } else {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            t.v[r][0] = acc.v[r][0];
+            t.v[r][1] = acc.v[r][1];
+            t.i[r] = r;
+        }
     }
+    return t;
 }
 
 // ---------------------------------------------------------------------------
@@ -421,8 +501,8 @@ __device__ __forceinline__ void tile_origin(const KParams &p, int tile, int &m0,
 // ---------------------------------------------------------------------------
 // Epilogue helpers.  Accumulator element e of block (i, j) in lane l sits at
 // row 32 i + 8 (e / 4) + 4 (l / 32) + e % 4 and column 32 j + l % 32 of the
-// wave's quarter (output layout of the 32x32 MFMA).  Only the quadrant waves
-// (k-half 0) take part in accumulator-layout steps.
+// wave's quarter (output layout of the 32x32 MFMA).  After merge_k_halves each
+// wave touches only the block rows it owns.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void zero_acc(Acc &acc) {
 #pragma unroll
@@ -434,18 +514,17 @@ __device__ __forceinline__ void zero_acc(Acc &acc) {
 }
 
 template <int NW, class F>
-__device__ __forceinline__ void for_each_element(int m0, int n0, int M, int N, F &&f) {
+__device__ __forceinline__ void for_each_element(const Tile<NW> &t, int m0, int n0, int M, int N, F &&f) {
     const Role<NW> w;
-    if (w.kh != 0) return;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int r = 0; r < Tile<NW>::R; ++r)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int col = n0 + w.wn * 64 + j * 32 + (w.lane & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = m0 + w.wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (w.lane >> 5) + (e & 3);
-                if (row < M && col < N) f(i, j, e, (size_t)row * N + col);
+                const int row = m0 + w.wm * 64 + t.i[r] * 32 + 8 * (e >> 2) + 4 * (w.lane >> 5) + (e & 3);
+                if (row < M && col < N) f(t.v[r][j][e], (size_t)row * N + col);
             }
         }
 }
@@ -459,18 +538,17 @@ constexpr int EPI_LD = BN;
 __device__ __forceinline__ int epi_swz(int r) { return ((r >> 2) & 1) << 5; }
 
 template <int NW>
-__device__ __forceinline__ void acc_to_lds(float *tile, const Acc &acc) {
+__device__ __forceinline__ void acc_to_lds(float *tile, const Tile<NW> &t) {
     const Role<NW> w;
-    if (w.kh != 0) return;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int r = 0; r < Tile<NW>::R; ++r)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int col = w.wn * 64 + j * 32 + (w.lane & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = w.wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (w.lane >> 5) + (e & 3);
-                tile[row * EPI_LD + (col ^ epi_swz(row))] = acc.v[i][j][e];
+                const int row = w.wm * 64 + t.i[r] * 32 + 8 * (e >> 2) + 4 * (w.lane >> 5) + (e & 3);
+                tile[row * EPI_LD + (col ^ epi_swz(row))] = t.v[r][j][e];
             }
         }
 }
@@ -501,24 +579,16 @@ __device__ __forceinline__ void put_quad(float *dst, f32x4 v, int nvalid, bool v
     }
 }
 
-// Write the accumulator tile to C.  `lds` must be free; it is free again on return.
+// Write the held rows to C straight from registers: each store instruction
+// writes two 128-byte row segments (lanes 0-31 and 32-63).
 template <int NW>
-__device__ __forceinline__ void store_tile(float *X, int m0, int n0, int M, int N, const Acc &acc,
-                                           char *lds) {
-    float *tile = reinterpret_cast<float *>(lds);
-    acc_to_lds<NW>(tile, acc);
-    __syncthreads();
-    const bool vec = (N & 3) == 0;
-    for_each_quad<NW>(m0, n0, M, N, [&](int, int r, int c, size_t off, int nv) {
-        put_quad(X + off, staged_quad(tile, r, c), nv, vec);
-    });
-    __syncthreads();
+__device__ __forceinline__ void store_tile(float *X, int m0, int n0, int M, int N, const Tile<NW> &t) {
+    for_each_element<NW>(t, m0, n0, M, N, [&](float v, size_t off) { X[off] = v; });
 }
 
 template <int NW>
-__device__ __forceinline__ void atomic_add_c(float *C, int m0, int n0, int M, int N, const Acc &acc) {
-    for_each_element<NW>(m0, n0, M, N,
-                         [&](int i, int j, int e, size_t off) { unsafeAtomicAdd(C + off, acc.v[i][j][e]); });
+__device__ __forceinline__ void atomic_add_c(float *C, int m0, int n0, int M, int N, const Tile<NW> &t) {
+    for_each_element<NW>(t, m0, n0, M, N, [&](float v, size_t off) { unsafeAtomicAdd(C + off, v); });
 }
 
 // ---------------------------------------------------------------------------
@@ -550,43 +620,49 @@ __device__ __forceinline__ float get_coherent(const float *p) {
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
 
 // Stream-K partial slot (64 KiB) in register-native order: for accumulator block
-// b and element quad e4, the 64 lanes of a quadrant wave move 1 KiB of
-// contiguous memory.
+// b = 2 i + j of a quarter and element quad e4, the 64 lanes of a wave move
+// 1 KiB of contiguous memory.
 __device__ __forceinline__ uint32_t slot_off(int quad, int b, int e4, int lane) {
     return (uint32_t)((((quad * 4 + b) * 4 + e4) * 64 + lane) * 16);
 }
 
 template <int NW>
-__device__ __forceinline__ void put_slot(float *slot, const Acc &acc) {
+__device__ __forceinline__ void put_slot(float *slot, const Tile<NW> &t) {
     const Role<NW> w;
-    if (w.kh != 0) return;
     const __amdgpu_buffer_rsrc_t r = span(slot, BM * BN * 4);
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int h = 0; h < Tile<NW>::R; ++h)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            const f32x16 &v = acc.v[b >> 1][b & 1];
-            put4_coherent(r, slot_off(w.quad, b, e4, w.lane),
-                          f32x4{v[4 * e4], v[4 * e4 + 1], v[4 * e4 + 2], v[4 * e4 + 3]});
-        }
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const f32x16 &v = t.v[h][j];
+                put4_coherent(r, slot_off(w.quad, 2 * t.i[h] + j, e4, w.lane),
+                              f32x4{v[4 * e4], v[4 * e4 + 1], v[4 * e4 + 2], v[4 * e4 + 3]});
+            }
 }
 
+// t += slot over the held rows.  Every load is issued before the first add, so
+// the wave waits for the partial once.
 template <int NW>
-__device__ __forceinline__ void add_slot(const float *slot, Acc &acc) {
+__device__ __forceinline__ void add_slot(const float *slot, Tile<NW> &t) {
     const Role<NW> w;
-    if (w.kh != 0) return;
     const __amdgpu_buffer_rsrc_t r = span(slot, BM * BN * 4);
-    // one accumulator block (four 1 KiB loads) per round keeps register pressure bounded
+    f32x4 x[Tile<NW>::R][2][4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        f32x4 x[4];
+    for (int h = 0; h < Tile<NW>::R; ++h)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) x[e4] = get4_coherent(r, slot_off(w.quad, b, e4, w.lane));
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4)
+            for (int e4 = 0; e4 < 4; ++e4) x[h][j][e4] = get4_coherent(r, slot_off(w.quad, 2 * t.i[h] + j, e4, w.lane));
 #pragma unroll
-            for (int y = 0; y < 4; ++y) acc.v[b >> 1][b & 1][4 * e4 + y] += x[e4][y];
-    }
+    for (int h = 0; h < Tile<NW>::R; ++h)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) t.v[h][j][4 * e4 + y] += x[h][j][e4][y];
 }
 
 // Poll `flag` until it holds `epoch` (one thread).  Gives up after `limit`
@@ -671,9 +747,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_dp(KParams p) {
     Acc acc;
     zero_acc(acc);
     mac_loop<DT, BL, NS, NW>(p, lds, m0, n0, 0, p.ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
-    merge_k_halves<NW>(acc, lds);
+    const Tile<NW> t = merge_k_halves<NW>(acc, lds);
     clk.mark(p, 0);
-    store_tile<NW>(p.C, m0, n0, p.M, p.N, acc, lds);
+    store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
     trace_segment(p, p.worker_base + w, 0, tile, 0, p.ipt, 0);
     trace_folded(p, tile, 0, p.worker_base + w);
     clk.done(p);
@@ -697,11 +773,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
     Acc acc;
     zero_acc(acc);
     mac_loop<DT, BL, NS, NW>(p, lds, m0, n0, k0, k1, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
-    merge_k_halves<NW>(acc, lds);
+    const Tile<NW> t = merge_k_halves<NW>(acc, lds);
     clk.mark(p, 0);
     trace_segment(p, w, 0, tile, k0, k1, S == 1 ? 0 : (s == 0 ? 1 : 2));
     if (S == 1) {
-        store_tile<NW>(p.C, m0, n0, p.M, p.N, acc, lds);
+        store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
         trace_folded(p, tile, 0, w);
         clk.done(p);
         return;
@@ -710,7 +786,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
     // with device-scope stores (LDS keeps the copy this workgroup may fold itself)
     const size_t mn = (size_t)p.M * p.N;
     float *stg = reinterpret_cast<float *>(lds);
-    acc_to_lds<NW>(stg, acc);
+    acc_to_lds<NW>(stg, t);
     __syncthreads();
     const size_t org = (size_t)m0 * p.N + n0;                 // tile origin within [M,N]
     const uint32_t span_bytes = (uint32_t)(((size_t)(min(BM, p.M - m0) - 1) * p.N + min(BN, p.N - n0)) * 4);
@@ -813,11 +889,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
     const int end = begin + p.q + (u < p.big ? 1 : 0);
     int nseg = 0;
     for (int pos = begin; pos < end;) {
-        const int t = pos / ipt;                 // tile index within the Stream-K part
-        const int tb = t * ipt;
+        const int ts = pos / ipt;                // tile index within the Stream-K part
+        const int tb = ts * ipt;
         const int k0 = pos - tb;
         const int k1 = min(end - tb, ipt);
-        const int tile = p.tile_base + t;
+        const int tile = p.tile_base + ts;
         int m0, n0;
         tile_origin(p, tile, m0, n0);
         const int role = k0 > 0 ? 2 : (k1 == ipt ? 0 : 1);
@@ -828,17 +904,17 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         const int owner = unit_of(tb, p.q, p.big);
         const int rot = (tb - unit_start(owner, p.q, p.big)) % ipt;
         mac_loop<DT, BL, NS, NW>(p, lds, m0, n0, k0, k1, rot, acc, p.trace ? trace_cov(p, tile) : nullptr);
-        merge_k_halves<NW>(acc, lds);
+        Tile<NW> t = merge_k_halves<NW>(acc, lds);
         clk.mark(p, 2 * min(nseg, 1));
         trace_segment(p, u, nseg++, tile, k0, k1, role);
         if (role == 0) {
-            store_tile<NW>(p.C, m0, n0, p.M, p.N, acc, lds);
+            store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
             trace_folded(p, tile, 0, u);
         } else if constexpr (ATOMIC) {
-            atomic_add_c<NW>(p.C, m0, n0, p.M, p.N, acc);
+            atomic_add_c<NW>(p.C, m0, n0, p.M, p.N, t);
         } else if (role == 2) {
             // starts mid-tile: publish the partial, then the flag
-            put_slot<NW>(p.part + (size_t)u * (BM * BN), acc);
+            put_slot<NW>(p.part + (size_t)u * (BM * BN), t);
             wait_vm_all();                 // this wave's partial stores are complete
             __syncthreads();               // ... and every other wave's
             if (threadIdx.x == 0 && !(p.debug & GEMM_DEBUG_NO_PUBLISH))
@@ -852,10 +928,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
                 if (unit_start(v, p.q, p.big) >= tile_end) break;
                 if (threadIdx.x == 0) wait_flag(p.flags + v, p.epoch, p.spin_limit, p.status);
                 __syncthreads();
-                add_slot<NW>(p.part + (size_t)v * (BM * BN), acc);
+                add_slot<NW>(p.part + (size_t)v * (BM * BN), t);
                 trace_folded(p, tile, pos_fold++, v);
             }
-            store_tile<NW>(p.C, m0, n0, p.M, p.N, acc, lds);
+            store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
         }
         clk.mark(p, 2 * min(nseg - 1, 1) + 1);
         pos = tb + k1;
@@ -900,7 +976,7 @@ struct Shape {
 template <int DT, int BL>
 KernelFn pick(int kmode, Shape &shape) {
     switch (kmode) {
-    case K_DP: shape = {2, 4}; return gemm_dp<DT, BL, 2, 4>;
+    case K_DP: shape = {4, 8}; return gemm_dp<DT, BL, 4, 8>;
     case K_SPLITK: shape = {4, 8}; return gemm_splitk<DT, BL, 4, 8>;
     case K_SK: shape = {4, 8}; return gemm_streamk<DT, BL, 4, 8, false>;
     case K_SK_ATOMIC: shape = {4, 8}; return gemm_streamk<DT, BL, 4, 8, true>;
