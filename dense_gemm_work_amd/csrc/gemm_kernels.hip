@@ -134,8 +134,10 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
 // Issued as inline assembly so that the compiler does not wait for it before
 // unrelated LDS reads; completion is awaited explicitly (wait_vm_lgkm).
 // `lds_addr` is the wave-uniform LDS byte address of the 1 KiB destination.
+// The s_nop is the one wait state a GFX9 LDS DMA needs after an SALU write of
+// M0 (the compiler cannot insert it inside the asm block).
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(lds_addr), "v"(voff), "s"(rsrc)
                  : "memory");
@@ -329,16 +331,16 @@ struct MainLoop {
     }
 };
 
-// acc += A[m0:m0+128, K-slabs] . B[K-slabs, n0:n0+128] over the tile's logical
-// k-iterations k0..k1-1, logical iteration k reading physical 64-wide K-slab
-// (k + rot) mod ipt (rot = 0 walks K in order; the set of slabs a segment
-// covers is what the schedule defines, the order inside a segment is free).
+// acc += A[m0:m0+128, K-slabs] . B[K-slabs, n0:n0+128] over the tile's MAC
+// iterations k0..k1-1, iteration k reading the 64-wide K-slab (k + rot) mod ipt
+// (rot = 0 maps iteration k to slab k; the caller uses one rot per tile, so the
+// iterations of all of a tile's segments still cover every slab exactly once).
 // With 8 waves each wave covers half of every slab's k-steps and holds a
 // partial sum of its quarter (see merge_k_halves).  Ends with a barrier, so the
 // LDS is free again on return.
 template <int DT, int BL, int NS, int NW, bool RAGGED>
 __device__ __forceinline__ void mac_loop_impl(const KParams &p, char *lds, int m0, int n0, int k0, int k1,
-                                              int rot, Acc &acc, int *cov) {
+                                              int rot, Acc &acc, int *cov, uint32_t *raise) {
     using ML = MainLoop<DT, BL, NS, NW>;
     constexpr int DPI = ML::DPI;
     const int n = k1 - k0;
@@ -359,6 +361,9 @@ __device__ __forceinline__ void mac_loop_impl(const KParams &p, char *lds, int m
     if (n > 3) issue_next(3);
     wait_vm_lgkm_stages<DPI>(min(NS, n) - 1);   // this wave's loads of iteration 0 landed
     __builtin_amdgcn_s_barrier();
+    // A partial published just before this loop: its stores preceded the loads
+    // waited for above in every wave, so they are complete and the flag may rise.
+    if (raise && threadIdx.x == 0) __hip_atomic_store(raise, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     ml.template read<0>(f[0]);
     int done = 0;                              // iterations issued to the matrix cores
     // One iteration; U = i % NS (the stage and, with NS even, the fragment buffer parity).
@@ -394,11 +399,13 @@ __device__ __forceinline__ void mac_loop_impl(const KParams &p, char *lds, int m
         for (int k = 0; k < done; ++k) atomicAdd(cov + k0 + k, 1);
 }
 
+// `raise` (optional): a flag to set to p.epoch once this workgroup's earlier
+// global stores are complete (the loop's first wait establishes that).
 template <int DT, int BL, int NS, int NW>
 __device__ __forceinline__ void mac_loop(const KParams &p, char *lds, int m0, int n0, int k0, int k1,
-                                         int rot, Acc &acc, int *cov) {
-    if (p.K % BK == 0) mac_loop_impl<DT, BL, NS, NW, false>(p, lds, m0, n0, k0, k1, rot, acc, cov);
-    else mac_loop_impl<DT, BL, NS, NW, true>(p, lds, m0, n0, k0, k1, rot, acc, cov);
+                                         int rot, Acc &acc, int *cov, uint32_t *raise = nullptr) {
+    if (p.K % BK == 0) mac_loop_impl<DT, BL, NS, NW, false>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise);
+    else mac_loop_impl<DT, BL, NS, NW, true>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise);
 }
 
 // With 8 waves the two waves of a quadrant (k-halves 0 and 1) each hold a
@@ -701,7 +708,7 @@ __device__ __forceinline__ void trace_segment(const KParams &p, int w, int nseg,
     rec[1 + 4 * nseg + 1] = k0;
     rec[1 + 4 * nseg + 2] = k1;
     rec[1 + 4 * nseg + 3] = role;
-    rec[0] = nseg + 1;
+    rec[0] = max(rec[0], nseg + 1);
 }
 __device__ __forceinline__ void trace_folded(const KParams &p, int tile, int pos, int w) {
     if (!p.trace || threadIdx.x != 0 || pos >= p.trace_maxfold) return;
@@ -878,6 +885,23 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
 
 // ---------------------------------------------------------------------------
 // Stream-K: persistent; workgroup b runs unit worker_of(b).
+//
+// A unit's range [begin, end) of the flattened (tile, k) space falls into
+// segments at tile edges (book chapter, Stream-K paragraph): a first segment
+// that may start mid-tile (a contributor: it publishes its partial), whole
+// tiles (stored directly) and a last segment that may hold k = 0 of a tile and
+// end mid-tile (its owner: it adds the next units' partials in k order and
+// stores the tile).  Segments run in range order; every unit publishes before
+// it waits, so all waits end.
+//
+// MAC iteration k of tile T reads K-slab (k + rot_T) mod ipt, where rot_T is
+// the number of iterations T's owner (the unit holding k = 0) computes before
+// reaching T.  This is a bijection on each tile's slabs, so every tile still
+// sums all of K exactly once, in the fixed fold order.  Its effect: an owner
+// or a whole tile reads slab (step mod ipt) at each step of its unit, and a
+// first segment that starts mid-tile reads slab ((step + q) mod ipt), so all
+// units stream the same few K-slabs at any moment and the A and B panels
+// shared by neighbouring tiles are reused from the XCD's L2.
 // ---------------------------------------------------------------------------
 template <int DT, int BL, int NS, int NW, bool ATOMIC>
 __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
@@ -888,6 +912,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
     const int begin = unit_start(u, p.q, p.big);
     const int end = begin + p.q + (u < p.big ? 1 : 0);
     int nseg = 0;
+    uint32_t *pending = nullptr;   // a published partial whose flag rises in the next segment's loop
     for (int pos = begin; pos < end;) {
         const int ts = pos / ipt;                // tile index within the Stream-K part
         const int tb = ts * ipt;
@@ -897,13 +922,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         int m0, n0;
         tile_origin(p, tile, m0, n0);
         const int role = k0 > 0 ? 2 : (k1 == ipt ? 0 : 1);
-        Acc acc;
-        zero_acc(acc);
-        // walk the tile's K-slabs in the phase of its k = 0 holder: the units that
-        // meet in this tile then stream the same slabs close together in time
         const int owner = unit_of(tb, p.q, p.big);
         const int rot = (tb - unit_start(owner, p.q, p.big)) % ipt;
-        mac_loop<DT, BL, NS, NW>(p, lds, m0, n0, k0, k1, rot, acc, p.trace ? trace_cov(p, tile) : nullptr);
+        Acc acc;
+        zero_acc(acc);
+        mac_loop<DT, BL, NS, NW>(p, lds, m0, n0, k0, k1, rot, acc, p.trace ? trace_cov(p, tile) : nullptr,
+                                 pending);
+        pending = nullptr;
         Tile<NW> t = merge_k_halves<NW>(acc, lds);
         clk.mark(p, 2 * min(nseg, 1));
         trace_segment(p, u, nseg++, tile, k0, k1, role);
@@ -913,12 +938,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         } else if constexpr (ATOMIC) {
             atomic_add_c<NW>(p.C, m0, n0, p.M, p.N, t);
         } else if (role == 2) {
-            // starts mid-tile: publish the partial, then the flag
+            // starts mid-tile: publish the partial, then the flag -- at once if
+            // this is the unit's last segment, else from the next segment's loop
+            // as soon as the stores are known complete (the loop has to wait for
+            // its first loads anyway)
             put_slot<NW>(p.part + (size_t)u * (BM * BN), t);
-            wait_vm_all();                 // this wave's partial stores are complete
-            __syncthreads();               // ... and every other wave's
-            if (threadIdx.x == 0 && !(p.debug & GEMM_DEBUG_NO_PUBLISH))
-                __hip_atomic_store(p.flags + u, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t *flag = (p.debug & GEMM_DEBUG_NO_PUBLISH) ? nullptr : p.flags + u;
+            if (tb + k1 < end) {
+                pending = flag;
+            } else {
+                wait_vm_all();             // this wave's partial stores are complete
+                __syncthreads();           // ... and every other wave's
+                if (flag && threadIdx.x == 0)
+                    __hip_atomic_store(flag, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         } else {
             // holds k = 0 of a split tile: fold the next units' partials in k order
             trace_folded(p, tile, 0, u);
