@@ -50,6 +50,8 @@ def parse():
                     help="override the workload's decomposition (for profiling one arm)")
     ap.add_argument("--splits", type=int, default=None, help="Split-K factor or Stream-K units")
     ap.add_argument("--atomic", action="store_true", help="Stream-K atomic fixup")
+    ap.add_argument("--no-timeline", action="store_true",
+                    help="skip the per-CU busy-time measurement (instrumented launches)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known-size "
                          "reference dispatch for HBM byte counters)")
@@ -185,6 +187,51 @@ def measured_traffic(profile: str, kernel: str):
     return int(entry["bytes"])
 
 
+def cu_timeline(dg, name, mode, splits=0, atomic=False):
+    """Per-CU busy time of one launch with the kernels' timing records (every
+    workgroup stores its start and end on the 100 MHz clock plus the CU it ran
+    on).  Returns the launch span, the busy fraction of the 256 CUs over the
+    span (1 - idle fraction), and how the CUs' last end times spread."""
+    import collections
+
+    import numpy as np
+    import torch
+    from workloads import WORKLOADS, make_operands
+
+    w = WORKLOADS[name]
+    A, B = make_operands(w)
+    a, b = A.cuda(), B.cuda()
+    c = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    p = dg.gemm_plan(w.M, w.N, w.K, dg.layout_word(w.b_layout, w.dtype), dg.mode_word(mode, atomic), splits,
+                     dg.gemm_num_cus())
+    tim = torch.full((8 * int(p.workers),), -1, dtype=torch.int64, device="cuda")
+    for _ in range(3):
+        dg.gemm_tensors(a, b, c, b_layout=w.b_layout, mode=mode, splits=splits, atomic=atomic)
+    dg.gemm_tensors(a, b, c, b_layout=w.b_layout, mode=mode, splits=splits, atomic=atomic, timing=tim)
+    torch.cuda.synchronize()
+    t = tim.cpu().numpy().reshape(-1, 8).astype(np.float64)
+    t = t[t[:, 0] >= 0]
+    t0 = t[:, 0].min()
+    start, end = (t[:, 0] - t0) / 100.0, (t[:, 1] - t0) / 100.0      # microseconds
+    span = float(end.max())
+    # HW_ID: CU id in bits 8..11, shader array bit 12, shader engine bits 13..15; XCC_ID separately
+    hw, xcc = t[:, 2].astype(np.int64), t[:, 3].astype(np.int64)
+    cu_key = xcc * 4096 + ((hw >> 13) & 7) * 256 + ((hw >> 12) & 1) * 16 + ((hw >> 8) & 15)
+    busy, last = collections.defaultdict(float), collections.defaultdict(float)
+    for k, s_, e_ in zip(cu_key, start, end):
+        busy[k] += e_ - s_
+        last[k] = max(last[k], e_)
+    ncu = dg.gemm_num_cus()
+    frac = sum(busy.values()) / (ncu * span)
+    ends = np.array(sorted(last.values()))
+    return {
+        "decision": dg.DECISION_NAMES[p.decision], "workgroups": int(p.workers), "cus_used": len(busy),
+        "span_us": round(span, 2), "busy_fraction": round(float(frac), 4), "idle_fraction": round(float(1 - frac), 4),
+        "cu_last_end_us": {"min": round(float(ends.min()), 2), "median": round(float(np.median(ends)), 2),
+                           "max": round(float(ends.max()), 2)},
+    }
+
+
 def cpu_baseline(w, A, B):
     from oracle import gemm as og
 
@@ -260,6 +307,15 @@ def main():
         for arm in ("dp", "splitk2", "splitk4"):
             speedups[f"streamk_vs_{arm}"] = round(c3[arm]["median_us"] / sk, 3)
 
+    timeline = {}
+    if not args.no_timeline:
+        for key, (name, mode, splits, atomic) in {
+            "c3_dp": ("c3_wavequant", "dp", 0, False), "c3_streamk": ("c3_wavequant", "heuristic", 0, False),
+            "c5_dp": ("c5_longk_fp16", "dp", 0, False), "c5_streamk": ("c5_longk_fp16", "streamk", 0, False),
+        }.items():
+            timeline[key] = cu_timeline(dg, name, mode, splits, atomic)
+            log(f"  timeline {key:11s} {timeline[key]}")
+
     cpu = None
     if not args.no_cpu:
         log("bench: timing the fp64 CPU oracle on the same workload")
@@ -300,6 +356,7 @@ def main():
             "kernel_mean_us": round(kern_ms * 1e3, 3),
         },
         "cpu_baseline": cpu,
+        "cu_timeline": timeline,
         "shapes": shapes,
     }
     print(json.dumps(line), flush=True)
