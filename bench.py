@@ -215,7 +215,10 @@ def cu_timeline(dg, name, mode, splits=0, atomic=False):
     start, end = (t[:, 0] - t0) / 100.0, (t[:, 1] - t0) / 100.0      # microseconds
     span = float(end.max())
     # HW_ID: CU id in bits 8..11, shader array bit 12, shader engine bits 13..15; XCC_ID separately
-    hw, xcc = t[:, 2].astype(np.int64), t[:, 3].astype(np.int64)
+    hwx = t[:, 2].astype(np.int64)
+    hw, xcc = hwx & 0xFFFFFFFF, hwx >> 32
+    # mean shader clock of each workgroup: s_memtime cycles over its real-time span
+    mhz = t[:, 3] / np.maximum(t[:, 1] - t[:, 0], 1) * 100.0
     cu_key = xcc * 4096 + ((hw >> 13) & 7) * 256 + ((hw >> 12) & 1) * 16 + ((hw >> 8) & 15)
     busy, last = collections.defaultdict(float), collections.defaultdict(float)
     for k, s_, e_ in zip(cu_key, start, end):
@@ -229,6 +232,8 @@ def cu_timeline(dg, name, mode, splits=0, atomic=False):
         "span_us": round(span, 2), "busy_fraction": round(float(frac), 4), "idle_fraction": round(float(1 - frac), 4),
         "cu_last_end_us": {"min": round(float(ends.min()), 2), "median": round(float(np.median(ends)), 2),
                            "max": round(float(ends.max()), 2)},
+        "shader_clock_mhz": {"median": round(float(np.median(mhz))), "min": round(float(mhz.min())),
+                             "max": round(float(mhz.max()))},
     }
 
 

@@ -2,10 +2,11 @@
 // planning, workspace management and kernel launches.
 //
 // Workspace (per device, owned by the library unless the caller passes one):
-//   control: a status word (64 words reserved), one flag per Stream-K unit and
-//            one arrival counter per Split-K tile.  It is zero-filled when it is
-//            (re)allocated and never again: flags hold the epoch of the launch
-//            that last raised them (a fresh epoch per Stream-K launch, so stale
+//   control: a status word (64 words reserved), flags (one per Stream-K unit,
+//            or one per Split-K (tile, split)) and one arrival counter per
+//            Split-K tile.  It is zero-filled when it is (re)allocated and never
+//            again: flags hold the epoch of the launch that last raised them (a
+//            fresh epoch per Stream-K or cooperative Split-K launch, so stale
 //            flags never match), and the last arriver of a tile resets its
 //            counter to zero.
 //   data:    Stream-K partial slots [units][128*128] fp32, or Split-K partials
@@ -178,7 +179,8 @@ int run(const gemm_args_t &a) {
                             a.num_cus > 0 ? a.num_cus : 256, &p, &why);
     if (rc != GEMM_OK) return fail(rc, why);
     if (a.num_cus < 0) return fail(GEMM_ERR_INVALID, "num_cus must be >= 0");
-    if ((a.debug & ~GEMM_DEBUG_NO_PUBLISH) != 0) return fail(GEMM_ERR_INVALID, "unknown debug bits");
+    if ((a.debug & ~(GEMM_DEBUG_NO_PUBLISH | GEMM_DEBUG_LAST_ARRIVER)) != 0)
+        return fail(GEMM_ERR_INVALID, "unknown debug bits");
     if (a.M == 0 || a.N == 0) return GEMM_OK;
     if ((rc = check_operands(a)) != GEMM_OK) return rc;
 
@@ -218,7 +220,7 @@ int run(const gemm_args_t &a) {
                                                   std::to_string((int64_t)bpc * ds->num_cus) + ")");
     }
 
-    if ((rc = ensure_control(*ds, std::max<int64_t>(p.sk_units, 1), p.tiles)) != GEMM_OK) return rc;
+    if ((rc = ensure_control(*ds, dgw::flag_words(p), p.tiles)) != GEMM_OK) return rc;
 
     // flags, counters and the data region
     uint32_t *flags = nullptr, *counters = nullptr;
@@ -231,7 +233,7 @@ int run(const gemm_args_t &a) {
         const int64_t cb = dgw::control_bytes(p);
         char *base = static_cast<char *>(a.workspace);
         flags = reinterpret_cast<uint32_t *>(base + 256);
-        counters = reinterpret_cast<uint32_t *>(base + 256 + (std::max<int64_t>(p.sk_units, 1) * 4 + 255) / 256 * 256);
+        counters = reinterpret_cast<uint32_t *>(base + 256 + (dgw::flag_words(p) * 4 + 255) / 256 * 256);
         part = reinterpret_cast<float *>(base + cb);
         if ((e = dgw::launch_zero(base, cb / 4, stream)) != hipSuccess) return fail_hip(e, "zero control");
     } else {
@@ -286,6 +288,20 @@ int run(const gemm_args_t &a) {
             return fail_hip(e, "launch DP kernel");
     } else if (p.decision == GEMM_SPLITK) {
         kp.ntiles = (int)p.tiles;
+        // With every (tile, split) workgroup resident at once and more than 4
+        // splits, the S splits of a tile fold it together, one row band each,
+        // after all S flags are up; otherwise the last arriver at the tile's
+        // counter folds it alone (for S <= 4 in one round of loads, which beats
+        // the flag handoff; beyond that one workgroup's bandwidth dominates).
+        if (p.splits > dgw::COOP_MIN_SPLITS && p.splits <= dgw::COOP_MAX_SPLITS && a.N % 4 == 0 &&
+            !(a.debug & GEMM_DEBUG_LAST_ARRIVER)) {
+            int &bpc = ds->bpc[dtype][blayout][kmode];
+            if (bpc == 0) {
+                if ((e = dgw::blocks_per_cu(dtype, blayout, kmode, &bpc)) != hipSuccess)
+                    return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+            }
+            if (p.tiles * p.splits <= (int64_t)bpc * ds->num_cus) kp.epoch = next_epoch();
+        }
         if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_SPLITK, (int)(p.tiles * p.splits), kp, stream)) !=
             hipSuccess)
             return fail_hip(e, "launch Split-K kernel");

@@ -166,6 +166,20 @@ __device__ __forceinline__ void wait_stage0() {
     __builtin_amdgcn_s_barrier();
 }
 
+// A device-scope (sc1) load of a 32-bit flag that the compiler does not track,
+// so that several can be in flight before one explicit vmcnt wait (the
+// compiler would wait after each atomic load).  flag_value() must only be
+// applied after such a wait has covered the load.
+__device__ __forceinline__ uint32_t load_flag_async(const uint32_t *flag) {
+    uint32_t v;
+    asm volatile("global_load_dword %0, %1, off sc1" : "=v"(v) : "v"(flag) : "memory");
+    return v;
+}
+__device__ __forceinline__ uint32_t flag_value(uint32_t v) {
+    asm volatile("" : "+v"(v));   // keeps every use of v after the preceding wait
+    return v;
+}
+
 template <int OFF>
 __device__ __forceinline__ u32x4 lds_b128(uint32_t addr) {
     return *reinterpret_cast<const lds_u32x4 *>(static_cast<uintptr_t>(addr + OFF));
@@ -672,15 +686,27 @@ __device__ __forceinline__ void add_slot(const float *slot, Tile<NW> &t) {
                 for (int y = 0; y < 4; ++y) t.v[h][j][4 * e4 + y] += x[h][j][e4][y];
 }
 
-// Poll `flag` until it holds `epoch` (one thread).  Gives up after `limit`
-// polls, recording STATUS_TIMEOUT.
-__device__ __forceinline__ void wait_flag(const uint32_t *flag, uint32_t epoch, uint32_t limit,
-                                          uint32_t *status) {
-    uint32_t polls = 0;
-    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
-        if (++polls >= limit) {
+// Poll flags first[0..n) (1 <= n <= MAXN <= 32, one thread) until all of them
+// hold `epoch`.  Every round issues all of its loads before waiting for any
+// (the asynchronous form keeps the compiler from waiting after each one), so a
+// round costs one memory round trip however many flags there are.  Gives up
+// after `limit` rounds, recording STATUS_TIMEOUT.
+template <int MAXN>
+__device__ __forceinline__ void wait_flags(const uint32_t *first, int n, uint32_t epoch, uint32_t limit,
+                                           uint32_t *status) {
+    static_assert(MAXN <= 32, "flag count");
+    for (uint32_t polls = 1;; ++polls) {
+        uint32_t v[MAXN];
+#pragma unroll
+        for (int i = 0; i < MAXN; ++i) v[i] = load_flag_async(first + min(i, n - 1));
+        wait_vm_all();
+        bool up = true;
+#pragma unroll
+        for (int i = 0; i < MAXN; ++i) up = up && flag_value(v[i]) == epoch;
+        if (up) return;
+        if (polls >= limit) {
             __hip_atomic_fetch_or(status, STATUS_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
+            return;
         }
         __builtin_amdgcn_s_sleep(1);
     }
@@ -718,11 +744,15 @@ __device__ __forceinline__ void trace_folded(const KParams &p, int tile, int pos
 }
 
 // Per-workgroup placement and busy time (only when p.timing is set): 8 int64 per
-// workgroup, {start, end, HW_ID, XCC_ID, mark0..mark3} in 100 MHz ticks.
+// workgroup, {start, end, HW_ID | XCC_ID << 32, shader cycles, mark0..mark3},
+// times in 100 MHz ticks.
 struct WgClock {
-    unsigned long long t0;
-    __device__ __forceinline__ explicit WgClock(const KParams &p) : t0(0) {
-        if (p.timing) t0 = __builtin_amdgcn_s_memrealtime();
+    unsigned long long t0, c0;   // start: 100 MHz real time, shader clock cycles
+    __device__ __forceinline__ explicit WgClock(const KParams &p) : t0(0), c0(0) {
+        if (p.timing) {
+            t0 = __builtin_amdgcn_s_memrealtime();
+            c0 = __builtin_amdgcn_s_memtime();
+        }
     }
     __device__ __forceinline__ long long *entry(const KParams &p) const {
         return p.timing + 8 * ((size_t)p.timing_base + blockIdx.x);
@@ -733,10 +763,13 @@ struct WgClock {
     __device__ __forceinline__ void done(const KParams &p) const {
         if (!p.timing || threadIdx.x != 0) return;
         long long *e = entry(p);
+        const unsigned long long c1 = __builtin_amdgcn_s_memtime();
         e[0] = (long long)t0;
         e[1] = (long long)__builtin_amdgcn_s_memrealtime();
-        e[2] = (long long)__builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));   // HW_REG_HW_ID
-        e[3] = (long long)__builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11));  // HW_REG_XCC_ID
+        const uint32_t hw = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));    // HW_REG_HW_ID
+        const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11));  // HW_REG_XCC_ID
+        e[2] = (long long)(((unsigned long long)xcc << 32) | hw);
+        e[3] = (long long)(c1 - c0);
     }
 };
 
@@ -765,6 +798,59 @@ __global__ __launch_bounds__(64 * NW) void gemm_dp(KParams p) {
 // ---------------------------------------------------------------------------
 // Split-K: worker w = tile * S + s covers k-iterations [s P / S, (s+1) P / S).
 // ---------------------------------------------------------------------------
+// Split-K cooperative fold: split s of a tile sums rows [s BM / S, (s + 1) BM / S)
+// of the S partials, ((P0 + P1) + P2) + ..., its own partial read from the LDS
+// staging copy, and stores them to C.  The row band has at most 16 row quads
+// per thread times partials (S <= COOP_MAX_SPLITS), all loaded before the
+// first add.  Needs N % 4 == 0 (16-byte partial and output quads).
+
+template <int NW>
+__device__ __forceinline__ void fold_rows(const KParams &p, const float *stg, int tile, int s, int m0, int n0,
+                                          size_t org, uint32_t span_bytes) {
+    constexpr int NT = 64 * NW;
+    const int S = p.splits;
+    const int r0 = s * BM / S, r1 = (s + 1) * BM / S;
+    static_assert(BN == 128, "32 row quads per tile row");
+    const int nq = (r1 - r0) * (BN / 4);           // row quads in the band
+    const int qt = (nq + NT - 1) / NT;             // quads per thread
+    const int slots = qt * S;                      // (quad, partial) pairs, <= 16
+    const size_t mn = (size_t)p.M * p.N;
+    // (quad g, partial t) of slot j = g S + t, stepped without division
+    f32x4 x[16];
+    {
+        int g = 0, t = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int fq = threadIdx.x + NT * g;
+            const int r = r0 + (fq >> 5), c = (fq & 31) * 4;
+            x[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (j < slots && t != s && fq < nq && m0 + r < p.M && n0 + c < p.N)
+                x[j] = get4_coherent(span(p.part + (size_t)t * mn + org, span_bytes),
+                                     (uint32_t)(((size_t)r * p.N + c) * 4));
+            if (++t == S) {
+                t = 0;
+                ++g;
+            }
+        }
+    }
+    f32x4 run = {0.f, 0.f, 0.f, 0.f};
+    int g = 0, t = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int fq = threadIdx.x + NT * g;
+        const int r = r0 + (fq >> 5), c = (fq & 31) * 4;
+        const bool ok = j < slots && fq < nq && m0 + r < p.M && n0 + c < p.N;
+        const f32x4 v = t == s ? staged_quad(stg, r & (BM - 1), c) : x[j];
+        run = t == 0 ? v : run + v;
+        if (t == S - 1 && ok)
+            put_quad(p.C + (size_t)(m0 + r) * p.N + n0 + c, run, min(4, p.N - (n0 + c)), true);
+        if (++t == S) {
+            t = 0;
+            ++g;
+        }
+    }
+}
+
 template <int DT, int BL, int NS, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
     constexpr int NT = Role<NW>::NT, QPT = BM * BN / 4 / NT;
@@ -813,6 +899,24 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
     wait_vm_all();                 // this wave's partial stores are complete
     __syncthreads();               // ... and every other wave's
     clk.mark(p, 1);
+    if (p.epoch != 0) {
+        // Cooperative fold (all S workgroups of every tile are resident): raise
+        // this split's flag, wait for the tile's other splits, then fold rows
+        // [s BM / S, (s + 1) BM / S) of the tile in split order.
+        uint32_t *tf = p.flags + (size_t)tile * S;
+        if (threadIdx.x == 0) {
+            if (!(p.debug & GEMM_DEBUG_NO_PUBLISH))
+                __hip_atomic_store(tf + s, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            wait_flags<COOP_MAX_SPLITS>(tf, S, p.epoch, p.spin_limit, p.status);
+        }
+        __syncthreads();
+        fold_rows<NW>(p, stg, tile, s, m0, n0, org, span_bytes);
+        if (s == 0)
+            for (int t = 0; t < S; ++t) trace_folded(p, tile, t, tile * S + t);
+        clk.mark(p, 2);
+        clk.done(p);
+        return;
+    }
     if (threadIdx.x == 0) {
         const uint32_t before =
             __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -827,56 +931,98 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
         return;
     }
     // Fold the S partials in split order, ((P0 + P1) + P2) + ..., taking this
-    // workgroup's own split from LDS.  Per round: 4 quads of the thread, and the
-    // loads of up to 4 partials for them in flight before they are added.
-    const bool vec = (p.N & 3) == 0;
-    for (int q0 = 0; q0 < QPT; q0 += 4) {
-        int rr[4], cc[4];
-        bool ok[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int fq = threadIdx.x + NT * (q0 + g);
-            rr[g] = fq >> 5;
-            cc[g] = (fq & 31) * 4;
-            ok[g] = m0 + rr[g] < p.M && n0 + cc[g] < p.N;
+    // workgroup's own split from LDS.  With N % 4 == 0 every quad of the tile is
+    // whole or wholly outside C, and the fold moves 16-byte quads: for S <= 4 all
+    // QPT quads of the thread with the S - 1 other partials in one round of
+    // loads, for larger S rounds of 4 quads with up to 4 partials each.  Any
+    // other N folds element by element.
+    auto quad_rc = [&](int g, int &r, int &c) {
+        const int fq = threadIdx.x + NT * g;
+        r = fq >> 5;
+        c = (fq & 31) * 4;
+    };
+    auto in_c = [&](int r, int c) { return m0 + r < p.M && n0 + c < p.N; };
+    auto get4 = [&](int t, int r, int c) {
+        return get4_coherent(span(p.part + (size_t)t * mn + org, span_bytes), quad_off(r, c));
+    };
+    if ((p.N & 3) != 0) {
+        for (int g = 0; g < QPT; ++g) {
+            int r, c;
+            quad_rc(g, r, c);
+            const f32x4 own = staged_quad(stg, r, c);
+            for (int x = 0; x < 4; ++x) {
+                if (!in_c(r, c + x)) continue;
+                const size_t off = (size_t)(m0 + r) * p.N + n0 + c + x;
+                float sum = 0.f;
+                for (int t = 0; t < S; ++t) {
+                    const float v = t == s ? own[x] : get_coherent(p.part + (size_t)t * mn + off);
+                    sum = t == 0 ? v : sum + v;
+                }
+                p.C[off] = sum;
+            }
         }
-        f32x4 sum[4];
-        for (int t0 = 0; t0 < S; t0 += 4) {
-            f32x4 buf[4][4];
+    } else if (S <= 4) {
+        f32x4 buf[3][QPT];   // buf[j]: the j-th partial other than this split's
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const int t = t0 + tt;
-                if (t >= S || t == s) continue;
-                const __amdgpu_buffer_rsrc_t rt = span(p.part + (size_t)t * mn + org, span_bytes);
-                const float *Pt = p.part + (size_t)t * mn;
+        for (int j = 0; j < 3; ++j) {
+            const int t = j < s ? j : j + 1;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    if (!ok[g]) continue;
-                    const int nv = min(4, p.N - (n0 + cc[g]));
-                    if (vec && nv == 4) {
-                        buf[tt][g] = get4_coherent(rt, quad_off(rr[g], cc[g]));
-                    } else {
-                        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                        for (int x = 0; x < nv; ++x)
-                            v[x] = get_coherent(Pt + (size_t)(m0 + rr[g]) * p.N + n0 + cc[g] + x);
-                        buf[tt][g] = v;
+            for (int g = 0; g < QPT; ++g) {
+                int r, c;
+                quad_rc(g, r, c);
+                buf[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (j < S - 1 && in_c(r, c)) buf[j][g] = get4(t, r, c);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < QPT; ++g) {
+            int r, c;
+            quad_rc(g, r, c);
+            // partial t in split order: this split's from LDS, else buf[t] (t < s)
+            // or buf[t - 1] (t > s)
+            const f32x4 own = staged_quad(stg, r, c);
+            f32x4 sum = s == 0 ? own : buf[0][g];
+            if (S > 1) sum += s == 1 ? own : (s > 1 ? buf[1][g] : buf[0][g]);
+            if (S > 2) sum += s == 2 ? own : (s > 2 ? buf[2][g] : buf[1][g]);
+            if (S > 3) sum += s == 3 ? own : buf[2][g];
+            if (in_c(r, c)) *reinterpret_cast<f32x4 *>(p.C + (size_t)(m0 + r) * p.N + n0 + c) = sum;
+        }
+    } else {
+        for (int q0 = 0; q0 < QPT; q0 += 4) {
+            f32x4 sum[4];
+            for (int t0 = 0; t0 < S; t0 += 4) {
+                f32x4 buf[4][4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const int t = t0 + tt;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        int r, c;
+                        quad_rc(q0 + g, r, c);
+                        buf[tt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (t < S && t != s && in_c(r, c)) buf[tt][g] = get4(t, r, c);
+                    }
+                }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const int t = t0 + tt;
+                    if (t >= S) break;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        int r, c;
+                        quad_rc(q0 + g, r, c);
+                        const f32x4 x = (t == s) ? staged_quad(stg, r, c) : buf[tt][g];
+                        sum[g] = (t == 0) ? x : sum[g] + x;
                     }
                 }
             }
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const int t = t0 + tt;
-                if (t >= S) break;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 x = (t == s) ? staged_quad(stg, rr[g], cc[g]) : buf[tt][g];
-                    sum[g] = (t == 0) ? x : sum[g] + x;
-                }
+            for (int g = 0; g < 4; ++g) {
+                int r, c;
+                quad_rc(q0 + g, r, c);
+                if (in_c(r, c)) *reinterpret_cast<f32x4 *>(p.C + (size_t)(m0 + r) * p.N + n0 + c) = sum[g];
             }
         }
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-            if (ok[g]) put_quad(p.C + (size_t)(m0 + rr[g]) * p.N + n0 + cc[g], sum[g], min(4, p.N - (n0 + cc[g])), vec);
     }
     for (int t = 0; t < S; ++t) trace_folded(p, tile, t, tile * S + t);
     clk.mark(p, 2);
@@ -959,7 +1105,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
             int pos_fold = 1;
             for (int v = u + 1; v < p.units; ++v) {
                 if (unit_start(v, p.q, p.big) >= tile_end) break;
-                if (threadIdx.x == 0) wait_flag(p.flags + v, p.epoch, p.spin_limit, p.status);
+                if (threadIdx.x == 0) wait_flags<1>(p.flags + v, 1, p.epoch, p.spin_limit, p.status);
                 __syncthreads();
                 add_slot<NW>(p.part + (size_t)v * (BM * BN), t);
                 trace_folded(p, tile, pos_fold++, v);
@@ -991,12 +1137,10 @@ __global__ void zero_words(uint32_t *p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// Host-side dispatch.  Kernel shapes (stages x waves):
-//   DP            2 stages x 4 waves  (64 KiB LDS: two workgroups share a CU)
-//   Split-K       4 stages x 8 waves  (128 KiB LDS; the same per-segment
-//                 accumulation order as Stream-K, so the two agree bit for bit
-//                 whenever their segments coincide)
-//   Stream-K      4 stages x 8 waves  (128 KiB LDS: one persistent workgroup per CU)
+// Host-side dispatch.  Every kernel runs 4 LDS stages x 8 waves (128 KiB of
+// LDS, one workgroup per CU).  Split-K and Stream-K share the per-segment
+// accumulation order, so the two agree bit for bit whenever their segments
+// coincide.
 // ---------------------------------------------------------------------------
 namespace {
 

@@ -15,6 +15,11 @@ enum KernelMode : int {
     K_SK_ATOMIC = 3,  // Stream-K, split tiles merged by fp32 atomic adds into zeroed C
 };
 
+// Split-K: splits whose workgroups fold a tile together (row bands) when all
+// are resident: COOP_MIN_SPLITS < S <= COOP_MAX_SPLITS.
+constexpr int COOP_MIN_SPLITS = 4;
+constexpr int COOP_MAX_SPLITS = 16;
+
 // Error bits of the device status word.
 enum : uint32_t { STATUS_TIMEOUT = 1u };
 
@@ -33,15 +38,15 @@ struct KParams {
     int splits;            // Split-K factor S
     int worker_base;       // trace id of this launch's worker 0
     float *part;           // Stream-K slots [units][BM*BN] or Split-K partials [S][M][N]
-    uint32_t *flags;       // Stream-K: flag per unit (epoch-valued)
+    uint32_t *flags;       // Stream-K: flag per unit; Split-K: flag per (tile, split) (epoch-valued)
     uint32_t *counters;    // Split-K: arrival counter per tile (reset by the last arriver)
     uint32_t *status;      // device error word
-    uint32_t epoch;        // value a publishing unit writes into its flag
+    uint32_t epoch;        // value a publishing unit writes into its flag (Split-K: 0 = last-arriver fold)
     uint32_t spin_limit;   // polls before a wait gives up
     uint32_t debug;        // GEMM_DEBUG_* bits
     const int *perm;       // optional workgroup -> worker map
     int *trace;            // optional debug trace (see gemm.h)
-    long long *timing;     // optional per-workgroup {start, end, HW_ID, XCC_ID}
+    long long *timing;     // optional per-workgroup {start, end, HW_ID | XCC_ID << 32, cycles, marks}
     int timing_base;       // entry of this launch's workgroup 0
     int trace_maxseg, trace_maxfold, trace_workers, trace_tiles;
 };

@@ -140,7 +140,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
         p.workers = p.tiles * S;
         p.max_segments = 1;
         p.max_fold = S;
-        // fp32 partials [S, M, N] plus one arrival counter per tile
+        // fp32 partials [S, M, N]; an arrival counter per tile and a flag per (tile, split)
         p.workspace_bytes = S > 1 ? int64_t(S) * M * N * 4 : 0;
         break;
     case GEMM_STREAMK: {
@@ -166,16 +166,22 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
         *why = "internal: no decision";
         return GEMM_ERR_INVALID;
     }
-    // control words: status (64 B), Stream-K flags, Split-K counters, each 256-B aligned
+    // control words: status (64 B), flags, Split-K counters, each 256-B aligned
     p.workspace_bytes += control_bytes(p);
     p.trace_ints = 8 + p.workers * (1 + 4 * int64_t(p.max_segments)) +
                    p.tiles * (1 + int64_t(p.max_fold)) + p.tiles * p.ipt;
     return GEMM_OK;
 }
 
+int64_t flag_words(const gemm_plan_t &p) {
+    // Stream-K: one flag per unit; Split-K: one per (tile, split) for the cooperative fold
+    const int64_t split_flags = p.decision == GEMM_SPLITK ? p.tiles * p.splits : 0;
+    return std::max<int64_t>({p.sk_units, split_flags, 1});
+}
+
 int64_t control_bytes(const gemm_plan_t &p) {
     auto round = [](int64_t b) { return (b + 255) / 256 * 256; };
-    return 256 + round(std::max<int64_t>(p.sk_units, 1) * 4) + round(std::max<int64_t>(p.tiles, 1) * 4);
+    return 256 + round(flag_words(p) * 4) + round(std::max<int64_t>(p.tiles, 1) * 4);
 }
 
 }  // namespace dgw

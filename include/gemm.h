@@ -16,9 +16,12 @@
  *   GEMM_DP       one workgroup per output tile, whole K loop (glossary, "Data-parallel").
  *   GEMM_SPLITK   S workgroups per tile; tile t, split s covers k-iterations
  *                 [s P/S, (s+1) P/S) of the tile's P iterations, stores an fp32
- *                 partial into a [S,M,N] workspace and arrives at the tile's
- *                 counter; the last arriver adds the S partials in split order
- *                 (docc StreamK page, "MMA fragment accumulators (aligned split)").
+ *                 partial into a [S,M,N] workspace, and C receives the S
+ *                 partials added in split order (docc StreamK page, "MMA
+ *                 fragment accumulators (aligned split)").  When all tiles x S
+ *                 workgroups are resident at once (4 < S <= 16, N % 4 == 0) the
+ *                 S splits of a tile raise flags and fold one row band each;
+ *                 otherwise the last arriver at the tile's counter folds it.
  *   GEMM_STREAMK  one persistent workgroup per unit; unit u owns a contiguous,
  *                 equal slice of the flattened (tile x k-iteration) space, the
  *                 first (total mod units) units taking one extra iteration
@@ -83,10 +86,14 @@ extern "C" {
 #define GEMM_ATOMIC        0x100u  /* fp32 atomic adds into a zero-filled C */
 
 /* ---- debug bits for gemm_args_t.debug -------------------------------------------- */
-#define GEMM_DEBUG_NO_PUBLISH 0x1u /* contributors store partials but never raise their
+#define GEMM_DEBUG_NO_PUBLISH 0x1u /* Stream-K contributors and cooperative Split-K
+                                      splits store partials but never raise their
                                       flags: every wait ends at its spin limit and
                                       gemm_sync_status() reports GEMM_ERR_TIMEOUT.
                                       Exercises the failure path; C is not valid.   */
+#define GEMM_DEBUG_LAST_ARRIVER 0x4u /* Split-K: the last arriver folds every tile even
+                                       when all workgroups are resident.  Same
+                                       result bits; exercises that path.           */
 
 /* Tile shape used by every decomposition. */
 #define GEMM_BM 128
@@ -142,9 +149,11 @@ typedef struct gemm_plan_t {
  *   debug:    GEMM_DEBUG_* bits (0 in normal use).
  *   timing:   optional device int64 buffer of at least 8 * plan.workers elements:
  *             workgroup g of the call (launch order: the main grid, then the DP
- *             tiles of a hybrid) writes {start, end, HW_ID, XCC_ID, m0, m1, m2, m3}:
- *             times in ticks of the 100 MHz s_memrealtime clock, HW_ID and XCC_ID
- *             as read from the hardware registers (CU, SE and XCD placement).
+ *             tiles of a hybrid) writes {start, end, HW_ID | XCC_ID << 32, cycles,
+ *             m0, m1, m2, m3}: times in ticks of the 100 MHz s_memrealtime clock,
+ *             HW_ID and XCC_ID as read from the hardware registers (CU, SE and XCD
+ *             placement), cycles = shader-clock ticks (s_memtime) from start to end,
+ *             so cycles / (end - start) * 100 MHz is the workgroup's mean clock.
  *             Marks: DP m0 = mainloop done; Split-K m0 = mainloop done, m1 =
  *             partial stored, m2 = fold done (last arriver); Stream-K m0/m1 =
  *             first segment's mainloop / fixup-and-store done, m2/m3 = the same

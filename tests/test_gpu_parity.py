@@ -239,6 +239,28 @@ def test_unit_order_does_not_change_bits(dg, order):
     assert torch.equal(c.view(torch.int32), ref.view(torch.int32))
 
 
+@pytest.mark.parametrize("name,M,N", [("c2a_m96_s8", None, None), ("c2b_m256_s2", None, None),
+                                      ("c1_sk32", None, None), ("c2a_m96_s8", 200, 392)])
+def test_splitk_cooperative_fold_equals_last_arriver(dg, name, M, N):
+    # the S splits of a tile fold one row band each, or the last arriver folds
+    # the whole tile: both add the partials in split order
+    w = WORKLOADS[name]
+    if M is not None:
+        w = w.with_(M=M, N=N)   # ragged tiles in M and N (N % 4 == 0)
+    splits = w.splits if w.mode == "splitk" else 4
+    A, B = make_operands(w)
+    a, b = A.to(DEV), B.to(DEV)
+    say(f"  cooperative vs last-arriver fold {w.name} {w.M}x{w.N}x{w.K} S={splits}")
+    full0, c0 = guarded_output(w.M, w.N, DEV)
+    full1, c1 = guarded_output(w.M, w.N, DEV)
+    dg.gemm_tensors(a, b, c0, b_layout=w.b_layout, mode="splitk", splits=splits)
+    dg.gemm_tensors(a, b, c1, b_layout=w.b_layout, mode="splitk", splits=splits, debug=dg.GEMM_DEBUG_LAST_ARRIVER)
+    assert dg.gemm_sync_status() == 0
+    assert guards_intact(full0, w.M, w.N) and guards_intact(full1, w.M, w.N)
+    assert torch.equal(c0.view(torch.int32), c1.view(torch.int32))
+    assert_parity(c0, A, B, w)
+
+
 def test_streamk_equals_splitk_bits_when_segments_coincide(dg):
     # 8 tiles x 32 iterations over 32 units = 4 segments of 8 per tile, the same k
     # ranges as Split-K with S = 4; both fold ((P0 + P1) + P2) + P3 in k order
@@ -281,6 +303,21 @@ def test_bounded_wait_reports_timeout(dg):
     # the status is cleared and the next call is healthy
     full, c2 = guarded_output(w.M, w.N, DEV)
     dg.gemm_tensors(a, b, c2, mode="streamk", splits=12)
+    assert dg.gemm_sync_status() == 0
+    assert_parity(c2, A, B, w)
+
+
+def test_bounded_wait_reports_timeout_splitk(dg):
+    w = WORKLOADS["c2a_m96_s8"].with_(name="timeout_splitk")   # S = 8: cooperative fold
+    A, B = make_operands(w)
+    a, b = A.to(DEV), B.to(DEV)
+    c = torch.empty((w.M, w.N), dtype=torch.float32, device=DEV)
+    say("  forced timeout (cooperative Split-K splits never raise flags, spin limit 2000 polls)")
+    dg.gemm_tensors(a, b, c, b_layout=w.b_layout, mode="splitk", splits=8, spin_limit=2000,
+                    debug=dg.GEMM_DEBUG_NO_PUBLISH)
+    assert dg.gemm_sync_status() == dg.GEMM_ERR_TIMEOUT
+    full, c2 = guarded_output(w.M, w.N, DEV)
+    dg.gemm_tensors(a, b, c2, b_layout=w.b_layout, mode="splitk", splits=8)
     assert dg.gemm_sync_status() == 0
     assert_parity(c2, A, B, w)
 
