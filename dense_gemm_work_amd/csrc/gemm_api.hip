@@ -69,7 +69,7 @@ struct DeviceState {
     int64_t cap_units = 0, cap_tiles = 0;
     void *data = nullptr;
     int64_t cap_data = 0;
-    int bpc[2][2][4] = {};         // resident workgroups per CU, 0 = not yet queried
+    int bpc[2][2][5] = {};         // resident workgroups per CU, 0 = not yet queried
 };
 
 std::mutex g_mu;
@@ -179,7 +179,7 @@ int run(const gemm_args_t &a) {
                             a.num_cus > 0 ? a.num_cus : 256, &p, &why);
     if (rc != GEMM_OK) return fail(rc, why);
     if (a.num_cus < 0) return fail(GEMM_ERR_INVALID, "num_cus must be >= 0");
-    if ((a.debug & ~(GEMM_DEBUG_NO_PUBLISH | GEMM_DEBUG_LAST_ARRIVER)) != 0)
+    if ((a.debug & ~(GEMM_DEBUG_NO_PUBLISH | GEMM_DEBUG_LAST_ARRIVER | GEMM_DEBUG_TILE_DP)) != 0)
         return fail(GEMM_ERR_INVALID, "unknown debug bits");
     if (a.M == 0 || a.N == 0) return GEMM_OK;
     if ((rc = check_operands(a)) != GEMM_OK) return rc;
@@ -284,8 +284,17 @@ int run(const gemm_args_t &a) {
 
     if (p.decision == GEMM_DP) {
         kp.ntiles = (int)p.tiles;
-        if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_DP, (int)p.tiles, kp, stream)) != hipSuccess)
+        // 2x2 tile groups when the tile grid splits into them and they still fill
+        // every CU (the group count is at least the CU count)
+        const bool groups = p.tiles_m % 2 == 0 && p.tiles_n % 2 == 0 && p.tiles / 4 >= ncu &&
+                            !(a.debug & GEMM_DEBUG_TILE_DP);
+        if (groups) {
+            if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_DP_GROUP, (int)(p.tiles / 4), kp, stream)) !=
+                hipSuccess)
+                return fail_hip(e, "launch DP tile-group kernel");
+        } else if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_DP, (int)p.tiles, kp, stream)) != hipSuccess) {
             return fail_hip(e, "launch DP kernel");
+        }
     } else if (p.decision == GEMM_SPLITK) {
         kp.ntiles = (int)p.tiles;
         // With every (tile, split) workgroup resident at once and more than 4

@@ -796,6 +796,276 @@ __global__ __launch_bounds__(64 * NW) void gemm_dp(KParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Data-parallel tile groups: one workgroup computes a 2x2 group of 128x128
+// tiles (a 256x256 block of C) over the whole K, for launches with enough
+// tiles to fill the chip four times over.  Each tile is still computed whole
+// by one workgroup with no fixup (the data-parallel schedule is unchanged);
+// what changes is the operand traffic per flop.  A 256x256x64 step moves
+// 64 KiB global -> LDS (half of what four 128x128 steps move) and, with eight
+// waves of 128x64, 192 KiB LDS -> registers (three quarters).  On MI355X the
+// clock under a dense MFMA load is set by that traffic, so the group runs
+// closer to the matrix-core bound (CUTLASS optimisation guide: larger
+// threadblock tiles raise arithmetic intensity).
+//
+// Waves: wave w owns rows 128 (w & 1) .. +128 and columns 64 (w >> 1) .. +64 of
+// the group, 4 x 2 blocks of 32 x 32 (eight accumulators), and issues all four
+// 16-wide k-steps of each iteration (no k-split, no merge).  Two LDS stages of
+// (A slab [256 x 64] | B slab [64 x 256]) = 64 KiB each; iteration i + 2 is
+// loaded into the stage iteration i used, after the barrier that ends
+// iteration i; within an iteration the fragments of k-step j + 1 are read
+// while the MFMAs of k-step j run.
+// ---------------------------------------------------------------------------
+constexpr int GB = 2 * BM;                     // group edge: 256
+constexpr int G_SLAB = GB * BK * 2;            // bytes of one operand slab of one stage: 32 KiB
+constexpr int G_NS = 2;                        // stages
+constexpr int G_BREG = G_NS * G_SLAB;          // B slabs start at 64 KiB
+constexpr int G_NW = 8;                        // waves
+
+struct GAcc {
+    f32x16 v[4][2];   // [32-row block][32-column block] of the wave's 128x64
+};
+
+template <int DT, int BL>
+struct GroupLoop {
+    static constexpr int DPW = 4;              // DMA instructions per wave and operand slab
+    static constexpr int DPI = 2 * DPW;        // per iteration
+
+    const KParams &p;
+    uint32_t lds0;
+    int lane, wave;
+    uint32_t aoff[4];                          // A fragment read address per k-step (stage 0, row block 0)
+    uint32_t boff[4];                          // B [N,K]: per k-step (column block 0); B [K,N]: per column block x 2
+    uint32_t adma[DPW], bdma[DPW];             // per-lane global byte offsets of the wave's loads at k = 0
+    int a_kc[DPW], b_kc[DPW];                  // first k of the lane's chunk (B [K,N]: the lane's k-row)
+    const char *a_base, *b_base;
+    uint32_t a_rows_bytes, b_rows_bytes;
+
+    __device__ __forceinline__ GroupLoop(const KParams &p_, char *lds, int m0, int n0) : p(p_) {
+        lds0 = (uint32_t)reinterpret_cast<uintptr_t>((const lds_void *)lds);
+        lane = threadIdx.x & 63;
+        wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+        const int wm = wave & 1, wn = wave >> 1;
+        const int K = p.K, N = p.N;
+        const int r32 = lane & 31, hk = lane >> 5;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const uint32_t rowpart = (uint32_t)(r32 * 128 + ((((2 * kk + hk) ^ kswz(r32)) & 7) << 4));
+            aoff[kk] = lds0 + wm * 128 * 128 + rowpart;
+            if constexpr (BL == 1) boff[kk] = lds0 + G_BREG + wn * 64 * 128 + rowpart;
+        }
+        if constexpr (BL == 0) {
+            // 256-column k-rows of 512 bytes (32 chunks), chunk c of k-row r at c ^ nswz(r)
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                const int n = wn * 64 + jb * 32 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+                const int r = 8 * hk + ((lane & 15) >> 2);
+                boff[jb] = lds0 + G_BREG + r * 512 + ((((n >> 3) ^ nswz(r)) & 31) << 4) + ((n & 7) << 1);
+            }
+        }
+        const int first = wave * DPW;
+        a_base = reinterpret_cast<const char *>(p.A) + (size_t)m0 * K * 2;
+        a_rows_bytes = (uint32_t)(min(GB, p.M - m0) * K * 2);
+#pragma unroll
+        for (int x = 0; x < DPW; ++x) {
+            const int r = 8 * (first + x) + (lane >> 3);          // 0..255
+            const int c = (lane & 7) ^ kswz(r);
+            adma[x] = (uint32_t)(r * K + 8 * c) * 2;
+            a_kc[x] = 8 * c;
+            if constexpr (BL == 1) {
+                bdma[x] = adma[x];
+                b_kc[x] = 8 * c;
+            } else {
+                const int rb = 2 * (first + x) + (lane >> 5);      // k-row 0..63
+                const int cb = (lane & 31) ^ nswz(rb);
+                bdma[x] = n0 + 8 * cb >= N ? OOB : (uint32_t)(rb * N + 8 * cb) * 2;
+                b_kc[x] = rb;
+            }
+        }
+        if constexpr (BL == 1) {
+            b_base = reinterpret_cast<const char *>(p.B) + (size_t)n0 * K * 2;
+            b_rows_bytes = (uint32_t)(min(GB, N - n0) * K * 2);
+        } else {
+            b_base = reinterpret_cast<const char *>(p.B) + (size_t)n0 * 2;
+            b_rows_bytes = 0;
+        }
+    }
+
+    // Loads of K-slab `slab` into stage `st`; RAGGED: chunks at or beyond K read zeros.
+    template <bool RAGGED>
+    __device__ __forceinline__ void issue(int slab, int st) const {
+        const int kb = slab * BK;
+        const int first = wave * DPW;
+        const i32x4 ra = make_rsrc(a_base + (size_t)kb * 2, a_rows_bytes - kb * 2);
+        i32x4 rb;
+        if constexpr (BL == 1) {
+            rb = make_rsrc(b_base + (size_t)kb * 2, b_rows_bytes - kb * 2);
+        } else {
+            const int krows = min(BK, p.K - kb);
+            rb = make_rsrc(b_base + (size_t)kb * p.N * 2, (uint32_t)(krows * p.N * 2));
+        }
+        const uint32_t a_dst = lds0 + st * G_SLAB + first * 1024;
+        const uint32_t b_dst = lds0 + G_BREG + st * G_SLAB + first * 1024;
+#pragma unroll
+        for (int x = 0; x < DPW; ++x) dma16(ra, a_dst + x * 1024, !RAGGED || kb + a_kc[x] < p.K ? adma[x] : OOB);
+#pragma unroll
+        for (int x = 0; x < DPW; ++x) {
+            uint32_t off = bdma[x];
+            if constexpr (RAGGED && BL == 1) off = kb + b_kc[x] < p.K ? off : OOB;
+            dma16(rb, b_dst + x * 1024, off);
+        }
+    }
+
+    struct Frags {
+        u32x4 a[4];   // [32-row block]
+        u32x4 b[2];   // [32-column block]
+    };
+
+    // Fragments of k-step KK of stage ST.
+    template <int ST, int KK>
+    __device__ __forceinline__ void read(Frags &f) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f.a[i] = lds_b128<ST * G_SLAB>(aoff[KK] + i * 4096);
+        if constexpr (BL == 1) {
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) f.b[jb] = lds_b128<ST * G_SLAB>(boff[KK] + jb * 4096);
+        } else {
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                const u32x2 h0 = lds_tr16<ST * G_SLAB + KK * 16 * 512>(boff[jb]);
+                const u32x2 h1 = lds_tr16<ST * G_SLAB + KK * 16 * 512 + 4 * 512>(boff[jb]);
+                f.b[jb] = u32x4{h0[0], h0[1], h1[0], h1[1]};
+            }
+        }
+    }
+
+    static __device__ __forceinline__ void mma(const Frags &f, GAcc &acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) acc.v[i][jb] = mfma<DT>(f.a[i], f.b[jb], acc.v[i][jb]);
+    }
+};
+
+// acc += the group's A rows . B columns over all ipt iterations.  Ends with a
+// barrier (LDS free on return).
+template <int DT, int BL, bool RAGGED>
+__device__ __forceinline__ void group_loop(const KParams &p, char *lds, int m0, int n0, GAcc &acc) {
+    using GL = GroupLoop<DT, BL>;
+    const int n = p.ipt;
+    if (n <= 0) return;
+    const GL gl(p, lds, m0, n0);
+    typename GL::Frags f[2];
+    gl.template issue<RAGGED>(0, 0);
+    if (n > 1) {
+        gl.template issue<RAGGED>(1, 1);
+        wait_vm_lgkm<GL::DPI>();
+    } else {
+        wait_vm_lgkm<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    gl.template read<0, 0>(f[0]);
+    // One iteration on stage ST: k-steps 0..2 read the next k-step's fragments
+    // and multiply the current ones; k-step 3 first hands the stage over: wait
+    // for this wave's loads of i + 1 and reads of (i, 3), barrier (every wave's
+    // loads of i + 1 landed and every wave is done reading stage ST), load
+    // iteration i + 2 into stage ST, read (i + 1, 0).
+    auto iter = [&](int i, auto ST) {
+        constexpr int st = decltype(ST)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        gl.template read<st, 1>(f[1]);
+        GL::mma(f[0], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        gl.template read<st, 2>(f[0]);
+        GL::mma(f[1], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        gl.template read<st, 3>(f[1]);
+        GL::mma(f[0], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < n) {
+            wait_vm_lgkm<0>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            gl.template read<st ^ 1, 0>(f[0]);
+            if (i + 2 < n) gl.template issue<RAGGED>(i + 2, st);
+        }
+        GL::mma(f[1], acc);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int i = 0; i < n; i += 2) {
+        iter(i, std::integral_constant<int, 0>());
+        if (i + 1 < n) iter(i + 1, std::integral_constant<int, 1>());
+    }
+    wait_stage0();
+}
+
+// The 128x128 tile with tile-grid coordinates (tm, tn): the inverse of tile_origin.
+__device__ __forceinline__ int tile_id(const KParams &p, int tm, int tn) {
+    const int gm_full = p.group_m > 0 ? p.group_m : p.tiles_m;
+    const int g = tm / gm_full;
+    const int first = g * gm_full;
+    const int gm = min(gm_full, p.tiles_m - first);
+    return g * gm_full * p.tiles_n + tn * gm + (tm - first);
+}
+
+// Group g of the (tiles_m / 2) x (tiles_n / 2) group grid, numbered like
+// tile_origin numbers tiles (bands of group_m / 2 group rows, column by column).
+__device__ __forceinline__ void group_origin(const KParams &p, int g, int &m0, int &n0) {
+    const int gms = p.tiles_m / 2, gns = p.tiles_n / 2;
+    const int gm_full = p.group_m > 1 ? p.group_m / 2 : gms;
+    const int per_band = gm_full * gns;
+    const int band = g / per_band;
+    const int first = band * gm_full;
+    const int gm = min(gm_full, gms - first);
+    const int w = g - band * per_band;
+    m0 = (first + w % gm) * GB;
+    n0 = (w / gm) * GB;
+}
+
+// Launch: ntiles / 4 workgroups, tiles_m and tiles_n even, tile_base 0.
+template <int DT, int BL>
+__global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
+    __shared__ __attribute__((aligned(16))) char lds[G_NS * 2 * G_SLAB];
+    const WgClock clk(p);
+    const int g = worker_of(p, p.ntiles / 4);
+    int m0, n0;
+    group_origin(p, g, m0, n0);
+    GAcc acc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc.v[i][j][e] = 0.0f;
+    if (p.K % BK == 0) group_loop<DT, BL, false>(p, lds, m0, n0, acc);
+    else group_loop<DT, BL, true>(p, lds, m0, n0, acc);
+    clk.mark(p, 0);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (row < p.M && col < p.N) p.C[(size_t)row * p.N + col] = acc.v[i][j][e];
+            }
+        }
+    if (p.trace && threadIdx.x == 0) {
+        // the four tiles of the group, each a whole-K data-parallel tile
+        for (int q = 0; q < 4; ++q) {
+            const int tile = tile_id(p, m0 / BM + (q & 1), n0 / BN + (q >> 1));
+            trace_segment(p, p.worker_base + tile, 0, tile, 0, p.ipt, 0);
+            trace_folded(p, tile, 0, p.worker_base + tile);
+            int *cov = trace_cov(p, tile);
+            for (int k = 0; k < p.ipt; ++k) atomicAdd(cov + k, 1);
+        }
+    }
+    clk.done(p);
+}
+
+// ---------------------------------------------------------------------------
 // Split-K: worker w = tile * S + s covers k-iterations [s P / S, (s+1) P / S).
 // ---------------------------------------------------------------------------
 // Split-K cooperative fold: split s of a tile sums rows [s BM / S, (s + 1) BM / S)
@@ -1137,10 +1407,10 @@ __global__ void zero_words(uint32_t *p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// Host-side dispatch.  Every kernel runs 4 LDS stages x 8 waves (128 KiB of
-// LDS, one workgroup per CU).  Split-K and Stream-K share the per-segment
-// accumulation order, so the two agree bit for bit whenever their segments
-// coincide.
+// Host-side dispatch.  Every kernel runs 8 waves on 128 KiB of LDS (one
+// workgroup per CU): 4 stages of 128x128 tiles, or 2 stages of 2x2 tile groups.
+// Split-K and Stream-K share the per-segment accumulation order, so the two
+// agree bit for bit whenever their segments coincide.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -1157,6 +1427,7 @@ KernelFn pick(int kmode, Shape &shape) {
     case K_SPLITK: shape = {4, 8}; return gemm_splitk<DT, BL, 4, 8>;
     case K_SK: shape = {4, 8}; return gemm_streamk<DT, BL, 4, 8, false>;
     case K_SK_ATOMIC: shape = {4, 8}; return gemm_streamk<DT, BL, 4, 8, true>;
+    case K_DP_GROUP: shape = {G_NS, G_NW}; return gemm_dp_group<DT, BL>;
     default: return nullptr;
     }
 }

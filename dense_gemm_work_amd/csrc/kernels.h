@@ -13,6 +13,7 @@ enum KernelMode : int {
     K_SPLITK = 1,     // split s of tile t; fp32 partial [S,M,N]; last arriver folds in split order
     K_SK = 2,         // Stream-K, deterministic turnstile through per-unit partial slots
     K_SK_ATOMIC = 3,  // Stream-K, split tiles merged by fp32 atomic adds into zeroed C
+    K_DP_GROUP = 4,   // whole-K tiles, one 2x2 group of tiles (256x256) per workgroup
 };
 
 // Split-K: splits whose workgroups fold a tile together (row bands) when all

@@ -94,6 +94,8 @@ extern "C" {
 #define GEMM_DEBUG_LAST_ARRIVER 0x4u /* Split-K: the last arriver folds every tile even
                                        when all workgroups are resident.  Same
                                        result bits; exercises that path.           */
+#define GEMM_DEBUG_TILE_DP 0x8u /* data-parallel launches run one 128x128 tile per
+                                   workgroup even where 2x2 tile groups apply.     */
 
 /* Tile shape used by every decomposition. */
 #define GEMM_BM 128

@@ -100,6 +100,26 @@ def test_c4_heuristic_dp(dg):
     assert_parity(c, A, B, w, rows=sample_rows(w.M, 10))
 
 
+@pytest.mark.parametrize("M,N,K,layout,cus", [
+    (4096, 4096, 320, "kn", 0),      # 1024 tiles -> 256 groups, odd iteration count
+    (4000, 4064, 200, "kn", 0),      # ragged M, N and K (K % 64 = 8)
+    (4096, 4096, 192, "nk", 0),      # B [N,K]
+    (1024, 1024, 512, "kn", 16),     # 64 tiles on 16 CUs
+])
+def test_dp_tile_groups(dg, M, N, K, layout, cus):
+    # data-parallel launches with at least 4 x CUs tiles run 2x2 tile groups per
+    # workgroup; checked against the oracle and against one-tile workgroups
+    w = WORKLOADS["c4_large_dp"].with_(name="dp_groups", M=M, N=N, K=K, b_layout=layout)
+    A, B, c = run(dg, w, mode="dp", splits=0, num_cus=cus)
+    rows = sample_rows(M, 12) + [M - 2, M - 129]
+    assert_parity(c, A, B, w, rows=sorted(set(rows)))
+    _, c_tile = guarded_output(M, N, DEV)
+    dg.gemm_tensors(A.to(DEV), B.to(DEV), c_tile, b_layout=layout, mode="dp", splits=0, num_cus=cus,
+                    debug=dg.GEMM_DEBUG_TILE_DP)
+    assert dg.gemm_sync_status() == 0
+    assert_parity(c_tile, A, B, w, rows=sorted(set(rows)))
+
+
 @pytest.mark.parametrize("atomic", [False, True])
 def test_c5_streamk_fp16(dg, atomic):
     w = WORKLOADS["c5_longk_fp16"]
@@ -174,6 +194,7 @@ TRACE_CASES = [
     ("ragged-7u", 300, 200, 320, "streamk", 7, 256, False),
     ("hybrid", 1408, 768, 1024, "heuristic", 0, 20, False),
     ("dp", 640, 384, 256, "dp", 0, 256, False),
+    ("dp-groups", 1024, 1024, 256, "dp", 0, 16, False),   # 2x2 tile groups (64 tiles, 16 CUs)
 ]
 
 
