@@ -812,29 +812,38 @@ __global__ __launch_bounds__(64 * NW) void gemm_dp(KParams p) {
 // 16-wide k-steps of each iteration (no k-split, no merge).  Two LDS stages of
 // (A slab [256 x 64] | B slab [64 x 256]) = 64 KiB each; iteration i + 2 is
 // loaded into the stage iteration i used, after the barrier that ends
-// iteration i; within an iteration the fragments of k-step j + 1 are read
-// while the MFMAs of k-step j run.
+// iteration i, one load between each pair of k-step-3 MFMAs; within an
+// iteration the fragments of k-step j + 1 are read while the MFMAs of k-step j
+// run.
 // ---------------------------------------------------------------------------
 constexpr int GB = 2 * BM;                     // group edge: 256
 constexpr int G_SLAB = GB * BK * 2;            // bytes of one operand slab of one stage: 32 KiB
 constexpr int G_NS = 2;                        // stages
 constexpr int G_BREG = G_NS * G_SLAB;          // B slabs start at 64 KiB
-constexpr int G_NW = 8;                        // waves
+// Waves per group: 8 of 128x64 (two per SIMD).  GroupLoop also builds with 4
+// waves of 128x128 (one per SIMD, accumulators in AGPRs, a third less LDS read
+// traffic); measured on the 8192^3 launch the eight-wave form is 2 % faster.
+constexpr int G_NW = 8;
 
+template <int NW>
 struct GAcc {
-    f32x16 v[4][2];   // [32-row block][32-column block] of the wave's 128x64
+    static constexpr int JB = NW == 4 ? 4 : 2; // 32-column blocks of a wave
+    f32x16 v[4][JB];                           // [32-row block][32-column block]
 };
 
-template <int DT, int BL>
+template <int DT, int BL, int NW>
 struct GroupLoop {
-    static constexpr int DPW = 4;              // DMA instructions per wave and operand slab
-    static constexpr int DPI = 2 * DPW;        // per iteration
+    static constexpr int WCOLS = NW == 4 ? 128 : 64;   // columns of a wave
+    static constexpr int JB = WCOLS / 32;              // 32-column blocks of a wave
+    static constexpr int DPW = 32 / NW;                // DMA instructions per wave and operand slab
+    static constexpr int DPI = 2 * DPW;                // per iteration
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
 
     const KParams &p;
     uint32_t lds0;
     int lane, wave;
     uint32_t aoff[4];                          // A fragment read address per k-step (stage 0, row block 0)
-    uint32_t boff[4];                          // B [N,K]: per k-step (column block 0); B [K,N]: per column block x 2
+    uint32_t boff[4];                          // B [N,K]: per k-step (column block 0); B [K,N]: per column block
     uint32_t adma[DPW], bdma[DPW];             // per-lane global byte offsets of the wave's loads at k = 0
     int a_kc[DPW], b_kc[DPW];                  // first k of the lane's chunk (B [K,N]: the lane's k-row)
     const char *a_base, *b_base;
@@ -851,13 +860,13 @@ struct GroupLoop {
         for (int kk = 0; kk < 4; ++kk) {
             const uint32_t rowpart = (uint32_t)(r32 * 128 + ((((2 * kk + hk) ^ kswz(r32)) & 7) << 4));
             aoff[kk] = lds0 + wm * 128 * 128 + rowpart;
-            if constexpr (BL == 1) boff[kk] = lds0 + G_BREG + wn * 64 * 128 + rowpart;
+            if constexpr (BL == 1) boff[kk] = lds0 + G_BREG + wn * WCOLS * 128 + rowpart;
         }
         if constexpr (BL == 0) {
             // 256-column k-rows of 512 bytes (32 chunks), chunk c of k-row r at c ^ nswz(r)
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                const int n = wn * 64 + jb * 32 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+            for (int jb = 0; jb < JB; ++jb) {
+                const int n = wn * WCOLS + jb * 32 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
                 const int r = 8 * hk + ((lane & 15) >> 2);
                 boff[jb] = lds0 + G_BREG + r * 512 + ((((n >> 3) ^ nswz(r)) & 31) << 4) + ((n & 7) << 1);
             }
@@ -890,34 +899,49 @@ struct GroupLoop {
         }
     }
 
-    // Loads of K-slab `slab` into stage `st`; RAGGED: chunks at or beyond K read zeros.
+    // Buffer resources and LDS destinations of the loads of K-slab `slab` into stage `st`.
+    struct Issue {
+        i32x4 ra, rb;
+        uint32_t a_dst, b_dst;
+        int kb;
+    };
+    __device__ __forceinline__ Issue prepare(int slab, int st) const {
+        Issue q;
+        q.kb = slab * BK;
+        q.ra = make_rsrc(a_base + (size_t)q.kb * 2, a_rows_bytes - q.kb * 2);
+        if constexpr (BL == 1) {
+            q.rb = make_rsrc(b_base + (size_t)q.kb * 2, b_rows_bytes - q.kb * 2);
+        } else {
+            const int krows = min(BK, p.K - q.kb);
+            q.rb = make_rsrc(b_base + (size_t)q.kb * p.N * 2, (uint32_t)(krows * p.N * 2));
+        }
+        q.a_dst = lds0 + st * G_SLAB + wave * DPW * 1024;
+        q.b_dst = lds0 + G_BREG + st * G_SLAB + wave * DPW * 1024;
+        return q;
+    }
+    // Load number x of the iteration (A slab loads first, then B); RAGGED: chunks
+    // at or beyond K read zeros.
+    template <bool RAGGED>
+    __device__ __forceinline__ void issue_one(const Issue &q, int x) const {
+        if (x < DPW) {
+            dma16(q.ra, q.a_dst + x * 1024, !RAGGED || q.kb + a_kc[x] < p.K ? adma[x] : OOB);
+        } else {
+            const int y = x - DPW;
+            uint32_t off = bdma[y];
+            if constexpr (RAGGED && BL == 1) off = q.kb + b_kc[y] < p.K ? off : OOB;
+            dma16(q.rb, q.b_dst + y * 1024, off);
+        }
+    }
     template <bool RAGGED>
     __device__ __forceinline__ void issue(int slab, int st) const {
-        const int kb = slab * BK;
-        const int first = wave * DPW;
-        const i32x4 ra = make_rsrc(a_base + (size_t)kb * 2, a_rows_bytes - kb * 2);
-        i32x4 rb;
-        if constexpr (BL == 1) {
-            rb = make_rsrc(b_base + (size_t)kb * 2, b_rows_bytes - kb * 2);
-        } else {
-            const int krows = min(BK, p.K - kb);
-            rb = make_rsrc(b_base + (size_t)kb * p.N * 2, (uint32_t)(krows * p.N * 2));
-        }
-        const uint32_t a_dst = lds0 + st * G_SLAB + first * 1024;
-        const uint32_t b_dst = lds0 + G_BREG + st * G_SLAB + first * 1024;
+        const Issue q = prepare(slab, st);
 #pragma unroll
-        for (int x = 0; x < DPW; ++x) dma16(ra, a_dst + x * 1024, !RAGGED || kb + a_kc[x] < p.K ? adma[x] : OOB);
-#pragma unroll
-        for (int x = 0; x < DPW; ++x) {
-            uint32_t off = bdma[x];
-            if constexpr (RAGGED && BL == 1) off = kb + b_kc[x] < p.K ? off : OOB;
-            dma16(rb, b_dst + x * 1024, off);
-        }
+        for (int x = 0; x < DPI; ++x) issue_one<RAGGED>(q, x);
     }
 
     struct Frags {
         u32x4 a[4];   // [32-row block]
-        u32x4 b[2];   // [32-column block]
+        u32x4 b[JB];  // [32-column block]
     };
 
     // Fragments of k-step KK of stage ST.
@@ -927,10 +951,10 @@ struct GroupLoop {
         for (int i = 0; i < 4; ++i) f.a[i] = lds_b128<ST * G_SLAB>(aoff[KK] + i * 4096);
         if constexpr (BL == 1) {
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) f.b[jb] = lds_b128<ST * G_SLAB>(boff[KK] + jb * 4096);
+            for (int jb = 0; jb < JB; ++jb) f.b[jb] = lds_b128<ST * G_SLAB>(boff[KK] + jb * 4096);
         } else {
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
+            for (int jb = 0; jb < JB; ++jb) {
                 const u32x2 h0 = lds_tr16<ST * G_SLAB + KK * 16 * 512>(boff[jb]);
                 const u32x2 h1 = lds_tr16<ST * G_SLAB + KK * 16 * 512 + 4 * 512>(boff[jb]);
                 f.b[jb] = u32x4{h0[0], h0[1], h1[0], h1[1]};
@@ -938,19 +962,34 @@ struct GroupLoop {
         }
     }
 
-    static __device__ __forceinline__ void mma(const Frags &f, GAcc &acc) {
+    static __device__ __forceinline__ void mma(const Frags &f, GAcc<NW> &acc) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) acc.v[i][jb] = mfma<DT>(f.a[i], f.b[jb], acc.v[i][jb]);
+            for (int jb = 0; jb < JB; ++jb) acc.v[i][jb] = mfma<DT>(f.a[i], f.b[jb], acc.v[i][jb]);
+    }
+    // The MFMAs of f, with the DPI loads of `q` (when `load`) issued between
+    // them so that the matrix pipe keeps running while they go out.
+    template <bool RAGGED>
+    __device__ __forceinline__ void mma_issue(const Frags &f, GAcc<NW> &acc, bool load, const Issue &q) const {
+        static_assert(4 * JB == DPI, "one load per MFMA");
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) {
+                acc.v[i][jb] = mfma<DT>(f.a[i], f.b[jb], acc.v[i][jb]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (load) issue_one<RAGGED>(q, i * JB + jb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
     }
 };
 
 // acc += the group's A rows . B columns over all ipt iterations.  Ends with a
 // barrier (LDS free on return).
-template <int DT, int BL, bool RAGGED>
-__device__ __forceinline__ void group_loop(const KParams &p, char *lds, int m0, int n0, GAcc &acc) {
-    using GL = GroupLoop<DT, BL>;
+template <int DT, int BL, int NW, bool RAGGED>
+__device__ __forceinline__ void group_loop(const KParams &p, char *lds, int m0, int n0, GAcc<NW> &acc) {
+    using GL = GroupLoop<DT, BL, NW>;
     const int n = p.ipt;
     if (n <= 0) return;
     const GL gl(p, lds, m0, n0);
@@ -967,8 +1006,9 @@ __device__ __forceinline__ void group_loop(const KParams &p, char *lds, int m0, 
     // One iteration on stage ST: k-steps 0..2 read the next k-step's fragments
     // and multiply the current ones; k-step 3 first hands the stage over: wait
     // for this wave's loads of i + 1 and reads of (i, 3), barrier (every wave's
-    // loads of i + 1 landed and every wave is done reading stage ST), load
-    // iteration i + 2 into stage ST, read (i + 1, 0).
+    // loads of i + 1 landed and every wave is done reading stage ST), read
+    // (i + 1, 0), then multiply k-step 3 while loading iteration i + 2 into
+    // stage ST.
     auto iter = [&](int i, auto ST) {
         constexpr int st = decltype(ST)::value;
         __builtin_amdgcn_sched_barrier(0);
@@ -986,9 +1026,8 @@ __device__ __forceinline__ void group_loop(const KParams &p, char *lds, int m0, 
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
             gl.template read<st ^ 1, 0>(f[0]);
-            if (i + 2 < n) gl.template issue<RAGGED>(i + 2, st);
         }
-        GL::mma(f[1], acc);
+        gl.template mma_issue<RAGGED>(f[1], acc, i + 2 < n, gl.prepare(i + 2, st));
         __builtin_amdgcn_sched_barrier(0);
     };
     for (int i = 0; i < n; i += 2) {
@@ -1025,27 +1064,28 @@ __device__ __forceinline__ void group_origin(const KParams &p, int g, int &m0, i
 template <int DT, int BL>
 __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
     __shared__ __attribute__((aligned(16))) char lds[G_NS * 2 * G_SLAB];
+    constexpr int JB = GAcc<G_NW>::JB;
     const WgClock clk(p);
     const int g = worker_of(p, p.ntiles / 4);
     int m0, n0;
     group_origin(p, g, m0, n0);
-    GAcc acc;
+    GAcc<G_NW> acc;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < JB; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc.v[i][j][e] = 0.0f;
-    if (p.K % BK == 0) group_loop<DT, BL, false>(p, lds, m0, n0, acc);
-    else group_loop<DT, BL, true>(p, lds, m0, n0, acc);
+    if (p.K % BK == 0) group_loop<DT, BL, G_NW, false>(p, lds, m0, n0, acc);
+    else group_loop<DT, BL, G_NW, true>(p, lds, m0, n0, acc);
     clk.mark(p, 0);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+        for (int j = 0; j < JB; ++j) {
+            const int col = n0 + wn * JB * 32 + j * 32 + (lane & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
