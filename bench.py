@@ -164,6 +164,10 @@ def shape_arms(dg, name, steps, warmup):
 
 def kernel_name(dg, plan, w):
     kind = {dg.GEMM_DP: "gemm_dp", dg.GEMM_SPLITK: "gemm_splitk", dg.GEMM_STREAMK: "gemm_streamk"}[plan.decision]
+    # the library runs 2x2 tile groups when the tile grid splits into them and they fill every CU
+    if plan.decision == dg.GEMM_DP and plan.tiles_m % 2 == 0 and plan.tiles_n % 2 == 0 \
+            and plan.tiles // 4 >= dg.gemm_num_cus():
+        kind = "gemm_dp_group"
     lay = "B[K,N]" if w.b_layout == "kn" else "B[N,K]"
     fix = (", atomic" if plan.atomic else ", deterministic") if plan.decision == dg.GEMM_STREAMK else ""
     return f"{kind}<{w.dtype}, {lay}{fix}>"
