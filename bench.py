@@ -148,6 +148,9 @@ def shape_arms(dg, name, steps, warmup):
     if name.startswith("c5"):
         arms["streamk_det"] = ("streamk", 0, False)
         arms["streamk_atomic"] = ("streamk", 0, True)
+    if name.startswith("x1"):
+        arms["heuristic"] = ("heuristic", 0, False)
+        arms["streamk"] = ("streamk", 0, False)
     out = {"M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype, "b_layout": w.b_layout}
     for arm, (mode, splits, atomic) in arms.items():
         call = Call(dg, a, b, c, w.b_layout, mode, splits, atomic)
@@ -164,9 +167,10 @@ def shape_arms(dg, name, steps, warmup):
 
 def kernel_name(dg, plan, w):
     kind = {dg.GEMM_DP: "gemm_dp", dg.GEMM_SPLITK: "gemm_splitk", dg.GEMM_STREAMK: "gemm_streamk"}[plan.decision]
-    # the library runs 2x2 tile groups when the tile grid splits into them and they fill every CU
-    if plan.decision == dg.GEMM_DP and plan.tiles_m % 2 == 0 and plan.tiles_n % 2 == 0 \
-            and plan.tiles // 4 >= dg.gemm_num_cus():
+    # the library runs 2x2 tile groups when their waves finish sooner (its rule, restated)
+    cus = dg.gemm_num_cus()
+    groups = ((plan.tiles_m + 1) // 2) * ((plan.tiles_n + 1) // 2)
+    if plan.decision == dg.GEMM_DP and -(-groups // cus) * 40 < -(-plan.tiles // cus) * 14:
         kind = "gemm_dp_group"
     lay = "B[K,N]" if w.b_layout == "kn" else "B[N,K]"
     fix = (", atomic" if plan.atomic else ", deterministic") if plan.decision == dg.GEMM_STREAMK else ""
@@ -307,7 +311,8 @@ def main():
 
     shapes = {}
     if not args.no_shapes:
-        for name in ("c3_wavequant", "c1_sk32", "c2a_m96_s8", "c2b_m256_s2", "c5_longk_fp16", "c4_large_dp"):
+        for name in ("c3_wavequant", "c1_sk32", "c2a_m96_s8", "c2b_m256_s2", "c5_longk_fp16", "c4_large_dp",
+                     "x1_hybrid"):
             shapes[name] = shape_arms(dg, name, args.shape_steps, 10)
     c3 = shapes.get("c3_wavequant", {})
     speedups = {}

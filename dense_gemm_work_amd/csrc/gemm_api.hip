@@ -284,13 +284,16 @@ int run(const gemm_args_t &a) {
 
     if (p.decision == GEMM_DP) {
         kp.ntiles = (int)p.tiles;
-        // 2x2 tile groups when the tile grid splits into them and they still fill
-        // every CU (the group count is at least the CU count)
-        const bool groups = p.tiles_m % 2 == 0 && p.tiles_n % 2 == 0 && p.tiles / 4 >= ncu &&
-                            !(a.debug & GEMM_DEBUG_TILE_DP);
+        // 2x2 tile groups when their waves finish sooner than the tiles' waves:
+        // a group takes about 4 / 1.4 tile times (measured on 8192^3: 1207 us
+        // with one tile per workgroup, 840 us with groups), so with G groups and
+        // T tiles on C CUs groups win when ceil(G / C) * 4 < ceil(T / C) * 1.4
+        const int64_t ngroups = ((p.tiles_m + 1) / 2) * ((p.tiles_n + 1) / 2);
+        const int64_t gwaves = (ngroups + ncu - 1) / ncu, twaves = (p.tiles + ncu - 1) / ncu;
+        const bool groups = gwaves * 40 < twaves * 14 && !(a.debug & GEMM_DEBUG_TILE_DP);
         if (groups) {
-            if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_DP_GROUP, (int)(p.tiles / 4), kp, stream)) !=
-                hipSuccess)
+            kp.ntiles = (int)ngroups;
+            if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_DP_GROUP, (int)ngroups, kp, stream)) != hipSuccess)
                 return fail_hip(e, "launch DP tile-group kernel");
         } else if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_DP, (int)p.tiles, kp, stream)) != hipSuccess) {
             return fail_hip(e, "launch DP kernel");

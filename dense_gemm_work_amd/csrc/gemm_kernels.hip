@@ -1,7 +1,8 @@
 // gemm_kernels.hip -- gfx950 (MI355X) kernels of the DP / Split-K / Stream-K GEMM.
 //
-// One mainloop serves every decomposition.  A workgroup computes one 128x128
-// fp32 output tile at a time; one "MAC-loop iteration" (Split-K/Stream-K book
+// One mainloop serves every decomposition (large data-parallel launches use a
+// second one for 2x2 tile groups, further down).  A workgroup computes one
+// 128x128 fp32 output tile at a time; one "MAC-loop iteration" (Split-K/Stream-K book
 // chapter, glossary) is a 64-wide step of K: the A slab [128 x 64] and the
 // B slab [64 x 128] are staged in LDS and the workgroup issues 64
 // v_mfma_f32_32x32x16_{bf16,f16} on them.  Every kernel runs eight waves (two
@@ -27,9 +28,13 @@
 // Epilogues (book chapter, Stream-K paragraph after the glossary; Case 4's
 // reduction modes; docc StreamK page):
 //   K_DP         store the tile.
-//   K_SPLITK     store the fp32 partial into P[s] of [S,M,N], arrive at the
-//                tile's counter; the last arriver sums P[0..S-1] in split order
-//                (its own split from LDS) and stores C.
+//   K_DP_GROUP   store the four tiles of the group.
+//   K_SPLITK     store the fp32 partial into P[s] of [S,M,N]; then either arrive
+//                at the tile's counter, the last arriver summing P[0..S-1] in
+//                split order (its own split from LDS) and storing C, or (all
+//                splits resident, 4 < S <= 16) raise the split's flag, wait for
+//                the tile's other flags and fold one 128/S-row band in the same
+//                order.
 //   K_SK         a segment that covers the whole tile is stored; one that starts
 //                mid-tile (always the unit's first) publishes its accumulator to
 //                the unit's slot and raises the unit's flag; the unit holding the
@@ -1046,10 +1051,12 @@ __device__ __forceinline__ int tile_id(const KParams &p, int tm, int tn) {
     return g * gm_full * p.tiles_n + tn * gm + (tm - first);
 }
 
-// Group g of the (tiles_m / 2) x (tiles_n / 2) group grid, numbered like
+// Group g of the ceil(tiles_m / 2) x ceil(tiles_n / 2) group grid, numbered like
 // tile_origin numbers tiles (bands of group_m / 2 group rows, column by column).
+// With an odd tile count along M or N the last groups hang over the edge; their
+// loads beyond M / N read zeros and their stores are masked.
 __device__ __forceinline__ void group_origin(const KParams &p, int g, int &m0, int &n0) {
-    const int gms = p.tiles_m / 2, gns = p.tiles_n / 2;
+    const int gms = (p.tiles_m + 1) / 2, gns = (p.tiles_n + 1) / 2;
     const int gm_full = p.group_m > 1 ? p.group_m / 2 : gms;
     const int per_band = gm_full * gns;
     const int band = g / per_band;
@@ -1060,13 +1067,13 @@ __device__ __forceinline__ void group_origin(const KParams &p, int g, int &m0, i
     n0 = (w / gm) * GB;
 }
 
-// Launch: ntiles / 4 workgroups, tiles_m and tiles_n even, tile_base 0.
+// Launch: one workgroup per group (ntiles = the group count), tile_base 0.
 template <int DT, int BL>
 __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
     __shared__ __attribute__((aligned(16))) char lds[G_NS * 2 * G_SLAB];
     constexpr int JB = GAcc<G_NW>::JB;
     const WgClock clk(p);
-    const int g = worker_of(p, p.ntiles / 4);
+    const int g = worker_of(p, p.ntiles);
     int m0, n0;
     group_origin(p, g, m0, n0);
     GAcc<G_NW> acc;
@@ -1095,7 +1102,9 @@ __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
     if (p.trace && threadIdx.x == 0) {
         // the four tiles of the group, each a whole-K data-parallel tile
         for (int q = 0; q < 4; ++q) {
-            const int tile = tile_id(p, m0 / BM + (q & 1), n0 / BN + (q >> 1));
+            const int tm = m0 / BM + (q & 1), tn = n0 / BN + (q >> 1);
+            if (tm >= p.tiles_m || tn >= p.tiles_n) continue;   // over the edge of the tile grid
+            const int tile = tile_id(p, tm, tn);
             trace_segment(p, p.worker_base + tile, 0, tile, 0, p.ipt, 0);
             trace_folded(p, tile, 0, p.worker_base + tile);
             int *cov = trace_cov(p, tile);

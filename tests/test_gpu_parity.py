@@ -92,6 +92,16 @@ def test_c3_heuristic_streamk(dg):
     assert_parity(c, A, B, w, rows=sample_rows(w.M, 48))
 
 
+def test_x1_hybrid_full_size(dg):
+    # the heuristic's hybrid regime at full size: 3 data-parallel waves + Stream-K
+    w = WORKLOADS["x1_hybrid"]
+    p = dg.gemm_plan(w.M, w.N, w.K, 0, dg.GEMM_HEURISTIC, 0, 256)
+    assert dg.DECISION_NAMES[p.decision] == "StreamK" and p.dp_tiles == 768 and p.sk_tiles == 288
+    assert p.sk_units == 256 and p.q == 72 and p.big == 0
+    A, B, c = run(dg, w)
+    assert_parity(c, A, B, w, rows=sample_rows(w.M, 10) + [3 * 1024 + 5, 4095])
+
+
 def test_c4_heuristic_dp(dg):
     w = WORKLOADS["c4_large_dp"]
     p = dg.gemm_plan(w.M, w.N, w.K, 0, dg.GEMM_HEURISTIC, 0, 256)
@@ -105,10 +115,12 @@ def test_c4_heuristic_dp(dg):
     (4000, 4064, 200, "kn", 0),      # ragged M, N and K (K % 64 = 8)
     (4096, 4096, 192, "nk", 0),      # B [N,K]
     (1024, 1024, 512, "kn", 16),     # 64 tiles on 16 CUs
+    (2900, 4000, 256, "kn", 0),      # 23 x 32 tiles: the last group row hangs over the edge of M
 ])
 def test_dp_tile_groups(dg, M, N, K, layout, cus):
-    # data-parallel launches with at least 4 x CUs tiles run 2x2 tile groups per
-    # workgroup; checked against the oracle and against one-tile workgroups
+    # data-parallel launches whose 2x2 tile groups finish in fewer tile times run
+    # them one per workgroup; checked against the oracle and against one-tile
+    # workgroups
     w = WORKLOADS["c4_large_dp"].with_(name="dp_groups", M=M, N=N, K=K, b_layout=layout)
     A, B, c = run(dg, w, mode="dp", splits=0, num_cus=cus)
     rows = sample_rows(M, 12) + [M - 2, M - 129]
@@ -195,6 +207,8 @@ TRACE_CASES = [
     ("hybrid", 1408, 768, 1024, "heuristic", 0, 20, False),
     ("dp", 640, 384, 256, "dp", 0, 256, False),
     ("dp-groups", 1024, 1024, 256, "dp", 0, 16, False),   # 2x2 tile groups (64 tiles, 16 CUs)
+    ("dp-groups-odd", 1152, 1024, 128, "dp", 0, 8, False),   # 9 x 8 tiles: the last group row hangs over M
+    ("x1-hybrid", 4096, 4224, 4096, "heuristic", 0, 256, False),   # 768 DP tiles + Stream-K over 288
 ]
 
 

@@ -18,7 +18,8 @@ workload, the seed; the rest is a stated reading):
   exact).  This mirrors the Metal split-K benchmark note's fixture design
   (first input row zero, last row at four times the ordinary scale).
 
-The five workloads below are the ones the performance and parity harness runs.
+The five workloads below are the ones the performance and parity harness runs
+(plus one beyond them, ``x1_hybrid``, for the heuristic's hybrid regime).
 Row counts, tile counts and wave arithmetic for each are derived from 128x128
 output tiles and 64-wide k-iterations, as the Split-K/Stream-K book chapter
 uses throughout its worked cases.
@@ -91,6 +92,11 @@ WORKLOADS = {
     "c5_longk_fp16": Workload("c5_longk_fp16", 1536, 1536, 16384, "fp16", "kn", "uniform", -0.5, 0.5,
                               mode="streamk", splits=0,
                               note="144 tiles x 256 iters; Stream-K 256 units; turnstile and atomic fixup"),
+    # Beyond the five: the heuristic's hybrid regime.  32x33 = 1056 tiles = 4 full
+    # waves + a 32-tile tail, so 3 waves stay data-parallel and the last 288 tiles
+    # go to 256 Stream-K units of 72 iterations.
+    "x1_hybrid": Workload("x1_hybrid", 4096, 4224, 4096, "bf16", "kn", "uniform", -1.0, 1.0,
+                          mode="heuristic", note="1056 tiles; heuristic -> 768 DP tiles + Stream-K over 288"),
 }
 
 
