@@ -71,7 +71,11 @@ class Call:
         args.A, args.B, args.C = a.data_ptr(), b.data_ptr(), c.data_ptr()
         args.M, args.N, args.K = M, N, K
         args.layout = dg.layout_word(b_layout, "bf16" if a.dtype == torch.bfloat16 else "fp16")
-        args.mode = dg.mode_word(mode, atomic)
+        # `atomic`: False, True, "two_pass" (Split-K partials added by a second
+        # kernel) or "last_arriver" (Split-K partials folded in the launch)
+        args.mode = dg.mode_word(mode, atomic is True, atomic == "two_pass")
+        if atomic == "last_arriver":
+            args.debug = dg.GEMM_DEBUG_LAST_ARRIVER
         args.splits = splits
         self.stream = stream or torch.cuda.current_stream()
         args.stream = self.stream.cuda_stream
@@ -135,14 +139,19 @@ def shape_arms(dg, name, steps, warmup):
     arms = {"dp": ("dp", 0, False)}
     if name.startswith("c2"):
         arms["splitk%d" % w.splits] = ("splitk", w.splits, False)
+        arms["splitk%d_last_arriver" % w.splits] = ("splitk", w.splits, "last_arriver")
+        arms["splitk%d_atomic" % w.splits] = ("splitk", w.splits, True)
     if name.startswith("c1"):
         arms["streamk32"] = ("streamk", 32, False)
         arms["splitk4"] = ("splitk", 4, False)
+        arms["splitk4_last_arriver"] = ("splitk", 4, "last_arriver")
         arms["heuristic"] = ("heuristic", 0, False)
     if name.startswith("c3"):
         arms["heuristic"] = ("heuristic", 0, False)
         arms["splitk2"] = ("splitk", 2, False)
         arms["splitk4"] = ("splitk", 4, False)
+        arms["splitk2_two_pass"] = ("splitk", 2, "two_pass")
+        arms["splitk4_two_pass"] = ("splitk", 4, "two_pass")
     if name.startswith("c4"):
         arms = {"heuristic": ("heuristic", 0, False)}
     if name.startswith("c5"):

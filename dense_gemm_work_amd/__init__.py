@@ -49,6 +49,7 @@ GEMM_SPLITK = 0x2
 GEMM_STREAMK = 0x3
 GEMM_DETERMINISTIC = 0x000
 GEMM_ATOMIC = 0x100
+GEMM_TWO_PASS = 0x200
 
 GEMM_DEBUG_NO_PUBLISH = 0x1
 GEMM_DEBUG_LAST_ARRIVER = 0x4
@@ -78,7 +79,7 @@ class GemmPlan(ctypes.Structure):
         ("tail", ctypes.c_int64), ("sk_tiles", ctypes.c_int64), ("sk_units", ctypes.c_int64),
         ("dp_tiles", ctypes.c_int64), ("q", ctypes.c_int64), ("big", ctypes.c_int64),
         ("splits", ctypes.c_int32), ("max_segments", ctypes.c_int32), ("max_fold", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("two_pass", ctypes.c_int32),
         ("workers", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64), ("trace_ints", ctypes.c_int64),
     ]
 
@@ -197,14 +198,14 @@ def layout_word(b_layout: str, dtype: str) -> int:
     return lw | {"bf16": GEMM_BF16, "fp16": GEMM_FP16}[dtype]
 
 
-def mode_word(mode: str, atomic: bool = False) -> int:
-    return MODES[mode] | (GEMM_ATOMIC if atomic else 0)
+def mode_word(mode: str, atomic: bool = False, two_pass: bool = False) -> int:
+    return MODES[mode] | (GEMM_ATOMIC if atomic else 0) | (GEMM_TWO_PASS if two_pass else 0)
 
 
 def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits: int = 0,
                  atomic: bool = False, num_cus: int = 0, unit_perm=None, trace=None,
                  workspace=None, spin_limit: int = 0, debug: int = 0, timing=None,
-                 stream=None) -> None:
+                 stream=None, two_pass: bool = False) -> None:
     """``c[M,N] = a[M,K] . b`` (b [K,N]) or ``a . b^T`` (b [N,K]) on torch tensors.
 
     a, b: contiguous bf16/fp16 tensors on one HIP device; c: contiguous fp32 [M,N].
@@ -245,7 +246,7 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
     args.A, args.B, args.C = a.data_ptr(), b.data_ptr(), c.data_ptr()
     args.M, args.N, args.K = M, N, K
     args.layout = layout_word(b_layout, dtype)
-    args.mode = mode_word(mode, atomic)
+    args.mode = mode_word(mode, atomic, two_pass)
     args.splits = splits
     args.num_cus = num_cus
     with torch.cuda.device(a.device):

@@ -2,11 +2,10 @@
 // planning, workspace management and kernel launches.
 //
 // Workspace (per device, owned by the library unless the caller passes one):
-//   control: a status word (64 words reserved), flags (one per Stream-K unit,
-//            or one per Split-K (tile, split)) and one arrival counter per
-//            Split-K tile.  It is zero-filled when it is (re)allocated and never
-//            again: flags hold the epoch of the launch that last raised them (a
-//            fresh epoch per Stream-K or cooperative Split-K launch, so stale
+//   control: a status word (64 words reserved), one flag per Stream-K unit and
+//            one arrival counter per Split-K tile.  It is zero-filled when it is
+//            (re)allocated and never again: flags hold the epoch of the launch
+//            that last raised them (a fresh epoch per Stream-K launch, so stale
 //            flags never match), and the last arriver of a tile resets its
 //            counter to zero.
 //   data:    Stream-K partial slots [units][128*128] fp32, or Split-K partials
@@ -220,7 +219,7 @@ int run(const gemm_args_t &a) {
                                                   std::to_string((int64_t)bpc * ds->num_cus) + ")");
     }
 
-    if ((rc = ensure_control(*ds, dgw::flag_words(p), p.tiles)) != GEMM_OK) return rc;
+    if ((rc = ensure_control(*ds, std::max<int64_t>(p.sk_units, 1), p.tiles)) != GEMM_OK) return rc;
 
     // flags, counters and the data region
     uint32_t *flags = nullptr, *counters = nullptr;
@@ -233,7 +232,7 @@ int run(const gemm_args_t &a) {
         const int64_t cb = dgw::control_bytes(p);
         char *base = static_cast<char *>(a.workspace);
         flags = reinterpret_cast<uint32_t *>(base + 256);
-        counters = reinterpret_cast<uint32_t *>(base + 256 + (dgw::flag_words(p) * 4 + 255) / 256 * 256);
+        counters = reinterpret_cast<uint32_t *>(base + 256 + (std::max<int64_t>(p.sk_units, 1) * 4 + 255) / 256 * 256);
         part = reinterpret_cast<float *>(base + cb);
         if ((e = dgw::launch_zero(base, cb / 4, stream)) != hipSuccess) return fail_hip(e, "zero control");
     } else {
@@ -300,23 +299,20 @@ int run(const gemm_args_t &a) {
         }
     } else if (p.decision == GEMM_SPLITK) {
         kp.ntiles = (int)p.tiles;
-        // With every (tile, split) workgroup resident at once and more than 4
-        // splits, the S splits of a tile fold it together, one row band each,
-        // after all S flags are up; otherwise the last arriver at the tile's
-        // counter folds it alone (for S <= 4 in one round of loads, which beats
-        // the flag handoff; beyond that one workgroup's bandwidth dominates).
-        if (p.splits > dgw::COOP_MIN_SPLITS && p.splits <= dgw::COOP_MAX_SPLITS && a.N % 4 == 0 &&
-            !(a.debug & GEMM_DEBUG_LAST_ARRIVER)) {
-            int &bpc = ds->bpc[dtype][blayout][kmode];
-            if (bpc == 0) {
-                if ((e = dgw::blocks_per_cu(dtype, blayout, kmode, &bpc)) != hipSuccess)
-                    return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
-            }
-            if (p.tiles * p.splits <= (int64_t)bpc * ds->num_cus) kp.epoch = next_epoch();
+        kp.merge = p.atomic                                        ? dgw::MERGE_ATOMIC
+                   : p.two_pass && !(a.debug & GEMM_DEBUG_LAST_ARRIVER) ? dgw::MERGE_TWO_PASS
+                                                                       : dgw::MERGE_IN_LAUNCH;
+        if (p.atomic) {
+            if ((e = dgw::launch_zero(a.C, a.M * a.N, stream)) != hipSuccess) return fail_hip(e, "zero C");
         }
         if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_SPLITK, (int)(p.tiles * p.splits), kp, stream)) !=
             hipSuccess)
             return fail_hip(e, "launch Split-K kernel");
+        if (kp.merge == dgw::MERGE_TWO_PASS) {
+            KParams rp = kp;
+            rp.timing = nullptr;   // timing records cover the Split-K launch's workgroups
+            if ((e = dgw::launch_splitk_reduce(rp, stream)) != hipSuccess) return fail_hip(e, "launch Split-K reduction");
+        }
     } else {
         if (p.atomic) {
             if ((e = dgw::launch_zero(a.C, a.M * a.N, stream)) != hipSuccess) return fail_hip(e, "zero C");

@@ -31,10 +31,9 @@
 //   K_DP_GROUP   store the four tiles of the group.
 //   K_SPLITK     store the fp32 partial into P[s] of [S,M,N]; then either arrive
 //                at the tile's counter, the last arriver summing P[0..S-1] in
-//                split order (its own split from LDS) and storing C, or (all
-//                splits resident, 4 < S <= 16) raise the split's flag, wait for
-//                the tile's other flags and fold one 128/S-row band in the same
-//                order.
+//                split order (its own split from LDS) and storing C, or leave
+//                the sum to splitk_reduce (two-pass), or (atomic) add the
+//                accumulator into a zero-filled C instead of storing a partial.
 //   K_SK         a segment that covers the whole tile is stored; one that starts
 //                mid-tile (always the unit's first) publishes its accumulator to
 //                the unit's slot and raises the unit's flag; the unit holding the
@@ -171,10 +170,10 @@ __device__ __forceinline__ void wait_stage0() {
     __builtin_amdgcn_s_barrier();
 }
 
-// A device-scope (sc1) load of a 32-bit flag that the compiler does not track,
-// so that several can be in flight before one explicit vmcnt wait (the
-// compiler would wait after each atomic load).  flag_value() must only be
-// applied after such a wait has covered the load.
+// A device-scope (sc1) load of a 32-bit flag that the compiler does not track
+// (it is awaited by an explicit vmcnt wait; measured cheaper to poll with than
+// an atomic load).  flag_value() must only be applied after such a wait has
+// covered the load.
 __device__ __forceinline__ uint32_t load_flag_async(const uint32_t *flag) {
     uint32_t v;
     asm volatile("global_load_dword %0, %1, off sc1" : "=v"(v) : "v"(flag) : "memory");
@@ -691,24 +690,13 @@ __device__ __forceinline__ void add_slot(const float *slot, Tile<NW> &t) {
                 for (int y = 0; y < 4; ++y) t.v[h][j][4 * e4 + y] += x[h][j][e4][y];
 }
 
-// Poll flags first[0..n) (1 <= n <= MAXN <= 32, one thread) until all of them
-// hold `epoch`.  Every round issues all of its loads before waiting for any
-// (the asynchronous form keeps the compiler from waiting after each one), so a
-// round costs one memory round trip however many flags there are.  Gives up
-// after `limit` rounds, recording STATUS_TIMEOUT.
-template <int MAXN>
-__device__ __forceinline__ void wait_flags(const uint32_t *first, int n, uint32_t epoch, uint32_t limit,
-                                           uint32_t *status) {
-    static_assert(MAXN <= 32, "flag count");
+// Poll `flag` (one thread) until it holds `epoch`, one untracked load per poll.
+// Gives up after `limit` polls, recording STATUS_TIMEOUT.
+__device__ __forceinline__ void wait_flag(const uint32_t *flag, uint32_t epoch, uint32_t limit, uint32_t *status) {
     for (uint32_t polls = 1;; ++polls) {
-        uint32_t v[MAXN];
-#pragma unroll
-        for (int i = 0; i < MAXN; ++i) v[i] = load_flag_async(first + min(i, n - 1));
+        uint32_t v = load_flag_async(flag);
         wait_vm_all();
-        bool up = true;
-#pragma unroll
-        for (int i = 0; i < MAXN; ++i) up = up && flag_value(v[i]) == epoch;
-        if (up) return;
+        if (flag_value(v) == epoch) return;
         if (polls >= limit) {
             __hip_atomic_fetch_or(status, STATUS_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;
@@ -1117,59 +1105,6 @@ __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
 // ---------------------------------------------------------------------------
 // Split-K: worker w = tile * S + s covers k-iterations [s P / S, (s+1) P / S).
 // ---------------------------------------------------------------------------
-// Split-K cooperative fold: split s of a tile sums rows [s BM / S, (s + 1) BM / S)
-// of the S partials, ((P0 + P1) + P2) + ..., its own partial read from the LDS
-// staging copy, and stores them to C.  The row band has at most 16 row quads
-// per thread times partials (S <= COOP_MAX_SPLITS), all loaded before the
-// first add.  Needs N % 4 == 0 (16-byte partial and output quads).
-
-template <int NW>
-__device__ __forceinline__ void fold_rows(const KParams &p, const float *stg, int tile, int s, int m0, int n0,
-                                          size_t org, uint32_t span_bytes) {
-    constexpr int NT = 64 * NW;
-    const int S = p.splits;
-    const int r0 = s * BM / S, r1 = (s + 1) * BM / S;
-    static_assert(BN == 128, "32 row quads per tile row");
-    const int nq = (r1 - r0) * (BN / 4);           // row quads in the band
-    const int qt = (nq + NT - 1) / NT;             // quads per thread
-    const int slots = qt * S;                      // (quad, partial) pairs, <= 16
-    const size_t mn = (size_t)p.M * p.N;
-    // (quad g, partial t) of slot j = g S + t, stepped without division
-    f32x4 x[16];
-    {
-        int g = 0, t = 0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int fq = threadIdx.x + NT * g;
-            const int r = r0 + (fq >> 5), c = (fq & 31) * 4;
-            x[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (j < slots && t != s && fq < nq && m0 + r < p.M && n0 + c < p.N)
-                x[j] = get4_coherent(span(p.part + (size_t)t * mn + org, span_bytes),
-                                     (uint32_t)(((size_t)r * p.N + c) * 4));
-            if (++t == S) {
-                t = 0;
-                ++g;
-            }
-        }
-    }
-    f32x4 run = {0.f, 0.f, 0.f, 0.f};
-    int g = 0, t = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int fq = threadIdx.x + NT * g;
-        const int r = r0 + (fq >> 5), c = (fq & 31) * 4;
-        const bool ok = j < slots && fq < nq && m0 + r < p.M && n0 + c < p.N;
-        const f32x4 v = t == s ? staged_quad(stg, r & (BM - 1), c) : x[j];
-        run = t == 0 ? v : run + v;
-        if (t == S - 1 && ok)
-            put_quad(p.C + (size_t)(m0 + r) * p.N + n0 + c, run, min(4, p.N - (n0 + c)), true);
-        if (++t == S) {
-            t = 0;
-            ++g;
-        }
-    }
-}
-
 template <int DT, int BL, int NS, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
     constexpr int NT = Role<NW>::NT, QPT = BM * BN / 4 / NT;
@@ -1191,6 +1126,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
     if (S == 1) {
         store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
         trace_folded(p, tile, 0, w);
+        clk.done(p);
+        return;
+    }
+    if (p.merge == MERGE_ATOMIC) {   // "parallel" Split-K: add into the zero-filled C
+        atomic_add_c<NW>(p.C, m0, n0, p.M, p.N, t);
         clk.done(p);
         return;
     }
@@ -1218,21 +1158,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
     wait_vm_all();                 // this wave's partial stores are complete
     __syncthreads();               // ... and every other wave's
     clk.mark(p, 1);
-    if (p.epoch != 0) {
-        // Cooperative fold (all S workgroups of every tile are resident): raise
-        // this split's flag, wait for the tile's other splits, then fold rows
-        // [s BM / S, (s + 1) BM / S) of the tile in split order.
-        uint32_t *tf = p.flags + (size_t)tile * S;
-        if (threadIdx.x == 0) {
-            if (!(p.debug & GEMM_DEBUG_NO_PUBLISH))
-                __hip_atomic_store(tf + s, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            wait_flags<COOP_MAX_SPLITS>(tf, S, p.epoch, p.spin_limit, p.status);
-        }
-        __syncthreads();
-        fold_rows<NW>(p, stg, tile, s, m0, n0, org, span_bytes);
-        if (s == 0)
-            for (int t = 0; t < S; ++t) trace_folded(p, tile, t, tile * S + t);
-        clk.mark(p, 2);
+    if (p.merge == MERGE_TWO_PASS) {   // the second kernel folds the partials
         clk.done(p);
         return;
     }
@@ -1349,6 +1275,53 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Two-pass Split-K, second pass ("serial" Split-K: a separate reduction over the
+// partials; CUTLASS optimisation guide, "Parallelized Reductions (Split-K)").
+// One thread per 16-byte quad of C, 16 workgroups of 256 threads per tile; the
+// partials are added in split order, ((P0 + P1) + P2) + ..., the loads of up to
+// 8 partials in flight before their adds -- the same order, hence the same
+// bits, as the in-launch fold.
+// ---------------------------------------------------------------------------
+constexpr int RED_THREADS = 256;
+constexpr int RED_BLOCKS_PER_TILE = BM * BN / 4 / RED_THREADS;   // 16
+
+__global__ __launch_bounds__(RED_THREADS) void splitk_reduce(KParams p) {
+    const int tile = blockIdx.x / RED_BLOCKS_PER_TILE;
+    const int q = (blockIdx.x % RED_BLOCKS_PER_TILE) * RED_THREADS + threadIdx.x;   // quad within the tile
+    int m0, n0;
+    tile_origin(p, tile, m0, n0);
+    const int r = q >> 5, c = (q & 31) * 4;
+    const int S = p.splits;
+    if (threadIdx.x == 0 && blockIdx.x % RED_BLOCKS_PER_TILE == 0)
+        for (int t = 0; t < S; ++t) trace_folded(p, tile, t, tile * S + t);
+    if (m0 + r >= p.M || n0 + c >= p.N) return;
+    const size_t mn = (size_t)p.M * p.N;
+    const size_t off = (size_t)(m0 + r) * p.N + n0 + c;
+    if ((p.N & 3) == 0) {
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+        for (int t0 = 0; t0 < S; t0 += 8) {
+            f32x4 x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (t0 + j < S) x[j] = *reinterpret_cast<const f32x4 *>(p.part + (size_t)(t0 + j) * mn + off);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (t0 + j < S) sum = t0 + j == 0 ? x[j] : sum + x[j];
+        }
+        *reinterpret_cast<f32x4 *>(p.C + off) = sum;
+    } else {
+        for (int e = 0; e < 4 && n0 + c + e < p.N; ++e) {
+            float sum = 0.f;
+            for (int t = 0; t < S; ++t) {
+                const float v = p.part[(size_t)t * mn + off + e];
+                sum = t == 0 ? v : sum + v;
+            }
+            p.C[off + e] = sum;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Stream-K: persistent; workgroup b runs unit worker_of(b).
 //
 // A unit's range [begin, end) of the flattened (tile, k) space falls into
@@ -1424,7 +1397,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
             int pos_fold = 1;
             for (int v = u + 1; v < p.units; ++v) {
                 if (unit_start(v, p.q, p.big) >= tile_end) break;
-                if (threadIdx.x == 0) wait_flags<1>(p.flags + v, 1, p.epoch, p.spin_limit, p.status);
+                if (threadIdx.x == 0) wait_flag(p.flags + v, p.epoch, p.spin_limit, p.status);
                 __syncthreads();
                 add_slot<NW>(p.part + (size_t)v * (BM * BN), t);
                 trace_folded(p, tile, pos_fold++, v);
@@ -1495,6 +1468,13 @@ hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParam
     KernelFn fn = kernel_for(dtype, blayout, kmode, shape);
     if (!fn || grid <= 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * shape.nw), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const KParams &p, hipStream_t stream) {
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    if (tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)(tiles * RED_BLOCKS_PER_TILE)), dim3(RED_THREADS), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -10,16 +10,16 @@ namespace dgw {
 // Which epilogue/fixup a launch performs.
 enum KernelMode : int {
     K_DP = 0,         // whole-K tiles, plain store
-    K_SPLITK = 1,     // split s of tile t; fp32 partial [S,M,N]; last arriver folds in split order
+    K_SPLITK = 1,     // split s of tile t; fp32 partial [S,M,N] folded in split order (see KParams::merge)
     K_SK = 2,         // Stream-K, deterministic turnstile through per-unit partial slots
     K_SK_ATOMIC = 3,  // Stream-K, split tiles merged by fp32 atomic adds into zeroed C
     K_DP_GROUP = 4,   // whole-K tiles, one 2x2 group of tiles (256x256) per workgroup
 };
 
-// Split-K: splits whose workgroups fold a tile together (row bands) when all
-// are resident: COOP_MIN_SPLITS < S <= COOP_MAX_SPLITS.
-constexpr int COOP_MIN_SPLITS = 4;
-constexpr int COOP_MAX_SPLITS = 16;
+// How Split-K merges its partials: folded in the same launch by the last
+// arriver at the tile's counter, folded by a second kernel, or added atomically
+// into a zero-filled C.
+enum : int { MERGE_IN_LAUNCH = 0, MERGE_TWO_PASS = 1, MERGE_ATOMIC = 2 };
 
 // Error bits of the device status word.
 enum : uint32_t { STATUS_TIMEOUT = 1u };
@@ -37,12 +37,13 @@ struct KParams {
     int ntiles;            // tiles of a DP / Split-K launch
     int units, q, big;     // Stream-K unit ranges: unit u starts at u*q + min(u, big)
     int splits;            // Split-K factor S
+    int merge;             // Split-K: MERGE_IN_LAUNCH, MERGE_TWO_PASS or MERGE_ATOMIC
     int worker_base;       // trace id of this launch's worker 0
     float *part;           // Stream-K slots [units][BM*BN] or Split-K partials [S][M][N]
-    uint32_t *flags;       // Stream-K: flag per unit; Split-K: flag per (tile, split) (epoch-valued)
+    uint32_t *flags;       // Stream-K: flag per unit (epoch-valued)
     uint32_t *counters;    // Split-K: arrival counter per tile (reset by the last arriver)
     uint32_t *status;      // device error word
-    uint32_t epoch;        // value a publishing unit writes into its flag (Split-K: 0 = last-arriver fold)
+    uint32_t epoch;        // value a publishing unit writes into its flag
     uint32_t spin_limit;   // polls before a wait gives up
     uint32_t debug;        // GEMM_DEBUG_* bits
     const int *perm;       // optional workgroup -> worker map
@@ -56,6 +57,10 @@ struct KParams {
 // dtype: 0 bf16, 1 fp16; blayout: 0 = B [K,N], 1 = B [N,K].
 hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParams &p,
                        hipStream_t stream);
+
+// Second pass of two-pass Split-K: C = ((P[0] + P[1]) + ...) + P[S-1] over the
+// partials [S,M,N] of `p` (p.part, p.splits, p.M, p.N, the tile grid and raster).
+hipError_t launch_splitk_reduce(const KParams &p, hipStream_t stream);
 
 // Fill n 32-bit words with zero (used instead of hipMemsetAsync so the call can
 // be captured in a HIP graph).

@@ -49,12 +49,17 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
     }
     const uint32_t decomp = mode & 0xFu;
     const bool atomic = (mode & GEMM_ATOMIC) != 0;
-    if ((mode & ~(0xFu | GEMM_ATOMIC)) || decomp > GEMM_STREAMK) {
+    const bool two_pass = (mode & GEMM_TWO_PASS) != 0;
+    if ((mode & ~(0xFu | GEMM_ATOMIC | GEMM_TWO_PASS)) || decomp > GEMM_STREAMK) {
         *why = "mode word has unknown bits";
         return GEMM_ERR_INVALID;
     }
-    if (atomic && decomp != GEMM_STREAMK && decomp != GEMM_HEURISTIC) {
-        *why = "GEMM_ATOMIC applies to Stream-K only";
+    if (atomic && decomp == GEMM_DP) {
+        *why = "GEMM_ATOMIC applies to Stream-K and Split-K only";
+        return GEMM_ERR_INVALID;
+    }
+    if (two_pass && (atomic || (decomp != GEMM_SPLITK && decomp != GEMM_HEURISTIC))) {
+        *why = "GEMM_TWO_PASS applies to deterministic Split-K only";
         return GEMM_ERR_INVALID;
     }
     if ((decomp == GEMM_DP || decomp == GEMM_HEURISTIC) && splits != 0) {
@@ -111,9 +116,8 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
                 chosen = GEMM_STREAMK;
             }
         }
-        if (atomic && chosen != GEMM_STREAMK) {
-            // atomic merging only changes Stream-K; other choices ignore it
-        }
+        // GEMM_ATOMIC / GEMM_TWO_PASS apply to whichever of Stream-K and Split-K
+        // the rule picks (two-pass to Split-K only); data-parallel ignores them
     } else if (decomp == GEMM_SPLITK) {
         if (splits < 1) { *why = "GEMM_SPLITK needs splits >= 1"; return GEMM_ERR_INVALID; }
         if (p.ipt == 0 || p.ipt % splits != 0) {
@@ -137,11 +141,21 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
         break;
     case GEMM_SPLITK:
         p.splits = S;
+        p.atomic = atomic && S > 1 ? 1 : 0;
+        // Deterministic: the partials are added in split order either by the last
+        // arriver at each tile's counter (in the launch) or by a second kernel.
+        // Same bits; the second kernel wins when the whole grid is resident at
+        // once (one workgroup per CU) -- the latency-bound small grids, where a
+        // kernel boundary costs less than the arrival round trip plus a fold
+        // serialised in one workgroup -- and loses on larger grids, whose last
+        // arrivers fold partials still warm in L2.
+        p.two_pass = !p.atomic && S > 1 && (two_pass || p.tiles * S <= num_cus) ? 1 : 0;
         p.workers = p.tiles * S;
         p.max_segments = 1;
         p.max_fold = S;
-        // fp32 partials [S, M, N]; an arrival counter per tile and a flag per (tile, split)
-        p.workspace_bytes = S > 1 ? int64_t(S) * M * N * 4 : 0;
+        // fp32 partials [S, M, N] (none with atomics); an arrival counter per tile
+        // and a flag per (tile, split)
+        p.workspace_bytes = S > 1 && !p.atomic ? int64_t(S) * M * N * 4 : 0;
         break;
     case GEMM_STREAMK: {
         p.atomic = atomic ? 1 : 0;
@@ -166,22 +180,16 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
         *why = "internal: no decision";
         return GEMM_ERR_INVALID;
     }
-    // control words: status (64 B), flags, Split-K counters, each 256-B aligned
+    // control words: status (64 B), Stream-K flags, Split-K counters, each 256-B aligned
     p.workspace_bytes += control_bytes(p);
     p.trace_ints = 8 + p.workers * (1 + 4 * int64_t(p.max_segments)) +
                    p.tiles * (1 + int64_t(p.max_fold)) + p.tiles * p.ipt;
     return GEMM_OK;
 }
 
-int64_t flag_words(const gemm_plan_t &p) {
-    // Stream-K: one flag per unit; Split-K: one per (tile, split) for the cooperative fold
-    const int64_t split_flags = p.decision == GEMM_SPLITK ? p.tiles * p.splits : 0;
-    return std::max<int64_t>({p.sk_units, split_flags, 1});
-}
-
 int64_t control_bytes(const gemm_plan_t &p) {
     auto round = [](int64_t b) { return (b + 255) / 256 * 256; };
-    return 256 + round(flag_words(p) * 4) + round(std::max<int64_t>(p.tiles, 1) * 4);
+    return 256 + round(std::max<int64_t>(p.sk_units, 1) * 4) + round(std::max<int64_t>(p.tiles, 1) * 4);
 }
 
 }  // namespace dgw

@@ -14,8 +14,6 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
 // First flattened iteration of Stream-K unit `unit` ("big" units first).
 int64_t unit_begin(int64_t unit, int64_t q, int64_t big);
 
-// Flags in the control block: one per Stream-K unit, or one per Split-K (tile, split).
-int64_t flag_words(const gemm_plan_t &p);
 // Bytes of control words (status, flags, counters) at the head of the workspace.
 int64_t control_bytes(const gemm_plan_t &p);
 

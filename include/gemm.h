@@ -18,10 +18,13 @@
  *                 [s P/S, (s+1) P/S) of the tile's P iterations, stores an fp32
  *                 partial into a [S,M,N] workspace, and C receives the S
  *                 partials added in split order (docc StreamK page, "MMA
- *                 fragment accumulators (aligned split)").  When all tiles x S
- *                 workgroups are resident at once (4 < S <= 16, N % 4 == 0) the
- *                 S splits of a tile raise flags and fold one row band each;
- *                 otherwise the last arriver at the tile's counter folds it.
+ *                 fragment accumulators (aligned split)"): by a second kernel
+ *                 ("serial" Split-K; chosen when all tiles x S workgroups fit on
+ *                 the CUs at once, or asked for with GEMM_TWO_PASS; plan.two_pass
+ *                 says which), else by the last arriver at the tile's counter
+ *                 in the same launch.  Both give the same bits.  GEMM_ATOMIC adds
+ *                 every split into a zero-filled C instead ("parallel" Split-K;
+ *                 CUTLASS optimisation guide, "Parallelized Reductions (Split-K)").
  *   GEMM_STREAMK  one persistent workgroup per unit; unit u owns a contiguous,
  *                 equal slice of the flattened (tile x k-iteration) space, the
  *                 first (total mod units) units taking one extra iteration
@@ -81,18 +84,21 @@ extern "C" {
 #define GEMM_DP        0x1u
 #define GEMM_SPLITK    0x2u
 #define GEMM_STREAMK   0x3u
-/* bit 8: how Stream-K merges split tiles */
-#define GEMM_DETERMINISTIC 0x000u  /* k-ordered turnstile through an fp32 partial workspace */
-#define GEMM_ATOMIC        0x100u  /* fp32 atomic adds into a zero-filled C */
+/* bits 8-9: how split tiles are merged (Stream-K and Split-K) */
+#define GEMM_DETERMINISTIC 0x000u  /* k-ordered: Stream-K turnstile / Split-K fold in the same launch */
+#define GEMM_ATOMIC        0x100u  /* fp32 atomic adds into a zero-filled C (Stream-K, Split-K) */
+#define GEMM_TWO_PASS      0x200u  /* Split-K only: always add the partials [S,M,N] in split
+                                      order by a second kernel (same bits as the in-launch fold) */
 
 /* ---- debug bits for gemm_args_t.debug -------------------------------------------- */
-#define GEMM_DEBUG_NO_PUBLISH 0x1u /* Stream-K contributors and cooperative Split-K
-                                      splits store partials but never raise their
-                                      flags: every wait ends at its spin limit and
-                                      gemm_sync_status() reports GEMM_ERR_TIMEOUT.
-                                      Exercises the failure path; C is not valid.   */
-#define GEMM_DEBUG_LAST_ARRIVER 0x4u /* Split-K: the last arriver folds every tile even
-                                       when all workgroups are resident.  Same
+#define GEMM_DEBUG_NO_PUBLISH 0x1u /* Stream-K contributors store partials but never
+                                      raise their flags: every wait ends at its spin
+                                      limit and gemm_sync_status() reports
+                                      GEMM_ERR_TIMEOUT.  Exercises the failure path;
+                                      C is not valid.                               */
+#define GEMM_DEBUG_LAST_ARRIVER 0x4u /* deterministic Split-K: the last arriver at each
+                                       tile's counter folds it in the launch even
+                                       where the plan chose a second kernel.  Same
                                        result bits; exercises that path.           */
 #define GEMM_DEBUG_TILE_DP 0x8u /* data-parallel launches run one 128x128 tile per
                                    workgroup even where 2x2 tile groups apply.     */
@@ -109,7 +115,7 @@ extern "C" {
  */
 typedef struct gemm_plan_t {
     int32_t decision;     /* GEMM_DP, GEMM_SPLITK or GEMM_STREAMK                          */
-    int32_t atomic;       /* 1 when Stream-K merges by atomics                              */
+    int32_t atomic;       /* 1 when split tiles (Stream-K or Split-K) merge by atomics      */
     int32_t bm, bn, bk;   /* tile shape                                                     */
     int32_t num_cus;      /* compute units the plan was made for                            */
     int64_t tiles_m, tiles_n, tiles;
@@ -125,7 +131,8 @@ typedef struct gemm_plan_t {
     int32_t splits;       /* Split-K factor S (1 for the other decompositions)              */
     int32_t max_segments; /* most tile segments one worker can touch                        */
     int32_t max_fold;     /* most workers contributing to one tile                          */
-    int32_t reserved;
+    int32_t two_pass;     /* 1 when Split-K partials are added by a second kernel (the plan
+                             picks it for grids that fit on the CUs at once)            */
     int64_t workers;      /* traced workers: units + dp_tiles, tiles * S, or tiles          */
     int64_t workspace_bytes; /* device workspace the call needs                             */
     int64_t trace_ints;   /* int32 elements of a debug trace buffer for this call           */
@@ -209,6 +216,7 @@ typedef struct gemm_args_t {
  *   M, N, K >= 0.  M == 0 or N == 0: nothing to do.  K == 0: C is zero-filled.
  *   layout: GEMM_B_KN|GEMM_B_NK combined with GEMM_BF16|GEMM_FP16.
  *   mode: GEMM_HEURISTIC|GEMM_DP|GEMM_SPLITK|GEMM_STREAMK, optionally | GEMM_ATOMIC
+ *         (Stream-K / Split-K) or | GEMM_TWO_PASS (Split-K)
  *         (Stream-K only).
  *   splits: GEMM_SPLITK: S >= 1 dividing ceil(K/64).  GEMM_STREAMK: unit count
  *           (0 = one per CU).  GEMM_DP / GEMM_HEURISTIC: must be 0.

@@ -171,6 +171,8 @@ def test_plan_rejects_bad_arguments(dg):
         dict(M=-1), dict(layout=0x2), dict(layout=0x20), dict(mode=0x7), dict(mode=0x400),
         dict(mode=dg.GEMM_DP, splits=2), dict(mode=dg.GEMM_SPLITK, splits=0),
         dict(mode=dg.GEMM_SPLITK, splits=3), dict(mode=dg.GEMM_DP | dg.GEMM_ATOMIC),
+        dict(mode=dg.GEMM_STREAMK | dg.GEMM_TWO_PASS), dict(mode=dg.GEMM_DP | dg.GEMM_TWO_PASS),
+        dict(mode=dg.GEMM_SPLITK | dg.GEMM_ATOMIC | dg.GEMM_TWO_PASS, splits=2),
         dict(cus=0),
     ]
     for b in bad:
@@ -201,3 +203,27 @@ def test_gemm_rejects_before_launch(dg):
     # empty problems are a no-op, even with null pointers
     assert dg.gemm(0, 0, 0, 0, 256, 256, 0, dg.GEMM_DP, 0) == dg.GEMM_OK
     assert dg.gemm(0, 0, 0, 256, 0, 256, 0, dg.GEMM_DP, 0) == dg.GEMM_OK
+
+
+def test_splitk_merge_modes_plan(dg):
+    # deterministic Split-K adds the partials in split order, by a second kernel
+    # when the whole grid fits on the CUs at once (or GEMM_TWO_PASS asks for it),
+    # else by the last arriver in the launch; atomics keep no partials
+    M, N, K, S = 96, 512, 2048, 8
+    lw = dg.layout_word("nk", "bf16")
+    auto = dg.gemm_plan(M, N, K, lw, dg.GEMM_SPLITK, S, 256)          # 4 tiles x 8 = 32 <= 256
+    fold = dg.gemm_plan(M, N, K, lw, dg.GEMM_SPLITK, S, 16)           # 32 > 16 CUs
+    two = dg.gemm_plan(M, N, K, lw, dg.GEMM_SPLITK | dg.GEMM_TWO_PASS, S, 16)
+    atom = dg.gemm_plan(M, N, K, lw, dg.GEMM_SPLITK | dg.GEMM_ATOMIC, S, 256)
+    assert (auto.two_pass, fold.two_pass, two.two_pass, atom.two_pass) == (1, 0, 1, 0)
+    assert (auto.atomic, fold.atomic, two.atomic, atom.atomic) == (0, 0, 0, 1)
+    assert auto.workspace_bytes == fold.workspace_bytes == two.workspace_bytes
+    assert fold.workspace_bytes - atom.workspace_bytes == S * M * N * 4
+    for p in (auto, fold, two, atom):
+        assert (p.decision, p.splits, p.tiles, p.ipt) == (dg.GEMM_SPLITK, S, 4, 32)
+    # the large split-K arms of the wave-quantized workload stay in the launch
+    big = dg.gemm_plan(2048, 2176, 4096, 0, dg.GEMM_SPLITK, 2, 256)
+    assert big.two_pass == 0
+    # one split: nothing to merge
+    one = dg.gemm_plan(M, N, K, lw, dg.GEMM_SPLITK | dg.GEMM_TWO_PASS, 1, 256)
+    assert (one.two_pass, one.atomic) == (0, 0)
