@@ -169,6 +169,45 @@ def test_small_shapes_all_modes(dg, shape, mode, splits, atomic):
     assert_parity(c, A, B, w)
 
 
+def _random_cases(n, seed=11):
+    """Seeded random small problems: shape, layout, dtype, decomposition, merge mode
+    and CU count (small CU counts make tile groups and hybrids appear)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        layout = str(rng.choice(["kn", "nk"]))
+        M = int(rng.integers(1, 700))
+        N = int(rng.integers(1, 90)) * 8 if layout == "kn" else int(rng.integers(1, 700))
+        K = int(rng.integers(1, 40)) * 8
+        dtype = str(rng.choice(["bf16", "fp16"]))
+        mode = str(rng.choice(["dp", "splitk", "streamk", "heuristic"]))
+        cus = int(rng.choice([0, 4, 16, 64]))
+        ipt = -(-K // 64)
+        splits, atomic, two_pass = 0, False, False
+        if mode == "splitk":
+            splits = int(rng.choice([s for s in range(1, 9) if ipt % s == 0]))
+            merge = int(rng.integers(0, 3))
+            atomic, two_pass = merge == 1, merge == 2
+        elif mode == "streamk":
+            splits = int(rng.integers(1, 40))
+            atomic = bool(rng.integers(0, 2))
+        cases.append((i, M, N, K, layout, dtype, mode, splits, atomic, two_pass, cus))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(24), ids=lambda c: f"r{c[0]}")
+def test_random_small_problems(dg, case):
+    i, M, N, K, layout, dtype, mode, splits, atomic, two_pass, cus = case
+    dist = dict(dist="uniform", low=-1.0, high=1.0) if dtype == "bf16" else dict(dist="uniform", low=-0.5, high=0.5)
+    w = WORKLOADS["c1_sk32"].with_(name=f"random{i}", M=M, N=N, K=K, b_layout=layout, dtype=dtype, seed=100 + i,
+                                   **dist)
+    cap = dg.gemm_num_cus() if cus == 0 else cus
+    if mode == "streamk" and splits > cap:
+        splits = cap   # Stream-K units must all be resident
+    A, B, c = run(dg, w, mode=mode, splits=splits, atomic=atomic, two_pass=two_pass, num_cus=cus)
+    assert_parity(c, A, B, w)
+
+
 def test_k_zero_writes_zeros(dg):
     full, c = guarded_output(64, 64, DEV)
     a = torch.empty((64, 0), dtype=torch.bfloat16, device=DEV)
