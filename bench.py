@@ -71,11 +71,12 @@ class Call:
         args.A, args.B, args.C = a.data_ptr(), b.data_ptr(), c.data_ptr()
         args.M, args.N, args.K = M, N, K
         args.layout = dg.layout_word(b_layout, "bf16" if a.dtype == torch.bfloat16 else "fp16")
-        # `atomic`: False, True, "two_pass" (Split-K partials added by a second
-        # kernel) or "last_arriver" (Split-K partials folded in the launch)
+        # `atomic`: False, True, "two_pass" (partials of split tiles added by a
+        # second kernel) or "in_launch" (added in the launch: Split-K last arriver,
+        # Stream-K turnstile)
         args.mode = dg.mode_word(mode, atomic is True, atomic == "two_pass")
-        if atomic == "last_arriver":
-            args.debug = dg.GEMM_DEBUG_LAST_ARRIVER
+        if atomic == "in_launch":
+            args.debug = dg.GEMM_DEBUG_IN_LAUNCH
         args.splits = splits
         self.stream = stream or torch.cuda.current_stream()
         args.stream = self.stream.cuda_stream
@@ -139,15 +140,17 @@ def shape_arms(dg, name, steps, warmup):
     arms = {"dp": ("dp", 0, False)}
     if name.startswith("c2"):
         arms["splitk%d" % w.splits] = ("splitk", w.splits, False)
-        arms["splitk%d_last_arriver" % w.splits] = ("splitk", w.splits, "last_arriver")
+        arms["splitk%d_in_launch" % w.splits] = ("splitk", w.splits, "in_launch")
         arms["splitk%d_atomic" % w.splits] = ("splitk", w.splits, True)
     if name.startswith("c1"):
         arms["streamk32"] = ("streamk", 32, False)
+        arms["streamk32_in_launch"] = ("streamk", 32, "in_launch")
         arms["splitk4"] = ("splitk", 4, False)
-        arms["splitk4_last_arriver"] = ("splitk", 4, "last_arriver")
+        arms["splitk4_in_launch"] = ("splitk", 4, "in_launch")
         arms["heuristic"] = ("heuristic", 0, False)
     if name.startswith("c3"):
         arms["heuristic"] = ("heuristic", 0, False)
+        arms["heuristic_two_pass"] = ("heuristic", 0, "two_pass")
         arms["splitk2"] = ("splitk", 2, False)
         arms["splitk4"] = ("splitk", 4, False)
         arms["splitk2_two_pass"] = ("splitk", 2, "two_pass")
@@ -156,6 +159,7 @@ def shape_arms(dg, name, steps, warmup):
         arms = {"heuristic": ("heuristic", 0, False)}
     if name.startswith("c5"):
         arms["streamk_det"] = ("streamk", 0, False)
+        arms["streamk_det_two_pass"] = ("streamk", 0, "two_pass")
         arms["streamk_atomic"] = ("streamk", 0, True)
     if name.startswith("x1"):
         arms["heuristic"] = ("heuristic", 0, False)

@@ -52,7 +52,7 @@ GEMM_ATOMIC = 0x100
 GEMM_TWO_PASS = 0x200
 
 GEMM_DEBUG_NO_PUBLISH = 0x1
-GEMM_DEBUG_LAST_ARRIVER = 0x4
+GEMM_DEBUG_IN_LAUNCH = 0x4
 GEMM_DEBUG_TILE_DP = 0x8
 
 GEMM_BM = 128

@@ -178,7 +178,7 @@ int run(const gemm_args_t &a) {
                             a.num_cus > 0 ? a.num_cus : 256, &p, &why);
     if (rc != GEMM_OK) return fail(rc, why);
     if (a.num_cus < 0) return fail(GEMM_ERR_INVALID, "num_cus must be >= 0");
-    if ((a.debug & ~(GEMM_DEBUG_NO_PUBLISH | GEMM_DEBUG_LAST_ARRIVER | GEMM_DEBUG_TILE_DP)) != 0)
+    if ((a.debug & ~(GEMM_DEBUG_NO_PUBLISH | GEMM_DEBUG_IN_LAUNCH | GEMM_DEBUG_TILE_DP)) != 0)
         return fail(GEMM_ERR_INVALID, "unknown debug bits");
     if (a.M == 0 || a.N == 0) return GEMM_OK;
     if ((rc = check_operands(a)) != GEMM_OK) return rc;
@@ -300,7 +300,7 @@ int run(const gemm_args_t &a) {
     } else if (p.decision == GEMM_SPLITK) {
         kp.ntiles = (int)p.tiles;
         kp.merge = p.atomic                                        ? dgw::MERGE_ATOMIC
-                   : p.two_pass && !(a.debug & GEMM_DEBUG_LAST_ARRIVER) ? dgw::MERGE_TWO_PASS
+                   : p.two_pass && !(a.debug & GEMM_DEBUG_IN_LAUNCH) ? dgw::MERGE_TWO_PASS
                                                                        : dgw::MERGE_IN_LAUNCH;
         if (p.atomic) {
             if ((e = dgw::launch_zero(a.C, a.M * a.N, stream)) != hipSuccess) return fail_hip(e, "zero C");
@@ -323,8 +323,16 @@ int run(const gemm_args_t &a) {
         kp.q = (int)p.q;
         kp.big = (int)p.big;
         kp.tile_base = (int)p.dp_tiles;
+        const bool two_pass = p.two_pass && !(a.debug & GEMM_DEBUG_IN_LAUNCH);
+        kp.merge = two_pass ? dgw::MERGE_TWO_PASS : dgw::MERGE_IN_LAUNCH;
         if ((e = dgw::launch_gemm(dtype, blayout, kmode, (int)p.sk_units, kp, stream)) != hipSuccess)
             return fail_hip(e, "launch Stream-K kernel");
+        if (two_pass) {
+            KParams rp = kp;
+            rp.timing = nullptr;   // timing records cover the Stream-K launch's workgroups
+            if ((e = dgw::launch_streamk_reduce(rp, p.sk_tiles, stream)) != hipSuccess)
+                return fail_hip(e, "launch Stream-K reduction");
+        }
         if (p.dp_tiles > 0) {
             // hybrid: the first dp_tiles tiles run as whole-K tiles
             KParams dp = kp;

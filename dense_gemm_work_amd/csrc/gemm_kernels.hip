@@ -39,7 +39,8 @@
 //                the unit's slot and raises the unit's flag; the unit holding the
 //                tile's k = 0 iteration (its last segment) waits for the next
 //                units in ascending k, adds each partial to its accumulator, and
-//                stores the tile.
+//                stores the tile.  Two-pass: both kinds of split segment publish
+//                (two slots per unit) and streamk_reduce adds them in k order.
 //   K_SK_ATOMIC  whole tiles are stored; every other segment atomically adds its
 //                accumulator into C (zero-filled by the host first).
 //
@@ -1322,6 +1323,53 @@ __global__ __launch_bounds__(RED_THREADS) void splitk_reduce(KParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Two-pass Stream-K, second pass (the book chapter's Case 3 design: a separate
+// fixup kernel that sums each split tile's partials in k order).  The owner of
+// tile T (the unit holding its k = 0 iteration) published its segment into the
+// second slot bank, the next units their first segments into the first bank;
+// C = ((owner + peer 1) + peer 2) + ..., the turnstile's order, so the bits are
+// the turnstile's.  Slots are in register-native order: 16-byte element f =
+// ((quad * 4 + b) * 4 + e4) * 64 + lane holds rows r..r+3 of one column.  One
+// thread per such element, 16 workgroups of 256 threads per Stream-K tile;
+// tiles that one unit computed whole were stored by it and are skipped.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
+    const int ts = blockIdx.x / RED_BLOCKS_PER_TILE;
+    const int f = (blockIdx.x % RED_BLOCKS_PER_TILE) * RED_THREADS + threadIdx.x;
+    const int tb = ts * p.ipt, tile_end = tb + p.ipt;
+    const int owner = unit_of(tb, p.q, p.big);
+    if (unit_start(owner, p.q, p.big) + p.q + (owner < p.big ? 1 : 0) >= tile_end) return;   // whole tile
+    int vend = owner + 1;
+    while (vend < p.units && unit_start(vend, p.q, p.big) < tile_end) ++vend;
+    const int tile = p.tile_base + ts;
+    if (f == 0) {
+        trace_folded(p, tile, 0, owner);
+        for (int v = owner + 1; v < vend; ++v) trace_folded(p, tile, v - owner, v);
+    }
+    const f32x4 *own = reinterpret_cast<const f32x4 *>(p.part + ((size_t)p.units + owner) * (BM * BN));
+    const f32x4 *first = reinterpret_cast<const f32x4 *>(p.part);
+    f32x4 sum = own[f];
+    for (int v0 = owner + 1; v0 < vend; v0 += 4) {
+        f32x4 x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (v0 + j < vend) x[j] = first[(size_t)(v0 + j) * (BM * BN / 4) + f];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (v0 + j < vend) sum += x[j];
+    }
+    int m0, n0;
+    tile_origin(p, tile, m0, n0);
+    const int lane = f & 63, e4 = (f >> 6) & 3, b = (f >> 8) & 3, quad = f >> 10;
+    const int row = m0 + (quad >> 1) * 64 + (b >> 1) * 32 + 8 * e4 + 4 * (lane >> 5);
+    const int col = n0 + (quad & 1) * 64 + (b & 1) * 32 + (lane & 31);
+    if (col >= p.N) return;
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+        if (row + y < p.M) p.C[(size_t)(row + y) * p.N + col] = sum[y];
+}
+
+// ---------------------------------------------------------------------------
 // Stream-K: persistent; workgroup b runs unit worker_of(b).
 //
 // A unit's range [begin, end) of the flattened (tile, k) space falls into
@@ -1375,6 +1423,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
             trace_folded(p, tile, 0, u);
         } else if constexpr (ATOMIC) {
             atomic_add_c<NW>(p.C, m0, n0, p.M, p.N, t);
+        } else if (p.merge == MERGE_TWO_PASS) {
+            // streamk_reduce adds the tile's partials: contributors publish into
+            // the first slot bank, owners into the second
+            put_slot<NW>(p.part + ((size_t)(role == 1 ? p.units : 0) + u) * (BM * BN), t);
         } else if (role == 2) {
             // starts mid-tile: publish the partial, then the flag -- at once if
             // this is the unit's last segment, else from the next segment's loop
@@ -1475,6 +1527,13 @@ hipError_t launch_splitk_reduce(const KParams &p, hipStream_t stream) {
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
     if (tiles <= 0) return hipSuccess;
     hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)(tiles * RED_BLOCKS_PER_TILE)), dim3(RED_THREADS), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_streamk_reduce(const KParams &p, int64_t sk_tiles, hipStream_t stream) {
+    if (sk_tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(streamk_reduce, dim3((unsigned)(sk_tiles * RED_BLOCKS_PER_TILE)), dim3(RED_THREADS), 0,
+                       stream, p);
     return hipGetLastError();
 }
 

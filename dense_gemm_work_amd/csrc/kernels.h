@@ -37,9 +37,9 @@ struct KParams {
     int ntiles;            // tiles of a DP / Split-K launch
     int units, q, big;     // Stream-K unit ranges: unit u starts at u*q + min(u, big)
     int splits;            // Split-K factor S
-    int merge;             // Split-K: MERGE_IN_LAUNCH, MERGE_TWO_PASS or MERGE_ATOMIC
+    int merge;             // MERGE_IN_LAUNCH, MERGE_TWO_PASS or (Split-K) MERGE_ATOMIC
     int worker_base;       // trace id of this launch's worker 0
-    float *part;           // Stream-K slots [units][BM*BN] or Split-K partials [S][M][N]
+    float *part;           // Stream-K slots [units][BM*BN] ([2][units][BM*BN] two-pass) or Split-K [S][M][N]
     uint32_t *flags;       // Stream-K: flag per unit (epoch-valued)
     uint32_t *counters;    // Split-K: arrival counter per tile (reset by the last arriver)
     uint32_t *status;      // device error word
@@ -61,6 +61,11 @@ hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParam
 // Second pass of two-pass Split-K: C = ((P[0] + P[1]) + ...) + P[S-1] over the
 // partials [S,M,N] of `p` (p.part, p.splits, p.M, p.N, the tile grid and raster).
 hipError_t launch_splitk_reduce(const KParams &p, hipStream_t stream);
+
+// Second pass of two-pass Stream-K: every split tile of the launch's Stream-K
+// part (sk_tiles tiles from p.tile_base) gets its owner's and peers' partials
+// added in k order.
+hipError_t launch_streamk_reduce(const KParams &p, int64_t sk_tiles, hipStream_t stream);
 
 // Fill n 32-bit words with zero (used instead of hipMemsetAsync so the call can
 // be captured in a HIP graph).

@@ -58,8 +58,8 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
         *why = "GEMM_ATOMIC applies to Stream-K and Split-K only";
         return GEMM_ERR_INVALID;
     }
-    if (two_pass && (atomic || (decomp != GEMM_SPLITK && decomp != GEMM_HEURISTIC))) {
-        *why = "GEMM_TWO_PASS applies to deterministic Split-K only";
+    if (two_pass && (atomic || decomp == GEMM_DP)) {
+        *why = "GEMM_TWO_PASS applies to deterministic Split-K and Stream-K only";
         return GEMM_ERR_INVALID;
     }
     if ((decomp == GEMM_DP || decomp == GEMM_HEURISTIC) && splits != 0) {
@@ -117,7 +117,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
             }
         }
         // GEMM_ATOMIC / GEMM_TWO_PASS apply to whichever of Stream-K and Split-K
-        // the rule picks (two-pass to Split-K only); data-parallel ignores them
+        // the rule picks; data-parallel ignores them
     } else if (decomp == GEMM_SPLITK) {
         if (splits < 1) { *why = "GEMM_SPLITK needs splits >= 1"; return GEMM_ERR_INVALID; }
         if (p.ipt == 0 || p.ipt % splits != 0) {
@@ -172,8 +172,19 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
                                                    ceil_div(longest, ipt1) + 1));
         p.max_fold = int32_t(std::min<int64_t>(units, ceil_div(ipt1, std::max<int64_t>(p.q, 1)) + 1));
         p.max_fold = std::max(p.max_fold, 1);
-        // fp32 partial slot per unit (a unit publishes at most its first segment)
-        p.workspace_bytes = atomic ? 0 : units * int64_t(GEMM_BM) * GEMM_BN * 4;
+        // Deterministic: the owner of a split tile adds its peers' partials in k
+        // order in the launch (turnstile), or every split segment publishes and a
+        // second kernel adds them in the same order (same bits).  The turnstile's
+        // owner takes its peers one after another, so with three or more peers per
+        // tile (short units: max_fold >= 4) the second kernel is faster (measured:
+        // 32 units of 8 iterations on 8 tiles 13.6 -> 11.9 us); with one or two
+        // peers the turnstile is (2048x2176x4096: 45.7 vs 49.3 us; 1536^2 x 16384
+        // fp16: 86.1 vs 88.9 us).
+        p.two_pass = !atomic && (two_pass || p.max_fold >= 4) ? 1 : 0;
+        // fp32 partial slots: one per unit for the turnstile (a unit publishes at
+        // most its first segment); two per unit with the second kernel (its first
+        // segment as a contributor, its last as an owner)
+        p.workspace_bytes = atomic ? 0 : (p.two_pass ? 2 : 1) * units * int64_t(GEMM_BM) * GEMM_BN * 4;
         break;
     }
     default:

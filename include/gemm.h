@@ -32,7 +32,11 @@
  *                 A unit that starts a tile mid-K publishes an fp32 partial and
  *                 a flag; the unit holding the tile's k = 0 iteration waits for
  *                 its peers in k order, adds their partials and writes C
- *                 (deterministic "turnstile", Case 4's reduction modes).  With
+ *                 (deterministic "turnstile", Case 4's reduction modes).  When a
+ *                 tile can have three or more peers (plan.max_fold >= 4), or with
+ *                 GEMM_TWO_PASS, every split segment publishes instead and a
+ *                 second kernel adds each tile's partials in the same k order
+ *                 (Case 3's separate fixup kernel; same bits; plan.two_pass).  With
  *                 GEMM_ATOMIC, split tiles are instead merged by fp32 atomic
  *                 adds into C, which the library zero-fills first
  *                 (nondeterministic mode; docc StreamK page, "Rewrite it produces").
@@ -87,8 +91,8 @@ extern "C" {
 /* bits 8-9: how split tiles are merged (Stream-K and Split-K) */
 #define GEMM_DETERMINISTIC 0x000u  /* k-ordered: Stream-K turnstile / Split-K fold in the same launch */
 #define GEMM_ATOMIC        0x100u  /* fp32 atomic adds into a zero-filled C (Stream-K, Split-K) */
-#define GEMM_TWO_PASS      0x200u  /* Split-K only: always add the partials [S,M,N] in split
-                                      order by a second kernel (same bits as the in-launch fold) */
+#define GEMM_TWO_PASS      0x200u  /* always add split tiles' partials in k order by a second
+                                      kernel (Split-K and Stream-K; same bits as in the launch) */
 
 /* ---- debug bits for gemm_args_t.debug -------------------------------------------- */
 #define GEMM_DEBUG_NO_PUBLISH 0x1u /* Stream-K contributors store partials but never
@@ -96,10 +100,10 @@ extern "C" {
                                       limit and gemm_sync_status() reports
                                       GEMM_ERR_TIMEOUT.  Exercises the failure path;
                                       C is not valid.                               */
-#define GEMM_DEBUG_LAST_ARRIVER 0x4u /* deterministic Split-K: the last arriver at each
-                                       tile's counter folds it in the launch even
-                                       where the plan chose a second kernel.  Same
-                                       result bits; exercises that path.           */
+#define GEMM_DEBUG_IN_LAUNCH 0x4u /* deterministic merges stay in the launch (Split-K:
+                                    the last arriver at each tile's counter; Stream-K:
+                                    the turnstile) even where the plan chose a second
+                                    kernel.  Same result bits; exercises that path. */
 #define GEMM_DEBUG_TILE_DP 0x8u /* data-parallel launches run one 128x128 tile per
                                    workgroup even where 2x2 tile groups apply.     */
 
@@ -131,8 +135,9 @@ typedef struct gemm_plan_t {
     int32_t splits;       /* Split-K factor S (1 for the other decompositions)              */
     int32_t max_segments; /* most tile segments one worker can touch                        */
     int32_t max_fold;     /* most workers contributing to one tile                          */
-    int32_t two_pass;     /* 1 when Split-K partials are added by a second kernel (the plan
-                             picks it for grids that fit on the CUs at once)            */
+    int32_t two_pass;     /* 1 when split tiles' partials are added by a second kernel (the
+                             plan picks it for Split-K grids that fit on the CUs at once
+                             and for Stream-K tiles with three or more peers)           */
     int64_t workers;      /* traced workers: units + dp_tiles, tiles * S, or tiles          */
     int64_t workspace_bytes; /* device workspace the call needs                             */
     int64_t trace_ints;   /* int32 elements of a debug trace buffer for this call           */

@@ -171,7 +171,7 @@ def test_plan_rejects_bad_arguments(dg):
         dict(M=-1), dict(layout=0x2), dict(layout=0x20), dict(mode=0x7), dict(mode=0x400),
         dict(mode=dg.GEMM_DP, splits=2), dict(mode=dg.GEMM_SPLITK, splits=0),
         dict(mode=dg.GEMM_SPLITK, splits=3), dict(mode=dg.GEMM_DP | dg.GEMM_ATOMIC),
-        dict(mode=dg.GEMM_STREAMK | dg.GEMM_TWO_PASS), dict(mode=dg.GEMM_DP | dg.GEMM_TWO_PASS),
+        dict(mode=dg.GEMM_STREAMK | dg.GEMM_ATOMIC | dg.GEMM_TWO_PASS), dict(mode=dg.GEMM_DP | dg.GEMM_TWO_PASS),
         dict(mode=dg.GEMM_SPLITK | dg.GEMM_ATOMIC | dg.GEMM_TWO_PASS, splits=2),
         dict(cus=0),
     ]
@@ -227,3 +227,17 @@ def test_splitk_merge_modes_plan(dg):
     # one split: nothing to merge
     one = dg.gemm_plan(M, N, K, lw, dg.GEMM_SPLITK | dg.GEMM_TWO_PASS, 1, 256)
     assert (one.two_pass, one.atomic) == (0, 0)
+
+
+def test_streamk_two_pass_plan(dg):
+    # the second kernel needs two partial slots per unit (first and last segment);
+    # the plan picks it when a tile can have three or more peers (short units)
+    c3 = dg.gemm_plan(2048, 2176, 4096, 0, dg.GEMM_HEURISTIC, 0, 256)               # max_fold 2
+    c3t = dg.gemm_plan(2048, 2176, 4096, 0, dg.GEMM_HEURISTIC | dg.GEMM_TWO_PASS, 0, 256)
+    c5 = dg.gemm_plan(1536, 1536, 16384, dg.GEMM_FP16, dg.GEMM_STREAMK, 0, 256)      # max_fold 3
+    c1 = dg.gemm_plan(256, 512, 2048, 0, dg.GEMM_STREAMK, 32, 256)                   # max_fold 5
+    c1a = dg.gemm_plan(256, 512, 2048, 0, dg.GEMM_STREAMK | dg.GEMM_ATOMIC, 32, 256)
+    assert (c3.max_fold, c5.max_fold, c1.max_fold) == (2, 3, 5)
+    assert (c3.two_pass, c3t.two_pass, c5.two_pass, c1.two_pass, c1a.two_pass) == (0, 1, 0, 1, 0)
+    assert c3t.workspace_bytes - c3.workspace_bytes == 256 * 128 * 128 * 4
+    assert (c3t.q, c3t.big, c3t.sk_units) == (c3.q, c3.big, c3.sk_units)

@@ -332,7 +332,7 @@ def test_splitk_two_pass_and_atomic(dg, name, M, N):
     full1, c1 = guarded_output(w.M, w.N, DEV)
     full2, c2 = guarded_output(w.M, w.N, DEV)
     dg.gemm_tensors(a, b, c0, b_layout=w.b_layout, mode="splitk", splits=splits)
-    dg.gemm_tensors(a, b, c1, b_layout=w.b_layout, mode="splitk", splits=splits, debug=dg.GEMM_DEBUG_LAST_ARRIVER)
+    dg.gemm_tensors(a, b, c1, b_layout=w.b_layout, mode="splitk", splits=splits, debug=dg.GEMM_DEBUG_IN_LAUNCH)
     dg.gemm_tensors(a, b, c2, b_layout=w.b_layout, mode="splitk", splits=splits, atomic=True)
     assert dg.gemm_sync_status() == 0
     for f in (full0, full1, full2):
@@ -356,6 +356,49 @@ def test_splitk_two_pass_trace(dg):
     assert dg.gemm_sync_status() == 0
     got = decode_trace(tr)
     _, segs, folds = expected_trace(M, N, K, "splitk", S, 256)
+    assert got["segments"] == segs and got["folds"] == folds
+    assert np.all(got["coverage"] == 1)
+
+
+@pytest.mark.parametrize("name,mode,splits,M,N,K,cus", [
+    ("c1_sk32", "streamk", 32, None, None, None, 0),
+    ("c3_wavequant", "heuristic", 0, None, None, None, 0),
+    ("c5_longk_fp16", "streamk", 0, None, None, None, 0),
+    ("c1_sk32", "streamk", 7, 300, 200, 320, 0),          # ragged M and N, units crossing tile edges
+    ("c1_sk32", "heuristic", 0, 1408, 768, 1024, 20),     # hybrid: DP tiles + Stream-K part
+])
+def test_streamk_two_pass_equals_turnstile(dg, name, mode, splits, M, N, K, cus):
+    # a second kernel adding each split tile's partials in k order gives the
+    # turnstile's bits
+    w = WORKLOADS[name]
+    if M is not None:
+        w = w.with_(M=M, N=N, K=K)
+    A, B = make_operands(w)
+    a, b = A.to(DEV), B.to(DEV)
+    say(f"  two-pass vs turnstile Stream-K {w.name} {w.M}x{w.N}x{w.K} units={splits} cus={cus}")
+    full0, c0 = guarded_output(w.M, w.N, DEV)
+    full1, c1 = guarded_output(w.M, w.N, DEV)
+    dg.gemm_tensors(a, b, c0, b_layout=w.b_layout, mode=mode, splits=splits, num_cus=cus,
+                    debug=dg.GEMM_DEBUG_IN_LAUNCH)
+    dg.gemm_tensors(a, b, c1, b_layout=w.b_layout, mode=mode, splits=splits, num_cus=cus, two_pass=True)
+    assert dg.gemm_sync_status() == 0
+    assert guards_intact(full0, w.M, w.N) and guards_intact(full1, w.M, w.N)
+    assert torch.equal(c0.view(torch.int32), c1.view(torch.int32))
+    assert_parity(c1, A, B, w, rows=sample_rows(w.M, 16))
+
+
+@pytest.mark.parametrize("M,N,K,units", [(256, 512, 2048, 32), (300, 200, 320, 7), (1536, 1536, 16384, 0)])
+def test_streamk_two_pass_trace(dg, M, N, K, units):
+    p = dg.gemm_plan(M, N, K, 0, dg.mode_word("streamk", two_pass=True), units, 256)
+    assert p.two_pass == 1
+    w = WORKLOADS["c1_sk32"].with_(M=M, N=N, K=K)
+    A, B = make_operands(w)
+    tr = torch.zeros(p.trace_ints, dtype=torch.int32, device=DEV)
+    _, c = guarded_output(M, N, DEV)
+    dg.gemm_tensors(A.to(DEV), B.to(DEV), c, mode="streamk", splits=units, two_pass=True, trace=tr)
+    assert dg.gemm_sync_status() == 0
+    got = decode_trace(tr)
+    _, segs, folds = expected_trace(M, N, K, "streamk", units, 256)
     assert got["segments"] == segs and got["folds"] == folds
     assert np.all(got["coverage"] == 1)
 
@@ -397,7 +440,8 @@ def test_bounded_wait_reports_timeout(dg):
     a, b = A.to(DEV), B.to(DEV)
     c = torch.empty((w.M, w.N), dtype=torch.float32, device=DEV)
     say("  forced timeout (contributors never raise flags, spin limit 2000 polls)")
-    dg.gemm_tensors(a, b, c, mode="streamk", splits=12, spin_limit=2000, debug=dg.GEMM_DEBUG_NO_PUBLISH)
+    dg.gemm_tensors(a, b, c, mode="streamk", splits=12, spin_limit=2000,
+                    debug=dg.GEMM_DEBUG_NO_PUBLISH | dg.GEMM_DEBUG_IN_LAUNCH)
     assert dg.gemm_sync_status() == dg.GEMM_ERR_TIMEOUT
     # the status is cleared and the next call is healthy
     full, c2 = guarded_output(w.M, w.N, DEV)
