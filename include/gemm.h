@@ -221,8 +221,7 @@ typedef struct gemm_args_t {
  *   M, N, K >= 0.  M == 0 or N == 0: nothing to do.  K == 0: C is zero-filled.
  *   layout: GEMM_B_KN|GEMM_B_NK combined with GEMM_BF16|GEMM_FP16.
  *   mode: GEMM_HEURISTIC|GEMM_DP|GEMM_SPLITK|GEMM_STREAMK, optionally | GEMM_ATOMIC
- *         (Stream-K / Split-K) or | GEMM_TWO_PASS (Split-K)
- *         (Stream-K only).
+ *         or | GEMM_TWO_PASS (Stream-K and Split-K; not both).
  *   splits: GEMM_SPLITK: S >= 1 dividing ceil(K/64).  GEMM_STREAMK: unit count
  *           (0 = one per CU).  GEMM_DP / GEMM_HEURISTIC: must be 0.
  * Requirements (else GEMM_ERR_UNSUPPORTED): A, B, C 16-byte aligned; K a
