@@ -61,7 +61,7 @@ def parse():
 class Call:
     """A prepared gemm_ex call (argument struct built once; each call is one ctypes call)."""
 
-    def __init__(self, dg, a, b, c, b_layout, mode, splits=0, atomic=False, stream=None):
+    def __init__(self, dg, a, b, c, b_layout, mode, splits=0, atomic=False, stream=None, epilogue=None):
         import torch
 
         self.dg = dg
@@ -78,6 +78,12 @@ class Call:
         if atomic == "in_launch":
             args.debug = dg.GEMM_DEBUG_IN_LAUNCH
         args.splits = splits
+        if epilogue is not None:
+            # fused epilogue c = act(alpha a.b + beta c + bias): (alpha, beta, bias tensor, act)
+            alpha, beta, bias, act = epilogue
+            args.epilogue = dg.GEMM_EPI_ALPHA_BETA | dg.GEMM_EPI_BIAS | dg.ACTIVATIONS[act]
+            args.alpha, args.beta, args.bias = alpha, beta, bias.data_ptr()
+            self.bias = bias
         self.stream = stream or torch.cuda.current_stream()
         args.stream = self.stream.cuda_stream
         self.args = args
@@ -136,7 +142,9 @@ def shape_arms(dg, name, steps, warmup):
     w = WORKLOADS[name]
     A, B = make_operands(w)
     a, b = A.cuda(), B.cuda()
-    c = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    c = torch.zeros((w.M, w.N), dtype=torch.float32, device="cuda")
+    bias = torch.linspace(-1.0, 1.0, w.N, dtype=torch.float32, device="cuda")
+    epi = (0.75, -0.5, bias, "gelu")   # alpha, beta, bias, activation of the "_epilogue" arms
     arms = {"dp": ("dp", 0, False)}
     if name.startswith("c2"):
         arms["splitk%d" % w.splits] = ("splitk", w.splits, False)
@@ -150,13 +158,14 @@ def shape_arms(dg, name, steps, warmup):
         arms["heuristic"] = ("heuristic", 0, False)
     if name.startswith("c3"):
         arms["heuristic"] = ("heuristic", 0, False)
+        arms["heuristic_epilogue"] = ("heuristic", 0, False, epi)
         arms["heuristic_two_pass"] = ("heuristic", 0, "two_pass")
         arms["splitk2"] = ("splitk", 2, False)
         arms["splitk4"] = ("splitk", 4, False)
         arms["splitk2_two_pass"] = ("splitk", 2, "two_pass")
         arms["splitk4_two_pass"] = ("splitk", 4, "two_pass")
     if name.startswith("c4"):
-        arms = {"heuristic": ("heuristic", 0, False)}
+        arms = {"heuristic": ("heuristic", 0, False), "heuristic_epilogue": ("heuristic", 0, False, epi)}
     if name.startswith("c5"):
         arms["streamk_det"] = ("streamk", 0, False)
         arms["streamk_det_two_pass"] = ("streamk", 0, "two_pass")
@@ -165,8 +174,8 @@ def shape_arms(dg, name, steps, warmup):
         arms["heuristic"] = ("heuristic", 0, False)
         arms["streamk"] = ("streamk", 0, False)
     out = {"M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype, "b_layout": w.b_layout}
-    for arm, (mode, splits, atomic) in arms.items():
-        call = Call(dg, a, b, c, w.b_layout, mode, splits, atomic)
+    for arm, (mode, splits, atomic, *ep) in arms.items():
+        call = Call(dg, a, b, c, w.b_layout, mode, splits, atomic, epilogue=ep[0] if ep else None)
         st = steps if not name.startswith("c4") else max(5, steps // 10)
         out[arm] = arm_result(w, call, st, warmup)
         log(f"  {name:14s} {arm:15s} {out[arm]}")

@@ -51,6 +51,12 @@ GEMM_DETERMINISTIC = 0x000
 GEMM_ATOMIC = 0x100
 GEMM_TWO_PASS = 0x200
 
+GEMM_EPI_ALPHA_BETA = 0x01
+GEMM_EPI_BIAS = 0x02
+GEMM_EPI_RELU = 0x10
+GEMM_EPI_GELU = 0x20
+ACTIVATIONS = {"none": 0, "relu": GEMM_EPI_RELU, "gelu": GEMM_EPI_GELU}
+
 GEMM_DEBUG_NO_PUBLISH = 0x1
 GEMM_DEBUG_IN_LAUNCH = 0x4
 GEMM_DEBUG_TILE_DP = 0x8
@@ -94,6 +100,8 @@ class GemmArgs(ctypes.Structure):
         ("trace", ctypes.c_void_p), ("trace_ints", ctypes.c_int64),
         ("spin_limit", ctypes.c_uint32), ("debug", ctypes.c_uint32),
         ("timing", ctypes.c_void_p),
+        ("epilogue", ctypes.c_uint32), ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
+        ("bias", ctypes.c_void_p),
     ]
 
 
@@ -205,9 +213,13 @@ def mode_word(mode: str, atomic: bool = False, two_pass: bool = False) -> int:
 def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits: int = 0,
                  atomic: bool = False, num_cus: int = 0, unit_perm=None, trace=None,
                  workspace=None, spin_limit: int = 0, debug: int = 0, timing=None,
-                 stream=None, two_pass: bool = False) -> None:
+                 stream=None, two_pass: bool = False, alpha: Optional[float] = None,
+                 beta: Optional[float] = None, bias=None, act: str = "none") -> None:
     """``c[M,N] = a[M,K] . b`` (b [K,N]) or ``a . b^T`` (b [N,K]) on torch tensors.
 
+    With ``alpha``/``beta``/``bias``/``act`` the call fuses the epilogue
+    ``c = act(alpha a.b + beta c + bias)`` (bias: contiguous fp32 [N] device tensor;
+    act: "none", "relu" or "gelu").
     a, b: contiguous bf16/fp16 tensors on one HIP device; c: contiguous fp32 [M,N].
     unit_perm / trace / workspace / timing: optional int32 / int32 / any-dtype / int64
     device tensors (see gemm_args_t in include/gemm.h).
@@ -270,4 +282,16 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
             args.timing = timing.data_ptr()
         args.spin_limit = spin_limit
         args.debug = debug
+        word = ACTIVATIONS[act]
+        if alpha is not None or beta is not None:
+            word |= GEMM_EPI_ALPHA_BETA
+            args.alpha = 1.0 if alpha is None else float(alpha)
+            args.beta = 0.0 if beta is None else float(beta)
+        if bias is not None:
+            if bias.dtype != torch.float32 or not bias.is_cuda or not bias.is_contiguous() or \
+                    tuple(bias.shape) != (N,):
+                raise TypeError("bias must be a contiguous fp32 [N] device tensor")
+            word |= GEMM_EPI_BIAS
+            args.bias = bias.data_ptr()
+        args.epilogue = word
         _check(gemm_ex(args))

@@ -156,9 +156,35 @@ int check_operands(const gemm_args_t &a) {
     if (overlaps(a.C, cb, a.A, ab) || overlaps(a.C, cb, a.B, bb))
         return fail(GEMM_ERR_INVALID, "C must not overlap A or B");
     if (a.trace && a.trace_ints <= 0) return fail(GEMM_ERR_INVALID, "trace_ints must be > 0");
+    if (a.epilogue & GEMM_EPI_BIAS) {
+        if (reinterpret_cast<uintptr_t>(a.bias) & 15) return fail(GEMM_ERR_UNSUPPORTED, "bias must be 16-byte aligned");
+        if (overlaps(a.C, cb, a.bias, a.N * 4)) return fail(GEMM_ERR_INVALID, "bias must not overlap C");
+    }
     if (a.workspace && reinterpret_cast<uintptr_t>(a.workspace) & 255)
         return fail(GEMM_ERR_INVALID, "a caller workspace must be 256-byte aligned");
     return GEMM_OK;
+}
+
+// Epilogue word and its operands (no HIP call).
+int check_epilogue(const gemm_args_t &a) {
+    const uint32_t known = GEMM_EPI_ALPHA_BETA | GEMM_EPI_BIAS | GEMM_EPI_RELU | GEMM_EPI_GELU;
+    if (a.epilogue & ~known) return fail(GEMM_ERR_INVALID, "epilogue word has unknown bits");
+    if ((a.epilogue & GEMM_EPI_RELU) && (a.epilogue & GEMM_EPI_GELU))
+        return fail(GEMM_ERR_INVALID, "GEMM_EPI_RELU and GEMM_EPI_GELU exclude each other");
+    if (((a.epilogue & GEMM_EPI_BIAS) != 0) != (a.bias != nullptr))
+        return fail(GEMM_ERR_INVALID, "bias must be given exactly when GEMM_EPI_BIAS is set");
+    return GEMM_OK;
+}
+
+// Fill the epilogue fields of `kp` for the final stores of a deterministic
+// launch (EPI_FULL) or of the launches around atomic merges (EPI_ACCUM).
+void set_epilogue(const gemm_args_t &a, bool accum, KParams &kp) {
+    const bool ab = (a.epilogue & GEMM_EPI_ALPHA_BETA) != 0;
+    kp.alpha = ab ? a.alpha : 1.0f;
+    kp.beta = ab ? a.beta : 0.0f;
+    kp.bias = (a.epilogue & GEMM_EPI_BIAS) ? a.bias : nullptr;
+    kp.act = (a.epilogue & GEMM_EPI_RELU) ? dgw::ACT_RELU : (a.epilogue & GEMM_EPI_GELU) ? dgw::ACT_GELU : dgw::ACT_NONE;
+    kp.epi = a.epilogue == 0 ? dgw::EPI_PLAIN : accum ? dgw::EPI_ACCUM : dgw::EPI_FULL;
 }
 
 struct TraceHeader {
@@ -180,6 +206,7 @@ int run(const gemm_args_t &a) {
     if (a.num_cus < 0) return fail(GEMM_ERR_INVALID, "num_cus must be >= 0");
     if ((a.debug & ~(GEMM_DEBUG_NO_PUBLISH | GEMM_DEBUG_IN_LAUNCH | GEMM_DEBUG_TILE_DP)) != 0)
         return fail(GEMM_ERR_INVALID, "unknown debug bits");
+    if ((rc = check_epilogue(a)) != GEMM_OK) return rc;
     if (a.M == 0 || a.N == 0) return GEMM_OK;
     if ((rc = check_operands(a)) != GEMM_OK) return rc;
 
@@ -199,7 +226,18 @@ int run(const gemm_args_t &a) {
     const int blayout = (a.layout & 0xFu) == GEMM_B_NK ? 1 : 0;
 
     if (a.K == 0) {  // the empty sum
-        if ((e = dgw::launch_zero(a.C, a.M * a.N, stream)) != hipSuccess) return fail_hip(e, "zero C");
+        if (a.epilogue == 0) {
+            if ((e = dgw::launch_zero(a.C, a.M * a.N, stream)) != hipSuccess) return fail_hip(e, "zero C");
+        } else {
+            KParams ep;
+            std::memset(&ep, 0, sizeof ep);
+            ep.C = a.C;
+            ep.M = (int)a.M;
+            ep.N = (int)a.N;
+            set_epilogue(a, false, ep);
+            if ((e = dgw::launch_epilogue_pass(ep, dgw::EPASS_ONLY, stream)) != hipSuccess)
+                return fail_hip(e, "epilogue of an empty sum");
+        }
         return GEMM_OK;
     }
 
@@ -264,6 +302,18 @@ int run(const gemm_args_t &a) {
     kp.spin_limit = a.spin_limit ? a.spin_limit : kDefaultSpin;
     kp.debug = a.debug;
     kp.perm = a.unit_perm;
+    // atomic merges add into C: with an epilogue, C first becomes beta C + bias,
+    // the merges add alpha acc, and the activation is a last elementwise pass
+    const bool atomic_merge = p.atomic && p.decision != GEMM_DP;
+    set_epilogue(a, atomic_merge, kp);
+    auto prepare_atomic_c = [&]() -> int {
+        if (kp.epi == dgw::EPI_PLAIN) {
+            if ((e = dgw::launch_zero(a.C, a.M * a.N, stream)) != hipSuccess) return fail_hip(e, "zero C");
+        } else if ((e = dgw::launch_epilogue_pass(kp, dgw::EPASS_PRE, stream)) != hipSuccess) {
+            return fail_hip(e, "epilogue pre-pass");
+        }
+        return GEMM_OK;
+    };
 
     if (a.trace) {
         if (a.trace_ints < p.trace_ints)
@@ -302,9 +352,7 @@ int run(const gemm_args_t &a) {
         kp.merge = p.atomic                                        ? dgw::MERGE_ATOMIC
                    : p.two_pass && !(a.debug & GEMM_DEBUG_IN_LAUNCH) ? dgw::MERGE_TWO_PASS
                                                                        : dgw::MERGE_IN_LAUNCH;
-        if (p.atomic) {
-            if ((e = dgw::launch_zero(a.C, a.M * a.N, stream)) != hipSuccess) return fail_hip(e, "zero C");
-        }
+        if (p.atomic && (rc = prepare_atomic_c()) != GEMM_OK) return rc;
         if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_SPLITK, (int)(p.tiles * p.splits), kp, stream)) !=
             hipSuccess)
             return fail_hip(e, "launch Split-K kernel");
@@ -315,7 +363,7 @@ int run(const gemm_args_t &a) {
         }
     } else {
         if (p.atomic) {
-            if ((e = dgw::launch_zero(a.C, a.M * a.N, stream)) != hipSuccess) return fail_hip(e, "zero C");
+            if ((rc = prepare_atomic_c()) != GEMM_OK) return rc;
         } else {
             kp.epoch = next_epoch();
         }
@@ -344,6 +392,10 @@ int run(const gemm_args_t &a) {
             if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_DP, (int)p.dp_tiles, dp, stream)) != hipSuccess)
                 return fail_hip(e, "launch DP kernel (hybrid part)");
         }
+    }
+    if (atomic_merge && kp.act != dgw::ACT_NONE) {
+        if ((e = dgw::launch_epilogue_pass(kp, dgw::EPASS_POST, stream)) != hipSuccess)
+            return fail_hip(e, "epilogue activation pass");
     }
     return GEMM_OK;
 }
@@ -433,6 +485,6 @@ int32_t gemm_num_cus(void) {
     return n;
 }
 
-int32_t gemm_version(void) { return 1; }
+int32_t gemm_version(void) { return 2; }
 
 }  // extern "C"

@@ -48,6 +48,7 @@
 // STATUS_TIMEOUT and the kernel goes on, so every wave always exits.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "../../include/gemm.h"
@@ -612,9 +613,229 @@ __device__ __forceinline__ void store_tile(float *X, int m0, int n0, int M, int 
     for_each_element<NW>(t, m0, n0, M, N, [&](float v, size_t off) { X[off] = v; });
 }
 
-template <int NW>
-__device__ __forceinline__ void atomic_add_c(float *C, int m0, int n0, int M, int N, const Tile<NW> &t) {
-    for_each_element<NW>(t, m0, n0, M, N, [&](float v, size_t off) { unsafeAtomicAdd(C + off, v); });
+// ---------------------------------------------------------------------------
+// Fused epilogue (CUTLASS optimisation guide, "Epilogue Optimization" and
+// "Fused Epilogue Operations"): y = alpha acc + beta c + bias[col], then ReLU
+// or GELU.  Every kernel evaluates it with this one sequence of fp32
+// operations, contraction off: y = fma(alpha, acc, beta c) + b, where c = 0
+// when beta == 0 (C is then not read) and b = 0 without a bias, then the
+// activation (GELU: (y / 2) (1 + erf(y / sqrt 2)), each step rounded).  A
+// deterministic merge therefore gives the same bits whichever kernel stores
+// the tile.  Stores of many elements run the activation's branch once for all
+// of them (`finish`), so the unrolled code runs straight through: with the
+// branch inside every element the code for 32 elements spans tens of KiB and
+// misses in the instruction cache on every tile.
+// ---------------------------------------------------------------------------
+// GELU(y) = (y / 2) (1 + erf(z)), z = y / sqrt 2.  1 + erf(z) is formed from
+// q = erfc(|z|) as 2 - q (y >= 0) or q (y < 0), so the negative side keeps its
+// relative accuracy, with q from the rational approximation of Abramowitz and
+// Stegun, Handbook of Mathematical Functions, 7.1.26:
+//   erfc(x) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2) + e(x),
+//   t = 1 / (1 + p x), |e(x)| <= 1.5e-7 for x >= 0,
+// evaluated with explicit fma, the hardware reciprocal and exp2, branch free.
+__device__ __forceinline__ float gelu_value(float y) {
+#pragma clang fp contract(off)
+    constexpr float P = 0.3275911f, A1 = 0.254829592f, A2 = -0.284496736f, A3 = 1.421413741f,
+                    A4 = -1.453152027f, A5 = 1.061405429f;
+    constexpr float RSQRT2 = 0.70710678118654752f, NEG_HALF_LOG2E = -0.72134752044448170f;
+    const float x = fabsf(y) * RSQRT2;
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(P, x, 1.0f));
+    float poly = __builtin_fmaf(A5, t, A4);
+    poly = __builtin_fmaf(poly, t, A3);
+    poly = __builtin_fmaf(poly, t, A2);
+    poly = __builtin_fmaf(poly, t, A1);
+    const float q = (poly * t) * __builtin_amdgcn_exp2f((y * y) * NEG_HALF_LOG2E);   // exp(-x^2) = 2^(-y^2 log2(e) / 2)
+    const float one_plus_erf = y >= 0.0f ? 2.0f - q : q;
+    return (0.5f * y) * one_plus_erf;
+}
+
+__device__ __forceinline__ float act_apply(int act, float y) {
+    if (act == ACT_RELU) return y > 0.0f ? y : 0.0f;
+    if (act == ACT_GELU) return gelu_value(y);
+    return y;
+}
+
+__device__ __forceinline__ float lin_value(float alpha, float beta, float acc, float c, float b) {
+#pragma clang fp contract(off)
+    return __builtin_fmaf(alpha, acc, beta * c) + b;
+}
+
+__device__ __forceinline__ float epi_value(const KParams &p, float acc, float c, float b) {
+    return act_apply(p.act, lin_value(p.alpha, p.beta, acc, c, b));
+}
+
+__device__ __forceinline__ bool reads_c(const KParams &p) { return p.epi == EPI_ACCUM || p.beta != 0.0f; }
+
+// Final values of n elements, in place: v holds the sums, c the prior C values
+// (0 where not read), b the bias values (0 without a bias).  EPI_ACCUM:
+// v = fma(alpha, v, c) with no activation (a later pass applies it).
+template <int N>
+__device__ __forceinline__ void finish(const KParams &p, float (&v)[N], const float (&c)[N], const float (&b)[N]) {
+    const float alpha = p.alpha, beta = p.beta;
+    if (p.epi == EPI_ACCUM) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = __builtin_fmaf(alpha, v[i], c[i]);
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = lin_value(alpha, beta, v[i], c[i], b[i]);
+    if (p.act == ACT_RELU) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = v[i] > 0.0f ? v[i] : 0.0f;
+    } else if (p.act == ACT_GELU) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = gelu_value(v[i]);
+    }
+}
+
+// One element, loads included (element-by-element paths only).
+__device__ __forceinline__ float final_scalar(const KParams &p, float acc, size_t off, int col) {
+    if (p.epi == EPI_PLAIN) return acc;
+    float v[1] = {acc};
+    const float c[1] = {reads_c(p) ? p.C[off] : 0.0f};
+    const float b[1] = {p.bias ? p.bias[col] : 0.0f};
+    finish<1>(p, v, c, b);
+    return v[0];
+}
+
+// One wave's 32-row block of C for the epilogue: element (e, j) of lane l is at
+// row R0 + 8 (e / 4) + 4 (l / 32) + e % 4, column C0 + 32 j + l % 32 (the
+// 32x32 MFMA result layout).  Accesses go through a buffer range that ends at
+// the block's last element inside C, so rows beyond M fall outside it, and a
+// lane whose column is beyond N gets an offset outside every range: masked
+// elements need no branches (their loads return 0, their stores are dropped).
+// The row offsets are wave-uniform (scalar) multiples of the row pitch.
+template <int NB>
+struct CBlock {
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t lane_off[NB];
+    uint32_t pitch;
+    __device__ __forceinline__ CBlock(const KParams &p, int R0, int C0) {
+        R0 = __builtin_amdgcn_readfirstlane(R0);
+        C0 = __builtin_amdgcn_readfirstlane(C0);
+        const int lane = threadIdx.x & 63;
+        const int vr = min(32, p.M - R0);
+        const uint32_t bytes =
+            (vr > 0 && C0 < p.N) ? ((uint32_t)(vr - 1) * (uint32_t)p.N + (uint32_t)(p.N - C0)) * 4u : 0u;
+        r = __builtin_amdgcn_make_buffer_rsrc(p.C + (size_t)R0 * p.N + C0, (short)0, (int)bytes, (int)RSRC_DW3);
+        pitch = (uint32_t)p.N * 4u;
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            lane_off[j] = C0 + 32 * j + (lane & 31) < p.N
+                              ? ((uint32_t)(4 * (lane >> 5)) * (uint32_t)p.N + 32 * j + (lane & 31)) * 4u
+                              : OOB;
+    }
+    __device__ __forceinline__ uint32_t off(int e, int j) const {
+        return lane_off[j] + (uint32_t)(8 * (e >> 2) + (e & 3)) * pitch;
+    }
+    __device__ __forceinline__ float load(int e, int j) const {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off(e, j), 0, 0));
+    }
+    __device__ __forceinline__ void store(int e, int j, float v) const {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off(e, j), 0, 0);
+    }
+};
+
+// The bias values of a lane's NB 32-column blocks from column C0 (0 outside N
+// or without a bias).
+template <int NB>
+__device__ __forceinline__ void lane_bias(const KParams &p, int C0, float (&bj)[NB]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int col = C0 + 32 * j + (lane & 31);
+        bj[j] = (p.bias && col < p.N) ? p.bias[col] : 0.0f;
+    }
+}
+
+// store_tile with the epilogue: the prior C values of the held rows are loaded
+// before the first store.
+template <int NW, bool EPI = true>
+__device__ __forceinline__ void store_final(const KParams &p, int m0, int n0, const Tile<NW> &t) {
+    if (!EPI || p.epi == EPI_PLAIN) {
+        store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
+        return;
+    }
+    const Role<NW> w;
+    const bool rc = reads_c(p);
+    const int C0 = n0 + w.wn * 64;
+    float bj[2];
+    lane_bias<2>(p, C0, bj);
+#pragma unroll
+    for (int r = 0; r < Tile<NW>::R; ++r) {
+        const CBlock<2> cb(p, m0 + w.wm * 64 + t.i[r] * 32, C0);
+        float v[32], cin[32], bv[32];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                v[j * 16 + e] = t.v[r][j][e];
+                bv[j * 16 + e] = bj[j];
+                cin[j * 16 + e] = 0.0f;
+            }
+        if (rc) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) cin[j * 16 + e] = cb.load(e, j);
+        }
+        finish<32>(p, v, cin, bv);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) cb.store(e, j, v[j * 16 + e]);
+    }
+}
+
+// Split parts of atomic merges: C += acc (EPI_ACCUM: C += alpha acc).
+template <int NW, bool EPI = true>
+__device__ __forceinline__ void atomic_add_c(const KParams &p, int m0, int n0, const Tile<NW> &t) {
+    if (EPI && p.epi == EPI_ACCUM) {
+        const float a = p.alpha;
+        for_each_element<NW>(t, m0, n0, p.M, p.N, [&](float v, size_t off) { unsafeAtomicAdd(p.C + off, a * v); });
+    } else {
+        for_each_element<NW>(t, m0, n0, p.M, p.N, [&](float v, size_t off) { unsafeAtomicAdd(p.C + off, v); });
+    }
+}
+
+// Store the thread's quads res[g] (quad g = threadIdx.x + NT g of the tile, N a
+// multiple of 4) with the epilogue; loads of prior C and bias quads come first.
+template <int NW, int QPT>
+__device__ __forceinline__ void store_quads_final(const KParams &p, int m0, int n0, const f32x4 (&res)[QPT]) {
+    constexpr int NT = Role<NW>::NT;
+    if (p.epi == EPI_PLAIN) {
+#pragma unroll
+        for (int g = 0; g < QPT; ++g) {
+            const int fq = threadIdx.x + NT * g, r = fq >> 5, c = (fq & 31) * 4;
+            if (m0 + r < p.M && n0 + c < p.N)
+                *reinterpret_cast<f32x4 *>(p.C + (size_t)(m0 + r) * p.N + n0 + c) = res[g];
+        }
+        return;
+    }
+    const bool rc = reads_c(p);
+    float v[4 * QPT], cin[4 * QPT], bv[4 * QPT];
+#pragma unroll
+    for (int g = 0; g < QPT; ++g) {
+        const int fq = threadIdx.x + NT * g, r = fq >> 5, c = (fq & 31) * 4;
+        const bool in = m0 + r < p.M && n0 + c < p.N;
+        f32x4 cq = {0.f, 0.f, 0.f, 0.f}, bq = {0.f, 0.f, 0.f, 0.f};
+        if (in && rc) cq = *reinterpret_cast<const f32x4 *>(p.C + (size_t)(m0 + r) * p.N + n0 + c);
+        if (in && p.bias) bq = *reinterpret_cast<const f32x4 *>(p.bias + n0 + c);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            v[4 * g + x] = res[g][x];
+            cin[4 * g + x] = cq[x];
+            bv[4 * g + x] = bq[x];
+        }
+    }
+    finish<4 * QPT>(p, v, cin, bv);
+#pragma unroll
+    for (int g = 0; g < QPT; ++g) {
+        const int fq = threadIdx.x + NT * g, r = fq >> 5, c = (fq & 31) * 4;
+        if (m0 + r < p.M && n0 + c < p.N)
+            *reinterpret_cast<f32x4 *>(p.C + (size_t)(m0 + r) * p.N + n0 + c) =
+                f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -783,7 +1004,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_dp(KParams p) {
     mac_loop<DT, BL, NS, NW>(p, lds, m0, n0, 0, p.ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
     const Tile<NW> t = merge_k_halves<NW>(acc, lds);
     clk.mark(p, 0);
-    store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
+    store_final<NW>(p, m0, n0, t);
     trace_segment(p, p.worker_base + w, 0, tile, 0, p.ipt, 0);
     trace_folded(p, tile, 0, p.worker_base + w);
     clk.done(p);
@@ -1077,17 +1298,59 @@ __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
     clk.mark(p, 0);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
+    if (p.epi == EPI_PLAIN) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < JB; ++j) {
-            const int col = n0 + wn * JB * 32 + j * 32 + (lane & 31);
+            for (int j = 0; j < JB; ++j) {
+                const int col = n0 + wn * JB * 32 + j * 32 + (lane & 31);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (row < p.M && col < p.N) p.C[(size_t)row * p.N + col] = acc.v[i][j][e];
+                for (int e = 0; e < 16; ++e) {
+                    const int row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    if (row < p.M && col < p.N) p.C[(size_t)row * p.N + col] = acc.v[i][j][e];
+                }
+            }
+    } else {
+        // epilogue, one 32-row block at a time; the prior C values of block
+        // i + 1 are loaded before block i is stored, so no wait for loaded
+        // values ever waits for stores as well (one counter covers both)
+        const bool rc = reads_c(p);
+        const int C0 = n0 + wn * JB * 32;
+        float bj[JB];
+        lane_bias<JB>(p, C0, bj);
+        auto block = [&](int i) { return CBlock<JB>(p, m0 + wm * 128 + i * 32, C0); };
+        float cbuf[2][JB * 16];
+        auto load_block = [&](int i, float (&cin)[JB * 16]) {
+            const CBlock<JB> cb = block(i);
+#pragma unroll
+            for (int j = 0; j < JB; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) cin[j * 16 + e] = rc ? cb.load(e, j) : 0.0f;
+        };
+        load_block(0, cbuf[0]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i + 1 < 4) load_block(i + 1, cbuf[(i + 1) & 1]);
+            const CBlock<JB> cb = block(i);
+            // 16 values at a time, fenced from the scheduler, so the epilogue
+            // arithmetic of many values is not interleaved into more live
+            // registers than the accumulators leave free
+#pragma unroll
+            for (int j = 0; j < JB; ++j) {
+                float v[16], cin[16], bv[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    bv[e] = bj[j];
+                    v[e] = acc.v[i][j][e];
+                    cin[e] = cbuf[i & 1][j * 16 + e];
+                }
+                finish<16>(p, v, cin, bv);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) cb.store(e, j, v[e]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+    }
     if (p.trace && threadIdx.x == 0) {
         // the four tiles of the group, each a whole-K data-parallel tile
         for (int q = 0; q < 4; ++q) {
@@ -1125,13 +1388,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
     clk.mark(p, 0);
     trace_segment(p, w, 0, tile, k0, k1, S == 1 ? 0 : (s == 0 ? 1 : 2));
     if (S == 1) {
-        store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
+        store_final<NW>(p, m0, n0, t);
         trace_folded(p, tile, 0, w);
         clk.done(p);
         return;
     }
     if (p.merge == MERGE_ATOMIC) {   // "parallel" Split-K: add into the zero-filled C
-        atomic_add_c<NW>(p.C, m0, n0, p.M, p.N, t);
+        atomic_add_c<NW>(p, m0, n0, t);
         clk.done(p);
         return;
     }
@@ -1204,10 +1467,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
                     const float v = t == s ? own[x] : get_coherent(p.part + (size_t)t * mn + off);
                     sum = t == 0 ? v : sum + v;
                 }
-                p.C[off] = sum;
+                p.C[off] = final_scalar(p, sum, off, n0 + c + x);
             }
         }
-    } else if (S <= 4) {
+    } else {
+      f32x4 res[QPT];
+      if (S <= 4) {
         f32x4 buf[3][QPT];   // buf[j]: the j-th partial other than this split's
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
@@ -1231,9 +1496,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
             if (S > 1) sum += s == 1 ? own : (s > 1 ? buf[1][g] : buf[0][g]);
             if (S > 2) sum += s == 2 ? own : (s > 2 ? buf[2][g] : buf[1][g]);
             if (S > 3) sum += s == 3 ? own : buf[2][g];
-            if (in_c(r, c)) *reinterpret_cast<f32x4 *>(p.C + (size_t)(m0 + r) * p.N + n0 + c) = sum;
+            res[g] = sum;
         }
-    } else {
+      } else {
+#pragma unroll
         for (int q0 = 0; q0 < QPT; q0 += 4) {
             f32x4 sum[4];
             for (int t0 = 0; t0 < S; t0 += 4) {
@@ -1263,12 +1529,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
                 }
             }
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                int r, c;
-                quad_rc(q0 + g, r, c);
-                if (in_c(r, c)) *reinterpret_cast<f32x4 *>(p.C + (size_t)(m0 + r) * p.N + n0 + c) = sum[g];
-            }
+            for (int g = 0; g < 4; ++g) res[q0 + g] = sum[g];
         }
+      }
+      store_quads_final<NW, QPT>(p, m0, n0, res);
     }
     for (int t = 0; t < S; ++t) trace_folded(p, tile, t, tile * S + t);
     clk.mark(p, 2);
@@ -1286,6 +1550,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
 constexpr int RED_THREADS = 256;
 constexpr int RED_BLOCKS_PER_TILE = BM * BN / 4 / RED_THREADS;   // 16
 
+template <bool EPI>
 __global__ __launch_bounds__(RED_THREADS) void splitk_reduce(KParams p) {
     const int tile = blockIdx.x / RED_BLOCKS_PER_TILE;
     const int q = (blockIdx.x % RED_BLOCKS_PER_TILE) * RED_THREADS + threadIdx.x;   // quad within the tile
@@ -1309,6 +1574,15 @@ __global__ __launch_bounds__(RED_THREADS) void splitk_reduce(KParams p) {
             for (int j = 0; j < 8; ++j)
                 if (t0 + j < S) sum = t0 + j == 0 ? x[j] : sum + x[j];
         }
+        if (EPI) {
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 cq = reads_c(p) ? *reinterpret_cast<const f32x4 *>(p.C + off) : zero;
+            const f32x4 bq = p.bias ? *reinterpret_cast<const f32x4 *>(p.bias + n0 + c) : zero;
+            float v[4] = {sum[0], sum[1], sum[2], sum[3]};
+            const float cin[4] = {cq[0], cq[1], cq[2], cq[3]}, bv[4] = {bq[0], bq[1], bq[2], bq[3]};
+            finish<4>(p, v, cin, bv);
+            sum = f32x4{v[0], v[1], v[2], v[3]};
+        }
         *reinterpret_cast<f32x4 *>(p.C + off) = sum;
     } else {
         for (int e = 0; e < 4 && n0 + c + e < p.N; ++e) {
@@ -1317,7 +1591,7 @@ __global__ __launch_bounds__(RED_THREADS) void splitk_reduce(KParams p) {
                 const float v = p.part[(size_t)t * mn + off + e];
                 sum = t == 0 ? v : sum + v;
             }
-            p.C[off + e] = sum;
+            p.C[off + e] = EPI ? final_scalar(p, sum, off + e, n0 + c + e) : sum;
         }
     }
 }
@@ -1333,6 +1607,7 @@ __global__ __launch_bounds__(RED_THREADS) void splitk_reduce(KParams p) {
 // thread per such element, 16 workgroups of 256 threads per Stream-K tile;
 // tiles that one unit computed whole were stored by it and are skipped.
 // ---------------------------------------------------------------------------
+template <bool EPI>
 __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
     const int ts = blockIdx.x / RED_BLOCKS_PER_TILE;
     const int f = (blockIdx.x % RED_BLOCKS_PER_TILE) * RED_THREADS + threadIdx.x;
@@ -1364,6 +1639,20 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
     const int row = m0 + (quad >> 1) * 64 + (b >> 1) * 32 + 8 * e4 + 4 * (lane >> 5);
     const int col = n0 + (quad & 1) * 64 + (b & 1) * 32 + (lane & 31);
     if (col >= p.N) return;
+    if (EPI) {
+        const bool rc = reads_c(p);
+        const float b = p.bias ? p.bias[col] : 0.0f;
+        float v[4], cin[4];
+        const float bv[4] = {b, b, b, b};
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            cin[y] = (rc && row + y < p.M) ? p.C[(size_t)(row + y) * p.N + col] : 0.0f;
+            v[y] = sum[y];
+        }
+        finish<4>(p, v, cin, bv);
+#pragma unroll
+        for (int y = 0; y < 4; ++y) sum[y] = v[y];
+    }
 #pragma unroll
     for (int y = 0; y < 4; ++y)
         if (row + y < p.M) p.C[(size_t)(row + y) * p.N + col] = sum[y];
@@ -1389,7 +1678,7 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
 // units stream the same few K-slabs at any moment and the A and B panels
 // shared by neighbouring tiles are reused from the XCD's L2.
 // ---------------------------------------------------------------------------
-template <int DT, int BL, int NS, int NW, bool ATOMIC>
+template <int DT, int BL, int NS, int NW, bool ATOMIC, bool EPI>
 __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
     __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_BYTES];
     const WgClock clk(p);
@@ -1419,10 +1708,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         clk.mark(p, 2 * min(nseg, 1));
         trace_segment(p, u, nseg++, tile, k0, k1, role);
         if (role == 0) {
-            store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
+            if constexpr (!EPI) store_final<NW, false>(p, m0, n0, t);
             trace_folded(p, tile, 0, u);
         } else if constexpr (ATOMIC) {
-            atomic_add_c<NW>(p.C, m0, n0, p.M, p.N, t);
+            atomic_add_c<NW, EPI>(p, m0, n0, t);
         } else if (p.merge == MERGE_TWO_PASS) {
             // streamk_reduce adds the tile's partials: contributors publish into
             // the first slot bank, owners into the second
@@ -1454,12 +1743,42 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
                 add_slot<NW>(p.part + (size_t)v * (BM * BN), t);
                 trace_folded(p, tile, pos_fold++, v);
             }
-            store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
+            if constexpr (!EPI) store_final<NW, false>(p, m0, n0, t);
+        }
+        // the epilogue build stores whole tiles and folded tiles from one call
+        // site (one inlined copy of the epilogue code)
+        if constexpr (EPI) {
+            if (role == 0 || (role == 1 && !ATOMIC && p.merge != MERGE_TWO_PASS)) store_final<NW, true>(p, m0, n0, t);
         }
         clk.mark(p, 2 * min(nseg - 1, 1) + 1);
         pos = tb + k1;
     }
     clk.done(p);
+}
+
+// ---------------------------------------------------------------------------
+// Elementwise epilogue pass over C (atomic merges and the empty sum):
+// EPASS_PRE  C = beta C + bias (C not read when beta == 0),
+// EPASS_POST C = act(C),
+// EPASS_ONLY C = act(beta C + bias), i.e. the epilogue of a zero product.
+// Rows are spread over blockIdx.y, columns over the x grid.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void epilogue_pass(KParams p, int stage) {
+#pragma clang fp contract(off)
+    const bool rc = p.beta != 0.0f;
+    for (int row = blockIdx.y; row < p.M; row += gridDim.y)
+        for (int col = blockIdx.x * blockDim.x + threadIdx.x; col < p.N; col += gridDim.x * blockDim.x) {
+            float *c = p.C + (size_t)row * p.N + col;
+            const float b = p.bias ? p.bias[col] : 0.0f;
+            if (stage == EPASS_POST) {
+                *c = act_apply(p.act, *c);
+            } else if (stage == EPASS_ONLY) {
+                *c = epi_value(p, 0.0f, rc ? *c : 0.0f, b);
+            } else {
+                const float t = rc ? p.beta * *c : 0.0f;
+                *c = p.bias ? t + b : t;
+            }
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -1495,20 +1814,26 @@ struct Shape {
 };
 
 template <int DT, int BL>
-KernelFn pick(int kmode, Shape &shape) {
+KernelFn pick(int kmode, bool epi, Shape &shape) {
+    // Stream-K has a separate build with the epilogue: its plain build keeps
+    // the register allocation of a kernel without one
     switch (kmode) {
     case K_DP: shape = {4, 8}; return gemm_dp<DT, BL, 4, 8>;
     case K_SPLITK: shape = {4, 8}; return gemm_splitk<DT, BL, 4, 8>;
-    case K_SK: shape = {4, 8}; return gemm_streamk<DT, BL, 4, 8, false>;
-    case K_SK_ATOMIC: shape = {4, 8}; return gemm_streamk<DT, BL, 4, 8, true>;
+    case K_SK:
+        shape = {4, 8};
+        return epi ? gemm_streamk<DT, BL, 4, 8, false, true> : gemm_streamk<DT, BL, 4, 8, false, false>;
+    case K_SK_ATOMIC:
+        shape = {4, 8};
+        return epi ? gemm_streamk<DT, BL, 4, 8, true, true> : gemm_streamk<DT, BL, 4, 8, true, false>;
     case K_DP_GROUP: shape = {G_NS, G_NW}; return gemm_dp_group<DT, BL>;
     default: return nullptr;
     }
 }
 
-KernelFn kernel_for(int dtype, int blayout, int kmode, Shape &shape) {
-    if (dtype == 0) return blayout == 0 ? pick<0, 0>(kmode, shape) : pick<0, 1>(kmode, shape);
-    if (dtype == 1) return blayout == 0 ? pick<1, 0>(kmode, shape) : pick<1, 1>(kmode, shape);
+KernelFn kernel_for(int dtype, int blayout, int kmode, bool epi, Shape &shape) {
+    if (dtype == 0) return blayout == 0 ? pick<0, 0>(kmode, epi, shape) : pick<0, 1>(kmode, epi, shape);
+    if (dtype == 1) return blayout == 0 ? pick<1, 0>(kmode, epi, shape) : pick<1, 1>(kmode, epi, shape);
     return nullptr;
 }
 
@@ -1517,7 +1842,7 @@ KernelFn kernel_for(int dtype, int blayout, int kmode, Shape &shape) {
 hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParams &p,
                        hipStream_t stream) {
     Shape shape{0, 0};
-    KernelFn fn = kernel_for(dtype, blayout, kmode, shape);
+    KernelFn fn = kernel_for(dtype, blayout, kmode, p.epi != EPI_PLAIN, shape);
     if (!fn || grid <= 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * shape.nw), 0, stream, p);
     return hipGetLastError();
@@ -1526,14 +1851,31 @@ hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParam
 hipError_t launch_splitk_reduce(const KParams &p, hipStream_t stream) {
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
     if (tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)(tiles * RED_BLOCKS_PER_TILE)), dim3(RED_THREADS), 0, stream, p);
+    // a separate build with the epilogue keeps the plain one's code unchanged
+    if (p.epi != EPI_PLAIN)
+        hipLaunchKernelGGL(splitk_reduce<true>, dim3((unsigned)(tiles * RED_BLOCKS_PER_TILE)), dim3(RED_THREADS), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL(splitk_reduce<false>, dim3((unsigned)(tiles * RED_BLOCKS_PER_TILE)), dim3(RED_THREADS), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
 hipError_t launch_streamk_reduce(const KParams &p, int64_t sk_tiles, hipStream_t stream) {
     if (sk_tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(streamk_reduce, dim3((unsigned)(sk_tiles * RED_BLOCKS_PER_TILE)), dim3(RED_THREADS), 0,
-                       stream, p);
+    if (p.epi != EPI_PLAIN)
+        hipLaunchKernelGGL(streamk_reduce<true>, dim3((unsigned)(sk_tiles * RED_BLOCKS_PER_TILE)), dim3(RED_THREADS),
+                           0, stream, p);
+    else
+        hipLaunchKernelGGL(streamk_reduce<false>, dim3((unsigned)(sk_tiles * RED_BLOCKS_PER_TILE)), dim3(RED_THREADS),
+                           0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_epilogue_pass(const KParams &p, int stage, hipStream_t stream) {
+    const int gx = (int)std::min<int64_t>((p.N + 255) / 256, 16);
+    const int gy = (int)std::min<int64_t>(p.M, 4096);
+    hipLaunchKernelGGL(epilogue_pass, dim3(gx, gy), dim3(256), 0, stream, p, stage);
     return hipGetLastError();
 }
 
@@ -1548,11 +1890,20 @@ hipError_t launch_zero(void *ptr, int64_t n_words, hipStream_t stream) {
 }
 
 hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int *out) {
-    Shape shape{0, 0};
-    KernelFn fn = kernel_for(dtype, blayout, kmode, shape);
-    if (!fn) return hipErrorInvalidValue;
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, reinterpret_cast<const void *>(fn),
-                                                        64 * shape.nw, 0);
+    // the smaller of the builds with and without the epilogue
+    int best = 1 << 30;
+    for (int epi = 0; epi < 2; ++epi) {
+        Shape shape{0, 0};
+        KernelFn fn = kernel_for(dtype, blayout, kmode, epi != 0, shape);
+        if (!fn) return hipErrorInvalidValue;
+        int n = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(fn),
+                                                                    64 * shape.nw, 0);
+        if (e != hipSuccess) return e;
+        best = std::min(best, n);
+    }
+    *out = best;
+    return hipSuccess;
 }
 
 }  // namespace dgw

@@ -21,6 +21,23 @@ enum KernelMode : int {
 // into a zero-filled C.
 enum : int { MERGE_IN_LAUNCH = 0, MERGE_TWO_PASS = 1, MERGE_ATOMIC = 2 };
 
+// How final values reach C (the fused epilogue of the CUTLASS optimisation
+// guide, "Epilogue Optimization": D = act(alpha acc + beta C + bias)).
+enum : int {
+    EPI_PLAIN = 0,   // C = acc
+    EPI_FULL = 1,    // C = act(alpha acc + beta C_in + bias[col]), C_in read only when beta != 0
+    EPI_ACCUM = 2,   // atomic merges: C already holds beta C_in + bias; whole tiles store
+                     // fma(alpha, acc, C), split parts add alpha acc atomically (activation: a later pass)
+};
+enum : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
+
+// Stages of the elementwise epilogue pass over C.
+enum : int {
+    EPASS_PRE = 0,    // C = beta C + bias (before atomic merges)
+    EPASS_POST = 1,   // C = act(C) (after atomic merges)
+    EPASS_ONLY = 2,   // C = act(beta C + bias) (K == 0: the product is zero)
+};
+
 // Error bits of the device status word.
 enum : uint32_t { STATUS_TIMEOUT = 1u };
 
@@ -46,6 +63,9 @@ struct KParams {
     uint32_t epoch;        // value a publishing unit writes into its flag
     uint32_t spin_limit;   // polls before a wait gives up
     uint32_t debug;        // GEMM_DEBUG_* bits
+    int epi, act;          // EPI_* and ACT_*: the fused epilogue of the final stores
+    float alpha, beta;     // epilogue scalars (EPI_FULL; EPI_ACCUM uses alpha)
+    const float *bias;     // optional fp32 [N] added per column (EPI_FULL)
     const int *perm;       // optional workgroup -> worker map
     int *trace;            // optional debug trace (see gemm.h)
     long long *timing;     // optional per-workgroup {start, end, HW_ID | XCC_ID << 32, cycles, marks}
@@ -66,6 +86,10 @@ hipError_t launch_splitk_reduce(const KParams &p, hipStream_t stream);
 // part (sk_tiles tiles from p.tile_base) gets its owner's and peers' partials
 // added in k order.
 hipError_t launch_streamk_reduce(const KParams &p, int64_t sk_tiles, hipStream_t stream);
+
+// Elementwise epilogue pass over C[M,N] (stage EPASS_*; p.C, p.M, p.N, p.beta,
+// p.bias, p.act).
+hipError_t launch_epilogue_pass(const KParams &p, int stage, hipStream_t stream);
 
 // Fill n 32-bit words with zero (used instead of hipMemsetAsync so the call can
 // be captured in a HIP graph).

@@ -7,7 +7,8 @@
  *     C[M,N] = A[M,K] . B^T        (B stored [N,K], row-major)        layout GEMM_B_NK
  *
  * A and B hold bf16 or fp16 values; products are accumulated in fp32 and C is
- * written in fp32 (overwrite: no alpha/beta).  The work decomposition is the
+ * written in fp32: overwritten with the product, or (gemm_ex with an epilogue
+ * word) C = act(alpha A.B + beta C + bias), see GEMM_EPI_* below.  The work decomposition is the
  * subject of the Split-K/Stream-K book chapter ("Split-K and Stream-K: The Last
  * Wave of a GEMM", kanthi.in): output tiles of 128x128 elements, one
  * "MAC-loop iteration" per 64-wide step of K (glossary table), and three ways
@@ -107,6 +108,33 @@ extern "C" {
 #define GEMM_DEBUG_TILE_DP 0x8u /* data-parallel launches run one 128x128 tile per
                                    workgroup even where 2x2 tile groups apply.     */
 
+/* ---- epilogue word for gemm_args_t.epilogue ------------------------------------------ */
+/*
+ * Fused epilogue (CUTLASS optimisation guide, "Epilogue Optimization": the
+ * epilogue forms alpha.AB + beta.C; "Fused Epilogue Operations": bias addition
+ * and a ReLU or GELU activation in the same pass).  With a non-zero word the
+ * call writes, for every element,
+ *
+ *     C[i][j] = act(alpha * (A.B)[i][j] + beta * C_in[i][j] + bias[j])
+ *
+ * where C_in is C's content before the call (read only when beta != 0, so a
+ * NaN there is ignored with beta == 0) and bias is one fp32 value per column.
+ * Arithmetic (fp32, each step rounded, no contraction): t = beta * C_in
+ * (0 when beta == 0), y = fma(alpha, acc, t), y = y + bias[j], then ReLU
+ * max(y, 0) or GELU (y / 2) * (1 + erf(y / sqrt 2)), erf from the rational
+ * approximation of Abramowitz and Stegun 7.1.26 (absolute error below
+ * 1.5e-7; relative error of GELU below 4e-7 of |y|).  Deterministic merges
+ * keep their guarantee: the same call gives the same bits on every run, and a
+ * two-pass merge the same bits as the in-launch one.  With GEMM_ATOMIC, C is
+ * first set to beta * C_in + bias, tiles and split segments add alpha * acc,
+ * and an activation runs as a final elementwise pass (tolerance only).  With
+ * K == 0 the product is zero: C = act(beta * C_in + bias).
+ */
+#define GEMM_EPI_ALPHA_BETA 0x01u  /* use alpha and beta (else alpha = 1, beta = 0)      */
+#define GEMM_EPI_BIAS       0x02u  /* add bias[j]: device fp32 [N], 16-byte aligned     */
+#define GEMM_EPI_RELU       0x10u  /* act = max(y, 0)                                   */
+#define GEMM_EPI_GELU       0x20u  /* act = y Phi(y), Phi the standard normal CDF       */
+
 /* Tile shape used by every decomposition. */
 #define GEMM_BM 128
 #define GEMM_BN 128
@@ -172,6 +200,10 @@ typedef struct gemm_plan_t {
  *             partial stored, m2 = fold done (last arriver); Stream-K m0/m1 =
  *             first segment's mainloop / fixup-and-store done, m2/m3 = the same
  *             for the unit's last segment.  Unset marks stay as the caller left them.
+ *   epilogue: GEMM_EPI_* bits (0: C is overwritten with A.B).  RELU and GELU
+ *             exclude each other; GEMM_EPI_BIAS is set exactly when bias != NULL.
+ *   alpha, beta: epilogue scalars, used with GEMM_EPI_ALPHA_BETA.
+ *   bias:     device fp32 [N] (16-byte aligned, not overlapping C), or NULL.
  * Tuning overrides read once from the environment (defaults in brackets):
  *   DGW_GROUP_M    tile rows per raster group [8]; tile ids run column by column
  *                  within a group of rows (0 = plain row-major)
@@ -195,6 +227,10 @@ typedef struct gemm_args_t {
     uint32_t spin_limit;
     uint32_t debug;
     int64_t *timing;
+    uint32_t epilogue;
+    float alpha;
+    float beta;
+    const float *bias;
 } gemm_args_t;
 
 /*
@@ -268,7 +304,7 @@ const char *gemm_last_error(void);
 /* gemm_num_cus -- compute units of the current device (0 if there is none). */
 int32_t gemm_num_cus(void);
 
-/* gemm_version -- ABI version of this header (1). */
+/* gemm_version -- ABI version of this header (2: gemm_args_t gained the epilogue fields). */
 int32_t gemm_version(void);
 
 #ifdef __cplusplus

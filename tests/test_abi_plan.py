@@ -54,21 +54,22 @@ def test_library_exports_every_declared_symbol(dg):
 def test_header_compiles_as_c(tmp_path):
     src = tmp_path / "t.c"
     src.write_text('#include "gemm.h"\nint main(void){gemm_plan_t p; gemm_args_t a; (void)p; (void)a;'
-                   ' return gemm_version() == 1 ? 0 : 1;}\n')
+                   ' return gemm_version() == 2 ? 0 : 1;}\n')
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-c", f"-I{HEADER.parent}", str(src),
                         "-o", str(tmp_path / "t.o")], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
 
 
 def test_version(dg):
-    assert dg.gemm_version() == 1
+    assert dg.gemm_version() == 2
 
 
 def test_struct_sizes_match_c(dg, tmp_path):
     src = tmp_path / "s.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "gemm.h"\n'
-                   'int main(void){printf("%zu %zu %zu %zu\\n", sizeof(gemm_plan_t), sizeof(gemm_args_t),'
-                   ' offsetof(gemm_args_t, stream), offsetof(gemm_plan_t, trace_ints)); return 0;}\n')
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(gemm_plan_t), sizeof(gemm_args_t),'
+                   ' offsetof(gemm_args_t, stream), offsetof(gemm_plan_t, trace_ints),'
+                   ' offsetof(gemm_args_t, epilogue), offsetof(gemm_args_t, bias)); return 0;}\n')
     exe = tmp_path / "s"
     subprocess.run(["gcc", f"-I{HEADER.parent}", str(src), "-o", str(exe)], check=True)
     got = subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()
@@ -76,6 +77,8 @@ def test_struct_sizes_match_c(dg, tmp_path):
     assert int(got[1]) == ctypes.sizeof(dg.GemmArgs)
     assert int(got[2]) == dg.GemmArgs.stream.offset
     assert int(got[3]) == dg.GemmPlan.trace_ints.offset
+    assert int(got[4]) == dg.GemmArgs.epilogue.offset
+    assert int(got[5]) == dg.GemmArgs.bias.offset
 
 
 # -- planner vs simulator -------------------------------------------------------------
@@ -203,6 +206,39 @@ def test_gemm_rejects_before_launch(dg):
     # empty problems are a no-op, even with null pointers
     assert dg.gemm(0, 0, 0, 0, 256, 256, 0, dg.GEMM_DP, 0) == dg.GEMM_OK
     assert dg.gemm(0, 0, 0, 256, 0, 256, 0, dg.GEMM_DP, 0) == dg.GEMM_OK
+
+
+def _epi_args(dg, epilogue, bias=0, M=256, N=256, K=256, C=1 << 30):
+    a = dg.GemmArgs()
+    a.A, a.B, a.C = 1 << 20, 1 << 24, C
+    a.M, a.N, a.K = M, N, K
+    a.mode = dg.GEMM_DP
+    a.epilogue = epilogue
+    a.bias = bias or None
+    return a
+
+
+def test_epilogue_rejects_before_launch(dg):
+    # host-detectable epilogue errors return before any HIP call (no GPU needed)
+    bad = [
+        (0x4, 0, "unknown bits"),
+        (0x100, 0, "unknown bits"),
+        (dg.GEMM_EPI_RELU | dg.GEMM_EPI_GELU, 0, "exclude"),
+        (dg.GEMM_EPI_BIAS, 0, "exactly when"),
+        (dg.GEMM_EPI_ALPHA_BETA, 1 << 28, "exactly when"),
+    ]
+    for word, bias, text in bad:
+        assert dg.gemm_ex(_epi_args(dg, word, bias)) == dg.GEMM_ERR_INVALID, (word, bias)
+        assert text in dg.gemm_last_error()
+        # checked before the early return of an empty problem
+        assert dg.gemm_ex(_epi_args(dg, word, bias, M=0)) == dg.GEMM_ERR_INVALID
+    # bias alignment and overlap with C
+    assert dg.gemm_ex(_epi_args(dg, dg.GEMM_EPI_BIAS, (1 << 28) + 4)) == dg.GEMM_ERR_UNSUPPORTED
+    assert "16-byte" in dg.gemm_last_error()
+    assert dg.gemm_ex(_epi_args(dg, dg.GEMM_EPI_BIAS, (1 << 30) + 1024)) == dg.GEMM_ERR_INVALID
+    assert "overlap" in dg.gemm_last_error()
+    # a valid epilogue on an empty problem is a no-op
+    assert dg.gemm_ex(_epi_args(dg, dg.GEMM_EPI_BIAS | dg.GEMM_EPI_GELU, 1 << 28, N=0)) == dg.GEMM_OK
 
 
 def test_splitk_merge_modes_plan(dg):

@@ -146,3 +146,12 @@ def operand_bits(t: torch.Tensor) -> np.ndarray:
     if t.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError("expected a bf16 or fp16 tensor")
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def make_epilogue_inputs(M: int, N: int, seed: int = 1):
+    """Seeded fp32 inputs of the fused epilogue: the prior output ``C_in`` [M,N]
+    and a per-column ``bias`` [N], both uniform on [-1, 1) (CPU torch tensors)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c_in = torch.from_numpy(rng.uniform(-1.0, 1.0, size=(M, N)).astype(np.float32))
+    bias = torch.from_numpy(rng.uniform(-1.0, 1.0, size=(N,)).astype(np.float32))
+    return c_in.contiguous(), bias.contiguous()
