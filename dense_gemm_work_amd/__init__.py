@@ -1,11 +1,11 @@
 """Python binding of the MI355X DP / Split-K / Stream-K GEMM library.
 
 Argument marshalling only: every step of the computation runs in the HIP
-kernels of ``libdgw_gemm.so`` (built in-tree by ``dense_gemm_work_amd.build``).
+kernels of ``libdgw_gemm.so`` (built in-tree by ``dense_gemm_work_amd/build.py``).
 The functions carry the names of the C entry points in ``include/gemm.h``:
 
 * ``gemm(A, B, C, M, N, K, layout, mode, splits)`` -- raw device pointers.
-* ``gemm_ex(args)``, ``gemm_plan(...)``, ``gemm_unit_range(...)``,
+* ``gemm_ex(args)``, ``gemm_plan(...)``, ``gemm_workspace_size(...)``, ``gemm_unit_range(...)``,
   ``gemm_set_stream``, ``gemm_sync_status``, ``gemm_release``,
   ``gemm_last_error``, ``gemm_num_cus``, ``gemm_version``.
 
@@ -22,7 +22,7 @@ from pathlib import Path
 from typing import Optional
 
 __all__ = [
-    "GemmError", "GemmPlan", "GemmArgs", "gemm", "gemm_ex", "gemm_plan", "gemm_unit_range",
+    "GemmError", "GemmPlan", "GemmArgs", "gemm", "gemm_ex", "gemm_plan", "gemm_workspace_size", "gemm_unit_range",
     "gemm_set_stream", "gemm_sync_status", "gemm_release", "gemm_last_error", "gemm_num_cus",
     "gemm_version", "gemm_tensors", "plan_dict", "library_path",
 ]
@@ -112,8 +112,8 @@ def library_path() -> Path:
 def _load() -> ctypes.CDLL:
     if not _LIB_PATH.exists():
         raise ImportError(
-            f"{_LIB_PATH} is not built; run __graft_entry__.build() (or python -m "
-            "dense_gemm_work_amd.build) first -- there is no fallback implementation")
+            f"{_LIB_PATH} is not built; run __graft_entry__.build() (or python3 "
+            "dense_gemm_work_amd/build.py) first -- there is no fallback implementation")
     lib = ctypes.CDLL(str(_LIB_PATH))
     i64, u32, i32, vp = ctypes.c_int64, ctypes.c_uint32, ctypes.c_int32, ctypes.c_void_p
     lib.gemm.restype = ctypes.c_int
@@ -122,6 +122,8 @@ def _load() -> ctypes.CDLL:
     lib.gemm_ex.argtypes = [ctypes.POINTER(GemmArgs)]
     lib.gemm_plan.restype = ctypes.c_int
     lib.gemm_plan.argtypes = [i64, i64, i64, u32, u32, i32, i32, ctypes.POINTER(GemmPlan)]
+    lib.gemm_workspace_size.restype = ctypes.c_int64
+    lib.gemm_workspace_size.argtypes = [i64, i64, i64, u32, u32, i32, i32]
     lib.gemm_unit_range.restype = ctypes.c_int
     lib.gemm_unit_range.argtypes = [ctypes.POINTER(GemmPlan), i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.gemm_set_stream.restype = ctypes.c_int
@@ -162,6 +164,10 @@ def gemm_plan(M: int, N: int, K: int, layout: int, mode: int, splits: int, num_c
     p = GemmPlan()
     _check(_lib.gemm_plan(M, N, K, layout, mode, splits, num_cus, ctypes.byref(p)))
     return p
+
+
+def gemm_workspace_size(M: int, N: int, K: int, layout: int, mode: int, splits: int, num_cus: int) -> int:
+    return _check(int(_lib.gemm_workspace_size(M, N, K, layout, mode, splits, num_cus)))
 
 
 def gemm_unit_range(plan: GemmPlan, unit: int):

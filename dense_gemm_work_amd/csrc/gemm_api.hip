@@ -434,6 +434,16 @@ int gemm_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
     return GEMM_OK;
 }
 
+int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, int32_t splits,
+                            int32_t num_cus) {
+    gemm_plan_t p;
+    const char *why = "";
+    int rc = dgw::make_plan(M, N, K, layout, mode, splits, num_cus, &p, &why);
+    if (rc != GEMM_OK) return fail(rc, why);
+    g_err.clear();
+    return p.workspace_bytes;
+}
+
 int gemm_set_stream(void *stream) {
     g_stream = reinterpret_cast<hipStream_t>(stream);
     return GEMM_OK;

@@ -279,6 +279,16 @@ int gemm_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode,
               int32_t splits, int32_t num_cus, gemm_plan_t *out);
 
 /*
+ * gemm_workspace_size -- device workspace bytes a call with these arguments
+ * needs (plan.workspace_bytes: Stream-K partial slots and flags, Split-K
+ * partials and counters, the status block), for a caller that passes its own
+ * gemm_args_t.workspace.  num_cus >= 1 (no device is queried).  Returns the
+ * byte count (>= 0) or a negative status for arguments gemm_plan rejects.
+ */
+int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode,
+                            int32_t splits, int32_t num_cus);
+
+/*
  * gemm_unit_range -- [begin, end) of Stream-K unit u in the flattened space of
  * the plan's Stream-K tiles (host arithmetic).  Returns a status.
  */

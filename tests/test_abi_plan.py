@@ -2,6 +2,7 @@
 include/gemm.h declares, rejects bad arguments before touching a GPU, and its
 planner agrees with the CPU schedule simulator (oracle/schedule.py)."""
 import ctypes
+import importlib.util
 import itertools
 import re
 import subprocess
@@ -17,8 +18,11 @@ HEADER = ROOT / "include" / "gemm.h"
 
 @pytest.fixture(scope="module")
 def dg():
-    from dense_gemm_work_amd import build as b
-
+    # the build script is loaded from its file: importing the package binds the
+    # library, which may predate a symbol the binding asks for
+    spec = importlib.util.spec_from_file_location("_dgw_hip_build", ROOT / "dense_gemm_work_amd" / "build.py")
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
     if b.is_stale():
         b.build()
     import dense_gemm_work_amd as dg
@@ -35,7 +39,7 @@ def _declared_functions():
 
 def test_header_declares_the_core_entry_points():
     names = _declared_functions()
-    for n in ("gemm", "gemm_ex", "gemm_plan", "gemm_unit_range", "gemm_set_stream",
+    for n in ("gemm", "gemm_ex", "gemm_plan", "gemm_workspace_size", "gemm_unit_range", "gemm_set_stream",
               "gemm_sync_status", "gemm_release", "gemm_last_error", "gemm_num_cus", "gemm_version"):
         assert n in names
 
@@ -239,6 +243,20 @@ def test_epilogue_rejects_before_launch(dg):
     assert "overlap" in dg.gemm_last_error()
     # a valid epilogue on an empty problem is a no-op
     assert dg.gemm_ex(_epi_args(dg, dg.GEMM_EPI_BIAS | dg.GEMM_EPI_GELU, 1 << 28, N=0)) == dg.GEMM_OK
+
+
+def test_workspace_size_matches_plan(dg):
+    for M, N, K, mode, splits in [(2048, 2176, 4096, dg.GEMM_HEURISTIC, 0), (96, 512, 2048, dg.GEMM_SPLITK, 8),
+                                  (256, 512, 2048, dg.GEMM_STREAMK, 32), (8192, 8192, 8192, dg.GEMM_DP, 0),
+                                  (1536, 1536, 16384, dg.GEMM_STREAMK | dg.GEMM_ATOMIC, 0)]:
+        p = dg.gemm_plan(M, N, K, 0, mode, splits, 256)
+        assert dg.gemm_workspace_size(M, N, K, 0, mode, splits, 256) == p.workspace_bytes
+    # Split-K partials [S, M, N] fp32 plus the control block
+    p = dg.gemm_plan(96, 512, 2048, 0, dg.GEMM_SPLITK, 8, 256)
+    assert p.workspace_bytes >= 8 * 96 * 512 * 4
+    with pytest.raises(dg.GemmError) as ei:
+        dg.gemm_workspace_size(96, 512, 2048, 0, dg.GEMM_SPLITK, 3, 256)
+    assert ei.value.status == dg.GEMM_ERR_INVALID
 
 
 def test_splitk_merge_modes_plan(dg):
