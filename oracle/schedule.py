@@ -300,22 +300,29 @@ class Schedule:
     q: int                        # floor(total / units) for Stream-K
     big: int                      # total mod units
     segments: List[Segment]
+    batch: int = 1                # matrices in a batched call (tile grids numbered batch after batch)
 
     @property
     def tiles(self):
-        return self.tiles_m * self.tiles_n
+        return self.batch * self.tiles_m * self.tiles_n
 
 
 def plan_schedule(M: int, N: int, K: int, mode: str, splits: int = 0, sms: int = 256,
-                  bm: int = 128, bn: int = 128, bk: int = 64) -> Schedule:
+                  bm: int = 128, bn: int = 128, bk: int = 64, batch: int = 1) -> Schedule:
     """What a GEMM call does, per mode ("heuristic", "dp", "splitk", "streamk").
 
     For "splitk", ``splits`` is S; for "streamk" it is the unit count (0 = one per SM).
     In a hybrid Stream-K decision the Stream-K part takes the *last* sk_tiles tiles
     and the first dp_tiles tiles run as plain data-parallel tiles.
+
+    A batched call (``batch`` independent products of one shape) is one problem
+    of batch x tiles_m x tiles_n output tiles, numbered batch after batch: the
+    decomposition rule, the Stream-K flattening and every unit range apply to
+    that tile count unchanged (book chapter, Case 1 arithmetic on the total
+    tile count; docc StreamK page, generality: batched GEMM).
     """
     tm, tn = tile_grid(M, N, bm, bn)
-    tiles = tm * tn
+    tiles = batch * tm * tn
     ipt = cdiv(K, bk)
     if mode == "heuristic":
         d = decide(tiles, ipt, sms)
@@ -331,15 +338,15 @@ def plan_schedule(M: int, N: int, K: int, mode: str, splits: int = 0, sms: int =
                     for s in streamk_segments(unit_ranges(total, units), ipt)]
             segs += [Segment(units + t, t, 0, ipt, FULL) for t in range(dp_tiles)]
             return Schedule("StreamK", tm, tn, ipt, 1, units, d.sk_tiles, dp_tiles,
-                            total // units, total % units, segs)
+                            total // units, total % units, segs, batch)
     if mode == "dp":
-        return Schedule("DataParallel", tm, tn, ipt, 1, 0, 0, 0, 0, 0, dp_segments(tiles, ipt))
+        return Schedule("DataParallel", tm, tn, ipt, 1, 0, 0, 0, 0, 0, dp_segments(tiles, ipt), batch)
     if mode == "splitk":
         return Schedule("SplitK", tm, tn, ipt, splits, 0, 0, 0, 0, 0,
-                        splitk_segments(tiles, ipt, splits))
+                        splitk_segments(tiles, ipt, splits), batch)
     if mode == "streamk":
         units = splits if splits > 0 else sms
         total = tiles * ipt
         return Schedule("StreamK", tm, tn, ipt, 1, units, tiles, 0, total // units, total % units,
-                        streamk_segments(unit_ranges(total, units), ipt))
+                        streamk_segments(unit_ranges(total, units), ipt), batch)
     raise ValueError(f"unknown mode {mode!r}")

@@ -194,3 +194,23 @@ def test_plan_schedule_modes():
     assert (s.sk_tiles, s.dp_tiles, s.units) == (160, 740, 148)
     cov = sch.coverage(s.segments, s.tiles, s.ipt)
     assert all(c == 1 for row in cov for c in row)
+
+
+@pytest.mark.parametrize("M,N,K,batch,mode,splits", [
+    (256, 512, 2048, 4, "heuristic", 0),
+    (384, 640, 1024, 3, "streamk", 0),
+    (128, 256, 4096, 8, "heuristic", 0),
+    (512, 512, 512, 6, "splitk", 2),
+    (1024, 1024, 1024, 5, "heuristic", 0),
+])
+def test_batched_schedule_is_the_stacked_problem(M, N, K, batch, mode, splits):
+    # with M a multiple of the tile height, `batch` products of M x N stack into one
+    # (batch M) x N problem with the same tile count; the schedules must coincide
+    b = sch.plan_schedule(M, N, K, mode, splits, sms=256, batch=batch)
+    s = sch.plan_schedule(batch * M, N, K, mode, splits, sms=256)
+    assert b.tiles == s.tiles == batch * b.tiles_m * b.tiles_n
+    assert (b.kind, b.splits, b.units, b.sk_tiles, b.dp_tiles, b.q, b.big) == \
+        (s.kind, s.splits, s.units, s.sk_tiles, s.dp_tiles, s.q, s.big)
+    assert [x.as_tuple() for x in b.segments] == [x.as_tuple() for x in s.segments]
+    cov = sch.coverage(b.segments, b.tiles, b.ipt)
+    assert all(c == 1 for row in cov for c in row)
