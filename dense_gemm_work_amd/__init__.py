@@ -5,7 +5,8 @@ kernels of ``libdgw_gemm.so`` (built in-tree by ``dense_gemm_work_amd/build.py``
 The functions carry the names of the C entry points in ``include/gemm.h``:
 
 * ``gemm(A, B, C, M, N, K, layout, mode, splits)`` -- raw device pointers.
-* ``gemm_ex(args)``, ``gemm_plan(...)``, ``gemm_workspace_size(...)``, ``gemm_unit_range(...)``,
+* ``gemm_ex(args)``, ``gemm_plan(...)``, ``gemm_plan_batched(...)``, ``gemm_workspace_size(...)``,
+  ``gemm_unit_range(...)``,
   ``gemm_set_stream``, ``gemm_sync_status``, ``gemm_release``,
   ``gemm_last_error``, ``gemm_num_cus``, ``gemm_version``.
 
@@ -22,7 +23,8 @@ from pathlib import Path
 from typing import Optional
 
 __all__ = [
-    "GemmError", "GemmPlan", "GemmArgs", "gemm", "gemm_ex", "gemm_plan", "gemm_workspace_size", "gemm_unit_range",
+    "GemmError", "GemmPlan", "GemmArgs", "gemm", "gemm_ex", "gemm_plan", "gemm_plan_batched",
+    "gemm_workspace_size", "gemm_unit_range",
     "gemm_set_stream", "gemm_sync_status", "gemm_release", "gemm_last_error", "gemm_num_cus",
     "gemm_version", "gemm_tensors", "plan_dict", "library_path",
 ]
@@ -87,6 +89,7 @@ class GemmPlan(ctypes.Structure):
         ("splits", ctypes.c_int32), ("max_segments", ctypes.c_int32), ("max_fold", ctypes.c_int32),
         ("two_pass", ctypes.c_int32),
         ("workers", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64), ("trace_ints", ctypes.c_int64),
+        ("batch", ctypes.c_int64),
     ]
 
 
@@ -102,6 +105,8 @@ class GemmArgs(ctypes.Structure):
         ("timing", ctypes.c_void_p),
         ("epilogue", ctypes.c_uint32), ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
         ("bias", ctypes.c_void_p),
+        ("batch", ctypes.c_int64), ("stride_a", ctypes.c_int64), ("stride_b", ctypes.c_int64),
+        ("stride_c", ctypes.c_int64),
     ]
 
 
@@ -123,7 +128,9 @@ def _load() -> ctypes.CDLL:
     lib.gemm_plan.restype = ctypes.c_int
     lib.gemm_plan.argtypes = [i64, i64, i64, u32, u32, i32, i32, ctypes.POINTER(GemmPlan)]
     lib.gemm_workspace_size.restype = ctypes.c_int64
-    lib.gemm_workspace_size.argtypes = [i64, i64, i64, u32, u32, i32, i32]
+    lib.gemm_workspace_size.argtypes = [i64, i64, i64, i64, u32, u32, i32, i32]
+    lib.gemm_plan_batched.restype = ctypes.c_int
+    lib.gemm_plan_batched.argtypes = [i64, i64, i64, i64, u32, u32, i32, i32, ctypes.POINTER(GemmPlan)]
     lib.gemm_unit_range.restype = ctypes.c_int
     lib.gemm_unit_range.argtypes = [ctypes.POINTER(GemmPlan), i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.gemm_set_stream.restype = ctypes.c_int
@@ -166,8 +173,16 @@ def gemm_plan(M: int, N: int, K: int, layout: int, mode: int, splits: int, num_c
     return p
 
 
-def gemm_workspace_size(M: int, N: int, K: int, layout: int, mode: int, splits: int, num_cus: int) -> int:
-    return _check(int(_lib.gemm_workspace_size(M, N, K, layout, mode, splits, num_cus)))
+def gemm_plan_batched(M: int, N: int, K: int, batch: int, layout: int, mode: int, splits: int,
+                      num_cus: int) -> GemmPlan:
+    p = GemmPlan()
+    _check(_lib.gemm_plan_batched(M, N, K, batch, layout, mode, splits, num_cus, ctypes.byref(p)))
+    return p
+
+
+def gemm_workspace_size(M: int, N: int, K: int, layout: int, mode: int, splits: int, num_cus: int,
+                        batch: int = 1) -> int:
+    return _check(int(_lib.gemm_workspace_size(M, N, K, batch, layout, mode, splits, num_cus)))
 
 
 def gemm_unit_range(plan: GemmPlan, unit: int):
@@ -216,6 +231,22 @@ def mode_word(mode: str, atomic: bool = False, two_pass: bool = False) -> int:
     return MODES[mode] | (GEMM_ATOMIC if atomic else 0) | (GEMM_TWO_PASS if two_pass else 0)
 
 
+def _matrix_strides(name: str, t, rows: int, cols: int):
+    """(batch entries or None, element stride between entries) of a row-major
+    matrix or a batch of them (``[rows, cols]`` or ``[batch, rows, cols]``)."""
+    if t.dim() == 2:
+        if tuple(t.shape) != (rows, cols):
+            raise ValueError(f"{name} must be [{rows}, {cols}]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return None, 0
+    if t.dim() != 3 or tuple(t.shape[1:]) != (rows, cols):
+        raise ValueError(f"{name} must be [{rows}, {cols}] or [batch, {rows}, {cols}]")
+    if (cols > 1 and t.stride(2) != 1) or (rows > 1 and t.stride(1) != cols):
+        raise ValueError(f"{name}: every batch entry must be a contiguous row-major matrix")
+    return t.shape[0], (t.stride(0) if t.shape[0] > 1 else 0)
+
+
 def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits: int = 0,
                  atomic: bool = False, num_cus: int = 0, unit_perm=None, trace=None,
                  workspace=None, spin_limit: int = 0, debug: int = 0, timing=None,
@@ -223,18 +254,21 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
                  beta: Optional[float] = None, bias=None, act: str = "none") -> None:
     """``c[M,N] = a[M,K] . b`` (b [K,N]) or ``a . b^T`` (b [N,K]) on torch tensors.
 
+    Batched: c ``[batch, M, N]``; a and b ``[batch, ...]`` or 2-D (one matrix
+    shared by every entry); each entry a contiguous row-major matrix, entries at
+    any stride (the tensors' own).
     With ``alpha``/``beta``/``bias``/``act`` the call fuses the epilogue
     ``c = act(alpha a.b + beta c + bias)`` (bias: contiguous fp32 [N] device tensor;
     act: "none", "relu" or "gelu").
-    a, b: contiguous bf16/fp16 tensors on one HIP device; c: contiguous fp32 [M,N].
+    a, b: bf16/fp16 tensors on one HIP device; c: fp32.
     unit_perm / trace / workspace / timing: optional int32 / int32 / any-dtype / int64
     device tensors (see gemm_args_t in include/gemm.h).
     Enqueues on ``stream`` (a torch.cuda.Stream) or torch's current stream.
     """
     import torch
 
-    if a.dim() != 2 or b.dim() != 2 or c.dim() != 2:
-        raise ValueError("a, b and c must be 2-D")
+    if c.dim() not in (2, 3) or a.dim() not in (2, 3) or b.dim() not in (2, 3):
+        raise ValueError("a, b and c must be 2-D (or 3-D batches)")
     if a.dtype not in (torch.bfloat16, torch.float16) or b.dtype != a.dtype:
         raise TypeError("a and b must both be bf16 or both fp16")
     if c.dtype != torch.float32:
@@ -242,23 +276,26 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
     for name, t in (("a", a), ("b", b), ("c", c)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
     if not (a.device == b.device == c.device):
         raise ValueError("a, b and c must be on one device")
-    M, K = a.shape
+    M, K = a.shape[-2], a.shape[-1]
     if b_layout == "kn":
-        if b.shape[0] != K:
-            raise ValueError("b must be [K, N]")
-        N = b.shape[1]
+        N = b.shape[-1]
+        b_rows, b_cols = K, N
     elif b_layout == "nk":
-        if b.shape[1] != K:
-            raise ValueError("b must be [N, K]")
-        N = b.shape[0]
+        N = b.shape[-2]
+        b_rows, b_cols = N, K
     else:
         raise ValueError("b_layout must be 'kn' or 'nk'")
-    if tuple(c.shape) != (M, N):
-        raise ValueError("c must be [M, N]")
+    batch_c, sc = _matrix_strides("c", c, M, N)
+    batch_a, sa = _matrix_strides("a", a, M, K)
+    batch_b, sb = _matrix_strides("b", b, b_rows, b_cols)
+    batch = batch_c or 1
+    for name, n in (("a", batch_a), ("b", batch_b)):
+        if n is not None and n != batch and n != 1:
+            raise ValueError(f"{name} has {n} batch entries, c has {batch}")
+    if batch_c is None and (batch_a or 1) * (batch_b or 1) > 1:
+        raise ValueError("a batched a or b needs a batched c [batch, M, N]")
     dtype = "bf16" if a.dtype == torch.bfloat16 else "fp16"
     args = GemmArgs()
     args.A, args.B, args.C = a.data_ptr(), b.data_ptr(), c.data_ptr()
@@ -267,6 +304,9 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
     args.mode = mode_word(mode, atomic, two_pass)
     args.splits = splits
     args.num_cus = num_cus
+    if batch > 1:
+        args.batch = batch
+        args.stride_a, args.stride_b, args.stride_c = sa, sb, (sc if sc else M * N)
     with torch.cuda.device(a.device):
         s = stream if stream is not None else torch.cuda.current_stream(a.device)
         args.stream = s.cuda_stream

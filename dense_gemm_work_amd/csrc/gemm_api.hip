@@ -152,7 +152,18 @@ int check_operands(const gemm_args_t &a) {
     const uintptr_t mis = (reinterpret_cast<uintptr_t>(a.A) | reinterpret_cast<uintptr_t>(a.B) |
                            reinterpret_cast<uintptr_t>(a.C)) & 15;
     if (mis) return fail(GEMM_ERR_UNSUPPORTED, "A, B and C must be 16-byte aligned");
-    const int64_t cb = a.M * a.N * 4, ab = a.M * a.K * 2, bb = a.K * a.N * 2;
+    const int64_t batch = a.batch > 1 ? a.batch : 1;
+    if (batch > 1) {
+        if (a.stride_a < 0 || a.stride_b < 0 || a.stride_c < a.M * a.N)
+            return fail(GEMM_ERR_INVALID, "batch strides: stride_a, stride_b >= 0 and stride_c >= M*N");
+        if ((a.stride_a & 7) || (a.stride_b & 7) || (a.stride_c & 3))
+            return fail(GEMM_ERR_UNSUPPORTED, "batch strides must keep 16-byte alignment "
+                                              "(stride_a, stride_b multiples of 8, stride_c of 4)");
+    }
+    // byte extents of all batch entries (a zero stride shares one matrix)
+    const int64_t sa = batch > 1 ? a.stride_a : 0, sb = batch > 1 ? a.stride_b : 0, sc = batch > 1 ? a.stride_c : 0;
+    const int64_t cb = ((batch - 1) * sc + a.M * a.N) * 4, ab = ((batch - 1) * sa + a.M * a.K) * 2,
+                  bb = ((batch - 1) * sb + a.K * a.N) * 2;
     if (overlaps(a.C, cb, a.A, ab) || overlaps(a.C, cb, a.B, bb))
         return fail(GEMM_ERR_INVALID, "C must not overlap A or B");
     if (a.trace && a.trace_ints <= 0) return fail(GEMM_ERR_INVALID, "trace_ints must be > 0");
@@ -187,6 +198,20 @@ void set_epilogue(const gemm_args_t &a, bool accum, KParams &kp) {
     kp.epi = a.epilogue == 0 ? dgw::EPI_PLAIN : accum ? dgw::EPI_ACCUM : dgw::EPI_FULL;
 }
 
+// C := 0 in every batch entry (what lies between entries is not touched).
+hipError_t zero_c(const gemm_args_t &a, int64_t batch, hipStream_t stream) {
+    if (batch == 1 || a.stride_c == a.M * a.N) return dgw::launch_zero(a.C, batch * a.M * a.N, stream);
+    KParams z;
+    std::memset(&z, 0, sizeof z);
+    z.C = a.C;
+    z.M = (int)a.M;
+    z.N = (int)a.N;
+    z.batch = (int)batch;
+    z.sC = a.stride_c;
+    z.alpha = 1.0f;   // EPASS_PRE with beta = 0 and no bias writes zeros
+    return dgw::launch_epilogue_pass(z, dgw::EPASS_PRE, stream);
+}
+
 struct TraceHeader {
     int v[8];
 };
@@ -200,7 +225,8 @@ int run(const gemm_args_t &a) {
     gemm_plan_t p;
     const char *why = "";
     // plan first with a placeholder CU count so argument errors surface before any HIP call
-    int rc = dgw::make_plan(a.M, a.N, a.K, a.layout, a.mode, a.splits,
+    const int64_t batch = a.batch > 1 ? a.batch : 1;
+    int rc = dgw::make_plan(a.M, a.N, a.K, batch, a.layout, a.mode, a.splits,
                             a.num_cus > 0 ? a.num_cus : 256, &p, &why);
     if (rc != GEMM_OK) return fail(rc, why);
     if (a.num_cus < 0) return fail(GEMM_ERR_INVALID, "num_cus must be >= 0");
@@ -219,7 +245,7 @@ int run(const gemm_args_t &a) {
     DeviceState *ds = nullptr;
     if ((rc = device_state(dev, &ds)) != GEMM_OK) return rc;
     const int ncu = a.num_cus > 0 ? a.num_cus : ds->num_cus;
-    if ((rc = dgw::make_plan(a.M, a.N, a.K, a.layout, a.mode, a.splits, ncu, &p, &why)) != GEMM_OK)
+    if ((rc = dgw::make_plan(a.M, a.N, a.K, batch, a.layout, a.mode, a.splits, ncu, &p, &why)) != GEMM_OK)
         return fail(rc, why);
 
     const int dtype = (a.layout & 0xF0u) == GEMM_FP16 ? 1 : 0;
@@ -227,13 +253,15 @@ int run(const gemm_args_t &a) {
 
     if (a.K == 0) {  // the empty sum
         if (a.epilogue == 0) {
-            if ((e = dgw::launch_zero(a.C, a.M * a.N, stream)) != hipSuccess) return fail_hip(e, "zero C");
+            if ((e = zero_c(a, batch, stream)) != hipSuccess) return fail_hip(e, "zero C");
         } else {
             KParams ep;
             std::memset(&ep, 0, sizeof ep);
             ep.C = a.C;
             ep.M = (int)a.M;
             ep.N = (int)a.N;
+            ep.batch = (int)batch;
+            ep.sC = batch > 1 ? a.stride_c : 0;
             set_epilogue(a, false, ep);
             if ((e = dgw::launch_epilogue_pass(ep, dgw::EPASS_ONLY, stream)) != hipSuccess)
                 return fail_hip(e, "epilogue of an empty sum");
@@ -302,13 +330,19 @@ int run(const gemm_args_t &a) {
     kp.spin_limit = a.spin_limit ? a.spin_limit : kDefaultSpin;
     kp.debug = a.debug;
     kp.perm = a.unit_perm;
+    kp.batch = (int)batch;
+    kp.sA = batch > 1 ? a.stride_a : 0;
+    kp.sB = batch > 1 ? a.stride_b : 0;
+    kp.sC = batch > 1 ? a.stride_c : 0;
+    // Split-K partials [batch][S][M][N]
+    kp.sP = p.decision == GEMM_SPLITK && !p.atomic ? (long long)p.splits * a.M * a.N : 0;
     // atomic merges add into C: with an epilogue, C first becomes beta C + bias,
     // the merges add alpha acc, and the activation is a last elementwise pass
     const bool atomic_merge = p.atomic && p.decision != GEMM_DP;
     set_epilogue(a, atomic_merge, kp);
     auto prepare_atomic_c = [&]() -> int {
         if (kp.epi == dgw::EPI_PLAIN) {
-            if ((e = dgw::launch_zero(a.C, a.M * a.N, stream)) != hipSuccess) return fail_hip(e, "zero C");
+            if ((e = zero_c(a, batch, stream)) != hipSuccess) return fail_hip(e, "zero C");
         } else if ((e = dgw::launch_epilogue_pass(kp, dgw::EPASS_PRE, stream)) != hipSuccess) {
             return fail_hip(e, "epilogue pre-pass");
         }
@@ -337,7 +371,7 @@ int run(const gemm_args_t &a) {
         // a group takes about 4 / 1.4 tile times (measured on 8192^3: 1207 us
         // with one tile per workgroup, 840 us with groups), so with G groups and
         // T tiles on C CUs groups win when ceil(G / C) * 4 < ceil(T / C) * 1.4
-        const int64_t ngroups = ((p.tiles_m + 1) / 2) * ((p.tiles_n + 1) / 2);
+        const int64_t ngroups = batch * ((p.tiles_m + 1) / 2) * ((p.tiles_n + 1) / 2);
         const int64_t gwaves = (ngroups + ncu - 1) / ncu, twaves = (p.tiles + ncu - 1) / ncu;
         const bool groups = gwaves * 40 < twaves * 14 && !(a.debug & GEMM_DEBUG_TILE_DP);
         if (groups) {
@@ -427,18 +461,23 @@ int gemm_ex(const gemm_args_t *args) {
 
 int gemm_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, int32_t splits,
               int32_t num_cus, gemm_plan_t *out) {
+    return gemm_plan_batched(M, N, K, 1, layout, mode, splits, num_cus, out);
+}
+
+int gemm_plan_batched(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, uint32_t mode,
+                      int32_t splits, int32_t num_cus, gemm_plan_t *out) {
     const char *why = "";
-    int rc = dgw::make_plan(M, N, K, layout, mode, splits, num_cus, out, &why);
+    int rc = dgw::make_plan(M, N, K, batch, layout, mode, splits, num_cus, out, &why);
     if (rc != GEMM_OK) return fail(rc, why);
     g_err.clear();
     return GEMM_OK;
 }
 
-int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, int32_t splits,
-                            int32_t num_cus) {
+int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, uint32_t mode,
+                            int32_t splits, int32_t num_cus) {
     gemm_plan_t p;
     const char *why = "";
-    int rc = dgw::make_plan(M, N, K, layout, mode, splits, num_cus, &p, &why);
+    int rc = dgw::make_plan(M, N, K, batch, layout, mode, splits, num_cus, &p, &why);
     if (rc != GEMM_OK) return fail(rc, why);
     g_err.clear();
     return p.workspace_bytes;

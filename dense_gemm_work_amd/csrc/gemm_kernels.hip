@@ -514,6 +514,7 @@ __device__ __forceinline__ int worker_of(const KParams &p, int n) {
     return p.xcd_spread ? spread(b, n) : b;
 }
 
+// Origin of tile `tile` of one batch entry's tile grid.
 __device__ __forceinline__ void tile_origin(const KParams &p, int tile, int &m0, int &n0) {
     const int gm_full = p.group_m > 0 ? p.group_m : p.tiles_m;
     const int per_group = gm_full * p.tiles_n;
@@ -523,6 +524,29 @@ __device__ __forceinline__ void tile_origin(const KParams &p, int tile, int &m0,
     const int w = tile - g * per_group;
     m0 = (first + w % gm) * BM;
     n0 = (w / gm) * BN;
+}
+
+// A copy of p whose A, B, C (and Split-K partials) point at batch entry b.
+__device__ __forceinline__ KParams batch_entry(const KParams &p, int b) {
+    KParams q = p;
+    q.A += (size_t)b * p.sA;
+    q.B += (size_t)b * p.sB;
+    q.C += (size_t)b * p.sC;
+    q.part += (size_t)b * p.sP;
+    return q;
+}
+
+// Tiles are numbered batch after batch: the view of global tile `tile`'s batch
+// entry and the tile's origin in it.
+__device__ __forceinline__ KParams tile_view(const KParams &p, int tile, int &m0, int &n0) {
+    if (p.batch <= 1) {
+        tile_origin(p, tile, m0, n0);
+        return p;
+    }
+    const int tpb = p.tiles_m * p.tiles_n;
+    const int b = tile / tpb;
+    tile_origin(p, tile - b * tpb, m0, n0);
+    return batch_entry(p, b);
 }
 
 // ---------------------------------------------------------------------------
@@ -998,13 +1022,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_dp(KParams p) {
     const int w = worker_of(p, p.ntiles);
     const int tile = p.tile_base + w;
     int m0, n0;
-    tile_origin(p, tile, m0, n0);
+    const KParams q = tile_view(p, tile, m0, n0);
     Acc acc;
     zero_acc(acc);
-    mac_loop<DT, BL, NS, NW>(p, lds, m0, n0, 0, p.ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
+    mac_loop<DT, BL, NS, NW>(q, lds, m0, n0, 0, p.ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
     const Tile<NW> t = merge_k_halves<NW>(acc, lds);
     clk.mark(p, 0);
-    store_final<NW>(p, m0, n0, t);
+    store_final<NW>(q, m0, n0, t);
     trace_segment(p, p.worker_base + w, 0, tile, 0, p.ipt, 0);
     trace_folded(p, tile, 0, p.worker_base + w);
     clk.done(p);
@@ -1284,8 +1308,12 @@ __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
     constexpr int JB = GAcc<G_NW>::JB;
     const WgClock clk(p);
     const int g = worker_of(p, p.ntiles);
+    // groups are numbered batch after batch, gpb per batch entry
+    const int gpb = ((p.tiles_m + 1) / 2) * ((p.tiles_n + 1) / 2);
+    const int b = p.batch > 1 ? g / gpb : 0;
+    const KParams q = p.batch > 1 ? batch_entry(p, b) : p;
     int m0, n0;
-    group_origin(p, g, m0, n0);
+    group_origin(p, g - b * gpb, m0, n0);
     GAcc<G_NW> acc;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1293,8 +1321,8 @@ __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
         for (int j = 0; j < JB; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc.v[i][j][e] = 0.0f;
-    if (p.K % BK == 0) group_loop<DT, BL, G_NW, false>(p, lds, m0, n0, acc);
-    else group_loop<DT, BL, G_NW, true>(p, lds, m0, n0, acc);
+    if (p.K % BK == 0) group_loop<DT, BL, G_NW, false>(q, lds, m0, n0, acc);
+    else group_loop<DT, BL, G_NW, true>(q, lds, m0, n0, acc);
     clk.mark(p, 0);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -1307,7 +1335,7 @@ __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    if (row < p.M && col < p.N) p.C[(size_t)row * p.N + col] = acc.v[i][j][e];
+                    if (row < p.M && col < p.N) q.C[(size_t)row * p.N + col] = acc.v[i][j][e];
                 }
             }
     } else {
@@ -1318,7 +1346,7 @@ __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
         const int C0 = n0 + wn * JB * 32;
         float bj[JB];
         lane_bias<JB>(p, C0, bj);
-        auto block = [&](int i) { return CBlock<JB>(p, m0 + wm * 128 + i * 32, C0); };
+        auto block = [&](int i) { return CBlock<JB>(q, m0 + wm * 128 + i * 32, C0); };
         float cbuf[2][JB * 16];
         auto load_block = [&](int i, float (&cin)[JB * 16]) {
             const CBlock<JB> cb = block(i);
@@ -1353,10 +1381,10 @@ __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
     }
     if (p.trace && threadIdx.x == 0) {
         // the four tiles of the group, each a whole-K data-parallel tile
-        for (int q = 0; q < 4; ++q) {
-            const int tm = m0 / BM + (q & 1), tn = n0 / BN + (q >> 1);
+        for (int x = 0; x < 4; ++x) {
+            const int tm = m0 / BM + (x & 1), tn = n0 / BN + (x >> 1);
             if (tm >= p.tiles_m || tn >= p.tiles_n) continue;   // over the edge of the tile grid
-            const int tile = tile_id(p, tm, tn);
+            const int tile = b * p.tiles_m * p.tiles_n + tile_id(p, tm, tn);
             trace_segment(p, p.worker_base + tile, 0, tile, 0, p.ipt, 0);
             trace_folded(p, tile, 0, p.worker_base + tile);
             int *cov = trace_cov(p, tile);
@@ -1370,17 +1398,17 @@ __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
 // Split-K: worker w = tile * S + s covers k-iterations [s P / S, (s+1) P / S).
 // ---------------------------------------------------------------------------
 template <int DT, int BL, int NS, int NW>
-__global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p) {
+__global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p0) {
     constexpr int NT = Role<NW>::NT, QPT = BM * BN / 4 / NT;
     __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_BYTES];
     __shared__ int last_arriver;
-    const WgClock clk(p);
-    const int S = p.splits;
-    const int w = worker_of(p, p.ntiles * S);
+    const WgClock clk(p0);
+    const int S = p0.splits;
+    const int w = worker_of(p0, p0.ntiles * S);
     const int tile = w / S, s = w % S;
-    const int k0 = (int)((int64_t)s * p.ipt / S), k1 = (int)((int64_t)(s + 1) * p.ipt / S);
+    const int k0 = (int)((int64_t)s * p0.ipt / S), k1 = (int)((int64_t)(s + 1) * p0.ipt / S);
     int m0, n0;
-    tile_origin(p, tile, m0, n0);
+    const KParams p = tile_view(p0, tile, m0, n0);   // the tile's batch entry
     Acc acc;
     zero_acc(acc);
     mac_loop<DT, BL, NS, NW>(p, lds, m0, n0, k0, k1, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
@@ -1551,11 +1579,11 @@ constexpr int RED_THREADS = 256;
 constexpr int RED_BLOCKS_PER_TILE = BM * BN / 4 / RED_THREADS;   // 16
 
 template <bool EPI>
-__global__ __launch_bounds__(RED_THREADS) void splitk_reduce(KParams p) {
+__global__ __launch_bounds__(RED_THREADS) void splitk_reduce(KParams p0) {
     const int tile = blockIdx.x / RED_BLOCKS_PER_TILE;
     const int q = (blockIdx.x % RED_BLOCKS_PER_TILE) * RED_THREADS + threadIdx.x;   // quad within the tile
     int m0, n0;
-    tile_origin(p, tile, m0, n0);
+    const KParams p = tile_view(p0, tile, m0, n0);   // the tile's batch entry
     const int r = q >> 5, c = (q & 31) * 4;
     const int S = p.splits;
     if (threadIdx.x == 0 && blockIdx.x % RED_BLOCKS_PER_TILE == 0)
@@ -1634,7 +1662,7 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
             if (v0 + j < vend) sum += x[j];
     }
     int m0, n0;
-    tile_origin(p, tile, m0, n0);
+    const KParams pv = tile_view(p, tile, m0, n0);   // the tile's batch entry
     const int lane = f & 63, e4 = (f >> 6) & 3, b = (f >> 8) & 3, quad = f >> 10;
     const int row = m0 + (quad >> 1) * 64 + (b >> 1) * 32 + 8 * e4 + 4 * (lane >> 5);
     const int col = n0 + (quad & 1) * 64 + (b & 1) * 32 + (lane & 31);
@@ -1646,7 +1674,7 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
         const float bv[4] = {b, b, b, b};
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
-            cin[y] = (rc && row + y < p.M) ? p.C[(size_t)(row + y) * p.N + col] : 0.0f;
+            cin[y] = (rc && row + y < p.M) ? pv.C[(size_t)(row + y) * p.N + col] : 0.0f;
             v[y] = sum[y];
         }
         finish<4>(p, v, cin, bv);
@@ -1655,7 +1683,7 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
     }
 #pragma unroll
     for (int y = 0; y < 4; ++y)
-        if (row + y < p.M) p.C[(size_t)(row + y) * p.N + col] = sum[y];
+        if (row + y < p.M) pv.C[(size_t)(row + y) * p.N + col] = sum[y];
 }
 
 // ---------------------------------------------------------------------------
@@ -1695,23 +1723,23 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         const int k1 = min(end - tb, ipt);
         const int tile = p.tile_base + ts;
         int m0, n0;
-        tile_origin(p, tile, m0, n0);
+        const KParams pv = tile_view(p, tile, m0, n0);   // the tile's batch entry
         const int role = k0 > 0 ? 2 : (k1 == ipt ? 0 : 1);
         const int owner = unit_of(tb, p.q, p.big);
         const int rot = (tb - unit_start(owner, p.q, p.big)) % ipt;
         Acc acc;
         zero_acc(acc);
-        mac_loop<DT, BL, NS, NW>(p, lds, m0, n0, k0, k1, rot, acc, p.trace ? trace_cov(p, tile) : nullptr,
+        mac_loop<DT, BL, NS, NW>(pv, lds, m0, n0, k0, k1, rot, acc, p.trace ? trace_cov(p, tile) : nullptr,
                                  pending);
         pending = nullptr;
         Tile<NW> t = merge_k_halves<NW>(acc, lds);
         clk.mark(p, 2 * min(nseg, 1));
         trace_segment(p, u, nseg++, tile, k0, k1, role);
         if (role == 0) {
-            if constexpr (!EPI) store_final<NW, false>(p, m0, n0, t);
+            if constexpr (!EPI) store_final<NW, false>(pv, m0, n0, t);
             trace_folded(p, tile, 0, u);
         } else if constexpr (ATOMIC) {
-            atomic_add_c<NW, EPI>(p, m0, n0, t);
+            atomic_add_c<NW, EPI>(pv, m0, n0, t);
         } else if (p.merge == MERGE_TWO_PASS) {
             // streamk_reduce adds the tile's partials: contributors publish into
             // the first slot bank, owners into the second
@@ -1743,12 +1771,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
                 add_slot<NW>(p.part + (size_t)v * (BM * BN), t);
                 trace_folded(p, tile, pos_fold++, v);
             }
-            if constexpr (!EPI) store_final<NW, false>(p, m0, n0, t);
+            if constexpr (!EPI) store_final<NW, false>(pv, m0, n0, t);
         }
         // the epilogue build stores whole tiles and folded tiles from one call
         // site (one inlined copy of the epilogue code)
         if constexpr (EPI) {
-            if (role == 0 || (role == 1 && !ATOMIC && p.merge != MERGE_TWO_PASS)) store_final<NW, true>(p, m0, n0, t);
+            if (role == 0 || (role == 1 && !ATOMIC && p.merge != MERGE_TWO_PASS)) store_final<NW, true>(pv, m0, n0, t);
         }
         clk.mark(p, 2 * min(nseg - 1, 1) + 1);
         pos = tb + k1;
@@ -1757,7 +1785,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Elementwise epilogue pass over C (atomic merges and the empty sum):
+// Elementwise epilogue pass over C, every batch entry (atomic merges and the
+// empty sum):
 // EPASS_PRE  C = beta C + bias (C not read when beta == 0),
 // EPASS_POST C = act(C),
 // EPASS_ONLY C = act(beta C + bias), i.e. the epilogue of a zero product.
@@ -1766,9 +1795,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
 __global__ __launch_bounds__(256) void epilogue_pass(KParams p, int stage) {
 #pragma clang fp contract(off)
     const bool rc = p.beta != 0.0f;
+    for (int z = blockIdx.z; z < p.batch; z += gridDim.z)
     for (int row = blockIdx.y; row < p.M; row += gridDim.y)
         for (int col = blockIdx.x * blockDim.x + threadIdx.x; col < p.N; col += gridDim.x * blockDim.x) {
-            float *c = p.C + (size_t)row * p.N + col;
+            float *c = p.C + (size_t)z * p.sC + (size_t)row * p.N + col;
             const float b = p.bias ? p.bias[col] : 0.0f;
             if (stage == EPASS_POST) {
                 *c = act_apply(p.act, *c);
@@ -1849,7 +1879,7 @@ hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParam
 }
 
 hipError_t launch_splitk_reduce(const KParams &p, hipStream_t stream) {
-    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t tiles = (int64_t)std::max(p.batch, 1) * p.tiles_m * p.tiles_n;   // every batch entry's tiles
     if (tiles <= 0) return hipSuccess;
     // a separate build with the epilogue keeps the plain one's code unchanged
     if (p.epi != EPI_PLAIN)
@@ -1875,7 +1905,8 @@ hipError_t launch_streamk_reduce(const KParams &p, int64_t sk_tiles, hipStream_t
 hipError_t launch_epilogue_pass(const KParams &p, int stage, hipStream_t stream) {
     const int gx = (int)std::min<int64_t>((p.N + 255) / 256, 16);
     const int gy = (int)std::min<int64_t>(p.M, 4096);
-    hipLaunchKernelGGL(epilogue_pass, dim3(gx, gy), dim3(256), 0, stream, p, stage);
+    const int gz = std::max(1, std::min(p.batch, 64));
+    hipLaunchKernelGGL(epilogue_pass, dim3(gx, gy, gz), dim3(256), 0, stream, p, stage);
     return hipGetLastError();
 }
 

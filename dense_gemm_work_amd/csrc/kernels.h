@@ -46,7 +46,7 @@ struct KParams {
     const uint16_t *B;     // [K,N] or [N,K] row-major
     float *C;              // [M,N] row-major fp32
     int M, N, K;
-    int tiles_m, tiles_n;  // output tiles along M and N
+    int tiles_m, tiles_n;  // output tiles along M and N (of one batch entry)
     int group_m;           // tile ids run column by column in groups of group_m tile rows (0: row-major)
     int xcd_spread;        // 1: give each XCD a contiguous range of workers
     int ipt;               // k-iterations per tile
@@ -63,6 +63,9 @@ struct KParams {
     uint32_t epoch;        // value a publishing unit writes into its flag
     uint32_t spin_limit;   // polls before a wait gives up
     uint32_t debug;        // GEMM_DEBUG_* bits
+    int batch;             // matrices of a batched call (tiles numbered batch after batch)
+    long long sA, sB, sC;  // element strides between batch entries of A, B (0: one shared matrix) and C
+    long long sP;          // Split-K: element stride between batch entries' partials ([batch][S][M][N])
     int epi, act;          // EPI_* and ACT_*: the fused epilogue of the final stores
     float alpha, beta;     // epilogue scalars (EPI_FULL; EPI_ACCUM uses alpha)
     const float *bias;     // optional fp32 [N] added per column (EPI_FULL)
@@ -87,8 +90,8 @@ hipError_t launch_splitk_reduce(const KParams &p, hipStream_t stream);
 // added in k order.
 hipError_t launch_streamk_reduce(const KParams &p, int64_t sk_tiles, hipStream_t stream);
 
-// Elementwise epilogue pass over C[M,N] (stage EPASS_*; p.C, p.M, p.N, p.beta,
-// p.bias, p.act).
+// Elementwise epilogue pass over C[M,N] of every batch entry (stage EPASS_*;
+// p.C, p.M, p.N, p.batch, p.sC, p.beta, p.bias, p.act).
 hipError_t launch_epilogue_pass(const KParams &p, int stage, hipStream_t stream);
 
 // Fill n 32-bit words with zero (used instead of hipMemsetAsync so the call can

@@ -33,7 +33,7 @@ int64_t unit_begin(int64_t unit, int64_t q, int64_t big) {
     return unit * q + std::min(unit, big);
 }
 
-int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, int32_t splits,
+int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, uint32_t mode, int32_t splits,
               int32_t num_cus, gemm_plan_t *out, const char **why) {
     static const char *none = "";
     *why = none;
@@ -41,6 +41,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
     std::memset(out, 0, sizeof *out);
     if (M < 0 || N < 0 || K < 0) { *why = "M, N and K must be >= 0"; return GEMM_ERR_INVALID; }
     if (num_cus < 1) { *why = "num_cus must be >= 1"; return GEMM_ERR_INVALID; }
+    if (batch < 1) { *why = "batch must be >= 1"; return GEMM_ERR_INVALID; }
     const uint32_t b_layout = layout & 0xFu, dtype = layout & 0xF0u;
     if ((layout & ~0xFFu) || (b_layout != GEMM_B_KN && b_layout != GEMM_B_NK) ||
         (dtype != GEMM_BF16 && dtype != GEMM_FP16)) {
@@ -83,9 +84,12 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
     p.atomic = 0;
     p.bm = GEMM_BM; p.bn = GEMM_BN; p.bk = GEMM_BK;
     p.num_cus = num_cus;
+    p.batch = batch;
     p.tiles_m = ceil_div(M, GEMM_BM);
     p.tiles_n = ceil_div(N, GEMM_BN);
-    p.tiles = p.tiles_m * p.tiles_n;
+    // a batched call is one problem of batch x tiles_m x tiles_n tiles, numbered
+    // batch after batch; the rule and the Stream-K flattening see that count
+    p.tiles = batch * p.tiles_m * p.tiles_n;
     p.ipt = ceil_div(K, GEMM_BK);
     p.full_waves = p.tiles / num_cus;
     p.total_waves = ceil_div(p.tiles, num_cus);
@@ -153,9 +157,9 @@ int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, i
         p.workers = p.tiles * S;
         p.max_segments = 1;
         p.max_fold = S;
-        // fp32 partials [S, M, N] (none with atomics); an arrival counter per tile
-        // and a flag per (tile, split)
-        p.workspace_bytes = S > 1 && !p.atomic ? int64_t(S) * M * N * 4 : 0;
+        // fp32 partials [batch, S, M, N] (none with atomics) and an arrival
+        // counter per tile
+        p.workspace_bytes = S > 1 && !p.atomic ? batch * int64_t(S) * M * N * 4 : 0;
         break;
     case GEMM_STREAMK: {
         p.atomic = atomic ? 1 : 0;

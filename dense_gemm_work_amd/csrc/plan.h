@@ -7,8 +7,9 @@
 
 namespace dgw {
 
-// Fill *out for a call; returns a GEMM_* status and points *why at a message.
-int make_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, int32_t splits,
+// Fill *out for a call of `batch` (>= 1) products; returns a GEMM_* status and
+// points *why at a message.
+int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, uint32_t mode, int32_t splits,
               int32_t num_cus, gemm_plan_t *out, const char **why);
 
 // First flattened iteration of Stream-K unit `unit` ("big" units first).

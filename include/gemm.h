@@ -6,6 +6,9 @@
  *     C[M,N] = A[M,K] . B          (B stored [K,N], row-major)        layout GEMM_B_KN
  *     C[M,N] = A[M,K] . B^T        (B stored [N,K], row-major)        layout GEMM_B_NK
  *
+ * for one product or (gemm_ex, gemm_args_t.batch) a batch of products of one
+ * shape with strided operands.
+ *
  * A and B hold bf16 or fp16 values; products are accumulated in fp32 and C is
  * written in fp32: overwritten with the product, or (gemm_ex with an epilogue
  * word) C = act(alpha A.B + beta C + bias), see GEMM_EPI_* below.  The work decomposition is the
@@ -169,6 +172,8 @@ typedef struct gemm_plan_t {
     int64_t workers;      /* traced workers: units + dp_tiles, tiles * S, or tiles          */
     int64_t workspace_bytes; /* device workspace the call needs                             */
     int64_t trace_ints;   /* int32 elements of a debug trace buffer for this call           */
+    int64_t batch;        /* products in the call; tiles = batch * tiles_m * tiles_n,
+                             numbered batch entry after batch entry                        */
 } gemm_plan_t;
 
 /*
@@ -203,7 +208,17 @@ typedef struct gemm_plan_t {
  *   epilogue: GEMM_EPI_* bits (0: C is overwritten with A.B).  RELU and GELU
  *             exclude each other; GEMM_EPI_BIAS is set exactly when bias != NULL.
  *   alpha, beta: epilogue scalars, used with GEMM_EPI_ALPHA_BETA.
- *   bias:     device fp32 [N] (16-byte aligned, not overlapping C), or NULL.
+ *   bias:     device fp32 [N] (16-byte aligned, not overlapping C), or NULL; one
+ *             bias serves every batch entry.
+ *   batch:    number of independent products C_b = A_b . B_b of one shape
+ *             (0 or 1: a single product).  Entry b starts stride_a / stride_b /
+ *             stride_c ELEMENTS after entry b - 1 (A and B: >= 0, a 0 stride
+ *             shares one matrix among all entries; C: >= M*N, entries must not
+ *             overlap; A and B strides multiples of 8, C's of 4, keeping 16-byte
+ *             alignment).  The decomposition sees batch * tiles_m * tiles_n tiles,
+ *             numbered entry after entry, so Stream-K units and Split-K work
+ *             spread over all entries (docc StreamK page, generality: batched
+ *             GEMM).  Strides are ignored when batch <= 1.
  * Tuning overrides read once from the environment (defaults in brackets):
  *   DGW_GROUP_M    tile rows per raster group [8]; tile ids run column by column
  *                  within a group of rows (0 = plain row-major)
@@ -231,6 +246,10 @@ typedef struct gemm_args_t {
     float alpha;
     float beta;
     const float *bias;
+    int64_t batch;
+    int64_t stride_a;
+    int64_t stride_b;
+    int64_t stride_c;
 } gemm_args_t;
 
 /*
@@ -278,15 +297,20 @@ int gemm_ex(const gemm_args_t *args);
 int gemm_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode,
               int32_t splits, int32_t num_cus, gemm_plan_t *out);
 
+/* gemm_plan_batched -- gemm_plan for a call of `batch` (>= 1) products. */
+int gemm_plan_batched(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout,
+                      uint32_t mode, int32_t splits, int32_t num_cus, gemm_plan_t *out);
+
 /*
  * gemm_workspace_size -- device workspace bytes a call with these arguments
  * needs (plan.workspace_bytes: Stream-K partial slots and flags, Split-K
  * partials and counters, the status block), for a caller that passes its own
- * gemm_args_t.workspace.  num_cus >= 1 (no device is queried).  Returns the
- * byte count (>= 0) or a negative status for arguments gemm_plan rejects.
+ * gemm_args_t.workspace.  batch >= 1; num_cus >= 1 (no device is queried).
+ * Returns the byte count (>= 0) or a negative status for arguments
+ * gemm_plan_batched rejects.
  */
-int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode,
-                            int32_t splits, int32_t num_cus);
+int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout,
+                            uint32_t mode, int32_t splits, int32_t num_cus);
 
 /*
  * gemm_unit_range -- [begin, end) of Stream-K unit u in the flattened space of

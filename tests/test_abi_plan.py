@@ -259,6 +259,38 @@ def test_workspace_size_matches_plan(dg):
     assert ei.value.status == dg.GEMM_ERR_INVALID
 
 
+def test_batched_plan_and_rejections(dg):
+    # the plan sees batch x tiles_m x tiles_n tiles (the simulator's batched plan)
+    for M, N, K, batch, mode in [(256, 512, 2048, 6, "heuristic"), (640, 640, 2048, 2, "heuristic"),
+                                 (384, 640, 1024, 3, "streamk")]:
+        p = dg.gemm_plan_batched(M, N, K, batch, 0, dg.mode_word(mode), 0, 256)
+        s = sch.plan_schedule(M, N, K, mode, 0, sms=256, batch=batch)
+        assert p.batch == batch and p.tiles == s.tiles
+        assert dg.DECISION_NAMES[p.decision] == s.kind
+        assert (p.sk_units, p.sk_tiles, p.dp_tiles, p.q, p.big, p.splits) == \
+            (s.units, s.sk_tiles, s.dp_tiles, s.q, s.big, s.splits)
+    p = dg.gemm_plan_batched(96, 512, 2048, 4, 1, dg.GEMM_SPLITK, 8, 256)
+    assert p.workspace_bytes >= 4 * 8 * 96 * 512 * 4     # partials [batch, S, M, N]
+    assert dg.gemm_workspace_size(96, 512, 2048, 1, dg.GEMM_SPLITK, 8, 256, batch=4) == p.workspace_bytes
+    with pytest.raises(dg.GemmError):
+        dg.gemm_plan_batched(96, 512, 2048, 0, 1, dg.GEMM_SPLITK, 8, 256)
+    # stride checks happen before any HIP call (fake, aligned, disjoint pointers)
+    a = dg.GemmArgs()
+    a.A, a.B, a.C = 1 << 20, 1 << 26, 1 << 32
+    a.M, a.N, a.K = 128, 128, 64
+    a.mode = dg.GEMM_DP
+    a.batch = 2
+    a.stride_a, a.stride_b, a.stride_c = 128 * 64, 64 * 128, 128 * 128 - 4
+    assert dg.gemm_ex(a) == dg.GEMM_ERR_INVALID and "stride_c" in dg.gemm_last_error()
+    a.stride_c = 128 * 128 + 2
+    assert dg.gemm_ex(a) == dg.GEMM_ERR_UNSUPPORTED
+    a.stride_c, a.stride_a = 128 * 128, 12
+    assert dg.gemm_ex(a) == dg.GEMM_ERR_UNSUPPORTED
+    # C's batch extent reaching into B
+    a.stride_a, a.C = 0, (1 << 26) - 2 * 128 * 128 * 4 + 64
+    assert dg.gemm_ex(a) == dg.GEMM_ERR_INVALID and "overlap" in dg.gemm_last_error()
+
+
 def test_splitk_merge_modes_plan(dg):
     # deterministic Split-K adds the partials in split order, by a second kernel
     # when the whole grid fits on the CUs at once (or GEMM_TWO_PASS asks for it),
