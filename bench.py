@@ -66,10 +66,14 @@ class Call:
 
         self.dg = dg
         args = dg.GemmArgs()
-        M, K = a.shape
-        N = c.shape[1]
+        M, K = a.shape[-2], a.shape[-1]
+        N = c.shape[-1]
         args.A, args.B, args.C = a.data_ptr(), b.data_ptr(), c.data_ptr()
         args.M, args.N, args.K = M, N, K
+        batch = c.shape[0] if c.dim() == 3 else 1
+        if batch > 1:   # contiguous [batch, ...] operands
+            args.batch = batch
+            args.stride_a, args.stride_b, args.stride_c = a.stride(0), b.stride(0), c.stride(0)
         args.layout = dg.layout_word(b_layout, "bf16" if a.dtype == torch.bfloat16 else "fp16")
         # `atomic`: False, True, "two_pass" (partials of split tiles added by a
         # second kernel) or "in_launch" (added in the launch: Split-K last arriver,
@@ -87,7 +91,7 @@ class Call:
         self.stream = stream or torch.cuda.current_stream()
         args.stream = self.stream.cuda_stream
         self.args = args
-        self.plan = dg.gemm_plan(M, N, K, args.layout, args.mode, splits, dg.gemm_num_cus())
+        self.plan = dg.gemm_plan_batched(M, N, K, batch, args.layout, args.mode, splits, dg.gemm_num_cus())
 
     def __call__(self):
         st = self.dg.gemm_ex(self.args)
@@ -142,7 +146,7 @@ def shape_arms(dg, name, steps, warmup):
     w = WORKLOADS[name]
     A, B = make_operands(w)
     a, b = A.cuda(), B.cuda()
-    c = torch.zeros((w.M, w.N), dtype=torch.float32, device="cuda")
+    c = torch.zeros(((w.batch,) if w.batch > 1 else ()) + (w.M, w.N), dtype=torch.float32, device="cuda")
     bias = torch.linspace(-1.0, 1.0, w.N, dtype=torch.float32, device="cuda")
     epi = (0.75, -0.5, bias, "gelu")   # alpha, beta, bias, activation of the "_epilogue" arms
     arms = {"dp": ("dp", 0, False)}
@@ -173,7 +177,13 @@ def shape_arms(dg, name, steps, warmup):
     if name.startswith("x1"):
         arms["heuristic"] = ("heuristic", 0, False)
         arms["streamk"] = ("streamk", 0, False)
+    if name.startswith("x2"):
+        arms["heuristic"] = ("heuristic", 0, False)
+        arms["streamk"] = ("streamk", 0, False)
+        arms["heuristic_epilogue"] = ("heuristic", 0, False, epi)
     out = {"M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype, "b_layout": w.b_layout}
+    if w.batch > 1:
+        out["batch"] = w.batch
     for arm, (mode, splits, atomic, *ep) in arms.items():
         call = Call(dg, a, b, c, w.b_layout, mode, splits, atomic, epilogue=ep[0] if ep else None)
         st = steps if not name.startswith("c4") else max(5, steps // 10)
@@ -303,7 +313,7 @@ def main():
                     atomic=args.atomic)
     A, B = make_operands(w)
     a, b = A.cuda(), B.cuda()
-    c = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    c = torch.empty(((w.batch,) if w.batch > 1 else ()) + (w.M, w.N), dtype=torch.float32, device="cuda")
     call = Call(dg, a, b, c, w.b_layout, w.mode, w.splits, w.atomic)
     log(f"bench: {w.name} {w.M}x{w.N}x{w.K} {w.dtype} plan={dg.plan_dict(call.plan)['decision_name']} "
         f"units={call.plan.sk_units} steps={args.steps} warmup={args.warmup}")
@@ -334,7 +344,7 @@ def main():
     shapes = {}
     if not args.no_shapes:
         for name in ("c3_wavequant", "c1_sk32", "c2a_m96_s8", "c2b_m256_s2", "c5_longk_fp16", "c4_large_dp",
-                     "x1_hybrid"):
+                     "x1_hybrid", "x2_batched"):
             shapes[name] = shape_arms(dg, name, args.shape_steps, 10)
     c3 = shapes.get("c3_wavequant", {})
     speedups = {}

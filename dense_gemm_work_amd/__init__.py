@@ -115,6 +115,14 @@ def library_path() -> Path:
 
 
 def _load() -> ctypes.CDLL:
+    # torch ships its own HIP runtime under the same soname (libamdhip64.so.7).
+    # Loading torch first makes the library bind to that one; loading the
+    # library first would bring in the system runtime as a second HIP runtime
+    # in the process, and torch would then not see the GPU.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not _LIB_PATH.exists():
         raise ImportError(
             f"{_LIB_PATH} is not built; run __graft_entry__.build() (or python3 "

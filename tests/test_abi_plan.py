@@ -6,6 +6,7 @@ import importlib.util
 import itertools
 import re
 import subprocess
+import sys
 from pathlib import Path
 
 import pytest
@@ -327,3 +328,17 @@ def test_streamk_two_pass_plan(dg):
     assert (c3.two_pass, c3t.two_pass, c5.two_pass, c1.two_pass, c1a.two_pass) == (0, 1, 0, 1, 0)
     assert c3t.workspace_bytes - c3.workspace_bytes == 256 * 128 * 128 * 4
     assert (c3t.q, c3t.big, c3t.sk_units) == (c3.q, c3.big, c3.sk_units)
+
+
+def test_binding_uses_one_hip_runtime(tmp_path):
+    # importing the package first must not load a second HIP runtime next to
+    # torch's (torch would then not see the GPU)
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import dense_gemm_work_amd\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "libs = {l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}\n"
+            "print(len(libs))\n") % str(ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1"

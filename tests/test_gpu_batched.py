@@ -175,3 +175,18 @@ def test_batched_rejects_bad_strides(dg):
     assert dg.gemm_ex(args) == dg.GEMM_ERR_INVALID
     args.stride_c = M * N + 2                                              # breaks 16-byte alignment
     assert dg.gemm_ex(args) == dg.GEMM_ERR_UNSUPPORTED
+
+
+def test_x2_batched_workload(dg):
+    # the benchmark's batched workload at full size: 5 x (1024x1024x2048), heuristic
+    w = WORKLOADS["x2_batched"]
+    p = dg.gemm_plan_batched(w.M, w.N, w.K, w.batch, 0, dg.GEMM_HEURISTIC, 0, 256)
+    assert (dg.DECISION_NAMES[p.decision], p.sk_units, p.tiles, p.q) == ("StreamK", 256, 320, 40)
+    A, B = make_operands(w)
+    assert tuple(A.shape) == (5, 1024, 2048) and tuple(B.shape) == (5, 2048, 1024)
+    full, c, stride = _strided_c(w.batch, w.M, w.N, 0)
+    say("  x2_batched")
+    dg.gemm_tensors(A.to(DEV), B.to(DEV), c, b_layout=w.b_layout)
+    assert dg.gemm_sync_status() == 0, dg.gemm_last_error()
+    assert _guards_ok(full, w.batch, w.M, w.N, stride)
+    _check_entries(A, B, c, w, w.batch, False, rows=[0, 1, 127, 128, 511, 640, 1000, 1023])

@@ -56,10 +56,11 @@ class Workload:
     splits: int = 0              # Split-K factor or Stream-K unit count (0 = one per CU)
     atomic: bool = False         # nondeterministic (atomic) fixup for Stream-K
     note: str = ""
+    batch: int = 1               # independent products of this shape (operands [batch, ...])
 
     @property
     def flops(self) -> int:
-        return 2 * self.M * self.N * self.K
+        return 2 * self.M * self.N * self.K * self.batch
 
     def b_shape(self):
         return (self.K, self.N) if self.b_layout == "kn" else (self.N, self.K)
@@ -97,6 +98,11 @@ WORKLOADS = {
     # go to 256 Stream-K units of 72 iterations.
     "x1_hybrid": Workload("x1_hybrid", 4096, 4224, 4096, "bf16", "kn", "uniform", -1.0, 1.0,
                           mode="heuristic", note="1056 tiles; heuristic -> 768 DP tiles + Stream-K over 288"),
+    # A wave-quantized batch: 5 x (1024x1024x2048) = 320 tiles (one full wave + a
+    # 64-tile tail on 256 CUs) x 32 iterations.
+    "x2_batched": Workload("x2_batched", 1024, 1024, 2048, "bf16", "kn", "uniform", -1.0, 1.0,
+                           mode="heuristic", batch=5,
+                           note="5 entries x 64 tiles x 32 iters; heuristic -> Stream-K, 256 units x 40 iterations"),
 }
 
 
@@ -124,20 +130,22 @@ def make_operands(w: Workload, seed: Optional[int] = None):
     """Return ``(A, B)`` as CPU torch tensors in the workload's 16-bit dtype.
 
     A has shape ``[M, K]``; B has shape ``[K, N]`` (layout "kn") or ``[N, K]``
-    (layout "nk").  Both are contiguous.
+    (layout "nk"); with ``batch > 1`` both gain a leading batch dimension (all
+    of A drawn before all of B).  Both are contiguous.
     """
     rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
     td = _torch_dtype(w.dtype)
-    a64 = _draw(rng, w, (w.M, w.K))
-    b64 = _draw(rng, w, w.b_shape())
+    lead = (w.batch,) if w.batch > 1 else ()
+    a64 = _draw(rng, w, lead + (w.M, w.K))
+    b64 = _draw(rng, w, lead + tuple(w.b_shape()))
     A = torch.from_numpy(a64.astype(np.float32)).to(td)
     del a64
     B = torch.from_numpy(b64.astype(np.float32)).to(td)
     del b64
     if w.M > 0 and w.zero_first_row:
-        A[0].zero_()
+        A[..., 0, :].zero_()
     if w.M > 0 and w.scale_last_row != 1.0:
-        A[w.M - 1] = (A[w.M - 1].float() * w.scale_last_row).to(td)
+        A[..., w.M - 1, :] = (A[..., w.M - 1, :].float() * w.scale_last_row).to(td)
     return A.contiguous(), B.contiguous()
 
 
