@@ -227,6 +227,66 @@ def measured_traffic(profile: str, kernel: str):
     return int(entry["bytes"])
 
 
+def _power_sensor():
+    """The board power file (microwatts) and cap of the first GPU hwmon, or None."""
+    import glob
+
+    for d in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
+        p = os.path.join(d, "power1_input")
+        if os.access(p, os.R_OK):
+            cap = os.path.join(d, "power1_cap")
+            cap_w = int(open(cap).read()) / 1e6 if os.access(cap, os.R_OK) else None
+            return p, cap_w
+    return None, None
+
+
+def power_snapshot(dg, name, mode, splits=0, atomic=False, seconds=1.5):
+    """Board power while `name` runs back to back for about `seconds` (sampled
+    every 10 ms from the GPU's hwmon power1_input), next to the power cap."""
+    import threading
+
+    import torch
+    from workloads import WORKLOADS, make_operands
+
+    path, cap_w = _power_sensor()
+    if path is None:
+        return None
+    w = WORKLOADS[name]
+    A, B = make_operands(w)
+    a, b = A.cuda(), B.cuda()
+    c = torch.empty(((w.batch,) if w.batch > 1 else ()) + (w.M, w.N), dtype=torch.float32, device="cuda")
+    call = Call(dg, a, b, c, w.b_layout, mode, splits, atomic)
+    for _ in range(20):
+        call()
+    torch.cuda.synchronize()
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                samples.append(int(open(path).read()) / 1e6)
+            except (OSError, ValueError):
+                pass
+            stop.wait(0.01)
+
+    th = threading.Thread(target=sample, daemon=True)
+    t0 = time.perf_counter()
+    calls = 0
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            call()
+        calls += 20
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    steady = sorted(samples[len(samples) // 4:]) or sorted(samples)   # past the ramp-up
+    return {"watts_median": round(steady[len(steady) // 2], 1), "watts_max": round(max(samples), 1),
+            "cap_watts": cap_w, "samples": len(samples), "calls": calls}
+
+
 def cu_timeline(dg, name, mode, splits=0, atomic=False):
     """Per-CU busy time of one launch with the kernels' timing records (every
     workgroup stores its start and end on the 100 MHz clock plus the CU it ran
@@ -362,6 +422,13 @@ def main():
             timeline[key] = cu_timeline(dg, name, mode, splits, atomic)
             log(f"  timeline {key:11s} {timeline[key]}")
 
+    power = {}
+    if not args.no_timeline:
+        for key, (name, mode) in {"c3_streamk": ("c3_wavequant", "heuristic"),
+                                  "c4_dp": ("c4_large_dp", "heuristic")}.items():
+            power[key] = power_snapshot(dg, name, mode)
+            log(f"  power {key:11s} {power[key]}")
+
     cpu = None
     if not args.no_cpu:
         log("bench: timing the fp64 CPU oracle on the same workload")
@@ -403,6 +470,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "cu_timeline": timeline,
+        "power": power,
         "shapes": shapes,
     }
     print(json.dumps(line), flush=True)
