@@ -62,6 +62,7 @@ ACTIVATIONS = {"none": 0, "relu": GEMM_EPI_RELU, "gelu": GEMM_EPI_GELU}
 GEMM_DEBUG_NO_PUBLISH = 0x1
 GEMM_DEBUG_IN_LAUNCH = 0x4
 GEMM_DEBUG_TILE_DP = 0x8
+GEMM_DEBUG_HYBRID_SPLIT = 0x10
 
 GEMM_BM = 128
 GEMM_BN = 128

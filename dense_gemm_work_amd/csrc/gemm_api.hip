@@ -230,7 +230,7 @@ int run(const gemm_args_t &a) {
                             a.num_cus > 0 ? a.num_cus : 256, &p, &why);
     if (rc != GEMM_OK) return fail(rc, why);
     if (a.num_cus < 0) return fail(GEMM_ERR_INVALID, "num_cus must be >= 0");
-    if ((a.debug & ~(GEMM_DEBUG_NO_PUBLISH | GEMM_DEBUG_IN_LAUNCH | GEMM_DEBUG_TILE_DP)) != 0)
+    if ((a.debug & ~(GEMM_DEBUG_NO_PUBLISH | GEMM_DEBUG_IN_LAUNCH | GEMM_DEBUG_TILE_DP | GEMM_DEBUG_HYBRID_SPLIT)) != 0)
         return fail(GEMM_ERR_INVALID, "unknown debug bits");
     if ((rc = check_epilogue(a)) != GEMM_OK) return rc;
     if (a.M == 0 || a.N == 0) return GEMM_OK;
@@ -405,6 +405,10 @@ int run(const gemm_args_t &a) {
         kp.q = (int)p.q;
         kp.big = (int)p.big;
         kp.tile_base = (int)p.dp_tiles;
+        // hybrid: the persistent units run the data-parallel tiles first, in the
+        // same launch (GEMM_DEBUG_HYBRID_SPLIT: a second launch after it)
+        const bool split_hybrid = (a.debug & GEMM_DEBUG_HYBRID_SPLIT) != 0;
+        kp.dp_tiles = split_hybrid ? 0 : (int)p.dp_tiles;
         const bool two_pass = p.two_pass && !(a.debug & GEMM_DEBUG_IN_LAUNCH);
         kp.merge = two_pass ? dgw::MERGE_TWO_PASS : dgw::MERGE_IN_LAUNCH;
         if ((e = dgw::launch_gemm(dtype, blayout, kmode, (int)p.sk_units, kp, stream)) != hipSuccess)
@@ -415,8 +419,8 @@ int run(const gemm_args_t &a) {
             if ((e = dgw::launch_streamk_reduce(rp, p.sk_tiles, stream)) != hipSuccess)
                 return fail_hip(e, "launch Stream-K reduction");
         }
-        if (p.dp_tiles > 0) {
-            // hybrid: the first dp_tiles tiles run as whole-K tiles
+        if (p.dp_tiles > 0 && split_hybrid) {
+            // hybrid, second launch: the first dp_tiles tiles run as whole-K tiles
             KParams dp = kp;
             dp.tile_base = 0;
             dp.ntiles = (int)p.dp_tiles;

@@ -1714,6 +1714,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
     const int ipt = p.ipt;
     const int begin = unit_start(u, p.q, p.big);
     const int end = begin + p.q + (u < p.big ? 1 : 0);
+    // Hybrid: the units first run the data-parallel tiles [0, dp_tiles), unit u
+    // the tiles u, u + units, ... (whole K, stored directly; traced as the DP
+    // workers units + tile), then their Stream-K ranges over the last tiles.
+    for (int tile = u; tile < p.dp_tiles; tile += p.units) {
+        int m0, n0;
+        const KParams pv = tile_view(p, tile, m0, n0);
+        Acc acc;
+        zero_acc(acc);
+        mac_loop<DT, BL, NS, NW>(pv, lds, m0, n0, 0, ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
+        const Tile<NW> t = merge_k_halves<NW>(acc, lds);
+        trace_segment(p, p.units + tile, 0, tile, 0, ipt, 0);
+        store_final<NW, EPI>(pv, m0, n0, t);
+        trace_folded(p, tile, 0, p.units + tile);
+    }
     int nseg = 0;
     uint32_t *pending = nullptr;   // a published partial whose flag rises in the next segment's loop
     for (int pos = begin; pos < end;) {

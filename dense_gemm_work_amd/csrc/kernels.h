@@ -51,6 +51,7 @@ struct KParams {
     int xcd_spread;        // 1: give each XCD a contiguous range of workers
     int ipt;               // k-iterations per tile
     int tile_base;         // first tile id of this launch (hybrid: Stream-K part starts at dp_tiles)
+    int dp_tiles;          // Stream-K launch of a hybrid: whole-K tiles [0, dp_tiles) the units run first
     int ntiles;            // tiles of a DP / Split-K launch
     int units, q, big;     // Stream-K unit ranges: unit u starts at u*q + min(u, big)
     int splits;            // Split-K factor S

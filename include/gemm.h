@@ -48,8 +48,9 @@
  *                 DP if there is no partial wave or P <= 8; DP if the tail wave
  *                 is at least half full; otherwise Stream-K over the last two
  *                 waves with at least 8 iterations per unit (the earlier waves
- *                 stay DP), or Split-K when those units divide evenly over the
- *                 Stream-K tiles.
+ *                 stay DP: the persistent units run those whole-K tiles first,
+ *                 in the same launch), or Split-K when those units divide
+ *                 evenly over the Stream-K tiles.
  *
  * Threading and streams: every call is asynchronous on a HIP stream (the one
  * given to gemm_ex, else the calling thread's stream from gemm_set_stream,
@@ -110,6 +111,9 @@ extern "C" {
                                     kernel.  Same result bits; exercises that path. */
 #define GEMM_DEBUG_TILE_DP 0x8u /* data-parallel launches run one 128x128 tile per
                                    workgroup even where 2x2 tile groups apply.     */
+#define GEMM_DEBUG_HYBRID_SPLIT 0x10u /* a hybrid's data-parallel tiles run as a second
+                                         launch after the Stream-K one instead of by
+                                         the persistent units first.  Same values.  */
 
 /* ---- epilogue word for gemm_args_t.epilogue ------------------------------------------ */
 /*
@@ -195,8 +199,9 @@ typedef struct gemm_plan_t {
  *   spin_limit: bound on every inter-workgroup wait, in polls (0 = default).
  *   debug:    GEMM_DEBUG_* bits (0 in normal use).
  *   timing:   optional device int64 buffer of at least 8 * plan.workers elements:
- *             workgroup g of the call (launch order: the main grid, then the DP
- *             tiles of a hybrid) writes {start, end, HW_ID | XCC_ID << 32, cycles,
+ *             workgroup g of the call (launch order: the main grid, then, with
+ *             GEMM_DEBUG_HYBRID_SPLIT, the DP tiles of a hybrid) writes
+ *             {start, end, HW_ID | XCC_ID << 32, cycles,
  *             m0, m1, m2, m3}: times in ticks of the 100 MHz s_memrealtime clock,
  *             HW_ID and XCC_ID as read from the hardware registers (CU, SE and XCD
  *             placement), cycles = shader-clock ticks (s_memtime) from start to end,

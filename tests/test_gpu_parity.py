@@ -475,3 +475,28 @@ def test_caller_workspace(dg):
     with pytest.raises(dg.GemmError) as ei:
         dg.gemm_tensors(A.to(DEV), B.to(DEV), c, mode="streamk", splits=32, workspace=small)
     assert ei.value.status == dg.GEMM_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("M,N,K,cus", [(1408, 768, 1024, 20), (4096, 4224, 4096, 256)])
+def test_hybrid_single_launch_equals_two_launches(dg, M, N, K, cus):
+    # the persistent units run the hybrid's data-parallel tiles first, in the
+    # Stream-K launch; GEMM_DEBUG_HYBRID_SPLIT runs them as a second launch.
+    # Same tiles, same k order: the same bits, and the same trace.
+    w = WORKLOADS["x1_hybrid"].with_(name="hybrid", M=M, N=N, K=K)
+    p = dg.gemm_plan(M, N, K, 0, dg.GEMM_HEURISTIC, 0, cus)
+    assert dg.DECISION_NAMES[p.decision] == "StreamK" and p.dp_tiles > 0
+    A, B = make_operands(w)
+    a, b = A.to(DEV), B.to(DEV)
+    outs, traces = [], []
+    for debug in (0, dg.GEMM_DEBUG_HYBRID_SPLIT):
+        c = torch.full((M, N), 7.0, dtype=torch.float32, device=DEV)
+        tr = torch.zeros(p.trace_ints, dtype=torch.int32, device=DEV)
+        say(f"  hybrid {M}x{N}x{K} cus={cus} debug={debug}")
+        dg.gemm_tensors(a, b, c, num_cus=cus, trace=tr, debug=debug)
+        assert dg.gemm_sync_status() == 0
+        outs.append(c.cpu())
+        traces.append(decode_trace(tr))
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    assert traces[0]["segments"] == traces[1]["segments"] and traces[0]["folds"] == traces[1]["folds"]
+    assert np.all(traces[0]["coverage"] == 1)
+    assert_parity(outs[0], A, B, w, rows=sample_rows(M, 8))
