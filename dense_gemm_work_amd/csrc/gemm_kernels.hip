@@ -1780,7 +1780,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
             int pos_fold = 1;
             for (int v = u + 1; v < p.units; ++v) {
                 if (unit_start(v, p.q, p.big) >= tile_end) break;
-                if (threadIdx.x == 0) wait_flag(p.flags + v, p.epoch, p.spin_limit, p.status);
+                if (threadIdx.x == 0) {
+                    wait_flag(p.flags + v, p.epoch, p.spin_limit, p.status);
+                    // each flag has this one reader: clear it once seen, so every
+                    // call starts with the flags at zero, also the replays of a
+                    // captured graph, whose epoch is fixed at capture
+                    __hip_atomic_store(p.flags + v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
                 __syncthreads();
                 add_slot<NW>(p.part + (size_t)v * (BM * BN), t);
                 trace_folded(p, tile, pos_fold++, v);

@@ -58,6 +58,11 @@
  * calls that use it must be ordered on the device (one stream, or streams
  * synchronised by the caller).  Calls that overlap on one device race.
  *
+ * Graph capture: a call enqueues kernels only (no memset or copy), so it can be
+ * captured in a HIP graph once an eager call with the same plan has sized the
+ * library workspace (or with a caller workspace); replays must not overlap.
+ * Stream-K flags clear themselves after use, so the replays' fixed epoch works.
+ *
  * Errors: a negative status is returned and nothing is launched (C untouched)
  * for every condition the host can detect; gemm_last_error() then describes it.
  */
