@@ -43,9 +43,9 @@ def _operands(w, batch, share_b=False):
 
 
 def _strided_c(batch, M, N, pad):
-    """A [batch, M, N] view whose entries are M*N + pad elements apart inside a
-    buffer poisoned with 7 and guarded (pads and tail) with 11."""
-    stride = M * N + pad
+    """A [batch, M, N] view whose entries are M*N (rounded up to 4) + pad elements
+    apart inside a buffer poisoned with 7 and guarded (pads and tail) with 11."""
+    stride = (M * N + 3) // 4 * 4 + pad      # entries 16-byte aligned
     full = torch.full((batch * stride + 64,), GUARD, dtype=torch.float32, device=DEV)
     c = torch.as_strided(full, (batch, M, N), (stride, N, 1))
     c.fill_(POISON)
@@ -190,3 +190,75 @@ def test_x2_batched_workload(dg):
     assert dg.gemm_sync_status() == 0, dg.gemm_last_error()
     assert _guards_ok(full, w.batch, w.M, w.N, stride)
     _check_entries(A, B, c, w, w.batch, False, rows=[0, 1, 127, 128, 511, 640, 1000, 1023])
+
+
+def _random_batched_cases(n, seed=23):
+    """Seeded random batched problems with random epilogues: shape, layout, dtype,
+    batch, C padding, a shared B, decomposition, merge mode, CU count."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        layout = str(rng.choice(["kn", "nk"]))
+        M = int(rng.integers(1, 400))
+        N = int(rng.integers(1, 50)) * 8 if layout == "kn" else int(rng.integers(1, 400))
+        K = int(rng.integers(1, 30)) * 8
+        dtype = str(rng.choice(["bf16", "fp16"]))
+        batch = int(rng.integers(1, 5))
+        pad = int(rng.integers(0, 4)) * 4
+        share_b = bool(rng.integers(0, 2))
+        mode = str(rng.choice(["dp", "splitk", "streamk", "heuristic"]))
+        cus = int(rng.choice([0, 4, 16]))
+        ipt = -(-K // 64)
+        splits, atomic, two_pass = 0, False, False
+        if mode == "splitk":
+            splits = int(rng.choice([s for s in range(1, 9) if ipt % s == 0]))
+            merge = int(rng.integers(0, 3))
+            atomic, two_pass = merge == 1, merge == 2
+        elif mode == "streamk":
+            splits = int(rng.integers(1, 24))
+            atomic = bool(rng.integers(0, 2))
+        kind = int(rng.integers(0, 5))
+        epi = [None, (1.5, 0.0, "none"), (-0.5, 0.75, "relu"), (0.75, -1.25, "gelu"), (1.0, 1.0, "gelu")][kind]
+        use_bias = bool(rng.integers(0, 2)) and epi is not None
+        cases.append((i, M, N, K, layout, dtype, batch, pad, share_b, mode, splits, atomic, two_pass, cus, epi,
+                      use_bias))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_batched_cases(20), ids=lambda c: f"rb{c[0]}")
+def test_random_batched_epilogue(dg, case):
+    i, M, N, K, layout, dtype, batch, pad, share_b, mode, splits, atomic, two_pass, cus, epi, use_bias = case
+    dist = dict(dist="uniform", low=-1.0, high=1.0) if dtype == "bf16" else dict(dist="uniform", low=-0.5, high=0.5)
+    w = WORKLOADS["c1_sk32"].with_(name=f"rb{i}", M=M, N=N, K=K, b_layout=layout, dtype=dtype, **dist)
+    if mode == "streamk":
+        splits = min(splits, dg.gemm_num_cus() if cus == 0 else cus)
+    A, B = _operands(w, batch, share_b)
+    if batch == 1:
+        A = A[0]
+    full, c, stride = _strided_c(batch, M, N, pad)
+    c_in, bias = make_epilogue_inputs(batch * M, N, seed=200 + i)
+    c_in = c_in.view(batch, M, N)
+    kw = {}
+    if epi is not None:
+        c.copy_(c_in.to(DEV))
+        kw = dict(alpha=epi[0], beta=epi[1], act=epi[2], bias=bias.to(DEV) if use_bias else None)
+    cc = c if batch > 1 else c[0]
+    say(f"  rb{i}: batch={batch} {M}x{N}x{K} {dtype} {layout} pad={pad} share_b={share_b} mode={mode} "
+        f"splits={splits} atomic={atomic} two_pass={two_pass} cus={cus} epi={epi} bias={use_bias}")
+    dg.gemm_tensors(A.to(DEV), B.to(DEV), cc, b_layout=layout, mode=mode, splits=splits, atomic=atomic,
+                    two_pass=two_pass, num_cus=cus, **kw)
+    assert dg.gemm_sync_status() == 0, dg.gemm_last_error()
+    assert _guards_ok(full, batch, M, N, stride), "a pad or the guard band was overwritten"
+    for b in range(batch):
+        Ab = A if batch == 1 else A[b]
+        Bb = B if share_b else B[b]
+        P, S = og.ref_gemm(Ab, Bb, M, N, K, layout, dtype)
+        got = c[b].cpu().numpy().astype(np.float64)
+        if epi is None:
+            ok, worst, idx = og.within_tolerance(got, P, S)
+        else:
+            c0 = c_in[b].numpy().astype(np.float64) if epi[1] != 0.0 else None
+            b64 = bias.numpy().astype(np.float64) if use_bias else None
+            D, _ = oe.epilogue_ref(P, c0, epi[0], epi[1], b64, epi[2])
+            ok, worst, idx = oe.within_bound(got, D, oe.epilogue_bound(S, P, c0, epi[0], epi[1], b64, epi[2]))
+        assert ok, f"entry {b}: worst ratio {worst} at {idx}"
