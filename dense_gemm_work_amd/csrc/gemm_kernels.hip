@@ -772,6 +772,45 @@ __device__ __forceinline__ void lane_bias(const KParams &p, int C0, float (&bj)[
     }
 }
 
+// The epilogue inputs of the one 32-row block an 8-wave tile's wave holds after
+// merge_k_halves (block row kh of its quarter): prior C values and the
+// column's bias.  Loaded early (before the k-half merge and any fixup), they
+// arrive while the tile is still being completed.
+__device__ __forceinline__ void epi_prefetch(const KParams &p, int m0, int n0, float (&cin)[32], float (&bj)[2]) {
+    const Role<8> w;
+    const int C0 = n0 + w.wn * 64;
+    lane_bias<2>(p, C0, bj);
+    const CBlock<2> cb(p, m0 + w.wm * 64 + w.kh * 32, C0);
+    const bool rc = reads_c(p);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) cin[j * 16 + e] = rc ? cb.load(e, j) : 0.0f;
+}
+
+// The epilogue and the stores of one held 32-row block (row r of the tile),
+// its prior C values and bias values given.
+template <int NW>
+__device__ __forceinline__ void finish_block(const KParams &p, int m0, int n0, const Tile<NW> &t, int r,
+                                             const float (&cin)[32], const float (&bj)[2]) {
+    const Role<NW> w;
+    const CBlock<2> cb(p, m0 + w.wm * 64 + t.i[r] * 32, n0 + w.wn * 64);
+    float v[32], c[32], bv[32];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            v[j * 16 + e] = t.v[r][j][e];
+            c[j * 16 + e] = cin[j * 16 + e];
+            bv[j * 16 + e] = bj[j];
+        }
+    finish<32>(p, v, c, bv);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) cb.store(e, j, v[j * 16 + e]);
+}
+
 // store_tile with the epilogue: the prior C values of the held rows are loaded
 // before the first store.
 template <int NW, bool EPI = true>
@@ -788,26 +827,12 @@ __device__ __forceinline__ void store_final(const KParams &p, int m0, int n0, co
 #pragma unroll
     for (int r = 0; r < Tile<NW>::R; ++r) {
         const CBlock<2> cb(p, m0 + w.wm * 64 + t.i[r] * 32, C0);
-        float v[32], cin[32], bv[32];
+        float cin[32];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                v[j * 16 + e] = t.v[r][j][e];
-                bv[j * 16 + e] = bj[j];
-                cin[j * 16 + e] = 0.0f;
-            }
-        if (rc) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) cin[j * 16 + e] = cb.load(e, j);
-        }
-        finish<32>(p, v, cin, bv);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) cb.store(e, j, v[j * 16 + e]);
+            for (int e = 0; e < 16; ++e) cin[j * 16 + e] = rc ? cb.load(e, j) : 0.0f;
+        finish_block<NW>(p, m0, n0, t, r, cin, bj);
     }
 }
 
@@ -1746,6 +1771,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         mac_loop<DT, BL, NS, NW>(pv, lds, m0, n0, k0, k1, rot, acc, p.trace ? trace_cov(p, tile) : nullptr,
                                  pending);
         pending = nullptr;
+        // a segment that stores C: with the epilogue, its inputs are loaded now,
+        // while the k-halves merge and any peers are waited for and added
+        const bool stores_c = role == 0 || (role == 1 && !ATOMIC && p.merge != MERGE_TWO_PASS);
+        float pre_c[32], pre_b[2];
+        if constexpr (EPI) {
+            static_assert(NW == 8, "the prefetch assumes one 32-row block per wave");
+            if (stores_c && p.epi != EPI_PLAIN) epi_prefetch(pv, m0, n0, pre_c, pre_b);
+        }
         Tile<NW> t = merge_k_halves<NW>(acc, lds);
         clk.mark(p, 2 * min(nseg, 1));
         trace_segment(p, u, nseg++, tile, k0, k1, role);
@@ -1796,7 +1829,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         // the epilogue build stores whole tiles and folded tiles from one call
         // site (one inlined copy of the epilogue code)
         if constexpr (EPI) {
-            if (role == 0 || (role == 1 && !ATOMIC && p.merge != MERGE_TWO_PASS)) store_final<NW, true>(pv, m0, n0, t);
+            if (stores_c) {
+                if (p.epi == EPI_PLAIN) store_tile<NW>(pv.C, m0, n0, p.M, p.N, t);
+                else finish_block<NW>(pv, m0, n0, t, 0, pre_c, pre_b);
+            }
         }
         clk.mark(p, 2 * min(nseg - 1, 1) + 1);
         pos = tb + k1;
