@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import gemm as og
 from oracle import schedule as sch
 from workloads import WORKLOADS, make_operands
 
@@ -500,3 +501,24 @@ def test_hybrid_single_launch_equals_two_launches(dg, M, N, K, cus):
     assert traces[0]["segments"] == traces[1]["segments"] and traces[0]["folds"] == traces[1]["folds"]
     assert np.all(traces[0]["coverage"] == 1)
     assert_parity(outs[0], A, B, w, rows=sample_rows(M, 8))
+
+
+@pytest.mark.parametrize("M,N,K,mode", [(65536, 33024, 64, "heuristic"), (40960, 53248, 512, "streamk")])
+def test_outputs_beyond_2_to_the_31_elements(dg, M, N, K, mode):
+    # C holds more than 2^31 fp32 elements (8.6 / 8.7 GB): every output offset
+    # past 2^31 must be formed in 64 bits; rows near the end are checked
+    w = WORKLOADS["c1_sk32"].with_(name="large", M=M, N=N, K=K)
+    assert M * N > 2 ** 31
+    A, B = make_operands(w)
+    c = torch.full((M, N), 7.0, dtype=torch.float32, device=DEV)
+    say(f"  large {M}x{N}x{K} {mode}")
+    dg.gemm_tensors(A.to(DEV), B.to(DEV), c, mode=mode)
+    assert dg.gemm_sync_status() == 0, dg.gemm_last_error()
+    rows = [0, 1, M // 2, 2 ** 31 // N + 1, M - 129, M - 2, M - 1]
+    got = c[torch.tensor(rows, device=DEV)].cpu().numpy().astype(np.float64)   # only the checked rows
+    del c
+    torch.cuda.empty_cache()
+    C, S = og.ref_gemm(A, B, M, N, K, "kn", "bf16", rows=rows)
+    ok, worst, idx = og.within_tolerance(got, C, S)
+    say(f"    worst err/bound = {worst:.3e} at {idx}")
+    assert ok, f"outside tolerance: worst ratio {worst} at {idx}"
