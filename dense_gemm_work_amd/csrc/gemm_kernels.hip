@@ -29,7 +29,7 @@
 // reduction modes; docc StreamK page):
 //   K_DP         store the tile.
 //   K_DP_GROUP   store the four tiles of the group.
-//   K_SPLITK     store the fp32 partial into P[s] of [S,M,N]; then either arrive
+//   K_SPLITK     store the fp32 partial into P[s] of [batch][S,M,N]; then either arrive
 //                at the tile's counter, the last arriver summing P[0..S-1] in
 //                split order (its own split from LDS) and storing C, or leave
 //                the sum to splitk_reduce (two-pass), or (atomic) add the
@@ -43,6 +43,11 @@
 //                (two slots per unit) and streamk_reduce adds them in k order.
 //   K_SK_ATOMIC  whole tiles are stored; every other segment atomically adds its
 //                accumulator into C (zero-filled by the host first).
+// In a hybrid plan the Stream-K units first run the data-parallel tiles, whole
+// K, before their Stream-K ranges.  Every final store can apply the fused
+// epilogue act(alpha acc + beta C + bias) (CUTLASS optimisation guide,
+// "Epilogue Optimization"); batched calls number their tiles entry after
+// entry and each tile's kernel code addresses its entry's operands.
 //
 // Every wait is bounded by spin_limit polls; on expiry the status word records
 // STATUS_TIMEOUT and the kernel goes on, so every wave always exits.
