@@ -209,20 +209,31 @@ def kernel_name(dg, plan, w):
     return f"{kind}<{w.dtype}, {lay}{fix}>"
 
 
+def kernel_code_digest(path=None) -> str:
+    """sha256 of the kernel source with comments removed and whitespace runs
+    collapsed: it changes with the code, not with its comments."""
+    import hashlib
+    import re
+
+    path = path or ROOT / "dense_gemm_work_amd" / "csrc" / "gemm_kernels.hip"
+    text = Path(path).read_text()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def measured_traffic(profile: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary `profile` (scaled by a plain copy of known size), or None
-    when there is none or the kernel source has changed since it was taken."""
-    import hashlib
-
+    when there is none or the kernel code has changed since it was taken."""
     path = ROOT / "profiles" / "traffic.json"
     if not path.exists():
         return None
     entry = json.loads(path.read_text()).get(profile)
     if not entry or kernel not in entry.get("kernel", ""):
         return None
-    src = ROOT / "dense_gemm_work_amd" / "csrc" / "gemm_kernels.hip"
-    if hashlib.sha256(src.read_bytes()).hexdigest() != entry.get("source_sha256"):
+    if kernel_code_digest() != entry.get("code_sha256"):
         return None
     return int(entry["bytes"])
 
