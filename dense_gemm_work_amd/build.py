@@ -50,7 +50,27 @@ def build(verbose: bool = False) -> Path:
     if verbose and noise:
         print("\n".join(noise[-40:]))
     os.replace(tmp, LIB)
+    build_example(verbose)
     return LIB
+
+
+EXAMPLE_SRC = PKG / "examples" / "gemm_c_api.c"
+EXAMPLE_BIN = PKG / "examples" / "gemm_c_api"
+
+
+def build_example(verbose: bool = False) -> Path:
+    """The plain-C usage example, linked against the in-tree library (host code
+    only; the platform macro is what the HIP runtime headers ask of C code)."""
+    rocm_include = Path(hipcc()).resolve().parent.parent / "include"
+    cmd = [hipcc(), "-x", "c", "-O2", "-D__HIP_PLATFORM_AMD__", f"-I{rocm_include}", str(EXAMPLE_SRC), f"-L{PKG}",
+           "-ldgw_gemm",
+           "-Wl,-rpath,$ORIGIN/..", "-o", str(EXAMPLE_BIN)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True, cwd=str(PKG))
+    if res.returncode != 0:
+        raise RuntimeError(f"example build failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stderr[-4000:]}")
+    return EXAMPLE_BIN
 
 
 def is_stale() -> bool:
