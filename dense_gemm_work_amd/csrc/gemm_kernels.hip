@@ -131,6 +131,11 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
 // offset beyond the range.
 constexpr uint32_t OOB = 0x7ffffff0u;        // an offset outside every buffer range used here
 constexpr uint32_t RSRC_DW3 = 0x00020000u;    // raw buffer, 32-bit data format
+// Cache policy of the final C stores: non-temporal.  C is written once and not
+// read again by the call, so it should not displace the A and B panels that
+// neighbouring tiles still read from L2 (measured: 8192^3 2.8 %, the
+// 2048x2176x4096 Stream-K call 1.5 % faster).
+constexpr int CPOL_NT = 2;
 
 __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -636,10 +641,10 @@ __device__ __forceinline__ void put_quad(float *dst, f32x4 v, int nvalid, bool v
 }
 
 // Write the held rows to C straight from registers: each store instruction
-// writes two 128-byte row segments (lanes 0-31 and 32-63).
+// writes two 128-byte row segments (lanes 0-31 and 32-63), non-temporal.
 template <int NW>
 __device__ __forceinline__ void store_tile(float *X, int m0, int n0, int M, int N, const Tile<NW> &t) {
-    for_each_element<NW>(t, m0, n0, M, N, [&](float v, size_t off) { X[off] = v; });
+    for_each_element<NW>(t, m0, n0, M, N, [&](float v, size_t off) { __builtin_nontemporal_store(v, X + off); });
 }
 
 // ---------------------------------------------------------------------------
@@ -761,7 +766,7 @@ struct CBlock {
         return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off(e, j), 0, 0));
     }
     __device__ __forceinline__ void store(int e, int j, float v) const {
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off(e, j), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off(e, j), 0, CPOL_NT);
     }
 };
 
@@ -862,7 +867,7 @@ __device__ __forceinline__ void store_quads_final(const KParams &p, int m0, int 
         for (int g = 0; g < QPT; ++g) {
             const int fq = threadIdx.x + NT * g, r = fq >> 5, c = (fq & 31) * 4;
             if (m0 + r < p.M && n0 + c < p.N)
-                *reinterpret_cast<f32x4 *>(p.C + (size_t)(m0 + r) * p.N + n0 + c) = res[g];
+                __builtin_nontemporal_store(res[g], reinterpret_cast<f32x4 *>(p.C + (size_t)(m0 + r) * p.N + n0 + c));
         }
         return;
     }
@@ -887,8 +892,8 @@ __device__ __forceinline__ void store_quads_final(const KParams &p, int m0, int 
     for (int g = 0; g < QPT; ++g) {
         const int fq = threadIdx.x + NT * g, r = fq >> 5, c = (fq & 31) * 4;
         if (m0 + r < p.M && n0 + c < p.N)
-            *reinterpret_cast<f32x4 *>(p.C + (size_t)(m0 + r) * p.N + n0 + c) =
-                f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+            __builtin_nontemporal_store(f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]},
+                                        reinterpret_cast<f32x4 *>(p.C + (size_t)(m0 + r) * p.N + n0 + c));
     }
 }
 
@@ -1365,7 +1370,7 @@ __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    if (row < p.M && col < p.N) q.C[(size_t)row * p.N + col] = acc.v[i][j][e];
+                    if (row < p.M && col < p.N) __builtin_nontemporal_store(acc.v[i][j][e], q.C + (size_t)row * p.N + col);
                 }
             }
     } else {
@@ -1641,7 +1646,7 @@ __global__ __launch_bounds__(RED_THREADS) void splitk_reduce(KParams p0) {
             finish<4>(p, v, cin, bv);
             sum = f32x4{v[0], v[1], v[2], v[3]};
         }
-        *reinterpret_cast<f32x4 *>(p.C + off) = sum;
+        __builtin_nontemporal_store(sum, reinterpret_cast<f32x4 *>(p.C + off));
     } else {
         for (int e = 0; e < 4 && n0 + c + e < p.N; ++e) {
             float sum = 0.f;
@@ -1713,7 +1718,7 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
     }
 #pragma unroll
     for (int y = 0; y < 4; ++y)
-        if (row + y < p.M) pv.C[(size_t)(row + y) * p.N + col] = sum[y];
+        if (row + y < p.M) __builtin_nontemporal_store(sum[y], pv.C + (size_t)(row + y) * p.N + col);
 }
 
 // ---------------------------------------------------------------------------
