@@ -10,7 +10,8 @@ The functions carry the names of the C entry points in ``include/gemm.h``:
   ``gemm_set_stream``, ``gemm_sync_status``, ``gemm_release``,
   ``gemm_last_error``, ``gemm_num_cus``, ``gemm_version``.
 
-``gemm_tensors(a, b, c, ...)`` is the torch-facing convenience: it checks the
+``gemm_tensors(a, b, c, ...)`` is the torch-facing convenience (``matmul(a, b)``
+returns a new fp32 tensor): it checks the
 tensors' device, dtype, shape and contiguity on the host, passes their data
 pointers and torch's current HIP stream, and raises ``GemmError`` on a
 negative status.  Importing this module fails loudly when the library has not
@@ -26,7 +27,7 @@ __all__ = [
     "GemmError", "GemmPlan", "GemmArgs", "gemm", "gemm_ex", "gemm_plan", "gemm_plan_batched",
     "gemm_workspace_size", "gemm_unit_range",
     "gemm_set_stream", "gemm_sync_status", "gemm_release", "gemm_last_error", "gemm_num_cus",
-    "gemm_version", "gemm_tensors", "plan_dict", "library_path",
+    "gemm_version", "gemm_tensors", "matmul", "plan_dict", "library_path",
 ]
 
 _PKG = Path(__file__).resolve().parent
@@ -350,3 +351,26 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
             args.bias = bias.data_ptr()
         args.epilogue = word
         _check(gemm_ex(args))
+
+
+def matmul(a, b, b_layout: str = "kn", out=None, alpha: Optional[float] = None, beta: Optional[float] = None,
+           bias=None, act: str = "none", mode: str = "heuristic", splits: int = 0, atomic: bool = False):
+    """``a . b`` (or ``a . b^T`` with b_layout "nk") as a new fp32 tensor, or into ``out``.
+
+    2-D operands, or 3-D batches (``a`` or ``b`` may be 2-D and shared); bf16 or
+    fp16 in, fp32 out.  ``alpha``, ``beta``, ``bias`` and ``act`` fuse the
+    epilogue ``act(alpha a.b + beta out + bias)`` (``beta`` needs ``out``).
+    """
+    import torch
+
+    M = a.shape[-2]
+    N = b.shape[-1] if b_layout == "kn" else b.shape[-2]
+    batch = max(a.shape[0] if a.dim() == 3 else 1, b.shape[0] if b.dim() == 3 else 1)
+    if out is None:
+        if beta:
+            raise ValueError("beta != 0 needs out (the prior C)")
+        shape = (batch, M, N) if (a.dim() == 3 or b.dim() == 3) else (M, N)
+        out = torch.empty(shape, dtype=torch.float32, device=a.device)
+    gemm_tensors(a, b, out, b_layout=b_layout, mode=mode, splits=splits, atomic=atomic, alpha=alpha, beta=beta,
+                 bias=bias, act=act)
+    return out

@@ -262,3 +262,20 @@ def test_random_batched_epilogue(dg, case):
             D, _ = oe.epilogue_ref(P, c0, epi[0], epi[1], b64, epi[2])
             ok, worst, idx = oe.within_bound(got, D, oe.epilogue_bound(S, P, c0, epi[0], epi[1], b64, epi[2]))
         assert ok, f"entry {b}: worst ratio {worst} at {idx}"
+
+
+def test_matmul_convenience(dg):
+    # matmul allocates the fp32 output: 2-D, a batch with a shared B, and the epilogue
+    w = _workload(200, 136, 256, "kn", "bf16")
+    A, B = _operands(w, 3, share_b=True)
+    out = dg.matmul(A.to(DEV), B.to(DEV))
+    assert tuple(out.shape) == (3, 200, 136) and out.dtype == torch.float32
+    _check_entries(A, B, out, w, 3, True)
+    bias = torch.linspace(-1, 1, 136, device=DEV)
+    one = dg.matmul(A[1].to(DEV), B.to(DEV), bias=bias, act="relu")
+    P, S = og.ref_gemm(A[1], B, 200, 136, 256, "kn", "bf16")
+    D, _ = oe.epilogue_ref(P, None, 1.0, 0.0, bias.cpu().numpy().astype(np.float64), "relu")
+    ok, worst, idx = oe.within_bound(one.cpu().numpy().astype(np.float64), D,
+                                     oe.epilogue_bound(S, P, None, 1.0, 0.0, bias.cpu().numpy().astype(np.float64),
+                                                       "relu"))
+    assert ok, worst
