@@ -14,7 +14,6 @@ inputs).  ``within_tolerance`` applies the elementwise bound
 from __future__ import annotations
 
 import ctypes
-import os
 import time
 from pathlib import Path
 from typing import Optional, Sequence

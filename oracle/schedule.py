@@ -40,7 +40,6 @@ coverage).
 from __future__ import annotations
 
 from dataclasses import dataclass
-from math import ceil
 from typing import Dict, List, Sequence, Tuple
 
 FULL = "full"        # segment covers the whole k range of its tile: plain epilogue

@@ -5,7 +5,6 @@ oracle's tolerance (atomic modes).  The library's workspace is allocated by an
 eager call before the capture; a call enqueues kernels only (no memset nodes),
 and the Stream-K turnstile's flags clear themselves after use, so the epoch
 fixed at capture time serves every replay."""
-import numpy as np
 import pytest
 import torch
 

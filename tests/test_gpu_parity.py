@@ -11,7 +11,6 @@ import pytest
 import torch
 
 from oracle import gemm as og
-from oracle import schedule as sch
 from workloads import WORKLOADS, make_operands
 
 from gpu_util import (check_against_oracle, decode_trace, expected_trace, guarded_output,
