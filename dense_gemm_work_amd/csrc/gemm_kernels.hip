@@ -1096,7 +1096,7 @@ constexpr int G_NS = 2;                        // stages
 constexpr int G_BREG = G_NS * G_SLAB;          // B slabs start at 64 KiB
 // Waves per group: 8 of 128x64 (two per SIMD).  GroupLoop also builds with 4
 // waves of 128x128 (one per SIMD, accumulators in AGPRs, a third less LDS read
-// traffic); measured on the 8192^3 launch the eight-wave form is 2 % faster.
+// traffic); measured on the 8192^3 launch the eight-wave form is 2-4 % faster.
 constexpr int G_NW = 8;
 
 template <int NW>
