@@ -986,6 +986,15 @@ __device__ __forceinline__ void wait_flag(const uint32_t *flag, uint32_t epoch, 
     }
 }
 
+// wait_flag whose first poll was issued earlier (v0 from load_flag_async), so
+// its latency overlapped other work.
+__device__ __forceinline__ void wait_flag_issued(const uint32_t *flag, uint32_t v0, uint32_t epoch, uint32_t limit,
+                                                 uint32_t *status) {
+    wait_vm_all();
+    if (flag_value(v0) == epoch) return;
+    wait_flag(flag, epoch, limit, status);
+}
+
 // ---------------------------------------------------------------------------
 // Debug trace (thread 0 only; active only when p.trace is set)
 // ---------------------------------------------------------------------------
@@ -1784,6 +1793,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         // a segment that stores C: with the epilogue, its inputs are loaded now,
         // while the k-halves merge and any peers are waited for and added
         const bool stores_c = role == 0 || (role == 1 && !ATOMIC && p.merge != MERGE_TWO_PASS);
+        // a turnstile owner's first peer is always unit u + 1: its flag is read
+        // now, its latency hidden behind the k-half merge
+        const bool turnstile_owner = role == 1 && !ATOMIC && p.merge != MERGE_TWO_PASS;
+        uint32_t first_flag = 0;
+        if (turnstile_owner && threadIdx.x == 0) first_flag = load_flag_async(p.flags + u + 1);
         float pre_c[32], pre_b[2];
         if constexpr (EPI) {
             static_assert(NW == 8, "the prefetch assumes one 32-row block per wave");
@@ -1824,7 +1838,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
             for (int v = u + 1; v < p.units; ++v) {
                 if (unit_start(v, p.q, p.big) >= tile_end) break;
                 if (threadIdx.x == 0) {
-                    wait_flag(p.flags + v, p.epoch, p.spin_limit, p.status);
+                    if (v == u + 1) wait_flag_issued(p.flags + v, first_flag, p.epoch, p.spin_limit, p.status);
+                    else wait_flag(p.flags + v, p.epoch, p.spin_limit, p.status);
                     // each flag has this one reader: clear it once seen, so every
                     // call starts with the flags at zero, also the replays of a
                     // captured graph, whose epoch is fixed at capture
