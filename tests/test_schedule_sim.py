@@ -160,6 +160,41 @@ def test_coverage_exactly_once(rule):
             for t, (owner, peers) in sch.tile_groups(segs).items():
                 i = nonempty.index(owner)
                 assert peers == nonempty[i + 1:i + 1 + len(peers)]
+            # roles agree with the tile groups: a tile one unit computes is whole;
+            # of a split tile the k = 0 holder is the owner and the rest contribute
+            per_tile = {}
+            for s in segs:
+                per_tile.setdefault(s.tile, []).append(s)
+            for t, lst in per_tile.items():
+                if len(lst) == 1:
+                    assert lst[0].role == sch.FULL and (lst[0].k0, lst[0].k1) == (0, ipt)
+                else:
+                    lst = sorted(lst, key=lambda s: s.k0)
+                    assert lst[0].role == sch.OWNER and lst[0].k0 == 0
+                    assert all(s.role == sch.CONTRIB for s in lst[1:])
+
+
+# -- book chapter, Case 2: "big units first" -------------------------------------
+def test_big_units_first():
+    # the units that own one iteration more than the others are the first ones:
+    # lengths never increase with the unit index and differ by at most one
+    for total in range(0, 200, 7):
+        for units in range(1, 40):
+            lens = [e - b for b, e in sch.unit_ranges(total, units)]
+            assert sum(lens) == total
+            assert max(lens) - min(lens) <= 1
+            assert all(lens[i] >= lens[i + 1] for i in range(units - 1)), (total, units, lens)
+
+
+# -- brute force: the tile grid covers every output element once ------------------
+def test_tile_grid_covers_every_element():
+    for bm, bn in ((128, 128), (64, 64)):
+        for M in list(range(1, 300, 13)) + [127, 128, 129, 256, 257]:
+            for N in (1, 63, 64, 65, 200, 384):
+                tm, tn = sch.tile_grid(M, N, bm, bn)
+                rows = {i // bm for i in range(M)}
+                cols = {j // bn for j in range(N)}
+                assert rows == set(range(tm)) and cols == set(range(tn)), (M, N, bm, bn)
 
 
 def test_rules_agree_when_units_divide():
