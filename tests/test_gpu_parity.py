@@ -13,7 +13,7 @@ import torch
 from oracle import gemm as og
 from workloads import WORKLOADS, make_operands
 
-from gpu_util import (check_against_oracle, decode_trace, expected_trace, guarded_output,
+from gpu_util import (POISON, check_against_oracle, decode_trace, expected_trace, guarded_output,
                       guards_intact, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
@@ -206,6 +206,43 @@ def test_random_small_problems(dg, case):
         splits = cap   # Stream-K units must all be resident
     A, B, c = run(dg, w, mode=mode, splits=splits, atomic=atomic, two_pass=two_pass, num_cus=cus)
     assert_parity(c, A, B, w)
+
+
+def _medium_cases(n, seed=23):
+    """Seeded random medium problems on the device's own CU count: enough tiles
+    for hybrids (three of the twelve on 256 CUs), tile groups (two) and
+    multi-wave plans to arise as they do in real calls (sampled rows against
+    the oracle, every element written)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        layout = str(rng.choice(["kn", "nk"]))
+        M = int(rng.integers(300, 6200))
+        N = int(rng.integers(40, 780)) * 8
+        K = int(rng.integers(8, 320)) * 8
+        dtype = str(rng.choice(["bf16", "fp16"]))
+        mode = str(rng.choice(["heuristic", "heuristic", "dp", "streamk", "splitk"]))
+        ipt = -(-K // 64)
+        splits, atomic = 0, False
+        if mode == "splitk":
+            splits = int(rng.choice([s for s in range(1, 9) if ipt % s == 0]))
+        elif mode == "streamk":
+            atomic = bool(rng.integers(0, 2))
+        cases.append((i, M, N, K, layout, dtype, mode, splits, atomic))
+    return cases
+
+
+@pytest.mark.parametrize("case", _medium_cases(12), ids=lambda c: f"m{c[0]}")
+def test_random_medium_problems(dg, case):
+    i, M, N, K, layout, dtype, mode, splits, atomic = case
+    dist = dict(dist="uniform", low=-1.0, high=1.0) if dtype == "bf16" else dict(dist="uniform", low=-0.5, high=0.5)
+    w = WORKLOADS["c1_sk32"].with_(name=f"medium{i}", M=M, N=N, K=K, b_layout=layout, dtype=dtype, seed=300 + i,
+                                   **dist)
+    A, B, c = run(dg, w, mode=mode, splits=splits, atomic=atomic)
+    # rows still holding the fill value join the sample: an element never
+    # written fails there, a product that happens to equal it passes
+    filled = torch.nonzero((c == POISON).any(dim=1)).flatten().tolist()[:64]
+    assert_parity(c, A, B, w, rows=sorted(set(sample_rows(M, 12, seed=i)) | set(filled)))
 
 
 def test_k_zero_writes_zeros(dg):
