@@ -197,6 +197,43 @@ def shape_arms(dg, name, steps, warmup):
     return out
 
 
+def vendor_blas(dg, name, calls, rounds=6):
+    """Context, not a baseline: the vendor BLAS (torch.mm with fp32 output) and
+    this library's call on the workload's operands, timed alternately in this
+    process (median over `rounds` of the mean of `calls` back-to-back calls)."""
+    import torch
+    from workloads import WORKLOADS, make_operands
+
+    w = WORKLOADS[name]
+    A, B = make_operands(w)
+    a, b = A.cuda(), B.cuda()
+    c = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    ours = Call(dg, a, b, c, w.b_layout, w.mode, w.splits, w.atomic)
+    stream = ours.stream
+
+    def vendor():
+        torch.mm(a, b, out_dtype=torch.float32)
+
+    res = {"ours": [], "vendor": []}
+    with torch.cuda.stream(stream):
+        for f in (ours, vendor):
+            for _ in range(calls):
+                f()
+        torch.cuda.synchronize()
+        for r in range(rounds):
+            for tag, f in ((("ours", ours), ("vendor", vendor)) if r % 2 == 0 else
+                           (("vendor", vendor), ("ours", ours))):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(calls):
+                    f()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                res[tag].append(e0.elapsed_time(e1) * 1e3 / calls)
+    o, v = statistics.median(res["ours"]), statistics.median(res["vendor"])
+    return {"mode": w.mode, "ours_us": round(o, 3), "vendor_us": round(v, 3), "vendor_over_ours": round(v / o, 3)}
+
+
 def kernel_name(dg, plan, w):
     kind = {dg.GEMM_DP: "gemm_dp", dg.GEMM_SPLITK: "gemm_splitk", dg.GEMM_STREAMK: "gemm_streamk"}[plan.decision]
     # the library runs 2x2 tile groups when their waves finish sooner (its rule, restated)
@@ -417,6 +454,12 @@ def main():
         for name in ("c3_wavequant", "c1_sk32", "c2a_m96_s8", "c2b_m256_s2", "c5_longk_fp16", "c4_large_dp",
                      "x1_hybrid", "x2_batched"):
             shapes[name] = shape_arms(dg, name, args.shape_steps, 10)
+    vendor = {}
+    if not args.no_shapes:
+        # operands with B [K,N] only (torch.mm is then given contiguous operands)
+        for name, calls in (("c3_wavequant", 100), ("c5_longk_fp16", 50), ("c4_large_dp", 5), ("x1_hybrid", 30)):
+            vendor[name] = vendor_blas(dg, name, calls)
+            log(f"  vendor {name:14s} {vendor[name]}")
     c3 = shapes.get("c3_wavequant", {})
     speedups = {}
     if c3:
@@ -483,6 +526,7 @@ def main():
         "cu_timeline": timeline,
         "power": power,
         "shapes": shapes,
+        "vendor_blas": vendor,
     }
     print(json.dumps(line), flush=True)
     return 0
