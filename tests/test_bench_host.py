@@ -1,0 +1,44 @@
+"""Host-side contract of bench.py (no GPU): the one-GPU refusal, the comment-
+insensitive kernel code digest, and the gating of the measured HBM traffic on
+that digest."""
+import json
+import subprocess
+import sys
+from pathlib import Path
+
+import bench
+
+ROOT = Path(__file__).resolve().parent.parent
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       cwd=str(ROOT), timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""   # no JSON line is printed
+
+
+def test_code_digest_ignores_comments_only(tmp_path):
+    src = "int f(int x) {\n    return x + 1;   // one more\n}\n/* a block\n   comment */\n"
+    a = tmp_path / "a.hip"
+    a.write_text(src)
+    b = tmp_path / "b.hip"
+    b.write_text("// a new header line\n" + src.replace("// one more", "// changed note").replace("    ", "\t"))
+    c = tmp_path / "c.hip"
+    c.write_text(src.replace("x + 1", "x + 2"))
+    assert bench.kernel_code_digest(a) == bench.kernel_code_digest(b)
+    assert bench.kernel_code_digest(a) != bench.kernel_code_digest(c)
+
+
+def test_traffic_is_reported_only_for_the_profiled_code(monkeypatch):
+    entries = json.loads((ROOT / "profiles" / "traffic.json").read_text())
+    name, entry = next(iter(entries.items()))
+    kernel = entry["kernel"]
+    monkeypatch.setattr(bench, "kernel_code_digest", lambda path=None: entry["code_sha256"])
+    assert bench.measured_traffic(name, kernel) == int(entry["bytes"])
+    assert bench.measured_traffic(name, "some_other_kernel") is None
+    assert bench.measured_traffic("no_such_profile", kernel) is None
+    monkeypatch.setattr(bench, "kernel_code_digest", lambda path=None: "0" * 64)
+    assert bench.measured_traffic(name, kernel) is None
+
