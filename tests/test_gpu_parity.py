@@ -156,7 +156,7 @@ SMALL = [
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s[:3])) + f"-{s[3]}-{s[4]}")
 @pytest.mark.parametrize("mode,splits,atomic", [
     ("dp", 0, False), ("splitk", 1, False), ("splitk", -1, False), ("streamk", 7, False),
-    ("streamk", 3, True), ("streamk", 0, False), ("heuristic", 0, False),
+    ("streamk", 3, True), ("streamk", 0, False), ("streamk", 1, False), ("heuristic", 0, False),
 ])
 def test_small_shapes_all_modes(dg, shape, mode, splits, atomic):
     M, N, K, layout, dtype = shape
