@@ -280,6 +280,8 @@ TRACE_CASES = [
     ("c5-atomic", 1536, 1536, 16384, "streamk", 0, 256, True),
     ("c2a", 96, 512, 2048, "splitk", 8, 256, False),
     ("ragged-7u", 300, 200, 320, "streamk", 7, 256, False),
+    ("one-unit", 300, 200, 328, "streamk", 1, 256, False),   # every tile whole, one after another
+    ("units-over-iterations", 256, 128, 128, "streamk", 6, 256, False),   # 4 iterations over 6 units
     ("hybrid", 1408, 768, 1024, "heuristic", 0, 20, False),
     ("dp", 640, 384, 256, "dp", 0, 256, False),
     ("dp-groups", 1024, 1024, 256, "dp", 0, 16, False),   # 2x2 tile groups (64 tiles, 16 CUs)
