@@ -560,3 +560,42 @@ def test_outputs_beyond_2_to_the_31_elements(dg, M, N, K, mode):
     ok, worst, idx = og.within_tolerance(got, C, S)
     say(f"    worst err/bound = {worst:.3e} at {idx}")
     assert ok, f"outside tolerance: worst ratio {worst} at {idx}"
+
+
+# ---------------------------------------------------------------------------
+# Flags and counters reset themselves: calls of every merge kind enqueued back
+# to back on one stream and one library workspace, twice over with fresh
+# operands, each checked against the oracle afterwards
+# ---------------------------------------------------------------------------
+def test_modes_interleaved_on_one_workspace(dg):
+    inl = dg.GEMM_DEBUG_IN_LAUNCH
+    seq = [  # (mode, splits, atomic, two_pass, debug)
+        ("streamk", 7, False, False, inl), ("splitk", 4, False, False, inl), ("splitk", 4, False, True, 0),
+        ("streamk", 5, True, False, 0), ("streamk", 9, False, True, 0), ("dp", 0, False, False, 0),
+        ("splitk", 2, True, False, 0), ("heuristic", 0, False, False, 0), ("streamk", 3, False, False, inl),
+    ]
+    shapes = [(512, 384, 1024, "kn", "bf16"), (300, 200, 328, "nk", "fp16")]
+    for rep in range(2):
+        pending = []
+        for si, (M, N, K, layout, dtype) in enumerate(shapes):
+            dist = dict(dist="uniform", low=-1.0, high=1.0) if dtype == "bf16" else \
+                dict(dist="uniform", low=-0.5, high=0.5)
+            w = WORKLOADS["c1_sk32"].with_(name=f"seq{rep}-{si}", M=M, N=N, K=K, b_layout=layout, dtype=dtype,
+                                           seed=500 + 10 * rep + si, **dist)
+            A, B = make_operands(w)
+            a, b = A.to(DEV), B.to(DEV)
+            ipt = -(-K // 64)
+            for mode, splits, atomic, two_pass, debug in seq:
+                if mode == "splitk":
+                    while ipt % splits:   # Split-K factors divide the k-iterations
+                        splits -= 1
+                full, c = guarded_output(M, N, DEV)
+                say(f"  enqueue rep {rep} {w.name} {M}x{N}x{K} mode={mode} splits={splits} atomic={atomic} "
+                    f"two_pass={two_pass} debug={debug}")
+                dg.gemm_tensors(a, b, c, b_layout=layout, mode=mode, splits=splits, atomic=atomic,
+                                two_pass=two_pass, debug=debug)
+                pending.append((w, A, B, full, c, mode, splits))
+        assert dg.gemm_sync_status() == 0, dg.gemm_last_error()
+        for w, A, B, full, c, mode, splits in pending:
+            assert guards_intact(full, w.M, w.N), f"guard band overwritten ({w.name} {mode} {splits})"
+            assert_parity(c, A, B, w)
