@@ -122,7 +122,7 @@ def time_call(call: Call, steps: int, warmup: int):
     return wall, e0.elapsed_time(e1)
 
 
-def arm_result(w, call, steps, warmup, rounds=5):
+def arm_result(w, call, steps, warmup, rounds=7):
     """Median over `rounds` of the mean launch duration of `steps` back-to-back calls."""
     per = []
     for r in range(rounds):
@@ -453,7 +453,7 @@ def main():
     if not args.no_shapes:
         for name in ("c3_wavequant", "c1_sk32", "c2a_m96_s8", "c2b_m256_s2", "c5_longk_fp16", "c4_large_dp",
                      "x1_hybrid", "x2_batched"):
-            shapes[name] = shape_arms(dg, name, args.shape_steps, 10)
+            shapes[name] = shape_arms(dg, name, args.shape_steps, 50)
     vendor = {}
     if not args.no_shapes:
         # operands with B [K,N] only (torch.mm is then given contiguous operands)
