@@ -45,7 +45,9 @@ def parse():
     ap.add_argument("--workload", default="c3_wavequant")
     ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape arms")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--shape-steps", type=int, default=50)
+    ap.add_argument("--rounds", type=int, default=9, help="rounds of the per-shape comparison protocol")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time the vendor BLAS alternately with the library (context only)")
     ap.add_argument("--mode", default=None, choices=["heuristic", "dp", "splitk", "streamk"],
                     help="override the workload's decomposition (for profiling one arm)")
     ap.add_argument("--splits", type=int, default=None, help="Split-K factor or Stream-K units")
@@ -122,24 +124,83 @@ def time_call(call: Call, steps: int, warmup: int):
     return wall, e0.elapsed_time(e1)
 
 
-def arm_result(w, call, steps, warmup, rounds=7):
-    """Median over `rounds` of the mean launch duration of `steps` back-to-back calls."""
-    per = []
+def time_arms(calls, rounds, samples, pack, warmup=20):
+    """The Metal split-K note's comparison protocol ("Comparison and independent
+    confirmation"): every arm warmed up, then `rounds` rounds of `samples`
+    samples; within a round the arm order is rotated by one at every sample and
+    every other round runs the rotated order in reverse, so no arm keeps a fixed
+    place in the clock and power history of a power-capped chip.  A sample is
+    one HIP event pair on the launch stream around `pack` back-to-back calls
+    (its mean per call).  Returns {arm: [[samples of round 0], [round 1], ...]}
+    in microseconds."""
+    import torch
+
+    names = list(calls)
+    for n in names:
+        for _ in range(warmup):
+            calls[n]()
+    torch.cuda.synchronize()
+    out = {n: [] for n in names}
     for r in range(rounds):
-        _, ev_ms = time_call(call, steps, warmup if r == 0 else 2)
-        per.append(ev_ms / steps)
-    med = statistics.median(per)
+        recs = []
+        for i in range(samples):
+            k = i % len(names)
+            order = names[k:] + names[:k]
+            if r % 2 == 1:
+                order = order[::-1]
+            for n in order:
+                c = calls[n]
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(c.stream)
+                for _ in range(pack):
+                    c()
+                e1.record(c.stream)
+                recs.append((n, e0, e1))
+        torch.cuda.synchronize()
+        per = {n: [] for n in names}
+        for n, e0, e1 in recs:
+            per[n].append(e0.elapsed_time(e1) * 1e3 / pack)
+        for n in names:
+            out[n].append(per[n])
+    return out
+
+
+def _q(xs, f):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(f * (len(xs) - 1)))))]
+
+
+def arm_result(w, call, rounds_us):
+    """Median and spread of an arm's samples (all rounds pooled)."""
+    flat = [x for r in rounds_us for x in r]
+    med = statistics.median(flat)
     return {
         "decision": call.dg.DECISION_NAMES[call.plan.decision],
         "units_or_splits": int(call.plan.sk_units or call.plan.splits),
-        "median_us": round(med * 1e3, 3),
-        "min_us": round(min(per) * 1e3, 3),
-        "tflops": round(w.flops / (med * 1e-3) / 1e12, 2),
-        "pct_peak": round(100 * w.flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "median_us": round(med, 3),
+        "p10_us": round(_q(flat, 0.1), 3),
+        "p90_us": round(_q(flat, 0.9), 3),
+        "min_us": round(min(flat), 3),
+        "round_medians_us": [round(statistics.median(r), 3) for r in rounds_us],
+        "tflops": round(w.flops / (med * 1e-6) / 1e12, 2),
+        "pct_peak": round(100 * w.flops / (med * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2),
     }
 
 
-def shape_arms(dg, name, steps, warmup):
+def paired_speedup(base_rounds, arm_rounds):
+    """Speedup of an arm over the base from paired rounds: per round the ratio of
+    the two arms' median samples (both timed interleaved in that round); the
+    median ratio and the smallest and largest round's."""
+    ratios = [statistics.median(b) / statistics.median(a) for b, a in zip(base_rounds, arm_rounds)]
+    return {"median": round(statistics.median(ratios), 3), "min": round(min(ratios), 3),
+            "max": round(max(ratios), 3)}
+
+
+# samples per round and calls per sample: a few seconds of GPU time per workload
+PROTOCOL = {"c1": (40, 8), "c2": (40, 8), "c3": (40, 8), "c4": (6, 2), "c5": (20, 8), "x1": (12, 4), "x2": (20, 8)}
+
+
+def shape_arms(dg, name, rounds):
     import torch
     from workloads import WORKLOADS, make_operands
 
@@ -184,16 +245,18 @@ def shape_arms(dg, name, steps, warmup):
     out = {"M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype, "b_layout": w.b_layout}
     if w.batch > 1:
         out["batch"] = w.batch
-    for arm, (mode, splits, atomic, *ep) in arms.items():
-        call = Call(dg, a, b, c, w.b_layout, mode, splits, atomic, epilogue=ep[0] if ep else None)
-        st = steps if not name.startswith("c4") else max(5, steps // 10)
-        out[arm] = arm_result(w, call, st, warmup)
-        log(f"  {name:14s} {arm:15s} {out[arm]}")
-    base = out.get("dp")
-    if base:
-        for arm in out:
-            if isinstance(out[arm], dict) and arm != "dp":
-                out[arm]["speedup_vs_dp"] = round(base["median_us"] / out[arm]["median_us"], 3)
+    calls = {arm: Call(dg, a, b, c, w.b_layout, mode, splits, atomic, epilogue=ep[0] if ep else None)
+             for arm, (mode, splits, atomic, *ep) in arms.items()}
+    samples, pack = PROTOCOL[name[:2]]
+    timed = time_arms(calls, rounds, samples, pack)
+    out["protocol"] = {"rounds": rounds, "samples_per_round": samples, "calls_per_sample": pack,
+                       "order": "rotated every sample, reversed every other round"}
+    for arm, call in calls.items():
+        out[arm] = arm_result(w, call, timed[arm])
+        if "dp" in timed and arm != "dp":
+            out[arm]["speedup_vs_dp"] = paired_speedup(timed["dp"], timed[arm])
+        log(f"  {name:14s} {arm:20s} {out[arm]['median_us']:9.3f} us  {out[arm]['tflops']:8.2f} TFLOP/s"
+            + (f"  x{out[arm]['speedup_vs_dp']['median']} vs dp" if "speedup_vs_dp" in out[arm] else ""))
     return out
 
 
@@ -386,19 +449,44 @@ def cu_timeline(dg, name, mode, splits=0, atomic=False):
 
 
 def cpu_baseline(w, A, B):
+    """The fp64 oracle timed on the host's cores over the whole workload; also
+    returns its (C, S), which check the GPU's output."""
     from oracle import gemm as og
 
-    rows = list(range(w.M))
-    secs = og.time_rows(A, B, w.M, w.N, w.K, w.b_layout, w.dtype, rows)
-    flops = 2.0 * len(rows) * w.N * w.K
+    t0 = time.perf_counter()
+    C, S = og.ref_gemm(A, B, w.M, w.N, w.K, w.b_layout, w.dtype)
+    secs = time.perf_counter() - t0
+    flops = 2.0 * w.M * w.N * w.K
     return {
         "value": round(flops / secs / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": og.num_threads(),
         "kind": "oracle",
-        "sample": f"all {len(rows)} rows of {w.M}x{w.N}x{w.K} ({w.dtype}); fp64 C and sum|a||b| "
+        "sample": f"all {w.M} rows of {w.M}x{w.N}x{w.K} ({w.dtype}); fp64 C and sum|a||b| "
                   f"in {secs:.2f} s; flops counted as 2*M*N*K of C only",
-    }
+    }, (C, S)
+
+
+def output_check(c_before, c_after, ref):
+    """Every element of the timed call's output, as it stood before and after the
+    timed region, against the fp64 oracle: |C - C_ref| <= 1e-4 sum|a||b| (Metal
+    split-K note, "Comparison and independent confirmation": complete-output
+    fp64 checks around the timing)."""
+    import numpy as np
+
+    from oracle import gemm as og
+
+    C, S = ref
+    res = {"elements": int(C.size), "tolerance": "1e-4 * sum_k |a_ik||b_kj|"}
+    ok_all = True
+    for tag, c in (("before", c_before), ("after", c_after)):
+        ok, worst, idx = og.within_tolerance(c.numpy().astype(np.float64), C, S)
+        res[f"worst_err_over_bound_{tag}"] = round(worst, 6)
+        ok_all = ok_all and ok
+    res["bit_identical_before_after"] = bool(np.array_equal(c_before.numpy().view(np.int32),
+                                                            c_after.numpy().view(np.int32)))
+    res["pass"] = bool(ok_all)
+    return res
 
 
 def main():
@@ -427,7 +515,11 @@ def main():
         f"units={call.plan.sk_units} steps={args.steps} warmup={args.warmup}")
 
     # ---- headline: whole-job throughput over exactly `steps` steps ----------------
+    call()
+    torch.cuda.synchronize()
+    c_before = c.cpu()   # the output of an untimed call, checked against the oracle below
     wall, ev_ms = time_call(call, args.steps, args.warmup)
+    c_after = c.cpu()    # ... and the output of the last timed call
     ms_per_step = wall * 1e3 / args.steps
     value = w.flops * args.steps / wall / 1e12
     kern_ms = ev_ms / args.steps
@@ -453,9 +545,9 @@ def main():
     if not args.no_shapes:
         for name in ("c3_wavequant", "c1_sk32", "c2a_m96_s8", "c2b_m256_s2", "c5_longk_fp16", "c4_large_dp",
                      "x1_hybrid", "x2_batched"):
-            shapes[name] = shape_arms(dg, name, args.shape_steps, 50)
+            shapes[name] = shape_arms(dg, name, args.rounds)
     vendor = {}
-    if not args.no_shapes:
+    if args.vendor and not args.no_shapes:
         # operands with B [K,N] only (torch.mm is then given contiguous operands)
         for name, calls in (("c3_wavequant", 100), ("c5_longk_fp16", 50), ("c4_large_dp", 5), ("x1_hybrid", 30)):
             vendor[name] = vendor_blas(dg, name, calls)
@@ -463,9 +555,11 @@ def main():
     c3 = shapes.get("c3_wavequant", {})
     speedups = {}
     if c3:
-        sk = c3["heuristic"]["median_us"]
-        for arm in ("dp", "splitk2", "splitk4"):
-            speedups[f"streamk_vs_{arm}"] = round(c3[arm]["median_us"] / sk, 3)
+        speedups["streamk_vs_dp"] = c3["heuristic"]["speedup_vs_dp"]
+        for arm in ("splitk2", "splitk4"):
+            # Stream-K over Split-K: quotient of the two arms' paired speedups over DP
+            speedups[f"streamk_vs_{arm}"] = round(c3["heuristic"]["speedup_vs_dp"]["median"] /
+                                                  c3[arm]["speedup_vs_dp"]["median"], 3)
 
     timeline = {}
     if not args.no_timeline:
@@ -483,11 +577,14 @@ def main():
             power[key] = power_snapshot(dg, name, mode)
             log(f"  power {key:11s} {power[key]}")
 
-    cpu = None
-    if not args.no_cpu:
+    cpu, check = None, None
+    if not args.no_cpu and w.batch == 1:
         log("bench: timing the fp64 CPU oracle on the same workload")
-        cpu = cpu_baseline(w, A, B)
+        cpu, ref = cpu_baseline(w, A, B)
         log(f"bench: cpu oracle {cpu['value']} TFLOP/s on {cpu['cores']} threads")
+        check = output_check(c_before, c_after, ref)
+        del ref
+        log(f"bench: output check {check}")
 
     line = {
         "metric": METRIC,
@@ -523,12 +620,16 @@ def main():
             "kernel_mean_us": round(kern_ms * 1e3, 3),
         },
         "cpu_baseline": cpu,
+        "output_check": check,
         "cu_timeline": timeline,
         "power": power,
         "shapes": shapes,
         "vendor_blas": vendor,
     }
     print(json.dumps(line), flush=True)
+    if check is not None and not check["pass"]:
+        log("bench: the timed call's output is outside the oracle's tolerance")
+        return 3
     return 0
 
 

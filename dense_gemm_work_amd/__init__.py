@@ -64,6 +64,7 @@ GEMM_DEBUG_NO_PUBLISH = 0x1
 GEMM_DEBUG_IN_LAUNCH = 0x4
 GEMM_DEBUG_TILE_DP = 0x8
 GEMM_DEBUG_HYBRID_SPLIT = 0x10
+GEMM_DEBUG_ZERO_PARTIAL = 0x20
 
 GEMM_BM = 128
 GEMM_BN = 128

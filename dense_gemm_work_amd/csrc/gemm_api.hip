@@ -10,6 +10,10 @@
 //            counter to zero.
 //   data:    Stream-K partial slots [units][128*128] fp32, or Split-K partials
 //            [S][M][N] fp32.
+// Both blocks only grow.  A block that is outgrown is retired, not freed: a
+// graph captured earlier keeps the addresses it was captured with, so retired
+// blocks stay allocated until gemm_release().  Growth needs hipMalloc and a
+// synchronous fill, so it is refused on a stream that is being captured.
 // A caller workspace holds [flags | counters | data] for the call's own plan
 // and has its control part zero-filled by the library on every call.
 #include <hip/hip_runtime.h>
@@ -68,6 +72,8 @@ struct DeviceState {
     int64_t cap_units = 0, cap_tiles = 0;
     void *data = nullptr;
     int64_t cap_data = 0;
+    std::vector<void *> retired;   // outgrown data blocks, freed by gemm_release()
+    std::vector<uint32_t *> retired_control;   // outgrown control blocks (status word first)
     int bpc[2][2][5] = {};         // resident workgroups per CU, 0 = not yet queried
 };
 
@@ -98,43 +104,54 @@ int device_state(int dev, DeviceState **out) {
     return GEMM_OK;
 }
 
+// GEMM_OK when `stream` is not being captured into a graph, else a
+// GEMM_ERR_WORKSPACE refusal naming `what`.
+int refuse_if_capturing(hipStream_t stream, const char *what) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return fail_hip(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(GEMM_ERR_WORKSPACE, std::string("the library workspace must grow (") + what +
+                                            ") while the stream is being captured; make one eager call "
+                                            "with the same plan first, or pass a caller workspace");
+    return GEMM_OK;
+}
+
 // Make sure the library control block covers `units` flags and `tiles` counters.
-int ensure_control(DeviceState &d, int64_t units, int64_t tiles) {
+// An outgrown block is retired (still allocated), never freed here.
+int ensure_control(DeviceState &d, int64_t units, int64_t tiles, hipStream_t stream) {
     if (d.control && units <= d.cap_units && tiles <= d.cap_tiles) return GEMM_OK;
+    int rc = refuse_if_capturing(stream, "control block");
+    if (rc != GEMM_OK) return rc;
     const int64_t cu = std::max<int64_t>({units, d.cap_units, 1024});
     const int64_t ct = std::max<int64_t>({tiles, d.cap_tiles, 4096});
-    hipError_t e;
-    if (d.control) {
-        // only ever replaced between launches that the device has finished
-        if ((e = hipDeviceSynchronize()) != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
-        if ((e = hipFree(d.control)) != hipSuccess) return fail_hip(e, "hipFree");
-        d.control = nullptr;
-    }
     const size_t bytes = (size_t)(kStatusWords + cu + ct) * 4;
-    if ((e = hipMalloc(&d.control, bytes)) != hipSuccess) {
-        d.control = nullptr;
-        d.cap_units = d.cap_tiles = 0;
+    uint32_t *fresh = nullptr;
+    hipError_t e;
+    if ((e = hipMalloc(&fresh, bytes)) != hipSuccess)
         return fail(GEMM_ERR_WORKSPACE, std::string("hipMalloc(control): ") + hipGetErrorString(e));
+    if ((e = hipMemset(fresh, 0, bytes)) != hipSuccess) {
+        (void)hipFree(fresh);
+        return fail_hip(e, "hipMemset(control)");
     }
-    if ((e = hipMemset(d.control, 0, bytes)) != hipSuccess) return fail_hip(e, "hipMemset(control)");
+    // a retired block keeps its status word, which gemm_sync_status still reads
+    if (d.control) d.retired_control.push_back(d.control);
+    d.control = fresh;
     d.cap_units = cu;
     d.cap_tiles = ct;
     return GEMM_OK;
 }
 
-int ensure_data(DeviceState &d, int64_t bytes) {
+int ensure_data(DeviceState &d, int64_t bytes, hipStream_t stream) {
     if (bytes <= d.cap_data) return GEMM_OK;
+    int rc = refuse_if_capturing(stream, "data block");
+    if (rc != GEMM_OK) return rc;
+    void *fresh = nullptr;
     hipError_t e;
-    if (d.data) {
-        if ((e = hipDeviceSynchronize()) != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
-        if ((e = hipFree(d.data)) != hipSuccess) return fail_hip(e, "hipFree");
-        d.data = nullptr;
-        d.cap_data = 0;
-    }
-    if ((e = hipMalloc(&d.data, (size_t)bytes)) != hipSuccess) {
-        d.data = nullptr;
+    if ((e = hipMalloc(&fresh, (size_t)bytes)) != hipSuccess)
         return fail(GEMM_ERR_WORKSPACE, std::string("hipMalloc(workspace): ") + hipGetErrorString(e));
-    }
+    if (d.data) d.retired.push_back(d.data);
+    d.data = fresh;
     d.cap_data = bytes;
     return GEMM_OK;
 }
@@ -230,7 +247,8 @@ int run(const gemm_args_t &a) {
                             a.num_cus > 0 ? a.num_cus : 256, &p, &why);
     if (rc != GEMM_OK) return fail(rc, why);
     if (a.num_cus < 0) return fail(GEMM_ERR_INVALID, "num_cus must be >= 0");
-    if ((a.debug & ~(GEMM_DEBUG_NO_PUBLISH | GEMM_DEBUG_IN_LAUNCH | GEMM_DEBUG_TILE_DP | GEMM_DEBUG_HYBRID_SPLIT)) != 0)
+    if ((a.debug & ~(GEMM_DEBUG_NO_PUBLISH | GEMM_DEBUG_IN_LAUNCH | GEMM_DEBUG_TILE_DP | GEMM_DEBUG_HYBRID_SPLIT |
+                    GEMM_DEBUG_ZERO_PARTIAL)) != 0)
         return fail(GEMM_ERR_INVALID, "unknown debug bits");
     if ((rc = check_epilogue(a)) != GEMM_OK) return rc;
     if (a.M == 0 || a.N == 0) return GEMM_OK;
@@ -285,7 +303,11 @@ int run(const gemm_args_t &a) {
                                                   std::to_string((int64_t)bpc * ds->num_cus) + ")");
     }
 
-    if ((rc = ensure_control(*ds, std::max<int64_t>(p.sk_units, 1), p.tiles)) != GEMM_OK) return rc;
+    // the status word always lives in the library's control block; its flags and
+    // counters are used only without a caller workspace
+    if ((rc = a.workspace ? ensure_control(*ds, 1, 1, stream)
+                          : ensure_control(*ds, std::max<int64_t>(p.sk_units, 1), p.tiles, stream)) != GEMM_OK)
+        return rc;
 
     // flags, counters and the data region
     uint32_t *flags = nullptr, *counters = nullptr;
@@ -302,7 +324,7 @@ int run(const gemm_args_t &a) {
         part = reinterpret_cast<float *>(base + cb);
         if ((e = dgw::launch_zero(base, cb / 4, stream)) != hipSuccess) return fail_hip(e, "zero control");
     } else {
-        if ((rc = ensure_data(*ds, data_bytes)) != GEMM_OK) return rc;
+        if ((rc = ensure_data(*ds, data_bytes, stream)) != GEMM_OK) return rc;
         flags = ds->control + kStatusWords;
         counters = flags + ds->cap_units;
         part = static_cast<float *>(ds->data);
@@ -500,13 +522,19 @@ int gemm_sync_status(void *stream) {
     if ((e = hipGetDevice(&dev)) != hipSuccess) return fail_hip(e, "hipGetDevice");
     std::lock_guard<std::mutex> lock(g_mu);
     if ((int)g_dev.size() <= dev || !g_dev[dev].control) return GEMM_OK;
+    // the current control block and the retired ones that captured graphs may still use
+    std::vector<uint32_t *> blocks = g_dev[dev].retired_control;
+    blocks.push_back(g_dev[dev].control);
     uint32_t status = 0;
-    if ((e = hipMemcpy(&status, g_dev[dev].control, 4, hipMemcpyDeviceToHost)) != hipSuccess)
-        return fail_hip(e, "read status");
+    for (uint32_t *blk : blocks) {
+        uint32_t st = 0;
+        if ((e = hipMemcpy(&st, blk, 4, hipMemcpyDeviceToHost)) != hipSuccess) return fail_hip(e, "read status");
+        if (st == 0) continue;
+        status |= st;
+        const uint32_t zero = 0;
+        if ((e = hipMemcpy(blk, &zero, 4, hipMemcpyHostToDevice)) != hipSuccess) return fail_hip(e, "clear status");
+    }
     if (status == 0) return GEMM_OK;
-    const uint32_t zero = 0;
-    if ((e = hipMemcpy(g_dev[dev].control, &zero, 4, hipMemcpyHostToDevice)) != hipSuccess)
-        return fail_hip(e, "clear status");
     return fail(GEMM_ERR_TIMEOUT, "a bounded inter-workgroup wait gave up (status word " +
                                       std::to_string(status) + ")");
 }
@@ -517,11 +545,15 @@ void gemm_release(void) {
     if (hipGetDevice(&cur) != hipSuccess) cur = 0;
     for (size_t dev = 0; dev < g_dev.size(); ++dev) {
         DeviceState &d = g_dev[dev];
-        if (!d.control && !d.data) continue;
+        if (!d.control && !d.data && d.retired.empty() && d.retired_control.empty()) continue;
         if (hipSetDevice((int)dev) != hipSuccess) continue;
         (void)hipDeviceSynchronize();
         if (d.control) (void)hipFree(d.control);
         if (d.data) (void)hipFree(d.data);
+        for (void *r : d.retired) (void)hipFree(r);
+        for (uint32_t *r : d.retired_control) (void)hipFree(r);
+        d.retired.clear();
+        d.retired_control.clear();
         d.control = nullptr;
         d.data = nullptr;
         d.cap_units = d.cap_tiles = d.cap_data = 0;

@@ -391,8 +391,10 @@ __device__ __forceinline__ void mac_loop_impl(const KParams &p, char *lds, int m
     if (n > 3) issue_next(3);
     wait_vm_lgkm_stages<DPI>(min(NS, n) - 1);   // this wave's loads of iteration 0 landed
     __builtin_amdgcn_s_barrier();
-    // A partial published just before this loop: its stores preceded the loads
-    // waited for above in every wave, so they are complete and the flag may rise.
+    // A partial published just before this loop: its stores were issued before
+    // the loads waited for above, and completion is reported in issue order, so
+    // in every wave they are complete (the barrier covers all waves) and the
+    // flag may rise.
     if (raise && threadIdx.x == 0) __hip_atomic_store(raise, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     ml.template read<0>(f[0]);
     int done = 0;                              // iterations issued to the matrix cores
@@ -700,6 +702,10 @@ __device__ __forceinline__ float epi_value(const KParams &p, float acc, float c,
 
 __device__ __forceinline__ bool reads_c(const KParams &p) { return p.epi == EPI_ACCUM || p.beta != 0.0f; }
 
+// Numerical control (GEMM_DEBUG_ZERO_PARTIAL): every partial handed to another
+// workgroup is written as zeros, so every split tile must come out wrong.
+__device__ __forceinline__ bool zero_partials(const KParams &p) { return (p.debug & GEMM_DEBUG_ZERO_PARTIAL) != 0; }
+
 // Final values of n elements, in place: v holds the sums, c the prior C values
 // (0 where not read), b the bias values (0 without a bias).  EPI_ACCUM:
 // v = fma(alpha, v, c) with no activation (a later pass applies it).
@@ -849,7 +855,9 @@ __device__ __forceinline__ void store_final(const KParams &p, int m0, int n0, co
 // Split parts of atomic merges: C += acc (EPI_ACCUM: C += alpha acc).
 template <int NW, bool EPI = true>
 __device__ __forceinline__ void atomic_add_c(const KParams &p, int m0, int n0, const Tile<NW> &t) {
-    if (EPI && p.epi == EPI_ACCUM) {
+    if (zero_partials(p)) {
+        for_each_element<NW>(t, m0, n0, p.M, p.N, [&](float, size_t off) { unsafeAtomicAdd(p.C + off, 0.0f); });
+    } else if (EPI && p.epi == EPI_ACCUM) {
         const float a = p.alpha;
         for_each_element<NW>(t, m0, n0, p.M, p.N, [&](float v, size_t off) { unsafeAtomicAdd(p.C + off, a * v); });
     } else {
@@ -898,12 +906,23 @@ __device__ __forceinline__ void store_quads_final(const KParams &p, int m0, int 
 }
 
 // ---------------------------------------------------------------------------
-// Partial exchange between workgroups.  Partials are written and read with
-// device-scope (sc1) buffer accesses, which the gfx950 memory hierarchy keeps
-// coherent across the XCDs' separate L2 caches without writing back or
-// invalidating whole caches; the writer waits for its stores to complete
-// before the flag or counter is raised, and the reader only loads after
-// observing it.
+// Partial exchange between workgroups ("store the partial, signal, the owner
+// waits and reads it": book chapter, "Mental model").  It rests on two
+// properties of the GFX942 memory model that gfx950 follows (LLVM AMDGPU
+// backend documentation, "Memory Model GFX942"):
+//  1. sc1 loads and stores are how the backend implements agent-scope relaxed
+//     atomic loads and stores, so they are coherent across the XCDs' separate
+//     L2 caches.  Every partial is written and read with sc1 buffer accesses,
+//     every flag and counter with agent-scope atomics.
+//  2. A wave's vector memory operations report completion (vmcnt) in the order
+//     they were issued, stores included; flat instructions that reach LDS are
+//     the documented exception and none is used here.
+// The writer waits until its partial stores are complete (a vmcnt wait in every
+// wave, then a barrier) before the flag or counter changes; the reader issues
+// its partial loads only after the flag's value has come back.  That is the
+// model's release/acquire pair without the L2 write-back and invalidate, which
+// serve non-sc1 accesses only -- and the invalidate would throw away the A and
+// B panels the other CUs of the XCD are streaming.
 // ---------------------------------------------------------------------------
 constexpr int CPOL_DEVICE = 16;   // cache-policy bits: sc1 (device scope)
 
@@ -933,9 +952,10 @@ __device__ __forceinline__ uint32_t slot_off(int quad, int b, int e4, int lane) 
 }
 
 template <int NW>
-__device__ __forceinline__ void put_slot(float *slot, const Tile<NW> &t) {
+__device__ __forceinline__ void put_slot(float *slot, const Tile<NW> &t, bool zero) {
     const Role<NW> w;
     const __amdgpu_buffer_rsrc_t r = span(slot, BM * BN * 4);
+    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};   // the zero-partial control
 #pragma unroll
     for (int h = 0; h < Tile<NW>::R; ++h)
 #pragma unroll
@@ -944,7 +964,7 @@ __device__ __forceinline__ void put_slot(float *slot, const Tile<NW> &t) {
             for (int e4 = 0; e4 < 4; ++e4) {
                 const f32x16 &v = t.v[h][j];
                 put4_coherent(r, slot_off(w.quad, 2 * t.i[h] + j, e4, w.lane),
-                              f32x4{v[4 * e4], v[4 * e4 + 1], v[4 * e4 + 2], v[4 * e4 + 3]});
+                              zero ? zero4 : f32x4{v[4 * e4], v[4 * e4 + 1], v[4 * e4 + 2], v[4 * e4 + 3]});
             }
 }
 
@@ -1482,8 +1502,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p0) {
     {
         const __amdgpu_buffer_rsrc_t rp = span(p.part + (size_t)s * mn + org, span_bytes);
         float *Ps = p.part + (size_t)s * mn;
+        const bool zero = zero_partials(p);   // the zero-partial control
         for_each_quad<NW>(m0, n0, p.M, p.N, [&](int, int r, int c, size_t off, int nv) {
-            const f32x4 v = staged_quad(stg, r, c);
+            const f32x4 v = zero ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : staged_quad(stg, r, c);
             if (nv == 4) {
                 put4_coherent(rp, quad_off(r, c), v);
             } else {
@@ -1814,13 +1835,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         } else if (p.merge == MERGE_TWO_PASS) {
             // streamk_reduce adds the tile's partials: contributors publish into
             // the first slot bank, owners into the second
-            put_slot<NW>(p.part + ((size_t)(role == 1 ? p.units : 0) + u) * (BM * BN), t);
+            put_slot<NW>(p.part + ((size_t)(role == 1 ? p.units : 0) + u) * (BM * BN), t, zero_partials(p));
         } else if (role == 2) {
             // starts mid-tile: publish the partial, then the flag -- at once if
             // this is the unit's last segment, else from the next segment's loop
             // as soon as the stores are known complete (the loop has to wait for
             // its first loads anyway)
-            put_slot<NW>(p.part + (size_t)u * (BM * BN), t);
+            put_slot<NW>(p.part + (size_t)u * (BM * BN), t, zero_partials(p));
             uint32_t *flag = (p.debug & GEMM_DEBUG_NO_PUBLISH) ? nullptr : p.flags + u;
             if (tb + k1 < end) {
                 pending = flag;

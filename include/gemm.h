@@ -59,9 +59,15 @@
  * synchronised by the caller).  Calls that overlap on one device race.
  *
  * Graph capture: a call enqueues kernels only (no memset or copy), so it can be
- * captured in a HIP graph once an eager call with the same plan has sized the
- * library workspace (or with a caller workspace); replays must not overlap.
- * Stream-K flags clear themselves after use, so the replays' fixed epoch works.
+ * captured in a HIP graph once an eager call with the same plan (any eager call
+ * on the device, with a caller workspace) has sized the library workspace;
+ * replays must not overlap.  A call that would have to grow the library
+ * workspace while its stream is being captured returns GEMM_ERR_WORKSPACE and
+ * launches nothing.  The library workspace only grows: an outgrown block is
+ * retired but stays allocated until gemm_release(), so a graph captured before
+ * a larger eager call still replays into valid memory (gemm_release() ends
+ * that: do not replay graphs of library-workspace calls after it).  Stream-K
+ * flags clear themselves after use, so the replays' fixed epoch works.
  *
  * Errors: a negative status is returned and nothing is launched (C untouched)
  * for every condition the host can detect; gemm_last_error() then describes it.
@@ -119,6 +125,14 @@ extern "C" {
 #define GEMM_DEBUG_HYBRID_SPLIT 0x10u /* a hybrid's data-parallel tiles run as a second
                                          launch after the Stream-K one instead of by
                                          the persistent units first.  Same values.  */
+#define GEMM_DEBUG_ZERO_PARTIAL 0x20u /* numerical control: every partial a split tile
+                                         hands to another workgroup is written as zeros
+                                         (Stream-K slots, Split-K partials of both merge
+                                         forms, atomic adds into C).  Every call with a
+                                         split tile then returns a wrong C; a parity
+                                         check that still passes has no teeth (Metal
+                                         split-K note, "Contract and numerical
+                                         coverage": the zero-partial control).       */
 
 /* ---- epilogue word for gemm_args_t.epilogue ------------------------------------------ */
 /*
@@ -313,18 +327,31 @@ int gemm_plan_batched(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t l
 
 /*
  * gemm_workspace_size -- device workspace bytes a call with these arguments
- * needs (plan.workspace_bytes: Stream-K partial slots and flags, Split-K
- * partials and counters, the status block), for a caller that passes its own
- * gemm_args_t.workspace.  batch >= 1; num_cus >= 1 (no device is queried).
- * Returns the byte count (>= 0) or a negative status for arguments
- * gemm_plan_batched rejects.
+ * needs (plan.workspace_bytes), for a caller that passes its own
+ * gemm_args_t.workspace.  What it holds follows the pages' merge designs: the
+ * docc StreamK page's aligned split ("MMA fragment accumulators") keeps one fp32
+ * slot per split and an arrival counter per tile (here Split-K partials
+ * [batch][S][M][N] and a counter per tile); the book chapter's Stream-K paragraph
+ * has a unit that starts mid-tile store an fp32 partial and signal (here one
+ * 64 KiB slot and one flag per unit; two slots per unit when a second kernel
+ * adds the partials, Case 3's fixup kernel).  Plus a 256-byte status block.
+ * Layout: [status 256 B | flags, 256-B aligned | counters, 256-B aligned | data].
+ * batch >= 1; num_cus >= 1 (no device is queried).  Returns the byte count
+ * (>= 0) or a negative status for arguments gemm_plan_batched rejects.
+ * Ownership: the caller allocates, zero-fills once and frees it.
  */
 int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout,
                             uint32_t mode, int32_t splits, int32_t num_cus);
 
 /*
- * gemm_unit_range -- [begin, end) of Stream-K unit u in the flattened space of
- * the plan's Stream-K tiles (host arithmetic).  Returns a status.
+ * gemm_unit_range -- [begin, end) of Stream-K unit u in the flattened
+ * (tile x k-iteration) space of the plan's Stream-K tiles: the book chapter's
+ * Stream-K paragraph gives every unit an equal contiguous slice of that space,
+ * and its Case 2 gives the first (total mod units) units one iteration more, so
+ * begin = u q + min(u, big) and end = begin + q + (u < big).  Iteration g of the
+ * space is k-iteration g mod ipt of Stream-K tile g / ipt (tile dp_tiles + g / ipt
+ * of the call).  Host arithmetic only.  Returns GEMM_OK, or GEMM_ERR_INVALID
+ * for a null pointer, a plan that is not Stream-K, or u outside [0, sk_units).
  */
 int gemm_unit_range(const gemm_plan_t *plan, int64_t unit, int64_t *begin, int64_t *end);
 
@@ -339,7 +366,9 @@ int gemm_set_stream(void *stream);
  */
 int gemm_sync_status(void *stream);
 
-/* gemm_release -- free the library-owned workspace of every device (synchronises them). */
+/* gemm_release -- free the library-owned workspace of every device, retired
+ * blocks included (synchronises every device first).  Graphs captured from
+ * calls on the library workspace must not be replayed afterwards. */
 void gemm_release(void);
 
 /* gemm_last_error -- text for the calling thread's last failing call ("" if none). */

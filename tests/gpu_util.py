@@ -38,6 +38,42 @@ def check_against_oracle(c_gpu: torch.Tensor, A, B, w, rows=None, tol=og.TOLERAN
     return ok, worst, idx
 
 
+_ORACLE_CACHE: dict = {}
+
+
+def oracle_full(w):
+    """(A, B, C_ref, S) of a workload's seeded operands over every row, computed
+    once per test session (the full-size products take a few seconds each)."""
+    from workloads import make_operands
+
+    if w not in _ORACLE_CACHE:
+        A, B = make_operands(w)
+        C, S = og.ref_gemm(A, B, w.M, w.N, w.K, w.b_layout, w.dtype)
+        _ORACLE_CACHE[w] = (A, B, C, S)
+    return _ORACLE_CACHE[w]
+
+
+def check_full(c_gpu: torch.Tensor, w, tol=og.TOLERANCE):
+    """Every element of C against the cached full-size oracle: (ok, worst ratio, index)."""
+    _, _, C, S = oracle_full(w)
+    got = c_gpu.detach().cpu().numpy().astype(np.float64)
+    return og.within_tolerance(got, C, S, tol)
+
+
+def poison_rows(c_gpu: torch.Tensor, limit: int = 64):
+    """Rows of C that still hold the fill value somewhere (at most `limit`)."""
+    return torch.nonzero((c_gpu == POISON).any(dim=1)).flatten().tolist()[:limit]
+
+
+def tile_row_sample(M: int, seed: int = 0, bm: int = 128):
+    """One random row inside every bm-row band of C, plus the first and last row."""
+    rng = np.random.default_rng(seed)
+    rows = {0, M - 1}
+    for r0 in range(0, M, bm):
+        rows.add(int(rng.integers(r0, min(M, r0 + bm))))
+    return sorted(rows)
+
+
 def sample_rows(M: int, n: int, seed: int = 0):
     """First, last, a ragged-tile row and n random rows (sorted, unique)."""
     rng = np.random.default_rng(seed)

@@ -73,3 +73,81 @@ def test_graph_replays_match_eager(dg, case):
         ok, worst, idx = og.within_tolerance(c.cpu().numpy()[rows], C, S)
         assert ok, f"replay {r}: worst ratio {worst} at {idx}"
     del g
+
+
+def test_capture_refuses_workspace_growth(dg):
+    # with no library workspace yet, a captured call would have to allocate one:
+    # it is refused (GEMM_ERR_WORKSPACE), nothing is captured, and the same call
+    # works eagerly afterwards
+    w = WORKLOADS["c1_sk32"]
+    A, B = make_operands(w)
+    a, b = A.to(DEV), B.to(DEV)
+    torch.cuda.synchronize()
+    dg.gemm_release()
+    c = torch.full((w.M, w.N), 7.0, dtype=torch.float32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    status = None
+    say("  capture with an empty library workspace")
+    with torch.cuda.graph(g):
+        try:
+            dg.gemm_tensors(a, b, c, mode="streamk", splits=32)
+        except dg.GemmError as e:
+            status = e.status
+    assert status == dg.GEMM_ERR_WORKSPACE, dg.gemm_last_error()
+    del g
+    torch.cuda.synchronize()
+    assert torch.all(c == 7.0), "a refused call must not touch C"
+    dg.gemm_tensors(a, b, c, mode="streamk", splits=32)
+    assert dg.gemm_sync_status() == 0
+    C, S = og.ref_gemm(A, B, w.M, w.N, w.K, w.b_layout, w.dtype)
+    ok, worst, idx = og.within_tolerance(c.cpu().numpy(), C, S)
+    assert ok, f"worst ratio {worst} at {idx}"
+
+
+def test_graph_replays_after_workspace_grows(dg):
+    # a graph captured on a small library workspace keeps replaying correctly
+    # after a larger eager call has grown the workspace (the outgrown blocks are
+    # retired, not freed)
+    small = WORKLOADS["c1_sk32"]
+    A, B = make_operands(small)
+    a, b = A.to(DEV), B.to(DEV)
+    torch.cuda.synchronize()
+    dg.gemm_release()
+    c = torch.empty((small.M, small.N), dtype=torch.float32, device=DEV)
+    call = lambda out: dg.gemm_tensors(a, b, out, mode="streamk", splits=32, debug=dg.GEMM_DEBUG_IN_LAUNCH)
+    call(c)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(c)
+    # grow both blocks: 65 x 65 = 4225 tiles need more Split-K counters than the
+    # first control block holds (4096), and S = 2 partials of 8320 x 8320 fp32
+    # (554 MB) more data than the Stream-K slots took
+    big = WORKLOADS["c1_sk32"].with_(name="grow", M=8320, N=8320, K=128)
+    A2, B2 = make_operands(big)
+    c2 = torch.empty((big.M, big.N), dtype=torch.float32, device=DEV)
+    say("  eager call that grows the workspace")
+    dg.gemm_tensors(A2.to(DEV), B2.to(DEV), c2, mode="splitk", splits=2, debug=dg.GEMM_DEBUG_IN_LAUNCH)
+    assert dg.gemm_sync_status() == 0
+    rows = [0, 4160, 8319]
+    C2, S2 = og.ref_gemm(A2, B2, big.M, big.N, big.K, big.b_layout, big.dtype, rows=rows)
+    ok, worst, idx = og.within_tolerance(c2.cpu().numpy()[rows], C2, S2)
+    assert ok, f"growing call: worst ratio {worst} at {idx}"
+    del c2
+    for r in range(3):
+        A3, B3 = make_operands(small, seed=70 + r)
+        a.copy_(A3.to(DEV))
+        b.copy_(B3.to(DEV))
+        c.fill_(7.0)
+        say(f"  replay {r} after growth")
+        g.replay()
+        torch.cuda.synchronize()
+        assert dg.gemm_sync_status() == 0, dg.gemm_last_error()
+        ce = torch.full_like(c, 7.0)
+        call(ce)
+        torch.cuda.synchronize()
+        assert torch.equal(c.view(torch.int32), ce.view(torch.int32)), f"replay {r} differs from eager"
+        C, S = og.ref_gemm(A3, B3, small.M, small.N, small.K, small.b_layout, small.dtype)
+        ok, worst, idx = og.within_tolerance(c.cpu().numpy(), C, S)
+        assert ok, f"replay {r}: worst ratio {worst} at {idx}"
+    del g

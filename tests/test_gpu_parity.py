@@ -13,8 +13,8 @@ import torch
 from oracle import gemm as og
 from workloads import WORKLOADS, make_operands
 
-from gpu_util import (POISON, check_against_oracle, decode_trace, expected_trace, guarded_output,
-                      guards_intact, sample_rows, say)
+from gpu_util import (POISON, check_against_oracle, check_full, decode_trace, expected_trace, guarded_output,
+                      guards_intact, oracle_full, poison_rows, sample_rows, say, tile_row_sample)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,8 +47,20 @@ def run(dg, w, mode=None, splits=None, atomic=None, A=None, B=None, **kw):
 
 
 def assert_parity(c, A, B, w, rows=None):
+    """Elementwise bound on every row, or on a row sample joined by every row
+    that still holds the fill value somewhere (an element never written fails
+    there; a product that happens to equal the fill value passes)."""
+    if rows is not None:
+        rows = sorted(set(rows) | set(poison_rows(c)))
     ok, worst, idx = check_against_oracle(c, A, B, w, rows=rows)
-    say(f"    worst err/bound = {worst:.3e} at {idx}")
+    say(f"    worst err/bound = {worst:.3e} at {idx}" + ("" if rows is None else f" ({len(rows)} rows)"))
+    assert ok, f"outside tolerance: worst ratio {worst} at {idx}"
+
+
+def assert_parity_full(c, w):
+    """Every element against the session's cached full-size oracle."""
+    ok, worst, idx = check_full(c, w)
+    say(f"    worst err/bound = {worst:.3e} at {idx} (all {w.M * w.N} elements)")
     assert ok, f"outside tolerance: worst ratio {worst} at {idx}"
 
 
@@ -85,29 +97,37 @@ def test_c2_splitk(dg, name):
 
 
 def test_c3_heuristic_streamk(dg):
+    # every element of the headline workload against the full fp64 product
     w = WORKLOADS["c3_wavequant"]
     p = dg.gemm_plan(w.M, w.N, w.K, 0, dg.GEMM_HEURISTIC, 0, 256)
     assert (dg.DECISION_NAMES[p.decision], p.sk_units, p.sk_tiles) == ("StreamK", 256, 272)
-    A, B, c = run(dg, w)
-    assert_parity(c, A, B, w, rows=sample_rows(w.M, 48))
+    A, B, _, _ = oracle_full(w)
+    _, _, c = run(dg, w, A=A, B=B)
+    assert_parity_full(c, w)
 
 
 def test_x1_hybrid_full_size(dg):
-    # the heuristic's hybrid regime at full size: 3 data-parallel waves + Stream-K
+    # the heuristic's hybrid regime at full size: 3 data-parallel waves + Stream-K,
+    # every element
     w = WORKLOADS["x1_hybrid"]
     p = dg.gemm_plan(w.M, w.N, w.K, 0, dg.GEMM_HEURISTIC, 0, 256)
     assert dg.DECISION_NAMES[p.decision] == "StreamK" and p.dp_tiles == 768 and p.sk_tiles == 288
     assert p.sk_units == 256 and p.q == 72 and p.big == 0
-    A, B, c = run(dg, w)
-    assert_parity(c, A, B, w, rows=sample_rows(w.M, 10) + [3 * 1024 + 5, 4095])
+    A, B, _, _ = oracle_full(w)
+    _, _, c = run(dg, w, A=A, B=B)
+    assert_parity_full(c, w)
 
 
 def test_c4_heuristic_dp(dg):
+    # 8192^3 (1.1 Tflop of fp64): one random row inside every 128-row tile row,
+    # plus every row that still holds the fill value
     w = WORKLOADS["c4_large_dp"]
     p = dg.gemm_plan(w.M, w.N, w.K, 0, dg.GEMM_HEURISTIC, 0, 256)
     assert dg.DECISION_NAMES[p.decision] == "DataParallel"
     A, B, c = run(dg, w)
-    assert_parity(c, A, B, w, rows=sample_rows(w.M, 10))
+    # a row holding the fill value joins the sample (an exact 7.0 is a legitimate
+    # product here: about 0.4 are expected among the 2^26 outputs)
+    assert_parity(c, A, B, w, rows=tile_row_sample(w.M, seed=4))
 
 
 @pytest.mark.parametrize("M,N,K,layout,cus", [
@@ -134,9 +154,52 @@ def test_dp_tile_groups(dg, M, N, K, layout, cus):
 
 @pytest.mark.parametrize("atomic", [False, True])
 def test_c5_streamk_fp16(dg, atomic):
+    # both fixup modes, every element against the full fp64 product
     w = WORKLOADS["c5_longk_fp16"]
-    A, B, c = run(dg, w, atomic=atomic)
-    assert_parity(c, A, B, w, rows=sample_rows(w.M, 24))
+    A, B, _, _ = oracle_full(w)
+    _, _, c = run(dg, w, A=A, B=B, atomic=atomic)
+    assert_parity_full(c, w)
+
+
+# ---------------------------------------------------------------------------
+# Numerical control: with every partial written as zeros, each workload with
+# split tiles must fail the oracle check, and pass again without the control
+# (Metal split-K note, "Contract and numerical coverage")
+# ---------------------------------------------------------------------------
+ZERO_PARTIAL_CASES = [   # (workload, merge kind, extra gemm_tensors arguments)
+    ("c1_sk32", "two-pass (plan)", {}),
+    ("c1_sk32", "turnstile", dict(debug_in_launch=True)),
+    ("c2a_m96_s8", "two-pass (plan)", {}),
+    ("c2a_m96_s8", "last arriver", dict(debug_in_launch=True)),
+    ("c2a_m96_s8", "atomic", dict(atomic=True)),
+    ("c2b_m256_s2", "two-pass (plan)", {}),
+    ("c2b_m256_s2", "last arriver", dict(debug_in_launch=True)),
+    ("c3_wavequant", "turnstile (plan)", {}),
+    ("c3_wavequant", "two-pass", dict(two_pass=True)),
+    ("c5_longk_fp16", "turnstile", {}),
+    ("c5_longk_fp16", "two-pass", dict(two_pass=True)),
+    ("c5_longk_fp16", "atomic", dict(atomic=True)),
+]
+
+
+@pytest.mark.parametrize("name,kind,extra", ZERO_PARTIAL_CASES, ids=lambda x: x if isinstance(x, str) else "")
+def test_zero_partial_control_fails(dg, name, kind, extra):
+    w = WORKLOADS[name]
+    A, B, _, _ = oracle_full(w)
+    a, b = A.to(DEV), B.to(DEV)
+    extra = dict(extra)
+    base_debug = dg.GEMM_DEBUG_IN_LAUNCH if extra.pop("debug_in_launch", False) else 0
+    kw = dict(b_layout=w.b_layout, mode=w.mode, splits=w.splits, **extra)
+    for control in (True, False):
+        full, c = guarded_output(w.M, w.N, DEV)
+        debug = base_debug | (dg.GEMM_DEBUG_ZERO_PARTIAL if control else 0)
+        say(f"  zero-partial control={control} {name} {kind}")
+        dg.gemm_tensors(a, b, c, debug=debug, **kw)
+        assert dg.gemm_sync_status() == 0, dg.gemm_last_error()
+        assert guards_intact(full, w.M, w.N)
+        ok, worst, idx = check_full(c, w)
+        say(f"    worst err/bound = {worst:.3e} at {idx}")
+        assert ok != control, ("the control must fail the check" if control else "the plain call must pass")
 
 
 # ---------------------------------------------------------------------------
@@ -279,6 +342,7 @@ TRACE_CASES = [
     ("c5", 1536, 1536, 16384, "streamk", 0, 256, False),
     ("c5-atomic", 1536, 1536, 16384, "streamk", 0, 256, True),
     ("c2a", 96, 512, 2048, "splitk", 8, 256, False),
+    ("c2b", 256, 512, 2048, "splitk", 2, 256, False),
     ("ragged-7u", 300, 200, 320, "streamk", 7, 256, False),
     ("one-unit", 300, 200, 328, "streamk", 1, 256, False),   # every tile whole, one after another
     ("units-over-iterations", 256, 128, 128, "streamk", 6, 256, False),   # 4 iterations over 6 units
@@ -293,7 +357,7 @@ TRACE_CASES = [
 @pytest.mark.parametrize("case", TRACE_CASES, ids=lambda c: c[0])
 def test_trace_matches_simulator(dg, case):
     name, M, N, K, mode, splits, cus, atomic = case
-    layout = "nk" if name == "c2a" else "kn"
+    layout = "nk" if name in ("c2a", "c2b") else "kn"
     lw = dg.layout_word(layout, "bf16")
     p = dg.gemm_plan(M, N, K, lw, dg.mode_word(mode, atomic), splits, cus)
     tr = torch.zeros(p.trace_ints, dtype=torch.int32, device=DEV)
@@ -318,7 +382,7 @@ def test_trace_matches_simulator(dg, case):
 # ---------------------------------------------------------------------------
 # Determinism
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["c1_sk32", "c5_longk_fp16", "c3_wavequant"])
+@pytest.mark.parametrize("name", ["c1_sk32", "c2a_m96_s8", "c2b_m256_s2", "c5_longk_fp16", "c3_wavequant"])
 def test_deterministic_bit_identical_10_runs(dg, name):
     w = WORKLOADS[name]
     A, B = make_operands(w)
