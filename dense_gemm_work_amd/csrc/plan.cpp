@@ -8,13 +8,14 @@
 //  * Stream-K paragraph after the glossary: unit u owns a contiguous slice of
 //    the flattened (tile, k-iteration) space; Case 2 gives the first
 //    (total mod units) units one extra iteration.
-//  * Case 2 and Case 4 (decomposition rule): data-parallel when there is no
-//    partial wave or a tile has at most 8 k-iterations; data-parallel when the
-//    tail wave is at least half full; otherwise Stream-K over the last two
-//    waves with at least 8 iterations per unit, and Split-K when the units
-//    divide evenly over the split tiles.
+//  * The toy figure's caption, Case 2's discussion and Case 4's knob table
+//    (decomposition rule): data-parallel when there is no partial wave or a
+//    tile has at most 8 k-iterations; data-parallel when the tail wave is at
+//    least half full; otherwise Stream-K over the last two waves with at least
+//    8 iterations per unit, and Split-K when the units divide evenly over the
+//    split tiles.
 // docc StreamK page, "MMA fragment accumulators (aligned split)": Split-K with
-// S dividing the panel count.
+// S dividing the panel count -- also a condition of the rule's Split-K choice.
 #include "plan.h"
 
 #include <algorithm>
@@ -104,18 +105,25 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, u
     int64_t units = 0, sk_tiles = 0;
     int32_t S = 1;
     if (decomp == GEMM_HEURISTIC) {
+        // the tail wave is the only thing the rule balances: a whole number of
+        // waves, a short K loop (at most 8 iterations) or a tail at least half
+        // the CUs stays data-parallel
         const int64_t min_iters = 8;
-        const bool whole_waves = p.full_waves == p.total_waves;
-        const int64_t tail = p.tiles - p.full_waves * num_cus;
-        if (whole_waves || p.ipt <= min_iters || 2 * tail >= num_cus) {
+        const bool ragged = p.tail > 0 && p.tail < num_cus;
+        if (!ragged || p.ipt <= min_iters || 2 * p.tail >= num_cus) {
             chosen = GEMM_DP;
         } else {
-            const int64_t dp_waves = p.full_waves > 1 ? p.full_waves - 1 : 0;
-            sk_tiles = p.tiles - dp_waves * num_cus;
+            // Stream-K over the tail wave and the full wave before it (if any);
+            // one unit per CU, but no fewer than 8 iterations per unit on average
+            const int64_t kept_waves = std::max<int64_t>(p.total_waves - 2, 0);
+            sk_tiles = p.tiles - kept_waves * num_cus;
             units = std::min<int64_t>(num_cus, (p.ipt * sk_tiles) / min_iters);
-            if (units > sk_tiles && units % sk_tiles == 0) {
+            // whole splits of every tile: plain Split-K, when S divides the tile's
+            // iterations (the aligned split); otherwise Stream-K with those units
+            const int64_t per_tile = units / sk_tiles;
+            if (units % sk_tiles == 0 && per_tile > 1 && p.ipt % per_tile == 0) {
                 chosen = GEMM_SPLITK;
-                S = int32_t(units / sk_tiles);
+                S = int32_t(per_tile);
             } else {
                 chosen = GEMM_STREAMK;
             }

@@ -24,11 +24,13 @@ Sources, by page and section:
   the epilogue.
 * Split-K ranges -- docc StreamK page, "MMA fragment accumulators (aligned
   split)": block (t, s) owns panels [s P / S, (s+1) P / S).
-* Decomposition rule -- book chapter, Case 2 ("cutlass_heuristic") and Case 4's
-  knob table: DP when there is no partial wave or a tile has at most 8
-  k-iterations, DP when the tail wave is at least half full, otherwise Stream-K
-  over the last two waves with at least 8 iterations per unit, and Split-K when
-  the units divide evenly over the split tiles.
+* Decomposition rule -- the toy figure's caption ("Mental model"), Case 2's
+  discussion of its table and Case 4's knob table: DP when there is no partial
+  wave or a tile has at most 8 k-iterations, DP when the tail wave is at least
+  half full, otherwise Stream-K over the last two waves with at least 8
+  iterations per unit, and Split-K when the units divide evenly over the split
+  tiles -- with the split factor dividing the tile's k-iterations, the aligned
+  split of the docc StreamK page ("MMA fragment accumulators").
 * Cost model -- book chapter, Case 2: 1 per MAC iteration, EPI per finished tile
   store, PART per fp32 partial store or load; the owner's wait is the later of
   its own progress and the peer's publish time.
@@ -70,6 +72,8 @@ def tile_grid(M: int, N: int, bm: int = 128, bn: int = 128) -> Tuple[int, int]:
 
 def wave_stats(tiles: int, sms: int) -> Waves:
     w = cdiv(tiles, sms)
+    if w == 0:                        # no tiles: no wave
+        return Waves(0, 0, 0, 0.0)
     last = tiles - (w - 1) * sms
     return Waves(tiles, w, last, tiles / (w * sms))
 
@@ -80,33 +84,29 @@ def wave_stats(tiles: int, sms: int) -> Waves:
 def unit_ranges(total: int, units: int, rule: str = "big_first") -> List[Tuple[int, int]]:
     """Half-open ``[b, e)`` ranges of the flattened space, one per unit.
 
-    rule "big_first": every unit gets floor(total/units) iterations and the
-                      first ``total mod units`` units one more (book chapter, Case 2).
-    rule "cdiv":      unit u starts at u*ceil(total/units), clipped to total (Case 3).
-    rule "floor":     unit u covers [floor(u*total/units), floor((u+1)*total/units))
-                      (docc StreamK page).
+    Every rule is a start function s(u) with s(0) = 0 and s(units) = total; unit u
+    covers [s(u), s(u + 1)).
+
+    rule "big_first": the shares differ by at most one iteration and the longer
+                      ones come first (book chapter, Case 2): with
+                      q, r = divmod(total, units), s(u) = u q + min(u, r).
+    rule "cdiv":      every unit but the last takes ceil(total/units) (Case 3's
+                      Triton kernel): s(u) = min(u ceil(total/units), total).
+    rule "floor":     s(u) = floor(u total / units) (docc StreamK page).
     """
     if units <= 0:
         raise ValueError("units must be positive")
-    out = []
     if rule == "big_first":
-        base, extra = divmod(total, units)
-        start = 0
-        for u in range(units):
-            n = base + (1 if u < extra else 0)
-            out.append((start, start + n))
-            start += n
+        q, r = divmod(total, units)
+        start = lambda u: u * q + min(u, r)
     elif rule == "cdiv":
-        q = cdiv(total, units)
-        for u in range(units):
-            b = min(u * q, total)
-            out.append((b, min(b + q, total)))
+        step = cdiv(total, units)
+        start = lambda u: min(u * step, total)
     elif rule == "floor":
-        for u in range(units):
-            out.append((u * total // units, (u + 1) * total // units))
+        start = lambda u: u * total // units
     else:
         raise ValueError(f"unknown split rule {rule!r}")
-    return out
+    return [(start(u), start(u + 1)) for u in range(units)]
 
 
 # ----------------------------------------------------------------------------
@@ -204,34 +204,48 @@ class Decision:
 
 
 def decide(tiles: int, ipt: int, sms: int, min_iters: int = 8) -> Decision:
-    waves_full = tiles // sms
-    waves_all = cdiv(tiles, sms)
-    if waves_full == waves_all or ipt <= min_iters:
-        return Decision("DataParallel", 0, 0)          # no partial wave, or too short a K loop
-    tail = tiles - waves_full * sms
-    if 2 * tail >= sms:
-        return Decision("DataParallel", 0, 0)          # tail wave at least half full
-    keep_dp = max(waves_full - 1, 0)                   # Stream-K takes the last two waves
-    sk_tiles = tiles - keep_dp * sms
-    sk_units = min(sms, (ipt * sk_tiles) // min_iters) # >= min_iters iterations per unit
-    if sk_units > sk_tiles and sk_units % sk_tiles == 0:
-        return Decision("SplitK", sk_tiles, sk_units)
-    return Decision("StreamK", sk_tiles, sk_units)
+    """The decomposition rule, stated in terms of the data-parallel waves.
+
+    * Nothing to balance -- the tiles fill whole waves, or a tile's K loop has
+      at most ``min_iters`` iterations -- or a last wave at least half full:
+      data-parallel.
+    * Otherwise the partial last wave and the full wave before it (if there is
+      one) become the Stream-K part; earlier waves stay data-parallel.
+    * Its units: one per SM, but never so many that a unit averages fewer than
+      ``min_iters`` iterations.
+    * If the units come out as a whole number S > 1 per Stream-K tile and S
+      divides the tile's iterations, every tile is simply split S ways: Split-K.
+    """
+    w = wave_stats(tiles, sms)
+    partial_last_wave = 0 < w.tail < sms
+    if not partial_last_wave or ipt <= min_iters or 2 * w.tail >= sms:
+        return Decision("DataParallel", 0, 0)
+    stream_waves = min(w.waves, 2)
+    sk_tiles = tiles - (w.waves - stream_waves) * sms
+    units = min(sms, sk_tiles * ipt // min_iters)
+    per_tile, left = divmod(units, sk_tiles)
+    if left == 0 and per_tile > 1 and ipt % per_tile == 0:
+        return Decision("SplitK", sk_tiles, units)
+    return Decision("StreamK", sk_tiles, units)
 
 
 # ----------------------------------------------------------------------------
 # Unit cost model (book chapter, Case 2).  Times are in MAC-iteration units.
 # ----------------------------------------------------------------------------
 def cost_dp(tiles: int, ipt: int, sms: int, epi: float = 2) -> float:
-    return cdiv(tiles, sms) * (ipt + epi)
+    """Every data-parallel wave costs one whole tile: its K loop and its epilogue."""
+    return wave_stats(tiles, sms).waves * (ipt + epi)
 
 
 def cost_splitk(tiles: int, ipt: int, sms: int, s: int, epi: float = 2, part: float = 2) -> float:
-    # Each wave of split workers is as slow as its worst member (one chunk of
-    # ceil(ipt/s) iterations plus one partial store or load); the tile's k = 0
-    # worker then loads the s - 1 remaining partials and writes the tile.
-    wave_cost = cdiv(ipt, s) + part
-    return cdiv(tiles * s, sms) * wave_cost + (s - 1) * part + epi
+    """Split-K in the chapter's model: the tiles x s workers run in waves of one
+    per SM; a wave lasts as long as its longest worker, which runs ceil(ipt / s)
+    iterations and moves one fp32 partial (stores it, or loads one); after the
+    last wave the tile's k = 0 worker adds the other s - 1 partials (a load
+    each) and writes the tile."""
+    worker = cdiv(ipt, s) + part
+    fold = (s - 1) * part + epi
+    return wave_stats(tiles * s, sms).waves * worker + fold
 
 
 def cost_streamk(segs: Sequence[Segment], units: int, ipt: int,
@@ -271,12 +285,14 @@ def cost_streamk_shape(tiles: int, ipt: int, units: int, epi: float = 2, part: f
 
 
 def cost_decided(tiles: int, ipt: int, sms: int, epi: float = 2, part: float = 2):
-    """(decision, makespan) of the rule's choice: the split/stream part, then DP waves."""
+    """(decision, makespan) of the rule's choice: its split part costed as
+    Stream-K units over the split tiles (Split-K is the special case whose
+    segments are whole splits), followed by the data-parallel waves it keeps."""
     d = decide(tiles, ipt, sms)
+    kept = cost_dp(tiles - d.sk_tiles, ipt, sms, epi)
     if d.kind == "DataParallel":
-        return d, cost_dp(tiles, ipt, sms, epi)
-    t = cost_streamk_shape(d.sk_tiles, ipt, d.sk_units, epi, part)
-    return d, t + cost_dp(tiles - d.sk_tiles, ipt, sms, epi)
+        return d, kept
+    return d, cost_streamk_shape(d.sk_tiles, ipt, d.sk_units, epi, part) + kept
 
 
 def ideal(tiles: int, ipt: int, sms: int, epi: float = 2) -> float:

@@ -342,3 +342,16 @@ def test_binding_uses_one_hip_runtime(tmp_path):
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr[-2000:]
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_heuristic_splitk_factor_divides_iterations(dg):
+    # 64 tiles x 34 iterations on 256 CUs: the rule's units (256) are 4 per tile,
+    # but 4 does not divide 34, so the aligned split is impossible and the units
+    # run as Stream-K (simulator and planner agree); 32 iterations keep Split-K
+    for K, kind, splits in ((34 * 64, "StreamK", 1), (32 * 64, "SplitK", 4)):
+        p = dg.gemm_plan(1024, 1024, K, 0, dg.GEMM_HEURISTIC, 0, 256)
+        d = sch.decide(64, K // 64, 256)
+        assert dg.DECISION_NAMES[p.decision] == d.kind == kind
+        assert p.splits == splits
+        if kind == "StreamK":
+            assert (p.sk_units, p.sk_tiles) == (d.sk_units, d.sk_tiles) == (256, 64)

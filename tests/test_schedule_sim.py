@@ -249,3 +249,11 @@ def test_batched_schedule_is_the_stacked_problem(M, N, K, batch, mode, splits):
     assert [x.as_tuple() for x in b.segments] == [x.as_tuple() for x in s.segments]
     cov = sch.coverage(b.segments, b.tiles, b.ipt)
     assert all(c == 1 for row in cov for c in row)
+
+
+def test_rule_splitk_needs_aligned_split():
+    # units = 4 per tile: Split-K only when 4 divides the tile's iterations
+    # (docc StreamK page, aligned split); 34 iterations fall back to Stream-K
+    assert sch.decide(64, 32, 256) == sch.Decision("SplitK", 64, 256)
+    assert sch.decide(64, 34, 256) == sch.Decision("StreamK", 64, 256)
+    assert sch.decide(64, 36, 256).kind == "SplitK"
