@@ -24,7 +24,7 @@ from pathlib import Path
 from typing import Optional
 
 __all__ = [
-    "GemmError", "GemmPlan", "GemmArgs", "gemm", "gemm_ex", "gemm_plan", "gemm_plan_batched",
+    "GemmError", "GemmPlan", "GemmArgs", "gemm", "gemm_ex", "gemm_ex_noalloc", "gemm_plan", "gemm_plan_batched",
     "gemm_workspace_size", "gemm_unit_range",
     "gemm_set_stream", "gemm_sync_status", "gemm_release", "gemm_last_error", "gemm_num_cus",
     "gemm_version", "gemm_tensors", "matmul", "plan_dict", "library_path",
@@ -67,6 +67,7 @@ GEMM_DEBUG_HYBRID_SPLIT = 0x10
 GEMM_DEBUG_ZERO_PARTIAL = 0x20
 
 GEMM_BM = 128
+GEMM_NOALLOC_MAX_BYTES = 32 * 1024 * 1024 + 256 * 1024   # gemm_ex_noalloc scratch per device
 GEMM_BN = 128
 GEMM_BK = 64
 
@@ -136,6 +137,8 @@ def _load() -> ctypes.CDLL:
     lib.gemm.argtypes = [vp, vp, vp, i64, i64, i64, u32, u32, i32]
     lib.gemm_ex.restype = ctypes.c_int
     lib.gemm_ex.argtypes = [ctypes.POINTER(GemmArgs)]
+    lib.gemm_ex_noalloc.restype = ctypes.c_int
+    lib.gemm_ex_noalloc.argtypes = [ctypes.POINTER(GemmArgs)]
     lib.gemm_plan.restype = ctypes.c_int
     lib.gemm_plan.argtypes = [i64, i64, i64, u32, u32, i32, i32, ctypes.POINTER(GemmPlan)]
     lib.gemm_workspace_size.restype = ctypes.c_int64
@@ -176,6 +179,11 @@ def gemm(A: int, B: int, C: int, M: int, N: int, K: int, layout: int, mode: int,
 
 def gemm_ex(args: GemmArgs) -> int:
     return _lib.gemm_ex(ctypes.byref(args))
+
+
+def gemm_ex_noalloc(args: GemmArgs) -> int:
+    """gemm_ex on the library's fixed per-device scratch array (no allocation)."""
+    return _lib.gemm_ex_noalloc(ctypes.byref(args))
 
 
 def gemm_plan(M: int, N: int, K: int, layout: int, mode: int, splits: int, num_cus: int) -> GemmPlan:
@@ -262,7 +270,7 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
                  atomic: bool = False, num_cus: int = 0, unit_perm=None, trace=None,
                  workspace=None, spin_limit: int = 0, debug: int = 0, timing=None,
                  stream=None, two_pass: bool = False, alpha: Optional[float] = None,
-                 beta: Optional[float] = None, bias=None, act: str = "none") -> None:
+                 beta: Optional[float] = None, bias=None, act: str = "none", noalloc: bool = False) -> None:
     """``c[M,N] = a[M,K] . b`` (b [K,N]) or ``a . b^T`` (b [N,K]) on torch tensors.
 
     Batched: c ``[batch, M, N]``; a and b ``[batch, ...]`` or 2-D (one matrix
@@ -275,6 +283,7 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
     unit_perm / trace / workspace / timing: optional int32 / int32 / any-dtype / int64
     device tensors (see gemm_args_t in include/gemm.h).
     Enqueues on ``stream`` (a torch.cuda.Stream) or torch's current stream.
+    ``noalloc``: call gemm_ex_noalloc (no workspace argument allowed).
     """
     import torch
 
@@ -351,7 +360,7 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
             word |= GEMM_EPI_BIAS
             args.bias = bias.data_ptr()
         args.epilogue = word
-        _check(gemm_ex(args))
+        _check(gemm_ex_noalloc(args) if noalloc else gemm_ex(args))
 
 
 def matmul(a, b, b_layout: str = "kn", out=None, alpha: Optional[float] = None, beta: Optional[float] = None,

@@ -65,8 +65,15 @@ int fail_hip(hipError_t e, const char *what) {
     return GEMM_ERR_HIP;
 }
 
+// Workspace of gemm_ex_noalloc: one fixed array per device, laid out like a
+// caller workspace ([status 256 B | flags | counters | data]).  Host code never
+// names it directly: its device address comes from hipGetSymbolAddress, once
+// per device (DeviceState::scratch).
+static __device__ __align__(256) unsigned char scratch[GEMM_NOALLOC_MAX_BYTES];
+
 struct DeviceState {
     bool ready = false;
+    unsigned char *scratch = nullptr;   // this device's copy of `scratch` (its device address)
     int num_cus = 0;
     uint32_t *control = nullptr;   // status words, then flags[cap_units], then counters[cap_tiles]
     int64_t cap_units = 0, cap_tiles = 0;
@@ -156,6 +163,27 @@ int ensure_data(DeviceState &d, int64_t bytes, hipStream_t stream) {
     return GEMM_OK;
 }
 
+// The device address of this device's `scratch` array, looked up the first time
+// gemm_ex_noalloc runs on the device (the device is current); its status words
+// are cleared then, on the call's stream (a kernel, so a captured first call
+// records no memset).
+int scratch_setup(DeviceState &d, hipStream_t stream) {
+    if (d.scratch) return GEMM_OK;
+    void *ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(GEMM_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+    if ((e = dgw::launch_zero(ptr, kStatusWords, stream)) != hipSuccess) return fail_hip(e, "zero scratch status");
+    d.scratch = static_cast<unsigned char *>(ptr);
+    return GEMM_OK;
+}
+
+int scratch_too_small(const gemm_plan_t &p) {
+    return fail(GEMM_ERR_WORKSPACE, "the call needs " + std::to_string(p.workspace_bytes) +
+                                        " workspace bytes; gemm_ex_noalloc holds at most " +
+                                        std::to_string((int64_t)GEMM_NOALLOC_MAX_BYTES));
+}
+
 bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
@@ -237,7 +265,9 @@ __global__ void put_trace_header(int *t, TraceHeader h) {
     if (threadIdx.x < 8) t[threadIdx.x] = h.v[threadIdx.x];
 }
 
-int run(const gemm_args_t &a) {
+// One call.  noalloc: the workspace is this device's `scratch` array and no
+// device memory is allocated (gemm_ex_noalloc).
+int run(const gemm_args_t &a, bool noalloc = false) {
     g_err.clear();
     gemm_plan_t p;
     const char *why = "";
@@ -253,6 +283,11 @@ int run(const gemm_args_t &a) {
     if ((rc = check_epilogue(a)) != GEMM_OK) return rc;
     if (a.M == 0 || a.N == 0) return GEMM_OK;
     if ((rc = check_operands(a)) != GEMM_OK) return rc;
+    if (noalloc) {
+        if (a.workspace) return fail(GEMM_ERR_INVALID, "gemm_ex_noalloc uses its own scratch: workspace must be NULL");
+        // with an explicit CU count this plan is final: refuse before any HIP call
+        if (a.num_cus > 0 && p.workspace_bytes > (int64_t)GEMM_NOALLOC_MAX_BYTES) return scratch_too_small(p);
+    }
 
     hipStream_t stream = a.stream ? reinterpret_cast<hipStream_t>(a.stream) : g_stream;
     int dev = 0;
@@ -265,6 +300,7 @@ int run(const gemm_args_t &a) {
     const int ncu = a.num_cus > 0 ? a.num_cus : ds->num_cus;
     if ((rc = dgw::make_plan(a.M, a.N, a.K, batch, a.layout, a.mode, a.splits, ncu, &p, &why)) != GEMM_OK)
         return fail(rc, why);
+    if (noalloc && p.workspace_bytes > (int64_t)GEMM_NOALLOC_MAX_BYTES) return scratch_too_small(p);
 
     const int dtype = (a.layout & 0xF0u) == GEMM_FP16 ? 1 : 0;
     const int blayout = (a.layout & 0xFu) == GEMM_B_NK ? 1 : 0;
@@ -303,26 +339,36 @@ int run(const gemm_args_t &a) {
                                                   std::to_string((int64_t)bpc * ds->num_cus) + ")");
     }
 
-    // the status word always lives in the library's control block; its flags and
-    // counters are used only without a caller workspace
-    if ((rc = a.workspace ? ensure_control(*ds, 1, 1, stream)
-                          : ensure_control(*ds, std::max<int64_t>(p.sk_units, 1), p.tiles, stream)) != GEMM_OK)
+    // the status word lives in the library's control block (the scratch array's
+    // first words for gemm_ex_noalloc); its flags and counters are used only
+    // without a caller workspace
+    if (noalloc) {
+        if ((rc = scratch_setup(*ds, stream)) != GEMM_OK) return rc;
+    } else if ((rc = a.workspace ? ensure_control(*ds, 1, 1, stream)
+                                 : ensure_control(*ds, std::max<int64_t>(p.sk_units, 1), p.tiles, stream)) !=
+               GEMM_OK) {
         return rc;
+    }
 
     // flags, counters and the data region
     uint32_t *flags = nullptr, *counters = nullptr;
     float *part = nullptr;
     const int64_t data_bytes = p.workspace_bytes - dgw::control_bytes(p);
-    if (a.workspace) {
-        if ((int64_t)a.workspace_bytes < p.workspace_bytes)
+    if (a.workspace || noalloc) {
+        if (a.workspace && (int64_t)a.workspace_bytes < p.workspace_bytes)
             return fail(GEMM_ERR_WORKSPACE, "caller workspace is smaller than plan.workspace_bytes (" +
                                                 std::to_string(p.workspace_bytes) + ")");
         const int64_t cb = dgw::control_bytes(p);
-        char *base = static_cast<char *>(a.workspace);
+        char *base = noalloc ? reinterpret_cast<char *>(ds->scratch) : static_cast<char *>(a.workspace);
         flags = reinterpret_cast<uint32_t *>(base + 256);
         counters = reinterpret_cast<uint32_t *>(base + 256 + (std::max<int64_t>(p.sk_units, 1) * 4 + 255) / 256 * 256);
         part = reinterpret_cast<float *>(base + cb);
-        if ((e = dgw::launch_zero(base, cb / 4, stream)) != hipSuccess) return fail_hip(e, "zero control");
+        // flags and counters start every call at zero (the scratch array keeps the
+        // last call's contents); the scratch status words stay until
+        // gemm_sync_status reads and clears them
+        const int64_t skip = noalloc ? 256 : 0;
+        if ((e = dgw::launch_zero(base + skip, (cb - skip) / 4, stream)) != hipSuccess)
+            return fail_hip(e, "zero control");
     } else {
         if ((rc = ensure_data(*ds, data_bytes, stream)) != GEMM_OK) return rc;
         flags = ds->control + kStatusWords;
@@ -348,7 +394,7 @@ int run(const gemm_args_t &a) {
     kp.part = part;
     kp.flags = flags;
     kp.counters = counters;
-    kp.status = ds->control;
+    kp.status = noalloc ? reinterpret_cast<uint32_t *>(ds->scratch) : ds->control;
     kp.spin_limit = a.spin_limit ? a.spin_limit : kDefaultSpin;
     kp.debug = a.debug;
     kp.perm = a.unit_perm;
@@ -485,6 +531,11 @@ int gemm_ex(const gemm_args_t *args) {
     return run(*args);
 }
 
+int gemm_ex_noalloc(const gemm_args_t *args) {
+    if (!args) return fail(GEMM_ERR_INVALID, "args is null");
+    return run(*args, true);
+}
+
 int gemm_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode, int32_t splits,
               int32_t num_cus, gemm_plan_t *out) {
     return gemm_plan_batched(M, N, K, 1, layout, mode, splits, num_cus, out);
@@ -521,10 +572,12 @@ int gemm_sync_status(void *stream) {
     int dev = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return fail_hip(e, "hipGetDevice");
     std::lock_guard<std::mutex> lock(g_mu);
-    if ((int)g_dev.size() <= dev || !g_dev[dev].control) return GEMM_OK;
-    // the current control block and the retired ones that captured graphs may still use
+    if ((int)g_dev.size() <= dev || (!g_dev[dev].control && !g_dev[dev].scratch)) return GEMM_OK;
+    // the current control block, the retired ones that captured graphs may still
+    // use, and the no-allocation scratch array's status words
     std::vector<uint32_t *> blocks = g_dev[dev].retired_control;
-    blocks.push_back(g_dev[dev].control);
+    if (g_dev[dev].control) blocks.push_back(g_dev[dev].control);
+    if (g_dev[dev].scratch) blocks.push_back(reinterpret_cast<uint32_t *>(g_dev[dev].scratch));
     uint32_t status = 0;
     for (uint32_t *blk : blocks) {
         uint32_t st = 0;

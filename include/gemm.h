@@ -315,6 +315,29 @@ int gemm(const void *A, const void *B, float *C, int64_t M, int64_t N, int64_t K
 int gemm_ex(const gemm_args_t *args);
 
 /*
+ * gemm_ex_noalloc -- gemm_ex() that allocates no device memory, for callers
+ * that cannot: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, same kernels and the same result bits
+ * as gemm_ex() with the library workspace, except:
+ *   - args->workspace must be NULL (else GEMM_ERR_INVALID): the workspace is a
+ *     fixed array of GEMM_NOALLOC_MAX_BYTES inside the library, one copy per
+ *     GPU, set up by the first call on that GPU and held until the process
+ *     ends.
+ *   - A call whose plan needs more (plan.workspace_bytes, e.g. Split-K
+ *     partials [S,M,N] beyond it) returns GEMM_ERR_WORKSPACE and launches
+ *     nothing.  Every decomposition of a 128x128-tile problem with at most 256
+ *     Stream-K units fits (two-pass Stream-K: 32 MiB of slots).
+ *   - Every call on a GPU shares that GPU's array and leaves its contents
+ *     behind; each call clears the flags and counters it uses (a kernel, no
+ *     memset).  Calls that overlap on one GPU race: order them on one stream
+ *     (or synchronise), as for the library workspace.
+ *   - gemm_sync_status() also reports the array's status word.
+ * Calls no hipMalloc, hipFree or other allocating routine.
+ */
+#define GEMM_NOALLOC_MAX_BYTES (32u * 1024u * 1024u + 256u * 1024u)
+int gemm_ex_noalloc(const gemm_args_t *args);
+
+/*
  * gemm_plan -- decide the decomposition for a call without running it.
  * num_cus >= 1 (no device is queried).  Fills *out; returns a status.
  */

@@ -355,3 +355,25 @@ def test_heuristic_splitk_factor_divides_iterations(dg):
         assert p.splits == splits
         if kind == "StreamK":
             assert (p.sk_units, p.sk_tiles) == (d.sk_units, d.sk_tiles) == (256, 64)
+
+
+def test_noalloc_refusals_before_any_hip_call(dg):
+    # host-side refusals of gemm_ex_noalloc (no device is touched): a plan whose
+    # workspace exceeds the fixed scratch array, and a caller workspace argument.
+    # The pointers are never dereferenced (aligned, non-overlapping addresses).
+    M = N = K = 2048
+    args = dg.GemmArgs()
+    args.A, args.B, args.C = 0x100000000, 0x200000000, 0x300000000
+    args.M, args.N, args.K = M, N, K
+    args.layout = dg.layout_word("kn", "bf16")
+    args.mode = dg.GEMM_SPLITK
+    args.splits = 4                      # partials [4, 2048, 2048] fp32 = 64 MiB
+    args.num_cus = 256
+    p = dg.gemm_plan(M, N, K, args.layout, args.mode, 4, 256)
+    assert p.workspace_bytes > dg.GEMM_NOALLOC_MAX_BYTES
+    assert dg.gemm_ex_noalloc(args) == dg.GEMM_ERR_WORKSPACE
+    assert "at most" in dg.gemm_last_error()
+    args.splits = 2
+    args.workspace, args.workspace_bytes = 0x400000000, 1 << 30
+    assert dg.gemm_ex_noalloc(args) == dg.GEMM_ERR_INVALID
+    assert "workspace must be NULL" in dg.gemm_last_error()
