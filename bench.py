@@ -63,7 +63,8 @@ def parse():
 class Call:
     """A prepared gemm_ex call (argument struct built once; each call is one ctypes call)."""
 
-    def __init__(self, dg, a, b, c, b_layout, mode, splits=0, atomic=False, stream=None, epilogue=None):
+    def __init__(self, dg, a, b, c, b_layout, mode, splits=0, atomic=False, stream=None, epilogue=None,
+                 tile="128x128"):
         import torch
 
         self.dg = dg
@@ -80,7 +81,7 @@ class Call:
         # `atomic`: False, True, "two_pass" (partials of split tiles added by a
         # second kernel) or "in_launch" (added in the launch: Split-K last arriver,
         # Stream-K turnstile)
-        args.mode = dg.mode_word(mode, atomic is True, atomic == "two_pass")
+        args.mode = dg.mode_word(mode, atomic is True, atomic == "two_pass", tile)
         if atomic == "in_launch":
             args.debug = dg.GEMM_DEBUG_IN_LAUNCH
         args.splits = splits
@@ -229,15 +230,18 @@ def shape_arms(dg, name, rounds):
         arms["splitk4"] = ("splitk", 4, False)
         arms["splitk2_two_pass"] = ("splitk", 2, "two_pass")
         arms["splitk4_two_pass"] = ("splitk", 4, "two_pass")
+        arms["streamk_256x128"] = ("streamk", 0, False)
     if name.startswith("c4"):
         arms = {"heuristic": ("heuristic", 0, False), "heuristic_epilogue": ("heuristic", 0, False, epi)}
     if name.startswith("c5"):
         arms["streamk_det"] = ("streamk", 0, False)
         arms["streamk_det_two_pass"] = ("streamk", 0, "two_pass")
         arms["streamk_atomic"] = ("streamk", 0, True)
+        arms["streamk_256x128"] = ("streamk", 0, False)
     if name.startswith("x1"):
         arms["heuristic"] = ("heuristic", 0, False)
         arms["streamk"] = ("streamk", 0, False)
+        arms["streamk_256x128"] = ("streamk", 0, False)
     if name.startswith("x2"):
         arms["heuristic"] = ("heuristic", 0, False)
         arms["streamk"] = ("streamk", 0, False)
@@ -245,8 +249,10 @@ def shape_arms(dg, name, rounds):
     out = {"M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype, "b_layout": w.b_layout}
     if w.batch > 1:
         out["batch"] = w.batch
-    calls = {arm: Call(dg, a, b, c, w.b_layout, mode, splits, atomic, epilogue=ep[0] if ep else None)
-             for arm, (mode, splits, atomic, *ep) in arms.items()}
+    calls = {}
+    for arm, (mode, splits, atomic, *ep) in arms.items():
+        tile = "256x128" if arm.endswith("256x128") else "128x128"
+        calls[arm] = Call(dg, a, b, c, w.b_layout, mode, splits, atomic, epilogue=ep[0] if ep else None, tile=tile)
     samples, pack = PROTOCOL[name[:2]]
     timed = time_arms(calls, rounds, samples, pack)
     out["protocol"] = {"rounds": rounds, "samples_per_round": samples, "calls_per_sample": pack,

@@ -53,6 +53,9 @@ GEMM_STREAMK = 0x3
 GEMM_DETERMINISTIC = 0x000
 GEMM_ATOMIC = 0x100
 GEMM_TWO_PASS = 0x200
+GEMM_TILE_128x128 = 0x0000
+GEMM_TILE_256x128 = 0x1000
+TILES = {"128x128": GEMM_TILE_128x128, "256x128": GEMM_TILE_256x128}
 
 GEMM_EPI_ALPHA_BETA = 0x01
 GEMM_EPI_BIAS = 0x02
@@ -246,8 +249,8 @@ def layout_word(b_layout: str, dtype: str) -> int:
     return lw | {"bf16": GEMM_BF16, "fp16": GEMM_FP16}[dtype]
 
 
-def mode_word(mode: str, atomic: bool = False, two_pass: bool = False) -> int:
-    return MODES[mode] | (GEMM_ATOMIC if atomic else 0) | (GEMM_TWO_PASS if two_pass else 0)
+def mode_word(mode: str, atomic: bool = False, two_pass: bool = False, tile: str = "128x128") -> int:
+    return MODES[mode] | (GEMM_ATOMIC if atomic else 0) | (GEMM_TWO_PASS if two_pass else 0) | TILES[tile]
 
 
 def _matrix_strides(name: str, t, rows: int, cols: int):
@@ -270,7 +273,8 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
                  atomic: bool = False, num_cus: int = 0, unit_perm=None, trace=None,
                  workspace=None, spin_limit: int = 0, debug: int = 0, timing=None,
                  stream=None, two_pass: bool = False, alpha: Optional[float] = None,
-                 beta: Optional[float] = None, bias=None, act: str = "none", noalloc: bool = False) -> None:
+                 beta: Optional[float] = None, bias=None, act: str = "none", noalloc: bool = False,
+                 tile: str = "128x128") -> None:
     """``c[M,N] = a[M,K] . b`` (b [K,N]) or ``a . b^T`` (b [N,K]) on torch tensors.
 
     Batched: c ``[batch, M, N]``; a and b ``[batch, ...]`` or 2-D (one matrix
@@ -284,6 +288,7 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
     device tensors (see gemm_args_t in include/gemm.h).
     Enqueues on ``stream`` (a torch.cuda.Stream) or torch's current stream.
     ``noalloc``: call gemm_ex_noalloc (no workspace argument allowed).
+    ``tile``: "128x128" or "256x128" (Stream-K only).
     """
     import torch
 
@@ -321,7 +326,7 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
     args.A, args.B, args.C = a.data_ptr(), b.data_ptr(), c.data_ptr()
     args.M, args.N, args.K = M, N, K
     args.layout = layout_word(b_layout, dtype)
-    args.mode = mode_word(mode, atomic, two_pass)
+    args.mode = mode_word(mode, atomic, two_pass, tile)
     args.splits = splits
     args.num_cus = num_cus
     if batch > 1:

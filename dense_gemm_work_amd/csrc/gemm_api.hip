@@ -81,7 +81,7 @@ struct DeviceState {
     int64_t cap_data = 0;
     std::vector<void *> retired;   // outgrown data blocks, freed by gemm_release()
     std::vector<uint32_t *> retired_control;   // outgrown control blocks (status word first)
-    int bpc[2][2][5] = {};         // resident workgroups per CU, 0 = not yet queried
+    int bpc[2][2][5][2] = {};      // resident workgroups per CU [dtype][B layout][kind][tall], 0 = not queried
 };
 
 std::mutex g_mu;
@@ -304,6 +304,9 @@ int run(const gemm_args_t &a, bool noalloc = false) {
 
     const int dtype = (a.layout & 0xF0u) == GEMM_FP16 ? 1 : 0;
     const int blayout = (a.layout & 0xFu) == GEMM_B_NK ? 1 : 0;
+    const bool tall = p.bm != GEMM_BM;   // 256 x 128 tiles
+    if (tall && a.epilogue != 0)
+        return fail(GEMM_ERR_UNSUPPORTED, "GEMM_TILE_256x128 has no fused epilogue");
 
     if (a.K == 0) {  // the empty sum
         if (a.epilogue == 0) {
@@ -329,9 +332,9 @@ int run(const gemm_args_t &a, bool noalloc = false) {
                                                   : dgw::K_SK;
     if (p.decision == GEMM_STREAMK) {
         // every unit must be resident at once: owners wait for higher units
-        int &bpc = ds->bpc[dtype][blayout][kmode];
+        int &bpc = ds->bpc[dtype][blayout][kmode][tall ? 1 : 0];
         if (bpc == 0) {
-            if ((e = dgw::blocks_per_cu(dtype, blayout, kmode, &bpc)) != hipSuccess)
+            if ((e = dgw::blocks_per_cu(dtype, blayout, kmode, p.bm, &bpc)) != hipSuccess)
                 return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
         }
         if (p.sk_units > (int64_t)bpc * ds->num_cus)
@@ -384,9 +387,11 @@ int run(const gemm_args_t &a, bool noalloc = false) {
     kp.M = (int)a.M;
     kp.N = (int)a.N;
     kp.K = (int)a.K;
+    kp.tm = p.bm;
     kp.tiles_m = (int)p.tiles_m;
     kp.tiles_n = (int)p.tiles_n;
-    kp.group_m = tuning().group_m;
+    // raster bands of group_m 128-row tile rows: the same height in rows for tall tiles
+    kp.group_m = tuning().group_m > 0 ? std::max(1, tuning().group_m * GEMM_BM / p.bm) : 0;
     kp.xcd_spread = a.unit_perm ? 0 : tuning().xcd_spread;
     kp.timing = reinterpret_cast<long long *>(a.timing);
     kp.ipt = (int)p.ipt;

@@ -77,9 +77,13 @@ constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = GEMM_BK;
 constexpr int SLAB = BM * BK;                 // 16-bit values per operand slab (A and B alike)
 constexpr int STAGE_BYTES = 2 * SLAB * 2;     // A slab then B slab: 32 KiB
 
-struct Acc {
-    f32x16 v[2][2];   // [i: 32-row block][j: 32-column block] of the wave's 64x64 quarter
+// Accumulators of one wave: its (TM / 2) x 64 part of a TM x 128 tile, as
+// [i: 32-row block][j: 32-column block].
+template <int TM>
+struct AccT {
+    f32x16 v[TM / 64][2];
 };
+using Acc = AccT<128>;
 
 // Wave roles in a workgroup of NW waves.
 template <int NW>
@@ -221,15 +225,27 @@ __device__ __forceinline__ u32x2 lds_tr16(uint32_t addr) {
 // other register buffer; issue the MFMAs of iteration i.  The MFMAs never wait
 // for LDS, and the fragment reads have a whole iteration to return.
 // ---------------------------------------------------------------------------
-constexpr int SLAB_BYTES = BM * BK * 2;   // 16 KiB
+constexpr int SLAB_BYTES = BM * BK * 2;   // 16 KiB: a B slab, or the A slab of a 128-row tile
 
-template <int DT, int BL, int NS, int NW>
+// Tile of TM x 128 (TM = 128, or 256 for the tall Stream-K tile): the A slab
+// is TM x 64, the B slab 64 x 128; each wave owns (TM / 2) x 64, i.e. RB
+// 32-row blocks by two 32-column blocks.
+template <int TM>
+constexpr int aslab_bytes() { return TM * BK * 2; }
+template <int TM>
+constexpr int lds_bytes(int ns) { return ns * (aslab_bytes<TM>() + SLAB_BYTES); }
+
+template <int DT, int BL, int NS, int NW, int TM = 128>
 struct MainLoop {
     static constexpr int KSW = 16 / NW;          // k-steps per wave and iteration
-    static constexpr int DPW = 16 / NW;          // loads per wave and operand slab
-    static constexpr int DPI = 2 * DPW;          // loads per wave and iteration
-    static constexpr int BREG = NS * SLAB_BYTES; // start of the B slabs
-    static_assert(NS == 4, "the unrolled loop body assumes four stages");
+    static constexpr int RB = TM / 64;           // 32-row blocks per wave
+    static constexpr int ASLAB = aslab_bytes<TM>();
+    static constexpr int DPWA = TM / 8 / NW;     // loads per wave of the A slab (1 KiB each)
+    static constexpr int DPWB = 16 / NW;         // loads per wave of the B slab
+    static constexpr int DPI = DPWA + DPWB;      // loads per wave and iteration
+    static constexpr int BREG = NS * ASLAB;      // start of the B slabs
+    static_assert(TM == 128 || TM == 256, "128- or 256-row tiles");
+    static_assert(NS >= 3 && NS <= 4, "three or four stages");
     static_assert(NW == 4 || NW == 8, "four or eight waves");
 
     const KParams &p;
@@ -239,8 +255,8 @@ struct MainLoop {
     // B [N,K]: block 0 per k-step; B [K,N]: column block jb at the wave's first k-step
     uint32_t aoff[KSW], boff[KSW > 2 ? KSW : 2];
     // per-lane global byte offsets of the wave's loads at k-slab 0
-    uint32_t adma[DPW], bdma[DPW];
-    int a_kc[DPW], b_kc[DPW];     // first k of the lane's chunk / B [K,N]: k-row of the lane
+    uint32_t adma[DPWA], bdma[DPWB];
+    int a_kc[DPWA], b_kc[DPWB];   // first k of the lane's chunk / B [K,N]: k-row of the lane
     const char *a_base, *b_base;
     uint32_t a_rows_bytes, b_rows_bytes;
 
@@ -256,7 +272,7 @@ struct MainLoop {
         for (int j = 0; j < KSW; ++j) {
             const int kk = kh * KSW + j;
             const uint32_t rowpart = (uint32_t)(r32 * 128 + ((((2 * kk + hk) ^ kswz(r32)) & 7) << 4));
-            aoff[j] = lds0 + wm * 8192 + rowpart;
+            aoff[j] = lds0 + wm * (TM / 2) * 128 + rowpart;
             if constexpr (BL == 1) boff[j] = lds0 + BREG + wn * 8192 + rowpart;
         }
         if constexpr (BL == 0) {
@@ -267,20 +283,24 @@ struct MainLoop {
                 boff[jb] = lds0 + BREG + r * 256 + ((((n >> 3) ^ nswz(r)) & 15) << 4) + ((n & 7) << 1);
             }
         }
-        const int first = wave * DPW;
         a_base = reinterpret_cast<const char *>(p.A) + (size_t)m0 * K * 2;
-        a_rows_bytes = (uint32_t)(min(BM, p.M - m0) * K * 2);
+        a_rows_bytes = (uint32_t)(min(TM, p.M - m0) * K * 2);
 #pragma unroll
-        for (int x = 0; x < DPW; ++x) {
-            const int r = 8 * (first + x) + (lane >> 3);
+        for (int x = 0; x < DPWA; ++x) {
+            const int r = 8 * (wave * DPWA + x) + (lane >> 3);
             const int c = (lane & 7) ^ kswz(r);
             adma[x] = (uint32_t)(r * K + 8 * c) * 2;
             a_kc[x] = 8 * c;
+        }
+#pragma unroll
+        for (int x = 0; x < DPWB; ++x) {
             if constexpr (BL == 1) {
-                bdma[x] = adma[x];
+                const int r = 8 * (wave * DPWB + x) + (lane >> 3);
+                const int c = (lane & 7) ^ kswz(r);
+                bdma[x] = (uint32_t)(r * K + 8 * c) * 2;
                 b_kc[x] = 8 * c;
             } else {
-                const int rb = 4 * (first + x) + (lane >> 4);
+                const int rb = 4 * (wave * DPWB + x) + (lane >> 4);
                 const int cb = (lane & 15) ^ nswz(rb);
                 // chunks beyond N (last tile column only) always read zeros
                 bdma[x] = n0 + 8 * cb >= N ? OOB : (uint32_t)(rb * N + 8 * cb) * 2;
@@ -301,7 +321,6 @@ struct MainLoop {
     template <bool RAGGED>
     __device__ __forceinline__ void issue(int slab, int st) const {
         const int kb = slab * BK;
-        const int first = wave * DPW;
         const i32x4 ra = make_rsrc(a_base + (size_t)kb * 2, a_rows_bytes - kb * 2);
         i32x4 rb;
         int krows = BK;
@@ -311,12 +330,12 @@ struct MainLoop {
             krows = min(BK, p.K - kb);   // k-rows beyond K fall outside the range
             rb = make_rsrc(b_base + (size_t)kb * p.N * 2, (uint32_t)(krows * p.N * 2));
         }
-        const uint32_t a_dst = lds0 + st * SLAB_BYTES + first * 1024;
-        const uint32_t b_dst = lds0 + BREG + st * SLAB_BYTES + first * 1024;
+        const uint32_t a_dst = lds0 + st * ASLAB + wave * DPWA * 1024;
+        const uint32_t b_dst = lds0 + BREG + st * SLAB_BYTES + wave * DPWB * 1024;
 #pragma unroll
-        for (int x = 0; x < DPW; ++x) dma16(ra, a_dst + x * 1024, !RAGGED || kb + a_kc[x] < p.K ? adma[x] : OOB);
+        for (int x = 0; x < DPWA; ++x) dma16(ra, a_dst + x * 1024, !RAGGED || kb + a_kc[x] < p.K ? adma[x] : OOB);
 #pragma unroll
-        for (int x = 0; x < DPW; ++x) {
+        for (int x = 0; x < DPWB; ++x) {
             uint32_t off = bdma[x];
             if constexpr (RAGGED && BL == 1) off = kb + b_kc[x] < p.K ? off : OOB;
             dma16(rb, b_dst + x * 1024, off);
@@ -324,16 +343,29 @@ struct MainLoop {
     }
 
     struct Frags {
-        u32x4 a[KSW][2];   // [k-step][32-row block]
+        u32x4 a[KSW][RB];  // [k-step][32-row block]
         u32x4 b[KSW][2];   // [k-step][32-column block]
     };
 
     template <int ST>
     __device__ __forceinline__ void read(Frags &f) const {
+        // A fragment offsets are immediates of at most 64 KiB: a stage that lies
+        // beyond moves 48 KiB of its offset into the base address
+        constexpr int AO = ST * ASLAB;
+        constexpr int AHI = AO + (RB - 1) * 4096 >= 65536 ? 49152 : 0;
 #pragma unroll
         for (int j = 0; j < KSW; ++j) {
-            f.a[j][0] = lds_b128<ST * SLAB_BYTES>(aoff[j]);
-            f.a[j][1] = lds_b128<ST * SLAB_BYTES + 4096>(aoff[j]);
+            const uint32_t abase = aoff[j] + AHI;
+            auto row_block = [&](auto RBC) {
+                constexpr int rb = decltype(RBC)::value;
+                f.a[j][rb] = lds_b128<AO - AHI + rb * 4096>(abase);
+            };
+            row_block(std::integral_constant<int, 0>());
+            row_block(std::integral_constant<int, 1>());
+            if constexpr (RB > 2) {
+                row_block(std::integral_constant<int, 2>());
+                row_block(std::integral_constant<int, 3>());
+            }
             if constexpr (BL == 1) {
                 f.b[j][0] = lds_b128<ST * SLAB_BYTES>(boff[j]);
                 f.b[j][1] = lds_b128<ST * SLAB_BYTES + 4096>(boff[j]);
@@ -351,11 +383,55 @@ struct MainLoop {
         }
     }
 
-    static __device__ __forceinline__ void mma(const Frags &f, Acc &acc) {
+    // One k-step's fragments (the tall tile's loop double-buffers per k-step:
+    // a whole iteration's fragments next to its 128 accumulator registers would
+    // not fit two waves per SIMD).
+    struct StepFrags {
+        u32x4 a[RB];
+        u32x4 b[2];
+    };
+
+    // Fragments of the wave's k-step J (0 .. KSW - 1) of stage ST.
+    template <int ST, int J>
+    __device__ __forceinline__ void read_step(StepFrags &f) const {
+        constexpr int AO = ST * ASLAB;
+        constexpr int AHI = AO + (RB - 1) * 4096 >= 65536 ? 49152 : 0;
+        const uint32_t abase = aoff[J] + AHI;
+        auto row_block = [&](auto RBC) {
+            constexpr int rb = decltype(RBC)::value;
+            f.a[rb] = lds_b128<AO - AHI + rb * 4096>(abase);
+        };
+        row_block(std::integral_constant<int, 0>());
+        row_block(std::integral_constant<int, 1>());
+        if constexpr (RB > 2) {
+            row_block(std::integral_constant<int, 2>());
+            row_block(std::integral_constant<int, 3>());
+        }
+        if constexpr (BL == 1) {
+            f.b[0] = lds_b128<ST * SLAB_BYTES>(boff[J]);
+            f.b[1] = lds_b128<ST * SLAB_BYTES + 4096>(boff[J]);
+        } else {
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                const u32x2 h0 = lds_tr16<ST * SLAB_BYTES + J * 4096>(boff[jb]);
+                const u32x2 h1 = lds_tr16<ST * SLAB_BYTES + J * 4096 + 1024>(boff[jb]);
+                f.b[jb] = u32x4{h0[0], h0[1], h1[0], h1[1]};
+            }
+        }
+    }
+
+    static __device__ __forceinline__ void mma_step(const StepFrags &f, AccT<TM> &acc) {
+#pragma unroll
+        for (int a = 0; a < RB; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) acc.v[a][b] = mfma<DT>(f.a[a], f.b[b], acc.v[a][b]);
+    }
+
+    static __device__ __forceinline__ void mma(const Frags &f, AccT<TM> &acc) {
 #pragma unroll
         for (int j = 0; j < KSW; ++j)
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < RB; ++a)
 #pragma unroll
                 for (int b = 0; b < 2; ++b) acc.v[a][b] = mfma<DT>(f.a[j][a], f.b[j][b], acc.v[a][b]);
     }
@@ -368,10 +444,10 @@ struct MainLoop {
 // With 8 waves each wave covers half of every slab's k-steps and holds a
 // partial sum of its quarter (see merge_k_halves).  Ends with a barrier, so the
 // LDS is free again on return.
-template <int DT, int BL, int NS, int NW, bool RAGGED>
+template <int DT, int BL, int NS, int NW, int TM, bool RAGGED>
 __device__ __forceinline__ void mac_loop_impl(const KParams &p, char *lds, int m0, int n0, int k0, int k1,
-                                              int rot, Acc &acc, int *cov, uint32_t *raise) {
-    using ML = MainLoop<DT, BL, NS, NW>;
+                                              int rot, AccT<TM> &acc, int *cov, uint32_t *raise) {
+    using ML = MainLoop<DT, BL, NS, NW, TM>;
     constexpr int DPI = ML::DPI;
     const int n = k1 - k0;
     if (n <= 0) return;
@@ -388,7 +464,7 @@ __device__ __forceinline__ void mac_loop_impl(const KParams &p, char *lds, int m
     issue_next(0);
     if (n > 1) issue_next(1);
     if (n > 2) issue_next(2);
-    if (n > 3) issue_next(3);
+    if (NS > 3 && n > 3) issue_next(3);
     wait_vm_lgkm_stages<DPI>(min(NS, n) - 1);   // this wave's loads of iteration 0 landed
     __builtin_amdgcn_s_barrier();
     // A partial published just before this loop: its stores were issued before
@@ -398,98 +474,190 @@ __device__ __forceinline__ void mac_loop_impl(const KParams &p, char *lds, int m
     if (raise && threadIdx.x == 0) __hip_atomic_store(raise, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     ml.template read<0>(f[0]);
     int done = 0;                              // iterations issued to the matrix cores
-    // One iteration; U = i % NS (the stage and, with NS even, the fragment buffer parity).
-    auto body = [&](int i, auto U, auto STEADY) {
+    // One iteration i: its stage U = i % NS, its register buffer P = i % 2.
+    auto body = [&](int i, auto U, auto P, auto STEADY) {
         constexpr int u = decltype(U)::value;
+        constexpr int par = decltype(P)::value;
         constexpr bool steady = decltype(STEADY)::value;
         if constexpr (steady) wait_vm_lgkm<(NS - 2) * DPI>();
         else wait_vm_lgkm_stages<DPI>(max(0, min(NS - 2, n - i - 2)));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         if (steady || i + NS < n) issue_next(u);
-        if (steady || i + 1 < n) ml.template read<(u + 1) % NS>(f[(u + 1) & 1]);
-        ML::mma(f[u & 1], acc);
+        if (steady || i + 1 < n) ml.template read<(u + 1) % NS>(f[par ^ 1]);
+        ML::mma(f[par], acc);
         __builtin_amdgcn_sched_barrier(0);
         ++done;
     };
+    // the loop body is unrolled over L = lcm(NS, 2) iterations, so that both the
+    // stage and the register buffer of every iteration are compile-time constants
+    constexpr int L = NS % 2 == 0 ? NS : 2 * NS;
+    using T = std::true_type;
+    using F = std::false_type;
+    auto group = [&](int i0, auto STEADY) {
+        using ST = decltype(STEADY);
+        body(i0 + 0, std::integral_constant<int, 0 % NS>(), std::integral_constant<int, 0>(), ST());
+        if (ST::value || i0 + 1 < n) body(i0 + 1, std::integral_constant<int, 1 % NS>(), std::integral_constant<int, 1>(), ST());
+        if (ST::value || i0 + 2 < n) body(i0 + 2, std::integral_constant<int, 2 % NS>(), std::integral_constant<int, 0>(), ST());
+        if (ST::value || i0 + 3 < n) body(i0 + 3, std::integral_constant<int, 3 % NS>(), std::integral_constant<int, 1>(), ST());
+        if constexpr (L == 6) {
+            if (ST::value || i0 + 4 < n) body(i0 + 4, std::integral_constant<int, 4 % NS>(), std::integral_constant<int, 0>(), ST());
+            if (ST::value || i0 + 5 < n) body(i0 + 5, std::integral_constant<int, 5 % NS>(), std::integral_constant<int, 1>(), ST());
+        }
+    };
     int i0 = 0;
-    for (; i0 + 2 * NS <= n; i0 += NS) {
-        body(i0 + 0, std::integral_constant<int, 0>(), std::true_type());
-        body(i0 + 1, std::integral_constant<int, 1>(), std::true_type());
-        body(i0 + 2, std::integral_constant<int, 2>(), std::true_type());
-        body(i0 + 3, std::integral_constant<int, 3>(), std::true_type());
-    }
-    for (; i0 < n; i0 += NS) {
-        body(i0 + 0, std::integral_constant<int, 0>(), std::false_type());
-        if (i0 + 1 < n) body(i0 + 1, std::integral_constant<int, 1>(), std::false_type());
-        if (i0 + 2 < n) body(i0 + 2, std::integral_constant<int, 2>(), std::false_type());
-        if (i0 + 3 < n) body(i0 + 3, std::integral_constant<int, 3>(), std::false_type());
-    }
+    for (; i0 + L + NS <= n; i0 += L) group(i0, T());
+    for (; i0 < n; i0 += L) group(i0, F());
     wait_stage0();
     // debug coverage: one count per logical iteration the loop above executed
     if (cov && threadIdx.x == 0)
         for (int k = 0; k < done; ++k) atomicAdd(cov + k0 + k, 1);
 }
 
+// The same iterations for the 256 x 128 tile, fragments double-buffered per
+// k-step.  Iteration i on stage U = i % NS, the wave's k-step 0 already in F0:
+// read k-step 1 into F1 and multiply F0; then (unless i is the last) wait for
+// this wave's loads of i + 1 and its reads of F1, barrier (every wave's loads
+// of i + 1 landed, every wave done reading stage U), read k-step 0 of i + 1
+// into F0 and issue the loads of i + NS into stage U; multiply F1.
+template <int DT, int BL, int NS, int NW, bool RAGGED>
+__device__ __forceinline__ void mac_loop_tall_impl(const KParams &p, char *lds, int m0, int n0, int k0, int k1,
+                                                   int rot, AccT<256> &acc, int *cov, uint32_t *raise) {
+    using ML = MainLoop<DT, BL, NS, NW, 256>;
+    static_assert(ML::KSW == 2, "two k-steps per wave and iteration");
+    constexpr int DPI = ML::DPI;
+    const int n = k1 - k0;
+    if (n <= 0) return;
+    const ML ml(p, lds, m0, n0);
+    const int ipt = p.ipt;
+    int phys = k0 + rot;                       // physical slab of the next load
+    phys = phys >= ipt ? phys - ipt : phys;
+    phys = phys >= ipt ? phys - ipt : phys;
+    auto issue_next = [&](int st) {
+        ml.template issue<RAGGED>(phys, st);
+        phys = phys + 1 == ipt ? 0 : phys + 1;
+    };
+    typename ML::StepFrags f0, f1;
+    issue_next(0);
+    if (n > 1) issue_next(1);
+    if (n > 2) issue_next(2);
+    if (NS > 3 && n > 3) issue_next(3);
+    wait_vm_lgkm_stages<DPI>(min(NS, n) - 1);   // this wave's loads of iteration 0 landed
+    __builtin_amdgcn_s_barrier();
+    // a partial published just before this loop: see mac_loop_impl
+    if (raise && threadIdx.x == 0) __hip_atomic_store(raise, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ml.template read_step<0, 0>(f0);
+    int done = 0;
+    auto iter = [&](int i, auto U, auto STEADY) {
+        constexpr int u = decltype(U)::value;
+        constexpr bool steady = decltype(STEADY)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        ml.template read_step<u, 1>(f1);
+        ML::mma_step(f0, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (steady || i + 1 < n) {
+            if constexpr (steady) wait_vm_lgkm<(NS - 2) * DPI>();
+            else wait_vm_lgkm_stages<DPI>(max(0, min(NS - 2, n - i - 2)));
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            ml.template read_step<(u + 1) % NS, 0>(f0);
+            if (steady || i + NS < n) issue_next(u);
+        }
+        ML::mma_step(f1, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        ++done;
+    };
+    auto group = [&](int i0, auto STEADY) {
+        using ST = decltype(STEADY);
+        iter(i0 + 0, std::integral_constant<int, 0>(), ST());
+        if (ST::value || i0 + 1 < n) iter(i0 + 1, std::integral_constant<int, 1 % NS>(), ST());
+        if (ST::value || i0 + 2 < n) iter(i0 + 2, std::integral_constant<int, 2 % NS>(), ST());
+        if constexpr (NS == 4)
+            if (ST::value || i0 + 3 < n) iter(i0 + 3, std::integral_constant<int, 3>(), ST());
+    };
+    int i0 = 0;
+    for (; i0 + 2 * NS <= n; i0 += NS) group(i0, std::true_type());
+    for (; i0 < n; i0 += NS) group(i0, std::false_type());
+    wait_stage0();
+    if (cov && threadIdx.x == 0)
+        for (int k = 0; k < done; ++k) atomicAdd(cov + k0 + k, 1);
+}
+
 // `raise` (optional): a flag to set to p.epoch once this workgroup's earlier
 // global stores are complete (the loop's first wait establishes that).
-template <int DT, int BL, int NS, int NW>
+template <int DT, int BL, int NS, int NW, int TM = 128>
 __device__ __forceinline__ void mac_loop(const KParams &p, char *lds, int m0, int n0, int k0, int k1,
-                                         int rot, Acc &acc, int *cov, uint32_t *raise = nullptr) {
-    if (p.K % BK == 0) mac_loop_impl<DT, BL, NS, NW, false>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise);
-    else mac_loop_impl<DT, BL, NS, NW, true>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise);
+                                         int rot, AccT<TM> &acc, int *cov, uint32_t *raise = nullptr) {
+    if constexpr (TM == 256) {
+        if (p.K % BK == 0) mac_loop_tall_impl<DT, BL, NS, NW, false>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise);
+        else mac_loop_tall_impl<DT, BL, NS, NW, true>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise);
+    } else {
+        if (p.K % BK == 0) mac_loop_impl<DT, BL, NS, NW, TM, false>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise);
+        else mac_loop_impl<DT, BL, NS, NW, TM, true>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise);
+    }
 }
 
 // With 8 waves the two waves of a quadrant (k-halves 0 and 1) each hold a
-// partial sum of the whole 64x64 quarter.  They swap halves through LDS: wave
-// (quad, kh) sends its 32-row block 1 - kh to its partner and adds the
-// partner's block kh to its own, so afterwards it holds the complete sums of
-// block row kh (fp32 addition is commutative, so both block rows are exactly
-// acc(kh 0) + acc(kh 1)).  With 4 waves every wave already holds both block
-// rows.  The result names its block rows at run time but keeps the values in
-// fixed registers (the accumulator is only ever indexed by constants, so it
-// stays in registers).  `lds` must be free; it is free on return.
-template <int NW>
+// partial sum of the whole (TM / 2) x 64 part of the tile.  They swap halves
+// through LDS: of its RB 32-row blocks, wave (quad, kh) keeps blocks
+// kh R .. kh R + R - 1 (R = RB / 2), sends the others to its partner and adds
+// the partner's copies of the kept ones, so afterwards it holds the complete
+// sums of R block rows (fp32 addition is commutative, so both waves' blocks
+// are exactly acc(kh 0) + acc(kh 1)).  With 4 waves every wave already holds
+// all its block rows.  The result names its block rows at run time but keeps
+// the values in fixed registers (the accumulator is only ever indexed by
+// constants, so it stays in registers).  `lds` must be free (TM / 2 KiB per
+// wave); it is free on return.
+template <int NW, int TM = 128>
 struct Tile {
-    static constexpr int R = NW == 8 ? 1 : 2;   // block rows a wave holds
-    f32x16 v[R][2];                             // [held row][32-column block]
-    int i[R];                                   // which 32-row block of the quarter
+    static constexpr int RB = TM / 64;              // 32-row blocks of a wave's part
+    static constexpr int R = NW == 8 ? RB / 2 : RB; // block rows a wave holds
+    f32x16 v[R][2];                                 // [held row][32-column block]
+    int i[R];                                       // which 32-row block of the wave's part
 };
 
-template <int NW>
-__device__ __forceinline__ Tile<NW> merge_k_halves(const Acc &acc, char *lds) {
-    Tile<NW> t;
+template <int NW, int TM = 128>
+__device__ __forceinline__ Tile<NW, TM> merge_k_halves(const AccT<TM> &acc, char *lds) {
+    Tile<NW, TM> t;
+    constexpr int R = Tile<NW, TM>::R;
     if constexpr (NW == 8) {
         const Role<NW> w;
         const bool hi = w.kh != 0;
         f32x4 *buf = reinterpret_cast<f32x4 *>(lds);
+        // wave (quad, kh) writes R x 2 blocks of 16 floats per lane at slot
+        // ((quad * 2 + kh) * R * 8 + (r * 2 + j) * 4 + e4) * 64 + lane
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const f32x16 give = hi ? acc.v[0][j] : acc.v[1][j];
+        for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4)
-                buf[((w.quad * 2 + w.kh) * 8 + j * 4 + e4) * 64 + w.lane] =
-                    f32x4{give[4 * e4], give[4 * e4 + 1], give[4 * e4 + 2], give[4 * e4 + 3]};
-        }
+            for (int j = 0; j < 2; ++j) {
+                const f32x16 give = hi ? acc.v[r][j] : acc.v[R + r][j];
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4)
+                    buf[((w.quad * 2 + w.kh) * R * 8 + (r * 2 + j) * 4 + e4) * 64 + w.lane] =
+                        f32x4{give[4 * e4], give[4 * e4 + 1], give[4 * e4 + 2], give[4 * e4 + 3]};
+            }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            f32x16 keep = hi ? acc.v[1][j] : acc.v[0][j];
+        for (int r = 0; r < R; ++r) {
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const f32x4 x = buf[((w.quad * 2 + (1 - w.kh)) * 8 + j * 4 + e4) * 64 + w.lane];
-                keep[4 * e4] += x[0];
-                keep[4 * e4 + 1] += x[1];
-                keep[4 * e4 + 2] += x[2];
-                keep[4 * e4 + 3] += x[3];
+            for (int j = 0; j < 2; ++j) {
+                f32x16 keep = hi ? acc.v[R + r][j] : acc.v[r][j];
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const f32x4 x = buf[((w.quad * 2 + (1 - w.kh)) * R * 8 + (r * 2 + j) * 4 + e4) * 64 + w.lane];
+                    keep[4 * e4] += x[0];
+                    keep[4 * e4 + 1] += x[1];
+                    keep[4 * e4 + 2] += x[2];
+                    keep[4 * e4 + 3] += x[3];
+                }
+                t.v[r][j] = keep;
             }
-            t.v[0][j] = keep;
+            t.i[r] = w.kh * R + r;
         }
-        t.i[0] = w.kh;
         __syncthreads();
     } else {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
+        for (int r = 0; r < R; ++r) {
             t.v[r][0] = acc.v[r][0];
             t.v[r][1] = acc.v[r][1];
             t.i[r] = r;
@@ -534,7 +702,7 @@ __device__ __forceinline__ void tile_origin(const KParams &p, int tile, int &m0,
     const int first = g * gm_full;
     const int gm = min(gm_full, p.tiles_m - first);
     const int w = tile - g * per_group;
-    m0 = (first + w % gm) * BM;
+    m0 = (first + w % gm) * p.tm;
     n0 = (w / gm) * BN;
 }
 
@@ -567,26 +735,27 @@ __device__ __forceinline__ KParams tile_view(const KParams &p, int tile, int &m0
 // wave's quarter (output layout of the 32x32 MFMA).  After merge_k_halves each
 // wave touches only the block rows it owns.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void zero_acc(Acc &acc) {
+template <int TM>
+__device__ __forceinline__ void zero_acc(AccT<TM> &acc) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM / 64; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc.v[i][j][e] = 0.0f;
 }
 
-template <int NW, class F>
-__device__ __forceinline__ void for_each_element(const Tile<NW> &t, int m0, int n0, int M, int N, F &&f) {
+template <int NW, int TM, class F>
+__device__ __forceinline__ void for_each_element(const Tile<NW, TM> &t, int m0, int n0, int M, int N, F &&f) {
     const Role<NW> w;
 #pragma unroll
-    for (int r = 0; r < Tile<NW>::R; ++r)
+    for (int r = 0; r < Tile<NW, TM>::R; ++r)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int col = n0 + w.wn * 64 + j * 32 + (w.lane & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = m0 + w.wm * 64 + t.i[r] * 32 + 8 * (e >> 2) + 4 * (w.lane >> 5) + (e & 3);
+                const int row = m0 + w.wm * (TM / 2) + t.i[r] * 32 + 8 * (e >> 2) + 4 * (w.lane >> 5) + (e & 3);
                 if (row < M && col < N) f(t.v[r][j][e], (size_t)row * N + col);
             }
         }
@@ -644,8 +813,8 @@ __device__ __forceinline__ void put_quad(float *dst, f32x4 v, int nvalid, bool v
 
 // Write the held rows to C straight from registers: each store instruction
 // writes two 128-byte row segments (lanes 0-31 and 32-63), non-temporal.
-template <int NW>
-__device__ __forceinline__ void store_tile(float *X, int m0, int n0, int M, int N, const Tile<NW> &t) {
+template <int NW, int TM>
+__device__ __forceinline__ void store_tile(float *X, int m0, int n0, int M, int N, const Tile<NW, TM> &t) {
     for_each_element<NW>(t, m0, n0, M, N, [&](float v, size_t off) { __builtin_nontemporal_store(v, X + off); });
 }
 
@@ -829,32 +998,37 @@ __device__ __forceinline__ void finish_block(const KParams &p, int m0, int n0, c
 
 // store_tile with the epilogue: the prior C values of the held rows are loaded
 // before the first store.
-template <int NW, bool EPI = true>
-__device__ __forceinline__ void store_final(const KParams &p, int m0, int n0, const Tile<NW> &t) {
-    if (!EPI || p.epi == EPI_PLAIN) {
+template <int NW, bool EPI = true, int TM = 128>
+__device__ __forceinline__ void store_final(const KParams &p, int m0, int n0, const Tile<NW, TM> &t) {
+    static_assert(!EPI || TM == 128, "the fused epilogue serves 128-row tiles");
+    if constexpr (!EPI) {
         store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
-        return;
-    }
-    const Role<NW> w;
-    const bool rc = reads_c(p);
-    const int C0 = n0 + w.wn * 64;
-    float bj[2];
-    lane_bias<2>(p, C0, bj);
+    } else {
+        if (p.epi == EPI_PLAIN) {
+            store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
+            return;
+        }
+        const Role<NW> w;
+        const bool rc = reads_c(p);
+        const int C0 = n0 + w.wn * 64;
+        float bj[2];
+        lane_bias<2>(p, C0, bj);
 #pragma unroll
-    for (int r = 0; r < Tile<NW>::R; ++r) {
-        const CBlock<2> cb(p, m0 + w.wm * 64 + t.i[r] * 32, C0);
-        float cin[32];
+        for (int r = 0; r < Tile<NW>::R; ++r) {
+            const CBlock<2> cb(p, m0 + w.wm * 64 + t.i[r] * 32, C0);
+            float cin[32];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) cin[j * 16 + e] = rc ? cb.load(e, j) : 0.0f;
-        finish_block<NW>(p, m0, n0, t, r, cin, bj);
+                for (int e = 0; e < 16; ++e) cin[j * 16 + e] = rc ? cb.load(e, j) : 0.0f;
+            finish_block<NW>(p, m0, n0, t, r, cin, bj);
+        }
     }
 }
 
 // Split parts of atomic merges: C += acc (EPI_ACCUM: C += alpha acc).
-template <int NW, bool EPI = true>
-__device__ __forceinline__ void atomic_add_c(const KParams &p, int m0, int n0, const Tile<NW> &t) {
+template <int NW, bool EPI = true, int TM = 128>
+__device__ __forceinline__ void atomic_add_c(const KParams &p, int m0, int n0, const Tile<NW, TM> &t) {
     if (zero_partials(p)) {
         for_each_element<NW>(t, m0, n0, p.M, p.N, [&](float, size_t off) { unsafeAtomicAdd(p.C + off, 0.0f); });
     } else if (EPI && p.epi == EPI_ACCUM) {
@@ -944,45 +1118,47 @@ __device__ __forceinline__ float get_coherent(const float *p) {
 // Wait until every vector-memory operation of this wave has completed.
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
 
-// Stream-K partial slot (64 KiB) in register-native order: for accumulator block
-// b = 2 i + j of a quarter and element quad e4, the 64 lanes of a wave move
-// 1 KiB of contiguous memory.
+// Stream-K partial slot (TM x 128 fp32: 64 or 128 KiB) in register-native
+// order: for accumulator block b = 2 i + j of a wave's part and element quad
+// e4, the 64 lanes of a wave move 1 KiB of contiguous memory.
+template <int TM = 128>
 __device__ __forceinline__ uint32_t slot_off(int quad, int b, int e4, int lane) {
-    return (uint32_t)((((quad * 4 + b) * 4 + e4) * 64 + lane) * 16);
+    return (uint32_t)((((quad * 2 * (TM / 64) + b) * 4 + e4) * 64 + lane) * 16);
 }
 
-template <int NW>
-__device__ __forceinline__ void put_slot(float *slot, const Tile<NW> &t, bool zero) {
+template <int NW, int TM>
+__device__ __forceinline__ void put_slot(float *slot, const Tile<NW, TM> &t, bool zero) {
     const Role<NW> w;
-    const __amdgpu_buffer_rsrc_t r = span(slot, BM * BN * 4);
+    const __amdgpu_buffer_rsrc_t r = span(slot, TM * BN * 4);
     const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};   // the zero-partial control
 #pragma unroll
-    for (int h = 0; h < Tile<NW>::R; ++h)
+    for (int h = 0; h < Tile<NW, TM>::R; ++h)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
                 const f32x16 &v = t.v[h][j];
-                put4_coherent(r, slot_off(w.quad, 2 * t.i[h] + j, e4, w.lane),
+                put4_coherent(r, slot_off<TM>(w.quad, 2 * t.i[h] + j, e4, w.lane),
                               zero ? zero4 : f32x4{v[4 * e4], v[4 * e4 + 1], v[4 * e4 + 2], v[4 * e4 + 3]});
             }
 }
 
 // t += slot over the held rows.  Every load is issued before the first add, so
 // the wave waits for the partial once.
-template <int NW>
-__device__ __forceinline__ void add_slot(const float *slot, Tile<NW> &t) {
+template <int NW, int TM>
+__device__ __forceinline__ void add_slot(const float *slot, Tile<NW, TM> &t) {
     const Role<NW> w;
-    const __amdgpu_buffer_rsrc_t r = span(slot, BM * BN * 4);
-    f32x4 x[Tile<NW>::R][2][4];
+    const __amdgpu_buffer_rsrc_t r = span(slot, TM * BN * 4);
+    f32x4 x[Tile<NW, TM>::R][2][4];
 #pragma unroll
-    for (int h = 0; h < Tile<NW>::R; ++h)
+    for (int h = 0; h < Tile<NW, TM>::R; ++h)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) x[h][j][e4] = get4_coherent(r, slot_off(w.quad, 2 * t.i[h] + j, e4, w.lane));
+            for (int e4 = 0; e4 < 4; ++e4)
+                x[h][j][e4] = get4_coherent(r, slot_off<TM>(w.quad, 2 * t.i[h] + j, e4, w.lane));
 #pragma unroll
-    for (int h = 0; h < Tile<NW>::R; ++h)
+    for (int h = 0; h < Tile<NW, TM>::R; ++h)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1771,9 +1947,11 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
 // units stream the same few K-slabs at any moment and the A and B panels
 // shared by neighbouring tiles are reused from the XCD's L2.
 // ---------------------------------------------------------------------------
-template <int DT, int BL, int NS, int NW, bool ATOMIC, bool EPI>
+template <int DT, int BL, int NS, int NW, bool ATOMIC, bool EPI, int TM = 128>
 __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
-    __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_BYTES];
+    static_assert(!EPI || TM == 128, "the fused epilogue serves 128-row tiles");
+    constexpr int SLOT = TM * BN;              // floats of one partial slot
+    __shared__ __attribute__((aligned(16))) char lds[lds_bytes<TM>(NS)];
     const WgClock clk(p);
     const int u = worker_of(p, p.units);
     const int ipt = p.ipt;
@@ -1785,10 +1963,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
     for (int tile = u; tile < p.dp_tiles; tile += p.units) {
         int m0, n0;
         const KParams pv = tile_view(p, tile, m0, n0);
-        Acc acc;
+        AccT<TM> acc;
         zero_acc(acc);
-        mac_loop<DT, BL, NS, NW>(pv, lds, m0, n0, 0, ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
-        const Tile<NW> t = merge_k_halves<NW>(acc, lds);
+        mac_loop<DT, BL, NS, NW, TM>(pv, lds, m0, n0, 0, ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
+        const Tile<NW, TM> t = merge_k_halves<NW, TM>(acc, lds);
         trace_segment(p, p.units + tile, 0, tile, 0, ipt, 0);
         store_final<NW, EPI>(pv, m0, n0, t);
         trace_folded(p, tile, 0, p.units + tile);
@@ -1806,10 +1984,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         const int role = k0 > 0 ? 2 : (k1 == ipt ? 0 : 1);
         const int owner = unit_of(tb, p.q, p.big);
         const int rot = (tb - unit_start(owner, p.q, p.big)) % ipt;
-        Acc acc;
+        AccT<TM> acc;
         zero_acc(acc);
-        mac_loop<DT, BL, NS, NW>(pv, lds, m0, n0, k0, k1, rot, acc, p.trace ? trace_cov(p, tile) : nullptr,
-                                 pending);
+        mac_loop<DT, BL, NS, NW, TM>(pv, lds, m0, n0, k0, k1, rot, acc, p.trace ? trace_cov(p, tile) : nullptr,
+                                     pending);
         pending = nullptr;
         // a segment that stores C: with the epilogue, its inputs are loaded now,
         // while the k-halves merge and any peers are waited for and added
@@ -1824,7 +2002,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
             static_assert(NW == 8, "the prefetch assumes one 32-row block per wave");
             if (stores_c && p.epi != EPI_PLAIN) epi_prefetch(pv, m0, n0, pre_c, pre_b);
         }
-        Tile<NW> t = merge_k_halves<NW>(acc, lds);
+        Tile<NW, TM> t = merge_k_halves<NW, TM>(acc, lds);
         clk.mark(p, 2 * min(nseg, 1));
         trace_segment(p, u, nseg++, tile, k0, k1, role);
         if (role == 0) {
@@ -1835,13 +2013,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         } else if (p.merge == MERGE_TWO_PASS) {
             // streamk_reduce adds the tile's partials: contributors publish into
             // the first slot bank, owners into the second
-            put_slot<NW>(p.part + ((size_t)(role == 1 ? p.units : 0) + u) * (BM * BN), t, zero_partials(p));
+            put_slot<NW>(p.part + ((size_t)(role == 1 ? p.units : 0) + u) * SLOT, t, zero_partials(p));
         } else if (role == 2) {
             // starts mid-tile: publish the partial, then the flag -- at once if
             // this is the unit's last segment, else from the next segment's loop
             // as soon as the stores are known complete (the loop has to wait for
             // its first loads anyway)
-            put_slot<NW>(p.part + (size_t)u * (BM * BN), t, zero_partials(p));
+            put_slot<NW>(p.part + (size_t)u * SLOT, t, zero_partials(p));
             uint32_t *flag = (p.debug & GEMM_DEBUG_NO_PUBLISH) ? nullptr : p.flags + u;
             if (tb + k1 < end) {
                 pending = flag;
@@ -1867,7 +2045,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
                     __hip_atomic_store(p.flags + v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
                 __syncthreads();
-                add_slot<NW>(p.part + (size_t)v * (BM * BN), t);
+                add_slot<NW>(p.part + (size_t)v * SLOT, t);
                 trace_folded(p, tile, pos_fold++, v);
             }
             if constexpr (!EPI) store_final<NW, false>(pv, m0, n0, t);
@@ -1946,7 +2124,17 @@ struct Shape {
 };
 
 template <int DT, int BL>
-KernelFn pick(int kmode, bool epi, Shape &shape) {
+KernelFn pick(int kmode, bool epi, int tm, Shape &shape) {
+    if (tm == 256) {
+        // the 256 x 128 tile: three stages of (32 KiB A + 16 KiB B), Stream-K only,
+        // no fused epilogue
+        if (epi) return nullptr;
+        shape = {3, 8};
+        if (kmode == K_SK) return gemm_streamk<DT, BL, 3, 8, false, false, 256>;
+        if (kmode == K_SK_ATOMIC) return gemm_streamk<DT, BL, 3, 8, true, false, 256>;
+        return nullptr;
+    }
+    if (tm != 128) return nullptr;
     // Stream-K has a separate build with the epilogue: its plain build keeps
     // the register allocation of a kernel without one
     switch (kmode) {
@@ -1963,9 +2151,9 @@ KernelFn pick(int kmode, bool epi, Shape &shape) {
     }
 }
 
-KernelFn kernel_for(int dtype, int blayout, int kmode, bool epi, Shape &shape) {
-    if (dtype == 0) return blayout == 0 ? pick<0, 0>(kmode, epi, shape) : pick<0, 1>(kmode, epi, shape);
-    if (dtype == 1) return blayout == 0 ? pick<1, 0>(kmode, epi, shape) : pick<1, 1>(kmode, epi, shape);
+KernelFn kernel_for(int dtype, int blayout, int kmode, bool epi, int tm, Shape &shape) {
+    if (dtype == 0) return blayout == 0 ? pick<0, 0>(kmode, epi, tm, shape) : pick<0, 1>(kmode, epi, tm, shape);
+    if (dtype == 1) return blayout == 0 ? pick<1, 0>(kmode, epi, tm, shape) : pick<1, 1>(kmode, epi, tm, shape);
     return nullptr;
 }
 
@@ -1974,7 +2162,7 @@ KernelFn kernel_for(int dtype, int blayout, int kmode, bool epi, Shape &shape) {
 hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParams &p,
                        hipStream_t stream) {
     Shape shape{0, 0};
-    KernelFn fn = kernel_for(dtype, blayout, kmode, p.epi != EPI_PLAIN, shape);
+    KernelFn fn = kernel_for(dtype, blayout, kmode, p.epi != EPI_PLAIN, p.tm, shape);
     if (!fn || grid <= 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * shape.nw), 0, stream, p);
     return hipGetLastError();
@@ -2022,12 +2210,13 @@ hipError_t launch_zero(void *ptr, int64_t n_words, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int *out) {
-    // the smaller of the builds with and without the epilogue
+hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int tm, int *out) {
+    // the smaller of the builds with and without the epilogue (the 256-row tile
+    // has no epilogue build)
     int best = 1 << 30;
-    for (int epi = 0; epi < 2; ++epi) {
+    for (int epi = 0; epi < (tm == 128 ? 2 : 1); ++epi) {
         Shape shape{0, 0};
-        KernelFn fn = kernel_for(dtype, blayout, kmode, epi != 0, shape);
+        KernelFn fn = kernel_for(dtype, blayout, kmode, epi != 0, tm, shape);
         if (!fn) return hipErrorInvalidValue;
         int n = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(fn),

@@ -46,6 +46,7 @@ struct KParams {
     const uint16_t *B;     // [K,N] or [N,K] row-major
     float *C;              // [M,N] row-major fp32
     int M, N, K;
+    int tm;                // tile rows: 128, or 256 for the tall Stream-K tile (tiles are tm x 128)
     int tiles_m, tiles_n;  // output tiles along M and N (of one batch entry)
     int group_m;           // tile ids run column by column in groups of group_m tile rows (0: row-major)
     int xcd_spread;        // 1: give each XCD a contiguous range of workers
@@ -78,7 +79,8 @@ struct KParams {
 };
 
 // Launch `grid` workgroups of the kernel for (dtype, B layout, mode) on `stream`.
-// dtype: 0 bf16, 1 fp16; blayout: 0 = B [K,N], 1 = B [N,K].
+// dtype: 0 bf16, 1 fp16; blayout: 0 = B [K,N], 1 = B [N,K].  p.tm = 256 selects
+// the 256 x 128 tile build (Stream-K kinds only, no fused epilogue).
 hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParams &p,
                        hipStream_t stream);
 
@@ -99,7 +101,7 @@ hipError_t launch_epilogue_pass(const KParams &p, int stage, hipStream_t stream)
 // be captured in a HIP graph).
 hipError_t launch_zero(void *ptr, int64_t n_words, hipStream_t stream);
 
-// Resident workgroups per CU for the kernel of (dtype, blayout, kmode).
-hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int *out);
+// Resident workgroups per CU for the kernel of (dtype, blayout, kmode, tile rows tm).
+hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int tm, int *out);
 
 }  // namespace dgw

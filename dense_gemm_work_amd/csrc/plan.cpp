@@ -52,9 +52,14 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, u
     const uint32_t decomp = mode & 0xFu;
     const bool atomic = (mode & GEMM_ATOMIC) != 0;
     const bool two_pass = (mode & GEMM_TWO_PASS) != 0;
-    if ((mode & ~(0xFu | GEMM_ATOMIC | GEMM_TWO_PASS)) || decomp > GEMM_STREAMK) {
+    const bool tall = (mode & GEMM_TILE_256x128) != 0;
+    if ((mode & ~(0xFu | GEMM_ATOMIC | GEMM_TWO_PASS | GEMM_TILE_256x128)) || decomp > GEMM_STREAMK) {
         *why = "mode word has unknown bits";
         return GEMM_ERR_INVALID;
+    }
+    if (tall && (decomp != GEMM_STREAMK || two_pass)) {
+        *why = "GEMM_TILE_256x128 applies to GEMM_STREAMK with the turnstile or atomic merge only";
+        return GEMM_ERR_UNSUPPORTED;
     }
     if (atomic && decomp == GEMM_DP) {
         *why = "GEMM_ATOMIC applies to Stream-K and Split-K only";
@@ -83,10 +88,10 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, u
 
     gemm_plan_t &p = *out;
     p.atomic = 0;
-    p.bm = GEMM_BM; p.bn = GEMM_BN; p.bk = GEMM_BK;
+    p.bm = tall ? 2 * GEMM_BM : GEMM_BM; p.bn = GEMM_BN; p.bk = GEMM_BK;
     p.num_cus = num_cus;
     p.batch = batch;
-    p.tiles_m = ceil_div(M, GEMM_BM);
+    p.tiles_m = ceil_div(M, p.bm);
     p.tiles_n = ceil_div(N, GEMM_BN);
     // a batched call is one problem of batch x tiles_m x tiles_n tiles, numbered
     // batch after batch; the rule and the Stream-K flattening see that count
@@ -192,11 +197,11 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, u
         // 32 units of 8 iterations on 8 tiles 13.6 -> 11.9 us); with one or two
         // peers the turnstile is (2048x2176x4096: 45.7 vs 49.3 us; 1536^2 x 16384
         // fp16: 86.1 vs 88.9 us).
-        p.two_pass = !atomic && (two_pass || p.max_fold >= 4) ? 1 : 0;
+        p.two_pass = !atomic && !tall && (two_pass || p.max_fold >= 4) ? 1 : 0;
         // fp32 partial slots: one per unit for the turnstile (a unit publishes at
         // most its first segment); two per unit with the second kernel (its first
         // segment as a contributor, its last as an owner)
-        p.workspace_bytes = atomic ? 0 : (p.two_pass ? 2 : 1) * units * int64_t(GEMM_BM) * GEMM_BN * 4;
+        p.workspace_bytes = atomic ? 0 : (p.two_pass ? 2 : 1) * units * int64_t(p.bm) * p.bn * 4;
         break;
     }
     default:

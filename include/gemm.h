@@ -109,6 +109,14 @@ extern "C" {
 #define GEMM_ATOMIC        0x100u  /* fp32 atomic adds into a zero-filled C (Stream-K, Split-K) */
 #define GEMM_TWO_PASS      0x200u  /* always add split tiles' partials in k order by a second
                                       kernel (Split-K and Stream-K; same bits as in the launch) */
+/* bits 12-13: output tile shape */
+#define GEMM_TILE_128x128  0x0000u /* 128 x 128 tiles (every decomposition)                     */
+#define GEMM_TILE_256x128  0x1000u /* 256 x 128 tiles: GEMM_STREAMK only (turnstile or
+                                      GEMM_ATOMIC merge; no GEMM_TWO_PASS, no fused epilogue).
+                                      The tile the book chapter's Case 4 names for CUTLASS's
+                                      Stream-K example (MmaTileShape 256 x 128 x 64); a unit's
+                                      64-wide k-iteration is then twice the work, the partial
+                                      slot 128 KiB.                                            */
 
 /* ---- debug bits for gemm_args_t.debug -------------------------------------------- */
 #define GEMM_DEBUG_NO_PUBLISH 0x1u /* Stream-K contributors store partials but never

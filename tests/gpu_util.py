@@ -105,8 +105,8 @@ def decode_trace(tr: torch.Tensor):
                 segments=sorted(segs), folds=folds, coverage=cov)
 
 
-def expected_trace(M, N, K, mode, splits, cus, batch=1):
-    s = sch.plan_schedule(M, N, K, mode, splits, sms=cus, batch=batch)
+def expected_trace(M, N, K, mode, splits, cus, batch=1, bm=128):
+    s = sch.plan_schedule(M, N, K, mode, splits, sms=cus, batch=batch, bm=bm)
     segs = sorted(x.as_tuple() for x in s.segments)
     groups = sch.tile_groups(s.segments)
     folds = {t: [owner] + peers for t, (owner, peers) in groups.items()}

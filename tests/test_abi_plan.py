@@ -87,10 +87,10 @@ def test_struct_sizes_match_c(dg, tmp_path):
 
 
 # -- planner vs simulator -------------------------------------------------------------
-def _compare(dg, M, N, K, mode, splits, cus, atomic=False):
-    mw = dg.mode_word(mode, atomic)
+def _compare(dg, M, N, K, mode, splits, cus, atomic=False, tile="128x128"):
+    mw = dg.mode_word(mode, atomic, tile=tile)
     p = dg.gemm_plan(M, N, K, dg.GEMM_B_KN | dg.GEMM_BF16, mw, splits, cus)
-    s = sch.plan_schedule(M, N, K, mode, splits, sms=cus)
+    s = sch.plan_schedule(M, N, K, mode, splits, sms=cus, bm=int(tile.split("x")[0]))
     assert dg.DECISION_NAMES[p.decision] == s.kind
     assert (p.tiles_m, p.tiles_n, p.ipt) == (s.tiles_m, s.tiles_n, s.ipt)
     w = sch.wave_stats(s.tiles, cus)
@@ -377,3 +377,30 @@ def test_noalloc_refusals_before_any_hip_call(dg):
     args.workspace, args.workspace_bytes = 0x400000000, 1 << 30
     assert dg.gemm_ex_noalloc(args) == dg.GEMM_ERR_INVALID
     assert "workspace must be NULL" in dg.gemm_last_error()
+
+
+@pytest.mark.parametrize("M,N,K,units,atomic", [
+    (2048, 2176, 4096, 256, False),    # 8 x 17 = 136 tiles of 256 x 128, 256 units of 34 iterations
+    (1536, 1536, 16384, 256, False),   # 72 tiles x 256 iterations
+    (4096, 4224, 4096, 256, True),     # 528 tiles
+    (300, 200, 328, 7, False),         # ragged M, N and K
+    (256, 128, 128, 6, False),         # more units than iterations
+])
+def test_tall_tile_plans_match_simulator(dg, M, N, K, units, atomic):
+    p, s = _compare(dg, M, N, K, "streamk", units, 256, atomic=atomic, tile="256x128")
+    assert (p.bm, p.bn, p.bk) == (256, 128, 64)
+    assert p.tiles_m == -(-M // 256) and p.two_pass == 0
+    # one 256 x 128 fp32 slot (128 KiB) per unit for the turnstile, none for atomics
+    data = p.workspace_bytes - (256 + -(-max(p.sk_units, 1) * 4 // 256) * 256 + -(-p.tiles * 4 // 256) * 256)
+    assert data == (0 if atomic else p.sk_units * 256 * 128 * 4)
+
+
+def test_tall_tile_refusals(dg):
+    lw = dg.GEMM_B_KN | dg.GEMM_BF16
+    for mode in ("dp", "splitk", "heuristic"):
+        with pytest.raises(dg.GemmError) as ei:
+            dg.gemm_plan(2048, 2176, 4096, lw, dg.mode_word(mode, tile="256x128"), 2 if mode == "splitk" else 0, 256)
+        assert ei.value.status == dg.GEMM_ERR_UNSUPPORTED
+    with pytest.raises(dg.GemmError) as ei:
+        dg.gemm_plan(2048, 2176, 4096, lw, dg.mode_word("streamk", two_pass=True, tile="256x128"), 0, 256)
+    assert ei.value.status == dg.GEMM_ERR_UNSUPPORTED
