@@ -68,6 +68,7 @@ GEMM_DEBUG_IN_LAUNCH = 0x4
 GEMM_DEBUG_TILE_DP = 0x8
 GEMM_DEBUG_HYBRID_SPLIT = 0x10
 GEMM_DEBUG_ZERO_PARTIAL = 0x20
+GEMM_DEBUG_SPLITK_BANDS = 0x40
 
 GEMM_BM = 128
 GEMM_NOALLOC_MAX_BYTES = 32 * 1024 * 1024 + 256 * 1024   # gemm_ex_noalloc scratch per device

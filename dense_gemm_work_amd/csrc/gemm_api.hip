@@ -278,7 +278,7 @@ int run(const gemm_args_t &a, bool noalloc = false) {
     if (rc != GEMM_OK) return fail(rc, why);
     if (a.num_cus < 0) return fail(GEMM_ERR_INVALID, "num_cus must be >= 0");
     if ((a.debug & ~(GEMM_DEBUG_NO_PUBLISH | GEMM_DEBUG_IN_LAUNCH | GEMM_DEBUG_TILE_DP | GEMM_DEBUG_HYBRID_SPLIT |
-                    GEMM_DEBUG_ZERO_PARTIAL)) != 0)
+                    GEMM_DEBUG_ZERO_PARTIAL | GEMM_DEBUG_SPLITK_BANDS)) != 0)
         return fail(GEMM_ERR_INVALID, "unknown debug bits");
     if ((rc = check_epilogue(a)) != GEMM_OK) return rc;
     if (a.M == 0 || a.N == 0) return GEMM_OK;
@@ -456,9 +456,20 @@ int run(const gemm_args_t &a, bool noalloc = false) {
         }
     } else if (p.decision == GEMM_SPLITK) {
         kp.ntiles = (int)p.tiles;
-        kp.merge = p.atomic                                        ? dgw::MERGE_ATOMIC
-                   : p.two_pass && !(a.debug & GEMM_DEBUG_IN_LAUNCH) ? dgw::MERGE_TWO_PASS
-                                                                       : dgw::MERGE_IN_LAUNCH;
+        const bool in_launch = (a.debug & (GEMM_DEBUG_IN_LAUNCH | GEMM_DEBUG_SPLITK_BANDS)) != 0;
+        kp.merge = p.atomic                      ? dgw::MERGE_ATOMIC
+                   : p.two_pass && !in_launch ? dgw::MERGE_TWO_PASS
+                                              : dgw::MERGE_IN_LAUNCH;
+        // in the launch: when every workgroup of the grid is resident at once, all
+        // S splits of a tile add up its row bands (the waits end); otherwise the
+        // last arriver at the tile's counter adds up the whole tile.
+        // GEMM_DEBUG_IN_LAUNCH keeps the last arriver.
+        if (kp.merge == dgw::MERGE_IN_LAUNCH && p.splits > 1 && (a.N & 3) == 0 && !(a.debug & GEMM_DEBUG_IN_LAUNCH)) {
+            int &bpc = ds->bpc[dtype][blayout][dgw::K_SPLITK][0];
+            if (bpc == 0 && (e = dgw::blocks_per_cu(dtype, blayout, dgw::K_SPLITK, GEMM_BM, &bpc)) != hipSuccess)
+                return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+            if (p.tiles * p.splits <= (int64_t)bpc * ds->num_cus) kp.merge = dgw::MERGE_BANDS;
+        }
         if (p.atomic && (rc = prepare_atomic_c()) != GEMM_OK) return rc;
         if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_SPLITK, (int)(p.tiles * p.splits), kp, stream)) !=
             hipSuccess)

@@ -1079,6 +1079,26 @@ __device__ __forceinline__ void store_quads_final(const KParams &p, int m0, int 
     }
 }
 
+// One 16-byte quad (quad q of the thread, N a multiple of 4) of final values with
+// the epilogue, or nothing when it lies outside C.
+template <int NW>
+__device__ __forceinline__ void store_quad_final(const KParams &p, int m0, int n0, int q, f32x4 v) {
+    constexpr int NT = Role<NW>::NT;
+    const int fq = threadIdx.x + NT * q, r = fq >> 5, c = (fq & 31) * 4;
+    if (m0 + r >= p.M || n0 + c >= p.N) return;
+    f32x4 *dst = reinterpret_cast<f32x4 *>(p.C + (size_t)(m0 + r) * p.N + n0 + c);
+    if (p.epi != EPI_PLAIN) {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 cq = reads_c(p) ? *dst : zero;
+        const f32x4 bq = p.bias ? *reinterpret_cast<const f32x4 *>(p.bias + n0 + c) : zero;
+        float w[4] = {v[0], v[1], v[2], v[3]};
+        const float cin[4] = {cq[0], cq[1], cq[2], cq[3]}, bv[4] = {bq[0], bq[1], bq[2], bq[3]};
+        finish<4>(p, w, cin, bv);
+        v = f32x4{w[0], w[1], w[2], w[3]};
+    }
+    __builtin_nontemporal_store(v, dst);
+}
+
 // ---------------------------------------------------------------------------
 // Partial exchange between workgroups ("store the partial, signal, the owner
 // waits and reads it": book chapter, "Mental model").  It rests on two
@@ -1174,6 +1194,21 @@ __device__ __forceinline__ void wait_flag(const uint32_t *flag, uint32_t epoch, 
         uint32_t v = load_flag_async(flag);
         wait_vm_all();
         if (flag_value(v) == epoch) return;
+        if (polls >= limit) {
+            __hip_atomic_fetch_or(status, STATUS_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// Poll a counter (one thread) until it reaches at least `target`; bounded like
+// wait_flag.
+__device__ __forceinline__ void wait_count(const uint32_t *ctr, uint32_t target, uint32_t limit, uint32_t *status) {
+    for (uint32_t polls = 1;; ++polls) {
+        uint32_t v = load_flag_async(ctr);
+        wait_vm_all();
+        if (flag_value(v) >= target) return;
         if (polls >= limit) {
             __hip_atomic_fetch_or(status, STATUS_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;
@@ -1675,11 +1710,16 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p0) {
     const size_t org = (size_t)m0 * p.N + n0;                 // tile origin within [M,N]
     const uint32_t span_bytes = (uint32_t)(((size_t)(min(BM, p.M - m0) - 1) * p.N + min(BN, p.N - n0)) * 4);
     auto quad_off = [&](int r, int c) { return (uint32_t)(((size_t)r * p.N + c) * 4); };
+    // MERGE_BANDS: row band q (rows 16 q .. 16 q + 15 of the tile, the thread's
+    // quad q) is added up by split q mod S, which takes its own part of the band
+    // from LDS and so does not store it
+    const bool bands = p.merge == MERGE_BANDS;
     {
         const __amdgpu_buffer_rsrc_t rp = span(p.part + (size_t)s * mn + org, span_bytes);
         float *Ps = p.part + (size_t)s * mn;
         const bool zero = zero_partials(p);   // the zero-partial control
-        for_each_quad<NW>(m0, n0, p.M, p.N, [&](int, int r, int c, size_t off, int nv) {
+        for_each_quad<NW>(m0, n0, p.M, p.N, [&](int q, int r, int c, size_t off, int nv) {
+            if (bands && q % S == s) return;
             const f32x4 v = zero ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : staged_quad(stg, r, c);
             if (nv == 4) {
                 put4_coherent(rp, quad_off(r, c), v);
@@ -1692,6 +1732,97 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p0) {
     __syncthreads();               // ... and every other wave's
     clk.mark(p, 1);
     if (p.merge == MERGE_TWO_PASS) {   // the second kernel folds the partials
+        clk.done(p);
+        return;
+    }
+    auto quad_rc = [&](int g, int &r, int &c) {
+        const int fq = threadIdx.x + NT * g;
+        r = fq >> 5;
+        c = (fq & 31) * 4;
+    };
+    auto in_c = [&](int r, int c) { return m0 + r < p.M && n0 + c < p.N; };
+    auto get4 = [&](int t, int r, int c) {
+        return get4_coherent(span(p.part + (size_t)t * mn + org, span_bytes), quad_off(r, c));
+    };
+    if (bands) {
+        // every split arrives at the tile's counter and waits until all S have (the
+        // whole grid is resident, so the wait ends); then it adds up its own bands
+        // q = s, s + S, ... (at most 4 of the QPT = 8), the partials in split
+        // order with its own from LDS; then it departs, and the last of the 2 S
+        // arrivals and departures resets the counter for the next call
+        if (threadIdx.x == 0) {
+            __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            wait_count(p.counters + tile, (uint32_t)S, p.spin_limit, p.status);
+        }
+        __syncthreads();
+        clk.mark(p, 3);
+        static_assert(QPT == 8, "eight row bands of 16 rows");
+        // every load of the split's bands in one round, then the adds: G band
+        // slots (q = s + g S) by the T splits other than s (the j-th other split
+        // is j, or j + 1 from s on)
+        auto fold = [&](auto GC, auto TC) {
+            constexpr int G = decltype(GC)::value, T = decltype(TC)::value;
+            f32x4 x[G][T];
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int j = 0; j < T; ++j) {
+                    const int q = s + g * S, t = j < s ? j : j + 1;
+                    int r, c;
+                    quad_rc(q, r, c);
+                    x[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (q < QPT && j < S - 1 && in_c(r, c)) x[g][j] = get4(t, r, c);
+                }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int q = s + g * S;
+                if (q >= QPT) continue;
+                int r, c;
+                quad_rc(q, r, c);
+                const f32x4 own = staged_quad(stg, r, c);
+                f32x4 sum = own;
+#pragma unroll
+                for (int t = 0; t <= T; ++t) {   // partial t in split order
+                    if (t >= S) break;
+                    // indices clamped into range; the loop is unrolled, so they are constants
+                    const f32x4 below = x[g][t < T ? t : T - 1], above = x[g][t >= 1 ? t - 1 : 0];
+                    const f32x4 v = t < s ? below : (t > s ? above : own);
+                    sum = t == 0 ? v : sum + v;
+                }
+                store_quad_final<NW>(p, m0, n0, q, sum);
+            }
+        };
+        if (S <= 4) {
+            fold(std::integral_constant<int, 4>(), std::integral_constant<int, 3>());
+        } else if (S <= 8) {
+            fold(std::integral_constant<int, 2>(), std::integral_constant<int, 7>());
+        } else if (s < QPT) {
+            // one band, its S partials in rounds of 8 loads
+            int r, c;
+            quad_rc(s, r, c);
+            f32x4 sum = staged_quad(stg, r, c);
+            for (int t0 = 0; t0 < S; t0 += 8) {
+                f32x4 x[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int t = t0 + k;
+                    x[k] = t == s || t >= S || !in_c(r, c) ? staged_quad(stg, r, c) : get4(t, r, c);
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (t0 + k < S) sum = t0 + k == 0 ? x[k] : sum + x[k];
+            }
+            store_quad_final<NW>(p, m0, n0, s, sum);
+        }
+        if (threadIdx.x == 0) {
+            const uint32_t before =
+                __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (before == (uint32_t)(2 * S - 1))
+                __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (s == 0)
+            for (int t = 0; t < S; ++t) trace_folded(p, tile, t, tile * S + t);
+        clk.mark(p, 2);
         clk.done(p);
         return;
     }
@@ -1714,15 +1845,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p0) {
     // QPT quads of the thread with the S - 1 other partials in one round of
     // loads, for larger S rounds of 4 quads with up to 4 partials each.  Any
     // other N folds element by element.
-    auto quad_rc = [&](int g, int &r, int &c) {
-        const int fq = threadIdx.x + NT * g;
-        r = fq >> 5;
-        c = (fq & 31) * 4;
-    };
-    auto in_c = [&](int r, int c) { return m0 + r < p.M && n0 + c < p.N; };
-    auto get4 = [&](int t, int r, int c) {
-        return get4_coherent(span(p.part + (size_t)t * mn + org, span_bytes), quad_off(r, c));
-    };
     if ((p.N & 3) != 0) {
         for (int g = 0; g < QPT; ++g) {
             int r, c;

@@ -17,9 +17,12 @@ enum KernelMode : int {
 };
 
 // How Split-K merges its partials: folded in the same launch by the last
-// arriver at the tile's counter, folded by a second kernel, or added atomically
-// into a zero-filled C.
-enum : int { MERGE_IN_LAUNCH = 0, MERGE_TWO_PASS = 1, MERGE_ATOMIC = 2 };
+// arriver at the tile's counter, folded by a second kernel, added atomically
+// into a zero-filled C, or (MERGE_BANDS, grids whose workgroups are all
+// resident at once) folded in the same launch by all S splits of a tile, each
+// adding up its own row bands once every split has arrived.  Every
+// deterministic form adds the partials in split order: the same bits.
+enum : int { MERGE_IN_LAUNCH = 0, MERGE_TWO_PASS = 1, MERGE_ATOMIC = 2, MERGE_BANDS = 3 };
 
 // How final values reach C (the fused epilogue of the CUTLASS optimisation
 // guide, "Epilogue Optimization": D = act(alpha acc + beta C + bias)).

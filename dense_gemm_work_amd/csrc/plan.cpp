@@ -159,14 +159,18 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, u
     case GEMM_SPLITK:
         p.splits = S;
         p.atomic = atomic && S > 1 ? 1 : 0;
-        // Deterministic: the partials are added in split order either by the last
-        // arriver at each tile's counter (in the launch) or by a second kernel.
-        // Same bits; the second kernel wins when the whole grid is resident at
-        // once (one workgroup per CU) -- the latency-bound small grids, where a
-        // kernel boundary costs less than the arrival round trip plus a fold
-        // serialised in one workgroup -- and loses on larger grids, whose last
-        // arrivers fold partials still warm in L2.
-        p.two_pass = !p.atomic && S > 1 && (two_pass || p.tiles * S <= num_cus) ? 1 : 0;
+        // Deterministic: the partials are added in split order, by a second
+        // kernel, or in the launch -- by all S splits of a tile, each adding up
+        // its own row bands, when the whole grid is resident at once (the
+        // library checks residency), else by the last arriver at the tile's
+        // counter.  Same bits.  Measured on the resident skinny grids (one
+        // workgroup per CU): the row bands win from S = 8 (96x512x2048:
+        // 11.1 us against 12.1 us with the second kernel), the second kernel
+        // below (S = 2 and 4: 13.8 vs 15.1 us, 12.3 vs 12.8 us), where the fold
+        // of a tile is spread over too few workgroups; larger grids' last
+        // arrivers fold partials still warm in L2 (2048x2176x4096 S = 2:
+        // 71.6 us in the launch, 75.9 us with the second kernel).
+        p.two_pass = !p.atomic && S > 1 && (two_pass || (p.tiles * S <= num_cus && S < 8)) ? 1 : 0;
         p.workers = p.tiles * S;
         p.max_segments = 1;
         p.max_fold = S;

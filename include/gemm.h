@@ -24,9 +24,11 @@
  *                 partials added in split order (docc StreamK page, "MMA
  *                 fragment accumulators (aligned split)"): by a second kernel
  *                 ("serial" Split-K; chosen when all tiles x S workgroups fit on
- *                 the CUs at once, or asked for with GEMM_TWO_PASS; plan.two_pass
- *                 says which), else by the last arriver at the tile's counter
- *                 in the same launch.  Both give the same bits.  GEMM_ATOMIC adds
+ *                 the CUs at once and S < 8, or asked for with GEMM_TWO_PASS;
+ *                 plan.two_pass says which), else in the same launch -- by all S
+ *                 splits of each tile, each adding up its own 16-row bands once
+ *                 every split has arrived, when the grid is resident at once, or
+ *                 by the last arriver at the tile's counter.  All give the same bits.  GEMM_ATOMIC adds
  *                 every split into a zero-filled C instead ("parallel" Split-K;
  *                 CUTLASS optimisation guide, "Parallelized Reductions (Split-K)").
  *   GEMM_STREAMK  one persistent workgroup per unit; unit u owns a contiguous,
@@ -133,6 +135,10 @@ extern "C" {
 #define GEMM_DEBUG_HYBRID_SPLIT 0x10u /* a hybrid's data-parallel tiles run as a second
                                          launch after the Stream-K one instead of by
                                          the persistent units first.  Same values.  */
+#define GEMM_DEBUG_SPLITK_BANDS 0x40u /* deterministic Split-K on a grid whose workgroups
+                                         are all resident: add the partials in the launch,
+                                         each split adding up its own row bands, even where
+                                         the plan chose a second kernel.  Same bits.      */
 #define GEMM_DEBUG_ZERO_PARTIAL 0x20u /* numerical control: every partial a split tile
                                          hands to another workgroup is written as zeros
                                          (Stream-K slots, Split-K partials of both merge
@@ -199,7 +205,7 @@ typedef struct gemm_plan_t {
     int32_t max_fold;     /* most workers contributing to one tile                          */
     int32_t two_pass;     /* 1 when split tiles' partials are added by a second kernel (the
                              plan picks it for Split-K grids that fit on the CUs at once
-                             and for Stream-K tiles with three or more peers)           */
+                             with S < 8, and for Stream-K tiles with three or more peers) */
     int64_t workers;      /* traced workers: units + dp_tiles, tiles * S, or tiles          */
     int64_t workspace_bytes; /* device workspace the call needs                             */
     int64_t trace_ints;   /* int32 elements of a debug trace buffer for this call           */
@@ -234,7 +240,8 @@ typedef struct gemm_plan_t {
  *             placement), cycles = shader-clock ticks (s_memtime) from start to end,
  *             so cycles / (end - start) * 100 MHz is the workgroup's mean clock.
  *             Marks: DP m0 = mainloop done; Split-K m0 = mainloop done, m1 =
- *             partial stored, m2 = fold done (last arriver); Stream-K m0/m1 =
+ *             partial stored, m2 = fold done (last arriver, or a split's bands),
+ *             m3 = every split of the tile arrived (row-band merge); Stream-K m0/m1 =
  *             first segment's mainloop / fixup-and-store done, m2/m3 = the same
  *             for the unit's last segment.  Unset marks stay as the caller left them.
  *   epilogue: GEMM_EPI_* bits (0: C is overwritten with A.B).  RELU and GELU

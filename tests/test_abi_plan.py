@@ -302,7 +302,12 @@ def test_splitk_merge_modes_plan(dg):
     fold = dg.gemm_plan(M, N, K, lw, dg.GEMM_SPLITK, S, 16)           # 32 > 16 CUs
     two = dg.gemm_plan(M, N, K, lw, dg.GEMM_SPLITK | dg.GEMM_TWO_PASS, S, 16)
     atom = dg.gemm_plan(M, N, K, lw, dg.GEMM_SPLITK | dg.GEMM_ATOMIC, S, 256)
-    assert (auto.two_pass, fold.two_pass, two.two_pass, atom.two_pass) == (1, 0, 1, 0)
+    # S = 8 on a grid that fits the CUs: in the launch (row bands); on 16 CUs the
+    # grid does not fit (last arriver); the second kernel on request
+    assert (auto.two_pass, fold.two_pass, two.two_pass, atom.two_pass) == (0, 0, 1, 0)
+    # S < 8 on a grid that fits: the second kernel
+    assert dg.gemm_plan(M, N, K, lw, dg.GEMM_SPLITK, 4, 256).two_pass == 1
+    assert dg.gemm_plan(256, 512, 2048, lw, dg.GEMM_SPLITK, 2, 256).two_pass == 1
     assert (auto.atomic, fold.atomic, two.atomic, atom.atomic) == (0, 0, 0, 1)
     assert auto.workspace_bytes == fold.workspace_bytes == two.workspace_bytes
     assert fold.workspace_bytes - atom.workspace_bytes == S * M * N * 4

@@ -232,6 +232,23 @@ def test_small_shapes_all_modes(dg, shape, mode, splits, atomic):
     assert_parity(c, A, B, w)
 
 
+@pytest.mark.parametrize("shape", SMALL[:5], ids=lambda s: "x".join(map(str, s[:3])) + f"-{s[3]}-{s[4]}")
+@pytest.mark.parametrize("splits", [2, 3, 5, 8, 10])
+def test_small_shapes_splitk_row_bands(dg, shape, splits):
+    # the in-launch row-band merge at split factors from 2 to 10 (the last arriver
+    # where N is not a multiple of 4), against the oracle and the second kernel's bits
+    M, N, K, layout, dtype = shape
+    ipt = -(-K // 64)
+    if ipt % splits:
+        pytest.skip(f"{splits} does not divide {ipt} k-iterations")
+    dist = dict(dist="uniform", low=-1.0, high=1.0) if dtype == "bf16" else dict(dist="uniform", low=-0.5, high=0.5)
+    w = WORKLOADS["c1_sk32"].with_(name="bands", M=M, N=N, K=K, b_layout=layout, dtype=dtype, **dist)
+    A, B, c = run(dg, w, mode="splitk", splits=splits, debug=dg.GEMM_DEBUG_SPLITK_BANDS)
+    assert_parity(c, A, B, w)
+    _, _, c2 = run(dg, w, mode="splitk", splits=splits, two_pass=True, A=A, B=B)
+    assert torch.equal(c.view(torch.int32), c2.view(torch.int32))
+
+
 def _random_cases(n, seed=11):
     """Seeded random small problems: shape, layout, dtype, decomposition, merge mode
     and CU count (small CU counts make tile groups and hybrids appear)."""
@@ -418,10 +435,11 @@ def test_unit_order_does_not_change_bits(dg, order):
 
 @pytest.mark.parametrize("name,M,N", [("c2a_m96_s8", None, None), ("c2b_m256_s2", None, None),
                                       ("c1_sk32", None, None), ("c2a_m96_s8", 200, 392)])
-def test_splitk_two_pass_and_atomic(dg, name, M, N):
-    # the partials added in split order by a second kernel (the library's choice
-    # for these small grids) or by the last arriver in the launch give the same
-    # bits; atomics into a zero-filled C are within tolerance
+def test_splitk_merges_agree(dg, name, M, N):
+    # the deterministic merges add the partials in split order, so they give the
+    # same bits: the row bands of a resident grid (the default here), the last
+    # arriver (GEMM_DEBUG_IN_LAUNCH) and a second kernel (GEMM_TWO_PASS); atomics
+    # into a zero-filled C are within tolerance
     w = WORKLOADS[name]
     if M is not None:
         w = w.with_(M=M, N=N)   # ragged tiles in M and N
@@ -429,20 +447,22 @@ def test_splitk_two_pass_and_atomic(dg, name, M, N):
     A, B = make_operands(w)
     a, b = A.to(DEV), B.to(DEV)
     p = dg.gemm_plan(w.M, w.N, w.K, dg.layout_word(w.b_layout, w.dtype), dg.GEMM_SPLITK, splits, dg.gemm_num_cus())
-    assert p.two_pass == 1
-    say(f"  two-pass / last-arriver / atomic Split-K {w.name} {w.M}x{w.N}x{w.K} S={splits}")
-    full0, c0 = guarded_output(w.M, w.N, DEV)
-    full1, c1 = guarded_output(w.M, w.N, DEV)
-    full2, c2 = guarded_output(w.M, w.N, DEV)
-    dg.gemm_tensors(a, b, c0, b_layout=w.b_layout, mode="splitk", splits=splits)
-    dg.gemm_tensors(a, b, c1, b_layout=w.b_layout, mode="splitk", splits=splits, debug=dg.GEMM_DEBUG_IN_LAUNCH)
-    dg.gemm_tensors(a, b, c2, b_layout=w.b_layout, mode="splitk", splits=splits, atomic=True)
+    assert p.two_pass == (1 if splits < 8 else 0)
+    say(f"  bands / last-arriver / two-pass / atomic Split-K {w.name} {w.M}x{w.N}x{w.K} S={splits}")
+    outs = []
+    for kw in (dict(debug=dg.GEMM_DEBUG_SPLITK_BANDS), dict(debug=dg.GEMM_DEBUG_IN_LAUNCH), dict(two_pass=True),
+               dict(atomic=True)):
+        full, c = guarded_output(w.M, w.N, DEV)
+        dg.gemm_tensors(a, b, c, b_layout=w.b_layout, mode="splitk", splits=splits, **kw)
+        outs.append((full, c))
     assert dg.gemm_sync_status() == 0
-    for f in (full0, full1, full2):
+    for f, _ in outs:
         assert guards_intact(f, w.M, w.N)
-    assert torch.equal(c0.view(torch.int32), c1.view(torch.int32))
+    c0 = outs[0][1]
+    for _, c in outs[1:3]:
+        assert torch.equal(c0.view(torch.int32), c.view(torch.int32))
     assert_parity(c0, A, B, w)
-    assert_parity(c2, A, B, w)
+    assert_parity(outs[3][1], A, B, w)
 
 
 def test_splitk_two_pass_trace(dg):
@@ -635,6 +655,7 @@ def test_modes_interleaved_on_one_workspace(dg):
     inl = dg.GEMM_DEBUG_IN_LAUNCH
     seq = [  # (mode, splits, atomic, two_pass, debug)
         ("streamk", 7, False, False, inl), ("splitk", 4, False, False, inl), ("splitk", 4, False, True, 0),
+        ("splitk", 3, False, False, dg.GEMM_DEBUG_SPLITK_BANDS), ("splitk", 8, False, False, 0),
         ("streamk", 5, True, False, 0), ("streamk", 9, False, True, 0), ("dp", 0, False, False, 0),
         ("splitk", 2, True, False, 0), ("heuristic", 0, False, False, 0), ("streamk", 3, False, False, inl),
     ]
