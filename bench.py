@@ -52,6 +52,10 @@ def parse():
                     help="override the workload's decomposition (for profiling one arm)")
     ap.add_argument("--splits", type=int, default=None, help="Split-K factor or Stream-K units")
     ap.add_argument("--atomic", action="store_true", help="Stream-K atomic fixup")
+    ap.add_argument("--tile", default="128x128", choices=["128x128", "256x128"],
+                    help="output tile of the timed call (256x128: Stream-K only)")
+    ap.add_argument("--shape", default=None,
+                    help="MxNxK: time the workload's recipe at another shape (profiling one launch)")
     ap.add_argument("--no-timeline", action="store_true",
                     help="skip the per-CU busy-time measurement (instrumented launches)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -303,16 +307,27 @@ def vendor_blas(dg, name, calls, rounds=6):
     return {"mode": w.mode, "ours_us": round(o, 3), "vendor_us": round(v, 3), "vendor_over_ours": round(v / o, 3)}
 
 
-def kernel_name(dg, plan, w):
+def kernel_kind(dg, plan):
     kind = {dg.GEMM_DP: "gemm_dp", dg.GEMM_SPLITK: "gemm_splitk", dg.GEMM_STREAMK: "gemm_streamk"}[plan.decision]
     # the library runs 2x2 tile groups when their waves finish sooner (its rule, restated)
     cus = dg.gemm_num_cus()
     groups = ((plan.tiles_m + 1) // 2) * ((plan.tiles_n + 1) // 2)
     if plan.decision == dg.GEMM_DP and -(-groups // cus) * 40 < -(-plan.tiles // cus) * 14:
         kind = "gemm_dp_group"
+    return kind
+
+
+def kernel_name(dg, plan, w):
     lay = "B[K,N]" if w.b_layout == "kn" else "B[N,K]"
     fix = (", atomic" if plan.atomic else ", deterministic") if plan.decision == dg.GEMM_STREAMK else ""
-    return f"{kind}<{w.dtype}, {lay}{fix}>"
+    tile = f", {plan.bm}x{plan.bn} tiles" if plan.bm != 128 else ""
+    return f"{kernel_kind(dg, plan)}<{w.dtype}, {lay}{fix}{tile}>"
+
+
+def profile_key(dg, plan, w):
+    """Name of the committed profile summary of this launch (profiles/<key>.md)."""
+    tile = f"_{plan.bm}x{plan.bn}" if plan.bm != 128 else ""
+    return f"{kernel_kind(dg, plan)}_{w.dtype}_{w.b_layout}_{w.M}x{w.N}x{w.K}{tile}"
 
 
 def kernel_code_digest(path=None) -> str:
@@ -329,15 +344,16 @@ def kernel_code_digest(path=None) -> str:
     return hashlib.sha256(text.encode()).hexdigest()
 
 
-def measured_traffic(profile: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary `profile` (scaled by a plain copy of known size), or None
-    when there is none or the kernel code has changed since it was taken."""
+def measured_traffic(profile: str):
+    """HBM bytes per launch of the profiled kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary `profile` (scaled by a plain copy of known
+    size), or None when there is none or the kernel code has changed since it
+    was taken."""
     path = ROOT / "profiles" / "traffic.json"
     if not path.exists():
         return None
     entry = json.loads(path.read_text()).get(profile)
-    if not entry or kernel not in entry.get("kernel", ""):
+    if not entry:
         return None
     if kernel_code_digest() != entry.get("code_sha256"):
         return None
@@ -513,10 +529,13 @@ def main():
     if args.mode is not None:
         w = w.with_(mode=args.mode, splits=args.splits if args.splits is not None else 0,
                     atomic=args.atomic)
+    if args.shape is not None:
+        M, N, K = (int(x) for x in args.shape.lower().split("x"))
+        w = w.with_(name=f"{w.name}@{M}x{N}x{K}", M=M, N=N, K=K)
     A, B = make_operands(w)
     a, b = A.cuda(), B.cuda()
     c = torch.empty(((w.batch,) if w.batch > 1 else ()) + (w.M, w.N), dtype=torch.float32, device="cuda")
-    call = Call(dg, a, b, c, w.b_layout, w.mode, w.splits, w.atomic)
+    call = Call(dg, a, b, c, w.b_layout, w.mode, w.splits, w.atomic, tile=args.tile)
     log(f"bench: {w.name} {w.M}x{w.N}x{w.K} {w.dtype} plan={dg.plan_dict(call.plan)['decision_name']} "
         f"units={call.plan.sk_units} steps={args.steps} warmup={args.warmup}")
 
@@ -604,11 +623,16 @@ def main():
         "scaling": "strong",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded normal(0,1)*0.1 rounded to bf16)",
+        "data": "synthetic (seeded " + (f"normal(0,1)*{w.scale}" if w.dist == "normal" else
+                                        f"uniform[{w.low},{w.high})") + f" rounded to {w.dtype})",
         "config": {
-            "workload": f"{w.name}: BF16 GEMM {w.M}x{w.N}x{w.K}, B [K,N], fp32 out, 128x128x64 tiles, "
-                        f"heuristic -> {dg.DECISION_NAMES[call.plan.decision]} "
-                        f"({call.plan.sk_units} units x {call.plan.q} iterations)",
+            "workload": f"{w.name}: {w.dtype.upper()} GEMM {w.M}x{w.N}x{w.K}, "
+                        f"B {'[K,N]' if w.b_layout == 'kn' else '[N,K]'}, fp32 out, "
+                        f"{call.plan.bm}x{call.plan.bn}x64 tiles, {w.mode} -> "
+                        f"{dg.DECISION_NAMES[call.plan.decision]}"
+                        + (f" ({call.plan.sk_units} units x {call.plan.q} iterations)"
+                           if call.plan.decision == dg.GEMM_STREAMK else
+                           f" (S = {call.plan.splits})" if call.plan.decision == dg.GEMM_SPLITK else ""),
             "M": w.M, "N": w.N, "K": w.K, "tiles": int(call.plan.tiles), "cus": dg.gemm_num_cus(),
         },
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
@@ -620,9 +644,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(f"gemm_streamk_bf16_kn_{w.M}x{w.N}x{w.K}", "gemm_streamk<0, 0,")
-            if call.plan.decision == dg.GEMM_STREAMK and not call.plan.atomic and w.dtype == "bf16"
-            and w.b_layout == "kn" else None,
+            "traffic": measured_traffic(profile_key(dg, call.plan, w)),
             "kernel_mean_us": round(kern_ms * 1e3, 3),
         },
         "cpu_baseline": cpu,

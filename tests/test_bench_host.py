@@ -34,11 +34,27 @@ def test_code_digest_ignores_comments_only(tmp_path):
 def test_traffic_is_reported_only_for_the_profiled_code(monkeypatch):
     entries = json.loads((ROOT / "profiles" / "traffic.json").read_text())
     name, entry = next(iter(entries.items()))
-    kernel = entry["kernel"]
     monkeypatch.setattr(bench, "kernel_code_digest", lambda path=None: entry["code_sha256"])
-    assert bench.measured_traffic(name, kernel) == int(entry["bytes"])
-    assert bench.measured_traffic(name, "some_other_kernel") is None
-    assert bench.measured_traffic("no_such_profile", kernel) is None
+    assert bench.measured_traffic(name) == int(entry["bytes"])
+    assert bench.measured_traffic("no_such_profile") is None
     monkeypatch.setattr(bench, "kernel_code_digest", lambda path=None: "0" * 64)
-    assert bench.measured_traffic(name, kernel) is None
+    assert bench.measured_traffic(name) is None
+
+
+def test_profile_key_names_the_launch():
+    class P:   # the plan fields profile_key reads
+        decision, atomic, bm, bn, tiles_m, tiles_n, tiles = 3, 0, 128, 128, 16, 17, 272
+
+    class DG:
+        GEMM_DP, GEMM_SPLITK, GEMM_STREAMK = 1, 2, 3
+
+        @staticmethod
+        def gemm_num_cus():
+            return 256
+
+    from workloads import WORKLOADS
+    w = WORKLOADS["c3_wavequant"]
+    assert bench.profile_key(DG, P, w) == "gemm_streamk_bf16_kn_2048x2176x4096"
+    P.bm = 256
+    assert bench.profile_key(DG, P, w) == "gemm_streamk_bf16_kn_2048x2176x4096_256x128"
 
