@@ -52,7 +52,7 @@ def parse():
                     help="override the workload's decomposition (for profiling one arm)")
     ap.add_argument("--splits", type=int, default=None, help="Split-K factor or Stream-K units")
     ap.add_argument("--atomic", action="store_true", help="Stream-K atomic fixup")
-    ap.add_argument("--tile", default="128x128", choices=["128x128", "256x128"],
+    ap.add_argument("--tile", default="128x128", choices=["128x128", "256x128", "64x128"],
                     help="output tile of the timed call (256x128: Stream-K only)")
     ap.add_argument("--shape", default=None,
                     help="MxNxK: time the workload's recipe at another shape (profiling one launch)")
@@ -202,7 +202,8 @@ def paired_speedup(base_rounds, arm_rounds):
 
 
 # samples per round and calls per sample: a few seconds of GPU time per workload
-PROTOCOL = {"c1": (40, 8), "c2": (40, 8), "c3": (40, 8), "c4": (6, 2), "c5": (20, 8), "x1": (12, 4), "x2": (20, 8)}
+PROTOCOL = {"c1": (40, 8), "c2": (40, 8), "c3": (40, 8), "c4": (6, 2), "c5": (20, 8), "x1": (12, 4), "x2": (20, 8),
+            "x3": (40, 8)}
 
 
 def shape_arms(dg, name, rounds):
@@ -220,12 +221,15 @@ def shape_arms(dg, name, rounds):
         arms["splitk%d" % w.splits] = ("splitk", w.splits, False)
         arms["splitk%d_in_launch" % w.splits] = ("splitk", w.splits, "in_launch")
         arms["splitk%d_atomic" % w.splits] = ("splitk", w.splits, True)
+        arms["splitk%d_64x128" % w.splits] = ("splitk", w.splits, False)
     if name.startswith("c1"):
         arms["streamk32"] = ("streamk", 32, False)
         arms["streamk32_in_launch"] = ("streamk", 32, "in_launch")
         arms["splitk4"] = ("splitk", 4, False)
         arms["splitk4_in_launch"] = ("splitk", 4, "in_launch")
         arms["heuristic"] = ("heuristic", 0, False)
+        arms["streamk32_64x128"] = ("streamk", 32, False)
+        arms["heuristic_64x128"] = ("heuristic", 0, False)
     if name.startswith("c3"):
         arms["heuristic"] = ("heuristic", 0, False)
         arms["heuristic_epilogue"] = ("heuristic", 0, False, epi)
@@ -246,6 +250,11 @@ def shape_arms(dg, name, rounds):
         arms["heuristic"] = ("heuristic", 0, False)
         arms["streamk"] = ("streamk", 0, False)
         arms["streamk_256x128"] = ("streamk", 0, False)
+    if name.startswith("x3"):
+        arms["heuristic"] = ("heuristic", 0, False)
+        arms["dp_64x128"] = ("dp", 0, False)
+        arms["heuristic_64x128"] = ("heuristic", 0, False)
+        arms["splitk8_64x128"] = ("splitk", 8, False)
     if name.startswith("x2"):
         arms["heuristic"] = ("heuristic", 0, False)
         arms["streamk"] = ("streamk", 0, False)
@@ -255,7 +264,7 @@ def shape_arms(dg, name, rounds):
         out["batch"] = w.batch
     calls = {}
     for arm, (mode, splits, atomic, *ep) in arms.items():
-        tile = "256x128" if arm.endswith("256x128") else "128x128"
+        tile = next((t for t in ("256x128", "64x128") if arm.endswith("_" + t)), "128x128")
         calls[arm] = Call(dg, a, b, c, w.b_layout, mode, splits, atomic, epilogue=ep[0] if ep else None, tile=tile)
     samples, pack = PROTOCOL[name[:2]]
     timed = time_arms(calls, rounds, samples, pack)
@@ -569,7 +578,7 @@ def main():
     shapes = {}
     if not args.no_shapes:
         for name in ("c3_wavequant", "c1_sk32", "c2a_m96_s8", "c2b_m256_s2", "c5_longk_fp16", "c4_large_dp",
-                     "x1_hybrid", "x2_batched"):
+                     "x1_hybrid", "x2_batched", "x3_decode"):
             shapes[name] = shape_arms(dg, name, args.rounds)
     vendor = {}
     if args.vendor and not args.no_shapes:

@@ -81,7 +81,7 @@ struct DeviceState {
     int64_t cap_data = 0;
     std::vector<void *> retired;   // outgrown data blocks, freed by gemm_release()
     std::vector<uint32_t *> retired_control;   // outgrown control blocks (status word first)
-    int bpc[2][2][5][2] = {};      // resident workgroups per CU [dtype][B layout][kind][tall], 0 = not queried
+    int bpc[2][2][5][3] = {};      // resident workgroups per CU [dtype][B layout][kind][tile shape], 0 = not queried
 };
 
 std::mutex g_mu;
@@ -304,9 +304,12 @@ int run(const gemm_args_t &a, bool noalloc = false) {
 
     const int dtype = (a.layout & 0xF0u) == GEMM_FP16 ? 1 : 0;
     const int blayout = (a.layout & 0xFu) == GEMM_B_NK ? 1 : 0;
-    const bool tall = p.bm != GEMM_BM;   // 256 x 128 tiles
-    if (tall && a.epilogue != 0)
+    // tile shape: 0 = 128 x 128, 1 = 256 x 128, 2 = 64 x 128
+    const int shape = p.bm == GEMM_BM ? 0 : (p.bm > GEMM_BM ? 1 : 2);
+    if (shape == 1 && a.epilogue != 0)
         return fail(GEMM_ERR_UNSUPPORTED, "GEMM_TILE_256x128 has no fused epilogue");
+    if (shape == 2 && a.epilogue != 0 && p.decision == GEMM_STREAMK)
+        return fail(GEMM_ERR_UNSUPPORTED, "GEMM_TILE_64x128 has no fused epilogue with Stream-K");
 
     if (a.K == 0) {  // the empty sum
         if (a.epilogue == 0) {
@@ -332,7 +335,7 @@ int run(const gemm_args_t &a, bool noalloc = false) {
                                                   : dgw::K_SK;
     if (p.decision == GEMM_STREAMK) {
         // every unit must be resident at once: owners wait for higher units
-        int &bpc = ds->bpc[dtype][blayout][kmode][tall ? 1 : 0];
+        int &bpc = ds->bpc[dtype][blayout][kmode][shape];
         if (bpc == 0) {
             if ((e = dgw::blocks_per_cu(dtype, blayout, kmode, p.bm, &bpc)) != hipSuccess)
                 return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
@@ -390,7 +393,8 @@ int run(const gemm_args_t &a, bool noalloc = false) {
     kp.tm = p.bm;
     kp.tiles_m = (int)p.tiles_m;
     kp.tiles_n = (int)p.tiles_n;
-    // raster bands of group_m 128-row tile rows: the same height in rows for tall tiles
+    // raster bands of group_m 128-row tile rows: the same height in rows for
+    // 256- and 64-row tiles
     kp.group_m = tuning().group_m > 0 ? std::max(1, tuning().group_m * GEMM_BM / p.bm) : 0;
     kp.xcd_spread = a.unit_perm ? 0 : tuning().xcd_spread;
     kp.timing = reinterpret_cast<long long *>(a.timing);
@@ -446,7 +450,7 @@ int run(const gemm_args_t &a, bool noalloc = false) {
         // T tiles on C CUs groups win when ceil(G / C) * 4 < ceil(T / C) * 1.4
         const int64_t ngroups = batch * ((p.tiles_m + 1) / 2) * ((p.tiles_n + 1) / 2);
         const int64_t gwaves = (ngroups + ncu - 1) / ncu, twaves = (p.tiles + ncu - 1) / ncu;
-        const bool groups = gwaves * 40 < twaves * 14 && !(a.debug & GEMM_DEBUG_TILE_DP);
+        const bool groups = shape == 0 && gwaves * 40 < twaves * 14 && !(a.debug & GEMM_DEBUG_TILE_DP);
         if (groups) {
             kp.ntiles = (int)ngroups;
             if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_DP_GROUP, (int)ngroups, kp, stream)) != hipSuccess)
@@ -465,8 +469,8 @@ int run(const gemm_args_t &a, bool noalloc = false) {
         // last arriver at the tile's counter adds up the whole tile.
         // GEMM_DEBUG_IN_LAUNCH keeps the last arriver.
         if (kp.merge == dgw::MERGE_IN_LAUNCH && p.splits > 1 && (a.N & 3) == 0 && !(a.debug & GEMM_DEBUG_IN_LAUNCH)) {
-            int &bpc = ds->bpc[dtype][blayout][dgw::K_SPLITK][0];
-            if (bpc == 0 && (e = dgw::blocks_per_cu(dtype, blayout, dgw::K_SPLITK, GEMM_BM, &bpc)) != hipSuccess)
+            int &bpc = ds->bpc[dtype][blayout][dgw::K_SPLITK][shape];
+            if (bpc == 0 && (e = dgw::blocks_per_cu(dtype, blayout, dgw::K_SPLITK, p.bm, &bpc)) != hipSuccess)
                 return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
             if (p.tiles * p.splits <= (int64_t)bpc * ds->num_cus) kp.merge = dgw::MERGE_BANDS;
         }

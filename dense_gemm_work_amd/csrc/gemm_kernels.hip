@@ -227,9 +227,9 @@ __device__ __forceinline__ u32x2 lds_tr16(uint32_t addr) {
 // ---------------------------------------------------------------------------
 constexpr int SLAB_BYTES = BM * BK * 2;   // 16 KiB: a B slab, or the A slab of a 128-row tile
 
-// Tile of TM x 128 (TM = 128, or 256 for the tall Stream-K tile): the A slab
-// is TM x 64, the B slab 64 x 128; each wave owns (TM / 2) x 64, i.e. RB
-// 32-row blocks by two 32-column blocks.
+// Tile of TM x 128 (TM = 128; 256 for the tall Stream-K tile; 64 for the
+// skinny tile, with 4 waves): the A slab is TM x 64, the B slab 64 x 128; each
+// wave owns (TM / 2) x 64, i.e. RB 32-row blocks by two 32-column blocks.
 template <int TM>
 constexpr int aslab_bytes() { return TM * BK * 2; }
 template <int TM>
@@ -244,7 +244,8 @@ struct MainLoop {
     static constexpr int DPWB = 16 / NW;         // loads per wave of the B slab
     static constexpr int DPI = DPWA + DPWB;      // loads per wave and iteration
     static constexpr int BREG = NS * ASLAB;      // start of the B slabs
-    static_assert(TM == 128 || TM == 256, "128- or 256-row tiles");
+    static_assert(TM == 64 || TM == 128 || TM == 256, "64-, 128- or 256-row tiles");
+    static_assert(TM != 64 || NW == 4, "the 64-row tile runs four waves (no k-halves to merge)");
     static_assert(NS >= 3 && NS <= 4, "three or four stages");
     static_assert(NW == 4 || NW == 8, "four or eight waves");
 
@@ -361,7 +362,7 @@ struct MainLoop {
                 f.a[j][rb] = lds_b128<AO - AHI + rb * 4096>(abase);
             };
             row_block(std::integral_constant<int, 0>());
-            row_block(std::integral_constant<int, 1>());
+            if constexpr (RB > 1) row_block(std::integral_constant<int, 1>());
             if constexpr (RB > 2) {
                 row_block(std::integral_constant<int, 2>());
                 row_block(std::integral_constant<int, 3>());
@@ -402,7 +403,7 @@ struct MainLoop {
             f.a[rb] = lds_b128<AO - AHI + rb * 4096>(abase);
         };
         row_block(std::integral_constant<int, 0>());
-        row_block(std::integral_constant<int, 1>());
+        if constexpr (RB > 1) row_block(std::integral_constant<int, 1>());
         if constexpr (RB > 2) {
             row_block(std::integral_constant<int, 2>());
             row_block(std::integral_constant<int, 3>());
@@ -761,7 +762,7 @@ __device__ __forceinline__ void for_each_element(const Tile<NW, TM> &t, int m0, 
         }
 }
 
-// Row-major staging of the fp32 tile in LDS (64 KiB), then coalesced float4
+// Row-major staging of the fp32 tile in LDS (TM / 2 KiB), then coalesced float4
 // traffic: thread t owns quads t + NT q, quad f covering columns 4 (f % 32) .. +3
 // of tile row f / 32.  Column c of row r is stored at c ^ epi_swz(r): the two
 // rows written by one MFMA result register (4 apart) then fall on different
@@ -769,17 +770,17 @@ __device__ __forceinline__ void for_each_element(const Tile<NW, TM> &t, int m0, 
 constexpr int EPI_LD = BN;
 __device__ __forceinline__ int epi_swz(int r) { return ((r >> 2) & 1) << 5; }
 
-template <int NW>
-__device__ __forceinline__ void acc_to_lds(float *tile, const Tile<NW> &t) {
+template <int NW, int TM>
+__device__ __forceinline__ void acc_to_lds(float *tile, const Tile<NW, TM> &t) {
     const Role<NW> w;
 #pragma unroll
-    for (int r = 0; r < Tile<NW>::R; ++r)
+    for (int r = 0; r < Tile<NW, TM>::R; ++r)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int col = w.wn * 64 + j * 32 + (w.lane & 31);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = w.wm * 64 + t.i[r] * 32 + 8 * (e >> 2) + 4 * (w.lane >> 5) + (e & 3);
+                const int row = w.wm * (TM / 2) + t.i[r] * 32 + 8 * (e >> 2) + 4 * (w.lane >> 5) + (e & 3);
                 tile[row * EPI_LD + (col ^ epi_swz(row))] = t.v[r][j][e];
             }
         }
@@ -791,9 +792,9 @@ __device__ __forceinline__ f32x4 staged_quad(const float *tile, int r, int c) {
 
 // Calls f(q, row, col, global offset, valid columns in the quad (1..4)) for the
 // thread's quads; rows beyond M and quads wholly beyond N are skipped.
-template <int NW, class F>
+template <int NW, int TM, class F>
 __device__ __forceinline__ void for_each_quad(int m0, int n0, int M, int N, F &&f) {
-    constexpr int NT = Role<NW>::NT, QPT = BM * BN / 4 / NT;
+    constexpr int NT = Role<NW>::NT, QPT = TM * BN / 4 / NT;
 #pragma unroll
     for (int q = 0; q < QPT; ++q) {
         const int fq = threadIdx.x + NT * q;
@@ -975,11 +976,11 @@ __device__ __forceinline__ void epi_prefetch(const KParams &p, int m0, int n0, f
 
 // The epilogue and the stores of one held 32-row block (row r of the tile),
 // its prior C values and bias values given.
-template <int NW>
-__device__ __forceinline__ void finish_block(const KParams &p, int m0, int n0, const Tile<NW> &t, int r,
+template <int NW, int TM>
+__device__ __forceinline__ void finish_block(const KParams &p, int m0, int n0, const Tile<NW, TM> &t, int r,
                                              const float (&cin)[32], const float (&bj)[2]) {
     const Role<NW> w;
-    const CBlock<2> cb(p, m0 + w.wm * 64 + t.i[r] * 32, n0 + w.wn * 64);
+    const CBlock<2> cb(p, m0 + w.wm * (TM / 2) + t.i[r] * 32, n0 + w.wn * 64);
     float v[32], c[32], bv[32];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -1000,7 +1001,7 @@ __device__ __forceinline__ void finish_block(const KParams &p, int m0, int n0, c
 // before the first store.
 template <int NW, bool EPI = true, int TM = 128>
 __device__ __forceinline__ void store_final(const KParams &p, int m0, int n0, const Tile<NW, TM> &t) {
-    static_assert(!EPI || TM == 128, "the fused epilogue serves 128-row tiles");
+    static_assert(!EPI || TM <= 128, "the fused epilogue serves 64- and 128-row tiles");
     if constexpr (!EPI) {
         store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
     } else {
@@ -1014,14 +1015,14 @@ __device__ __forceinline__ void store_final(const KParams &p, int m0, int n0, co
         float bj[2];
         lane_bias<2>(p, C0, bj);
 #pragma unroll
-        for (int r = 0; r < Tile<NW>::R; ++r) {
-            const CBlock<2> cb(p, m0 + w.wm * 64 + t.i[r] * 32, C0);
+        for (int r = 0; r < Tile<NW, TM>::R; ++r) {
+            const CBlock<2> cb(p, m0 + w.wm * (TM / 2) + t.i[r] * 32, C0);
             float cin[32];
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) cin[j * 16 + e] = rc ? cb.load(e, j) : 0.0f;
-            finish_block<NW>(p, m0, n0, t, r, cin, bj);
+            finish_block<NW, TM>(p, m0, n0, t, r, cin, bj);
         }
     }
 }
@@ -1290,18 +1291,18 @@ struct WgClock {
 // ---------------------------------------------------------------------------
 // Data-parallel: one workgroup per tile of [tile_base, tile_base + ntiles).
 // ---------------------------------------------------------------------------
-template <int DT, int BL, int NS, int NW>
+template <int DT, int BL, int NS, int NW, int TM = 128>
 __global__ __launch_bounds__(64 * NW) void gemm_dp(KParams p) {
-    __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds[lds_bytes<TM>(NS)];
     const WgClock clk(p);
     const int w = worker_of(p, p.ntiles);
     const int tile = p.tile_base + w;
     int m0, n0;
     const KParams q = tile_view(p, tile, m0, n0);
-    Acc acc;
+    AccT<TM> acc;
     zero_acc(acc);
-    mac_loop<DT, BL, NS, NW>(q, lds, m0, n0, 0, p.ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
-    const Tile<NW> t = merge_k_halves<NW>(acc, lds);
+    mac_loop<DT, BL, NS, NW, TM>(q, lds, m0, n0, 0, p.ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
+    const Tile<NW, TM> t = merge_k_halves<NW, TM>(acc, lds);
     clk.mark(p, 0);
     store_final<NW>(q, m0, n0, t);
     trace_segment(p, p.worker_base + w, 0, tile, 0, p.ipt, 0);
@@ -1672,10 +1673,12 @@ __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
 // ---------------------------------------------------------------------------
 // Split-K: worker w = tile * S + s covers k-iterations [s P / S, (s+1) P / S).
 // ---------------------------------------------------------------------------
-template <int DT, int BL, int NS, int NW>
+template <int DT, int BL, int NS, int NW, int TM = 128>
 __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p0) {
-    constexpr int NT = Role<NW>::NT, QPT = BM * BN / 4 / NT;
-    __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_BYTES];
+    constexpr int NT = Role<NW>::NT, QPT = TM * BN / 4 / NT;
+    // the stages, reused to stage the fp32 tile (TM x 128) after the loop
+    static_assert(lds_bytes<TM>(NS) >= TM * BN * 4, "the staged tile fits the stages");
+    __shared__ __attribute__((aligned(16))) char lds[lds_bytes<TM>(NS)];
     __shared__ int last_arriver;
     const WgClock clk(p0);
     const int S = p0.splits;
@@ -1684,10 +1687,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p0) {
     const int k0 = (int)((int64_t)s * p0.ipt / S), k1 = (int)((int64_t)(s + 1) * p0.ipt / S);
     int m0, n0;
     const KParams p = tile_view(p0, tile, m0, n0);   // the tile's batch entry
-    Acc acc;
+    AccT<TM> acc;
     zero_acc(acc);
-    mac_loop<DT, BL, NS, NW>(p, lds, m0, n0, k0, k1, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
-    const Tile<NW> t = merge_k_halves<NW>(acc, lds);
+    mac_loop<DT, BL, NS, NW, TM>(p, lds, m0, n0, k0, k1, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
+    const Tile<NW, TM> t = merge_k_halves<NW, TM>(acc, lds);
     clk.mark(p, 0);
     trace_segment(p, w, 0, tile, k0, k1, S == 1 ? 0 : (s == 0 ? 1 : 2));
     if (S == 1) {
@@ -1705,20 +1708,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p0) {
     // with device-scope stores (LDS keeps the copy this workgroup may fold itself)
     const size_t mn = (size_t)p.M * p.N;
     float *stg = reinterpret_cast<float *>(lds);
-    acc_to_lds<NW>(stg, t);
+    acc_to_lds<NW, TM>(stg, t);
     __syncthreads();
     const size_t org = (size_t)m0 * p.N + n0;                 // tile origin within [M,N]
-    const uint32_t span_bytes = (uint32_t)(((size_t)(min(BM, p.M - m0) - 1) * p.N + min(BN, p.N - n0)) * 4);
+    const uint32_t span_bytes = (uint32_t)(((size_t)(min(TM, p.M - m0) - 1) * p.N + min(BN, p.N - n0)) * 4);
     auto quad_off = [&](int r, int c) { return (uint32_t)(((size_t)r * p.N + c) * 4); };
-    // MERGE_BANDS: row band q (rows 16 q .. 16 q + 15 of the tile, the thread's
-    // quad q) is added up by split q mod S, which takes its own part of the band
+    // MERGE_BANDS: row band q (rows TM q / 8 .. TM (q + 1) / 8 - 1 of the tile,
+    // the threads' quad q) is added up by split q mod S, which takes its own part of the band
     // from LDS and so does not store it
     const bool bands = p.merge == MERGE_BANDS;
     {
         const __amdgpu_buffer_rsrc_t rp = span(p.part + (size_t)s * mn + org, span_bytes);
         float *Ps = p.part + (size_t)s * mn;
         const bool zero = zero_partials(p);   // the zero-partial control
-        for_each_quad<NW>(m0, n0, p.M, p.N, [&](int q, int r, int c, size_t off, int nv) {
+        for_each_quad<NW, TM>(m0, n0, p.M, p.N, [&](int q, int r, int c, size_t off, int nv) {
             if (bands && q % S == s) return;
             const f32x4 v = zero ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : staged_quad(stg, r, c);
             if (nv == 4) {
@@ -1939,17 +1942,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p0) {
 // bits, as the in-launch fold.
 // ---------------------------------------------------------------------------
 constexpr int RED_THREADS = 256;
-constexpr int RED_BLOCKS_PER_TILE = BM * BN / 4 / RED_THREADS;   // 16
+// workgroups per tile of tm rows: 16 for 128-row tiles
+__host__ __device__ constexpr int red_blocks_per_tile(int tm) { return tm * BN / 4 / RED_THREADS; }
 
 template <bool EPI>
 __global__ __launch_bounds__(RED_THREADS) void splitk_reduce(KParams p0) {
-    const int tile = blockIdx.x / RED_BLOCKS_PER_TILE;
-    const int q = (blockIdx.x % RED_BLOCKS_PER_TILE) * RED_THREADS + threadIdx.x;   // quad within the tile
+    const int bpt = red_blocks_per_tile(p0.tm);
+    const int tile = blockIdx.x / bpt;
+    const int q = (blockIdx.x % bpt) * RED_THREADS + threadIdx.x;   // quad within the tile
     int m0, n0;
     const KParams p = tile_view(p0, tile, m0, n0);   // the tile's batch entry
     const int r = q >> 5, c = (q & 31) * 4;
     const int S = p.splits;
-    if (threadIdx.x == 0 && blockIdx.x % RED_BLOCKS_PER_TILE == 0)
+    if (threadIdx.x == 0 && blockIdx.x % bpt == 0)
         for (int t = 0; t < S; ++t) trace_folded(p, tile, t, tile * S + t);
     if (m0 + r >= p.M || n0 + c >= p.N) return;
     const size_t mn = (size_t)p.M * p.N;
@@ -1994,14 +1999,17 @@ __global__ __launch_bounds__(RED_THREADS) void splitk_reduce(KParams p0) {
 // second slot bank, the next units their first segments into the first bank;
 // C = ((owner + peer 1) + peer 2) + ..., the turnstile's order, so the bits are
 // the turnstile's.  Slots are in register-native order: 16-byte element f =
-// ((quad * 4 + b) * 4 + e4) * 64 + lane holds rows r..r+3 of one column.  One
-// thread per such element, 16 workgroups of 256 threads per Stream-K tile;
-// tiles that one unit computed whole were stored by it and are skipped.
+// ((quad * BPQ + b) * 4 + e4) * 64 + lane (BPQ = tm / 32 blocks of 32 x 32 per
+// wave quadrant) holds rows r..r+3 of one column.  One thread per such element,
+// tm / 8 workgroups of 256 threads per Stream-K tile; tiles that one unit
+// computed whole were stored by it and are skipped.
 // ---------------------------------------------------------------------------
 template <bool EPI>
 __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
-    const int ts = blockIdx.x / RED_BLOCKS_PER_TILE;
-    const int f = (blockIdx.x % RED_BLOCKS_PER_TILE) * RED_THREADS + threadIdx.x;
+    const int bpt = red_blocks_per_tile(p.tm);
+    const int slot = p.tm * BN;                 // floats of one partial slot
+    const int ts = blockIdx.x / bpt;
+    const int f = (blockIdx.x % bpt) * RED_THREADS + threadIdx.x;
     const int tb = ts * p.ipt, tile_end = tb + p.ipt;
     const int owner = unit_of(tb, p.q, p.big);
     if (unit_start(owner, p.q, p.big) + p.q + (owner < p.big ? 1 : 0) >= tile_end) return;   // whole tile
@@ -2012,22 +2020,23 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
         trace_folded(p, tile, 0, owner);
         for (int v = owner + 1; v < vend; ++v) trace_folded(p, tile, v - owner, v);
     }
-    const f32x4 *own = reinterpret_cast<const f32x4 *>(p.part + ((size_t)p.units + owner) * (BM * BN));
+    const f32x4 *own = reinterpret_cast<const f32x4 *>(p.part + ((size_t)p.units + owner) * slot);
     const f32x4 *first = reinterpret_cast<const f32x4 *>(p.part);
     f32x4 sum = own[f];
     for (int v0 = owner + 1; v0 < vend; v0 += 4) {
         f32x4 x[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (v0 + j < vend) x[j] = first[(size_t)(v0 + j) * (BM * BN / 4) + f];
+            if (v0 + j < vend) x[j] = first[(size_t)(v0 + j) * (slot / 4) + f];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             if (v0 + j < vend) sum += x[j];
     }
     int m0, n0;
     const KParams pv = tile_view(p, tile, m0, n0);   // the tile's batch entry
-    const int lane = f & 63, e4 = (f >> 6) & 3, b = (f >> 8) & 3, quad = f >> 10;
-    const int row = m0 + (quad >> 1) * 64 + (b >> 1) * 32 + 8 * e4 + 4 * (lane >> 5);
+    const int bpq = p.tm / 32;                  // 32 x 32 blocks per wave quadrant
+    const int lane = f & 63, e4 = (f >> 6) & 3, b = (f >> 8) % bpq, quad = (f >> 8) / bpq;
+    const int row = m0 + (quad >> 1) * (p.tm / 2) + (b >> 1) * 32 + 8 * e4 + 4 * (lane >> 5);
     const int col = n0 + (quad & 1) * 64 + (b & 1) * 32 + (lane & 31);
     if (col >= p.N) return;
     if (EPI) {
@@ -2232,8 +2241,10 @@ __global__ void zero_words(uint32_t *p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// Host-side dispatch.  Every kernel runs 8 waves on 128 KiB of LDS (one
-// workgroup per CU): 4 stages of 128x128 tiles, or 2 stages of 2x2 tile groups.
+// Host-side dispatch.  The 128x128 tile kernels run 8 waves on 128 KiB of LDS
+// (one workgroup per CU): 4 stages of 128x128 tiles, or 2 stages of 2x2 tile
+// groups; the 256x128 tile 8 waves on 3 stages (144 KiB); the 64x128 tile 4
+// waves on 3 stages (72 KiB, two workgroups per CU).
 // Split-K and Stream-K share the per-segment accumulation order, so the two
 // agree bit for bit whenever their segments coincide.
 // ---------------------------------------------------------------------------
@@ -2255,6 +2266,19 @@ KernelFn pick(int kmode, bool epi, int tm, Shape &shape) {
         if (kmode == K_SK) return gemm_streamk<DT, BL, 3, 8, false, false, 256>;
         if (kmode == K_SK_ATOMIC) return gemm_streamk<DT, BL, 3, 8, true, false, 256>;
         return nullptr;
+    }
+    if (tm == 64) {
+        // the skinny 64 x 128 tile: four waves of 32 x 64 over every k-step, three
+        // stages of (8 KiB A + 16 KiB B), so two workgroups share a CU; the
+        // epilogue in the data-parallel and Split-K builds, not in Stream-K
+        shape = {3, 4};
+        switch (kmode) {
+        case K_DP: return gemm_dp<DT, BL, 3, 4, 64>;
+        case K_SPLITK: return gemm_splitk<DT, BL, 3, 4, 64>;
+        case K_SK: return epi ? nullptr : gemm_streamk<DT, BL, 3, 4, false, false, 64>;
+        case K_SK_ATOMIC: return epi ? nullptr : gemm_streamk<DT, BL, 3, 4, true, false, 64>;
+        default: return nullptr;
+        }
     }
     if (tm != 128) return nullptr;
     // Stream-K has a separate build with the epilogue: its plain build keeps
@@ -2295,10 +2319,10 @@ hipError_t launch_splitk_reduce(const KParams &p, hipStream_t stream) {
     if (tiles <= 0) return hipSuccess;
     // a separate build with the epilogue keeps the plain one's code unchanged
     if (p.epi != EPI_PLAIN)
-        hipLaunchKernelGGL(splitk_reduce<true>, dim3((unsigned)(tiles * RED_BLOCKS_PER_TILE)), dim3(RED_THREADS), 0,
+        hipLaunchKernelGGL(splitk_reduce<true>, dim3((unsigned)(tiles * red_blocks_per_tile(p.tm))), dim3(RED_THREADS), 0,
                            stream, p);
     else
-        hipLaunchKernelGGL(splitk_reduce<false>, dim3((unsigned)(tiles * RED_BLOCKS_PER_TILE)), dim3(RED_THREADS), 0,
+        hipLaunchKernelGGL(splitk_reduce<false>, dim3((unsigned)(tiles * red_blocks_per_tile(p.tm))), dim3(RED_THREADS), 0,
                            stream, p);
     return hipGetLastError();
 }
@@ -2306,10 +2330,10 @@ hipError_t launch_splitk_reduce(const KParams &p, hipStream_t stream) {
 hipError_t launch_streamk_reduce(const KParams &p, int64_t sk_tiles, hipStream_t stream) {
     if (sk_tiles <= 0) return hipSuccess;
     if (p.epi != EPI_PLAIN)
-        hipLaunchKernelGGL(streamk_reduce<true>, dim3((unsigned)(sk_tiles * RED_BLOCKS_PER_TILE)), dim3(RED_THREADS),
+        hipLaunchKernelGGL(streamk_reduce<true>, dim3((unsigned)(sk_tiles * red_blocks_per_tile(p.tm))), dim3(RED_THREADS),
                            0, stream, p);
     else
-        hipLaunchKernelGGL(streamk_reduce<false>, dim3((unsigned)(sk_tiles * RED_BLOCKS_PER_TILE)), dim3(RED_THREADS),
+        hipLaunchKernelGGL(streamk_reduce<false>, dim3((unsigned)(sk_tiles * red_blocks_per_tile(p.tm))), dim3(RED_THREADS),
                            0, stream, p);
     return hipGetLastError();
 }
@@ -2334,7 +2358,7 @@ hipError_t launch_zero(void *ptr, int64_t n_words, hipStream_t stream) {
 
 hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int tm, int *out) {
     // the smaller of the builds with and without the epilogue (the 256-row tile
-    // has no epilogue build)
+    // has no epilogue build, the 64-row tile's plain build serves both)
     int best = 1 << 30;
     for (int epi = 0; epi < (tm == 128 ? 2 : 1); ++epi) {
         Shape shape{0, 0};

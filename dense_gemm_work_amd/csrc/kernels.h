@@ -49,7 +49,7 @@ struct KParams {
     const uint16_t *B;     // [K,N] or [N,K] row-major
     float *C;              // [M,N] row-major fp32
     int M, N, K;
-    int tm;                // tile rows: 128, or 256 for the tall Stream-K tile (tiles are tm x 128)
+    int tm;                // tile rows: 128, 256 (tall Stream-K tile) or 64 (skinny tile); tiles are tm x 128
     int tiles_m, tiles_n;  // output tiles along M and N (of one batch entry)
     int group_m;           // tile ids run column by column in groups of group_m tile rows (0: row-major)
     int xcd_spread;        // 1: give each XCD a contiguous range of workers
@@ -61,7 +61,7 @@ struct KParams {
     int splits;            // Split-K factor S
     int merge;             // MERGE_IN_LAUNCH, MERGE_TWO_PASS or (Split-K) MERGE_ATOMIC
     int worker_base;       // trace id of this launch's worker 0
-    float *part;           // Stream-K slots [units][BM*BN] ([2][units][BM*BN] two-pass) or Split-K [S][M][N]
+    float *part;           // Stream-K slots [units][tm*BN] ([2][units][tm*BN] two-pass) or Split-K [S][M][N]
     uint32_t *flags;       // Stream-K: flag per unit (epoch-valued)
     uint32_t *counters;    // Split-K: arrival counter per tile (reset by the last arriver)
     uint32_t *status;      // device error word
@@ -83,7 +83,9 @@ struct KParams {
 
 // Launch `grid` workgroups of the kernel for (dtype, B layout, mode) on `stream`.
 // dtype: 0 bf16, 1 fp16; blayout: 0 = B [K,N], 1 = B [N,K].  p.tm = 256 selects
-// the 256 x 128 tile build (Stream-K kinds only, no fused epilogue).
+// the 256 x 128 tile build (Stream-K kinds only, no fused epilogue); p.tm = 64
+// the 64 x 128 tile builds (data-parallel, Split-K, Stream-K; no fused epilogue
+// in Stream-K, no 2x2 tile groups).
 hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParams &p,
                        hipStream_t stream);
 

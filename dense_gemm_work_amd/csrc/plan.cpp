@@ -52,8 +52,10 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, u
     const uint32_t decomp = mode & 0xFu;
     const bool atomic = (mode & GEMM_ATOMIC) != 0;
     const bool two_pass = (mode & GEMM_TWO_PASS) != 0;
-    const bool tall = (mode & GEMM_TILE_256x128) != 0;
-    if ((mode & ~(0xFu | GEMM_ATOMIC | GEMM_TWO_PASS | GEMM_TILE_256x128)) || decomp > GEMM_STREAMK) {
+    const uint32_t tile = mode & (GEMM_TILE_256x128 | GEMM_TILE_64x128);
+    const bool tall = tile == GEMM_TILE_256x128;
+    if ((mode & ~(0xFu | GEMM_ATOMIC | GEMM_TWO_PASS | GEMM_TILE_256x128 | GEMM_TILE_64x128)) ||
+        decomp > GEMM_STREAMK || tile == (GEMM_TILE_256x128 | GEMM_TILE_64x128)) {
         *why = "mode word has unknown bits";
         return GEMM_ERR_INVALID;
     }
@@ -88,7 +90,8 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, u
 
     gemm_plan_t &p = *out;
     p.atomic = 0;
-    p.bm = tall ? 2 * GEMM_BM : GEMM_BM; p.bn = GEMM_BN; p.bk = GEMM_BK;
+    p.bm = tall ? 2 * GEMM_BM : (tile == GEMM_TILE_64x128 ? GEMM_BM / 2 : GEMM_BM);
+    p.bn = GEMM_BN; p.bk = GEMM_BK;
     p.num_cus = num_cus;
     p.batch = batch;
     p.tiles_m = ceil_div(M, p.bm);

@@ -119,6 +119,16 @@ extern "C" {
                                       Stream-K example (MmaTileShape 256 x 128 x 64); a unit's
                                       64-wide k-iteration is then twice the work, the partial
                                       slot 128 KiB.                                            */
+#define GEMM_TILE_64x128   0x2000u /* 64 x 128 tiles: the skinny shape for small M (the CUTLASS
+                                      guide's "Tile Size Selection", tall/skinny tab: 64-row
+                                      tiles when N is much larger than M; the book chapter's
+                                      skinny-problem paragraph: a decode batch of M = 128 has
+                                      too few 128-row tiles to fill the GPU).  Every
+                                      decomposition and merge; with GEMM_STREAMK (also when
+                                      the heuristic picks it) no fused epilogue, and no 2x2
+                                      tile groups for data-parallel launches.  Twice the tile
+                                      rows of 128 x 128 tiles (M = 128 gives two), half the
+                                      partial bytes per split (32 KiB slots).                 */
 
 /* ---- debug bits for gemm_args_t.debug -------------------------------------------- */
 #define GEMM_DEBUG_NO_PUBLISH 0x1u /* Stream-K contributors store partials but never

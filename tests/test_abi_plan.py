@@ -409,3 +409,39 @@ def test_tall_tile_refusals(dg):
     with pytest.raises(dg.GemmError) as ei:
         dg.gemm_plan(2048, 2176, 4096, lw, dg.mode_word("streamk", two_pass=True, tile="256x128"), 0, 256)
     assert ei.value.status == dg.GEMM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("M,N,K,mode,splits,atomic", [
+    (96, 512, 2048, "splitk", 8, False),      # 2 x 4 tiles of 64 x 128 (rows 96..127 empty)
+    (128, 4096, 4096, "splitk", 4, False),    # a decode-sized batch: 64 tiles, 256 workers
+    (64, 4096, 4096, "heuristic", 0, False),  # 32 tiles: Stream-K or Split-K by the rule
+    (128, 4096, 4096, "heuristic", 0, False),
+    (256, 512, 2048, "streamk", 32, True),
+    (300, 200, 328, "streamk", 7, False),     # ragged M, N and K
+    (64, 128, 128, "streamk", 6, False),      # more units than iterations
+    (1000, 1000, 640, "dp", 0, False),
+])
+def test_skinny_tile_plans_match_simulator(dg, M, N, K, mode, splits, atomic):
+    p, s = _compare(dg, M, N, K, mode, splits, 256, atomic=atomic, tile="64x128")
+    assert (p.bm, p.bn, p.bk) == (64, 128, 64)
+    assert p.tiles_m == -(-M // 64)
+    if s.kind == "StreamK" and not atomic:
+        # 64 x 128 fp32 slots (32 KiB): one per unit, two with the second kernel
+        data = p.workspace_bytes - (256 + -(-max(p.sk_units, 1) * 4 // 256) * 256 + -(-p.tiles * 4 // 256) * 256)
+        assert data == (2 if p.two_pass else 1) * p.sk_units * 64 * 128 * 4
+
+
+def test_skinny_tile_doubles_tile_rows_of_a_decode_batch(dg):
+    # the book chapter's skinny case: M = 128 through a 4096-wide projection has
+    # 32 tiles of 128 x 128 and 64 of 64 x 128
+    lw = dg.GEMM_B_KN | dg.GEMM_BF16
+    p128 = dg.gemm_plan(128, 4096, 4096, lw, dg.mode_word("dp"), 0, 256)
+    p64 = dg.gemm_plan(128, 4096, 4096, lw, dg.mode_word("dp", tile="64x128"), 0, 256)
+    assert (p128.tiles, p64.tiles) == (32, 64)
+
+
+def test_tile_bits_are_exclusive(dg):
+    lw = dg.GEMM_B_KN | dg.GEMM_BF16
+    with pytest.raises(dg.GemmError) as ei:
+        dg.gemm_plan(256, 512, 2048, lw, dg.MODES["streamk"] | dg.GEMM_TILE_256x128 | dg.GEMM_TILE_64x128, 0, 256)
+    assert ei.value.status == dg.GEMM_ERR_INVALID

@@ -103,6 +103,11 @@ WORKLOADS = {
     "x2_batched": Workload("x2_batched", 1024, 1024, 2048, "bf16", "kn", "uniform", -1.0, 1.0,
                            mode="heuristic", batch=5,
                            note="5 entries x 64 tiles x 32 iters; heuristic -> Stream-K, 256 units x 40 iterations"),
+    # The book chapter's skinny case: a decode-time batch of 128 rows through a
+    # 4096-wide projection, weights stored [N,K]: 32 tiles of 128x128 (64 of
+    # 64x128) on 256 CUs, 64 iterations each.
+    "x3_decode": Workload("x3_decode", 128, 4096, 4096, "bf16", "nk", "uniform", -1.0, 1.0,
+                          mode="heuristic", note="32 tiles (64 of 64x128); heuristic -> Split-K"),
 }
 
 
