@@ -83,11 +83,14 @@ class Call:
             args.stride_a, args.stride_b, args.stride_c = a.stride(0), b.stride(0), c.stride(0)
         args.layout = dg.layout_word(b_layout, "bf16" if a.dtype == torch.bfloat16 else "fp16")
         # `atomic`: False, True, "two_pass" (partials of split tiles added by a
-        # second kernel) or "in_launch" (added in the launch: Split-K last arriver,
-        # Stream-K turnstile)
+        # second kernel), "in_launch" (added in the launch: Split-K last arriver,
+        # Stream-K turnstile) or "bands" (Split-K: every split adds up its row
+        # bands in the launch)
         args.mode = dg.mode_word(mode, atomic is True, atomic == "two_pass", tile)
         if atomic == "in_launch":
             args.debug = dg.GEMM_DEBUG_IN_LAUNCH
+        if atomic == "bands":
+            args.debug = dg.GEMM_DEBUG_SPLITK_BANDS
         args.splits = splits
         if epilogue is not None:
             # fused epilogue c = act(alpha a.b + beta c + bias): (alpha, beta, bias tensor, act)

@@ -159,21 +159,27 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, u
         p.max_fold = 1;
         p.workspace_bytes = 0;
         break;
-    case GEMM_SPLITK:
+    case GEMM_SPLITK: {
         p.splits = S;
         p.atomic = atomic && S > 1 ? 1 : 0;
         // Deterministic: the partials are added in split order, by a second
         // kernel, or in the launch -- by all S splits of a tile, each adding up
         // its own row bands, when the whole grid is resident at once (the
         // library checks residency), else by the last arriver at the tile's
-        // counter.  Same bits.  Measured on the resident skinny grids (one
-        // workgroup per CU): the row bands win from S = 8 (96x512x2048:
-        // 11.1 us against 12.1 us with the second kernel), the second kernel
-        // below (S = 2 and 4: 13.8 vs 15.1 us, 12.3 vs 12.8 us), where the fold
-        // of a tile is spread over too few workgroups; larger grids' last
-        // arrivers fold partials still warm in L2 (2048x2176x4096 S = 2:
-        // 71.6 us in the launch, 75.9 us with the second kernel).
-        p.two_pass = !p.atomic && S > 1 && (two_pass || (p.tiles * S <= num_cus && S < 8)) ? 1 : 0;
+        // counter.  Same bits.  Measured on grids that fit the CUs: the row
+        // bands win from S = 8 on small grids (96x512x2048 S = 8: 11.2 us
+        // against 12.0 us with the second kernel; 64 and 128 workgroups within
+        // 10 %), the second kernel below S = 8 (S = 2 and 4: 13.7 vs 15.0 us,
+        // 11.5 vs 12.0 us), where a tile's fold is spread over too few
+        // workgroups, and on grids of more than half the CUs, where every
+        // split waits for the slowest (128x4096x4096 S = 8, 256 workgroups:
+        // 18.1 us against 21.7 us in the launch); grids larger than the CUs
+        // keep the last arriver, which folds partials still warm in L2
+        // (2048x2176x4096 S = 2: 71.6 us in the launch, 75.9 us with the
+        // second kernel).
+        const bool fits = p.tiles * S <= num_cus;
+        const bool bands = S >= 8 && 2 * p.tiles * S <= num_cus;
+        p.two_pass = !p.atomic && S > 1 && (two_pass || (fits && !bands)) ? 1 : 0;
         p.workers = p.tiles * S;
         p.max_segments = 1;
         p.max_fold = S;
@@ -181,6 +187,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, u
         // counter per tile
         p.workspace_bytes = S > 1 && !p.atomic ? batch * int64_t(S) * M * N * 4 : 0;
         break;
+    }
     case GEMM_STREAMK: {
         p.atomic = atomic ? 1 : 0;
         p.sk_units = units;

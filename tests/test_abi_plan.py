@@ -308,6 +308,10 @@ def test_splitk_merge_modes_plan(dg):
     # S < 8 on a grid that fits: the second kernel
     assert dg.gemm_plan(M, N, K, lw, dg.GEMM_SPLITK, 4, 256).two_pass == 1
     assert dg.gemm_plan(256, 512, 2048, lw, dg.GEMM_SPLITK, 2, 256).two_pass == 1
+    # S >= 8 on a grid of more than half the CUs: the second kernel (32 tiles x 8
+    # = 256 workgroups); at most half: in the launch (16 tiles x 8 = 128)
+    assert dg.gemm_plan(128, 4096, 4096, lw, dg.GEMM_SPLITK, 8, 256).two_pass == 1
+    assert dg.gemm_plan(128, 2048, 4096, lw, dg.GEMM_SPLITK, 8, 256).two_pass == 0
     assert (auto.atomic, fold.atomic, two.atomic, atom.atomic) == (0, 0, 0, 1)
     assert auto.workspace_bytes == fold.workspace_bytes == two.workspace_bytes
     assert fold.workspace_bytes - atom.workspace_bytes == S * M * N * 4
