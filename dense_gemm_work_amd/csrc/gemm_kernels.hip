@@ -444,10 +444,13 @@ struct MainLoop {
 // iterations of all of a tile's segments still cover every slab exactly once).
 // With 8 waves each wave covers half of every slab's k-steps and holds a
 // partial sum of its quarter (see merge_k_halves).  Ends with a barrier, so the
-// LDS is free again on return.
+// LDS is free again on return.  `probe` (optional): a flag every lane loads
+// once the first iteration's operands have landed, into `probe_val` (complete
+// on return; unchanged when the segment is empty).
 template <int DT, int BL, int NS, int NW, int TM, bool RAGGED>
 __device__ __forceinline__ void mac_loop_impl(const KParams &p, char *lds, int m0, int n0, int k0, int k1,
-                                              int rot, AccT<TM> &acc, int *cov, uint32_t *raise) {
+                                              int rot, AccT<TM> &acc, int *cov, uint32_t *raise,
+                                              const uint32_t *probe = nullptr, uint32_t *probe_val = nullptr) {
     using ML = MainLoop<DT, BL, NS, NW, TM>;
     constexpr int DPI = ML::DPI;
     const int n = k1 - k0;
@@ -473,6 +476,9 @@ __device__ __forceinline__ void mac_loop_impl(const KParams &p, char *lds, int m
     // in every wave they are complete (the barrier covers all waves) and the
     // flag may rise.
     if (raise && threadIdx.x == 0) __hip_atomic_store(raise, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // issued after the prologue's loads, so no wait of the loop waits for it
+    // before those (completion is reported in issue order)
+    if (probe) *probe_val = load_flag_async(probe);
     ml.template read<0>(f[0]);
     int done = 0;                              // iterations issued to the matrix cores
     // One iteration i: its stage U = i % NS, its register buffer P = i % 2.
@@ -586,15 +592,19 @@ __device__ __forceinline__ void mac_loop_tall_impl(const KParams &p, char *lds, 
 
 // `raise` (optional): a flag to set to p.epoch once this workgroup's earlier
 // global stores are complete (the loop's first wait establishes that).
+// `probe` / `probe_val` (64- and 128-row tiles only): see mac_loop_impl.
 template <int DT, int BL, int NS, int NW, int TM = 128>
 __device__ __forceinline__ void mac_loop(const KParams &p, char *lds, int m0, int n0, int k0, int k1,
-                                         int rot, AccT<TM> &acc, int *cov, uint32_t *raise = nullptr) {
+                                         int rot, AccT<TM> &acc, int *cov, uint32_t *raise = nullptr,
+                                         const uint32_t *probe = nullptr, uint32_t *probe_val = nullptr) {
     if constexpr (TM == 256) {
         if (p.K % BK == 0) mac_loop_tall_impl<DT, BL, NS, NW, false>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise);
         else mac_loop_tall_impl<DT, BL, NS, NW, true>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise);
     } else {
-        if (p.K % BK == 0) mac_loop_impl<DT, BL, NS, NW, TM, false>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise);
-        else mac_loop_impl<DT, BL, NS, NW, TM, true>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise);
+        if (p.K % BK == 0)
+            mac_loop_impl<DT, BL, NS, NW, TM, false>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise, probe, probe_val);
+        else
+            mac_loop_impl<DT, BL, NS, NW, TM, true>(p, lds, m0, n0, k0, k1, rot, acc, cov, raise, probe, probe_val);
     }
 }
 
@@ -616,6 +626,12 @@ struct Tile {
     f32x16 v[R][2];                                 // [held row][32-column block]
     int i[R];                                       // which 32-row block of the wave's part
 };
+
+// The block row merge_k_halves leaves in slot r of a wave's Tile.
+template <int NW, int TM>
+__device__ __forceinline__ int held_row(int r) {
+    return NW == 8 ? Role<NW>().kh * Tile<NW, TM>::R + r : r;
+}
 
 template <int NW, int TM = 128>
 __device__ __forceinline__ Tile<NW, TM> merge_k_halves(const AccT<TM> &acc, char *lds) {
@@ -653,7 +669,7 @@ __device__ __forceinline__ Tile<NW, TM> merge_k_halves(const AccT<TM> &acc, char
                 }
                 t.v[r][j] = keep;
             }
-            t.i[r] = w.kh * R + r;
+            t.i[r] = held_row<NW, TM>(r);
         }
         __syncthreads();
     } else {
@@ -661,7 +677,7 @@ __device__ __forceinline__ Tile<NW, TM> merge_k_halves(const AccT<TM> &acc, char
         for (int r = 0; r < R; ++r) {
             t.v[r][0] = acc.v[r][0];
             t.v[r][1] = acc.v[r][1];
-            t.i[r] = r;
+            t.i[r] = held_row<NW, TM>(r);
         }
     }
     return t;
@@ -1164,20 +1180,29 @@ __device__ __forceinline__ void put_slot(float *slot, const Tile<NW, TM> &t, boo
             }
 }
 
-// t += slot over the held rows.  Every load is issued before the first add, so
-// the wave waits for the partial once.
+// A wave's share of a partial slot: the values of its held block rows.
 template <int NW, int TM>
-__device__ __forceinline__ void add_slot(const float *slot, Tile<NW, TM> &t) {
+struct SlotPart {
+    f32x4 x[Tile<NW, TM>::R][2][4];
+};
+
+// Loads of the wave's share of `slot` for the block rows held_row(0 .. R - 1),
+// all issued at once (the wave later waits for them once).
+template <int NW, int TM>
+__device__ __forceinline__ void load_slot(const float *slot, SlotPart<NW, TM> &s) {
     const Role<NW> w;
     const __amdgpu_buffer_rsrc_t r = span(slot, TM * BN * 4);
-    f32x4 x[Tile<NW, TM>::R][2][4];
 #pragma unroll
     for (int h = 0; h < Tile<NW, TM>::R; ++h)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4)
-                x[h][j][e4] = get4_coherent(r, slot_off<TM>(w.quad, 2 * t.i[h] + j, e4, w.lane));
+                s.x[h][j][e4] = get4_coherent(r, slot_off<TM>(w.quad, 2 * held_row<NW, TM>(h) + j, e4, w.lane));
+}
+
+template <int NW, int TM>
+__device__ __forceinline__ void add_part(Tile<NW, TM> &t, const SlotPart<NW, TM> &s) {
 #pragma unroll
     for (int h = 0; h < Tile<NW, TM>::R; ++h)
 #pragma unroll
@@ -1185,7 +1210,15 @@ __device__ __forceinline__ void add_slot(const float *slot, Tile<NW, TM> &t) {
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4)
 #pragma unroll
-                for (int y = 0; y < 4; ++y) t.v[h][j][4 * e4 + y] += x[h][j][e4][y];
+                for (int y = 0; y < 4; ++y) t.v[h][j][4 * e4 + y] += s.x[h][j][e4][y];
+}
+
+// t += slot over the held rows.
+template <int NW, int TM>
+__device__ __forceinline__ void add_slot(const float *slot, Tile<NW, TM> &t) {
+    SlotPart<NW, TM> s;
+    load_slot<NW, TM>(slot, s);
+    add_part(t, s);
 }
 
 // Poll `flag` (one thread) until it holds `epoch`, one untracked load per poll.
@@ -2082,6 +2115,10 @@ template <int DT, int BL, int NS, int NW, bool ATOMIC, bool EPI, int TM = 128>
 __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
     static_assert(!EPI || TM == 128, "the fused epilogue serves 128-row tiles");
     constexpr int SLOT = TM * BN;              // floats of one partial slot
+    // turnstile owners load their first peer's partial before the k-half merge
+    // (not in the epilogue build, whose C prefetch holds those registers, nor for
+    // 256-row tiles, whose accumulators fill them)
+    constexpr bool EARLY = !EPI && !ATOMIC && TM <= 128;
     __shared__ __attribute__((aligned(16))) char lds[lds_bytes<TM>(NS)];
     const WgClock clk(p);
     const int u = worker_of(p, p.units);
@@ -2115,19 +2152,35 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         const int role = k0 > 0 ? 2 : (k1 == ipt ? 0 : 1);
         const int owner = unit_of(tb, p.q, p.big);
         const int rot = (tb - unit_start(owner, p.q, p.big)) % ipt;
+        // a turnstile owner's first peer is always unit u + 1, which published
+        // its partial at the end of its first segment, usually long before this
+        // owner's segment ends
+        const bool turnstile_owner = role == 1 && !ATOMIC && p.merge != MERGE_TWO_PASS;
+        uint32_t first_flag = 0;
         AccT<TM> acc;
         zero_acc(acc);
+        // EARLY: every wave reads that flag during the mainloop; if it is already
+        // up there, the wave's loads of the peer's partial go out right after the
+        // loop and land during the k-half merge
         mac_loop<DT, BL, NS, NW, TM>(pv, lds, m0, n0, k0, k1, rot, acc, p.trace ? trace_cov(p, tile) : nullptr,
-                                     pending);
+                                     pending, EARLY && turnstile_owner ? p.flags + u + 1 : nullptr, &first_flag);
         pending = nullptr;
         // a segment that stores C: with the epilogue, its inputs are loaded now,
         // while the k-halves merge and any peers are waited for and added
         const bool stores_c = role == 0 || (role == 1 && !ATOMIC && p.merge != MERGE_TWO_PASS);
-        // a turnstile owner's first peer is always unit u + 1: its flag is read
-        // now, its latency hidden behind the k-half merge
-        const bool turnstile_owner = role == 1 && !ATOMIC && p.merge != MERGE_TWO_PASS;
-        uint32_t first_flag = 0;
-        if (turnstile_owner && threadIdx.x == 0) first_flag = load_flag_async(p.flags + u + 1);
+        // otherwise thread 0 reads the flag now, its latency hidden behind the
+        // k-half merge
+        if (!EARLY && turnstile_owner && threadIdx.x == 0) first_flag = load_flag_async(p.flags + u + 1);
+        SlotPart<NW, TM> early_part;
+        bool early = false;
+        if constexpr (EARLY) {
+            if (turnstile_owner) {
+                // the loop's last wait covered the flag's load; the same value in
+                // every lane of the wave
+                early = __builtin_amdgcn_readfirstlane(flag_value(first_flag)) == p.epoch;
+                if (early) load_slot<NW, TM>(p.part + (size_t)(u + 1) * SLOT, early_part);
+            }
+        }
         float pre_c[32], pre_b[2];
         if constexpr (EPI) {
             static_assert(NW == 8, "the prefetch assumes one 32-row block per wave");
@@ -2176,7 +2229,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
                     __hip_atomic_store(p.flags + v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
                 __syncthreads();
-                add_slot<NW>(p.part + (size_t)v * SLOT, t);
+                if (EARLY && v == u + 1 && early) add_part(t, early_part);
+                else add_slot<NW>(p.part + (size_t)v * SLOT, t);
                 trace_folded(p, tile, pos_fold++, v);
             }
             if constexpr (!EPI) store_final<NW, false>(pv, m0, n0, t);
