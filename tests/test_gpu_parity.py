@@ -118,6 +118,18 @@ def test_x1_hybrid_full_size(dg):
     assert_parity_full(c, w)
 
 
+def test_x3_decode_heuristic_full_size(dg):
+    # the book chapter's skinny case: a 128-row batch through a 4096-wide
+    # projection (32 tiles); the rule picks Split-K S = 8 over 256 workgroups,
+    # partials added by the second kernel; every element
+    w = WORKLOADS["x3_decode"]
+    p = dg.gemm_plan(w.M, w.N, w.K, dg.layout_word(w.b_layout, w.dtype), dg.GEMM_HEURISTIC, 0, 256)
+    assert (dg.DECISION_NAMES[p.decision], p.splits, p.tiles, p.two_pass) == ("SplitK", 8, 32, 1)
+    A, B, _, _ = oracle_full(w)
+    _, _, c = run(dg, w, A=A, B=B)
+    assert_parity_full(c, w)
+
+
 def test_c4_heuristic_dp(dg):
     # 8192^3 (1.1 Tflop of fp64): one random row inside every 128-row tile row,
     # plus every row that still holds the fill value

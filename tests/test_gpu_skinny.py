@@ -131,6 +131,20 @@ def test_skinny_decode_batch(dg):
         assert ok, f"{mode}: outside tolerance: worst ratio {worst} at {idx}"
 
 
+def test_skinny_hybrid_full_size(dg):
+    # 4096x4224x4096 on 64x128 tiles: 64 x 33 = 2112 tiles = 8 full waves + a
+    # 64-tile tail, so the rule keeps 7 waves data-parallel and runs Stream-K over
+    # the last 320 tiles, all in one persistent launch; every element
+    w = WORKLOADS["x1_hybrid"]
+    p = dg.gemm_plan(w.M, w.N, w.K, 0, dg.mode_word("heuristic", tile=SKINNY), 0, 256)
+    assert dg.DECISION_NAMES[p.decision] == "StreamK" and (p.dp_tiles, p.sk_tiles) == (1792, 320)
+    A, B, _, _ = oracle_full(w)
+    c = run_skinny(dg, w, A, B, "heuristic")
+    ok, worst, idx = check_full(c, w)
+    say(f"    worst err/bound = {worst:.3e} at {idx} (all {w.M * w.N} elements)")
+    assert ok, f"outside tolerance: worst ratio {worst} at {idx}"
+
+
 TRACE = [   # (M, N, K, mode, splits)
     (96, 512, 2048, "splitk", 8),
     (128, 4096, 4096, "splitk", 4),
