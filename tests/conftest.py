@@ -23,7 +23,7 @@ def _gpu_available() -> bool:
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are selected with -m gpu on a GPU machine.  If they are collected on
+    # GPU tests are selected with -m gpu on a machine with a GPU.  If they are collected on
     # a host without a GPU they fail loudly rather than being skipped silently,
     # unless the marker expression deselects them.
     pass
