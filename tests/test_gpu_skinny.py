@@ -280,3 +280,64 @@ def test_skinny_streamk_refuses_epilogue(dg):
     assert ei.value.status == dg.GEMM_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert torch.all(c == 7.0)
+
+
+@pytest.mark.parametrize("name,mode,splits,extra", [
+    ("c1_sk32", "streamk", 32, {"debug": "IN_LAUNCH"}),   # turnstile owners reading their peers' flags
+    ("c2a_m96_s8", "splitk", 8, {}),                      # row bands in the launch
+    ("c2b_m256_s2", "splitk", 2, {}),                     # second kernel
+])
+def test_skinny_graph_replays_match_eager(dg, name, mode, splits, extra):
+    w = WORKLOADS[name]
+    kw = _kw(dg, extra)
+    A, B = make_operands(w)
+    a, b = A.to(DEV), B.to(DEV)
+    c = torch.empty((w.M, w.N), dtype=torch.float32, device=DEV)
+    call = lambda out: dg.gemm_tensors(a, b, out, b_layout=w.b_layout, mode=mode, splits=splits, tile=SKINNY, **kw)
+    call(c)                      # eager: the workspace exists before the capture
+    torch.cuda.synchronize()
+    assert dg.gemm_sync_status() == 0
+    g = torch.cuda.CUDAGraph()
+    say(f"  capture skinny {name} {mode} S={splits} {extra}")
+    with torch.cuda.graph(g):
+        call(c)
+    for r in range(3):
+        A2, B2 = make_operands(w, seed=60 + r)
+        a.copy_(A2.to(DEV))
+        b.copy_(B2.to(DEV))
+        c.fill_(7.0)
+        say(f"  replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert dg.gemm_sync_status() == 0, dg.gemm_last_error()
+        ce = torch.full_like(c, 7.0)
+        call(ce)                 # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(c.view(torch.int32), ce.view(torch.int32)), f"replay {r} differs from eager"
+        ok, worst, idx = check_against_oracle(c, A2, B2, w)
+        assert ok, f"replay {r}: worst ratio {worst} at {idx}"
+    del g
+
+
+@pytest.mark.parametrize("mode,splits,extra", [("splitk", 4, {}), ("streamk", 40, {"debug": "IN_LAUNCH"}),
+                                               ("heuristic", 0, {})])
+def test_skinny_batched(dg, mode, splits, extra):
+    # three entries of 96x512x2048 (B [N,K]) at a padded stride of C
+    w = _w(96, 512, 2048, "nk", "bf16", name="skinny-batched")
+    batch, pad = 3, 20
+    As, Bs = zip(*(make_operands(w, seed=200 + e) for e in range(batch)))
+    A, B = torch.stack(As), torch.stack(Bs)
+    stride = (w.M * w.N + 3) // 4 * 4 + pad
+    full = torch.full((batch * stride + NGUARD,), GUARD, dtype=torch.float32, device=DEV)
+    c = torch.as_strided(full, (batch, w.M, w.N), (stride, w.N, 1))
+    c.fill_(7.0)
+    say(f"  skinny batched {mode} S={splits} {extra}")
+    dg.gemm_tensors(A.to(DEV), B.to(DEV), c, b_layout="nk", mode=mode, splits=splits, tile=SKINNY, **_kw(dg, extra))
+    assert dg.gemm_sync_status() == 0, dg.gemm_last_error()
+    mask = torch.ones_like(full, dtype=torch.bool)
+    for e in range(batch):
+        mask[e * stride: e * stride + w.M * w.N] = False
+    assert bool(torch.all(full[mask] == GUARD)), "a pad or the guard band was overwritten"
+    for e in range(batch):
+        ok, worst, idx = check_against_oracle(c[e], As[e], Bs[e], w)
+        assert ok, f"entry {e}: worst ratio {worst} at {idx}"
