@@ -24,11 +24,13 @@
  *                 partials added in split order (docc StreamK page, "MMA
  *                 fragment accumulators (aligned split)"): by a second kernel
  *                 ("serial" Split-K; chosen when all tiles x S workgroups fit on
- *                 the CUs at once and S < 8, or asked for with GEMM_TWO_PASS;
- *                 plan.two_pass says which), else in the same launch -- by all S
- *                 splits of each tile, each adding up its own 16-row bands once
- *                 every split has arrived, when the grid is resident at once, or
- *                 by the last arriver at the tile's counter.  All give the same bits.  GEMM_ATOMIC adds
+ *                 the CUs at once, unless S >= 8 and they fill at most half of
+ *                 them, or asked for with GEMM_TWO_PASS; plan.two_pass says
+ *                 which), else in the same launch -- by all S splits of each
+ *                 tile, each adding up its own row bands (an eighth of the tile
+ *                 each) once every split has arrived, when the grid is resident
+ *                 at once, or by the last arriver at the tile's counter.  All
+ *                 give the same bits.  GEMM_ATOMIC adds
  *                 every split into a zero-filled C instead ("parallel" Split-K;
  *                 CUTLASS optimisation guide, "Parallelized Reductions (Split-K)").
  *   GEMM_STREAMK  one persistent workgroup per unit; unit u owns a contiguous,
@@ -214,8 +216,9 @@ typedef struct gemm_plan_t {
     int32_t max_segments; /* most tile segments one worker can touch                        */
     int32_t max_fold;     /* most workers contributing to one tile                          */
     int32_t two_pass;     /* 1 when split tiles' partials are added by a second kernel (the
-                             plan picks it for Split-K grids that fit on the CUs at once
-                             with S < 8, and for Stream-K tiles with three or more peers) */
+                             plan picks it for Split-K grids that fit on the CUs at once,
+                             except S >= 8 on at most half of them, and for Stream-K
+                             tiles with three or more peers)                              */
     int64_t workers;      /* traced workers: units + dp_tiles, tiles * S, or tiles          */
     int64_t workspace_bytes; /* device workspace the call needs                             */
     int64_t trace_ints;   /* int32 elements of a debug trace buffer for this call           */
