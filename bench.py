@@ -192,7 +192,16 @@ def arm_result(w, call, rounds_us):
         "round_medians_us": [round(statistics.median(r), 3) for r in rounds_us],
         "tflops": round(w.flops / (med * 1e-6) / 1e12, 2),
         "pct_peak": round(100 * w.flops / (med * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        # the bytes every method must move (A and B read once, C written once) per
+        # the median time: the HBM view of the skinny, memory-side shapes
+        "compulsory_gbps": round(compulsory_bytes(w) / (med * 1e-6) / 1e9, 1),
+        "pct_hbm_peak": round(100 * compulsory_bytes(w) / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
     }
+
+
+def compulsory_bytes(w) -> int:
+    """A [M,K] and B read once (16-bit), C [M,N] fp32 written once, per batch entry."""
+    return w.batch * (w.M * w.K * 2 + w.K * w.N * 2 + w.M * w.N * 4)
 
 
 def paired_speedup(base_rounds, arm_rounds):
@@ -278,6 +287,7 @@ def shape_arms(dg, name, rounds):
         if "dp" in timed and arm != "dp":
             out[arm]["speedup_vs_dp"] = paired_speedup(timed["dp"], timed[arm])
         log(f"  {name:14s} {arm:20s} {out[arm]['median_us']:9.3f} us  {out[arm]['tflops']:8.2f} TFLOP/s"
+            f"  {out[arm]['compulsory_gbps']:7.1f} GB/s"
             + (f"  x{out[arm]['speedup_vs_dp']['median']} vs dp" if "speedup_vs_dp" in out[arm] else ""))
     return out
 

@@ -58,3 +58,13 @@ def test_profile_key_names_the_launch():
     P.bm = 256
     assert bench.profile_key(DG, P, w) == "gemm_streamk_bf16_kn_2048x2176x4096_256x128"
 
+
+
+def test_compulsory_bytes():
+    import bench
+    from workloads import WORKLOADS
+
+    w = WORKLOADS["c2a_m96_s8"]
+    assert bench.compulsory_bytes(w) == 96 * 2048 * 2 + 2048 * 512 * 2 + 96 * 512 * 4
+    x2 = WORKLOADS["x2_batched"]
+    assert bench.compulsory_bytes(x2) == 5 * (1024 * 2048 * 2 * 2 + 1024 * 1024 * 4)
