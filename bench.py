@@ -289,6 +289,19 @@ def shape_arms(dg, name, rounds):
         log(f"  {name:14s} {arm:20s} {out[arm]['median_us']:9.3f} us  {out[arm]['tflops']:8.2f} TFLOP/s"
             f"  {out[arm]['compulsory_gbps']:7.1f} GB/s"
             + (f"  x{out[arm]['speedup_vs_dp']['median']} vs dp" if "speedup_vs_dp" in out[arm] else ""))
+    if pack > 1 and name[:2] in ("c1", "c2", "x3"):
+        # the small shapes also at pack 1 (one call per event pair, the Metal
+        # note's other pack size): each call then also carries the event markers'
+        # and the launch's own latency
+        timed1 = time_arms(calls, rounds, samples, 1)
+        out["protocol"]["also_pack_1"] = True
+        for arm, call in calls.items():
+            r = arm_result(w, call, timed1[arm])
+            out[arm]["pack1"] = {k: r[k] for k in ("median_us", "p10_us", "p90_us", "min_us")}
+            if "dp" in timed1 and arm != "dp":
+                out[arm]["pack1"]["speedup_vs_dp"] = paired_speedup(timed1["dp"], timed1[arm])
+            log(f"  {name:14s} {arm:20s} {r['median_us']:9.3f} us  (pack 1)"
+                + (f"  x{out[arm]['pack1']['speedup_vs_dp']['median']} vs dp" if arm != "dp" and "dp" in timed1 else ""))
     return out
 
 
