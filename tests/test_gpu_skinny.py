@@ -118,6 +118,18 @@ def test_skinny_config_shapes_full(dg, name, mode, splits, extra):
         assert torch.all(c[0] == 0.0), "A row 0 is zero, so C row 0 must be exactly zero"
 
 
+@pytest.mark.parametrize("atomic", [False, True])
+def test_skinny_longk_fp16_full(dg, atomic):
+    # 1536^2 x 16384 fp16 on 64x128 tiles (288 tiles x 256 iterations over 256
+    # units), both fixup modes; every element
+    w = WORKLOADS["c5_longk_fp16"]
+    A, B, _, _ = oracle_full(w)
+    c = run_skinny(dg, w, A, B, "streamk", 0, atomic=atomic)
+    ok, worst, idx = check_full(c, w)
+    say(f"    worst err/bound = {worst:.3e} at {idx} (all {w.M * w.N} elements)")
+    assert ok, f"outside tolerance: worst ratio {worst} at {idx}"
+
+
 def test_skinny_decode_batch(dg):
     # the book chapter's skinny case: a 128-row batch through a 4096-wide
     # projection (64 tiles of 64 x 128); the rule's choice and Split-K S = 4
