@@ -244,15 +244,16 @@ def test_small_shapes_all_modes(dg, shape, mode, splits, atomic):
     assert_parity(c, A, B, w)
 
 
-@pytest.mark.parametrize("shape", SMALL[:5], ids=lambda s: "x".join(map(str, s[:3])) + f"-{s[3]}-{s[4]}")
-@pytest.mark.parametrize("splits", [2, 3, 5, 8, 10])
+# (shape, S) pairs of SMALL[:5] and S in 2, 3, 5, 8, 10 where S divides the k-iterations
+BAND_CASES = [(shape, S) for shape in SMALL[:5] for S in (2, 3, 5, 8, 10) if -(-shape[2] // 64) % S == 0]
+
+
+@pytest.mark.parametrize("shape,splits", BAND_CASES,
+                         ids=["x".join(map(str, c[0][:3])) + f"-{c[0][3]}-{c[0][4]}-s{c[1]}" for c in BAND_CASES])
 def test_small_shapes_splitk_row_bands(dg, shape, splits):
     # the in-launch row-band merge at split factors from 2 to 10 (the last arriver
     # where N is not a multiple of 4), against the oracle and the second kernel's bits
     M, N, K, layout, dtype = shape
-    ipt = -(-K // 64)
-    if ipt % splits:
-        pytest.skip(f"{splits} does not divide {ipt} k-iterations")
     dist = dict(dist="uniform", low=-1.0, high=1.0) if dtype == "bf16" else dict(dist="uniform", low=-0.5, high=0.5)
     w = WORKLOADS["c1_sk32"].with_(name="bands", M=M, N=N, K=K, b_layout=layout, dtype=dtype, **dist)
     A, B, c = run(dg, w, mode="splitk", splits=splits, debug=dg.GEMM_DEBUG_SPLITK_BANDS)

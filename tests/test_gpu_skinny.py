@@ -83,13 +83,16 @@ def _fits(M, N, K, mode, splits):
     return mode != "splitk" or (ipt % splits == 0)
 
 
-@pytest.mark.parametrize("path", PATHS, ids=lambda p: f"{p[0]}{p[1]}-" + "-".join(f"{k}{v}" for k, v in p[2].items()))
-@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s[:3])) + f"-{s[3]}-{s[4]}")
+# every (shape, path) pair where Split-K's S divides the k-iterations
+SMALL_CASES = [(shape, path) for shape in SMALL for path in PATHS if _fits(*shape[:3], path[0], path[1])]
+
+
+@pytest.mark.parametrize("shape,path", SMALL_CASES,
+                         ids=["x".join(map(str, c[0][:3])) + f"-{c[0][3]}-{c[0][4]}-{c[1][0]}{c[1][1]}-"
+                              + "-".join(f"{k}{v}" for k, v in c[1][2].items()) for c in SMALL_CASES])
 def test_skinny_small_shapes(dg, shape, path):
     M, N, K, layout, dtype = shape
     mode, splits, extra = path
-    if not _fits(M, N, K, mode, splits):
-        pytest.skip("splits must divide the k-iterations")
     w = _w(M, N, K, layout, dtype)
     A, B = make_operands(w)
     c = run_skinny(dg, w, A, B, mode, splits, **_kw(dg, extra))
