@@ -75,6 +75,8 @@ def test_graph_replays_match_eager(dg, case):
     del g
 
 
+# the refused call enqueues nothing, so torch reports the captured graph as empty
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")
 def test_capture_refuses_workspace_growth(dg):
     # with no library workspace yet, a captured call would have to allocate one:
     # it is refused (GEMM_ERR_WORKSPACE), nothing is captured, and the same call
