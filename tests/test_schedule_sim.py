@@ -188,7 +188,7 @@ def test_big_units_first():
 
 # -- brute force: the tile grid covers every output element once ------------------
 def test_tile_grid_covers_every_element():
-    for bm, bn in ((128, 128), (64, 64)):
+    for bm, bn in ((128, 128), (64, 64), (64, 128), (256, 128)):
         for M in list(range(1, 300, 13)) + [127, 128, 129, 256, 257]:
             for N in (1, 63, 64, 65, 200, 384):
                 tm, tn = sch.tile_grid(M, N, bm, bn)
