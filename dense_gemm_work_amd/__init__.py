@@ -119,6 +119,14 @@ class GemmArgs(ctypes.Structure):
     ]
 
 
+class GemmGroup(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64)]
+
+
+GEMM_MAX_GROUPS = 64
+
+
 def library_path() -> Path:
     return _LIB_PATH
 
@@ -150,6 +158,10 @@ def _load() -> ctypes.CDLL:
     lib.gemm_workspace_size.argtypes = [i64, i64, i64, i64, u32, u32, i32, i32]
     lib.gemm_plan_batched.restype = ctypes.c_int
     lib.gemm_plan_batched.argtypes = [i64, i64, i64, i64, u32, u32, i32, i32, ctypes.POINTER(GemmPlan)]
+    lib.gemm_grouped.restype = ctypes.c_int
+    lib.gemm_grouped.argtypes = [ctypes.POINTER(GemmArgs), ctypes.POINTER(GemmGroup), i32]
+    lib.gemm_plan_grouped.restype = ctypes.c_int
+    lib.gemm_plan_grouped.argtypes = [ctypes.POINTER(GemmGroup), i32, i64, u32, u32, i32, i32, ctypes.POINTER(GemmPlan)]
     lib.gemm_unit_range.restype = ctypes.c_int
     lib.gemm_unit_range.argtypes = [ctypes.POINTER(GemmPlan), i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.gemm_set_stream.restype = ctypes.c_int
@@ -207,6 +219,28 @@ def gemm_plan_batched(M: int, N: int, K: int, batch: int, layout: int, mode: int
 def gemm_workspace_size(M: int, N: int, K: int, layout: int, mode: int, splits: int, num_cus: int,
                         batch: int = 1) -> int:
     return _check(int(_lib.gemm_workspace_size(M, N, K, batch, layout, mode, splits, num_cus)))
+
+
+def _group_array(groups):
+    """A ctypes array of GemmGroup from (A, B, C, M, N) tuples or GemmGroup items."""
+    arr = (GemmGroup * max(len(groups), 1))()
+    for i, g in enumerate(groups):
+        arr[i] = g if isinstance(g, GemmGroup) else GemmGroup(*g)
+    return arr
+
+
+def gemm_grouped(common: GemmArgs, groups) -> int:
+    """gemm_grouped(): ``groups`` a sequence of (A, B, C, M, N) (device addresses)."""
+    arr = _group_array(groups)
+    return _lib.gemm_grouped(ctypes.byref(common), arr, len(groups))
+
+
+def gemm_plan_grouped(shapes, K: int, layout: int, mode: int, splits: int, num_cus: int) -> GemmPlan:
+    """gemm_plan_grouped() for problems of the given (M, N) shapes."""
+    arr = _group_array([(None, None, None, M, N) for M, N in shapes])
+    p = GemmPlan()
+    _check(_lib.gemm_plan_grouped(arr, len(shapes), K, layout, mode, splits, num_cus, ctypes.byref(p)))
+    return p
 
 
 def gemm_unit_range(plan: GemmPlan, unit: int):
@@ -369,6 +403,64 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
             args.bias = bias.data_ptr()
         args.epilogue = word
         _check(gemm_ex_noalloc(args) if noalloc else gemm_ex(args))
+
+
+def gemm_grouped_tensors(problems, b_layout: str = "kn", mode: str = "heuristic", splits: int = 0,
+                         atomic: bool = False, two_pass: bool = False, num_cus: int = 0, trace=None,
+                         workspace=None, spin_limit: int = 0, debug: int = 0, timing=None, unit_perm=None,
+                         stream=None, tile: str = "128x128") -> None:
+    """``c_g = a_g . b_g`` (b [K,N]) or ``a_g . b_g^T`` (b [N,K]) for every (a_g, b_g, c_g)
+    in ``problems`` as one grouped call: 2-D contiguous tensors on one device,
+    one K and one 16-bit dtype for all, each problem its own M and N."""
+    import torch
+
+    if not 1 <= len(problems) <= GEMM_MAX_GROUPS:
+        raise ValueError(f"a grouped call takes 1..{GEMM_MAX_GROUPS} problems")
+    a0 = problems[0][0]
+    K = a0.shape[-1]
+    dtype = a0.dtype
+    if dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("a and b must be bf16 or fp16")
+    groups = []
+    for i, (a, b, c) in enumerate(problems):
+        if a.dim() != 2 or b.dim() != 2 or c.dim() != 2:
+            raise ValueError(f"problem {i}: a, b and c must be 2-D")
+        if a.dtype != dtype or b.dtype != dtype or c.dtype != torch.float32:
+            raise TypeError(f"problem {i}: a and b of the first problem's dtype, c fp32")
+        if not (a.is_cuda and b.is_cuda and c.is_cuda and a.device == b.device == c.device == a0.device):
+            raise ValueError(f"problem {i}: tensors must be on the first problem's device")
+        if not (a.is_contiguous() and b.is_contiguous() and c.is_contiguous()):
+            raise ValueError(f"problem {i}: tensors must be contiguous")
+        M = a.shape[0]
+        if a.shape[1] != K:
+            raise ValueError(f"problem {i}: K = {a.shape[1]}, the call's K is {K}")
+        N = b.shape[1] if b_layout == "kn" else b.shape[0]
+        if (b_layout == "kn" and b.shape[0] != K) or (b_layout == "nk" and b.shape[1] != K):
+            raise ValueError(f"problem {i}: b does not match K = {K}")
+        if tuple(c.shape) != (M, N):
+            raise ValueError(f"problem {i}: c must be [{M}, {N}]")
+        groups.append((a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N))
+    args = GemmArgs()
+    args.K = K
+    args.layout = layout_word(b_layout, "bf16" if dtype == torch.bfloat16 else "fp16")
+    args.mode = mode_word(mode, atomic, two_pass, tile)
+    args.splits = splits
+    args.num_cus = num_cus
+    with torch.cuda.device(a0.device):
+        s = stream if stream is not None else torch.cuda.current_stream(a0.device)
+        args.stream = s.cuda_stream
+        if trace is not None:
+            args.trace, args.trace_ints = trace.data_ptr(), trace.numel()
+        if timing is not None:
+            args.timing = timing.data_ptr()
+        if unit_perm is not None:
+            args.unit_perm = unit_perm.data_ptr()
+        if workspace is not None:
+            args.workspace = workspace.data_ptr()
+            args.workspace_bytes = workspace.numel() * workspace.element_size()
+        args.spin_limit = spin_limit
+        args.debug = debug
+        _check(gemm_grouped(args, groups))
 
 
 def matmul(a, b, b_layout: str = "kn", out=None, alpha: Optional[float] = None, beta: Optional[float] = None,

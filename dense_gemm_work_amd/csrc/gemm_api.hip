@@ -81,7 +81,7 @@ struct DeviceState {
     int64_t cap_data = 0;
     std::vector<void *> retired;   // outgrown data blocks, freed by gemm_release()
     std::vector<uint32_t *> retired_control;   // outgrown control blocks (status word first)
-    int bpc[2][2][5][3] = {};      // resident workgroups per CU [dtype][B layout][kind][tile shape], 0 = not queried
+    int bpc[2][2][5][3][2] = {};   // resident workgroups per CU [dtype][B layout][kind][tile shape][grouped], 0 = not queried
 };
 
 std::mutex g_mu;
@@ -265,24 +265,56 @@ __global__ void put_trace_header(int *t, TraceHeader h) {
     if (threadIdx.x < 8) t[threadIdx.x] = h.v[threadIdx.x];
 }
 
+// The problems of a grouped call (no HIP call): the common arguments carry no
+// problem of their own, every problem's operands are aligned and C does not
+// overlap its A or B.
+int check_groups(const gemm_args_t &a, const gemm_group_t *groups, int32_t count) {
+    if (a.A || a.B || a.C || a.M || a.N || a.bias || a.batch > 1)
+        return fail(GEMM_ERR_INVALID, "a grouped call's common arguments must leave A, B, C, M, N, bias and batch unset");
+    if (a.epilogue) return fail(GEMM_ERR_UNSUPPORTED, "grouped calls have no fused epilogue");
+    for (int32_t g = 0; g < count; ++g) {
+        const gemm_group_t &x = groups[g];
+        if (x.M == 0 || x.N == 0) continue;
+        if (!x.C || (a.K > 0 && (!x.A || !x.B)))
+            return fail(GEMM_ERR_INVALID, "problem " + std::to_string(g) + ": A, B and C must be non-null");
+        if ((reinterpret_cast<uintptr_t>(x.A) | reinterpret_cast<uintptr_t>(x.B) | reinterpret_cast<uintptr_t>(x.C)) & 15)
+            return fail(GEMM_ERR_UNSUPPORTED, "problem " + std::to_string(g) + ": A, B and C must be 16-byte aligned");
+        if (overlaps(x.C, x.M * x.N * 4, x.A, x.M * a.K * 2) || overlaps(x.C, x.M * x.N * 4, x.B, a.K * x.N * 2))
+            return fail(GEMM_ERR_INVALID, "problem " + std::to_string(g) + ": C must not overlap A or B");
+    }
+    if (a.trace && a.trace_ints <= 0) return fail(GEMM_ERR_INVALID, "trace_ints must be > 0");
+    if (a.workspace && reinterpret_cast<uintptr_t>(a.workspace) & 255)
+        return fail(GEMM_ERR_INVALID, "a caller workspace must be 256-byte aligned");
+    return GEMM_OK;
+}
+
 // One call.  noalloc: the workspace is this device's `scratch` array and no
-// device memory is allocated (gemm_ex_noalloc).
-int run(const gemm_args_t &a, bool noalloc = false) {
+// device memory is allocated (gemm_ex_noalloc).  groups / ngroups: a grouped
+// call (gemm_grouped), whose problems replace a's A, B, C, M and N.
+int run(const gemm_args_t &a, bool noalloc = false, const gemm_group_t *groups = nullptr, int32_t ngroups = 0) {
     g_err.clear();
     gemm_plan_t p;
     const char *why = "";
     // plan first with a placeholder CU count so argument errors surface before any HIP call
     const int64_t batch = a.batch > 1 ? a.batch : 1;
-    int rc = dgw::make_plan(a.M, a.N, a.K, batch, a.layout, a.mode, a.splits,
-                            a.num_cus > 0 ? a.num_cus : 256, &p, &why);
+    auto plan_for = [&](int32_t cus) {
+        return groups ? dgw::make_plan_grouped(groups, ngroups, a.K, a.layout, a.mode, a.splits, cus, &p, &why)
+                      : dgw::make_plan(a.M, a.N, a.K, batch, a.layout, a.mode, a.splits, cus, &p, &why);
+    };
+    int rc = plan_for(a.num_cus > 0 ? a.num_cus : 256);
     if (rc != GEMM_OK) return fail(rc, why);
     if (a.num_cus < 0) return fail(GEMM_ERR_INVALID, "num_cus must be >= 0");
     if ((a.debug & ~(GEMM_DEBUG_NO_PUBLISH | GEMM_DEBUG_IN_LAUNCH | GEMM_DEBUG_TILE_DP | GEMM_DEBUG_HYBRID_SPLIT |
                     GEMM_DEBUG_ZERO_PARTIAL | GEMM_DEBUG_SPLITK_BANDS)) != 0)
         return fail(GEMM_ERR_INVALID, "unknown debug bits");
     if ((rc = check_epilogue(a)) != GEMM_OK) return rc;
-    if (a.M == 0 || a.N == 0) return GEMM_OK;
-    if ((rc = check_operands(a)) != GEMM_OK) return rc;
+    if (groups) {
+        if ((rc = check_groups(a, groups, ngroups)) != GEMM_OK) return rc;
+        if (p.tiles == 0) return GEMM_OK;
+    } else {
+        if (a.M == 0 || a.N == 0) return GEMM_OK;
+        if ((rc = check_operands(a)) != GEMM_OK) return rc;
+    }
     if (noalloc) {
         if (a.workspace) return fail(GEMM_ERR_INVALID, "gemm_ex_noalloc uses its own scratch: workspace must be NULL");
         // with an explicit CU count this plan is final: refuse before any HIP call
@@ -298,8 +330,7 @@ int run(const gemm_args_t &a, bool noalloc = false) {
     DeviceState *ds = nullptr;
     if ((rc = device_state(dev, &ds)) != GEMM_OK) return rc;
     const int ncu = a.num_cus > 0 ? a.num_cus : ds->num_cus;
-    if ((rc = dgw::make_plan(a.M, a.N, a.K, batch, a.layout, a.mode, a.splits, ncu, &p, &why)) != GEMM_OK)
-        return fail(rc, why);
+    if ((rc = plan_for(ncu)) != GEMM_OK) return fail(rc, why);
     if (noalloc && p.workspace_bytes > (int64_t)GEMM_NOALLOC_MAX_BYTES) return scratch_too_small(p);
 
     const int dtype = (a.layout & 0xF0u) == GEMM_FP16 ? 1 : 0;
@@ -311,6 +342,13 @@ int run(const gemm_args_t &a, bool noalloc = false) {
     if (shape == 2 && a.epilogue != 0 && p.decision == GEMM_STREAMK)
         return fail(GEMM_ERR_UNSUPPORTED, "GEMM_TILE_64x128 has no fused epilogue with Stream-K");
 
+    if (a.K == 0 && groups) {   // the empty sums: every problem's C := 0
+        for (int32_t g = 0; g < ngroups; ++g)
+            if (groups[g].M > 0 && groups[g].N > 0 &&
+                (e = dgw::launch_zero(groups[g].C, groups[g].M * groups[g].N, stream)) != hipSuccess)
+                return fail_hip(e, "zero C");
+        return GEMM_OK;
+    }
     if (a.K == 0) {  // the empty sum
         if (a.epilogue == 0) {
             if ((e = zero_c(a, batch, stream)) != hipSuccess) return fail_hip(e, "zero C");
@@ -335,9 +373,9 @@ int run(const gemm_args_t &a, bool noalloc = false) {
                                                   : dgw::K_SK;
     if (p.decision == GEMM_STREAMK) {
         // every unit must be resident at once: owners wait for higher units
-        int &bpc = ds->bpc[dtype][blayout][kmode][shape];
+        int &bpc = ds->bpc[dtype][blayout][kmode][shape][ngroups > 0];
         if (bpc == 0) {
-            if ((e = dgw::blocks_per_cu(dtype, blayout, kmode, p.bm, &bpc)) != hipSuccess)
+            if ((e = dgw::blocks_per_cu(dtype, blayout, kmode, p.bm, ngroups > 0, &bpc)) != hipSuccess)
                 return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
         }
         if (p.sk_units > (int64_t)bpc * ds->num_cus)
@@ -382,6 +420,39 @@ int run(const gemm_args_t &a, bool noalloc = false) {
         part = static_cast<float *>(ds->data);
     }
 
+    // a grouped call's problem table, at the end of the data region: nonempty
+    // problems in call order, their first tile ids and the offsets of their
+    // Split-K partials [S][M_g][N_g]
+    dgw::GroupDesc *table = nullptr;
+    int32_t nonempty = 0;
+    bool all_n4 = (a.N & 3) == 0;
+    if (groups) {
+        static_assert(sizeof(dgw::GroupTable) <= 3200, "the table travels as kernel arguments");
+        dgw::GroupTable t;
+        std::memset(&t, 0, sizeof t);
+        const int64_t bm = p.bm, splits_kept = p.decision == GEMM_SPLITK && !p.atomic ? p.splits : 0;
+        int64_t tile0 = 0, part_off = 0;
+        for (int32_t g = 0; g < ngroups; ++g) {
+            const gemm_group_t &x = groups[g];
+            if (x.M == 0 || x.N == 0) continue;
+            dgw::GroupDesc &d = t.g[nonempty++];
+            d.A = static_cast<const uint16_t *>(x.A);
+            d.B = static_cast<const uint16_t *>(x.B);
+            d.C = x.C;
+            d.part = part_off;
+            d.M = (int)x.M;
+            d.N = (int)x.N;
+            d.tile0 = (int)tile0;
+            tile0 += (x.M + bm - 1) / bm * ((x.N + GEMM_BN - 1) / GEMM_BN);
+            part_off += splits_kept * x.M * x.N;
+            all_n4 = all_n4 && (x.N & 3) == 0;
+        }
+        table = reinterpret_cast<dgw::GroupDesc *>(reinterpret_cast<char *>(part) + data_bytes -
+                                                   dgw::group_table_bytes(ngroups));
+        if ((e = dgw::launch_put_groups(table, t, nonempty, stream)) != hipSuccess)
+            return fail_hip(e, "write the problem table");
+    }
+
     KParams kp;
     std::memset(&kp, 0, sizeof kp);
     kp.A = static_cast<const uint16_t *>(a.A);
@@ -390,6 +461,8 @@ int run(const gemm_args_t &a, bool noalloc = false) {
     kp.M = (int)a.M;
     kp.N = (int)a.N;
     kp.K = (int)a.K;
+    kp.groups = table;
+    kp.ngroups = nonempty;
     kp.tm = p.bm;
     kp.tiles_m = (int)p.tiles_m;
     kp.tiles_n = (int)p.tiles_n;
@@ -418,6 +491,13 @@ int run(const gemm_args_t &a, bool noalloc = false) {
     const bool atomic_merge = p.atomic && p.decision != GEMM_DP;
     set_epilogue(a, atomic_merge, kp);
     auto prepare_atomic_c = [&]() -> int {
+        if (groups) {   // no epilogue in a grouped call: every problem's C := 0
+            for (int32_t g = 0; g < ngroups; ++g)
+                if (groups[g].M > 0 && groups[g].N > 0 &&
+                    (e = dgw::launch_zero(groups[g].C, groups[g].M * groups[g].N, stream)) != hipSuccess)
+                    return fail_hip(e, "zero C");
+            return GEMM_OK;
+        }
         if (kp.epi == dgw::EPI_PLAIN) {
             if ((e = zero_c(a, batch, stream)) != hipSuccess) return fail_hip(e, "zero C");
         } else if ((e = dgw::launch_epilogue_pass(kp, dgw::EPASS_PRE, stream)) != hipSuccess) {
@@ -448,12 +528,12 @@ int run(const gemm_args_t &a, bool noalloc = false) {
         // a group takes about 4 / 1.4 tile times (measured on 8192^3: 1207 us
         // with one tile per workgroup, 840 us with groups), so with G groups and
         // T tiles on C CUs groups win when ceil(G / C) * 4 < ceil(T / C) * 1.4
-        const int64_t ngroups = batch * ((p.tiles_m + 1) / 2) * ((p.tiles_n + 1) / 2);
-        const int64_t gwaves = (ngroups + ncu - 1) / ncu, twaves = (p.tiles + ncu - 1) / ncu;
-        const bool groups = shape == 0 && gwaves * 40 < twaves * 14 && !(a.debug & GEMM_DEBUG_TILE_DP);
-        if (groups) {
-            kp.ntiles = (int)ngroups;
-            if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_DP_GROUP, (int)ngroups, kp, stream)) != hipSuccess)
+        const int64_t quads = batch * ((p.tiles_m + 1) / 2) * ((p.tiles_n + 1) / 2);
+        const int64_t gwaves = (quads + ncu - 1) / ncu, twaves = (p.tiles + ncu - 1) / ncu;
+        const bool tile_groups = shape == 0 && !groups && gwaves * 40 < twaves * 14 && !(a.debug & GEMM_DEBUG_TILE_DP);
+        if (tile_groups) {
+            kp.ntiles = (int)quads;
+            if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_DP_GROUP, (int)quads, kp, stream)) != hipSuccess)
                 return fail_hip(e, "launch DP tile-group kernel");
         } else if ((e = dgw::launch_gemm(dtype, blayout, dgw::K_DP, (int)p.tiles, kp, stream)) != hipSuccess) {
             return fail_hip(e, "launch DP kernel");
@@ -468,9 +548,10 @@ int run(const gemm_args_t &a, bool noalloc = false) {
         // S splits of a tile add up its row bands (the waits end); otherwise the
         // last arriver at the tile's counter adds up the whole tile.
         // GEMM_DEBUG_IN_LAUNCH keeps the last arriver.
-        if (kp.merge == dgw::MERGE_IN_LAUNCH && p.splits > 1 && (a.N & 3) == 0 && !(a.debug & GEMM_DEBUG_IN_LAUNCH)) {
-            int &bpc = ds->bpc[dtype][blayout][dgw::K_SPLITK][shape];
-            if (bpc == 0 && (e = dgw::blocks_per_cu(dtype, blayout, dgw::K_SPLITK, p.bm, &bpc)) != hipSuccess)
+        if (kp.merge == dgw::MERGE_IN_LAUNCH && p.splits > 1 && all_n4 && !(a.debug & GEMM_DEBUG_IN_LAUNCH)) {
+            int &bpc = ds->bpc[dtype][blayout][dgw::K_SPLITK][shape][ngroups > 0];
+            if (bpc == 0 &&
+                (e = dgw::blocks_per_cu(dtype, blayout, dgw::K_SPLITK, p.bm, ngroups > 0, &bpc)) != hipSuccess)
                 return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
             if (p.tiles * p.splits <= (int64_t)bpc * ds->num_cus) kp.merge = dgw::MERGE_BANDS;
         }
@@ -549,6 +630,11 @@ int gemm(const void *A, const void *B, float *C, int64_t M, int64_t N, int64_t K
 int gemm_ex(const gemm_args_t *args) {
     if (!args) return fail(GEMM_ERR_INVALID, "args is null");
     return run(*args);
+}
+
+int gemm_grouped(const gemm_args_t *common, const gemm_group_t *groups, int32_t count) {
+    if (!common || !groups) return fail(GEMM_ERR_INVALID, "common arguments and groups must be non-null");
+    return run(*common, false, groups, count);
 }
 
 int gemm_ex_noalloc(const gemm_args_t *args) {

@@ -74,8 +74,6 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = GEMM_BK;
-constexpr int SLAB = BM * BK;                 // 16-bit values per operand slab (A and B alike)
-constexpr int STAGE_BYTES = 2 * SLAB * 2;     // A slab then B slab: 32 KiB
 
 // Accumulators of one wave: its (TM / 2) x 64 part of a TM x 128 tile, as
 // [i: 32-row block][j: 32-column block].
@@ -733,9 +731,34 @@ __device__ __forceinline__ KParams batch_entry(const KParams &p, int b) {
     return q;
 }
 
-// Tiles are numbered batch after batch: the view of global tile `tile`'s batch
-// entry and the tile's origin in it.
+// Grouped call: the problem holding global tile `tile` (the nonempty problems'
+// first tile ids ascend; lane l compares problem l's, so one vector load and a
+// ballot find it), and the view of it.
+__device__ __forceinline__ KParams group_view(const KParams &p, int tile, int &m0, int &n0) {
+    const int lane = threadIdx.x & 63;
+    const int t0 = lane < p.ngroups ? p.groups[lane].tile0 : 0x7fffffff;
+    const uint64_t below = __ballot(t0 <= tile);
+    const int g = __builtin_amdgcn_readfirstlane(63 - __builtin_clzll(below));
+    const GroupDesc &d = p.groups[g];
+    KParams q = p;
+    q.A = d.A;
+    q.B = d.B;
+    q.C = d.C;
+    q.part = p.part ? p.part + d.part : nullptr;
+    q.M = d.M;
+    q.N = d.N;
+    q.tiles_m = (d.M + p.tm - 1) / p.tm;
+    q.tiles_n = (d.N + BN - 1) / BN;
+    tile_origin(q, tile - d.tile0, m0, n0);
+    return q;
+}
+
+// Tiles are numbered batch after batch (or problem after problem in a grouped
+// call, the GRP builds): the view of global tile `tile`'s batch entry and the
+// tile's origin in it.
+template <bool GRP = false>
 __device__ __forceinline__ KParams tile_view(const KParams &p, int tile, int &m0, int &n0) {
+    if constexpr (GRP) return group_view(p, tile, m0, n0);
     if (p.batch <= 1) {
         tile_origin(p, tile, m0, n0);
         return p;
@@ -1324,14 +1347,14 @@ struct WgClock {
 // ---------------------------------------------------------------------------
 // Data-parallel: one workgroup per tile of [tile_base, tile_base + ntiles).
 // ---------------------------------------------------------------------------
-template <int DT, int BL, int NS, int NW, int TM = 128>
+template <int DT, int BL, int NS, int NW, int TM = 128, bool GRP = false>
 __global__ __launch_bounds__(64 * NW) void gemm_dp(KParams p) {
     __shared__ __attribute__((aligned(16))) char lds[lds_bytes<TM>(NS)];
     const WgClock clk(p);
     const int w = worker_of(p, p.ntiles);
     const int tile = p.tile_base + w;
     int m0, n0;
-    const KParams q = tile_view(p, tile, m0, n0);
+    const KParams q = tile_view<GRP>(p, tile, m0, n0);
     AccT<TM> acc;
     zero_acc(acc);
     mac_loop<DT, BL, NS, NW, TM>(q, lds, m0, n0, 0, p.ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
@@ -1706,7 +1729,7 @@ __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
 // ---------------------------------------------------------------------------
 // Split-K: worker w = tile * S + s covers k-iterations [s P / S, (s+1) P / S).
 // ---------------------------------------------------------------------------
-template <int DT, int BL, int NS, int NW, int TM = 128>
+template <int DT, int BL, int NS, int NW, int TM = 128, bool GRP = false>
 __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p0) {
     constexpr int NT = Role<NW>::NT, QPT = TM * BN / 4 / NT;
     // the stages, reused to stage the fp32 tile (TM x 128) after the loop
@@ -1719,7 +1742,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p0) {
     const int tile = w / S, s = w % S;
     const int k0 = (int)((int64_t)s * p0.ipt / S), k1 = (int)((int64_t)(s + 1) * p0.ipt / S);
     int m0, n0;
-    const KParams p = tile_view(p0, tile, m0, n0);   // the tile's batch entry
+    const KParams p = tile_view<GRP>(p0, tile, m0, n0);   // the tile's batch entry
     AccT<TM> acc;
     zero_acc(acc);
     mac_loop<DT, BL, NS, NW, TM>(p, lds, m0, n0, k0, k1, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
@@ -1978,13 +2001,13 @@ constexpr int RED_THREADS = 256;
 // workgroups per tile of tm rows: 16 for 128-row tiles
 __host__ __device__ constexpr int red_blocks_per_tile(int tm) { return tm * BN / 4 / RED_THREADS; }
 
-template <bool EPI>
+template <bool EPI, bool GRP = false>
 __global__ __launch_bounds__(RED_THREADS) void splitk_reduce(KParams p0) {
     const int bpt = red_blocks_per_tile(p0.tm);
     const int tile = blockIdx.x / bpt;
     const int q = (blockIdx.x % bpt) * RED_THREADS + threadIdx.x;   // quad within the tile
     int m0, n0;
-    const KParams p = tile_view(p0, tile, m0, n0);   // the tile's batch entry
+    const KParams p = tile_view<GRP>(p0, tile, m0, n0);   // the tile's batch entry
     const int r = q >> 5, c = (q & 31) * 4;
     const int S = p.splits;
     if (threadIdx.x == 0 && blockIdx.x % bpt == 0)
@@ -2037,7 +2060,7 @@ __global__ __launch_bounds__(RED_THREADS) void splitk_reduce(KParams p0) {
 // tm / 8 workgroups of 256 threads per Stream-K tile; tiles that one unit
 // computed whole were stored by it and are skipped.
 // ---------------------------------------------------------------------------
-template <bool EPI>
+template <bool EPI, bool GRP = false>
 __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
     const int bpt = red_blocks_per_tile(p.tm);
     const int slot = p.tm * BN;                 // floats of one partial slot
@@ -2066,12 +2089,12 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
             if (v0 + j < vend) sum += x[j];
     }
     int m0, n0;
-    const KParams pv = tile_view(p, tile, m0, n0);   // the tile's batch entry
+    const KParams pv = tile_view<GRP>(p, tile, m0, n0);   // the tile's batch entry
     const int bpq = p.tm / 32;                  // 32 x 32 blocks per wave quadrant
     const int lane = f & 63, e4 = (f >> 6) & 3, b = (f >> 8) % bpq, quad = (f >> 8) / bpq;
     const int row = m0 + (quad >> 1) * (p.tm / 2) + (b >> 1) * 32 + 8 * e4 + 4 * (lane >> 5);
     const int col = n0 + (quad & 1) * 64 + (b & 1) * 32 + (lane & 31);
-    if (col >= p.N) return;
+    if (col >= pv.N) return;
     if (EPI) {
         const bool rc = reads_c(p);
         const float b = p.bias ? p.bias[col] : 0.0f;
@@ -2079,7 +2102,7 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
         const float bv[4] = {b, b, b, b};
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
-            cin[y] = (rc && row + y < p.M) ? pv.C[(size_t)(row + y) * p.N + col] : 0.0f;
+            cin[y] = (rc && row + y < pv.M) ? pv.C[(size_t)(row + y) * pv.N + col] : 0.0f;
             v[y] = sum[y];
         }
         finish<4>(p, v, cin, bv);
@@ -2088,7 +2111,7 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
     }
 #pragma unroll
     for (int y = 0; y < 4; ++y)
-        if (row + y < p.M) __builtin_nontemporal_store(sum[y], pv.C + (size_t)(row + y) * p.N + col);
+        if (row + y < pv.M) __builtin_nontemporal_store(sum[y], pv.C + (size_t)(row + y) * pv.N + col);
 }
 
 // ---------------------------------------------------------------------------
@@ -2111,7 +2134,7 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
 // units stream the same few K-slabs at any moment and the A and B panels
 // shared by neighbouring tiles are reused from the XCD's L2.
 // ---------------------------------------------------------------------------
-template <int DT, int BL, int NS, int NW, bool ATOMIC, bool EPI, int TM = 128>
+template <int DT, int BL, int NS, int NW, bool ATOMIC, bool EPI, int TM = 128, bool GRP = false>
 __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
     static_assert(!EPI || TM == 128, "the fused epilogue serves 128-row tiles");
     constexpr int SLOT = TM * BN;              // floats of one partial slot
@@ -2130,7 +2153,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
     // workers units + tile), then their Stream-K ranges over the last tiles.
     for (int tile = u; tile < p.dp_tiles; tile += p.units) {
         int m0, n0;
-        const KParams pv = tile_view(p, tile, m0, n0);
+        const KParams pv = tile_view<GRP>(p, tile, m0, n0);
         AccT<TM> acc;
         zero_acc(acc);
         mac_loop<DT, BL, NS, NW, TM>(pv, lds, m0, n0, 0, ipt, 0, acc, p.trace ? trace_cov(p, tile) : nullptr);
@@ -2148,7 +2171,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         const int k1 = min(end - tb, ipt);
         const int tile = p.tile_base + ts;
         int m0, n0;
-        const KParams pv = tile_view(p, tile, m0, n0);   // the tile's batch entry
+        const KParams pv = tile_view<GRP>(p, tile, m0, n0);   // the tile's batch entry
         const int role = k0 > 0 ? 2 : (k1 == ipt ? 0 : 1);
         const int owner = unit_of(tb, p.q, p.big);
         const int rot = (tb - unit_start(owner, p.q, p.big)) % ipt;
@@ -2239,7 +2262,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         // site (one inlined copy of the epilogue code)
         if constexpr (EPI) {
             if (stores_c) {
-                if (p.epi == EPI_PLAIN) store_tile<NW>(pv.C, m0, n0, p.M, p.N, t);
+                if (p.epi == EPI_PLAIN) store_tile<NW>(pv.C, m0, n0, pv.M, pv.N, t);
                 else finish_block<NW>(pv, m0, n0, t, 0, pre_c, pre_b);
             }
         }
@@ -2279,6 +2302,11 @@ __global__ __launch_bounds__(256) void epilogue_pass(KParams p, int stage) {
 // ---------------------------------------------------------------------------
 // Zero fill (n 32-bit words), 16-byte stores where possible.
 // ---------------------------------------------------------------------------
+__global__ void put_groups(GroupDesc *dst, GroupTable t, int n) {
+    const int i = threadIdx.x;
+    if (i < n) dst[i] = t.g[i];
+}
+
 __global__ void zero_words(uint32_t *p, int64_t n) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -2309,6 +2337,32 @@ typedef void (*KernelFn)(KParams);
 struct Shape {
     int ns, nw;
 };
+
+// Grouped calls (problem table, no epilogue, 128- and 64-row tiles) run builds
+// of their own, so the plain builds carry no table lookup.
+template <int DT, int BL>
+KernelFn pick_grouped(int kmode, bool epi, int tm, Shape &shape) {
+    if (epi) return nullptr;
+    if (tm == 64) {
+        shape = {3, 4};
+        switch (kmode) {
+        case K_DP: return gemm_dp<DT, BL, 3, 4, 64, true>;
+        case K_SPLITK: return gemm_splitk<DT, BL, 3, 4, 64, true>;
+        case K_SK: return gemm_streamk<DT, BL, 3, 4, false, false, 64, true>;
+        case K_SK_ATOMIC: return gemm_streamk<DT, BL, 3, 4, true, false, 64, true>;
+        default: return nullptr;
+        }
+    }
+    if (tm != 128) return nullptr;
+    shape = {4, 8};
+    switch (kmode) {
+    case K_DP: return gemm_dp<DT, BL, 4, 8, 128, true>;
+    case K_SPLITK: return gemm_splitk<DT, BL, 4, 8, 128, true>;
+    case K_SK: return gemm_streamk<DT, BL, 4, 8, false, false, 128, true>;
+    case K_SK_ATOMIC: return gemm_streamk<DT, BL, 4, 8, true, false, 128, true>;
+    default: return nullptr;
+    }
+}
 
 template <int DT, int BL>
 KernelFn pick(int kmode, bool epi, int tm, Shape &shape) {
@@ -2351,7 +2405,14 @@ KernelFn pick(int kmode, bool epi, int tm, Shape &shape) {
     }
 }
 
-KernelFn kernel_for(int dtype, int blayout, int kmode, bool epi, int tm, Shape &shape) {
+KernelFn kernel_for(int dtype, int blayout, int kmode, bool epi, int tm, bool grp, Shape &shape) {
+    if (grp) {
+        if (dtype == 0)
+            return blayout == 0 ? pick_grouped<0, 0>(kmode, epi, tm, shape) : pick_grouped<0, 1>(kmode, epi, tm, shape);
+        if (dtype == 1)
+            return blayout == 0 ? pick_grouped<1, 0>(kmode, epi, tm, shape) : pick_grouped<1, 1>(kmode, epi, tm, shape);
+        return nullptr;
+    }
     if (dtype == 0) return blayout == 0 ? pick<0, 0>(kmode, epi, tm, shape) : pick<0, 1>(kmode, epi, tm, shape);
     if (dtype == 1) return blayout == 0 ? pick<1, 0>(kmode, epi, tm, shape) : pick<1, 1>(kmode, epi, tm, shape);
     return nullptr;
@@ -2362,7 +2423,7 @@ KernelFn kernel_for(int dtype, int blayout, int kmode, bool epi, int tm, Shape &
 hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParams &p,
                        hipStream_t stream) {
     Shape shape{0, 0};
-    KernelFn fn = kernel_for(dtype, blayout, kmode, p.epi != EPI_PLAIN, p.tm, shape);
+    KernelFn fn = kernel_for(dtype, blayout, kmode, p.epi != EPI_PLAIN, p.tm, p.ngroups > 0, shape);
     if (!fn || grid <= 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * shape.nw), 0, stream, p);
     return hipGetLastError();
@@ -2372,7 +2433,10 @@ hipError_t launch_splitk_reduce(const KParams &p, hipStream_t stream) {
     const int64_t tiles = (int64_t)std::max(p.batch, 1) * p.tiles_m * p.tiles_n;   // every batch entry's tiles
     if (tiles <= 0) return hipSuccess;
     // a separate build with the epilogue keeps the plain one's code unchanged
-    if (p.epi != EPI_PLAIN)
+    if (p.ngroups > 0)
+        hipLaunchKernelGGL((splitk_reduce<false, true>), dim3((unsigned)(tiles * red_blocks_per_tile(p.tm))),
+                           dim3(RED_THREADS), 0, stream, p);
+    else if (p.epi != EPI_PLAIN)
         hipLaunchKernelGGL(splitk_reduce<true>, dim3((unsigned)(tiles * red_blocks_per_tile(p.tm))), dim3(RED_THREADS), 0,
                            stream, p);
     else
@@ -2383,7 +2447,10 @@ hipError_t launch_splitk_reduce(const KParams &p, hipStream_t stream) {
 
 hipError_t launch_streamk_reduce(const KParams &p, int64_t sk_tiles, hipStream_t stream) {
     if (sk_tiles <= 0) return hipSuccess;
-    if (p.epi != EPI_PLAIN)
+    if (p.ngroups > 0)
+        hipLaunchKernelGGL((streamk_reduce<false, true>), dim3((unsigned)(sk_tiles * red_blocks_per_tile(p.tm))),
+                           dim3(RED_THREADS), 0, stream, p);
+    else if (p.epi != EPI_PLAIN)
         hipLaunchKernelGGL(streamk_reduce<true>, dim3((unsigned)(sk_tiles * red_blocks_per_tile(p.tm))), dim3(RED_THREADS),
                            0, stream, p);
     else
@@ -2400,6 +2467,12 @@ hipError_t launch_epilogue_pass(const KParams &p, int stage, hipStream_t stream)
     return hipGetLastError();
 }
 
+hipError_t launch_put_groups(GroupDesc *dst, const GroupTable &t, int n, hipStream_t stream) {
+    if (n <= 0 || n > MAX_GROUPS) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(put_groups, dim3(1), dim3(64), 0, stream, dst, t, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_zero(void *ptr, int64_t n_words, hipStream_t stream) {
     if (n_words <= 0) return hipSuccess;
     int64_t blocks = (n_words / 4 + 255) / 256;
@@ -2410,13 +2483,14 @@ hipError_t launch_zero(void *ptr, int64_t n_words, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int tm, int *out) {
+hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int tm, bool grp, int *out) {
     // the smaller of the builds with and without the epilogue (the 256-row tile
-    // has no epilogue build, the 64-row tile's plain build serves both)
+    // has no epilogue build, the 64-row tile's plain build serves both, grouped
+    // builds have none)
     int best = 1 << 30;
-    for (int epi = 0; epi < (tm == 128 ? 2 : 1); ++epi) {
+    for (int epi = 0; epi < (tm == 128 && !grp ? 2 : 1); ++epi) {
         Shape shape{0, 0};
-        KernelFn fn = kernel_for(dtype, blayout, kmode, epi != 0, tm, shape);
+        KernelFn fn = kernel_for(dtype, blayout, kmode, epi != 0, tm, grp, shape);
         if (!fn) return hipErrorInvalidValue;
         int n = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(fn),

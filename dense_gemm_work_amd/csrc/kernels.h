@@ -44,6 +44,22 @@ enum : int {
 // Error bits of the device status word.
 enum : uint32_t { STATUS_TIMEOUT = 1u };
 
+// One problem of a grouped call (device table, nonempty problems only, in
+// call order): its operands, sizes, first global tile id and the offset of
+// its Split-K partials [S][M][N] in KParams::part.
+struct GroupDesc {
+    const uint16_t *A;
+    const uint16_t *B;
+    float *C;
+    long long part;        // floats from KParams::part
+    int M, N;
+    int tile0;             // global id of the problem's first tile
+    int pad;
+};
+static_assert(sizeof(GroupDesc) == 48, "device table entry");
+// Problems per grouped call: one wave's lanes find a tile's problem at once.
+constexpr int MAX_GROUPS = 64;
+
 struct KParams {
     const uint16_t *A;     // [M,K] row-major 16-bit operands
     const uint16_t *B;     // [K,N] or [N,K] row-major
@@ -69,6 +85,8 @@ struct KParams {
     uint32_t spin_limit;   // polls before a wait gives up
     uint32_t debug;        // GEMM_DEBUG_* bits
     int batch;             // matrices of a batched call (tiles numbered batch after batch)
+    const GroupDesc *groups;  // grouped call: the problems' table (tiles numbered problem after problem)
+    int ngroups;           // entries of `groups` (0: not a grouped call)
     long long sA, sB, sC;  // element strides between batch entries of A, B (0: one shared matrix) and C
     long long sP;          // Split-K: element stride between batch entries' partials ([batch][S][M][N])
     int epi, act;          // EPI_* and ACT_*: the fused epilogue of the final stores
@@ -102,11 +120,18 @@ hipError_t launch_streamk_reduce(const KParams &p, int64_t sk_tiles, hipStream_t
 // p.C, p.M, p.N, p.batch, p.sC, p.beta, p.bias, p.act).
 hipError_t launch_epilogue_pass(const KParams &p, int stage, hipStream_t stream);
 
+// Write a grouped call's problem table (at most MAX_GROUPS entries) to `dst`.
+struct GroupTable {
+    GroupDesc g[MAX_GROUPS];
+};
+hipError_t launch_put_groups(GroupDesc *dst, const GroupTable &t, int n, hipStream_t stream);
+
 // Fill n 32-bit words with zero (used instead of hipMemsetAsync so the call can
 // be captured in a HIP graph).
 hipError_t launch_zero(void *ptr, int64_t n_words, hipStream_t stream);
 
-// Resident workgroups per CU for the kernel of (dtype, blayout, kmode, tile rows tm).
-hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int tm, int *out);
+// Resident workgroups per CU for the kernel of (dtype, blayout, kmode, tile rows
+// tm), the grouped build when grp.
+hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int tm, bool grp, int *out);
 
 }  // namespace dgw

@@ -229,12 +229,56 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, u
     return GEMM_OK;
 }
 
+int64_t group_table_bytes(int32_t count) { return (int64_t(count) * 48 + 255) / 256 * 256; }
+
+int make_plan_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint32_t layout, uint32_t mode,
+                      int32_t splits, int32_t num_cus, gemm_plan_t *out, const char **why) {
+    static const char *none = "";
+    *why = none;
+    if (!out) { *why = "plan output pointer is null"; return GEMM_ERR_INVALID; }
+    if (!groups || count < 1 || count > GEMM_MAX_GROUPS) {
+        *why = "a grouped call takes 1..GEMM_MAX_GROUPS problems";
+        return GEMM_ERR_INVALID;
+    }
+    const uint32_t tile = mode & (GEMM_TILE_256x128 | GEMM_TILE_64x128);
+    const int64_t bm = tile == GEMM_TILE_256x128 ? 2 * GEMM_BM : (tile == GEMM_TILE_64x128 ? GEMM_BM / 2 : GEMM_BM);
+    int64_t tiles = 0, mn = 0;
+    for (int32_t g = 0; g < count; ++g) {
+        const int64_t M = groups[g].M, N = groups[g].N;
+        if (M < 0 || N < 0) { *why = "every problem's M and N must be >= 0"; return GEMM_ERR_INVALID; }
+        if (M > (int64_t(1) << 31) || N > (int64_t(1) << 22)) {
+            *why = "every problem's M must be at most 2^31 and N at most 2^22";
+            return GEMM_ERR_UNSUPPORTED;
+        }
+        if ((layout & 0xFu) == GEMM_B_KN && N % 8 != 0) {
+            *why = "every N must be a multiple of 8 when B is stored [K,N] (128-bit row loads)";
+            return GEMM_ERR_UNSUPPORTED;
+        }
+        tiles += ceil_div(M, bm) * ceil_div(N, GEMM_BN);
+        mn += M * N;
+    }
+    // tiles are numbered problem after problem: the schedule is that of one
+    // problem of the same tile count (a column of `tiles` tiles)
+    const int rc = make_plan(tiles * bm, GEMM_BN, K, 1, layout, mode, splits, num_cus, out, why);
+    if (rc != GEMM_OK) return rc;
+    if (out->decision == GEMM_SPLITK && !out->atomic && out->splits > 1)
+        out->workspace_bytes = control_bytes(*out) + int64_t(out->splits) * mn * 4;
+    out->workspace_bytes = (out->workspace_bytes + 255) / 256 * 256 + group_table_bytes(count);
+    return GEMM_OK;
+}
+
 int64_t control_bytes(const gemm_plan_t &p) {
     auto round = [](int64_t b) { return (b + 255) / 256 * 256; };
     return 256 + round(std::max<int64_t>(p.sk_units, 1) * 4) + round(std::max<int64_t>(p.tiles, 1) * 4);
 }
 
 }  // namespace dgw
+
+extern "C" int gemm_plan_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint32_t layout, uint32_t mode,
+                                 int32_t splits, int32_t num_cus, gemm_plan_t *out) {
+    const char *why = "";
+    return dgw::make_plan_grouped(groups, count, K, layout, mode, splits, num_cus, out, &why);
+}
 
 extern "C" int gemm_unit_range(const gemm_plan_t *plan, int64_t unit, int64_t *begin, int64_t *end) {
     if (!plan || !begin || !end) return GEMM_ERR_INVALID;

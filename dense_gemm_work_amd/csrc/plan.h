@@ -12,6 +12,13 @@ namespace dgw {
 int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, uint32_t mode, int32_t splits,
               int32_t num_cus, gemm_plan_t *out, const char **why);
 
+// Fill *out for a grouped call (only M and N of the groups are read): the plan
+// of one problem with the same tile count, with the workspace of the groups'
+// Split-K partials and their table (group_table_bytes(count) at its end).
+int make_plan_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint32_t layout, uint32_t mode,
+                      int32_t splits, int32_t num_cus, gemm_plan_t *out, const char **why);
+int64_t group_table_bytes(int32_t count);
+
 // First flattened iteration of Stream-K unit `unit` ("big" units first).
 int64_t unit_begin(int64_t unit, int64_t q, int64_t big);
 

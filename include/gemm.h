@@ -366,6 +366,47 @@ int gemm_ex(const gemm_args_t *args);
 int gemm_ex_noalloc(const gemm_args_t *args);
 
 /*
+ * Grouped calls: several problems C_g = A_g . B_g (or A_g . B_g^T) of one K,
+ * layout and dtype but their own M_g and N_g (e.g. the experts of a mixture
+ * layer), decomposed as one call (docc StreamK page, generality: grouped
+ * GEMM).  Their tiles are numbered problem after problem, so the rule, the
+ * Stream-K flattening and Split-K see every problem's tiles at once and one
+ * persistent launch balances them; the plan is the plan of one problem with
+ * the same tile count.  Up to GEMM_MAX_GROUPS problems; M_g = 0 or N_g = 0
+ * skips a problem.
+ */
+typedef struct gemm_group_t {
+    const void *A;   /* device, [M,K] row-major, 16-byte aligned (may be NULL when M*N == 0) */
+    const void *B;   /* device, [K,N] or [N,K] row-major, 16-byte aligned                   */
+    float *C;        /* device, [M,N] row-major fp32, overwritten; must not overlap A or B  */
+    int64_t M, N;    /* >= 0; N a multiple of 8 for GEMM_B_KN                               */
+} gemm_group_t;
+#define GEMM_MAX_GROUPS 64
+
+/*
+ * gemm_grouped -- run `count` (1..GEMM_MAX_GROUPS) problems as one call.
+ * `common` carries what the problems share and the call's options, as for
+ * gemm_ex(): K, layout, mode, splits, stream, workspace / workspace_bytes,
+ * num_cus, unit_perm, trace / trace_ints, spin_limit, debug, timing.  Its A, B,
+ * C, M, N, bias and batch must be zero / NULL (GEMM_ERR_INVALID otherwise), and
+ * the fused epilogue is not offered (epilogue != 0: GEMM_ERR_UNSUPPORTED).
+ * Data-parallel launches run one tile per workgroup (no 2x2 tile groups).
+ * The problem table is copied into the workspace by a kernel (no memset, no
+ * host-to-device copy), so the call can be captured in a graph; `groups` is
+ * read on the host before the call returns.  Asynchronous; returns a status.
+ */
+int gemm_grouped(const gemm_args_t *common, const gemm_group_t *groups, int32_t count);
+
+/*
+ * gemm_plan_grouped -- gemm_plan for a grouped call (only M and N of each group
+ * are read).  tiles is the problems' total; tiles_m = tiles and tiles_n = 1
+ * (the stacked problem whose schedule the call runs); workspace_bytes includes
+ * the Split-K partials of every problem ([S][M_g][N_g] each) and the table.
+ */
+int gemm_plan_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint32_t layout, uint32_t mode,
+                      int32_t splits, int32_t num_cus, gemm_plan_t *out);
+
+/*
  * gemm_plan -- decide the decomposition for a call without running it.
  * num_cus >= 1 (no device is queried).  Fills *out; returns a status.
  */

@@ -365,3 +365,17 @@ def plan_schedule(M: int, N: int, K: int, mode: str, splits: int = 0, sms: int =
         return Schedule("StreamK", tm, tn, ipt, 1, units, tiles, 0, total // units, total % units,
                         streamk_segments(unit_ranges(total, units), ipt), batch)
     raise ValueError(f"unknown mode {mode!r}")
+def plan_schedule_grouped(shapes, K: int, mode: str, splits: int = 0, sms: int = 256,
+                          bm: int = 128, bn: int = 128, bk: int = 64) -> Schedule:
+    """What a grouped call does: problems of the given (M, N) shapes with one K.
+
+    Reading (the docc StreamK page lists grouped GEMM among what the rewrite
+    covers but gives no schedule): the problems' tiles are numbered problem after
+    problem, like a batch's entries, so the rule, the Stream-K flattening and the
+    unit ranges see one tile count; the schedule is that of a single problem
+    with that many tiles (one column of them).  Problems with no tile add none.
+    """
+    tiles = sum(cdiv(M, bm) * cdiv(N, bn) for M, N in shapes)
+    return plan_schedule(tiles * bm, bn, K, mode, splits, sms, bm, bn, bk)
+
+

@@ -449,3 +449,70 @@ def test_tile_bits_are_exclusive(dg):
     with pytest.raises(dg.GemmError) as ei:
         dg.gemm_plan(256, 512, 2048, lw, dg.MODES["streamk"] | dg.GEMM_TILE_256x128 | dg.GEMM_TILE_64x128, 0, 256)
     assert ei.value.status == dg.GEMM_ERR_INVALID
+
+
+GROUP_SETS = [
+    [(96, 512), (0, 512), (300, 1024), (1, 8)],
+    [(256, 512)] * 4,
+    [(64 * i + 1, 4096) for i in range(8)],       # ragged expert batch sizes through one projection
+    [(2048, 2176)] + [(128, 128)] * 3,
+]
+
+
+@pytest.mark.parametrize("shapes", GROUP_SETS, ids=lambda s: f"{len(s)}groups")
+@pytest.mark.parametrize("mode,splits,tile", [("heuristic", 0, "128x128"), ("streamk", 0, "128x128"),
+                                              ("splitk", 4, "128x128"), ("dp", 0, "64x128"),
+                                              ("heuristic", 0, "64x128")])
+def test_grouped_plans_match_simulator(dg, shapes, mode, splits, tile):
+    K = 2048
+    lw = dg.layout_word("nk", "bf16")
+    p = dg.gemm_plan_grouped(shapes, K, lw, dg.mode_word(mode, tile=tile), splits, 256)
+    bm = int(tile.split("x")[0])
+    s = sch.plan_schedule_grouped(shapes, K, mode, splits, 256, bm=bm)
+    assert dg.DECISION_NAMES[p.decision] == s.kind
+    tiles = sum(-(-M // bm) * -(-N // 128) for M, N in shapes)
+    assert (p.tiles, p.tiles_m, p.tiles_n, p.ipt) == (tiles, tiles, 1, K // 64)
+    if s.kind == "StreamK":
+        assert (p.sk_units, p.sk_tiles, p.dp_tiles, p.q, p.big) == (s.units, s.sk_tiles, s.dp_tiles, s.q, s.big)
+    if s.kind == "SplitK":
+        assert p.splits == s.splits
+    # workspace: control words, the Split-K partials of every problem, the table
+    ctrl = 256 + -(-max(p.sk_units, 1) * 4 // 256) * 256 + -(-p.tiles * 4 // 256) * 256
+    table = -(-len(shapes) * 48 // 256) * 256
+    if s.kind == "SplitK" and p.splits > 1:
+        data = p.splits * sum(M * N for M, N in shapes) * 4
+    elif s.kind == "StreamK":
+        data = (2 if p.two_pass else 1) * p.sk_units * bm * 128 * 4
+    else:
+        data = 0
+    assert p.workspace_bytes == -(-(ctrl + data) // 256) * 256 + table
+
+
+def test_grouped_plan_refusals(dg):
+    lw_kn, lw_nk = dg.layout_word("kn", "bf16"), dg.layout_word("nk", "bf16")
+    mw = dg.mode_word("heuristic")
+    for shapes, lw, status in (([], lw_nk, dg.GEMM_ERR_INVALID),
+                               ([(8, 8)] * (dg.GEMM_MAX_GROUPS + 1), lw_nk, dg.GEMM_ERR_INVALID),
+                               ([(8, 8), (-1, 8)], lw_nk, dg.GEMM_ERR_INVALID),
+                               ([(8, 12)], lw_kn, dg.GEMM_ERR_UNSUPPORTED)):
+        with pytest.raises(dg.GemmError) as ei:
+            dg.gemm_plan_grouped(shapes, 2048, lw, mw, 0, 256)
+        assert ei.value.status == status
+    # the same shapes with B [N,K] are fine
+    dg.gemm_plan_grouped([(8, 12)], 2048, lw_nk, mw, 0, 256)
+
+
+def test_grouped_call_argument_checks_need_no_gpu(dg):
+    # refusals that happen before any HIP call
+    common = dg.GemmArgs()
+    common.K = 256
+    common.layout = dg.layout_word("nk", "bf16")
+    common.M = 8   # the common arguments must not carry a problem
+    assert dg.gemm_grouped(common, [(0x1000, 0x2000, 0x3000, 8, 8)]) == dg.GEMM_ERR_INVALID
+    common.M = 0
+    common.epilogue = dg.GEMM_EPI_ALPHA_BETA
+    common.alpha = 2.0
+    assert dg.gemm_grouped(common, [(0x1000, 0x2000, 0x3000, 8, 8)]) == dg.GEMM_ERR_UNSUPPORTED
+    common.epilogue = 0
+    assert dg.gemm_grouped(common, [(0x1001, 0x2000, 0x3000, 8, 8)]) == dg.GEMM_ERR_UNSUPPORTED   # misaligned A
+    assert dg.gemm_grouped(common, [(0x1000, 0x2000, 0x1000, 8, 8)]) == dg.GEMM_ERR_INVALID       # C overlaps A

@@ -4,6 +4,8 @@ Values come from the pages' printed results (tests/golden/, each file cites its
 table), the toy figure of the book chapter's "Mental model" section, the
 structural facts printed by its Triton case, and brute force."""
 import itertools
+
+import numpy as np
 from pathlib import Path
 
 import pytest
@@ -257,3 +259,29 @@ def test_rule_splitk_needs_aligned_split():
     assert sch.decide(64, 32, 256) == sch.Decision("SplitK", 64, 256)
     assert sch.decide(64, 34, 256) == sch.Decision("StreamK", 64, 256)
     assert sch.decide(64, 36, 256).kind == "SplitK"
+
+
+@pytest.mark.parametrize("shapes,K,mode,splits", [
+    ([(256, 512)] * 4, 2048, "heuristic", 0),
+    ([(1000, 1000)] * 3, 640, "streamk", 7),
+    ([(96, 512)] * 8, 2048, "splitk", 4),
+])
+def test_grouped_schedule_of_equal_shapes_is_the_batch(shapes, K, mode, splits):
+    # problems of one shape, numbered problem after problem, are a batch
+    M, N = shapes[0]
+    g = sch.plan_schedule_grouped(shapes, K, mode, splits)
+    b = sch.plan_schedule(M, N, K, mode, splits, batch=len(shapes))
+    assert (g.kind, g.ipt, g.splits, g.units, g.sk_tiles, g.dp_tiles, g.q, g.big) == \
+           (b.kind, b.ipt, b.splits, b.units, b.sk_tiles, b.dp_tiles, b.q, b.big)
+    assert sorted(x.as_tuple() for x in g.segments) == sorted(x.as_tuple() for x in b.segments)
+
+
+def test_grouped_schedule_counts_every_problem_tile():
+    shapes = [(96, 512), (0, 512), (300, 1024), (1, 8), (64, 0)]
+    for bm in (64, 128, 256):
+        g = sch.plan_schedule_grouped(shapes, 1024, "streamk", 5, bm=bm)
+        tiles = sum(-(-M // bm) * -(-N // 128) for M, N in shapes)
+        cov = np.zeros((tiles, 16), dtype=int)
+        for x in g.segments:
+            cov[x.tile, x.k0:x.k1] += 1
+        assert np.all(cov == 1)
