@@ -241,7 +241,11 @@ int make_plan_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint
         return GEMM_ERR_INVALID;
     }
     const uint32_t tile = mode & (GEMM_TILE_256x128 | GEMM_TILE_64x128);
-    const int64_t bm = tile == GEMM_TILE_256x128 ? 2 * GEMM_BM : (tile == GEMM_TILE_64x128 ? GEMM_BM / 2 : GEMM_BM);
+    if (tile == GEMM_TILE_256x128) {
+        *why = "grouped calls run 128- and 64-row tiles (GEMM_TILE_256x128 is not offered)";
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    const int64_t bm = tile == GEMM_TILE_64x128 ? GEMM_BM / 2 : GEMM_BM;
     int64_t tiles = 0, mn = 0;
     for (int32_t g = 0; g < count; ++g) {
         const int64_t M = groups[g].M, N = groups[g].N;

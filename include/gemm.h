@@ -390,6 +390,7 @@ typedef struct gemm_group_t {
  * num_cus, unit_perm, trace / trace_ints, spin_limit, debug, timing.  Its A, B,
  * C, M, N, bias and batch must be zero / NULL (GEMM_ERR_INVALID otherwise), and
  * the fused epilogue is not offered (epilogue != 0: GEMM_ERR_UNSUPPORTED).
+ * Tiles: 128x128 or GEMM_TILE_64x128 (GEMM_TILE_256x128: GEMM_ERR_UNSUPPORTED).
  * Data-parallel launches run one tile per workgroup (no 2x2 tile groups).
  * The problem table is copied into the workspace by a kernel (no memset, no
  * host-to-device copy), so the call can be captured in a graph; `groups` is

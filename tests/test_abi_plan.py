@@ -500,6 +500,10 @@ def test_grouped_plan_refusals(dg):
         assert ei.value.status == status
     # the same shapes with B [N,K] are fine
     dg.gemm_plan_grouped([(8, 12)], 2048, lw_nk, mw, 0, 256)
+    # grouped calls have no 256-row tile build
+    with pytest.raises(dg.GemmError) as ei:
+        dg.gemm_plan_grouped([(512, 512)], 2048, lw_nk, dg.mode_word("streamk", tile="256x128"), 0, 256)
+    assert ei.value.status == dg.GEMM_ERR_UNSUPPORTED
 
 
 def test_grouped_call_argument_checks_need_no_gpu(dg):
