@@ -109,6 +109,46 @@ class Call:
             raise self.dg.GemmError(st, self.dg.gemm_last_error())
 
 
+class GroupedCall:
+    """A prepared gemm_grouped call over (a_g, b_g, c_g) device tensors (one K,
+    one dtype; argument struct and problem table built once)."""
+
+    def __init__(self, dg, problems, b_layout, mode="heuristic", splits=0, stream=None, tile="128x128"):
+        import torch
+
+        self.dg = dg
+        common = dg.GemmArgs()
+        K = problems[0][0].shape[-1]
+        common.K = K
+        common.layout = dg.layout_word(b_layout, "bf16" if problems[0][0].dtype == torch.bfloat16 else "fp16")
+        common.mode = dg.mode_word(mode, tile=tile)
+        common.splits = splits
+        self.stream = stream or torch.cuda.current_stream()
+        common.stream = self.stream.cuda_stream
+        self.common = common
+        shapes = [(a.shape[0], c.shape[1]) for a, _, c in problems]
+        self.groups = dg.group_array([(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N)
+                                      for (a, b, c), (M, N) in zip(problems, shapes)])
+        self.plan = dg.gemm_plan_grouped(shapes, K, common.layout, common.mode, splits, dg.gemm_num_cus())
+
+    def __call__(self):
+        st = self.dg.gemm_grouped(self.common, self.groups)
+        if st != 0:
+            raise self.dg.GemmError(st, self.dg.gemm_last_error())
+
+
+class SeparateCalls:
+    """The same problems as one gemm_ex call each, back to back on one stream."""
+
+    def __init__(self, calls):
+        self.calls = calls
+        self.stream = calls[0].stream
+
+    def __call__(self):
+        for c in self.calls:
+            c()
+
+
 def time_call(call: Call, steps: int, warmup: int):
     """Warm up, then time exactly `steps` back-to-back calls: the wall clock of
     the timed region (synchronised on both sides) and one HIP event pair on the
@@ -215,7 +255,7 @@ def paired_speedup(base_rounds, arm_rounds):
 
 # samples per round and calls per sample: a few seconds of GPU time per workload
 PROTOCOL = {"c1": (40, 8), "c2": (40, 8), "c3": (40, 8), "c4": (6, 2), "c5": (20, 8), "x1": (12, 4), "x2": (20, 8),
-            "x3": (40, 8)}
+            "x3": (40, 8), "x4": (20, 4)}
 
 
 def shape_arms(dg, name, rounds):
@@ -302,6 +342,68 @@ def shape_arms(dg, name, rounds):
                 out[arm]["pack1"]["speedup_vs_dp"] = paired_speedup(timed1["dp"], timed1[arm])
             log(f"  {name:14s} {arm:20s} {r['median_us']:9.3f} us  (pack 1)"
                 + (f"  x{out[arm]['pack1']['speedup_vs_dp']['median']} vs dp" if arm != "dp" and "dp" in timed1 else ""))
+    return out
+
+
+def grouped_operands(gw):
+    """Device operands of a grouped workload: the problems' A_g, their weights
+    as one [G, ...] tensor, and fp32 outputs."""
+    import torch
+    from workloads import make_group_operands
+
+    As, B = make_group_operands(gw)
+    a = [x.cuda() for x in As]
+    b = B.cuda()
+    c = [torch.zeros((M, gw.N), dtype=torch.float32, device="cuda") for M in gw.Ms]
+    return a, b, c
+
+
+def grouped_arms(dg, name, rounds):
+    """A grouped workload three ways: one grouped call (the rule over all the
+    problems' tiles), one call per problem (the rule per problem), and a batched
+    call over the problems padded to the largest row count; speedups paired
+    against the per-problem calls."""
+    import torch
+    from workloads import GROUPED
+
+    gw = GROUPED[name]
+    a, b, c = grouped_operands(gw)
+    G, Mmax = len(gw.Ms), max(gw.Ms)
+    a_pad = torch.zeros((G, Mmax, gw.K), dtype=a[0].dtype, device="cuda")
+    for g, x in enumerate(a):
+        a_pad[g, : x.shape[0]] = x
+    c_pad = torch.zeros((G, Mmax, gw.N), dtype=torch.float32, device="cuda")
+    calls = {
+        "separate": SeparateCalls([Call(dg, a[g], b[g], c[g], gw.b_layout, "heuristic") for g in range(G)]),
+        "grouped": GroupedCall(dg, list(zip(a, b, c)), gw.b_layout),
+        "grouped_64x128": GroupedCall(dg, list(zip(a, b, c)), gw.b_layout, tile="64x128"),
+        "batched_padded": Call(dg, a_pad, b, c_pad, gw.b_layout, "heuristic"),
+    }
+    samples, pack = PROTOCOL[name[:2]]
+    timed = time_arms(calls, rounds, samples, pack)
+    out = {"Ms": list(gw.Ms), "N": gw.N, "K": gw.K, "dtype": gw.dtype, "b_layout": gw.b_layout,
+           "protocol": {"rounds": rounds, "samples_per_round": samples, "calls_per_sample": pack,
+                        "order": "rotated every sample, reversed every other round"}}
+    # A and the outputs once, every problem's weights once
+    compulsory = sum(M * gw.K * 2 + M * gw.N * 4 for M in gw.Ms) + G * gw.N * gw.K * 2
+    for arm, call in calls.items():
+        flat = [x for r in timed[arm] for x in r]
+        med = statistics.median(flat)
+        r = {"median_us": round(med, 3), "p10_us": round(_q(flat, 0.1), 3), "p90_us": round(_q(flat, 0.9), 3),
+             "min_us": round(min(flat), 3),
+             "tflops": round(gw.flops / (med * 1e-6) / 1e12, 2),   # useful flops (padding rows not counted)
+             "pct_peak": round(100 * gw.flops / (med * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2),
+             "compulsory_gbps": round(compulsory / (med * 1e-6) / 1e9, 1)}
+        plan = getattr(call, "plan", None)
+        if plan is not None:
+            r["decision"] = dg.DECISION_NAMES[plan.decision]
+            r["tiles"] = int(plan.tiles)
+            r["units_or_splits"] = int(plan.sk_units or plan.splits)
+        if arm != "separate":
+            r["speedup_vs_separate"] = paired_speedup(timed["separate"], timed[arm])
+        out[arm] = r
+        log(f"  {name:14s} {arm:20s} {r['median_us']:9.3f} us  {r['tflops']:8.2f} TFLOP/s"
+            + (f"  x{r['speedup_vs_separate']['median']} vs separate" if "speedup_vs_separate" in r else ""))
     return out
 
 
@@ -546,6 +648,67 @@ def output_check(c_before, c_after, ref):
     return res
 
 
+def copy_probe(mib: int) -> None:
+    """One plain device copy of `mib` MiB: a dispatch of known size for scaling
+    the HBM byte counters."""
+    import torch
+
+    if mib <= 0:
+        return
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"bench: copy probe {mib} MiB read + {mib} MiB written")
+
+
+def grouped_profile_key(dg, plan, gw) -> str:
+    """Name of the committed profile summary of a grouped launch (profiles/<key>.md)."""
+    kind = {dg.GEMM_DP: "gemm_dp", dg.GEMM_SPLITK: "gemm_splitk", dg.GEMM_STREAMK: "gemm_streamk"}[plan.decision]
+    return (f"{kind}_grouped_{gw.dtype}_{gw.b_layout}_{len(gw.Ms)}_problems_{sum(gw.Ms)}x{gw.N}x{gw.K}"
+            + (f"_{plan.bm}x{plan.bn}" if plan.bm != 128 else ""))
+
+
+def grouped_main(args, dg) -> int:
+    """--workload of a grouped workload: time exactly `steps` grouped calls (for
+    profiling that launch), one JSON line; the headline workload is single."""
+    import torch
+    from workloads import GROUPED
+
+    gw = GROUPED[args.workload]
+    a, b, c = grouped_operands(gw)
+    mode = args.mode or "heuristic"
+    call = GroupedCall(dg, list(zip(a, b, c)), gw.b_layout, mode, args.splits or 0, tile=args.tile)
+    p = call.plan
+    log(f"bench: {gw.name} {len(gw.Ms)} problems, {p.tiles} tiles, plan={dg.DECISION_NAMES[p.decision]} "
+        f"units={p.sk_units} steps={args.steps} warmup={args.warmup}")
+    wall, ev_ms = time_call(call, args.steps, args.warmup)
+    st = dg.gemm_sync_status()
+    if st != 0:
+        raise RuntimeError(f"device status {st}: {dg.gemm_last_error()}")
+    kern_ms = ev_ms / args.steps
+    achieved = gw.flops / (kern_ms * 1e-3) / 1e12
+    log(f"bench: kernel mean {kern_ms * 1e3:.2f} us ({achieved:.1f} TFLOP/s)")
+    copy_probe(args.copy_probe_mb)
+    profile = grouped_profile_key(dg, p, gw)
+    line = {
+        "metric": "grouped GEMM TFLOP/s (useful flops)", "value": round(gw.flops * args.steps / wall / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True, "scaling": "strong",
+        "vs_baseline": None, "dtype": gw.dtype, "data": f"synthetic (seeded uniform[{gw.low},{gw.high}))",
+        "config": {"workload": f"{gw.name}: {len(gw.Ms)} problems M={list(gw.Ms)}, N={gw.N}, K={gw.K}, "
+                               f"{p.bm}x{p.bn}x64 tiles, {mode} -> {dg.DECISION_NAMES[p.decision]}",
+                   "tiles": int(p.tiles), "cus": dg.gemm_num_cus()},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(profile),
+                     "kernel_mean_us": round(kern_ms * 1e3, 3)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -558,8 +721,10 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
     import dense_gemm_work_amd as dg
-    from workloads import WORKLOADS, make_operands
+    from workloads import GROUPED, WORKLOADS, make_operands
 
+    if args.workload in GROUPED:
+        return grouped_main(args, dg)
     w = WORKLOADS[args.workload]
     if args.mode is not None:
         w = w.with_(mode=args.mode, splits=args.splits if args.splits is not None else 0,
@@ -591,21 +756,14 @@ def main():
         f"({achieved:.1f} TFLOP/s, {100 * achieved / PEAK_BF16_TFLOPS:.1f}% of peak)")
 
     # ---- arms on the same shape and the other shapes -------------------------------
-    if args.copy_probe_mb > 0:
-        n = args.copy_probe_mb * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"bench: copy probe {args.copy_probe_mb} MiB read + {args.copy_probe_mb} MiB written")
-        del src, dst
+    copy_probe(args.copy_probe_mb)
 
     shapes = {}
     if not args.no_shapes:
         for name in ("c3_wavequant", "c1_sk32", "c2a_m96_s8", "c2b_m256_s2", "c5_longk_fp16", "c4_large_dp",
                      "x1_hybrid", "x2_batched", "x3_decode"):
             shapes[name] = shape_arms(dg, name, args.rounds)
+        shapes["x4_grouped"] = grouped_arms(dg, "x4_grouped", args.rounds)
     vendor = {}
     if args.vendor and not args.no_shapes:
         # operands with B [K,N] only (torch.mm is then given contiguous operands)

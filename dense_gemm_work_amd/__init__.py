@@ -24,7 +24,8 @@ from pathlib import Path
 from typing import Optional
 
 __all__ = [
-    "GemmError", "GemmPlan", "GemmArgs", "gemm", "gemm_ex", "gemm_ex_noalloc", "gemm_plan", "gemm_plan_batched",
+    "GemmError", "GemmPlan", "GemmArgs", "GemmGroup", "gemm", "gemm_ex", "gemm_ex_noalloc", "gemm_grouped",
+    "gemm_plan", "gemm_plan_batched", "gemm_plan_grouped", "group_array", "gemm_grouped_tensors",
     "gemm_workspace_size", "gemm_unit_range",
     "gemm_set_stream", "gemm_sync_status", "gemm_release", "gemm_last_error", "gemm_num_cus",
     "gemm_version", "gemm_tensors", "matmul", "plan_dict", "library_path",
@@ -230,9 +231,15 @@ def _group_array(groups):
 
 
 def gemm_grouped(common: GemmArgs, groups) -> int:
-    """gemm_grouped(): ``groups`` a sequence of (A, B, C, M, N) (device addresses)."""
-    arr = _group_array(groups)
+    """gemm_grouped(): ``groups`` a sequence of (A, B, C, M, N) (device addresses),
+    or an array from ``group_array`` (built once, passed as it is)."""
+    arr = groups if isinstance(groups, ctypes.Array) else _group_array(groups)
     return _lib.gemm_grouped(ctypes.byref(common), arr, len(groups))
+
+
+def group_array(groups):
+    """A reusable ctypes array of GemmGroup for gemm_grouped()."""
+    return _group_array(groups)
 
 
 def gemm_plan_grouped(shapes, K: int, layout: int, mode: int, splits: int, num_cus: int) -> GemmPlan:

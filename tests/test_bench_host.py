@@ -59,6 +59,13 @@ def test_profile_key_names_the_launch():
     assert bench.profile_key(DG, P, w) == "gemm_streamk_bf16_kn_2048x2176x4096_256x128"
 
 
+    # a grouped launch: the key of the committed grouped profile
+    from workloads import GROUPED
+    P.bm = 128
+    key = bench.grouped_profile_key(DG, P, GROUPED["x4_grouped"])
+    assert key == "gemm_streamk_grouped_bf16_nk_8_problems_2048x2048x4096"
+    assert (ROOT / "profiles" / (key + ".md")).exists()
+
 
 def test_compulsory_bytes():
     import bench

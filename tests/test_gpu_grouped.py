@@ -183,3 +183,25 @@ def test_grouped_k_zero_and_all_empty(dg):
         assert torch.all(p["c"] == 0.0)
     probs = _problems([(0, 512), (64, 0)], 256, "nk", "bf16")
     _run(dg, probs, "nk")   # nothing to do: no launch, guards intact
+
+
+@pytest.mark.parametrize("mode,splits,tile", [("heuristic", 0, "128x128"), ("heuristic", 0, "64x128")])
+def test_grouped_expert_layer_full_size(dg, mode, splits, tile):
+    """The grouped bench workload (8 problems, 2048 tokens, 4096 -> 2048) at its
+    full size, every element of every problem against the oracle."""
+    from workloads import GROUPED, make_group_operands
+
+    gw = GROUPED["x4_grouped"]
+    As, B = make_group_operands(gw)
+    b = B.to(DEV)
+    probs = []
+    for g, (A, M) in enumerate(zip(As, gw.Ms)):
+        full = torch.full((M * gw.N + NGUARD,), POISON, dtype=torch.float32, device=DEV)
+        full[M * gw.N:] = GUARD
+        probs.append(dict(M=M, N=gw.N, A=A, B=B[g], a=A.to(DEV), b=b[g], full=full,
+                          c=full[: M * gw.N].view(M, gw.N)))
+    _run(dg, probs, gw.b_layout, mode=mode, splits=splits, tile=tile)
+    for p in probs:
+        assert not bool(torch.any(p["c"] == POISON)), "an output element was never written"
+    _check(probs, gw.K, gw.b_layout, gw.dtype)
+

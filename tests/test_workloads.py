@@ -74,3 +74,29 @@ def test_seed_determines_the_operands():
     assert np.array_equal(operand_bits(A1), operand_bits(A2))
     assert np.array_equal(operand_bits(B1), operand_bits(B2))
     assert not np.array_equal(operand_bits(A1), operand_bits(A3))
+
+
+def test_grouped_draws_every_a_then_all_weights():
+    from dataclasses import replace
+
+    from workloads import GROUPED, make_group_operands
+
+    gw = replace(GROUPED["x4_grouped"], Ms=(5, 0, 3), N=16, K=24)
+    As, B = make_group_operands(gw)
+    rng = np.random.Generator(np.random.PCG64(gw.seed))
+    for M, A in zip(gw.Ms, As):
+        a32 = rng.uniform(gw.low, gw.high, size=(M, gw.K)).astype(np.float32)
+        assert tuple(A.shape) == (M, gw.K)
+        assert np.array_equal(operand_bits(A), _bf16_rne_bits(a32))
+    b32 = rng.uniform(gw.low, gw.high, size=(3, gw.N, gw.K)).astype(np.float32)
+    assert tuple(B.shape) == (3, gw.N, gw.K)
+    assert np.array_equal(operand_bits(B), _bf16_rne_bits(b32))
+    assert gw.flops == 2 * 8 * 16 * 24
+
+
+def test_grouped_workload_tile_count():
+    from workloads import GROUPED
+
+    gw = GROUPED["x4_grouped"]
+    assert sum(-(-M // 128) for M in gw.Ms) * (gw.N // 128) == 304
+    assert sum(gw.Ms) == 2048

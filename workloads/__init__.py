@@ -32,7 +32,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_operands", "operand_bits", "get"]
+__all__ = ["Workload", "WORKLOADS", "make_operands", "operand_bits", "get", "GroupedWorkload", "GROUPED",
+           "make_group_operands"]
 
 
 @dataclass(frozen=True)
@@ -113,6 +114,60 @@ WORKLOADS = {
 
 def get(name: str) -> Workload:
     return WORKLOADS[name]
+
+
+@dataclass(frozen=True)
+class GroupedWorkload:
+    """Problems of one K and one weight shape with their own row counts, run as
+    one grouped call: an expert layer, where problem g multiplies the ``Ms[g]``
+    tokens routed to expert g by that expert's own weights."""
+
+    name: str
+    Ms: tuple
+    N: int
+    K: int
+    dtype: str = "bf16"
+    b_layout: str = "nk"
+    low: float = -1.0
+    high: float = 1.0
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def flops(self) -> int:
+        return 2 * sum(self.Ms) * self.N * self.K
+
+    def member(self, g: int) -> Workload:
+        """Problem g as a single-problem workload (same distribution)."""
+        return Workload(f"{self.name}[{g}]", self.Ms[g], self.N, self.K, self.dtype, self.b_layout, "uniform",
+                        self.low, self.high)
+
+    def b_shape(self):
+        return (self.K, self.N) if self.b_layout == "kn" else (self.N, self.K)
+
+
+GROUPED = {
+    # 2048 tokens routed unevenly over 8 experts, each a 4096 -> 2048 projection
+    # with weights stored [N,K]: 19 tile rows x 16 = 304 tiles of 128x128 (one
+    # full wave on 256 CUs and a 48-tile tail), 64 iterations each.
+    "x4_grouped": GroupedWorkload("x4_grouped", (448, 96, 320, 64, 512, 160, 256, 192), 2048, 4096,
+                                  note="8 problems, 304 tiles; heuristic -> Stream-K over all of them"),
+}
+
+
+def make_group_operands(gw: GroupedWorkload, seed: Optional[int] = None):
+    """Return ``([A_g], B)`` as CPU torch tensors in the workload's 16-bit dtype:
+    ``A_g`` of shape ``[Ms[g], K]`` drawn in problem order, then every problem's
+    weights as one ``[G, N, K]`` (layout "nk") or ``[G, K, N]`` array, all from
+    one ``PCG64(seed)`` stream, uniform on [low, high), rounded as in
+    ``make_operands``."""
+    rng = np.random.Generator(np.random.PCG64(gw.seed if seed is None else seed))
+    td = _torch_dtype(gw.dtype)
+    As = [torch.from_numpy(rng.uniform(gw.low, gw.high, size=(M, gw.K)).astype(np.float32)).to(td).contiguous()
+          for M in gw.Ms]
+    b64 = rng.uniform(gw.low, gw.high, size=(len(gw.Ms),) + tuple(gw.b_shape()))
+    B = torch.from_numpy(b64.astype(np.float32)).to(td).contiguous()
+    return As, B
 
 
 def _torch_dtype(dtype: str) -> torch.dtype:
