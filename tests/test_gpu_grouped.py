@@ -205,3 +205,52 @@ def test_grouped_expert_layer_full_size(dg, mode, splits, tile):
         assert not bool(torch.any(p["c"] == POISON)), "an output element was never written"
     _check(probs, gw.K, gw.b_layout, gw.dtype)
 
+
+
+@pytest.mark.parametrize("mode,splits,tile", [("streamk", 0, "128x128"), ("splitk", 4, "128x128"),
+                                              ("dp", 0, "64x128"), ("streamk", 0, "64x128")])
+def test_grouped_ragged_k(dg, mode, splits, tile):
+    """K not a multiple of the 64-wide iteration: the last iteration of every
+    tile is zero-filled beyond K, in every problem."""
+    K = 1000
+    probs = _problems(SETS["ragged"], K, "nk", "bf16", seed=500)
+    _run(dg, probs, "nk", mode=mode, splits=splits, tile=tile)
+    _check(probs, K, "nk", "bf16")
+
+
+@pytest.mark.parametrize("mode,splits", [("heuristic", 0), ("splitk", 4), ("streamk", 37)])
+def test_grouped_graph_replays_match_eager(dg, mode, splits):
+    """A grouped call captured in a HIP graph (its problem table is written by a
+    kernel, no memset or host copy): every replay on fresh operands gives the
+    bits of an eager call, with eager work between the replays."""
+    shapes = SETS["experts"]
+    K = 1024
+    probs = _problems(shapes, K, "kn", "fp16", seed=600)
+    triples = [(p["a"], p["b"], p["c"]) for p in probs]
+    call = lambda outs: dg.gemm_grouped_tensors([(a, b, o) for (a, b, _), o in zip(triples, outs)],
+                                                b_layout="kn", mode=mode, splits=splits)
+    call([p["c"] for p in probs])           # eager: allocates the workspace outside the capture
+    torch.cuda.synchronize()
+    assert dg.gemm_sync_status() == 0
+    g = torch.cuda.CUDAGraph()
+    say(f"  capture grouped {mode}{splits}")
+    with torch.cuda.graph(g):
+        call([p["c"] for p in probs])
+    for r in range(3):
+        fresh = _problems(shapes, K, "kn", "fp16", seed=700 + 10 * r)
+        for p, q in zip(probs, fresh):
+            p["a"].copy_(q["a"])
+            p["b"].copy_(q["b"])
+            p["c"].fill_(POISON)
+            p["A"], p["B"] = q["A"], q["B"]
+        say(f"  replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert dg.gemm_sync_status() == 0, dg.gemm_last_error()
+        eager = [torch.full_like(p["c"], POISON) for p in probs]
+        call(eager)                          # eager work between the replays, on the same operands
+        torch.cuda.synchronize()
+        for i, (p, e) in enumerate(zip(probs, eager)):
+            assert torch.equal(p["c"].view(torch.int32), e.view(torch.int32)), f"replay {r}: problem {i} differs"
+        _check(probs, K, "kn", "fp16")
+    del g
