@@ -307,6 +307,10 @@ def _matrix_strides(name: str, t, rows: int, cols: int):
         return None, 0
     if t.dim() != 3 or tuple(t.shape[1:]) != (rows, cols):
         raise ValueError(f"{name} must be [{rows}, {cols}] or [batch, {rows}, {cols}]")
+    if rows * cols == 0:
+        # an empty entry (K == 0 operands, an empty C) is never read or written:
+        # its strides carry no layout (torch gives such tensors arbitrary ones)
+        return t.shape[0], 0
     if (cols > 1 and t.stride(2) != 1) or (rows > 1 and t.stride(1) != cols):
         raise ValueError(f"{name}: every batch entry must be a contiguous row-major matrix")
     return t.shape[0], (t.stride(0) if t.shape[0] > 1 else 0)

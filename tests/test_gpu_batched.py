@@ -177,6 +177,29 @@ def test_batched_rejects_bad_strides(dg):
     assert dg.gemm_ex(args) == dg.GEMM_ERR_UNSUPPORTED
 
 
+def test_batched_empty_k(dg):
+    # K = 0 in a batch: the operands are empty tensors (torch gives them strides
+    # that describe no layout) and every entry of C is the empty sum, 0, or with
+    # the epilogue act(beta C_in + bias)
+    M, N = 200, 136
+    for layout in ("kn", "nk"):
+        a = torch.empty(3, M, 0, dtype=torch.bfloat16, device=DEV)
+        b = torch.empty((3, 0, N) if layout == "kn" else (3, N, 0), dtype=torch.bfloat16, device=DEV)
+        c = torch.full((3, M, N), 7.0, dtype=torch.float32, device=DEV)
+        say(f"  batched K = 0, {layout}")
+        dg.gemm_tensors(a, b, c, b_layout=layout, mode="heuristic")
+        assert dg.gemm_sync_status() == 0
+        assert bool(torch.all(c == 0.0))
+        c_in, bias = make_epilogue_inputs(M, N)
+        c = c_in.to(DEV).expand(3, M, N).contiguous()
+        dg.gemm_tensors(a, b, c, b_layout=layout, alpha=2.0, beta=-1.0, bias=bias.to(DEV), act="relu")
+        assert dg.gemm_sync_status() == 0
+        D, _ = oe.epilogue_ref(np.zeros((M, N)), c_in.numpy().astype(np.float64), 2.0, -1.0,
+                               bias.numpy().astype(np.float64), "relu")
+        for e in range(3):
+            assert np.allclose(c[e].cpu().numpy(), D, rtol=0, atol=1e-6)
+
+
 def test_x2_batched_workload(dg):
     # the benchmark's batched workload at full size: 5 x (1024x1024x2048), heuristic
     w = WORKLOADS["x2_batched"]
