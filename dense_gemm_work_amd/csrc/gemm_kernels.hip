@@ -687,29 +687,47 @@ __device__ __forceinline__ Tile<NW, TM> merge_k_halves(const AccT<TM> &acc, char
 // are numbered in groups of `group_m` tile rows, column by column inside a
 // group, so a contiguous range of tile ids is a compact 2-D block.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int spread(int b, int n) {
-    const int x = b & 7, j = b >> 3;
-    int base = 0;
-    for (int xx = 0; xx < x; ++xx) base += (n - xx + 7) >> 3;
-    return base + j;
+// floor(n / d) for 0 <= n < 2^31 (FastDiv in kernels.h).
+__device__ __forceinline__ int fdiv(int n, FastDiv d) {
+    return (int)((__umulhi((uint32_t)n, d.m) + (uint32_t)n) >> d.s);
 }
 
 // First flattened iteration of Stream-K unit u (the first `big` units own q + 1).
 __device__ __forceinline__ int unit_start(int u, int q, int big) { return u * q + min(u, big); }
 
 // The unit whose range contains flattened iteration g (q >= 1, or g < big).
-__device__ __forceinline__ int unit_of(int g, int q, int big) {
-    const int long_part = big * (q + 1);
-    return g < long_part ? g / (q + 1) : big + (g - long_part) / max(q, 1);
+__device__ __forceinline__ int unit_of(const KParams &p, int g) {
+    const int long_part = p.big * (p.q + 1);
+    return g < long_part ? fdiv(g, p.d_q1) : p.big + fdiv(g - long_part, p.d_q);
 }
 
-__device__ __forceinline__ int worker_of(const KParams &p, int n) {
+// The worker workgroup b runs: unit_perm's entry, or with XCD spreading the
+// b / 8-th worker of XCD b % 8's contiguous range (XCD x holds n / 8 workers,
+// one more for x < n % 8, after those of the XCDs before it), or b.  The same
+// value in every lane.
+__device__ __forceinline__ int worker_of(const KParams &p) {
     const int b = (int)blockIdx.x;
-    if (p.perm) return p.perm[b];
-    return p.xcd_spread ? spread(b, n) : b;
+    if (p.perm) return __builtin_amdgcn_readfirstlane(p.perm[b]);
+    if (!p.xcd_spread) return b;
+    const int x = b & 7;
+    return x * p.spread_a + min(x, p.spread_r) + (b >> 3);
 }
 
-// Origin of tile `tile` of one batch entry's tile grid.
+// Origin of tile `tile` of one batch entry's tile grid, by the launch's
+// division constants.
+__device__ __forceinline__ void tile_origin_fast(const KParams &p, int tile, int &m0, int &n0) {
+    const int gm_full = p.group_m > 0 ? p.group_m : p.tiles_m;
+    const int g = fdiv(tile, p.d_band);
+    const int first = g * gm_full;
+    const bool last = p.tiles_m - first < gm_full;
+    const int gm = last ? p.tiles_m - first : gm_full;
+    const int w = tile - g * gm_full * p.tiles_n;
+    const int col = fdiv(w, last ? p.d_rows_last : p.d_rows);
+    m0 = (first + w - col * gm) * p.tm;
+    n0 = col * BN;
+}
+
+// The same for any tile grid (a grouped call's problems have grids of their own).
 __device__ __forceinline__ void tile_origin(const KParams &p, int tile, int &m0, int &n0) {
     const int gm_full = p.group_m > 0 ? p.group_m : p.tiles_m;
     const int per_group = gm_full * p.tiles_n;
@@ -760,12 +778,11 @@ template <bool GRP = false>
 __device__ __forceinline__ KParams tile_view(const KParams &p, int tile, int &m0, int &n0) {
     if constexpr (GRP) return group_view(p, tile, m0, n0);
     if (p.batch <= 1) {
-        tile_origin(p, tile, m0, n0);
+        tile_origin_fast(p, tile, m0, n0);
         return p;
     }
-    const int tpb = p.tiles_m * p.tiles_n;
-    const int b = tile / tpb;
-    tile_origin(p, tile - b * tpb, m0, n0);
+    const int b = fdiv(tile, p.d_entry);
+    tile_origin_fast(p, tile - b * p.tiles_m * p.tiles_n, m0, n0);
     return batch_entry(p, b);
 }
 
@@ -1351,7 +1368,7 @@ template <int DT, int BL, int NS, int NW, int TM = 128, bool GRP = false>
 __global__ __launch_bounds__(64 * NW) void gemm_dp(KParams p) {
     __shared__ __attribute__((aligned(16))) char lds[lds_bytes<TM>(NS)];
     const WgClock clk(p);
-    const int w = worker_of(p, p.ntiles);
+    const int w = worker_of(p);
     const int tile = p.tile_base + w;
     int m0, n0;
     const KParams q = tile_view<GRP>(p, tile, m0, n0);
@@ -1639,7 +1656,7 @@ __global__ __launch_bounds__(64 * G_NW) void gemm_dp_group(KParams p) {
     __shared__ __attribute__((aligned(16))) char lds[G_NS * 2 * G_SLAB];
     constexpr int JB = GAcc<G_NW>::JB;
     const WgClock clk(p);
-    const int g = worker_of(p, p.ntiles);
+    const int g = worker_of(p);
     // groups are numbered batch after batch, gpb per batch entry
     const int gpb = ((p.tiles_m + 1) / 2) * ((p.tiles_n + 1) / 2);
     const int b = p.batch > 1 ? g / gpb : 0;
@@ -1738,9 +1755,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk(KParams p0) {
     __shared__ int last_arriver;
     const WgClock clk(p0);
     const int S = p0.splits;
-    const int w = worker_of(p0, p0.ntiles * S);
-    const int tile = w / S, s = w % S;
-    const int k0 = (int)((int64_t)s * p0.ipt / S), k1 = (int)((int64_t)(s + 1) * p0.ipt / S);
+    const int w = worker_of(p0);
+    const int tile = fdiv(w, p0.d_splits), s = w - tile * S;
+    // S divides the iterations in every plan (aligned split); the general
+    // bounds [s P / S, (s + 1) P / S) otherwise
+    const int chunk = fdiv(p0.ipt, p0.d_splits);
+    const bool aligned = chunk * S == p0.ipt;
+    const int k0 = aligned ? s * chunk : (int)((int64_t)s * p0.ipt / S);
+    const int k1 = aligned ? k0 + chunk : (int)((int64_t)(s + 1) * p0.ipt / S);
     int m0, n0;
     const KParams p = tile_view<GRP>(p0, tile, m0, n0);   // the tile's batch entry
     AccT<TM> acc;
@@ -2067,7 +2089,7 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
     const int ts = blockIdx.x / bpt;
     const int f = (blockIdx.x % bpt) * RED_THREADS + threadIdx.x;
     const int tb = ts * p.ipt, tile_end = tb + p.ipt;
-    const int owner = unit_of(tb, p.q, p.big);
+    const int owner = unit_of(p, tb);
     if (unit_start(owner, p.q, p.big) + p.q + (owner < p.big ? 1 : 0) >= tile_end) return;   // whole tile
     int vend = owner + 1;
     while (vend < p.units && unit_start(vend, p.q, p.big) < tile_end) ++vend;
@@ -2144,7 +2166,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
     constexpr bool EARLY = !EPI && !ATOMIC && TM <= 128;
     __shared__ __attribute__((aligned(16))) char lds[lds_bytes<TM>(NS)];
     const WgClock clk(p);
-    const int u = worker_of(p, p.units);
+    const int u = worker_of(p);
     const int ipt = p.ipt;
     const int begin = unit_start(u, p.q, p.big);
     const int end = begin + p.q + (u < p.big ? 1 : 0);
@@ -2165,7 +2187,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
     int nseg = 0;
     uint32_t *pending = nullptr;   // a published partial whose flag rises in the next segment's loop
     for (int pos = begin; pos < end;) {
-        const int ts = pos / ipt;                // tile index within the Stream-K part
+        const int ts = fdiv(pos, p.d_ipt);       // tile index within the Stream-K part
         const int tb = ts * ipt;
         const int k0 = pos - tb;
         const int k1 = min(end - tb, ipt);
@@ -2173,8 +2195,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         int m0, n0;
         const KParams pv = tile_view<GRP>(p, tile, m0, n0);   // the tile's batch entry
         const int role = k0 > 0 ? 2 : (k1 == ipt ? 0 : 1);
-        const int owner = unit_of(tb, p.q, p.big);
-        const int rot = (tb - unit_start(owner, p.q, p.big)) % ipt;
+        const int owner = unit_of(p, tb);
+        const int since = tb - unit_start(owner, p.q, p.big);   // the owner's iterations before this tile
+        const int rot = since - fdiv(since, p.d_ipt) * ipt;
         // a turnstile owner's first peer is always unit u + 1, which published
         // its partial at the end of its first segment, usually long before this
         // owner's segment ends
@@ -2418,6 +2441,32 @@ KernelFn kernel_for(int dtype, int blayout, int kmode, bool epi, int tm, bool gr
     return nullptr;
 }
 
+FastDiv fast_div(int64_t d) {
+    if (d < 1) d = 1;   // a divisor the launch does not use
+    uint32_t s = 0;
+    while ((int64_t(1) << s) < d) ++s;
+    const uint64_t m = ((uint64_t(1) << (32 + s)) + uint64_t(d) - 1) / uint64_t(d);   // in [2^32, 2^33)
+    return FastDiv{uint32_t(m - (uint64_t(1) << 32)), s};
+}
+
+// The launch constants of the index arithmetic, for a launch of `grid` workers.
+KParams with_divisors(const KParams &p, int grid) {
+    KParams q = p;
+    const int gm_full = p.group_m > 0 ? p.group_m : p.tiles_m;
+    const int bands = gm_full > 0 ? (p.tiles_m + gm_full - 1) / gm_full : 1;
+    q.d_band = fast_div(int64_t(gm_full) * p.tiles_n);
+    q.d_rows = fast_div(gm_full);
+    q.d_rows_last = fast_div(p.tiles_m - (bands - 1) * gm_full);
+    q.d_entry = fast_div(int64_t(p.tiles_m) * p.tiles_n);
+    q.d_ipt = fast_div(p.ipt);
+    q.d_q = fast_div(std::max(p.q, 1));
+    q.d_q1 = fast_div(int64_t(p.q) + 1);
+    q.d_splits = fast_div(p.splits);
+    q.spread_a = grid / 8;
+    q.spread_r = grid % 8;
+    return q;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParams &p,
@@ -2425,7 +2474,7 @@ hipError_t launch_gemm(int dtype, int blayout, int kmode, int grid, const KParam
     Shape shape{0, 0};
     KernelFn fn = kernel_for(dtype, blayout, kmode, p.epi != EPI_PLAIN, p.tm, p.ngroups > 0, shape);
     if (!fn || grid <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * shape.nw), 0, stream, p);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * shape.nw), 0, stream, with_divisors(p, grid));
     return hipGetLastError();
 }
 
@@ -2433,29 +2482,31 @@ hipError_t launch_splitk_reduce(const KParams &p, hipStream_t stream) {
     const int64_t tiles = (int64_t)std::max(p.batch, 1) * p.tiles_m * p.tiles_n;   // every batch entry's tiles
     if (tiles <= 0) return hipSuccess;
     // a separate build with the epilogue keeps the plain one's code unchanged
+    const KParams q = with_divisors(p, 0);
     if (p.ngroups > 0)
         hipLaunchKernelGGL((splitk_reduce<false, true>), dim3((unsigned)(tiles * red_blocks_per_tile(p.tm))),
-                           dim3(RED_THREADS), 0, stream, p);
+                           dim3(RED_THREADS), 0, stream, q);
     else if (p.epi != EPI_PLAIN)
         hipLaunchKernelGGL(splitk_reduce<true>, dim3((unsigned)(tiles * red_blocks_per_tile(p.tm))), dim3(RED_THREADS), 0,
-                           stream, p);
+                           stream, q);
     else
         hipLaunchKernelGGL(splitk_reduce<false>, dim3((unsigned)(tiles * red_blocks_per_tile(p.tm))), dim3(RED_THREADS), 0,
-                           stream, p);
+                           stream, q);
     return hipGetLastError();
 }
 
 hipError_t launch_streamk_reduce(const KParams &p, int64_t sk_tiles, hipStream_t stream) {
     if (sk_tiles <= 0) return hipSuccess;
+    const KParams q = with_divisors(p, 0);
     if (p.ngroups > 0)
         hipLaunchKernelGGL((streamk_reduce<false, true>), dim3((unsigned)(sk_tiles * red_blocks_per_tile(p.tm))),
-                           dim3(RED_THREADS), 0, stream, p);
+                           dim3(RED_THREADS), 0, stream, q);
     else if (p.epi != EPI_PLAIN)
         hipLaunchKernelGGL(streamk_reduce<true>, dim3((unsigned)(sk_tiles * red_blocks_per_tile(p.tm))), dim3(RED_THREADS),
-                           0, stream, p);
+                           0, stream, q);
     else
         hipLaunchKernelGGL(streamk_reduce<false>, dim3((unsigned)(sk_tiles * red_blocks_per_tile(p.tm))), dim3(RED_THREADS),
-                           0, stream, p);
+                           0, stream, q);
     return hipGetLastError();
 }
 

@@ -60,6 +60,17 @@ static_assert(sizeof(GroupDesc) == 48, "device table entry");
 // Problems per grouped call: one wave's lanes find a tile's problem at once.
 constexpr int MAX_GROUPS = 64;
 
+// Division by a launch constant d (1 <= d <= 2^31) of an index n in
+// [0, 2^31) without a divide sequence: with s = ceil(log2 d) and
+// m = ceil(2^(32+s) / d) (so 2^32 <= m < 2^33), floor(n / d) =
+// floor(n m / 2^(32+s)) = (umulhi(n, m - 2^32) + n) >> s.  Exact: the error
+// of m, m d - 2^(32+s), is below d <= 2^s, so n m / 2^(32+s) exceeds n / d by
+// less than n / 2^(32+s) < 1 / (2 d), which cannot reach the next integer.
+struct FastDiv {
+    uint32_t m;   // m - 2^32
+    uint32_t s;
+};
+
 struct KParams {
     const uint16_t *A;     // [M,K] row-major 16-bit operands
     const uint16_t *B;     // [K,N] or [N,K] row-major
@@ -97,6 +108,16 @@ struct KParams {
     long long *timing;     // optional per-workgroup {start, end, HW_ID | XCC_ID << 32, cycles, marks}
     int timing_base;       // entry of this launch's workgroup 0
     int trace_maxseg, trace_maxfold, trace_workers, trace_tiles;
+    // launch constants for the kernels' index arithmetic (set by the launch
+    // functions below from the fields above and the grid)
+    FastDiv d_band;        // tiles of a full raster band: group_m (or tiles_m) x tiles_n
+    FastDiv d_rows;        // tile rows of a full band
+    FastDiv d_rows_last;   // tile rows of the last band
+    FastDiv d_entry;       // tiles of one batch entry: tiles_m x tiles_n
+    FastDiv d_ipt;         // k-iterations per tile
+    FastDiv d_q, d_q1;     // Stream-K unit lengths max(q, 1) and q + 1
+    FastDiv d_splits;      // Split-K factor
+    int spread_a, spread_r;  // workers of the launch: per XCD (n / 8) and the remainder (n % 8)
 };
 
 // Launch `grid` workgroups of the kernel for (dtype, B layout, mode) on `stream`.
