@@ -57,7 +57,9 @@ GEMM_TWO_PASS = 0x200
 GEMM_TILE_128x128 = 0x0000
 GEMM_TILE_256x128 = 0x1000
 GEMM_TILE_64x128 = 0x2000
-TILES = {"128x128": GEMM_TILE_128x128, "256x128": GEMM_TILE_256x128, "64x128": GEMM_TILE_64x128}
+GEMM_TILE_AUTO = 0x3000
+TILES = {"128x128": GEMM_TILE_128x128, "256x128": GEMM_TILE_256x128, "64x128": GEMM_TILE_64x128,
+         "auto": GEMM_TILE_AUTO}
 
 GEMM_EPI_ALPHA_BETA = 0x01
 GEMM_EPI_BIAS = 0x02
@@ -335,8 +337,8 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
     device tensors (see gemm_args_t in include/gemm.h).
     Enqueues on ``stream`` (a torch.cuda.Stream) or torch's current stream.
     ``noalloc``: call gemm_ex_noalloc (no workspace argument allowed).
-    ``tile``: "128x128", "256x128" (Stream-K only) or "64x128" (no fused epilogue
-    with Stream-K).
+    ``tile``: "128x128", "256x128" (Stream-K only), "64x128" (no fused epilogue
+    with Stream-K) or "auto" (the library picks one of them, GEMM_TILE_AUTO).
     """
     import torch
 

@@ -34,11 +34,47 @@ int64_t unit_begin(int64_t unit, int64_t q, int64_t big) {
     return unit * q + std::min(unit, big);
 }
 
+constexpr uint32_t kTileBits = GEMM_TILE_256x128 | GEMM_TILE_64x128;
+
+// GEMM_TILE_AUTO (CUTLASS guide, "Tile Size Selection": the tile follows the
+// problem's shape).  Measured on MI355X, each against the 128 x 128 default:
+// 64 x 128 tiles win wherever the 128 x 128 grid has too few tiles to fill half
+// the CUs (256x512x2048 10.7 vs 12.1 us, 96x512x2048 9.5 vs 11.2 us,
+// 128x4096x4096 14.2 vs 18.1 us); 256 x 128 Stream-K tiles halve the L2 -> LDS
+// bytes per flop and win where a unit still runs many iterations
+// (1536^2x16384: 72 per unit, 86.6 vs 91.7 us; 4096x4224x4096: 132 per unit,
+// 130.0 vs 143.1 us) but lose where the fixed cost of a unit's segments
+// dominates (2048x2176x4096: 34 per unit, 47.5 vs 42.4 us).
+uint32_t choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, uint32_t mode, int32_t splits,
+                     int32_t num_cus, bool epilogue) {
+    if ((mode & kTileBits) != GEMM_TILE_AUTO) return mode;
+    const uint32_t base = mode & ~kTileBits;   // 128 x 128
+    const char *why = nullptr;
+    gemm_plan_t p128, p;
+    if (make_plan(M, N, K, batch, layout, base, splits, num_cus, &p128, &why) != GEMM_OK) return base;
+    if (2 * p128.tiles <= num_cus) {
+        const uint32_t skinny = base | GEMM_TILE_64x128;
+        if (make_plan(M, N, K, batch, layout, skinny, splits, num_cus, &p, &why) == GEMM_OK &&
+            !(epilogue && p.decision == GEMM_STREAMK))
+            return skinny;
+        return base;
+    }
+    const uint32_t decomp = base & 0xFu;
+    if (p128.decision == GEMM_STREAMK && !epilogue && !(base & GEMM_TWO_PASS) &&
+        (decomp == GEMM_HEURISTIC || decomp == GEMM_STREAMK)) {
+        const uint32_t tall = (base & ~0xFu) | GEMM_STREAMK | GEMM_TILE_256x128;
+        if (make_plan(M, N, K, batch, layout, tall, splits, num_cus, &p, &why) == GEMM_OK && p.q >= 64) return tall;
+    }
+    return base;
+}
+
 int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, uint32_t mode, int32_t splits,
               int32_t num_cus, gemm_plan_t *out, const char **why) {
     static const char *none = "";
     *why = none;
     if (!out) { *why = "plan output pointer is null"; return GEMM_ERR_INVALID; }
+    if ((mode & kTileBits) == GEMM_TILE_AUTO && num_cus >= 1)
+        mode = choose_tile(M, N, K, batch, layout, mode, splits, num_cus, false);
     std::memset(out, 0, sizeof *out);
     if (M < 0 || N < 0 || K < 0) { *why = "M, N and K must be >= 0"; return GEMM_ERR_INVALID; }
     if (num_cus < 1) { *why = "num_cus must be >= 1"; return GEMM_ERR_INVALID; }
@@ -240,7 +276,9 @@ int make_plan_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint
         *why = "a grouped call takes 1..GEMM_MAX_GROUPS problems";
         return GEMM_ERR_INVALID;
     }
-    const uint32_t tile = mode & (GEMM_TILE_256x128 | GEMM_TILE_64x128);
+    if ((mode & kTileBits) == GEMM_TILE_AUTO && num_cus >= 1)
+        mode = choose_tile_grouped(groups, count, K, layout, mode, splits, num_cus, false);
+    const uint32_t tile = mode & kTileBits;
     if (tile == GEMM_TILE_256x128) {
         *why = "grouped calls run 128- and 64-row tiles (GEMM_TILE_256x128 is not offered)";
         return GEMM_ERR_UNSUPPORTED;
@@ -269,6 +307,23 @@ int make_plan_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint
         out->workspace_bytes = control_bytes(*out) + int64_t(out->splits) * mn * 4;
     out->workspace_bytes = (out->workspace_bytes + 255) / 256 * 256 + group_table_bytes(count);
     return GEMM_OK;
+}
+
+// GEMM_TILE_AUTO for a grouped call: 64 x 128 tiles when the problems' 128 x 128
+// tiles cannot fill half the CUs (the rule of choose_tile without 256 x 128).
+uint32_t choose_tile_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint32_t layout, uint32_t mode,
+                             int32_t splits, int32_t num_cus, bool epilogue) {
+    if ((mode & kTileBits) != GEMM_TILE_AUTO) return mode;
+    const uint32_t base = mode & ~kTileBits;
+    const char *why = nullptr;
+    gemm_plan_t p128, p;
+    if (make_plan_grouped(groups, count, K, layout, base, splits, num_cus, &p128, &why) != GEMM_OK) return base;
+    const uint32_t skinny = base | GEMM_TILE_64x128;
+    if (2 * p128.tiles <= num_cus &&
+        make_plan_grouped(groups, count, K, layout, skinny, splits, num_cus, &p, &why) == GEMM_OK &&
+        !(epilogue && p.decision == GEMM_STREAMK))
+        return skinny;
+    return base;
 }
 
 int64_t control_bytes(const gemm_plan_t &p) {

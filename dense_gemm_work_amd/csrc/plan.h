@@ -19,6 +19,13 @@ int make_plan_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint
                       int32_t splits, int32_t num_cus, gemm_plan_t *out, const char **why);
 int64_t group_table_bytes(int32_t count);
 
+// The mode word with GEMM_TILE_AUTO replaced by the tile it picks for this call
+// (any other mode word comes back unchanged); `epilogue`: the call fuses one.
+uint32_t choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, uint32_t mode, int32_t splits,
+                     int32_t num_cus, bool epilogue);
+uint32_t choose_tile_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint32_t layout, uint32_t mode,
+                             int32_t splits, int32_t num_cus, bool epilogue);
+
 // First flattened iteration of Stream-K unit `unit` ("big" units first).
 int64_t unit_begin(int64_t unit, int64_t q, int64_t big);
 

@@ -131,6 +131,20 @@ extern "C" {
                                       tile groups for data-parallel launches.  Twice the tile
                                       rows of 128 x 128 tiles (M = 128 gives two), half the
                                       partial bytes per split (32 KiB slots).                 */
+#define GEMM_TILE_AUTO     0x3000u /* the library picks one of the three per call (the CUTLASS
+                                      guide's "Tile Size Selection": the tile follows the
+                                      problem's shape).  The choice is fixed per shape, CU
+                                      count and mode, and is taken before planning; gemm_plan
+                                      reports it in bm.  With T = tiles of the 128 x 128 plan
+                                      and C the CUs: 64 x 128 when 2 T <= C (too few tiles to
+                                      fill half the GPU; every decomposition, without a fused
+                                      epilogue where the 64 x 128 plan is Stream-K); else
+                                      256 x 128 Stream-K when the 128 x 128 plan is Stream-K
+                                      (GEMM_HEURISTIC or GEMM_STREAMK; not GEMM_TWO_PASS, no
+                                      fused epilogue) and each unit of the 256 x 128 plan runs
+                                      at least 64 k-iterations, so its fixed cost stays small
+                                      beside its loop; else 128 x 128.  Grouped calls choose
+                                      between 128 x 128 and 64 x 128 only.                    */
 
 /* ---- debug bits for gemm_args_t.debug -------------------------------------------- */
 #define GEMM_DEBUG_NO_PUBLISH 0x1u /* Stream-K contributors store partials but never
@@ -409,7 +423,9 @@ int gemm_plan_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint
 
 /*
  * gemm_plan -- decide the decomposition for a call without running it.
- * num_cus >= 1 (no device is queried).  Fills *out; returns a status.
+ * num_cus >= 1 (no device is queried).  Fills *out; returns a status.  With
+ * GEMM_TILE_AUTO, bm reports the tile picked for a call without a fused
+ * epilogue.
  */
 int gemm_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode,
               int32_t splits, int32_t num_cus, gemm_plan_t *out);
@@ -429,7 +445,9 @@ int gemm_plan_batched(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t l
  * 64 KiB slot and one flag per unit; two slots per unit when a second kernel
  * adds the partials, Case 3's fixup kernel).  Plus a 256-byte status block.
  * Layout: [status 256 B | flags, 256-B aligned | counters, 256-B aligned | data].
- * batch >= 1; num_cus >= 1 (no device is queried).  Returns the byte count
+ * batch >= 1; num_cus >= 1 (no device is queried).  With GEMM_TILE_AUTO the
+ * larger of the two tiles' needs (a call with a fused epilogue may get another
+ * tile than gemm_plan reports).  Returns the byte count
  * (>= 0) or a negative status for arguments gemm_plan_batched rejects.
  * Ownership: the caller allocates, zero-fills once and frees it.
  */

@@ -444,11 +444,82 @@ def test_skinny_tile_doubles_tile_rows_of_a_decode_batch(dg):
     assert (p128.tiles, p64.tiles) == (32, 64)
 
 
-def test_tile_bits_are_exclusive(dg):
+def test_tile_bits_beyond_the_four_shapes_are_refused(dg):
     lw = dg.GEMM_B_KN | dg.GEMM_BF16
-    with pytest.raises(dg.GemmError) as ei:
-        dg.gemm_plan(256, 512, 2048, lw, dg.MODES["streamk"] | dg.GEMM_TILE_256x128 | dg.GEMM_TILE_64x128, 0, 256)
-    assert ei.value.status == dg.GEMM_ERR_INVALID
+    for extra in (0x4000, 0x8000, 0x400):
+        with pytest.raises(dg.GemmError) as ei:
+            dg.gemm_plan(256, 512, 2048, lw, dg.MODES["streamk"] | dg.GEMM_TILE_AUTO | extra, 0, 256)
+        assert ei.value.status == dg.GEMM_ERR_INVALID
+
+
+# (workload, the tile GEMM_TILE_AUTO picks on 256 CUs with the workload's own mode)
+AUTO_CASES = [
+    ("c1_sk32", "64x128"), ("c2a_m96_s8", "64x128"), ("c2b_m256_s2", "64x128"), ("x3_decode", "64x128"),
+    ("c3_wavequant", "128x128"), ("c4_large_dp", "128x128"), ("x2_batched", "128x128"),
+    ("c5_longk_fp16", "256x128"), ("x1_hybrid", "256x128"),
+]
+
+
+@pytest.mark.parametrize("name,tile", AUTO_CASES)
+def test_auto_tile_is_the_plan_of_the_tile_it_picks(dg, name, tile):
+    from workloads import WORKLOADS
+
+    w = WORKLOADS[name]
+    lw = dg.layout_word(w.b_layout, w.dtype)
+    auto = dg.plan_dict(dg.gemm_plan_batched(w.M, w.N, w.K, w.batch, lw, dg.mode_word(w.mode, tile="auto"),
+                                             w.splits, 256))
+    # 256 x 128 tiles run as Stream-K, whatever decomposition the caller asked for
+    mode = "streamk" if tile == "256x128" else w.mode
+    explicit = dg.plan_dict(dg.gemm_plan_batched(w.M, w.N, w.K, w.batch, lw, dg.mode_word(mode, tile=tile),
+                                                 w.splits, 256))
+    assert auto == explicit
+    assert auto["bm"] == int(tile.split("x")[0])
+
+
+def test_auto_tile_rule_edges(dg):
+    lw = dg.GEMM_B_KN | dg.GEMM_BF16
+    auto = dg.mode_word("heuristic", tile="auto")
+
+    def bm(M, N, K, mode=auto, splits=0, cus=256):
+        return dg.gemm_plan(M, N, K, lw, mode, splits, cus).bm
+
+    # 64 x 128 up to 2 T = C: 128 tiles of 128 x 128 on 256 CUs, 129 not
+    assert bm(128 * 16, 128 * 8, 2048) == 64
+    assert bm(128 * 129, 128, 2048) == 128
+    # the same shapes on fewer CUs
+    assert bm(128 * 16, 128 * 8, 2048, cus=255) == 128
+    # 256 x 128 needs a Stream-K 128 x 128 plan and >= 64 iterations per unit of the taller tile:
+    # 1536^2 x 16384 has 72, 1536^2 x 8192 36
+    st = dg.mode_word("streamk", tile="auto")
+    assert bm(1536, 1536, 16384, st) == 256
+    assert bm(1536, 1536, 8192, st) == 128
+    # never with GEMM_TWO_PASS, and not when the 128 x 128 plan is data-parallel or Split-K
+    assert bm(1536, 1536, 16384, dg.mode_word("streamk", two_pass=True, tile="auto")) == 128
+    assert bm(8192, 8192, 8192) == 128
+    assert bm(1536, 1536, 16384, dg.mode_word("dp", tile="auto")) == 128
+    assert bm(1536, 1536, 16384, dg.mode_word("splitk", tile="auto"), splits=2) == 128
+
+
+def test_auto_tile_workspace_covers_a_call_with_an_epilogue(dg):
+    lw = dg.GEMM_B_KN | dg.GEMM_FP16
+    auto = dg.mode_word("streamk", tile="auto")
+    p = dg.gemm_plan(1536, 1536, 16384, lw, auto, 0, 256)
+    p128 = dg.gemm_plan(1536, 1536, 16384, lw, dg.mode_word("streamk"), 0, 256)
+    assert p.bm == 256
+    # with a fused epilogue the call runs 128 x 128 tiles; the size covers both
+    size = dg.gemm_workspace_size(1536, 1536, 16384, lw, auto, 0, 256)
+    assert size == max(p.workspace_bytes, p128.workspace_bytes)
+
+
+def test_auto_tile_grouped(dg):
+    lw = dg.GEMM_B_NK | dg.GEMM_BF16
+    small = [(96, 512), (64, 1024), (17, 512)]        # 10 tiles of 128 x 128
+    p = dg.gemm_plan_grouped(small, 2048, lw, dg.mode_word("heuristic", tile="auto"), 0, 256)
+    q = dg.gemm_plan_grouped(small, 2048, lw, dg.mode_word("heuristic", tile="64x128"), 0, 256)
+    assert dg.plan_dict(p) == dg.plan_dict(q) and p.bm == 64
+    big = [(2048, 2048)] * 4                          # 1024 tiles
+    p = dg.gemm_plan_grouped(big, 2048, lw, dg.mode_word("streamk", tile="auto"), 0, 256)
+    assert p.bm == 128
 
 
 GROUP_SETS = [
