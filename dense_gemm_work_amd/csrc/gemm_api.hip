@@ -301,7 +301,7 @@ int run(const gemm_args_t &a, bool noalloc = false, const gemm_group_t *groups =
         // GEMM_TILE_AUTO picks the tile here, where the fused epilogue is known
         const bool epi = a.epilogue != 0;
         if (groups) {
-            const uint32_t mode = dgw::choose_tile_grouped(groups, ngroups, a.K, a.layout, a.mode, a.splits, cus, epi);
+            const uint32_t mode = dgw::choose_tile_grouped(groups, ngroups, a.K, a.layout, a.mode, a.splits, cus);
             return dgw::make_plan_grouped(groups, ngroups, a.K, a.layout, mode, a.splits, cus, &p, &why);
         }
         const uint32_t mode = dgw::choose_tile(a.M, a.N, a.K, batch, a.layout, a.mode, a.splits, cus, epi);
@@ -345,8 +345,6 @@ int run(const gemm_args_t &a, bool noalloc = false, const gemm_group_t *groups =
     const int shape = p.bm == GEMM_BM ? 0 : (p.bm > GEMM_BM ? 1 : 2);
     if (shape == 1 && a.epilogue != 0)
         return fail(GEMM_ERR_UNSUPPORTED, "GEMM_TILE_256x128 has no fused epilogue");
-    if (shape == 2 && a.epilogue != 0 && p.decision == GEMM_STREAMK)
-        return fail(GEMM_ERR_UNSUPPORTED, "GEMM_TILE_64x128 has no fused epilogue with Stream-K");
 
     if (a.K == 0 && groups) {   // the empty sums: every problem's C := 0
         for (int32_t g = 0; g < ngroups; ++g)

@@ -2158,7 +2158,7 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
 // ---------------------------------------------------------------------------
 template <int DT, int BL, int NS, int NW, bool ATOMIC, bool EPI, int TM = 128, bool GRP = false>
 __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
-    static_assert(!EPI || TM == 128, "the fused epilogue serves 128-row tiles");
+    static_assert(!EPI || TM <= 128, "the fused epilogue serves 64- and 128-row tiles");
     constexpr int SLOT = TM * BN;              // floats of one partial slot
     // turnstile owners load their first peer's partial before the k-half merge
     // (not in the epilogue build, whose C prefetch holds those registers, nor for
@@ -2227,8 +2227,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
                 if (early) load_slot<NW, TM>(p.part + (size_t)(u + 1) * SLOT, early_part);
             }
         }
+        // (128-row tiles; a 64-row tile loads them when it stores)
         float pre_c[32], pre_b[2];
-        if constexpr (EPI) {
+        if constexpr (EPI && TM == 128) {
             static_assert(NW == 8, "the prefetch assumes one 32-row block per wave");
             if (stores_c && p.epi != EPI_PLAIN) epi_prefetch(pv, m0, n0, pre_c, pre_b);
         }
@@ -2285,8 +2286,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
         // site (one inlined copy of the epilogue code)
         if constexpr (EPI) {
             if (stores_c) {
-                if (p.epi == EPI_PLAIN) store_tile<NW>(pv.C, m0, n0, pv.M, pv.N, t);
-                else finish_block<NW>(pv, m0, n0, t, 0, pre_c, pre_b);
+                if constexpr (TM == 128) {
+                    if (p.epi == EPI_PLAIN) store_tile<NW>(pv.C, m0, n0, pv.M, pv.N, t);
+                    else finish_block<NW>(pv, m0, n0, t, 0, pre_c, pre_b);
+                } else {
+                    store_final<NW, true, TM>(pv, m0, n0, t);
+                }
             }
         }
         clk.mark(p, 2 * min(nseg - 1, 1) + 1);
@@ -2400,14 +2405,15 @@ KernelFn pick(int kmode, bool epi, int tm, Shape &shape) {
     }
     if (tm == 64) {
         // the skinny 64 x 128 tile: four waves of 32 x 64 over every k-step, three
-        // stages of (8 KiB A + 16 KiB B), so two workgroups share a CU; the
-        // epilogue in the data-parallel and Split-K builds, not in Stream-K
+        // stages of (8 KiB A + 16 KiB B), so two workgroups share a CU; Stream-K
+        // has a separate build with the epilogue, like the 128-row tile
         shape = {3, 4};
         switch (kmode) {
         case K_DP: return gemm_dp<DT, BL, 3, 4, 64>;
         case K_SPLITK: return gemm_splitk<DT, BL, 3, 4, 64>;
-        case K_SK: return epi ? nullptr : gemm_streamk<DT, BL, 3, 4, false, false, 64>;
-        case K_SK_ATOMIC: return epi ? nullptr : gemm_streamk<DT, BL, 3, 4, true, false, 64>;
+        case K_SK: return epi ? gemm_streamk<DT, BL, 3, 4, false, true, 64> : gemm_streamk<DT, BL, 3, 4, false, false, 64>;
+        case K_SK_ATOMIC:
+            return epi ? gemm_streamk<DT, BL, 3, 4, true, true, 64> : gemm_streamk<DT, BL, 3, 4, true, false, 64>;
         default: return nullptr;
         }
     }
@@ -2536,10 +2542,10 @@ hipError_t launch_zero(void *ptr, int64_t n_words, hipStream_t stream) {
 
 hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int tm, bool grp, int *out) {
     // the smaller of the builds with and without the epilogue (the 256-row tile
-    // has no epilogue build, the 64-row tile's plain build serves both, grouped
-    // builds have none)
+    // and the grouped builds have no epilogue build; for the data-parallel and
+    // Split-K kernels both lookups give the one build that serves both)
     int best = 1 << 30;
-    for (int epi = 0; epi < (tm == 128 && !grp ? 2 : 1); ++epi) {
+    for (int epi = 0; epi < (tm <= 128 && !grp ? 2 : 1); ++epi) {
         Shape shape{0, 0};
         KernelFn fn = kernel_for(dtype, blayout, kmode, epi != 0, tm, grp, shape);
         if (!fn) return hipErrorInvalidValue;

@@ -54,10 +54,7 @@ uint32_t choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t la
     if (make_plan(M, N, K, batch, layout, base, splits, num_cus, &p128, &why) != GEMM_OK) return base;
     if (2 * p128.tiles <= num_cus) {
         const uint32_t skinny = base | GEMM_TILE_64x128;
-        if (make_plan(M, N, K, batch, layout, skinny, splits, num_cus, &p, &why) == GEMM_OK &&
-            !(epilogue && p.decision == GEMM_STREAMK))
-            return skinny;
-        return base;
+        return make_plan(M, N, K, batch, layout, skinny, splits, num_cus, &p, &why) == GEMM_OK ? skinny : base;
     }
     const uint32_t decomp = base & 0xFu;
     if (p128.decision == GEMM_STREAMK && !epilogue && !(base & GEMM_TWO_PASS) &&
@@ -277,7 +274,7 @@ int make_plan_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint
         return GEMM_ERR_INVALID;
     }
     if ((mode & kTileBits) == GEMM_TILE_AUTO && num_cus >= 1)
-        mode = choose_tile_grouped(groups, count, K, layout, mode, splits, num_cus, false);
+        mode = choose_tile_grouped(groups, count, K, layout, mode, splits, num_cus);
     const uint32_t tile = mode & kTileBits;
     if (tile == GEMM_TILE_256x128) {
         *why = "grouped calls run 128- and 64-row tiles (GEMM_TILE_256x128 is not offered)";
@@ -309,10 +306,10 @@ int make_plan_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint
     return GEMM_OK;
 }
 
-// GEMM_TILE_AUTO for a grouped call: 64 x 128 tiles when the problems' 128 x 128
-// tiles cannot fill half the CUs (the rule of choose_tile without 256 x 128).
+// GEMM_TILE_AUTO for a grouped call (no epilogue, no 256-row tiles): 64 x 128
+// tiles when the problems' 128 x 128 tiles cannot fill half the CUs.
 uint32_t choose_tile_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint32_t layout, uint32_t mode,
-                             int32_t splits, int32_t num_cus, bool epilogue) {
+                             int32_t splits, int32_t num_cus) {
     if ((mode & kTileBits) != GEMM_TILE_AUTO) return mode;
     const uint32_t base = mode & ~kTileBits;
     const char *why = nullptr;
@@ -320,8 +317,7 @@ uint32_t choose_tile_grouped(const gemm_group_t *groups, int32_t count, int64_t 
     if (make_plan_grouped(groups, count, K, layout, base, splits, num_cus, &p128, &why) != GEMM_OK) return base;
     const uint32_t skinny = base | GEMM_TILE_64x128;
     if (2 * p128.tiles <= num_cus &&
-        make_plan_grouped(groups, count, K, layout, skinny, splits, num_cus, &p, &why) == GEMM_OK &&
-        !(epilogue && p.decision == GEMM_STREAMK))
+        make_plan_grouped(groups, count, K, layout, skinny, splits, num_cus, &p, &why) == GEMM_OK)
         return skinny;
     return base;
 }

@@ -24,7 +24,7 @@ int64_t group_table_bytes(int32_t count);
 uint32_t choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, uint32_t mode, int32_t splits,
                      int32_t num_cus, bool epilogue);
 uint32_t choose_tile_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint32_t layout, uint32_t mode,
-                             int32_t splits, int32_t num_cus, bool epilogue);
+                             int32_t splits, int32_t num_cus);
 
 // First flattened iteration of Stream-K unit `unit` ("big" units first).
 int64_t unit_begin(int64_t unit, int64_t q, int64_t big);

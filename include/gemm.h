@@ -126,8 +126,7 @@ extern "C" {
                                       tiles when N is much larger than M; the book chapter's
                                       skinny-problem paragraph: a decode batch of M = 128 has
                                       too few 128-row tiles to fill the GPU).  Every
-                                      decomposition and merge; with GEMM_STREAMK (also when
-                                      the heuristic picks it) no fused epilogue, and no 2x2
+                                      decomposition, merge and fused epilogue; no 2x2
                                       tile groups for data-parallel launches.  Twice the tile
                                       rows of 128 x 128 tiles (M = 128 gives two), half the
                                       partial bytes per split (32 KiB slots).                 */
@@ -137,8 +136,7 @@ extern "C" {
                                       count and mode, and is taken before planning; gemm_plan
                                       reports it in bm.  With T = tiles of the 128 x 128 plan
                                       and C the CUs: 64 x 128 when 2 T <= C (too few tiles to
-                                      fill half the GPU; every decomposition, without a fused
-                                      epilogue where the 64 x 128 plan is Stream-K); else
+                                      fill half the GPU; every decomposition); else
                                       256 x 128 Stream-K when the 128 x 128 plan is Stream-K
                                       (GEMM_HEURISTIC or GEMM_STREAMK; not GEMM_TWO_PASS, no
                                       fused epilogue) and each unit of the 256 x 128 plan runs

@@ -1,7 +1,7 @@
 """GEMM_TILE_AUTO on the GPU, through the C ABI: a call with tile "auto" runs the
 plan of the tile the library picks (the same bits as a call that names that
 tile), its output matches the fp64 oracle, and with a fused epilogue it falls
-back to 128 x 128 tiles where the picked tile has no epilogue build."""
+back from 256 x 128 tiles, which have no epilogue build, to 128 x 128."""
 import pytest
 import torch
 
@@ -65,7 +65,7 @@ def test_auto_runs_the_picked_tile(dg, w, tile):
 
 @pytest.mark.parametrize("w,expect", [
     (LONG_K, "128x128"),                   # 256 x 128 has no epilogue build
-    (WORKLOADS["c1_sk32"], "128x128"),     # its 64 x 128 plan is Stream-K: no epilogue build
+    (WORKLOADS["c1_sk32"], "64x128"),      # 64 x 128 Stream-K fuses the epilogue
     (WORKLOADS["c2a_m96_s8"], "64x128"),   # 64 x 128 Split-K fuses the epilogue
 ], ids=["c5_longk_fp16", "c1_sk32", "c2a_m96_s8"])
 def test_auto_with_an_epilogue_takes_a_tile_that_has_one(dg, w, expect):

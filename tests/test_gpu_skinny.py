@@ -260,8 +260,12 @@ def test_skinny_zero_partial_control(dg, name, mode, splits, extra):
         assert ok != control
 
 
-@pytest.mark.parametrize("mode,splits,extra", [("dp", 0, {}), ("splitk", 8, {}), ("splitk", 8, {"two_pass": True}),
-                                               ("splitk", 8, {"atomic": True})])
+@pytest.mark.parametrize("mode,splits,extra", [
+    ("dp", 0, {}), ("splitk", 8, {}), ("splitk", 8, {"two_pass": True}), ("splitk", 8, {"atomic": True}),
+    # 8 tiles x 32 iterations: 12 units split every tile over at most three (the turnstile), 24 units over
+    # four (the second kernel adds them), 20 units with atomics
+    ("streamk", 12, {}), ("streamk", 24, {}), ("streamk", 12, {"two_pass": True}), ("streamk", 20, {"atomic": True}),
+    ("heuristic", 0, {})])
 def test_skinny_epilogue(dg, mode, splits, extra):
     w = _w(96, 512, 2048, "nk", "bf16", name="skinny-epi")
     A, B = make_operands(w)
@@ -285,16 +289,22 @@ def test_skinny_epilogue(dg, mode, splits, extra):
     assert ok, f"outside the epilogue bound: worst ratio {worst} at {idx}"
 
 
-def test_skinny_streamk_refuses_epilogue(dg):
-    w = WORKLOADS["c1_sk32"]
-    a = torch.zeros((w.M, w.K), dtype=torch.bfloat16, device=DEV)
-    b = torch.zeros((w.K, w.N), dtype=torch.bfloat16, device=DEV)
-    c = torch.full((w.M, w.N), 7.0, dtype=torch.float32, device=DEV)
-    with pytest.raises(dg.GemmError) as ei:
-        dg.gemm_tensors(a, b, c, mode="streamk", splits=8, tile=SKINNY, alpha=2.0)
-    assert ei.value.status == dg.GEMM_ERR_UNSUPPORTED
-    torch.cuda.synchronize()
-    assert torch.all(c == 7.0)
+def test_skinny_streamk_epilogue_is_deterministic(dg):
+    # the turnstile and the second kernel give the same bits with the epilogue,
+    # in any unit order, run after run
+    w = _w(96, 512, 2048, "nk", "bf16", name="skinny-epi-bits")
+    A, B = make_operands(w)
+    a, b = A.to(DEV), B.to(DEV)
+    c_in, bias = make_epilogue_inputs(w.M, w.N)
+    epi = dict(alpha=0.75, beta=-0.5, bias=bias.to(DEV), act="relu")
+    outs = []
+    for extra in ({}, {"two_pass": True}, {}, {"unit_perm": torch.arange(11, -1, -1, dtype=torch.int32, device=DEV)}):
+        c = c_in.to(DEV).clone()
+        dg.gemm_tensors(a, b, c, b_layout=w.b_layout, mode="streamk", splits=12, tile=SKINNY, **epi, **extra)
+        assert dg.gemm_sync_status() == 0, dg.gemm_last_error()
+        outs.append(c.view(torch.int32).clone())
+    for o in outs[1:]:
+        assert torch.equal(outs[0], o)
 
 
 @pytest.mark.parametrize("name,mode,splits,extra", [
