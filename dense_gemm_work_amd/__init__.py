@@ -337,8 +337,8 @@ def gemm_tensors(a, b, c, b_layout: str = "kn", mode: str = "heuristic", splits:
     device tensors (see gemm_args_t in include/gemm.h).
     Enqueues on ``stream`` (a torch.cuda.Stream) or torch's current stream.
     ``noalloc``: call gemm_ex_noalloc (no workspace argument allowed).
-    ``tile``: "128x128", "256x128" (Stream-K only, no fused epilogue), "64x128" or
-    "auto" (the library picks one of them, GEMM_TILE_AUTO).
+    ``tile``: "128x128", "256x128" (Stream-K only), "64x128" or "auto" (the library
+    picks one of them, GEMM_TILE_AUTO).
     """
     import torch
 

@@ -298,14 +298,8 @@ int run(const gemm_args_t &a, bool noalloc = false, const gemm_group_t *groups =
     // plan first with a placeholder CU count so argument errors surface before any HIP call
     const int64_t batch = a.batch > 1 ? a.batch : 1;
     auto plan_for = [&](int32_t cus) {
-        // GEMM_TILE_AUTO picks the tile here, where the fused epilogue is known
-        const bool epi = a.epilogue != 0;
-        if (groups) {
-            const uint32_t mode = dgw::choose_tile_grouped(groups, ngroups, a.K, a.layout, a.mode, a.splits, cus);
-            return dgw::make_plan_grouped(groups, ngroups, a.K, a.layout, mode, a.splits, cus, &p, &why);
-        }
-        const uint32_t mode = dgw::choose_tile(a.M, a.N, a.K, batch, a.layout, a.mode, a.splits, cus, epi);
-        return dgw::make_plan(a.M, a.N, a.K, batch, a.layout, mode, a.splits, cus, &p, &why);
+        return groups ? dgw::make_plan_grouped(groups, ngroups, a.K, a.layout, a.mode, a.splits, cus, &p, &why)
+                      : dgw::make_plan(a.M, a.N, a.K, batch, a.layout, a.mode, a.splits, cus, &p, &why);
     };
     int rc = plan_for(a.num_cus > 0 ? a.num_cus : 256);
     if (rc != GEMM_OK) return fail(rc, why);
@@ -343,8 +337,6 @@ int run(const gemm_args_t &a, bool noalloc = false, const gemm_group_t *groups =
     const int blayout = (a.layout & 0xFu) == GEMM_B_NK ? 1 : 0;
     // tile shape: 0 = 128 x 128, 1 = 256 x 128, 2 = 64 x 128
     const int shape = p.bm == GEMM_BM ? 0 : (p.bm > GEMM_BM ? 1 : 2);
-    if (shape == 1 && a.epilogue != 0)
-        return fail(GEMM_ERR_UNSUPPORTED, "GEMM_TILE_256x128 has no fused epilogue");
 
     if (a.K == 0 && groups) {   // the empty sums: every problem's C := 0
         for (int32_t g = 0; g < ngroups; ++g)
@@ -666,16 +658,8 @@ int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t batch, uint
     const char *why = "";
     int rc = dgw::make_plan(M, N, K, batch, layout, mode, splits, num_cus, &p, &why);
     if (rc != GEMM_OK) return fail(rc, why);
-    int64_t bytes = p.workspace_bytes;
-    if ((mode & (GEMM_TILE_256x128 | GEMM_TILE_64x128)) == GEMM_TILE_AUTO && num_cus >= 1) {
-        // a call with a fused epilogue may get another tile: enough for either
-        const uint32_t with_epi = dgw::choose_tile(M, N, K, batch, layout, mode, splits, num_cus, true);
-        if ((rc = dgw::make_plan(M, N, K, batch, layout, with_epi, splits, num_cus, &p, &why)) != GEMM_OK)
-            return fail(rc, why);
-        bytes = std::max(bytes, p.workspace_bytes);
-    }
     g_err.clear();
-    return bytes;
+    return p.workspace_bytes;
 }
 
 int gemm_set_stream(void *stream) {

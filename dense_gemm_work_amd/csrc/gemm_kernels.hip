@@ -1057,7 +1057,6 @@ __device__ __forceinline__ void finish_block(const KParams &p, int m0, int n0, c
 // before the first store.
 template <int NW, bool EPI = true, int TM = 128>
 __device__ __forceinline__ void store_final(const KParams &p, int m0, int n0, const Tile<NW, TM> &t) {
-    static_assert(!EPI || TM <= 128, "the fused epilogue serves 64- and 128-row tiles");
     if constexpr (!EPI) {
         store_tile<NW>(p.C, m0, n0, p.M, p.N, t);
     } else {
@@ -2158,7 +2157,6 @@ __global__ __launch_bounds__(RED_THREADS) void streamk_reduce(KParams p) {
 // ---------------------------------------------------------------------------
 template <int DT, int BL, int NS, int NW, bool ATOMIC, bool EPI, int TM = 128, bool GRP = false>
 __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
-    static_assert(!EPI || TM <= 128, "the fused epilogue serves 64- and 128-row tiles");
     constexpr int SLOT = TM * BN;              // floats of one partial slot
     // turnstile owners load their first peer's partial before the k-half merge
     // (not in the epilogue build, whose C prefetch holds those registers, nor for
@@ -2227,7 +2225,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_streamk(KParams p) {
                 if (early) load_slot<NW, TM>(p.part + (size_t)(u + 1) * SLOT, early_part);
             }
         }
-        // (128-row tiles; a 64-row tile loads them when it stores)
+        // (128-row tiles; 64- and 256-row tiles load them when they store)
         float pre_c[32], pre_b[2];
         if constexpr (EPI && TM == 128) {
             static_assert(NW == 8, "the prefetch assumes one 32-row block per wave");
@@ -2395,12 +2393,13 @@ KernelFn pick_grouped(int kmode, bool epi, int tm, Shape &shape) {
 template <int DT, int BL>
 KernelFn pick(int kmode, bool epi, int tm, Shape &shape) {
     if (tm == 256) {
-        // the 256 x 128 tile: three stages of (32 KiB A + 16 KiB B), Stream-K only,
-        // no fused epilogue
-        if (epi) return nullptr;
+        // the 256 x 128 tile: three stages of (32 KiB A + 16 KiB B), Stream-K
+        // only, a separate build with the epilogue
         shape = {3, 8};
-        if (kmode == K_SK) return gemm_streamk<DT, BL, 3, 8, false, false, 256>;
-        if (kmode == K_SK_ATOMIC) return gemm_streamk<DT, BL, 3, 8, true, false, 256>;
+        if (kmode == K_SK)
+            return epi ? gemm_streamk<DT, BL, 3, 8, false, true, 256> : gemm_streamk<DT, BL, 3, 8, false, false, 256>;
+        if (kmode == K_SK_ATOMIC)
+            return epi ? gemm_streamk<DT, BL, 3, 8, true, true, 256> : gemm_streamk<DT, BL, 3, 8, true, false, 256>;
         return nullptr;
     }
     if (tm == 64) {
@@ -2541,11 +2540,11 @@ hipError_t launch_zero(void *ptr, int64_t n_words, hipStream_t stream) {
 }
 
 hipError_t blocks_per_cu(int dtype, int blayout, int kmode, int tm, bool grp, int *out) {
-    // the smaller of the builds with and without the epilogue (the 256-row tile
-    // and the grouped builds have no epilogue build; for the data-parallel and
-    // Split-K kernels both lookups give the one build that serves both)
+    // the smaller of the builds with and without the epilogue (the grouped
+    // builds have no epilogue build; for the data-parallel and Split-K kernels
+    // both lookups give the one build that serves both)
     int best = 1 << 30;
-    for (int epi = 0; epi < (tm <= 128 && !grp ? 2 : 1); ++epi) {
+    for (int epi = 0; epi < (grp ? 1 : 2); ++epi) {
         Shape shape{0, 0};
         KernelFn fn = kernel_for(dtype, blayout, kmode, epi != 0, tm, grp, shape);
         if (!fn) return hipErrorInvalidValue;

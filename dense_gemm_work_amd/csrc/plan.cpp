@@ -46,7 +46,7 @@ constexpr uint32_t kTileBits = GEMM_TILE_256x128 | GEMM_TILE_64x128;
 // 130.0 vs 143.1 us) but lose where the fixed cost of a unit's segments
 // dominates (2048x2176x4096: 34 per unit, 47.5 vs 42.4 us).
 uint32_t choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, uint32_t mode, int32_t splits,
-                     int32_t num_cus, bool epilogue) {
+                     int32_t num_cus) {
     if ((mode & kTileBits) != GEMM_TILE_AUTO) return mode;
     const uint32_t base = mode & ~kTileBits;   // 128 x 128
     const char *why = nullptr;
@@ -57,7 +57,7 @@ uint32_t choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t la
         return make_plan(M, N, K, batch, layout, skinny, splits, num_cus, &p, &why) == GEMM_OK ? skinny : base;
     }
     const uint32_t decomp = base & 0xFu;
-    if (p128.decision == GEMM_STREAMK && !epilogue && !(base & GEMM_TWO_PASS) &&
+    if (p128.decision == GEMM_STREAMK && !(base & GEMM_TWO_PASS) &&
         (decomp == GEMM_HEURISTIC || decomp == GEMM_STREAMK)) {
         const uint32_t tall = (base & ~0xFu) | GEMM_STREAMK | GEMM_TILE_256x128;
         if (make_plan(M, N, K, batch, layout, tall, splits, num_cus, &p, &why) == GEMM_OK && p.q >= 64) return tall;
@@ -71,7 +71,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, u
     *why = none;
     if (!out) { *why = "plan output pointer is null"; return GEMM_ERR_INVALID; }
     if ((mode & kTileBits) == GEMM_TILE_AUTO && num_cus >= 1)
-        mode = choose_tile(M, N, K, batch, layout, mode, splits, num_cus, false);
+        mode = choose_tile(M, N, K, batch, layout, mode, splits, num_cus);
     std::memset(out, 0, sizeof *out);
     if (M < 0 || N < 0 || K < 0) { *why = "M, N and K must be >= 0"; return GEMM_ERR_INVALID; }
     if (num_cus < 1) { *why = "num_cus must be >= 1"; return GEMM_ERR_INVALID; }

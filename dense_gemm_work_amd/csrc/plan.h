@@ -20,9 +20,9 @@ int make_plan_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint
 int64_t group_table_bytes(int32_t count);
 
 // The mode word with GEMM_TILE_AUTO replaced by the tile it picks for this call
-// (any other mode word comes back unchanged); `epilogue`: the call fuses one.
+// (any other mode word comes back unchanged).
 uint32_t choose_tile(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t layout, uint32_t mode, int32_t splits,
-                     int32_t num_cus, bool epilogue);
+                     int32_t num_cus);
 uint32_t choose_tile_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint32_t layout, uint32_t mode,
                              int32_t splits, int32_t num_cus);
 

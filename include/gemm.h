@@ -116,7 +116,7 @@ extern "C" {
 /* bits 12-13: output tile shape */
 #define GEMM_TILE_128x128  0x0000u /* 128 x 128 tiles (every decomposition)                     */
 #define GEMM_TILE_256x128  0x1000u /* 256 x 128 tiles: GEMM_STREAMK only (turnstile or
-                                      GEMM_ATOMIC merge; no GEMM_TWO_PASS, no fused epilogue).
+                                      GEMM_ATOMIC merge; no GEMM_TWO_PASS).
                                       The tile the book chapter's Case 4 names for CUTLASS's
                                       Stream-K example (MmaTileShape 256 x 128 x 64); a unit's
                                       64-wide k-iteration is then twice the work, the partial
@@ -138,8 +138,8 @@ extern "C" {
                                       and C the CUs: 64 x 128 when 2 T <= C (too few tiles to
                                       fill half the GPU; every decomposition); else
                                       256 x 128 Stream-K when the 128 x 128 plan is Stream-K
-                                      (GEMM_HEURISTIC or GEMM_STREAMK; not GEMM_TWO_PASS, no
-                                      fused epilogue) and each unit of the 256 x 128 plan runs
+                                      (GEMM_HEURISTIC or GEMM_STREAMK; not GEMM_TWO_PASS)
+                                      and each unit of the 256 x 128 plan runs
                                       at least 64 k-iterations, so its fixed cost stays small
                                       beside its loop; else 128 x 128.  Grouped calls choose
                                       between 128 x 128 and 64 x 128 only.                    */
@@ -422,8 +422,7 @@ int gemm_plan_grouped(const gemm_group_t *groups, int32_t count, int64_t K, uint
 /*
  * gemm_plan -- decide the decomposition for a call without running it.
  * num_cus >= 1 (no device is queried).  Fills *out; returns a status.  With
- * GEMM_TILE_AUTO, bm reports the tile picked for a call without a fused
- * epilogue.
+ * GEMM_TILE_AUTO, bm reports the tile the call runs.
  */
 int gemm_plan(int64_t M, int64_t N, int64_t K, uint32_t layout, uint32_t mode,
               int32_t splits, int32_t num_cus, gemm_plan_t *out);
@@ -443,9 +442,7 @@ int gemm_plan_batched(int64_t M, int64_t N, int64_t K, int64_t batch, uint32_t l
  * 64 KiB slot and one flag per unit; two slots per unit when a second kernel
  * adds the partials, Case 3's fixup kernel).  Plus a 256-byte status block.
  * Layout: [status 256 B | flags, 256-B aligned | counters, 256-B aligned | data].
- * batch >= 1; num_cus >= 1 (no device is queried).  With GEMM_TILE_AUTO the
- * larger of the two tiles' needs (a call with a fused epilogue may get another
- * tile than gemm_plan reports).  Returns the byte count
+ * batch >= 1; num_cus >= 1 (no device is queried).  Returns the byte count
  * (>= 0) or a negative status for arguments gemm_plan_batched rejects.
  * Ownership: the caller allocates, zero-fills once and frees it.
  */

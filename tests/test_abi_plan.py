@@ -500,15 +500,13 @@ def test_auto_tile_rule_edges(dg):
     assert bm(1536, 1536, 16384, dg.mode_word("splitk", tile="auto"), splits=2) == 128
 
 
-def test_auto_tile_workspace_covers_a_call_with_an_epilogue(dg):
+def test_auto_tile_workspace_is_the_picked_plans(dg):
     lw = dg.GEMM_B_KN | dg.GEMM_FP16
-    auto = dg.mode_word("streamk", tile="auto")
-    p = dg.gemm_plan(1536, 1536, 16384, lw, auto, 0, 256)
-    p128 = dg.gemm_plan(1536, 1536, 16384, lw, dg.mode_word("streamk"), 0, 256)
-    assert p.bm == 256
-    # with a fused epilogue the call runs 128 x 128 tiles; the size covers both
-    size = dg.gemm_workspace_size(1536, 1536, 16384, lw, auto, 0, 256)
-    assert size == max(p.workspace_bytes, p128.workspace_bytes)
+    for M, N, K, mode, splits in [(1536, 1536, 16384, "streamk", 0), (96, 512, 2048, "splitk", 8),
+                                  (2048, 2176, 4096, "heuristic", 0)]:
+        auto = dg.mode_word(mode, tile="auto")
+        p = dg.gemm_plan(M, N, K, lw, auto, splits, 256)
+        assert dg.gemm_workspace_size(M, N, K, lw, auto, splits, 256) == p.workspace_bytes
 
 
 def test_auto_tile_grouped(dg):

@@ -1,13 +1,13 @@
 """GEMM_TILE_AUTO on the GPU, through the C ABI: a call with tile "auto" runs the
 plan of the tile the library picks (the same bits as a call that names that
-tile), its output matches the fp64 oracle, and with a fused epilogue it falls
-back from 256 x 128 tiles, which have no epilogue build, to 128 x 128."""
+tile), with and without a fused epilogue, and its output matches the fp64
+oracle."""
 import pytest
 import torch
 
 from workloads import WORKLOADS, make_epilogue_inputs, make_operands
 
-from gpu_util import POISON, check_against_oracle, guarded_output, guards_intact, poison_rows, say, tile_row_sample
+from gpu_util import check_against_oracle, guarded_output, guards_intact, poison_rows, say, tile_row_sample
 
 pytestmark = pytest.mark.gpu
 
@@ -64,11 +64,11 @@ def test_auto_runs_the_picked_tile(dg, w, tile):
 
 
 @pytest.mark.parametrize("w,expect", [
-    (LONG_K, "128x128"),                   # 256 x 128 has no epilogue build
-    (WORKLOADS["c1_sk32"], "64x128"),      # 64 x 128 Stream-K fuses the epilogue
-    (WORKLOADS["c2a_m96_s8"], "64x128"),   # 64 x 128 Split-K fuses the epilogue
+    (LONG_K, "256x128"),
+    (WORKLOADS["c1_sk32"], "64x128"),
+    (WORKLOADS["c2a_m96_s8"], "64x128"),
 ], ids=["c5_longk_fp16", "c1_sk32", "c2a_m96_s8"])
-def test_auto_with_an_epilogue_takes_a_tile_that_has_one(dg, w, expect):
+def test_auto_with_an_epilogue(dg, w, expect):
     A, B = make_operands(w)
     a, b = A.to(DEV), B.to(DEV)
     c_in, bias = make_epilogue_inputs(w.M, w.N, seed=11)
@@ -77,5 +77,6 @@ def test_auto_with_an_epilogue_takes_a_tile_that_has_one(dg, w, expect):
     say(f"  auto + epilogue {w.name} {w.M}x{w.N}x{w.K} -> {expect}")
     c_auto = _call(dg, w, a, b, "auto", start, **epi)
     c_named = _call(dg, w, a, b, expect, start, **epi)
-    assert not bool(torch.any(c_auto == POISON)), "elements never written"
+    # C starts at C_in here, so only the bits of the named tile's call (checked
+    # against the oracle by the tile's own tests) tell a missed element
     assert torch.equal(c_auto.view(torch.int32), c_named.view(torch.int32)), "auto and the named tile differ"

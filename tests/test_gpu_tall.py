@@ -7,7 +7,9 @@ import numpy as np
 import pytest
 import torch
 
-from workloads import WORKLOADS, make_operands
+from oracle import epilogue as oe
+from oracle import gemm as og
+from workloads import WORKLOADS, make_epilogue_inputs, make_operands
 
 from gpu_util import (check_against_oracle, check_full, decode_trace, expected_trace, guarded_output,
                       guards_intact, oracle_full, say)
@@ -126,13 +128,58 @@ def test_tall_zero_partial_control(dg, name, atomic):
         assert ok != control
 
 
-def test_tall_refuses_epilogue(dg):
-    w = WORKLOADS["c1_sk32"]
-    a = torch.zeros((w.M, w.K), dtype=torch.bfloat16, device=DEV)
-    b = torch.zeros((w.K, w.N), dtype=torch.bfloat16, device=DEV)
-    c = torch.full((w.M, w.N), 7.0, dtype=torch.float32, device=DEV)
-    with pytest.raises(dg.GemmError) as ei:
-        dg.gemm_tensors(a, b, c, mode="streamk", splits=8, tile=TALL, alpha=2.0)
-    assert ei.value.status == dg.GEMM_ERR_UNSUPPORTED
-    torch.cuda.synchronize()
-    assert torch.all(c == 7.0)
+def _tall_epilogue(dg, w, A, B, units, atomic, alpha, beta, act, use_bias=True, **kw):
+    c_in, bias = make_epilogue_inputs(w.M, w.N, seed=5)
+    full, c = guarded_output(w.M, w.N, DEV)
+    c.copy_(c_in.to(DEV))
+    say(f"  tall epilogue {w.name} {w.M}x{w.N}x{w.K} units={units} atomic={atomic} "
+        f"alpha={alpha} beta={beta} act={act} bias={use_bias}")
+    dg.gemm_tensors(A.to(DEV), B.to(DEV), c, b_layout=w.b_layout, mode="streamk", splits=units, atomic=atomic,
+                    tile=TALL, alpha=alpha, beta=beta, bias=bias.to(DEV) if use_bias else None, act=act, **kw)
+    assert dg.gemm_sync_status() == 0, dg.gemm_last_error()
+    assert guards_intact(full, w.M, w.N), "guard band overwritten"
+    return c, c_in, bias
+
+
+@pytest.mark.parametrize("atomic", [False, True])
+@pytest.mark.parametrize("shape,epi", [
+    ((300, 200, 328, "nk", "bf16", 7), (1.5, -0.75, "gelu", True)),     # ragged M, N and K
+    ((520, 136, 72, "kn", "fp16", 3), (0.5, 0.0, "relu", True)),         # beta = 0: C_in is not read
+    ((768, 384, 1024, "kn", "bf16", 12), (-1.0, 1.25, "none", False)),
+], ids=["ragged", "beta0", "no-bias"])
+def test_tall_epilogue(dg, shape, epi, atomic):
+    M, N, K, layout, dtype, units = shape
+    alpha, beta, act, use_bias = epi
+    dist = dict(dist="uniform", low=-1.0, high=1.0) if dtype == "bf16" else dict(dist="uniform", low=-0.5, high=0.5)
+    w = WORKLOADS["c1_sk32"].with_(name="tall-epi", M=M, N=N, K=K, b_layout=layout, dtype=dtype, **dist)
+    A, B = make_operands(w)
+    c, c_in, bias = _tall_epilogue(dg, w, A, B, units, atomic, alpha, beta, act, use_bias)
+    P, S = og.ref_gemm(A, B, M, N, K, layout, dtype)
+    c0 = c_in.numpy().astype(np.float64) if beta != 0.0 else None
+    b64 = bias.numpy().astype(np.float64) if use_bias else None
+    D, _ = oe.epilogue_ref(P, c0, alpha, beta, b64, act)
+    ok, worst, idx = oe.within_bound(c.cpu().numpy().astype(np.float64), D,
+                                     oe.epilogue_bound(S, P, c0, alpha, beta, b64, act))
+    say(f"    worst err/bound = {worst:.3e} at {idx}")
+    assert ok, f"outside the epilogue bound: worst ratio {worst} at {idx}"
+
+
+def test_tall_epilogue_full_size_and_bits(dg):
+    # every element of 1536^2 x 16384 with the epilogue, and the turnstile's bits
+    # again on a second run and in reverse unit order
+    w = WORKLOADS["c5_longk_fp16"]
+    A, B, P, S = oracle_full(w)
+    alpha, beta, act = 0.75, -0.5, "gelu"
+    c, c_in, bias = _tall_epilogue(dg, w, A, B, 0, False, alpha, beta, act)
+    c0, b64 = c_in.numpy().astype(np.float64), bias.numpy().astype(np.float64)
+    D, _ = oe.epilogue_ref(P, c0, alpha, beta, b64, act)
+    ok, worst, idx = oe.within_bound(c.cpu().numpy().astype(np.float64), D,
+                                     oe.epilogue_bound(S, P, c0, alpha, beta, b64, act))
+    say(f"    worst err/bound = {worst:.3e} at {idx}")
+    assert ok, f"outside the epilogue bound: worst ratio {worst} at {idx}"
+    units = dg.gemm_plan(w.M, w.N, w.K, dg.layout_word(w.b_layout, w.dtype), dg.mode_word("streamk", tile=TALL),
+                         0, dg.gemm_num_cus()).sk_units
+    perm = torch.arange(units - 1, -1, -1, dtype=torch.int32, device=DEV)
+    for kw in ({}, {"unit_perm": perm}):
+        again, _, _ = _tall_epilogue(dg, w, A, B, 0, False, alpha, beta, act, **kw)
+        assert torch.equal(again.view(torch.int32), c.view(torch.int32))
