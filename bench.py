@@ -712,8 +712,8 @@ def grouped_main(args, dg) -> int:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is a design note, not code).", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding over several GPUs is designed, not implemented).", file=sys.stderr)
         return 2
     import torch
 

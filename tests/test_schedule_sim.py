@@ -103,7 +103,7 @@ def test_triton_structure_facts():
     assert sch.max_units_per_tile(s40) == 4                  # "up to 4 peers/tile"
 
 
-# -- spec facts about the five workloads (256 CUs) ---------------------------
+# -- the rule's decisions on the five workloads (256 CUs) --------------------------
 def test_workload_decisions():
     d = sch.decide(272, 64, 256)          # 2048x2176x4096
     assert (d.kind, d.sk_tiles, d.sk_units) == ("StreamK", 272, 256)
