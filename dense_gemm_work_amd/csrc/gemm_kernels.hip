@@ -687,7 +687,7 @@ __device__ __forceinline__ Tile<NW, TM> merge_k_halves(const AccT<TM> &acc, char
 // are numbered in groups of `group_m` tile rows, column by column inside a
 // group, so a contiguous range of tile ids is a compact 2-D block.
 // ---------------------------------------------------------------------------
-// floor(n / d) for 0 <= n < 2^31 (FastDiv in kernels.h).
+// floor(n / d) for 0 <= n < 2^31 (FastDiv in fastdiv.h).
 __device__ __forceinline__ int fdiv(int n, FastDiv d) {
     return (int)((__umulhi((uint32_t)n, d.m) + (uint32_t)n) >> d.s);
 }
@@ -2444,14 +2444,6 @@ KernelFn kernel_for(int dtype, int blayout, int kmode, bool epi, int tm, bool gr
     if (dtype == 0) return blayout == 0 ? pick<0, 0>(kmode, epi, tm, shape) : pick<0, 1>(kmode, epi, tm, shape);
     if (dtype == 1) return blayout == 0 ? pick<1, 0>(kmode, epi, tm, shape) : pick<1, 1>(kmode, epi, tm, shape);
     return nullptr;
-}
-
-FastDiv fast_div(int64_t d) {
-    if (d < 1) d = 1;   // a divisor the launch does not use
-    uint32_t s = 0;
-    while ((int64_t(1) << s) < d) ++s;
-    const uint64_t m = ((uint64_t(1) << (32 + s)) + uint64_t(d) - 1) / uint64_t(d);   // in [2^32, 2^33)
-    return FastDiv{uint32_t(m - (uint64_t(1) << 32)), s};
 }
 
 // The launch constants of the index arithmetic, for a launch of `grid` workers.

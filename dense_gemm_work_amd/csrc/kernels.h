@@ -5,6 +5,8 @@
 
 #include <cstdint>
 
+#include "fastdiv.h"
+
 namespace dgw {
 
 // Which epilogue/fixup a launch performs.
@@ -59,17 +61,6 @@ struct GroupDesc {
 static_assert(sizeof(GroupDesc) == 48, "device table entry");
 // Problems per grouped call: one wave's lanes find a tile's problem at once.
 constexpr int MAX_GROUPS = 64;
-
-// Division by a launch constant d (1 <= d <= 2^31) of an index n in
-// [0, 2^31) without a divide sequence: with s = ceil(log2 d) and
-// m = ceil(2^(32+s) / d) (so 2^32 <= m < 2^33), floor(n / d) =
-// floor(n m / 2^(32+s)) = (umulhi(n, m - 2^32) + n) >> s.  Exact: the error
-// of m, m d - 2^(32+s), is below d <= 2^s, so n m / 2^(32+s) exceeds n / d by
-// less than n / 2^(32+s) < 1 / (2 d), which cannot reach the next integer.
-struct FastDiv {
-    uint32_t m;   // m - 2^32
-    uint32_t s;
-};
 
 struct KParams {
     const uint16_t *A;     // [M,K] row-major 16-bit operands
