@@ -1,6 +1,7 @@
 """Seeded randomised sweeps through the C ABI: many small problems drawn over
-every decomposition, merge, tile shape, B layout, dtype, batch count, fused
-epilogue and CU count, plus grouped calls and the no-allocation entry point.
+every decomposition, merge, tile shape (the library's own choice included), B
+layout, dtype, batch count, fused epilogue and CU count, plus grouped calls and
+the no-allocation entry point.
 Each call is checked against the fp64 oracle (every element; the epilogue
 bound where one is fused), its guard band and the device status word, and a
 deterministic call is run twice for the same bits.  Combinations the library
@@ -52,7 +53,7 @@ def test_sweep_single_and_batched(dg):
         N = int(rng.integers(1, 90)) * 8 if layout == "kn" else int(rng.integers(1, 700))
         K = int(rng.integers(0, 130)) * 8
         batch = int(rng.choice([1, 1, 1, 2, 3]))
-        tile = str(rng.choice(["128x128", "128x128", "64x128", "256x128"]))
+        tile = str(rng.choice(["128x128", "128x128", "64x128", "256x128", "auto"]))
         mode = str(rng.choice(["dp", "splitk", "streamk", "heuristic", "streamk"]))
         cus = int(rng.choice([0, 0, 8, 32, 100]))
         cap = cap_dev if cus == 0 else cus
@@ -138,7 +139,7 @@ def test_sweep_grouped_and_noalloc(dg):
         layout = str(rng.choice(["kn", "nk"]))
         dtype = str(rng.choice(["bf16", "fp16"]))
         mode = str(rng.choice(["dp", "splitk", "streamk", "heuristic"]))
-        tile = str(rng.choice(["128x128", "64x128"]))
+        tile = str(rng.choice(["128x128", "64x128", "auto"]))
         atomic, two_pass = _merge(rng)
         K = int(rng.integers(1 if not grouped else 0, 200)) * 8
         ipt = -(-K // 64)
