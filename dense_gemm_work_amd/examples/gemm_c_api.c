@@ -2,12 +2,13 @@
  * gemm_c_api.c -- the C ABI used from plain C: device buffers from the HIP
  * runtime, one heuristic call (3 x 2 tiles of 5 k-iterations, ragged in M and
  * N: the rule stays data-parallel), one Stream-K call with 7 units and a fused
- * epilogue through gemm_ex, and a host check of both.
+ * epilogue through gemm_ex, one heuristic call with the tile left to the
+ * library (GEMM_TILE_AUTO), and a host check of each.
  *
  * Build (done by dense_gemm_work_amd/build.py):
  *   hipcc -x c ... gemm_c_api.c -L<pkg> -ldgw_gemm -o gemm_c_api
  * Run: ./gemm_c_api  -> prints the largest relative error of each call and
- * exits 0 when both are within 1e-4 of sum|a||b|.
+ * exits 0 when all are within their bounds (1e-4 of sum|a||b| for the products).
  */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
@@ -127,6 +128,24 @@ int main(void) {
         }
     printf("gemm_ex epilogue: worst |err| / bound = %.3e\n", worst2);
     ok = ok && worst2 <= 1.0;
+
+    /* 3: C = A.B, the library picking the tile: 6 tiles of 128 x 128 would fill
+     * few CUs, so it takes 64 x 128 */
+    gemm_plan_t plan3;
+    const uint32_t mode3 = GEMM_HEURISTIC | GEMM_TILE_AUTO;
+    if (gemm_plan(M, N, K, GEMM_B_KN | GEMM_BF16, mode3, 0, gemm_num_cus(), &plan3) != GEMM_OK ||
+        gemm(dA, dB, dC, M, N, K, GEMM_B_KN | GEMM_BF16, mode3, 0) != GEMM_OK || gemm_sync_status(NULL) != GEMM_OK) {
+        fprintf(stderr, "gemm with GEMM_TILE_AUTO: %s\n", gemm_last_error());
+        return 1;
+    }
+    CHECK_HIP(hipMemcpy(c2, dC, 4 * M * N, hipMemcpyDeviceToHost));
+    double worst3 = 0;
+    for (int64_t i = 0; i < M * N; ++i) {
+        const double r = fabs(c2[i] - ref[i]) / (1e-4 * mag[i] + 1e-30);
+        if (r > worst3) worst3 = r;
+    }
+    printf("gemm GEMM_TILE_AUTO: %d x %d tiles, worst |err| / (1e-4 sum|a||b|) = %.3e\n", plan3.bm, plan3.bn, worst3);
+    ok = ok && worst3 <= 1.0;
 
     hipFree(dA);
     hipFree(dB);
